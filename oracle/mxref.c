@@ -1,0 +1,332 @@
+/* mxref.c - CPU oracle for OCP MXFP4 block quantization.
+ *
+ * TEST INFRASTRUCTURE. The plain, slow, scalar reference the GPU library is
+ * checked against; only tests, the smoke check and the benchmark's CPU
+ * baseline use it. It shares no code with the GPU library.
+ *
+ * What it computes, and where the pages state it:
+ *  - An MX block is 32 contiguous elements of the last dimension sharing one
+ *    scale (vLLM MXFP8/MXFP4 page, "MXFP8: Block-32 scaling" section and the
+ *    MX format table; Axolotl MXFP4 PR page, section 2: block size must be 32).
+ *  - The scale is E8M0: a bare power of two stored in one byte (vLLM page, MX
+ *    format table; "Unveiling the Potential of Quantization with MXFP4",
+ *    technical summary section 1). The byte's bias is 127 and 255 is NaN
+ *    (reading taken where the pages are silent).
+ *  - The element is E2M1: sign, 2 exponent bits, 1 mantissa bit, largest
+ *    magnitude 6.0 (Axolotl page, section 2; "Unveiling..." section 2.A).
+ *  - Two 4-bit codes per byte, so a row of k elements packs to k/2 bytes
+ *    (vLLM page, "MXFP4: 4-bit MoE" section). Even element in the low nibble
+ *    (reading; the pages do not fix the order).
+ *  - Scale exponent: floor(log2(amax)) - 2, so the block maximum lands in
+ *    [4, 8) (the OCP rule; the pages only say the scale is 2^k).
+ *  - Elements round to the nearest E2M1 value, ties to the even code,
+ *    saturating at 6 (reading; the pages are silent on rounding).
+ *  - Overflow-aware scaling ("Unveiling..." section 2.A): a block may take a
+ *    scale one step smaller, letting its top values saturate, when that
+ *    lowers the block's squared error.
+ *  - Error measure: mean of squared differences (MXFP4 wiki page, example 2)
+ *    and per-block sum of squared errors ("Unveiling..." section 2.B).
+ *
+ * Arithmetic is C double throughout (exact for every quantity here: x/2^k,
+ * grid midpoints, decoded values), except the overflow-aware decision, which
+ * both this oracle and the device take in float in one fixed order.
+ * Build with -O2 -ffp-contract=off, never -ffast-math.
+ */
+#include "mxref.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <string.h>
+#include <xmmintrin.h>
+
+#define BLOCK 32
+
+/* E2M1 magnitudes in code order 0..7: exponent field e (2 bits, bias 1) and
+ * mantissa bit m give m*0.5 when e == 0, else 2^(e-1) * (1 + m/2). */
+static const double kGrid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* Denormals must be honoured on the host as on the device. */
+static unsigned int enter_ieee(void) {
+  unsigned int old = _mm_getcsr();
+  _mm_setcsr(old & ~(0x8000u | 0x0040u)); /* clear FTZ and DAZ */
+  return old;
+}
+static void leave_ieee(unsigned int old) { _mm_setcsr(old); }
+
+static double bf16_bits_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static uint16_t float_to_bf16_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if (isnan(f)) return 0x7FC0;
+  /* round to nearest, ties to even, on the dropped 16 bits */
+  uint32_t lsb = (u >> 16) & 1u;
+  return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+static double load_elem(const void *x, int dtype, int64_t i) {
+  if (dtype == MXREF_F32) return (double)((const float *)x)[i];
+  return bf16_bits_to_double(((const uint16_t *)x)[i]);
+}
+
+static void store_elem(void *y, int dtype, int64_t i, double v) {
+  float f = (float)v; /* exact for every decoded value below 2^128 */
+  if (isnan(v)) {
+    uint32_t q = 0x7FC00000u; /* canonical quiet NaN */
+    memcpy(&f, &q, 4);
+  }
+  if (dtype == MXREF_F32)
+    ((float *)y)[i] = f;
+  else
+    ((uint16_t *)y)[i] = float_to_bf16_bits(f);
+}
+
+/* OCP shared exponent: floor(log2 amax) - 2, biased by 127, clamped to the
+ * finite E8M0 range [0, 254]. amax == 0 gives byte 0. */
+int mxref_ocp_scale(double amax) {
+  if (amax == 0.0) return 0;
+  int e2;
+  (void)frexp(amax, &e2); /* amax = f * 2^e2, f in [0.5, 1) */
+  int floor_log2 = e2 - 1;
+  int s = floor_log2 - 2 + 127;
+  if (s < 0) s = 0;
+  if (s > 254) s = 254;
+  return s;
+}
+
+/* Nearest E2M1 value to |x| / 2^(s-127), ties to the even code, saturating. */
+int mxref_encode(double x, int s) {
+  int sign = signbit(x) ? 8 : 0;
+  if (s == 255) return sign;
+  double v = fabs(x) / ldexp(1.0, s - 127); /* exact: power-of-two divisor */
+  int idx;
+  if (v >= 6.0) {
+    idx = 7;
+  } else {
+    int lo = 0;
+    while (lo < 6 && kGrid[lo + 1] <= v) lo++;
+    int hi = lo + 1;
+    double mid = 0.5 * (kGrid[lo] + kGrid[hi]); /* exact: quarter multiples */
+    if (v < mid)
+      idx = lo;
+    else if (v > mid)
+      idx = hi;
+    else
+      idx = (lo % 2 == 0) ? lo : hi;
+  }
+  return sign | idx;
+}
+
+/* Exact value of code c at scale byte s; byte 255 decodes to NaN. */
+double mxref_decode(int c, int s) {
+  if (s == 255) return NAN;
+  double mag = kGrid[c & 7] * ldexp(1.0, s - 127);
+  return (c & 8) ? -mag : mag;
+}
+
+/* Block squared error at scale byte s, in float, in the fixed order the
+ * device uses: four groups of eight consecutive elements; inside a group one
+ * accumulator takes the even positions and one the odd positions, each by
+ * fused multiply-add; then group = even + odd, total = (g0 + g1) + (g2 + g3). */
+float mxref_oas_sse32(const double *xb, int s) {
+  float grp[4];
+  for (int g = 0; g < 4; g++) {
+    float acc_even = 0.0f, acc_odd = 0.0f;
+    for (int t = 0; t < 4; t++) {
+      int i = 8 * g + 2 * t;
+      float d0 = (float)xb[i] - (float)mxref_decode(mxref_encode(xb[i], s), s);
+      float d1 = (float)xb[i + 1] - (float)mxref_decode(mxref_encode(xb[i + 1], s), s);
+      acc_even = fmaf(d0, d0, acc_even);
+      acc_odd = fmaf(d1, d1, acc_odd);
+    }
+    grp[g] = acc_even + acc_odd;
+  }
+  return (grp[0] + grp[1]) + (grp[2] + grp[3]);
+}
+
+/* Scale byte of one block (xb holds its 32 values). */
+static int block_scale(const double *xb, int mode) {
+  double amax = 0.0;
+  for (int i = 0; i < BLOCK; i++) {
+    if (isnan(xb[i]) || isinf(xb[i])) return 255;
+    double a = fabs(xb[i]);
+    if (a > amax) amax = a;
+  }
+  int s0 = mxref_ocp_scale(amax);
+  if (mode == MXREF_OAS && s0 >= 1) {
+    float sse_ocp = mxref_oas_sse32(xb, s0);
+    float sse_low = mxref_oas_sse32(xb, s0 - 1);
+    if (sse_low < sse_ocp) return s0 - 1; /* strict: a tie keeps the OCP byte */
+  }
+  return s0;
+}
+
+/* ---- row-parallel drivers ---------------------------------------------- */
+
+typedef struct {
+  int op; /* 0 quantize, 1 dequantize, 2 fakequant, 3 block_mse */
+  const void *x;
+  int dtype;
+  int mode;
+  int64_t k;
+  const uint8_t *codes_in;
+  const uint8_t *scales_in;
+  uint8_t *codes;
+  uint8_t *scales;
+  void *y;
+  float *block_mse;
+  int64_t r0, r1;
+  long double sse; /* per-thread partial of the tensor SSE */
+} job_t;
+
+static void run_rows(job_t *j) {
+  unsigned int csr = enter_ieee();
+  const int64_t nb = j->k / BLOCK;
+  double xb[BLOCK];
+  j->sse = 0.0L;
+  for (int64_t r = j->r0; r < j->r1; r++) {
+    for (int64_t b = 0; b < nb; b++) {
+      const int64_t e0 = r * j->k + b * BLOCK; /* first element of the block */
+      const int64_t bi = r * nb + b;           /* block index */
+      if (j->op == 0 || j->op == 2) {
+        for (int i = 0; i < BLOCK; i++) xb[i] = load_elem(j->x, j->dtype, e0 + i);
+        int s = block_scale(xb, j->mode);
+        int code[BLOCK];
+        for (int i = 0; i < BLOCK; i++) code[i] = mxref_encode(xb[i], s);
+        if (j->op == 0) {
+          for (int t = 0; t < BLOCK / 2; t++)
+            j->codes[e0 / 2 + t] = (uint8_t)(code[2 * t] | (code[2 * t + 1] << 4));
+          j->scales[bi] = (uint8_t)s;
+        } else {
+          for (int i = 0; i < BLOCK; i++)
+            store_elem(j->y, j->dtype, e0 + i, mxref_decode(code[i], s));
+        }
+      } else {
+        const int s = j->scales_in[bi];
+        double sse = 0.0;
+        for (int i = 0; i < BLOCK; i++) {
+          uint8_t byte = j->codes_in[(e0 + i) / 2];
+          int c = (i % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+          double q = mxref_decode(c, s);
+          if (j->op == 1) {
+            store_elem(j->y, j->dtype, e0 + i, q);
+          } else {
+            /* the reconstruction is the value a dequantize in x's dtype
+               would return: round the exact value to float */
+            double qf = isnan(q) ? q : (double)(float)q;
+            double d = load_elem(j->x, j->dtype, e0 + i) - qf;
+            sse += d * d;
+          }
+        }
+        if (j->op == 3) {
+          if (j->block_mse) j->block_mse[bi] = (float)(sse / BLOCK);
+          j->sse += (long double)sse;
+        }
+      }
+    }
+  }
+  leave_ieee(csr);
+}
+
+static void *thread_main(void *arg) {
+  run_rows((job_t *)arg);
+  return NULL;
+}
+
+#define MAX_THREADS 256
+
+static int run(job_t proto, int64_t rows, int threads, long double *sse_out) {
+  if (threads < 1) threads = 1;
+  if (threads > MAX_THREADS) threads = MAX_THREADS;
+  if (threads > rows) threads = rows > 0 ? (int)rows : 1;
+  job_t jobs[MAX_THREADS];
+  pthread_t tid[MAX_THREADS];
+  for (int t = 0; t < threads; t++) {
+    jobs[t] = proto;
+    jobs[t].r0 = rows * t / threads;
+    jobs[t].r1 = rows * (t + 1) / threads;
+  }
+  if (threads == 1) {
+    run_rows(&jobs[0]);
+  } else {
+    for (int t = 0; t < threads; t++)
+      if (pthread_create(&tid[t], NULL, thread_main, &jobs[t]) != 0) return -9;
+    for (int t = 0; t < threads; t++) pthread_join(tid[t], NULL);
+  }
+  if (sse_out) {
+    long double s = 0.0L;
+    for (int t = 0; t < threads; t++) s += jobs[t].sse;
+    *sse_out = s;
+  }
+  return 0;
+}
+
+static int check_shape(int64_t rows, int64_t k) {
+  if (rows < 0 || k <= 0 || k % BLOCK != 0) return -2;
+  return 0;
+}
+
+int mxref_quantize(const void *x, int dtype, int64_t rows, int64_t k, int mode,
+                   uint8_t *codes, uint8_t *scales, int threads) {
+  if (check_shape(rows, k)) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (mode != MXREF_OCP && mode != MXREF_OAS) return -4;
+  if (rows == 0) return 0;
+  if (!x || !codes || !scales) return -1;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.op = 0; j.x = x; j.dtype = dtype; j.mode = mode; j.k = k;
+  j.codes = codes; j.scales = scales;
+  return run(j, rows, threads, NULL);
+}
+
+int mxref_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                     int64_t k, int dtype, void *y, int threads) {
+  if (check_shape(rows, k)) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (rows == 0) return 0;
+  if (!codes || !scales || !y) return -1;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.op = 1; j.dtype = dtype; j.k = k;
+  j.codes_in = codes; j.scales_in = scales; j.y = y;
+  return run(j, rows, threads, NULL);
+}
+
+int mxref_fakequant(const void *x, int dtype, int64_t rows, int64_t k, int mode,
+                    void *y, int threads) {
+  if (check_shape(rows, k)) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (mode != MXREF_OCP && mode != MXREF_OAS) return -4;
+  if (rows == 0) return 0;
+  if (!x || !y) return -1;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.op = 2; j.x = x; j.dtype = dtype; j.mode = mode; j.k = k; j.y = y;
+  return run(j, rows, threads, NULL);
+}
+
+int mxref_block_mse(const void *x, int dtype, const uint8_t *codes,
+                    const uint8_t *scales, int64_t rows, int64_t k,
+                    float *block_mse, double *tensor_sse, int threads) {
+  if (check_shape(rows, k)) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (rows == 0) {
+    if (tensor_sse) *tensor_sse = 0.0;
+    return 0;
+  }
+  if (!x || !codes || !scales) return -1;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.op = 3; j.x = x; j.dtype = dtype; j.k = k;
+  j.codes_in = codes; j.scales_in = scales; j.block_mse = block_mse;
+  long double sse = 0.0L;
+  int rc = run(j, rows, threads, &sse);
+  if (tensor_sse) *tensor_sse = (double)sse;
+  return rc;
+}
