@@ -1,0 +1,225 @@
+"""Benchmark of the MXFP4 hot path on one MI355X.
+
+One step = every operation of the path over one batch of bf16 activations
+[8192 tokens, 4096 hidden] (Student-t(3) body, 20 outlier channels x50):
+  quantize (OCP scale), quantize (overflow-aware scale), dequantize -> bf16,
+  fused fake-quant (OCP), per-block MSE of the OCP result.
+Throughput = algorithmic bytes of the step / step time (inputs resident in
+HBM). Buffer sets rotate so the working set is >= 1 GiB and the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+Prints ONE JSON line. --gpus N with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "MXFP4 quantize/fake-quant GB/s (bf16 in) and % of HBM peak, 1× MI355X"
+WORKLOAD = ("bf16 activations 8192 tokens x 4096 hidden, Student-t(nu=3), "
+            "20 outlier channels x50 (seed 2)")
+
+# algorithmic bytes per element (bf16 input): what each op must move
+BYTES_PER_ELEM = {
+    "quantize_ocp": 2 + 0.5 + 1 / 32,      # x in, codes + scales out
+    "quantize_oas": 2 + 0.5 + 1 / 32,
+    "dequantize_bf16": 0.5 + 1 / 32 + 2,   # codes + scales in, y out
+    "fakequant_ocp": 2 + 2,                # x in, y out
+    "block_mse": 2 + 0.5 + 1 / 32 + 4 / 32,  # x, codes, scales in; fp32/block out
+}
+OPS = list(BYTES_PER_ELEM)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate-gib", type=float, default=1.5,
+                    help="minimum working set across rotated buffer sets")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; every MX block is independent, "
+              "so the path shards by rows with no exchange (see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import microscaling_fp4_block_mx_amd as mx
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mx.load_library()
+
+    x_host = workloads.bf16_student_t_outlier_channels(2)
+    R_, K_ = x_host.shape
+    n = x_host.numel()
+    per_set = n * (2 + 0.5 * 2 + 2 / 32 + 2 + 2 + 4 / 32)
+    n_sets = max(2, int(np.ceil(args.rotate_gib * 2 ** 30 / per_set)))
+
+    x0 = x_host.to(dev)
+    sets = []
+    for _ in range(n_sets):
+        sets.append(dict(
+            x=x0.clone(),
+            c_ocp=torch.empty((R_, K_ // 2), dtype=torch.uint8, device=dev),
+            s_ocp=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
+            c_oas=torch.empty((R_, K_ // 2), dtype=torch.uint8, device=dev),
+            s_oas=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
+            y_dq=torch.empty_like(x0),
+            y_fq=torch.empty_like(x0),
+            bm=torch.empty((R_, K_ // 32), dtype=torch.float32, device=dev),
+        ))
+    del x0
+    sse = torch.empty((), dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def run(op, b):
+        if op == "quantize_ocp":
+            st = mx.mx_quantize(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP,
+                                b["c_ocp"].data_ptr(), b["s_ocp"].data_ptr(), sh)
+        elif op == "quantize_oas":
+            st = mx.mx_quantize(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mx.MX_SCALE_OAS,
+                                b["c_oas"].data_ptr(), b["s_oas"].data_ptr(), sh)
+        elif op == "dequantize_bf16":
+            st = mx.mx_dequantize(b["c_ocp"].data_ptr(), b["s_ocp"].data_ptr(), R_, K_,
+                                  mx.MX_BF16, b["y_dq"].data_ptr(), sh)
+        elif op == "fakequant_ocp":
+            st = mx.mx_fakequant(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP,
+                                 b["y_fq"].data_ptr(), sh)
+        else:
+            st = mx.mx_block_mse(b["x"].data_ptr(), mx.MX_BF16, b["c_ocp"].data_ptr(),
+                                 b["s_ocp"].data_ptr(), R_, K_, b["bm"].data_ptr(),
+                                 sse.data_ptr(), sh)
+        if st != mx.MX_OK:
+            raise RuntimeError(mx.mx_status_string(st))
+
+    # warmup (also produces the codes each set's dequantize / block_mse read)
+    for i in range(max(args.warmup, n_sets)):
+        for op in OPS:
+            run(op, sets[i % n_sets])
+    torch.cuda.synchronize()
+
+    # timed region: events on the launch stream between consecutive ops
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(OPS) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        b = sets[i % n_sets]
+        ev[i][0].record(stream)
+        for j, op in enumerate(OPS):
+            run(op, b)
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    op_ms = {op: 0.0 for op in OPS}
+    step_ms = 0.0
+    for i in range(K):
+        for j, op in enumerate(OPS):
+            op_ms[op] += ev[i][j].elapsed_time(ev[i][j + 1])
+        step_ms += ev[i][0].elapsed_time(ev[i][-1])
+    op_ms = {op: t / K for op, t in op_ms.items()}
+    ms_per_step = step_ms / K
+    bytes_op = {op: BYTES_PER_ELEM[op] * n for op in OPS}
+    bytes_step = sum(bytes_op.values())
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    breakdown = {}
+    for op in OPS:
+        gbs = bytes_op[op] / (op_ms[op] * 1e-3) / 1e9
+        breakdown[op] = {"us": round(op_ms[op] * 1e3, 2), "GB/s": round(gbs, 1),
+                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                         "bytes": int(bytes_op[op])}
+    dom = max(OPS, key=lambda o: op_ms[o])
+    dom_gbs = bytes_op[dom] / (op_ms[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "bytes_per_launch": int(bytes_op[dom]),
+                "avg_launch_us": round(op_ms[dom] * 1e3, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x_host, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "rows": R_, "k": K_, "step": OPS,
+                   "bytes_per_step": int(bytes_step),
+                   "elements_per_s": round(n / (ms_per_step * 1e-3), 1),
+                   "rotation_sets": n_sets,
+                   "working_set_gib": round(n_sets * per_set / 2 ** 30, 2),
+                   "wall_s_timed": round(wall, 4)},
+        "breakdown": breakdown,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(x_host, target_s):
+    """The oracle as it stands, on the host cores, over a bounded sample of
+    the same workload (leading rows), running the same step."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    oracle.build(force=not os.path.exists(os.path.join(ROOT, "oracle", "libmxref.so")))
+    cores = max(1, len(os.sched_getaffinity(0)))
+    xs_full = workloads.to_bf16_bits(x_host)
+    rows = 256
+    xs = np.ascontiguousarray(xs_full[:rows])
+    n = xs.size
+    bytes_step = sum(BYTES_PER_ELEM[o] for o in OPS) * n
+    done, t0 = 0, time.perf_counter()
+    while True:
+        c, s = oracle.quantize(xs, "ocp", threads=cores)
+        oracle.quantize(xs, "oas", threads=cores)
+        oracle.dequantize(c, s, "bf16", threads=cores)
+        oracle.fakequant(xs, "ocp", threads=cores)
+        oracle.block_mse(xs, c, s, threads=cores)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+        if done == 1:  # size the sample so the loop lands near the target
+            rows_next = int(min(xs_full.shape[0], rows * max(1.0, target_s / max(el, 1e-3) / 3)))
+            if rows_next > rows:
+                rows = rows_next
+                xs = np.ascontiguousarray(xs_full[:rows])
+                n = xs.size
+                bytes_step = sum(BYTES_PER_ELEM[o] for o in OPS) * n
+                done, t0 = 0, time.perf_counter()
+    gbs = done * bytes_step / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} step(s) over the first {rows} rows x 4096 of the same tensor "
+                      f"({el:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+/* mx.h - C ABI of the MI355X (gfx950) MXFP4 block-quantization library.
+ *
+ * Format (OCP microscaling, MXFP4):
+ *   - an MX block is 32 contiguous elements of the last dimension sharing one
+ *     scale (vLLM MXFP8/MXFP4 page, "MXFP8: Block-32 scaling" section and MX
+ *     format table; Axolotl MXFP4 PR page, section 2 fixes the block at 32);
+ *   - the scale is E8M0, a power of two 2^(s-127) stored as one byte s; 255
+ *     is NaN (vLLM page, MX format table; "Unveiling the Potential of
+ *     Quantization with MXFP4", technical summary section 1);
+ *   - each element is E2M1 (sign, 2 exponent bits, 1 mantissa bit; values
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6; Axolotl page section 2, "Unveiling..."
+ *     section 2.A), two codes per byte, the even element in the low nibble
+ *     (vLLM page, "MXFP4: 4-bit MoE" section gives the two-per-byte packing
+ *     and the k/2 last dimension).
+ *
+ * Layout: every tensor is contiguous row-major; leading dimensions are
+ * flattened into `rows` by the caller (the vLLM page makes the weight
+ * contiguous before quantizing). For x/y of shape [rows, k]:
+ *   codes  uint8 [rows, k/2]     scales  uint8 [rows, k/32]
+ * k must be a positive multiple of 32 (vLLM page, MXFP8 section: the input
+ * dimension must be a multiple of 32); the block size is not a parameter.
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers, allocated and owned by the
+ *     caller; the library allocates no device memory and keeps no state
+ *     between calls. It is safe to call from several host threads.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Arguments are validated synchronously on the host; on MX_OK the work
+ *     has been enqueued on `stream` and completes asynchronously. A device
+ *     fault surfaces at the caller's next synchronization.
+ *   - rows == 0 returns MX_OK without launching anything (pointers may then
+ *     be NULL).
+ *   - x, y, codes and scales must be 16-byte aligned (MX_ERR_ALIGN).
+ *   - Outputs must not overlap inputs, except that mx_fakequant accepts
+ *     y == x exactly (in place). Partial overlap is MX_ERR_ALIAS.
+ *   - On any error nothing is launched and no output is touched.
+ */
+#ifndef MX_H
+#define MX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,   /* a required pointer is NULL                          */
+  MX_ERR_SHAPE = 2,  /* rows < 0, k <= 0, k % 32 != 0, or rows*k overflows   */
+  MX_ERR_DTYPE = 3,  /* dtype is not MX_F32 / MX_BF16                        */
+  MX_ERR_MODE = 4,   /* mode is not a mx_scale_mode_t value                  */
+  MX_ERR_ALIGN = 5,  /* a data pointer is not 16-byte aligned                */
+  MX_ERR_HIP = 6,    /* the HIP launch failed; see mx_last_error_detail()    */
+  MX_ERR_ALIAS = 7   /* an output partially overlaps an input                */
+} mx_status_t;
+
+typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype_t;
+
+typedef enum {
+  /* OCP rule: s = floor(log2(amax)) - 2 + 127, clamped to [0, 254], so the
+     block maximum lands in [4, 8) and values above 6 saturate; s = 255 when
+     the block holds a NaN or an infinity. amax == 0 gives s = 0. */
+  MX_SCALE_OCP = 0,
+  /* Overflow-aware scaling ("Unveiling the Potential of Quantization with
+     MXFP4", technical summary section 2.A: take a smaller scale and let the
+     top values saturate when that lowers the error). With s0 the OCP byte,
+     a block with s0 >= 1 takes s0 - 1 when its squared error at s0 - 1 is
+     strictly smaller than at s0; ties keep s0. The squared error is computed
+     in fp32 in one fixed order: elements 8g..8g+7 form group g (g = 0..3);
+     within a group one accumulator takes the even positions and one the odd
+     positions, each acc = fma(d, d, acc) with d = x - x_hat (fp32); group =
+     even + odd; total = (g0 + g1) + (g2 + g3). */
+  MX_SCALE_OAS = 1
+} mx_scale_mode_t;
+
+/* Quantize x [rows, k] (fp32 or bf16) to packed E2M1 codes [rows, k/2] and
+ * E8M0 scales [rows, k/32]. Each element is rounded to the nearest E2M1
+ * value of x / 2^(s-127), ties to the even code, saturating at 6; the sign
+ * is kept (so -0 and negative values that round to zero give code 0x8).
+ * In a NaN/Inf block every code is the element's sign bit alone.
+ * Source: vLLM MXFP8/MXFP4 page (online quantization after loading,
+ * "MXFP8: Block-32 scaling" and "MXFP4: 4-bit MoE" sections). */
+mx_status_t mx_quantize(const void *x, mx_dtype_t x_dtype, int64_t rows,
+                        int64_t k, mx_scale_mode_t mode, uint8_t *codes,
+                        uint8_t *scales, void *stream);
+
+/* Dequantize codes [rows, k/2] and scales [rows, k/32] to y [rows, k] in
+ * y_dtype: y = +-E2M1(code) * 2^(s-127), exact for s <= 252; s = 253, 254
+ * may overflow to +-Inf; s = 255 gives the canonical quiet NaN (fp32
+ * 0x7FC00000, bf16 0x7FC0) for every element of the block.
+ * Source: vLLM MXFP8/MXFP4 page ("Why this design": bf16 weights converted
+ * at load time and used in the low-precision format). */
+mx_status_t mx_dequantize(const uint8_t *codes, const uint8_t *scales,
+                          int64_t rows, int64_t k, mx_dtype_t y_dtype, void *y,
+                          void *stream);
+
+/* Fused quantize -> dequantize: y = dequantize(quantize(x, mode)) in x's
+ * dtype, with nothing else written. y may equal x (in place).
+ * Source: Axolotl MXFP4 PR page, sections 2-3 (fake-quantization of weights
+ * and activations for quantization-aware training, block size 32). */
+mx_status_t mx_fakequant(const void *x, mx_dtype_t dtype, int64_t rows,
+                         int64_t k, mx_scale_mode_t mode, void *y,
+                         void *stream);
+
+/* Quantization error of x against (codes, scales): per block
+ * SSE = sum_i (x_i - x_hat_i)^2 in fp64, with x_hat_i the value
+ * mx_dequantize returns in x's dtype; block_mse[b] = (float)(SSE_b / 32).
+ * tensor_sse (one device double, overwritten) receives the sum of all block
+ * SSEs in fp64; the tensor MSE is tensor_sse / (rows * k). Either output may
+ * be NULL (both NULL is MX_ERR_NULL). block_mse must be 4-byte aligned and
+ * tensor_sse 8-byte aligned. The block values are deterministic; the tensor
+ * sum's rounding may differ between runs (fp64 atomics).
+ * Source: MXFP4 wiki page, example 2 (MSE as the quantization error);
+ * "Unveiling..." section 2.B (block SSE as the objective). */
+mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype,
+                         const uint8_t *codes, const uint8_t *scales,
+                         int64_t rows, int64_t k, float *block_mse,
+                         double *tensor_sse, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *mx_status_string(mx_status_t s);
+
+/* Detail of the last MX_ERR_HIP on the calling thread ("" if none). */
+const char *mx_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MX_H */

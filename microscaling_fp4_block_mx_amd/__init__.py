@@ -1,0 +1,193 @@
+"""MXFP4 block quantization on MI355X (gfx950): Python binding of libmx.so.
+
+This module only marshals arguments: every step of quantize, dequantize,
+fake-quant and the error reduction runs in the HIP kernels behind the C ABI
+declared in include/mx.h. PyTorch supplies device memory and the current
+stream. There is no CPU fallback: if libmx.so is missing or a tensor is not
+on a GPU, the call raises.
+
+Two layers:
+  * ``mx_quantize``, ``mx_dequantize``, ``mx_fakequant``, ``mx_block_mse``,
+    ``mx_status_string``: the C entry points, same names and arguments
+    (raw device pointers as ints, stream handle as int), returning the status.
+  * ``quantize``, ``dequantize``, ``fakequant``, ``block_mse``: tensor-level
+    helpers that allocate outputs with torch and raise on a bad status
+    (``ValueError`` for argument errors, as the Axolotl MXFP4 PR page does
+    for a block size other than 32; ``RuntimeError`` for HIP errors).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmx.so")
+
+MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_DTYPE, MX_ERR_MODE, MX_ERR_ALIGN, MX_ERR_HIP, \
+    MX_ERR_ALIAS = range(8)
+MX_F32, MX_BF16 = 0, 1
+MX_SCALE_OCP, MX_SCALE_OAS = 0, 1
+BLOCK = 32
+
+_MODES = {"ocp": MX_SCALE_OCP, "oas": MX_SCALE_OAS}
+_DTYPES = {torch.float32: MX_F32, torch.bfloat16: MX_BF16}
+EXPORTS = ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
+           "mx_status_string", "mx_last_error_detail")
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmx.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m microscaling_fp4_block_mx_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.mx_quantize.argtypes = [p, i32, i64, i64, i32, p, p, p]
+    lib.mx_dequantize.argtypes = [p, p, i64, i64, i32, p, p]
+    lib.mx_fakequant.argtypes = [p, i32, i64, i64, i32, p, p]
+    lib.mx_block_mse.argtypes = [p, i32, p, p, i64, i64, p, p, p]
+    for f in ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse"):
+        getattr(lib, f).restype = i32
+    lib.mx_status_string.argtypes = [i32]
+    lib.mx_status_string.restype = ctypes.c_char_p
+    lib.mx_last_error_detail.argtypes = []
+    lib.mx_last_error_detail.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---- C entry points, same names -------------------------------------------
+
+def mx_quantize(x, x_dtype, rows, k, mode, codes, scales, stream) -> int:
+    return load_library().mx_quantize(x, x_dtype, rows, k, mode, codes, scales, stream)
+
+
+def mx_dequantize(codes, scales, rows, k, y_dtype, y, stream) -> int:
+    return load_library().mx_dequantize(codes, scales, rows, k, y_dtype, y, stream)
+
+
+def mx_fakequant(x, dtype, rows, k, mode, y, stream) -> int:
+    return load_library().mx_fakequant(x, dtype, rows, k, mode, y, stream)
+
+
+def mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse, tensor_sse, stream) -> int:
+    return load_library().mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse,
+                                       tensor_sse, stream)
+
+
+def mx_status_string(status: int) -> str:
+    return load_library().mx_status_string(status).decode()
+
+
+# ---- tensor helpers --------------------------------------------------------
+
+def _raise(status: int):
+    if status == MX_OK:
+        return
+    msg = mx_status_string(status)
+    if status == MX_ERR_HIP:
+        raise RuntimeError(msg + ": " + load_library().mx_last_error_detail().decode())
+    raise ValueError(msg)
+
+
+def _check_input(x: torch.Tensor):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError("MXFP4 kernels need a GPU tensor")
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() == 0:
+        raise ValueError("need at least one dimension")
+    if not x.is_contiguous():
+        raise ValueError("input must be contiguous")
+    k = x.shape[-1]
+    if k <= 0 or k % BLOCK:
+        raise ValueError("MXFP4 needs the last dimension to be a multiple of 32")
+    return x.numel() // k if x.numel() else 0, k
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _mode(mode: str) -> int:
+    try:
+        return _MODES[mode]
+    except KeyError:
+        raise ValueError(f"mode must be 'ocp' or 'oas', got {mode!r}") from None
+
+
+def quantize(x: torch.Tensor, mode: str = "ocp", codes: torch.Tensor | None = None,
+             scales: torch.Tensor | None = None):
+    """x [..., k] -> (codes uint8 [..., k/2], scales uint8 [..., k/32])."""
+    rows, k = _check_input(x)
+    lead = tuple(x.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (k // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + (k // BLOCK,), dtype=torch.uint8, device=x.device)
+    if codes.numel() * 2 != x.numel() or scales.numel() * BLOCK != x.numel():
+        raise ValueError("output sizes do not match x")
+    with torch.cuda.device(x.device):
+        _raise(mx_quantize(x.data_ptr(), _DTYPES[x.dtype], rows, k, _mode(mode),
+                           codes.data_ptr(), scales.data_ptr(), _stream(x.device)))
+    return codes, scales
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, dtype=torch.bfloat16,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """codes [..., k/2] + scales [..., k/32] -> y [..., k] in dtype."""
+    if not codes.is_cuda or codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise ValueError("codes and scales must be uint8 GPU tensors")
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("codes and scales must be contiguous")
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
+    k = codes.shape[-1] * 2
+    rows = codes.numel() // (k // 2) if codes.numel() else 0
+    if scales.numel() * BLOCK != codes.numel() * 2:
+        raise ValueError("scales do not match codes")
+    if out is None:
+        out = torch.empty(tuple(codes.shape[:-1]) + (k,), dtype=dtype, device=codes.device)
+    with torch.cuda.device(codes.device):
+        _raise(mx_dequantize(codes.data_ptr(), scales.data_ptr(), rows, k, _DTYPES[dtype],
+                             out.data_ptr(), _stream(codes.device)))
+    return out
+
+
+def fakequant(x: torch.Tensor, mode: str = "ocp", out: torch.Tensor | None = None) -> torch.Tensor:
+    """dequantize(quantize(x)) in x's dtype; out may be x (in place)."""
+    rows, k = _check_input(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.numel() != x.numel() or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    with torch.cuda.device(x.device):
+        _raise(mx_fakequant(x.data_ptr(), _DTYPES[x.dtype], rows, k, _mode(mode),
+                            out.data_ptr(), _stream(x.device)))
+    return out
+
+
+def block_mse(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+              per_block: bool = True):
+    """-> (block_mse float32 [..., k/32] or None, tensor SSE as a 0-dim float64
+    GPU tensor). Tensor MSE = SSE / x.numel()."""
+    rows, k = _check_input(x)
+    if codes.numel() * 2 != x.numel() or scales.numel() * BLOCK != x.numel():
+        raise ValueError("codes/scales do not match x")
+    bm = None
+    if per_block:
+        bm = torch.empty(tuple(x.shape[:-1]) + (k // BLOCK,), dtype=torch.float32,
+                         device=x.device)
+    sse = torch.empty((), dtype=torch.float64, device=x.device)
+    with torch.cuda.device(x.device):
+        _raise(mx_block_mse(x.data_ptr(), _DTYPES[x.dtype], codes.data_ptr(), scales.data_ptr(),
+                            rows, k, bm.data_ptr() if bm is not None else None,
+                            sse.data_ptr(), _stream(x.device)))
+    return bm, sse

@@ -1,0 +1,142 @@
+// mx_api.cpp - C ABI of the MXFP4 library: synchronous host-side argument
+// validation, then one asynchronous launch on the caller's stream.
+// Every check here runs before any HIP call, so the error paths can be
+// exercised on a machine without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "mx_internal.h"
+
+namespace {
+
+thread_local char g_detail[256] = "";
+
+constexpr int64_t kBlock = 32;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mx_status_t check_shape(int64_t rows, int64_t k) {
+  if (rows < 0 || k <= 0 || k % kBlock != 0) return MX_ERR_SHAPE;
+  // rows * k elements, each up to 4 bytes wide, must be addressable.
+  if (rows > 0 && k > (INT64_MAX / 8) / rows) return MX_ERR_SHAPE;
+  return MX_OK;
+}
+
+bool dtype_ok(int d) { return d == MX_F32 || d == MX_BF16; }
+bool mode_ok(int m) { return m == MX_SCALE_OCP || m == MX_SCALE_OAS; }
+int64_t elem_bytes(int d) { return d == MX_F32 ? 4 : 2; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+mx_status_t finish(hipError_t e) {
+  if (e == hipSuccess) return MX_OK;
+  strncpy(g_detail, hipGetErrorString(e), sizeof g_detail - 1);
+  g_detail[sizeof g_detail - 1] = 0;
+  return MX_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status_t mx_quantize(const void *x, mx_dtype_t x_dtype, int64_t rows, int64_t k,
+                        mx_scale_mode_t mode, uint8_t *codes, uint8_t *scales, void *stream) {
+  if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;
+  if (!mode_ok(mode)) return MX_ERR_MODE;
+  if (mx_status_t s = check_shape(rows, k)) return s;
+  if (rows == 0) return MX_OK;
+  if (!x || !codes || !scales) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  const int64_t nx = n * elem_bytes(x_dtype);
+  if (overlap(x, nx, codes, n / 2) || overlap(x, nx, scales, n / kBlock) ||
+      overlap(codes, n / 2, scales, n / kBlock))
+    return MX_ERR_ALIAS;
+  return finish(mxi_launch_quantize(x, x_dtype == MX_BF16, mode, n / 8, codes, scales,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t k,
+                          mx_dtype_t y_dtype, void *y, void *stream) {
+  if (!dtype_ok(y_dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape(rows, k)) return s;
+  if (rows == 0) return MX_OK;
+  if (!codes || !scales || !y) return MX_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(y)) return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  const int64_t ny = n * elem_bytes(y_dtype);
+  if (overlap(y, ny, codes, n / 2) || overlap(y, ny, scales, n / kBlock)) return MX_ERR_ALIAS;
+  return finish(mxi_launch_dequantize(codes, scales, y_dtype == MX_BF16, n / 8, y,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_fakequant(const void *x, mx_dtype_t dtype, int64_t rows, int64_t k,
+                         mx_scale_mode_t mode, void *y, void *stream) {
+  if (!dtype_ok(dtype)) return MX_ERR_DTYPE;
+  if (!mode_ok(mode)) return MX_ERR_MODE;
+  if (mx_status_t s = check_shape(rows, k)) return s;
+  if (rows == 0) return MX_OK;
+  if (!x || !y) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return MX_ERR_ALIGN;
+  const int64_t nb = rows * k * elem_bytes(dtype);
+  if (x != y && overlap(x, nb, y, nb)) return MX_ERR_ALIAS;
+  return finish(mxi_launch_fakequant(x, dtype == MX_BF16, mode, rows * k / 8, y,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype, const uint8_t *codes,
+                         const uint8_t *scales, int64_t rows, int64_t k, float *block_mse,
+                         double *tensor_sse, void *stream) {
+  if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape(rows, k)) return s;
+  if (!block_mse && !tensor_sse) return MX_ERR_NULL;
+  if (rows == 0) {
+    // an empty tensor has zero error; still a device write, so it is enqueued
+    if (tensor_sse) {
+      if ((reinterpret_cast<uintptr_t>(tensor_sse) & 7u) != 0) return MX_ERR_ALIGN;
+      return finish(mxi_launch_block_mse(nullptr, 0, nullptr, nullptr, 0, nullptr, tensor_sse,
+                                         static_cast<hipStream_t>(stream)));
+    }
+    return MX_OK;
+  }
+  if (!x || !codes || !scales) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGN;
+  if (block_mse && (reinterpret_cast<uintptr_t>(block_mse) & 3u) != 0) return MX_ERR_ALIGN;
+  if (tensor_sse && (reinterpret_cast<uintptr_t>(tensor_sse) & 7u) != 0) return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  const int64_t nx = n * elem_bytes(x_dtype);
+  if (block_mse && (overlap(block_mse, 4 * (n / kBlock), x, nx) ||
+                    overlap(block_mse, 4 * (n / kBlock), codes, n / 2) ||
+                    overlap(block_mse, 4 * (n / kBlock), scales, n / kBlock)))
+    return MX_ERR_ALIAS;
+  if (tensor_sse && (overlap(tensor_sse, 8, x, nx) || overlap(tensor_sse, 8, codes, n / 2) ||
+                     overlap(tensor_sse, 8, scales, n / kBlock) ||
+                     (block_mse && overlap(tensor_sse, 8, block_mse, 4 * (n / kBlock)))))
+    return MX_ERR_ALIAS;
+  return finish(mxi_launch_block_mse(x, x_dtype == MX_BF16, codes, scales, n / 8, block_mse,
+                                     tensor_sse, static_cast<hipStream_t>(stream)));
+}
+
+const char *mx_status_string(mx_status_t s) {
+  switch (s) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: need rows >= 0 and k a positive multiple of 32";
+    case MX_ERR_DTYPE: return "MX_ERR_DTYPE: dtype must be MX_F32 or MX_BF16";
+    case MX_ERR_MODE: return "MX_ERR_MODE: mode must be MX_SCALE_OCP or MX_SCALE_OAS";
+    case MX_ERR_ALIGN: return "MX_ERR_ALIGN: data pointers must be 16-byte aligned";
+    case MX_ERR_HIP: return "MX_ERR_HIP: HIP launch failed";
+    case MX_ERR_ALIAS: return "MX_ERR_ALIAS: an output overlaps an input";
+  }
+  return "unknown mx_status_t";
+}
+
+const char *mx_last_error_detail(void) { return g_detail; }
+
+}  // extern "C"

@@ -1,0 +1,20 @@
+// mx_internal.h - launchers shared by the C ABI (mx_api.cpp) and the kernels.
+#ifndef MX_INTERNAL_H
+#define MX_INTERNAL_H
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx.h"
+
+// nitems = rows * k / 8 (one item = 8 elements = 4 code bytes); callers have
+// validated shapes, alignment and aliasing.
+hipError_t mxi_launch_quantize(const void *x, int bf16, int mode, int64_t nitems,
+                               uint8_t *codes, uint8_t *scales, hipStream_t st);
+hipError_t mxi_launch_fakequant(const void *x, int bf16, int mode, int64_t nitems, void *y,
+                                hipStream_t st);
+hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, int bf16,
+                                 int64_t nitems, void *y, hipStream_t st);
+hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
+                                const uint8_t *scales, int64_t nitems, float *block_mse,
+                                double *tensor_sse, hipStream_t st);
+#endif

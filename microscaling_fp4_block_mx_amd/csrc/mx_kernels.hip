@@ -1,0 +1,499 @@
+// mx_kernels.hip - gfx950 kernels for OCP MXFP4 block quantization.
+//
+// Work decomposition (all ops): the tensor is a flat run of 32-element MX
+// blocks (rows are contiguous and k % 32 == 0, so block b covers elements
+// 32b..32b+31 and owns scale byte b and code bytes 16b..16b+15). A block is
+// handled by a quad of 4 adjacent lanes; lane q of the quad owns elements
+// 8q..8q+7 ("item" = 8 elements = one 16-byte bf16 load, one 32-bit code
+// word). A wave64 covers 16 blocks per item step: 1 KiB of bf16 in, 256 B of
+// codes and 16 B of scales out, all contiguous.
+//
+// Cross-lane work inside a quad (block amax, block squared error) uses DPP
+// quad permutations, so quads must always be whole: every launch covers a
+// multiple of 4 items and the per-thread item stride is a multiple of 4.
+//
+// Element conversion uses the gfx950 scaled FP4 converts:
+//   v_cvt_scalef32_pk_fp4_{bf16,f32}: two values / 2^(s-127) -> two E2M1
+//     codes in one byte (first value in the low nibble), nearest with ties
+//     to the even code, saturating at +-6;
+//   v_cvt_scalef32_pk_{bf16,f32}_fp4: one byte of two codes -> two values
+//     E2M1 * 2^(s-127).
+// The scale operand is passed as the fp32 bit pattern s << 23, whose
+// exponent field is the E8M0 byte. These were checked against the CPU
+// oracle over every finite bf16 pair at scale bytes 0..252 (subnormal inputs
+// included) and over every code byte at every scale byte before adoption;
+// the one difference, the NaN produced for scale byte 255 (0xFFC00000
+// instead of the canonical 0x7FC00000), is corrected here.
+//
+// Format facts (E2M1 grid 0, .5, 1, 1.5, 2, 3, 4, 6; E8M0 scale 2^(s-127);
+// two codes per byte, even element low) are stated with their sources in
+// include/mx.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx_internal.h"
+
+namespace mxk {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+#ifndef MX_UNROLL
+#define MX_UNROLL 4
+#endif
+#ifndef MX_GRID_CAP
+#define MX_GRID_CAP 65536
+#endif
+constexpr int kThreads = 256;
+constexpr int kUnroll = MX_UNROLL;  // items per thread per grid-stride step
+constexpr uint32_t kNaN32 = 0x7FC00000u;
+constexpr uint32_t kNaN16x2 = 0x7FC07FC0u;
+
+// ---- cross-lane helpers (quad = 4 adjacent lanes) --------------------------
+
+// quad_perm [1,0,3,2] and [2,3,0,1]: exchange with lane^1 and lane^2.
+__device__ __forceinline__ uint32_t dpp_x1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_x2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = max(v, dpp_x1(v));
+  v = max(v, dpp_x2(v));
+  return v;
+}
+
+// (p0 + p1) + (p2 + p3) on every lane of the quad; fp32 addition commutes,
+// so all four lanes hold the same bits.
+__device__ __forceinline__ float quad_sum_f32(float p) {
+  p = p + __uint_as_float(dpp_x1(__float_as_uint(p)));
+  p = p + __uint_as_float(dpp_x2(__float_as_uint(p)));
+  return p;
+}
+
+__device__ __forceinline__ double dpp_x1_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = dpp_x1((uint32_t)u), hi = dpp_x1((uint32_t)(u >> 32));
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double dpp_x2_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = dpp_x2((uint32_t)u), hi = dpp_x2((uint32_t)(u >> 32));
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double quad_sum_f64(double p) {
+  p = p + dpp_x1_f64(p);
+  p = p + dpp_x2_f64(p);
+  return p;
+}
+
+// ---- items -----------------------------------------------------------------
+
+// Raw bits of one item: 8 elements. bf16 uses w[0..3] (two elements per
+// word, even element in the low half); fp32 uses w[0..7].
+template <bool BF16>
+struct Item {
+  uint32_t w[BF16 ? 4 : 8];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_item(const void *base, int64_t it, Item<BF16> &x) {
+  if constexpr (BF16) {
+    const u32x4 d = reinterpret_cast<const u32x4 *>(base)[it];
+#pragma unroll
+    for (int j = 0; j < 4; j++) x.w[j] = d[j];
+  } else {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(base) + 2 * it;
+    const u32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      x.w[j] = a[j];
+      x.w[4 + j] = b[j];
+    }
+  }
+}
+
+// Store the output words of one item (bf16: 4 words, fp32: 8 words).
+template <bool BF16>
+__device__ __forceinline__ void store_item(void *base, int64_t it,
+                                           const uint32_t (&y)[BF16 ? 4 : 8]) {
+  if constexpr (BF16) {
+    reinterpret_cast<u32x4 *>(base)[it] = u32x4{y[0], y[1], y[2], y[3]};
+  } else {
+    u32x4 *p = reinterpret_cast<u32x4 *>(base) + 2 * it;
+    p[0] = u32x4{y[0], y[1], y[2], y[3]};
+    p[1] = u32x4{y[4], y[5], y[6], y[7]};
+  }
+}
+
+// Element i of the item widened to fp32 (exact).
+template <bool BF16>
+__device__ __forceinline__ float elem(const Item<BF16> &x, int i) {
+  if constexpr (BF16) return __uint_as_float((i & 1) ? (x.w[i >> 1] & 0xFFFF0000u) : (x.w[i >> 1] << 16));
+  return __uint_as_float(x.w[i]);
+}
+
+// Largest |x| bit pattern of the item, in fp32 layout (bf16 widened).
+template <bool BF16>
+__device__ __forceinline__ uint32_t item_amax_bits(const Item<BF16> &x) {
+  if constexpr (BF16) {
+    u16x2 m = __builtin_bit_cast(u16x2, x.w[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int j = 1; j < 4; j++)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, x.w[j] & 0x7FFF7FFFu));
+    return (uint32_t)max(m.x, m.y) << 16;
+  } else {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) m = max(m, x.w[j] & 0x7FFFFFFFu);
+    return m;
+  }
+}
+
+// ---- the format --------------------------------------------------------------
+
+// E8M0 byte of the OCP rule from the block's largest |x| bit pattern:
+// floor(log2 amax) - 2 + 127 = exponent field - 2 (0 for zero/subnormal
+// amax), 255 for a NaN/Inf block.
+__device__ __forceinline__ uint32_t ocp_scale_byte(uint32_t amax_bits) {
+  if (amax_bits >= 0x7F800000u) return 255u;
+  const uint32_t e = amax_bits >> 23;
+  return e > 2u ? e - 2u : 0u;
+}
+
+// Scale operand of the converts for byte s.
+__device__ __forceinline__ float scale_operand(uint32_t s) { return __uint_as_float(s << 23); }
+
+// 8 codes of the item at scale byte s (finite block), packed in one word,
+// element i in nibble i.
+template <bool BF16>
+__device__ __forceinline__ uint32_t encode_item(const Item<BF16> &x, uint32_t s) {
+  const float sc = scale_operand(s);
+  uint32_t r = 0;
+  if constexpr (BF16) {
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x.w[0]), sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x.w[1]), sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x.w[2]), sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x.w[3]), sc, 3);
+  } else {
+    const float *f = reinterpret_cast<const float *>(x.w);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[0], f[1], sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[2], f[3], sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[4], f[5], sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, f[6], f[7], sc, 3);
+  }
+  return r;
+}
+
+// Codes of a NaN/Inf block: the sign bit alone.
+template <bool BF16>
+__device__ __forceinline__ uint32_t sign_codes(const Item<BF16> &x) {
+  uint32_t r = 0;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      r |= (((x.w[j] >> 12) & 0x8u) | ((x.w[j] >> 24) & 0x80u)) << (8 * j);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) r |= ((x.w[i] >> 31) << 3) << (4 * i);
+  }
+  return r;
+}
+
+// Decode the 8 codes of word c at byte s into output words: bf16 gives 4
+// words (two elements each), fp32 gives 8. Byte 255 gives canonical NaNs.
+template <bool BF16>
+__device__ __forceinline__ void decode_item(uint32_t c, uint32_t s, uint32_t (&y)[BF16 ? 4 : 8]) {
+  const float sc = scale_operand(s);
+  if constexpr (BF16) {
+    y[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0));
+    y[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1));
+    y[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2));
+    y[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3));
+    if (__builtin_expect(s == 255u, 0)) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) y[j] = kNaN16x2;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f32x2 v;
+      switch (j) {
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 3); break;
+      }
+      y[2 * j] = __float_as_uint(v.x);
+      y[2 * j + 1] = __float_as_uint(v.y);
+    }
+    if (__builtin_expect(s == 255u, 0)) {
+#pragma unroll
+      for (int j = 0; j < 8; j++) y[j] = kNaN32;
+    }
+  }
+}
+
+// The 8 decoded values of word c at byte s as fp32 (Inf/NaN passed through).
+__device__ __forceinline__ void decode_f32(uint32_t c, uint32_t s, float (&q)[8]) {
+  const float sc = scale_operand(s);
+  f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 0);
+  f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 1);
+  f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 2);
+  f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 3);
+  q[0] = v0.x; q[1] = v0.y; q[2] = v1.x; q[3] = v1.y;
+  q[4] = v2.x; q[5] = v2.y; q[6] = v3.x; q[7] = v3.y;
+}
+
+// Lane share of the pinned fp32 block squared error at scale byte c:
+// d = x - x_hat in fp32, even positions in one fma accumulator, odd in
+// another, lane share = even + odd. Returns the candidate's codes too.
+template <bool BF16>
+__device__ __forceinline__ float lane_sse(const Item<BF16> &x, uint32_t c, uint32_t &codes) {
+  codes = encode_item<BF16>(x, c);
+  float q[8];
+  decode_f32(codes, c, q);
+  float acc_e = 0.0f, acc_o = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const float d0 = elem<BF16>(x, i) - q[i];
+    const float d1 = elem<BF16>(x, i + 1) - q[i + 1];
+    acc_e = __builtin_fmaf(d0, d0, acc_e);
+    acc_o = __builtin_fmaf(d1, d1, acc_o);
+  }
+  return acc_e + acc_o;
+}
+
+// Block scale byte and this lane's 8 codes (all quad lanes agree on s).
+template <bool BF16, int MODE>
+__device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t &codes) {
+  const uint32_t s = ocp_scale_byte(quad_max_u32(item_amax_bits<BF16>(x)));
+  if (__builtin_expect(s == 255u, 0)) {
+    codes = sign_codes<BF16>(x);
+    return s;
+  }
+  if (MODE == MX_SCALE_OAS && s >= 1u) {
+    uint32_t c_ocp, c_low;
+    const float sse_ocp = quad_sum_f32(lane_sse<BF16>(x, s, c_ocp));
+    const float sse_low = quad_sum_f32(lane_sse<BF16>(x, s - 1u, c_low));
+    const bool low = sse_low < sse_ocp;  // strict: a tie keeps the OCP byte
+    codes = low ? c_low : c_ocp;
+    return low ? s - 1u : s;
+  }
+  codes = encode_item<BF16>(x, s);
+  return s;
+}
+
+// ---- kernels -----------------------------------------------------------------
+
+// Grid-stride over tiles of kThreads * kUnroll items; each thread's kUnroll
+// items are spaced kThreads apart so every load instruction is coalesced,
+// and all loads of a tile are issued before any is consumed. Full tiles run
+// without bounds checks; the one partial tile (if any) is handled by the
+// workgroup whose stride lands on it, with per-item checks.
+template <typename Load, typename Use>
+__device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
+  const int64_t tile = (int64_t)kThreads * kUnroll;
+  const int64_t nfull = nitems / tile;
+  int64_t t = blockIdx.x;
+  for (; t < nfull; t += gridDim.x) {
+    const int64_t base = t * tile + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) load(u, base + u * kThreads);
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) use(u, base + u * kThreads);
+  }
+  if (t == nfull && nfull * tile < nitems) {
+    const int64_t base = t * tile + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++)
+      if (base + u * kThreads < nitems) load(u, base + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++)  // whole quads drop out together
+      if (base + u * kThreads < nitems) use(u, base + u * kThreads);
+  }
+}
+
+template <bool BF16, int MODE>
+__global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ x,
+                                                       uint32_t *__restrict__ codes,
+                                                       uint8_t *__restrict__ scales,
+                                                       int64_t nitems) {
+  Item<BF16> xv[kUnroll];
+  tile_loop(
+      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t it) {
+        uint32_t c;
+        const uint32_t s = quantize_item<BF16, MODE>(xv[u], c);
+        codes[it] = c;
+        if ((threadIdx.x & 3) == 0) scales[it >> 2] = (uint8_t)s;
+      });
+}
+
+template <bool BF16, int MODE>
+__global__ __launch_bounds__(kThreads) void k_fakequant(const void *x, void *y, int64_t nitems) {
+  Item<BF16> xv[kUnroll];
+  tile_loop(
+      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t it) {
+        uint32_t c;
+        const uint32_t s = quantize_item<BF16, MODE>(xv[u], c);
+        uint32_t out[BF16 ? 4 : 8];
+        decode_item<BF16>(c, s, out);
+        store_item<BF16>(y, it, out);
+      });
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restrict__ codes,
+                                                         const uint8_t *__restrict__ scales,
+                                                         void *__restrict__ y, int64_t nitems) {
+  uint32_t cw[kUnroll], sb[kUnroll];
+  tile_loop(
+      nitems,
+      [&](int u, int64_t it) {
+        cw[u] = codes[it];
+        sb[u] = scales[it >> 2];
+      },
+      [&](int u, int64_t it) {
+        uint32_t out[BF16 ? 4 : 8];
+        decode_item<BF16>(cw[u], sb[u], out);
+        store_item<BF16>(y, it, out);
+      });
+}
+
+__global__ void k_zero_f64(double *p) { *p = 0.0; }
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__ x,
+                                                        const uint32_t *__restrict__ codes,
+                                                        const uint8_t *__restrict__ scales,
+                                                        float *__restrict__ block_mse,
+                                                        double *__restrict__ tensor_sse,
+                                                        int64_t nitems) {
+  __shared__ double wave_part[kThreads / 64];
+  double mine = 0.0;  // sum of the block SSEs this lane reports (q == 0 lanes)
+  Item<BF16> xv[kUnroll];
+  uint32_t cw[kUnroll], sb[kUnroll];
+  tile_loop(
+      nitems,
+      [&](int u, int64_t it) {
+        load_item<BF16>(x, it, xv[u]);
+        cw[u] = codes[it];
+        sb[u] = scales[it >> 2];
+      },
+      [&](int u, int64_t it) {
+        float q[8];
+        decode_f32(cw[u], sb[u], q);
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const double d = (double)elem<BF16>(xv[u], i) - (double)q[i];
+          acc = __builtin_fma(d, d, acc);
+        }
+        const double sse = quad_sum_f64(acc);
+        if ((threadIdx.x & 3) == 0) {
+          if (block_mse) block_mse[it >> 2] = (float)(sse * (1.0 / 32.0));
+          mine += sse;
+        }
+      });
+  if (tensor_sse) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mine += __shfl_xor(mine, off, 64);
+    if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = mine;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+      for (int w = 0; w < kThreads / 64; w++) t += wave_part[w];
+      atomicAdd(tensor_sse, t);
+    }
+  }
+}
+
+// ---- launchers -----------------------------------------------------------------
+
+static unsigned grid_for(int64_t nitems, int64_t cap) {
+  const int64_t tile = (int64_t)kThreads * kUnroll;
+  int64_t g = (nitems + tile - 1) / tile;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace mxk
+
+using namespace mxk;
+
+hipError_t mxi_launch_quantize(const void *x, int bf16, int mode, int64_t nitems,
+                               uint8_t *codes, uint8_t *scales, hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  uint32_t *c = reinterpret_cast<uint32_t *>(codes);
+  if (bf16) {
+    if (mode == MX_SCALE_OAS)
+      hipLaunchKernelGGL((k_quantize<true, MX_SCALE_OAS>), g, b, 0, st, x, c, scales, nitems);
+    else
+      hipLaunchKernelGGL((k_quantize<true, MX_SCALE_OCP>), g, b, 0, st, x, c, scales, nitems);
+  } else {
+    if (mode == MX_SCALE_OAS)
+      hipLaunchKernelGGL((k_quantize<false, MX_SCALE_OAS>), g, b, 0, st, x, c, scales, nitems);
+    else
+      hipLaunchKernelGGL((k_quantize<false, MX_SCALE_OCP>), g, b, 0, st, x, c, scales, nitems);
+  }
+  return hipGetLastError();
+}
+
+hipError_t mxi_launch_fakequant(const void *x, int bf16, int mode, int64_t nitems, void *y,
+                                hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  if (bf16) {
+    if (mode == MX_SCALE_OAS)
+      hipLaunchKernelGGL((k_fakequant<true, MX_SCALE_OAS>), g, b, 0, st, x, y, nitems);
+    else
+      hipLaunchKernelGGL((k_fakequant<true, MX_SCALE_OCP>), g, b, 0, st, x, y, nitems);
+  } else {
+    if (mode == MX_SCALE_OAS)
+      hipLaunchKernelGGL((k_fakequant<false, MX_SCALE_OAS>), g, b, 0, st, x, y, nitems);
+    else
+      hipLaunchKernelGGL((k_fakequant<false, MX_SCALE_OCP>), g, b, 0, st, x, y, nitems);
+  }
+  return hipGetLastError();
+}
+
+hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, int bf16,
+                                 int64_t nitems, void *y, hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
+  if (bf16)
+    hipLaunchKernelGGL((k_dequantize<true>), g, b, 0, st, c, scales, y, nitems);
+  else
+    hipLaunchKernelGGL((k_dequantize<false>), g, b, 0, st, c, scales, y, nitems);
+  return hipGetLastError();
+}
+
+#ifndef MX_MSE_GRID_CAP
+#define MX_MSE_GRID_CAP 65536
+#endif
+
+hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
+                                const uint8_t *scales, int64_t nitems, float *block_mse,
+                                double *tensor_sse, hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_MSE_GRID_CAP)), b(kThreads);
+  const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
+  if (tensor_sse) {
+    hipLaunchKernelGGL(k_zero_f64, dim3(1), dim3(1), 0, st, tensor_sse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (bf16)
+    hipLaunchKernelGGL((k_block_mse<true>), g, b, 0, st, x, c, scales, block_mse, tensor_sse,
+                       nitems);
+  else
+    hipLaunchKernelGGL((k_block_mse<false>), g, b, 0, st, x, c, scales, block_mse, tensor_sse,
+                       nitems);
+  return hipGetLastError();
+}

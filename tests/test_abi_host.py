@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+include/mx.h declares, and rejects bad arguments synchronously. Every call
+here fails validation before any HIP call, so no GPU is needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import microscaling_fp4_block_mx_amd as mx
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mx.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mx.LIB_PATH):
+        from microscaling_fp4_block_mx_amd import build
+        build.build()
+    return mx.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(mx_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(mx.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert mx.mx_status_string(s).startswith("MX_")
+    assert "unknown" in mx.mx_status_string(99)
+
+
+A = 1 << 20  # fake, 16-byte aligned addresses: validation fails before any use
+B = 2 << 30
+C = 3 << 30
+
+
+@pytest.mark.parametrize("rows,k", [(-1, 32), (1, 0), (1, -32), (4, 48), (2, 33),
+                                    (1 << 40, 1 << 30)])
+def test_bad_shapes(lib, rows, k):
+    assert mx.mx_quantize(A, mx.MX_BF16, rows, k, 0, B, C, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_dequantize(B, C, rows, k, mx.MX_F32, A, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_fakequant(A, mx.MX_F32, rows, k, 0, B, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_block_mse(A, mx.MX_F32, B, C, rows, k, A + (64 << 30), None, None) == \
+        mx.MX_ERR_SHAPE
+
+
+def test_bad_dtype_and_mode(lib):
+    assert mx.mx_quantize(A, 2, 1, 32, 0, B, C, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, 2, B, C, None) == mx.MX_ERR_MODE
+    assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, -1, B, C, None) == mx.MX_ERR_MODE
+    assert mx.mx_dequantize(B, C, 1, 32, 7, A, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_fakequant(A, -1, 1, 32, 0, B, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_fakequant(A, mx.MX_F32, 1, 32, 9, B, None) == mx.MX_ERR_MODE
+    assert mx.mx_block_mse(A, 5, B, C, 1, 32, None, A + 64, None) == mx.MX_ERR_DTYPE
+
+
+def test_null_pointers(lib):
+    assert mx.mx_quantize(None, mx.MX_BF16, 1, 32, 0, B, C, None) == mx.MX_ERR_NULL
+    assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, 0, None, C, None) == mx.MX_ERR_NULL
+    assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, 0, B, None, None) == mx.MX_ERR_NULL
+    assert mx.mx_dequantize(None, C, 1, 32, 0, A, None) == mx.MX_ERR_NULL
+    assert mx.mx_dequantize(B, C, 1, 32, 0, None, None) == mx.MX_ERR_NULL
+    assert mx.mx_fakequant(A, 0, 1, 32, 0, None, None) == mx.MX_ERR_NULL
+    # both error outputs NULL
+    assert mx.mx_block_mse(A, 0, B, C, 1, 32, None, None, None) == mx.MX_ERR_NULL
+    assert mx.mx_block_mse(None, 0, B, C, 1, 32, A + 64, None, None) == mx.MX_ERR_NULL
+
+
+def test_empty_is_ok_without_launch(lib):
+    assert mx.mx_quantize(None, mx.MX_BF16, 0, 32, 0, None, None, None) == mx.MX_OK
+    assert mx.mx_dequantize(None, None, 0, 4096, 0, None, None) == mx.MX_OK
+    assert mx.mx_fakequant(None, 1, 0, 64, 1, None, None) == mx.MX_OK
+    assert mx.mx_block_mse(None, 1, None, None, 0, 64, A, None, None) == mx.MX_OK
+
+
+def test_alignment(lib):
+    assert mx.mx_quantize(A + 2, mx.MX_BF16, 1, 32, 0, B, C, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, 0, B + 4, C, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, 0, B, C + 1, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_dequantize(B, C, 1, 32, 0, A + 8, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_fakequant(A, 0, 1, 32, 0, B + 8, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_block_mse(A, 0, B, C, 1, 32, A + (1 << 25) + 2, None, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_block_mse(A, 0, B, C, 1, 32, None, A + (1 << 25) + 4, None) == mx.MX_ERR_ALIGN
+
+
+def test_aliasing(lib):
+    # codes inside x
+    assert mx.mx_quantize(A, mx.MX_F32, 4, 64, 0, A + 64, C, None) == mx.MX_ERR_ALIAS
+    # scales inside codes
+    assert mx.mx_quantize(A, mx.MX_F32, 4, 64, 0, B, B + 16, None) == mx.MX_ERR_ALIAS
+    # dequant output over codes
+    assert mx.mx_dequantize(B, C, 4, 64, 0, B - 256, None) == mx.MX_ERR_ALIAS
+    # fake-quant: exact in-place is allowed (would launch, so not called
+    # here); a shifted overlap is rejected
+    assert mx.mx_fakequant(A, 0, 4, 64, 0, A + 16, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_block_mse(A, 0, B, C, 4, 64, A, None, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_block_mse(A, 0, B, C, 4, 64, None, ctypes.c_void_p(B + 64), None) == \
+        mx.MX_ERR_ALIAS
+
+
+def test_tensor_helpers_refuse_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mx.quantize(x)
+    with pytest.raises(ValueError):
+        mx.fakequant(x)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    import importlib
+    saved = mx._lib
+    try:
+        mx._lib = None
+        with pytest.raises(RuntimeError):
+            mx.load_library(str(tmp_path / "nope.so"))
+    finally:
+        mx._lib = saved
+        importlib.reload  # keep linters quiet
