@@ -35,6 +35,30 @@ BYTES_PER_ELEM = {
     "block_mse": 2 + 0.5 + 1 / 32 + 4 / 32,  # x, codes, scales in; fp32/block out
 }
 OPS = list(BYTES_PER_ELEM)
+KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0>", "quantize_oas": "k_quantize<true, 1>",
+             "dequantize_bf16": "k_dequantize<true>", "fakequant_ocp": "k_fakequant<true, 0>",
+             "block_mse": "k_block_mse<true>"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mx_bf16_8192x4096_hbm_traffic.md")
+KERNEL_SRC = os.path.join(ROOT, "microscaling_fp4_block_mx_amd", "csrc", "mx_kernels.hip")
+
+
+def measured_traffic(op):
+    """HBM bytes per launch of op's kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None if that summary was taken on a
+    different kernel source than the one built here."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+        h = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if ("source_sha256_prefix " + h) not in lines:
+        return None
+    key = "traffic_bytes " + KERNEL_OF[op] + " "
+    for ln in lines:
+        if ln.startswith(key):
+            return int(ln.split()[-1])
+    return None
 
 
 def parse():
@@ -90,6 +114,8 @@ def main():
         ))
     del x0
     sse = torch.empty((), dtype=torch.float64, device=dev)
+    ws_bytes = mx.mx_block_mse_workspace_size(R_, K_)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
@@ -109,38 +135,62 @@ def main():
         else:
             st = mx.mx_block_mse(b["x"].data_ptr(), mx.MX_BF16, b["c_ocp"].data_ptr(),
                                  b["s_ocp"].data_ptr(), R_, K_, b["bm"].data_ptr(),
-                                 sse.data_ptr(), sh)
+                                 sse.data_ptr(), ws.data_ptr(), ws_bytes, sh)
         if st != mx.MX_OK:
             raise RuntimeError(mx.mx_status_string(st))
 
+    def step(i):
+        b = sets[i % n_sets]
+        for op in OPS:
+            run(op, b)
+
     # warmup (also produces the codes each set's dequantize / block_mse read)
     for i in range(max(args.warmup, n_sets)):
-        for op in OPS:
-            run(op, sets[i % n_sets])
+        step(i)
     torch.cuda.synchronize()
 
-    # timed region: events on the launch stream between consecutive ops
+    # timed region: K whole steps between two events on the launch stream
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(OPS) + 1)] for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(K):
-        b = sets[i % n_sets]
-        ev[i][0].record(stream)
-        for j, op in enumerate(OPS):
-            run(op, b)
-            ev[i][j + 1].record(stream)
+        step(i)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / K
 
-    op_ms = {op: 0.0 for op in OPS}
-    step_ms = 0.0
-    for i in range(K):
-        for j, op in enumerate(OPS):
-            op_ms[op] += ev[i][j].elapsed_time(ev[i][j + 1])
-        step_ms += ev[i][0].elapsed_time(ev[i][-1])
-    op_ms = {op: t / K for op, t in op_ms.items()}
-    ms_per_step = step_ms / K
+    # per-kernel launch time: each op alone, back to back over the rotating
+    # sets, K * n_sets launches between two events on the same stream
+    op_ms = {}
+    for op in OPS:
+        for i in range(n_sets):
+            run(op, sets[i])
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m = max(K, 2 * n_sets)
+        a0.record(stream)
+        for i in range(m):
+            run(op, sets[i % n_sets])
+        a1.record(stream)
+        torch.cuda.synchronize()
+        op_ms[op] = a0.elapsed_time(a1) / m
+
+    # reference: a plain device copy of the same bf16 tensor (read n*2 bytes,
+    # write n*2 bytes) timed the same way; it is also the calibration kernel
+    # for the HBM traffic counters
+    for i in range(n_sets):
+        sets[i]["y_fq"].copy_(sets[i]["x"])
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m = max(K, 2 * n_sets)
+    c0.record(stream)
+    for i in range(m):
+        sets[i % n_sets]["y_fq"].copy_(sets[i % n_sets]["x"])
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_us = c0.elapsed_time(c1) * 1e3 / m
+
     bytes_op = {op: BYTES_PER_ELEM[op] * n for op in OPS}
     bytes_step = sum(bytes_op.values())
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
@@ -155,7 +205,7 @@ def main():
     dom_gbs = bytes_op[dom] / (op_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(dom),
                 "bytes_per_launch": int(bytes_op[dom]),
                 "avg_launch_us": round(op_ms[dom] * 1e3, 2)}
 
@@ -173,7 +223,9 @@ def main():
                    "elements_per_s": round(n / (ms_per_step * 1e-3), 1),
                    "rotation_sets": n_sets,
                    "working_set_gib": round(n_sets * per_set / 2 ** 30, 2),
-                   "wall_s_timed": round(wall, 4)},
+                   "wall_s_timed": round(wall, 4),
+                   "device_copy_reference": {"bytes": 4 * n, "us": round(copy_us, 2),
+                                             "GB/s": round(4 * n / copy_us / 1e3, 1)}},
         "breakdown": breakdown,
         "roofline": roofline,
         "cpu_baseline": cpu,

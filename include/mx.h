@@ -22,14 +22,16 @@
  *
  * Conventions shared by every entry point:
  *   - All data pointers are DEVICE pointers, allocated and owned by the
- *     caller; the library allocates no device memory and keeps no state
- *     between calls. It is safe to call from several host threads.
+ *     caller (scratch too: mx_block_mse takes a workspace argument); the
+ *     library allocates no device memory and keeps no state between calls.
+ *     It is safe to call from several host threads.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *     Arguments are validated synchronously on the host; on MX_OK the work
  *     has been enqueued on `stream` and completes asynchronously. A device
  *     fault surfaces at the caller's next synchronization.
- *   - rows == 0 returns MX_OK without launching anything (pointers may then
- *     be NULL).
+ *   - rows == 0 returns MX_OK without reading or writing any tensor
+ *     (pointers may then be NULL); only mx_block_mse still enqueues the
+ *     write of 0 to tensor_sse.
  *   - x, y, codes and scales must be 16-byte aligned (MX_ERR_ALIGN).
  *   - Outputs must not overlap inputs, except that mx_fakequant accepts
  *     y == x exactly (in place). Partial overlap is MX_ERR_ALIAS.
@@ -38,6 +40,7 @@
 #ifndef MX_H
 #define MX_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -52,7 +55,8 @@ typedef enum {
   MX_ERR_MODE = 4,   /* mode is not a mx_scale_mode_t value                  */
   MX_ERR_ALIGN = 5,  /* a data pointer is not 16-byte aligned                */
   MX_ERR_HIP = 6,    /* the HIP launch failed; see mx_last_error_detail()    */
-  MX_ERR_ALIAS = 7   /* an output partially overlaps an input                */
+  MX_ERR_ALIAS = 7,  /* an output partially overlaps an input                */
+  MX_ERR_WORKSPACE = 8 /* workspace NULL, misaligned or below the size needed  */
 } mx_status_t;
 
 typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype_t;
@@ -109,14 +113,24 @@ mx_status_t mx_fakequant(const void *x, mx_dtype_t dtype, int64_t rows,
  * tensor_sse (one device double, overwritten) receives the sum of all block
  * SSEs in fp64; the tensor MSE is tensor_sse / (rows * k). Either output may
  * be NULL (both NULL is MX_ERR_NULL). block_mse must be 4-byte aligned and
- * tensor_sse 8-byte aligned. The block values are deterministic; the tensor
- * sum's rounding may differ between runs (fp64 atomics).
+ * tensor_sse 8-byte aligned. Both outputs are deterministic: the tensor sum
+ * is taken in a fixed order (per-workgroup partial sums, then one ordered
+ * reduction), never with atomics.
+ * workspace: device scratch for those partial sums, needed only when
+ * tensor_sse != NULL; at least mx_block_mse_workspace_size(rows, k) bytes,
+ * 8-byte aligned, not overlapping any argument. Its contents on entry do not
+ * matter; calls that share a workspace must be ordered (same stream).
  * Source: MXFP4 wiki page, example 2 (MSE as the quantization error);
  * "Unveiling..." section 2.B (block SSE as the objective). */
 mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype,
                          const uint8_t *codes, const uint8_t *scales,
                          int64_t rows, int64_t k, float *block_mse,
-                         double *tensor_sse, void *stream);
+                         double *tensor_sse, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace mx_block_mse needs for a [rows, k] tensor when it is
+ * asked for tensor_sse (at most 16 KiB); 0 for an invalid shape. */
+size_t mx_block_mse_workspace_size(int64_t rows, int64_t k);
 
 /* Static, human-readable name of a status code. */
 const char *mx_status_string(mx_status_t s);

@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmx.so")
 
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_DTYPE, MX_ERR_MODE, MX_ERR_ALIGN, MX_ERR_HIP, \
-    MX_ERR_ALIAS = range(8)
+    MX_ERR_ALIAS, MX_ERR_WORKSPACE = range(9)
 MX_F32, MX_BF16 = 0, 1
 MX_SCALE_OCP, MX_SCALE_OAS = 0, 1
 BLOCK = 32
@@ -34,7 +34,7 @@ BLOCK = 32
 _MODES = {"ocp": MX_SCALE_OCP, "oas": MX_SCALE_OAS}
 _DTYPES = {torch.float32: MX_F32, torch.bfloat16: MX_BF16}
 EXPORTS = ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
-           "mx_status_string", "mx_last_error_detail")
+           "mx_block_mse_workspace_size", "mx_status_string", "mx_last_error_detail")
 
 _lib = None
 
@@ -52,7 +52,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mx_quantize.argtypes = [p, i32, i64, i64, i32, p, p, p]
     lib.mx_dequantize.argtypes = [p, p, i64, i64, i32, p, p]
     lib.mx_fakequant.argtypes = [p, i32, i64, i64, i32, p, p]
-    lib.mx_block_mse.argtypes = [p, i32, p, p, i64, i64, p, p, p]
+    lib.mx_block_mse.argtypes = [p, i32, p, p, i64, i64, p, p, p, ctypes.c_size_t, p]
+    lib.mx_block_mse_workspace_size.argtypes = [i64, i64]
+    lib.mx_block_mse_workspace_size.restype = ctypes.c_size_t
     for f in ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse"):
         getattr(lib, f).restype = i32
     lib.mx_status_string.argtypes = [i32]
@@ -77,9 +79,14 @@ def mx_fakequant(x, dtype, rows, k, mode, y, stream) -> int:
     return load_library().mx_fakequant(x, dtype, rows, k, mode, y, stream)
 
 
-def mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse, tensor_sse, stream) -> int:
+def mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse, tensor_sse, workspace,
+                 workspace_bytes, stream) -> int:
     return load_library().mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse,
-                                       tensor_sse, stream)
+                                       tensor_sse, workspace, workspace_bytes, stream)
+
+
+def mx_block_mse_workspace_size(rows, k) -> int:
+    return load_library().mx_block_mse_workspace_size(rows, k)
 
 
 def mx_status_string(status: int) -> str:
@@ -186,8 +193,10 @@ def block_mse(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
         bm = torch.empty(tuple(x.shape[:-1]) + (k // BLOCK,), dtype=torch.float32,
                          device=x.device)
     sse = torch.empty((), dtype=torch.float64, device=x.device)
+    ws_bytes = mx_block_mse_workspace_size(rows, k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):
         _raise(mx_block_mse(x.data_ptr(), _DTYPES[x.dtype], codes.data_ptr(), scales.data_ptr(),
                             rows, k, bm.data_ptr() if bm is not None else None,
-                            sse.data_ptr(), _stream(x.device)))
+                            sse.data_ptr(), ws.data_ptr(), ws_bytes, _stream(x.device)))
     return bm, sse

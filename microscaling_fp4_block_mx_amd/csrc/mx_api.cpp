@@ -90,37 +90,54 @@ mx_status_t mx_fakequant(const void *x, mx_dtype_t dtype, int64_t rows, int64_t 
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t mx_block_mse_workspace_size(int64_t rows, int64_t k) {
+  if (check_shape(rows, k) != MX_OK) return 0;
+  const size_t n = mxi_block_mse_partials(rows * k / 8);
+  return (n > 0 ? n : 1) * sizeof(double);
+}
+
 mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype, const uint8_t *codes,
                          const uint8_t *scales, int64_t rows, int64_t k, float *block_mse,
-                         double *tensor_sse, void *stream) {
+                         double *tensor_sse, void *workspace, size_t workspace_bytes,
+                         void *stream) {
   if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;
   if (mx_status_t s = check_shape(rows, k)) return s;
   if (!block_mse && !tensor_sse) return MX_ERR_NULL;
+  if (tensor_sse) {
+    if ((reinterpret_cast<uintptr_t>(tensor_sse) & 7u) != 0) return MX_ERR_ALIGN;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0 ||
+        workspace_bytes < mx_block_mse_workspace_size(rows, k))
+      return MX_ERR_WORKSPACE;
+    if (overlap(tensor_sse, 8, workspace, (int64_t)workspace_bytes)) return MX_ERR_ALIAS;
+  }
   if (rows == 0) {
     // an empty tensor has zero error; still a device write, so it is enqueued
-    if (tensor_sse) {
-      if ((reinterpret_cast<uintptr_t>(tensor_sse) & 7u) != 0) return MX_ERR_ALIGN;
-      return finish(mxi_launch_block_mse(nullptr, 0, nullptr, nullptr, 0, nullptr, tensor_sse,
-                                         static_cast<hipStream_t>(stream)));
-    }
-    return MX_OK;
+    if (!tensor_sse) return MX_OK;
+    return finish(mxi_launch_block_mse(nullptr, 0, nullptr, nullptr, 0, nullptr, tensor_sse,
+                                       static_cast<double *>(workspace),
+                                       static_cast<hipStream_t>(stream)));
   }
   if (!x || !codes || !scales) return MX_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGN;
   if (block_mse && (reinterpret_cast<uintptr_t>(block_mse) & 3u) != 0) return MX_ERR_ALIGN;
-  if (tensor_sse && (reinterpret_cast<uintptr_t>(tensor_sse) & 7u) != 0) return MX_ERR_ALIGN;
   const int64_t n = rows * k;
   const int64_t nx = n * elem_bytes(x_dtype);
-  if (block_mse && (overlap(block_mse, 4 * (n / kBlock), x, nx) ||
-                    overlap(block_mse, 4 * (n / kBlock), codes, n / 2) ||
-                    overlap(block_mse, 4 * (n / kBlock), scales, n / kBlock)))
+  const int64_t nbm = 4 * (n / kBlock);
+  if (block_mse && (overlap(block_mse, nbm, x, nx) || overlap(block_mse, nbm, codes, n / 2) ||
+                    overlap(block_mse, nbm, scales, n / kBlock)))
     return MX_ERR_ALIAS;
-  if (tensor_sse && (overlap(tensor_sse, 8, x, nx) || overlap(tensor_sse, 8, codes, n / 2) ||
-                     overlap(tensor_sse, 8, scales, n / kBlock) ||
-                     (block_mse && overlap(tensor_sse, 8, block_mse, 4 * (n / kBlock)))))
-    return MX_ERR_ALIAS;
+  if (tensor_sse) {
+    const int64_t nw = (int64_t)workspace_bytes;
+    if (overlap(tensor_sse, 8, x, nx) || overlap(tensor_sse, 8, codes, n / 2) ||
+        overlap(tensor_sse, 8, scales, n / kBlock) ||
+        (block_mse && overlap(tensor_sse, 8, block_mse, nbm)) || overlap(workspace, nw, x, nx) ||
+        overlap(workspace, nw, codes, n / 2) || overlap(workspace, nw, scales, n / kBlock) ||
+        (block_mse && overlap(workspace, nw, block_mse, nbm)))
+      return MX_ERR_ALIAS;
+  }
   return finish(mxi_launch_block_mse(x, x_dtype == MX_BF16, codes, scales, n / 8, block_mse,
-                                     tensor_sse, static_cast<hipStream_t>(stream)));
+                                     tensor_sse, static_cast<double *>(workspace),
+                                     static_cast<hipStream_t>(stream)));
 }
 
 const char *mx_status_string(mx_status_t s) {
@@ -133,6 +150,7 @@ const char *mx_status_string(mx_status_t s) {
     case MX_ERR_ALIGN: return "MX_ERR_ALIGN: data pointers must be 16-byte aligned";
     case MX_ERR_HIP: return "MX_ERR_HIP: HIP launch failed";
     case MX_ERR_ALIAS: return "MX_ERR_ALIAS: an output overlaps an input";
+    case MX_ERR_WORKSPACE: return "MX_ERR_WORKSPACE: workspace missing, misaligned or too small";
   }
   return "unknown mx_status_t";
 }

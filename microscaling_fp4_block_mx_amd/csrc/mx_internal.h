@@ -14,7 +14,9 @@ hipError_t mxi_launch_fakequant(const void *x, int bf16, int mode, int64_t nitem
                                 hipStream_t st);
 hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, int bf16,
                                  int64_t nitems, void *y, hipStream_t st);
+// Number of fp64 partial sums the block-error launch writes for nitems.
+size_t mxi_block_mse_partials(int64_t nitems);
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                                 const uint8_t *scales, int64_t nitems, float *block_mse,
-                                double *tensor_sse, hipStream_t st);
+                                double *tensor_sse, double *partial, hipStream_t st);
 #endif

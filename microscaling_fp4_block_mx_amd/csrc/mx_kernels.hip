@@ -91,6 +91,26 @@ __device__ __forceinline__ double quad_sum_f64(double p) {
   return p;
 }
 
+// ---- memory helpers -----------------------------------------------------------
+
+// Streaming accesses. Each bf16 item is one 16-byte access and a wave's 64
+// accesses cover 1 KiB contiguously, so bf16 tensors are read and written
+// with the non-temporal hint (no reuse; fewer dirty L2 lines to write back
+// at the end of the kernel). fp32 items take two 16-byte accesses whose
+// per-instruction footprint is strided (32-byte lane pitch): those, and the
+// small code/scale accesses, stay on the default cache policy, which
+// measured faster for them.
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void st(T *p, T v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // ---- items -----------------------------------------------------------------
 
 // Raw bits of one item: 8 elements. bf16 uses w[0..3] (two elements per
@@ -103,12 +123,12 @@ struct Item {
 template <bool BF16>
 __device__ __forceinline__ void load_item(const void *base, int64_t it, Item<BF16> &x) {
   if constexpr (BF16) {
-    const u32x4 d = reinterpret_cast<const u32x4 *>(base)[it];
+    const u32x4 d = ld<true>(reinterpret_cast<const u32x4 *>(base) + it);
 #pragma unroll
     for (int j = 0; j < 4; j++) x.w[j] = d[j];
   } else {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(base) + 2 * it;
-    const u32x4 a = p[0], b = p[1];
+    const u32x4 a = ld<false>(p), b = ld<false>(p + 1);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       x.w[j] = a[j];
@@ -122,11 +142,11 @@ template <bool BF16>
 __device__ __forceinline__ void store_item(void *base, int64_t it,
                                            const uint32_t (&y)[BF16 ? 4 : 8]) {
   if constexpr (BF16) {
-    reinterpret_cast<u32x4 *>(base)[it] = u32x4{y[0], y[1], y[2], y[3]};
+    st<true>(reinterpret_cast<u32x4 *>(base) + it, u32x4{y[0], y[1], y[2], y[3]});
   } else {
     u32x4 *p = reinterpret_cast<u32x4 *>(base) + 2 * it;
-    p[0] = u32x4{y[0], y[1], y[2], y[3]};
-    p[1] = u32x4{y[4], y[5], y[6], y[7]};
+    st<false>(p, u32x4{y[0], y[1], y[2], y[3]});
+    st<false>(p + 1, u32x4{y[4], y[5], y[6], y[7]});
   }
 }
 
@@ -330,8 +350,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ 
       [&](int u, int64_t it) {
         uint32_t c;
         const uint32_t s = quantize_item<BF16, MODE>(xv[u], c);
-        codes[it] = c;
-        if ((threadIdx.x & 3) == 0) scales[it >> 2] = (uint8_t)s;
+        st<false>(codes + it, c);
+        if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)s);
       });
 }
 
@@ -357,8 +377,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restr
   tile_loop(
       nitems,
       [&](int u, int64_t it) {
-        cw[u] = codes[it];
-        sb[u] = scales[it >> 2];
+        cw[u] = ld<false>(codes + it);
+        sb[u] = ld<false>(scales + (it >> 2));
       },
       [&](int u, int64_t it) {
         uint32_t out[BF16 ? 4 : 8];
@@ -367,14 +387,17 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restr
       });
 }
 
-__global__ void k_zero_f64(double *p) { *p = 0.0; }
-
+// Block error. Per block: SSE = sum (x - x_hat)^2 in fp64 (quad sum in a
+// fixed order), block_mse = (float)(SSE / 32). The tensor sum is taken in two
+// stages with fixed order and no atomics: each workgroup writes the sum of
+// its blocks' SSEs to partial[blockIdx.x] (lane sums, then a butterfly over
+// the wave, then the waves in order), and k_sum_partials adds the partials.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__ x,
                                                         const uint32_t *__restrict__ codes,
                                                         const uint8_t *__restrict__ scales,
                                                         float *__restrict__ block_mse,
-                                                        double *__restrict__ tensor_sse,
+                                                        double *__restrict__ partial,
                                                         int64_t nitems) {
   __shared__ double wave_part[kThreads / 64];
   double mine = 0.0;  // sum of the block SSEs this lane reports (q == 0 lanes)
@@ -384,8 +407,8 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
       nitems,
       [&](int u, int64_t it) {
         load_item<BF16>(x, it, xv[u]);
-        cw[u] = codes[it];
-        sb[u] = scales[it >> 2];
+        cw[u] = ld<false>(codes + it);
+        sb[u] = ld<false>(scales + (it >> 2));
       },
       [&](int u, int64_t it) {
         float q[8];
@@ -398,11 +421,11 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
         }
         const double sse = quad_sum_f64(acc);
         if ((threadIdx.x & 3) == 0) {
-          if (block_mse) block_mse[it >> 2] = (float)(sse * (1.0 / 32.0));
+          if (block_mse) st<false>(block_mse + (it >> 2), (float)(sse * (1.0 / 32.0)));
           mine += sse;
         }
       });
-  if (tensor_sse) {
+  if (partial) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mine += __shfl_xor(mine, off, 64);
     if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = mine;
@@ -410,9 +433,25 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
     if (threadIdx.x == 0) {
       double t = 0.0;
       for (int w = 0; w < kThreads / 64; w++) t += wave_part[w];
-      atomicAdd(tensor_sse, t);
+      partial[blockIdx.x] = t;
     }
   }
+}
+
+// One workgroup: out = sum of partial[0..n) (strided per thread, then a
+// fixed tree over the workgroup). n == 0 writes 0.
+__global__ __launch_bounds__(kThreads) void k_sum_partials(const double *__restrict__ partial,
+                                                           int n, double *__restrict__ out) {
+  __shared__ double part[kThreads];
+  double t = 0.0;
+  for (int i = threadIdx.x; i < n; i += kThreads) t += partial[i];
+  part[threadIdx.x] = t;
+  __syncthreads();
+  for (int w = kThreads / 2; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = part[0];
 }
 
 // ---- launchers -----------------------------------------------------------------
@@ -476,24 +515,31 @@ hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, in
 }
 
 #ifndef MX_MSE_GRID_CAP
-#define MX_MSE_GRID_CAP 65536
+#define MX_MSE_GRID_CAP 2048
 #endif
+
+size_t mxi_block_mse_partials(int64_t nitems) { return grid_for(nitems, MX_MSE_GRID_CAP); }
 
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                                 const uint8_t *scales, int64_t nitems, float *block_mse,
-                                double *tensor_sse, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_MSE_GRID_CAP)), b(kThreads);
+                                double *tensor_sse, double *partial, hipStream_t st) {
+  const unsigned grid = grid_for(nitems, MX_MSE_GRID_CAP);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
-  if (tensor_sse) {
-    hipLaunchKernelGGL(k_zero_f64, dim3(1), dim3(1), 0, st, tensor_sse);
+  double *part = tensor_sse ? partial : nullptr;
+  if (nitems > 0) {
+    if (bf16)
+      hipLaunchKernelGGL((k_block_mse<true>), dim3(grid), dim3(kThreads), 0, st, x, c, scales,
+                         block_mse, part, nitems);
+    else
+      hipLaunchKernelGGL((k_block_mse<false>), dim3(grid), dim3(kThreads), 0, st, x, c, scales,
+                         block_mse, part, nitems);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (bf16)
-    hipLaunchKernelGGL((k_block_mse<true>), g, b, 0, st, x, c, scales, block_mse, tensor_sse,
-                       nitems);
-  else
-    hipLaunchKernelGGL((k_block_mse<false>), g, b, 0, st, x, c, scales, block_mse, tensor_sse,
-                       nitems);
-  return hipGetLastError();
+  if (tensor_sse) {
+    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kThreads), 0, st, partial,
+                       nitems > 0 ? (int)grid : 0, tensor_sse);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }

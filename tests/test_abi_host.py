@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert mx.mx_status_string(s).startswith("MX_")
     assert "unknown" in mx.mx_status_string(99)
 
@@ -44,6 +44,7 @@ def test_status_strings(lib):
 A = 1 << 20  # fake, 16-byte aligned addresses: validation fails before any use
 B = 2 << 30
 C = 3 << 30
+W = 5 << 30  # fake workspace / tensor_sse region
 
 
 @pytest.mark.parametrize("rows,k", [(-1, 32), (1, 0), (1, -32), (4, 48), (2, 33),
@@ -52,8 +53,9 @@ def test_bad_shapes(lib, rows, k):
     assert mx.mx_quantize(A, mx.MX_BF16, rows, k, 0, B, C, None) == mx.MX_ERR_SHAPE
     assert mx.mx_dequantize(B, C, rows, k, mx.MX_F32, A, None) == mx.MX_ERR_SHAPE
     assert mx.mx_fakequant(A, mx.MX_F32, rows, k, 0, B, None) == mx.MX_ERR_SHAPE
-    assert mx.mx_block_mse(A, mx.MX_F32, B, C, rows, k, A + (64 << 30), None, None) == \
-        mx.MX_ERR_SHAPE
+    assert mx.mx_block_mse(A, mx.MX_F32, B, C, rows, k, A + (64 << 30), None, None, 0,
+                           None) == mx.MX_ERR_SHAPE
+    assert mx.mx_block_mse_workspace_size(rows, k) == 0
 
 
 def test_bad_dtype_and_mode(lib):
@@ -63,7 +65,7 @@ def test_bad_dtype_and_mode(lib):
     assert mx.mx_dequantize(B, C, 1, 32, 7, A, None) == mx.MX_ERR_DTYPE
     assert mx.mx_fakequant(A, -1, 1, 32, 0, B, None) == mx.MX_ERR_DTYPE
     assert mx.mx_fakequant(A, mx.MX_F32, 1, 32, 9, B, None) == mx.MX_ERR_MODE
-    assert mx.mx_block_mse(A, 5, B, C, 1, 32, None, A + 64, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_block_mse(A, 5, B, C, 1, 32, None, A + 64, W, 64, None) == mx.MX_ERR_DTYPE
 
 
 def test_null_pointers(lib):
@@ -74,15 +76,15 @@ def test_null_pointers(lib):
     assert mx.mx_dequantize(B, C, 1, 32, 0, None, None) == mx.MX_ERR_NULL
     assert mx.mx_fakequant(A, 0, 1, 32, 0, None, None) == mx.MX_ERR_NULL
     # both error outputs NULL
-    assert mx.mx_block_mse(A, 0, B, C, 1, 32, None, None, None) == mx.MX_ERR_NULL
-    assert mx.mx_block_mse(None, 0, B, C, 1, 32, A + 64, None, None) == mx.MX_ERR_NULL
+    assert mx.mx_block_mse(A, 0, B, C, 1, 32, None, None, W, 64, None) == mx.MX_ERR_NULL
+    assert mx.mx_block_mse(None, 0, B, C, 1, 32, A + 64, None, None, 0, None) == mx.MX_ERR_NULL
 
 
 def test_empty_is_ok_without_launch(lib):
     assert mx.mx_quantize(None, mx.MX_BF16, 0, 32, 0, None, None, None) == mx.MX_OK
     assert mx.mx_dequantize(None, None, 0, 4096, 0, None, None) == mx.MX_OK
     assert mx.mx_fakequant(None, 1, 0, 64, 1, None, None) == mx.MX_OK
-    assert mx.mx_block_mse(None, 1, None, None, 0, 64, A, None, None) == mx.MX_OK
+    assert mx.mx_block_mse(None, 1, None, None, 0, 64, A, None, None, 0, None) == mx.MX_OK
 
 
 def test_alignment(lib):
@@ -91,8 +93,10 @@ def test_alignment(lib):
     assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, 0, B, C + 1, None) == mx.MX_ERR_ALIGN
     assert mx.mx_dequantize(B, C, 1, 32, 0, A + 8, None) == mx.MX_ERR_ALIGN
     assert mx.mx_fakequant(A, 0, 1, 32, 0, B + 8, None) == mx.MX_ERR_ALIGN
-    assert mx.mx_block_mse(A, 0, B, C, 1, 32, A + (1 << 25) + 2, None, None) == mx.MX_ERR_ALIGN
-    assert mx.mx_block_mse(A, 0, B, C, 1, 32, None, A + (1 << 25) + 4, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_block_mse(A, 0, B, C, 1, 32, A + (1 << 25) + 2, None, None, 0, None) == \
+        mx.MX_ERR_ALIGN
+    assert mx.mx_block_mse(A, 0, B, C, 1, 32, None, A + (1 << 25) + 4, W, 64, None) == \
+        mx.MX_ERR_ALIGN
 
 
 def test_aliasing(lib):
@@ -105,9 +109,25 @@ def test_aliasing(lib):
     # fake-quant: exact in-place is allowed (would launch, so not called
     # here); a shifted overlap is rejected
     assert mx.mx_fakequant(A, 0, 4, 64, 0, A + 16, None) == mx.MX_ERR_ALIAS
-    assert mx.mx_block_mse(A, 0, B, C, 4, 64, A, None, None) == mx.MX_ERR_ALIAS
-    assert mx.mx_block_mse(A, 0, B, C, 4, 64, None, ctypes.c_void_p(B + 64), None) == \
+    assert mx.mx_block_mse(A, 0, B, C, 4, 64, A, None, None, 0, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_block_mse(A, 0, B, C, 4, 64, None, ctypes.c_void_p(B + 64), W, 64, None) == \
         mx.MX_ERR_ALIAS
+    # workspace over the input
+    assert mx.mx_block_mse(A, 0, B, C, 4, 64, None, W, A + 32, 64, None) == mx.MX_ERR_ALIAS
+    # tensor_sse inside the workspace
+    assert mx.mx_block_mse(A, 0, B, C, 4, 64, None, W + 8, W, 64, None) == mx.MX_ERR_ALIAS
+
+
+def test_workspace(lib):
+    need = mx.mx_block_mse_workspace_size(8192, 4096)
+    assert 8 <= need <= 16384 and need % 8 == 0
+    assert mx.mx_block_mse_workspace_size(0, 64) >= 8
+    # missing / small / misaligned workspace when the tensor sum is asked for
+    assert mx.mx_block_mse(A, 1, B, C, 8192, 4096, None, W, None, 0, None) == mx.MX_ERR_WORKSPACE
+    assert mx.mx_block_mse(A, 1, B, C, 8192, 4096, None, W, W + 64, need - 8, None) == \
+        mx.MX_ERR_WORKSPACE
+    assert mx.mx_block_mse(A, 1, B, C, 8192, 4096, None, W, W + 68, need, None) == \
+        mx.MX_ERR_WORKSPACE
 
 
 def test_tensor_helpers_refuse_cpu_tensors(lib):
@@ -120,7 +140,6 @@ def test_tensor_helpers_refuse_cpu_tensors(lib):
 
 
 def test_missing_library_fails_loudly(tmp_path):
-    import importlib
     saved = mx._lib
     try:
         mx._lib = None
@@ -128,4 +147,3 @@ def test_missing_library_fails_loudly(tmp_path):
             mx.load_library(str(tmp_path / "nope.so"))
     finally:
         mx._lib = saved
-        importlib.reload  # keep linters quiet
