@@ -28,8 +28,9 @@ _SRC = os.path.join(_HERE, "mxref.c")
 _LIB = os.path.join(_HERE, "libmxref.so")
 
 F32, BF16 = 0, 1
-OCP, OAS = 0, 1
-_MODES = {"ocp": OCP, "oas": OAS}
+OCP, OAS, OAS_BITS, OAS_NF = 0, 1, 2, 3
+_MODES = {"ocp": OCP, "oas": OAS, "oas_bits": OAS_BITS, "oas_nf": OAS_NF}
+MODES = tuple(_MODES)
 
 _lib = None
 
@@ -138,18 +139,26 @@ def fakequant(x: np.ndarray, mode: str = "ocp", threads: int = 1) -> np.ndarray:
 
 
 def block_mse(x: np.ndarray, codes: np.ndarray, scales: np.ndarray,
-              threads: int = 1):
-    """Return (block_mse float32 [..., k/32], tensor_sse float)."""
+              threads: int = 1, with_energy: bool = False):
+    """Return (block_mse float32 [..., k/32], tensor_sse float), or with
+    with_energy=True (block_mse, tensor_sse, sum of x^2)."""
     x = np.ascontiguousarray(x)
     rows, k = _shape2(x)
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     bm = np.empty(x.shape[:-1] + (k // 32,), np.float32)
-    sse = ctypes.c_double(0.0)
+    sums = np.zeros(2, np.float64)
     _check(_load().mxref_block_mse(_ptr(x), _dtype_code(x), _ptr(codes), _ptr(scales),
-                                   rows, k, _ptr(bm), ctypes.cast(ctypes.pointer(sse), ctypes.c_void_p),
-                                   threads))
-    return bm, float(sse.value)
+                                   rows, k, _ptr(bm), _ptr(sums), threads))
+    if with_energy:
+        return bm, float(sums[0]), float(sums[1])
+    return bm, float(sums[0])
+
+
+def qsnr_db(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, threads: int = 1) -> float:
+    """10 log10(sum x^2 / sum (x - x_hat)^2) of the whole tensor."""
+    _, sse, ssq = block_mse(x, codes, scales, threads, with_energy=True)
+    return float(10.0 * np.log10(ssq / sse))
 
 
 # --- single-element helpers (used by the oracle's own pins) -----------------

@@ -23,7 +23,14 @@
  *    saturating at 6 (reading; the pages are silent on rounding).
  *  - Overflow-aware scaling ("Unveiling..." section 2.A): a block may take a
  *    scale one step smaller, letting its top values saturate, when that
- *    lowers the block's squared error.
+ *    lowers the block's squared error (MXREF_OAS: around the OCP byte). The
+ *    page's own form starts from the scale that maps the block maximum to at
+ *    most 6 and halves it when the maximum lands in (3, 3.5] under that
+ *    scale, a test on the maximum's mantissa bits (MXREF_OAS_BITS); the
+ *    error-driven choice around that no-overflow scale is MXREF_OAS_NF.
+ *  - Signal-to-noise of the quantization error (QSNR, "Unveiling..."
+ *    sections 3-4): 10 log10(sum x^2 / sum (x - x_hat)^2); the oracle
+ *    returns both sums.
  *  - Error measure: mean of squared differences (MXFP4 wiki page, example 2)
  *    and per-block sum of squared errors ("Unveiling..." section 2.B).
  *
@@ -149,6 +156,15 @@ float mxref_oas_sse32(const double *xb, int s) {
   return (grp[0] + grp[1]) + (grp[2] + grp[3]);
 }
 
+/* No-overflow byte: the smallest byte s >= 0 with amax / 2^(s-127) <= 6,
+ * so no element saturates. Clamped to 252, the largest byte whose every code
+ * decodes to a finite fp32/bf16 value. */
+static int no_overflow_scale(double amax) {
+  int s = 0;
+  while (s < 252 && amax / ldexp(1.0, s - 127) > 6.0) s++;
+  return s;
+}
+
 /* Scale byte of one block (xb holds its 32 values). */
 static int block_scale(const double *xb, int mode) {
   double amax = 0.0;
@@ -157,13 +173,31 @@ static int block_scale(const double *xb, int mode) {
     double a = fabs(xb[i]);
     if (a > amax) amax = a;
   }
-  int s0 = mxref_ocp_scale(amax);
-  if (mode == MXREF_OAS && s0 >= 1) {
-    float sse_ocp = mxref_oas_sse32(xb, s0);
-    float sse_low = mxref_oas_sse32(xb, s0 - 1);
-    if (sse_low < sse_ocp) return s0 - 1; /* strict: a tie keeps the OCP byte */
+  if (mode == MXREF_OCP || mode == MXREF_OAS) {
+    int s0 = mxref_ocp_scale(amax);
+    if (mode == MXREF_OAS && s0 >= 1) {
+      float sse_ocp = mxref_oas_sse32(xb, s0);
+      float sse_low = mxref_oas_sse32(xb, s0 - 1);
+      if (sse_low < sse_ocp) return s0 - 1; /* strict: a tie keeps the OCP byte */
+    }
+    return s0;
   }
-  return s0;
+  int snf = no_overflow_scale(amax);
+  if (mode == MXREF_OAS_BITS) {
+    /* the block maximum under the no-overflow scale lies in (3, 6]; in
+       (3, 3.5] the doubled value (6, 7] overflows 6 with no more relative
+       error than rounding at the larger scale, so the scale is halved */
+    double v = amax / ldexp(1.0, snf - 127);
+    if (snf >= 1 && v > 3.0 && v <= 3.5) return snf - 1;
+    return snf;
+  }
+  /* MXREF_OAS_NF: the smaller of the two errors, ties keep snf */
+  if (snf >= 1) {
+    float sse_nf = mxref_oas_sse32(xb, snf);
+    float sse_low = mxref_oas_sse32(xb, snf - 1);
+    if (sse_low < sse_nf) return snf - 1;
+  }
+  return snf;
 }
 
 /* ---- row-parallel drivers ---------------------------------------------- */
@@ -182,6 +216,7 @@ typedef struct {
   float *block_mse;
   int64_t r0, r1;
   long double sse; /* per-thread partial of the tensor SSE */
+  long double ssq; /* per-thread partial of the tensor sum of x^2 */
 } job_t;
 
 static void run_rows(job_t *j) {
@@ -189,6 +224,7 @@ static void run_rows(job_t *j) {
   const int64_t nb = j->k / BLOCK;
   double xb[BLOCK];
   j->sse = 0.0L;
+  j->ssq = 0.0L;
   for (int64_t r = j->r0; r < j->r1; r++) {
     for (int64_t b = 0; b < nb; b++) {
       const int64_t e0 = r * j->k + b * BLOCK; /* first element of the block */
@@ -208,7 +244,7 @@ static void run_rows(job_t *j) {
         }
       } else {
         const int s = j->scales_in[bi];
-        double sse = 0.0;
+        double sse = 0.0, ssq = 0.0;
         for (int i = 0; i < BLOCK; i++) {
           uint8_t byte = j->codes_in[(e0 + i) / 2];
           int c = (i % 2 == 0) ? (byte & 0xF) : (byte >> 4);
@@ -219,13 +255,16 @@ static void run_rows(job_t *j) {
             /* the reconstruction is the value a dequantize in x's dtype
                would return: round the exact value to float */
             double qf = isnan(q) ? q : (double)(float)q;
-            double d = load_elem(j->x, j->dtype, e0 + i) - qf;
+            double xv = load_elem(j->x, j->dtype, e0 + i);
+            double d = xv - qf;
             sse += d * d;
+            ssq += xv * xv;
           }
         }
         if (j->op == 3) {
           if (j->block_mse) j->block_mse[bi] = (float)(sse / BLOCK);
           j->sse += (long double)sse;
+          j->ssq += (long double)ssq;
         }
       }
     }
@@ -240,7 +279,8 @@ static void *thread_main(void *arg) {
 
 #define MAX_THREADS 256
 
-static int run(job_t proto, int64_t rows, int threads, long double *sse_out) {
+static int run(job_t proto, int64_t rows, int threads, long double *sse_out,
+               long double *ssq_out) {
   if (threads < 1) threads = 1;
   if (threads > MAX_THREADS) threads = MAX_THREADS;
   if (threads > rows) threads = rows > 0 ? (int)rows : 1;
@@ -259,9 +299,13 @@ static int run(job_t proto, int64_t rows, int threads, long double *sse_out) {
     for (int t = 0; t < threads; t++) pthread_join(tid[t], NULL);
   }
   if (sse_out) {
-    long double s = 0.0L;
-    for (int t = 0; t < threads; t++) s += jobs[t].sse;
+    long double s = 0.0L, q = 0.0L;
+    for (int t = 0; t < threads; t++) {
+      s += jobs[t].sse;
+      q += jobs[t].ssq;
+    }
     *sse_out = s;
+    if (ssq_out) *ssq_out = q;
   }
   return 0;
 }
@@ -275,14 +319,14 @@ int mxref_quantize(const void *x, int dtype, int64_t rows, int64_t k, int mode,
                    uint8_t *codes, uint8_t *scales, int threads) {
   if (check_shape(rows, k)) return -2;
   if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
-  if (mode != MXREF_OCP && mode != MXREF_OAS) return -4;
+  if (mode < MXREF_OCP || mode > MXREF_OAS_NF) return -4;
   if (rows == 0) return 0;
   if (!x || !codes || !scales) return -1;
   job_t j;
   memset(&j, 0, sizeof j);
   j.op = 0; j.x = x; j.dtype = dtype; j.mode = mode; j.k = k;
   j.codes = codes; j.scales = scales;
-  return run(j, rows, threads, NULL);
+  return run(j, rows, threads, NULL, NULL);
 }
 
 int mxref_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
@@ -295,29 +339,29 @@ int mxref_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
   memset(&j, 0, sizeof j);
   j.op = 1; j.dtype = dtype; j.k = k;
   j.codes_in = codes; j.scales_in = scales; j.y = y;
-  return run(j, rows, threads, NULL);
+  return run(j, rows, threads, NULL, NULL);
 }
 
 int mxref_fakequant(const void *x, int dtype, int64_t rows, int64_t k, int mode,
                     void *y, int threads) {
   if (check_shape(rows, k)) return -2;
   if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
-  if (mode != MXREF_OCP && mode != MXREF_OAS) return -4;
+  if (mode < MXREF_OCP || mode > MXREF_OAS_NF) return -4;
   if (rows == 0) return 0;
   if (!x || !y) return -1;
   job_t j;
   memset(&j, 0, sizeof j);
   j.op = 2; j.x = x; j.dtype = dtype; j.mode = mode; j.k = k; j.y = y;
-  return run(j, rows, threads, NULL);
+  return run(j, rows, threads, NULL, NULL);
 }
 
 int mxref_block_mse(const void *x, int dtype, const uint8_t *codes,
                     const uint8_t *scales, int64_t rows, int64_t k,
-                    float *block_mse, double *tensor_sse, int threads) {
+                    float *block_mse, double *tensor_sums, int threads) {
   if (check_shape(rows, k)) return -2;
   if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
   if (rows == 0) {
-    if (tensor_sse) *tensor_sse = 0.0;
+    if (tensor_sums) tensor_sums[0] = tensor_sums[1] = 0.0;
     return 0;
   }
   if (!x || !codes || !scales) return -1;
@@ -325,8 +369,11 @@ int mxref_block_mse(const void *x, int dtype, const uint8_t *codes,
   memset(&j, 0, sizeof j);
   j.op = 3; j.x = x; j.dtype = dtype; j.k = k;
   j.codes_in = codes; j.scales_in = scales; j.block_mse = block_mse;
-  long double sse = 0.0L;
-  int rc = run(j, rows, threads, &sse);
-  if (tensor_sse) *tensor_sse = (double)sse;
+  long double sse = 0.0L, ssq = 0.0L;
+  int rc = run(j, rows, threads, &sse, &ssq);
+  if (tensor_sums) {
+    tensor_sums[0] = (double)sse;
+    tensor_sums[1] = (double)ssq;
+  }
   return rc;
 }

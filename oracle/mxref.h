@@ -23,7 +23,7 @@ extern "C" {
 #endif
 
 enum { MXREF_F32 = 0, MXREF_BF16 = 1 };
-enum { MXREF_OCP = 0, MXREF_OAS = 1 };
+enum { MXREF_OCP = 0, MXREF_OAS = 1, MXREF_OAS_BITS = 2, MXREF_OAS_NF = 3 };
 
 int mxref_quantize(const void *x, int dtype, int64_t rows, int64_t k, int mode,
                    uint8_t *codes, uint8_t *scales, int threads);
@@ -31,10 +31,11 @@ int mxref_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                      int64_t k, int dtype, void *y, int threads);
 int mxref_fakequant(const void *x, int dtype, int64_t rows, int64_t k, int mode,
                     void *y, int threads);
-/* block_mse may be NULL; tensor_sse may be NULL. */
+/* block_mse may be NULL; tensor_sums (2 doubles: sum (x - x_hat)^2, sum x^2)
+ * may be NULL. */
 int mxref_block_mse(const void *x, int dtype, const uint8_t *codes,
                     const uint8_t *scales, int64_t rows, int64_t k,
-                    float *block_mse, double *tensor_sse, int threads);
+                    float *block_mse, double *tensor_sums, int threads);
 
 /* Single-block helpers exposed for the oracle's own pins. */
 int mxref_ocp_scale(double amax);                 /* E8M0 byte of the OCP rule */

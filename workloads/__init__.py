@@ -188,3 +188,21 @@ def special_blocks_f32() -> np.ndarray:
     b = z.copy(); b[0] = np.ldexp(f(1.5), -126); b[1] = np.ldexp(f(1), -127); blocks.append(b)
     b = np.linspace(-7.5, 7.5, 32).astype(f); blocks.append(b)
     return np.stack(blocks)
+
+
+def oas_tie_prone_blocks(seed: int, n_blocks: int) -> np.ndarray:
+    """fp32 blocks [n_blocks, 32] built so that the overflow-aware choice goes
+    both ways: many values that sit on rounding ties at scale 2^(s-127) but on
+    the grid at half that scale, mixed with eighths, a top element near 4 and
+    a random power-of-two block scale."""
+    rng = np.random.default_rng(seed)
+    tie_prone = np.array([0.25, 0.75, 0.75, 0.5, 1.0, 1.25, 0.0])
+    x = (rng.integers(-8, 9, (n_blocks, 32)) / 8.0)
+    n_tie = rng.integers(8, 33, n_blocks)
+    mask = np.arange(32)[None, :] < n_tie[:, None]
+    tie = rng.choice(tie_prone, (n_blocks, 32)) * rng.choice([-1.0, 1.0], (n_blocks, 32))
+    x = np.where(mask, tie, x)
+    top = rng.choice([4.0, 4.0, 4.125, -4.0, 5.0, 7.5], n_blocks)
+    x[np.arange(n_blocks), rng.integers(0, 32, n_blocks)] = top
+    x *= 2.0 ** rng.integers(-100, 100, (n_blocks, 1))
+    return x.astype(np.float32)
