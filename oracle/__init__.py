@@ -70,6 +70,17 @@ def _load():
         lib.mxref_decode.restype = ctypes.c_double
         lib.mxref_oas_sse32.argtypes = [ctypes.POINTER(ctypes.c_double), i32]
         lib.mxref_oas_sse32.restype = ctypes.c_float
+        lib.mxref8_quantize.argtypes = [p, i32, i64, i64, p, p, i32]
+        lib.mxref8_dequantize.argtypes = [p, p, i64, i64, i32, p, i32]
+        lib.mxref8_fakequant.argtypes = [p, i32, i64, i64, p, i32]
+        for f in ("mxref8_quantize", "mxref8_dequantize", "mxref8_fakequant"):
+            getattr(lib, f).restype = i32
+        lib.mxref8_scale.argtypes = [ctypes.c_double]
+        lib.mxref8_scale.restype = i32
+        lib.mxref8_encode.argtypes = [ctypes.c_double, i32]
+        lib.mxref8_encode.restype = i32
+        lib.mxref8_decode.argtypes = [i32, i32]
+        lib.mxref8_decode.restype = ctypes.c_double
         _lib = lib
     return _lib
 
@@ -180,3 +191,50 @@ def oas_sse32(block: np.ndarray, scale_byte: int) -> float:
     assert b.shape == (32,)
     return float(_load().mxref_oas_sse32(b.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
                                          int(scale_byte)))
+
+
+# --- MXFP8 (E4M3 elements, one byte each) ----------------------------------
+
+def quantize_mxfp8(x: np.ndarray, threads: int = 1):
+    """Return (codes uint8 [..., k], scales uint8 [..., k/32])."""
+    x = np.ascontiguousarray(x)
+    rows, k = _shape2(x)
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty(x.shape[:-1] + (k // 32,), np.uint8)
+    _check(_load().mxref8_quantize(_ptr(x), _dtype_code(x), rows, k, _ptr(codes), _ptr(scales),
+                                   threads))
+    return codes, scales
+
+
+def dequantize_mxfp8(codes: np.ndarray, scales: np.ndarray, dtype: str = "bf16",
+                     threads: int = 1) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    k = codes.shape[-1]
+    rows = int(np.prod(codes.shape[:-1])) if codes.ndim > 1 else 1
+    if scales.size != rows * (k // 32):
+        raise ValueError("scales do not match codes")
+    y = np.empty(codes.shape, np.float32 if dtype == "f32" else np.uint16)
+    _check(_load().mxref8_dequantize(_ptr(codes), _ptr(scales), rows, k,
+                                     F32 if dtype == "f32" else BF16, _ptr(y), threads))
+    return y
+
+
+def fakequant_mxfp8(x: np.ndarray, threads: int = 1) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    rows, k = _shape2(x)
+    y = np.empty_like(x)
+    _check(_load().mxref8_fakequant(_ptr(x), _dtype_code(x), rows, k, _ptr(y), threads))
+    return y
+
+
+def scale_mxfp8(amax: float) -> int:
+    return _load().mxref8_scale(float(amax))
+
+
+def encode_e4m3(x: float, scale_byte: int) -> int:
+    return _load().mxref8_encode(float(x), int(scale_byte))
+
+
+def decode_e4m3(code: int, scale_byte: int) -> float:
+    return _load().mxref8_decode(int(code), int(scale_byte))

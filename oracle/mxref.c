@@ -377,3 +377,163 @@ int mxref_block_mse(const void *x, int dtype, const uint8_t *codes,
   }
   return rc;
 }
+
+/* ======================================================================
+ * MXFP8 (E4M3 elements) - vLLM MXFP8/MXFP4 page, "MXFP8: Block-32 scaling"
+ * section (online MXFP8 quantization: FP8 values plus one uint8 scale per
+ * 32 elements) and the MX format table (MXFP8: E4M3/E5M2, block 32, E8M0).
+ *  - E4M3 ("fn"): sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ *    0 is subnormal (m/8 * 2^-6); no infinities; exponent 15 with mantissa 7
+ *    is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+ *  - Scale: floor(log2 amax) - 8 (8 = exponent of 448), biased by 127 and
+ *    clamped to [0, 254]; NaN/Inf blocks get 255 (as for MXFP4). The block
+ *    maximum lands in [256, 512) and values above 448 saturate (reading: the
+ *    same saturation as the FP4 elements).
+ *  - Elements: nearest E4M3 value, ties to the even code; the sign is kept.
+ *    NaN/Inf blocks: codes hold the sign bit alone, decode to NaN.
+ * ====================================================================== */
+
+/* Magnitude of E4M3 code c (0..126) from its fields. */
+static double e4m3_value(int c) {
+  int e = (c >> 3) & 15, m = c & 7;
+  if (e == 0) return ldexp((double)m / 8.0, -6);
+  return ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
+int mxref8_scale(double amax) {
+  if (amax == 0.0) return 0;
+  int e2;
+  (void)frexp(amax, &e2);
+  int s = (e2 - 1) - 8 + 127;
+  if (s < 0) s = 0;
+  if (s > 254) s = 254;
+  return s;
+}
+
+int mxref8_encode(double x, int s) {
+  int sign = signbit(x) ? 0x80 : 0;
+  if (s == 255) return sign;
+  double v = fabs(x) / ldexp(1.0, s - 127);
+  if (v >= 448.0) return sign | 0x7E;
+  int lo = 0; /* largest code with value <= v */
+  while (lo < 126 && e4m3_value(lo + 1) <= v) lo++;
+  int hi = lo + 1;
+  double mid = 0.5 * (e4m3_value(lo) + e4m3_value(hi)); /* exact in double */
+  int c;
+  if (v < mid)
+    c = lo;
+  else if (v > mid)
+    c = hi;
+  else
+    c = (lo % 2 == 0) ? lo : hi;
+  return sign | c;
+}
+
+/* Exact value of E4M3 code c at scale byte s; NaN for byte 255 or a NaN code. */
+double mxref8_decode(int c, int s) {
+  if (s == 255 || (c & 0x7F) == 0x7F) return NAN;
+  double mag = e4m3_value(c & 0x7F) * ldexp(1.0, s - 127);
+  return (c & 0x80) ? -mag : mag;
+}
+
+typedef struct {
+  int op; /* 0 quantize, 1 dequantize, 2 fakequant */
+  const void *x;
+  int dtype;
+  int64_t k;
+  const uint8_t *codes_in, *scales_in;
+  uint8_t *codes, *scales;
+  void *y;
+  int64_t r0, r1;
+} job8_t;
+
+static void *run8_rows(void *arg) {
+  job8_t *j = (job8_t *)arg;
+  unsigned int csr = enter_ieee();
+  const int64_t nb = j->k / BLOCK;
+  for (int64_t r = j->r0; r < j->r1; r++) {
+    for (int64_t b = 0; b < nb; b++) {
+      const int64_t e0 = r * j->k + b * BLOCK, bi = r * nb + b;
+      if (j->op == 1) {
+        int s = j->scales_in[bi];
+        for (int i = 0; i < BLOCK; i++)
+          store_elem(j->y, j->dtype, e0 + i, mxref8_decode(j->codes_in[e0 + i], s));
+        continue;
+      }
+      double xb[BLOCK], amax = 0.0;
+      int nonfinite = 0;
+      for (int i = 0; i < BLOCK; i++) {
+        xb[i] = load_elem(j->x, j->dtype, e0 + i);
+        if (isnan(xb[i]) || isinf(xb[i])) nonfinite = 1;
+        else if (fabs(xb[i]) > amax) amax = fabs(xb[i]);
+      }
+      int s = nonfinite ? 255 : mxref8_scale(amax);
+      for (int i = 0; i < BLOCK; i++) {
+        int c = mxref8_encode(xb[i], s);
+        if (j->op == 0)
+          j->codes[e0 + i] = (uint8_t)c;
+        else
+          store_elem(j->y, j->dtype, e0 + i, mxref8_decode(c, s));
+      }
+      if (j->op == 0) j->scales[bi] = (uint8_t)s;
+    }
+  }
+  leave_ieee(csr);
+  return NULL;
+}
+
+static int run8(job8_t proto, int64_t rows, int threads) {
+  if (threads < 1) threads = 1;
+  if (threads > MAX_THREADS) threads = MAX_THREADS;
+  if (threads > rows) threads = rows > 0 ? (int)rows : 1;
+  job8_t jobs[MAX_THREADS];
+  pthread_t tid[MAX_THREADS];
+  for (int t = 0; t < threads; t++) {
+    jobs[t] = proto;
+    jobs[t].r0 = rows * t / threads;
+    jobs[t].r1 = rows * (t + 1) / threads;
+  }
+  if (threads == 1) {
+    run8_rows(&jobs[0]);
+    return 0;
+  }
+  for (int t = 0; t < threads; t++)
+    if (pthread_create(&tid[t], NULL, run8_rows, &jobs[t]) != 0) return -9;
+  for (int t = 0; t < threads; t++) pthread_join(tid[t], NULL);
+  return 0;
+}
+
+int mxref8_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
+                    uint8_t *scales, int threads) {
+  if (check_shape(rows, k)) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (rows == 0) return 0;
+  if (!x || !codes || !scales) return -1;
+  job8_t j;
+  memset(&j, 0, sizeof j);
+  j.op = 0; j.x = x; j.dtype = dtype; j.k = k; j.codes = codes; j.scales = scales;
+  return run8(j, rows, threads);
+}
+
+int mxref8_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t k,
+                      int dtype, void *y, int threads) {
+  if (check_shape(rows, k)) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (rows == 0) return 0;
+  if (!codes || !scales || !y) return -1;
+  job8_t j;
+  memset(&j, 0, sizeof j);
+  j.op = 1; j.dtype = dtype; j.k = k; j.codes_in = codes; j.scales_in = scales; j.y = y;
+  return run8(j, rows, threads);
+}
+
+int mxref8_fakequant(const void *x, int dtype, int64_t rows, int64_t k, void *y, int threads) {
+  if (check_shape(rows, k)) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (rows == 0) return 0;
+  if (!x || !y) return -1;
+  job8_t j;
+  memset(&j, 0, sizeof j);
+  j.op = 2; j.x = x; j.dtype = dtype; j.k = k; j.y = y;
+  return run8(j, rows, threads);
+}

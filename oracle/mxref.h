@@ -43,6 +43,17 @@ int mxref_encode(double x, int scale_byte);       /* 4-bit code of one element *
 double mxref_decode(int code, int scale_byte);    /* exact value of one code   */
 float mxref_oas_sse32(const double *x32, int scale_byte); /* pinned fp32 SSE */
 
+/* MXFP8 with E4M3 elements: codes [rows, k] uint8 (one byte per element),
+ * scales [rows, k/32] as above. OCP scale only. */
+int mxref8_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
+                    uint8_t *scales, int threads);
+int mxref8_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t k,
+                      int dtype, void *y, int threads);
+int mxref8_fakequant(const void *x, int dtype, int64_t rows, int64_t k, void *y, int threads);
+int mxref8_scale(double amax);
+int mxref8_encode(double x, int scale_byte);
+double mxref8_decode(int code, int scale_byte);
+
 #ifdef __cplusplus
 }
 #endif
