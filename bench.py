@@ -35,9 +35,21 @@ BYTES_PER_ELEM = {
     "block_mse": 2 + 0.5 + 1 / 32 + 4 / 32,  # x, codes, scales in; fp32/block out
 }
 OPS = list(BYTES_PER_ELEM)
+# measured beside the step (not part of it): the page-faithful
+# overflow-aware variants and fake-quant in the overflow-aware modes
+EXTRA_BYTES_PER_ELEM = {
+    "quantize_oas_bits": 2 + 0.5 + 1 / 32,
+    "quantize_oas_nf": 2 + 0.5 + 1 / 32,
+    "fakequant_oas": 4.0,
+    "fakequant_oas_nf": 4.0,
+    # MXFP8 (E4M3): one code byte per element
+    "quantize_mxfp8": 2 + 1 + 1 / 32,
+    "dequantize_mxfp8_bf16": 1 + 1 / 32 + 2,
+    "fakequant_mxfp8": 4.0,
+}
 KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0>", "quantize_oas": "k_quantize<true, 1>",
              "dequantize_bf16": "k_dequantize<true>", "fakequant_ocp": "k_fakequant<true, 0>",
-             "block_mse": "k_block_mse<true>"}
+             "block_mse": "k_block_mse<true, true>"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mx_bf16_8192x4096_hbm_traffic.md")
 KERNEL_SRC = os.path.join(ROOT, "microscaling_fp4_block_mx_amd", "csrc", "mx_kernels.hip")
 
@@ -96,7 +108,7 @@ def main():
     x_host = workloads.bf16_student_t_outlier_channels(2)
     R_, K_ = x_host.shape
     n = x_host.numel()
-    per_set = n * (2 + 0.5 * 2 + 2 / 32 + 2 + 2 + 4 / 32)
+    per_set = n * (2 + 0.5 * 2 + 2 / 32 + 2 + 2 + 4 / 32 + 1 + 1 / 32)
     n_sets = max(2, int(np.ceil(args.rotate_gib * 2 ** 30 / per_set)))
 
     x0 = x_host.to(dev)
@@ -111,9 +123,11 @@ def main():
             y_dq=torch.empty_like(x0),
             y_fq=torch.empty_like(x0),
             bm=torch.empty((R_, K_ // 32), dtype=torch.float32, device=dev),
+            c8=torch.empty((R_, K_), dtype=torch.uint8, device=dev),
+            s8=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
         ))
     del x0
-    sse = torch.empty((), dtype=torch.float64, device=dev)
+    sums = torch.empty(2, dtype=torch.float64, device=dev)
     ws_bytes = mx.mx_block_mse_workspace_size(R_, K_)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -132,10 +146,27 @@ def main():
         elif op == "fakequant_ocp":
             st = mx.mx_fakequant(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP,
                                  b["y_fq"].data_ptr(), sh)
+        elif op in ("quantize_oas_bits", "quantize_oas_nf"):
+            mode = mx.MX_SCALE_OAS_BITS if op.endswith("bits") else mx.MX_SCALE_OAS_NF
+            st = mx.mx_quantize(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mode,
+                                b["c_oas"].data_ptr(), b["s_oas"].data_ptr(), sh)
+        elif op == "quantize_mxfp8":
+            st = mx.mx_quantize_mxfp8(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["c8"].data_ptr(),
+                                      b["s8"].data_ptr(), sh)
+        elif op == "dequantize_mxfp8_bf16":
+            st = mx.mx_dequantize_mxfp8(b["c8"].data_ptr(), b["s8"].data_ptr(), R_, K_, mx.MX_BF16,
+                                        b["y_dq"].data_ptr(), sh)
+        elif op == "fakequant_mxfp8":
+            st = mx.mx_fakequant_mxfp8(b["x"].data_ptr(), mx.MX_BF16, R_, K_,
+                                       b["y_fq"].data_ptr(), sh)
+        elif op in ("fakequant_oas", "fakequant_oas_nf"):
+            mode = mx.MX_SCALE_OAS if op == "fakequant_oas" else mx.MX_SCALE_OAS_NF
+            st = mx.mx_fakequant(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mode,
+                                 b["y_fq"].data_ptr(), sh)
         else:
             st = mx.mx_block_mse(b["x"].data_ptr(), mx.MX_BF16, b["c_ocp"].data_ptr(),
                                  b["s_ocp"].data_ptr(), R_, K_, b["bm"].data_ptr(),
-                                 sse.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+                                 sums.data_ptr(), ws.data_ptr(), ws_bytes, sh)
         if st != mx.MX_OK:
             raise RuntimeError(mx.mx_status_string(st))
 
@@ -164,8 +195,10 @@ def main():
 
     # per-kernel launch time: each op alone, back to back over the rotating
     # sets, K * n_sets launches between two events on the same stream
+    for i in range(n_sets):  # codes for the MXFP8 dequantize
+        run("quantize_mxfp8", sets[i])
     op_ms = {}
-    for op in OPS:
+    for op in OPS + list(EXTRA_BYTES_PER_ELEM):
         for i in range(n_sets):
             run(op, sets[i])
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -201,6 +234,11 @@ def main():
         breakdown[op] = {"us": round(op_ms[op] * 1e3, 2), "GB/s": round(gbs, 1),
                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes": int(bytes_op[op])}
+    extra = {}
+    for op, bpe in EXTRA_BYTES_PER_ELEM.items():
+        gbs = bpe * n / (op_ms[op] * 1e-3) / 1e9
+        extra[op] = {"us": round(op_ms[op] * 1e3, 2), "GB/s": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(bpe * n)}
     dom = max(OPS, key=lambda o: op_ms[o])
     dom_gbs = bytes_op[dom] / (op_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
@@ -208,6 +246,22 @@ def main():
                 "traffic": measured_traffic(dom),
                 "bytes_per_launch": int(bytes_op[dom]),
                 "avg_launch_us": round(op_ms[dom] * 1e3, 2)}
+
+    # quantization quality of the bench tensor per scale mode (outside the
+    # timed region): tensor MSE and QSNR from the block-error kernel
+    quality = {}
+    b = sets[0]
+    for mode in mx.MODES:
+        c, sc = mx.quantize(b["x"], mode)
+        _, sums = mx.block_mse(b["x"], c, sc, per_block=False)
+        sse, ssq = sums.tolist()
+        quality["mxfp4_" + mode] = {"mse": sse / n, "qsnr_db": round(10 * np.log10(ssq / sse), 4)}
+    y8 = mx.fakequant_mxfp8(b["x"]).float()
+    xf = b["x"].float()
+    sse8 = float(((xf - y8).double() ** 2).sum())
+    quality["mxfp8"] = {"mse": sse8 / n,
+                        "qsnr_db": round(10 * np.log10(float((xf.double() ** 2).sum()) / sse8), 4)}
+    del y8, xf
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -227,6 +281,8 @@ def main():
                    "device_copy_reference": {"bytes": 4 * n, "us": round(copy_us, 2),
                                              "GB/s": round(4 * n / copy_us / 1e3, 1)}},
         "breakdown": breakdown,
+        "beside_the_step": extra,
+        "quality": quality,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -31,7 +31,7 @@
  *     fault surfaces at the caller's next synchronization.
  *   - rows == 0 returns MX_OK without reading or writing any tensor
  *     (pointers may then be NULL); only mx_block_mse still enqueues the
- *     write of 0 to tensor_sse.
+ *     write of 0 to tensor_sums.
  *   - x, y, codes and scales must be 16-byte aligned (MX_ERR_ALIGN).
  *   - Outputs must not overlap inputs, except that mx_fakequant accepts
  *     y == x exactly (in place). Partial overlap is MX_ERR_ALIAS.
@@ -52,7 +52,7 @@ typedef enum {
   MX_ERR_NULL = 1,   /* a required pointer is NULL                          */
   MX_ERR_SHAPE = 2,  /* rows < 0, k <= 0, k % 32 != 0, or rows*k overflows   */
   MX_ERR_DTYPE = 3,  /* dtype is not MX_F32 / MX_BF16                        */
-  MX_ERR_MODE = 4,   /* mode is not a mx_scale_mode_t value                  */
+  MX_ERR_MODE = 4,   /* mode is not an mx_scale_mode_t value                 */
   MX_ERR_ALIGN = 5,  /* a data pointer is not 16-byte aligned                */
   MX_ERR_HIP = 6,    /* the HIP launch failed; see mx_last_error_detail()    */
   MX_ERR_ALIAS = 7,  /* an output partially overlaps an input                */
@@ -75,7 +75,21 @@ typedef enum {
      within a group one accumulator takes the even positions and one the odd
      positions, each acc = fma(d, d, acc) with d = x - x_hat (fp32); group =
      even + odd; total = (g0 + g1) + (g2 + g3). */
-  MX_SCALE_OAS = 1
+  MX_SCALE_OAS = 1,
+  /* Overflow-aware scaling in the page's own form ("Unveiling...", technical
+     summary section 2.A): start from the no-overflow byte s_nf, the smallest
+     byte with amax / 2^(s_nf-127) <= 6; when that normalized maximum lies in
+     (3, 3.5], take s_nf - 1, so it maps to (6, 7] and saturates at 6 with no
+     more relative error than rounding at s_nf would give, while every smaller
+     value gains a binade. This is a test on amax's mantissa bits: relative to
+     the OCP byte it is s0 + 1 when amax / 2^(s0-127) > 7, else s0. */
+  MX_SCALE_OAS_BITS = 2,
+  /* Error-driven form around the no-overflow byte: the block takes s_nf - 1
+     when its squared error (the fp32 order above) is strictly smaller than at
+     s_nf; ties keep s_nf. */
+  MX_SCALE_OAS_NF = 3
+  /* In the two page modes the scale byte never exceeds 252, the largest byte
+     at which every code decodes to a finite fp32/bf16 value. */
 } mx_scale_mode_t;
 
 /* Quantize x [rows, k] (fp32 or bf16) to packed E2M1 codes [rows, k/2] and
@@ -110,27 +124,53 @@ mx_status_t mx_fakequant(const void *x, mx_dtype_t dtype, int64_t rows,
 /* Quantization error of x against (codes, scales): per block
  * SSE = sum_i (x_i - x_hat_i)^2 in fp64, with x_hat_i the value
  * mx_dequantize returns in x's dtype; block_mse[b] = (float)(SSE_b / 32).
- * tensor_sse (one device double, overwritten) receives the sum of all block
- * SSEs in fp64; the tensor MSE is tensor_sse / (rows * k). Either output may
- * be NULL (both NULL is MX_ERR_NULL). block_mse must be 4-byte aligned and
- * tensor_sse 8-byte aligned. Both outputs are deterministic: the tensor sum
- * is taken in a fixed order (per-workgroup partial sums, then one ordered
- * reduction), never with atomics.
+ * tensor_sums (two device doubles, overwritten) receives
+ *   tensor_sums[0] = sum of all block SSEs (tensor MSE = [0] / (rows * k)),
+ *   tensor_sums[1] = sum of x_i^2 (QSNR = 10 log10([1] / [0]) dB),
+ * both in fp64. Either output may be NULL (both NULL is MX_ERR_NULL).
+ * block_mse must be 4-byte aligned and tensor_sums 8-byte aligned. Both
+ * outputs are deterministic: the tensor sums are taken in a fixed order
+ * (per-workgroup partial sums, then one ordered reduction), never with atomics.
  * workspace: device scratch for those partial sums, needed only when
- * tensor_sse != NULL; at least mx_block_mse_workspace_size(rows, k) bytes,
+ * tensor_sums != NULL; at least mx_block_mse_workspace_size(rows, k) bytes,
  * 8-byte aligned, not overlapping any argument. Its contents on entry do not
  * matter; calls that share a workspace must be ordered (same stream).
  * Source: MXFP4 wiki page, example 2 (MSE as the quantization error);
- * "Unveiling..." section 2.B (block SSE as the objective). */
+ * "Unveiling..." section 2.B (block SSE as the objective) and sections 3-4
+ * (QSNR). */
 mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype,
                          const uint8_t *codes, const uint8_t *scales,
                          int64_t rows, int64_t k, float *block_mse,
-                         double *tensor_sse, void *workspace,
+                         double *tensor_sums, void *workspace,
                          size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace mx_block_mse needs for a [rows, k] tensor when it is
- * asked for tensor_sse (at most 16 KiB); 0 for an invalid shape. */
+ * asked for tensor_sums (at most 32 KiB); 0 for an invalid shape. */
 size_t mx_block_mse_workspace_size(int64_t rows, int64_t k);
+
+/* ---- MXFP8 (E4M3 elements) ------------------------------------------------
+ * vLLM MXFP8/MXFP4 page, "MXFP8: Block-32 scaling" section: online MXFP8
+ * quantization produces FP8 values plus one uint8 scale per 32 elements of
+ * the (multiple-of-32) input dimension; MX format table: MXFP8 = E4M3 (or
+ * E5M2) elements, block 32, E8M0 scale. Here: E4M3 ("fn": no infinities,
+ * NaN = S.1111.111, largest magnitude 448), one code byte per element,
+ * codes uint8 [rows, k], scales uint8 [rows, k/32]. Scale byte:
+ * floor(log2 amax) - 8 + 127 (8 is the exponent of 448), clamped to
+ * [0, 254]; 255 for a NaN/Inf block (codes = sign bit alone). Elements:
+ * nearest E4M3 value of x / 2^(s-127), ties to the even code, saturating at
+ * +-448. Decoding a NaN code (0x7F/0xFF) or scale byte 255 gives the
+ * canonical quiet NaN; bf16 outputs are rounded to nearest even (values
+ * below bf16's subnormal step occur at scale bytes 0..3). Same pointer,
+ * alignment, aliasing and error conventions as the MXFP4 entry points. */
+mx_status_t mx_quantize_mxfp8(const void *x, mx_dtype_t x_dtype, int64_t rows,
+                              int64_t k, uint8_t *codes, uint8_t *scales,
+                              void *stream);
+mx_status_t mx_dequantize_mxfp8(const uint8_t *codes, const uint8_t *scales,
+                                int64_t rows, int64_t k, mx_dtype_t y_dtype,
+                                void *y, void *stream);
+/* y = mx_dequantize_mxfp8(mx_quantize_mxfp8(x)) in x's dtype; y may equal x. */
+mx_status_t mx_fakequant_mxfp8(const void *x, mx_dtype_t dtype, int64_t rows,
+                               int64_t k, void *y, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *mx_status_string(mx_status_t s);

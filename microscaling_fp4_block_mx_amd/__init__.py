@@ -28,13 +28,16 @@ LIB_PATH = os.path.join(_HERE, "libmx.so")
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_DTYPE, MX_ERR_MODE, MX_ERR_ALIGN, MX_ERR_HIP, \
     MX_ERR_ALIAS, MX_ERR_WORKSPACE = range(9)
 MX_F32, MX_BF16 = 0, 1
-MX_SCALE_OCP, MX_SCALE_OAS = 0, 1
+MX_SCALE_OCP, MX_SCALE_OAS, MX_SCALE_OAS_BITS, MX_SCALE_OAS_NF = 0, 1, 2, 3
 BLOCK = 32
 
-_MODES = {"ocp": MX_SCALE_OCP, "oas": MX_SCALE_OAS}
+_MODES = {"ocp": MX_SCALE_OCP, "oas": MX_SCALE_OAS, "oas_bits": MX_SCALE_OAS_BITS,
+          "oas_nf": MX_SCALE_OAS_NF}
+MODES = tuple(_MODES)
 _DTYPES = {torch.float32: MX_F32, torch.bfloat16: MX_BF16}
 EXPORTS = ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
-           "mx_block_mse_workspace_size", "mx_status_string", "mx_last_error_detail")
+           "mx_block_mse_workspace_size", "mx_quantize_mxfp8", "mx_dequantize_mxfp8",
+           "mx_fakequant_mxfp8", "mx_status_string", "mx_last_error_detail")
 
 _lib = None
 
@@ -55,7 +58,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mx_block_mse.argtypes = [p, i32, p, p, i64, i64, p, p, p, ctypes.c_size_t, p]
     lib.mx_block_mse_workspace_size.argtypes = [i64, i64]
     lib.mx_block_mse_workspace_size.restype = ctypes.c_size_t
-    for f in ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse"):
+    lib.mx_quantize_mxfp8.argtypes = [p, i32, i64, i64, p, p, p]
+    lib.mx_dequantize_mxfp8.argtypes = [p, p, i64, i64, i32, p, p]
+    lib.mx_fakequant_mxfp8.argtypes = [p, i32, i64, i64, p, p]
+    for f in ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
+              "mx_quantize_mxfp8", "mx_dequantize_mxfp8", "mx_fakequant_mxfp8"):
         getattr(lib, f).restype = i32
     lib.mx_status_string.argtypes = [i32]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -87,6 +94,18 @@ def mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse, tensor_sse, work
 
 def mx_block_mse_workspace_size(rows, k) -> int:
     return load_library().mx_block_mse_workspace_size(rows, k)
+
+
+def mx_quantize_mxfp8(x, x_dtype, rows, k, codes, scales, stream) -> int:
+    return load_library().mx_quantize_mxfp8(x, x_dtype, rows, k, codes, scales, stream)
+
+
+def mx_dequantize_mxfp8(codes, scales, rows, k, y_dtype, y, stream) -> int:
+    return load_library().mx_dequantize_mxfp8(codes, scales, rows, k, y_dtype, y, stream)
+
+
+def mx_fakequant_mxfp8(x, dtype, rows, k, y, stream) -> int:
+    return load_library().mx_fakequant_mxfp8(x, dtype, rows, k, y, stream)
 
 
 def mx_status_string(status: int) -> str:
@@ -127,7 +146,7 @@ def _mode(mode: str) -> int:
     try:
         return _MODES[mode]
     except KeyError:
-        raise ValueError(f"mode must be 'ocp' or 'oas', got {mode!r}") from None
+        raise ValueError(f"mode must be one of {MODES}, got {mode!r}") from None
 
 
 def quantize(x: torch.Tensor, mode: str = "ocp", codes: torch.Tensor | None = None,
@@ -183,8 +202,9 @@ def fakequant(x: torch.Tensor, mode: str = "ocp", out: torch.Tensor | None = Non
 
 def block_mse(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
               per_block: bool = True):
-    """-> (block_mse float32 [..., k/32] or None, tensor SSE as a 0-dim float64
-    GPU tensor). Tensor MSE = SSE / x.numel()."""
+    """-> (block_mse float32 [..., k/32] or None, sums float64 GPU tensor [2])
+    with sums[0] = sum (x - x_hat)^2 and sums[1] = sum x^2. Tensor MSE =
+    sums[0] / x.numel(); QSNR = 10 log10(sums[1] / sums[0]) dB."""
     rows, k = _check_input(x)
     if codes.numel() * 2 != x.numel() or scales.numel() * BLOCK != x.numel():
         raise ValueError("codes/scales do not match x")
@@ -192,11 +212,66 @@ def block_mse(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     if per_block:
         bm = torch.empty(tuple(x.shape[:-1]) + (k // BLOCK,), dtype=torch.float32,
                          device=x.device)
-    sse = torch.empty((), dtype=torch.float64, device=x.device)
+    sums = torch.empty(2, dtype=torch.float64, device=x.device)
     ws_bytes = mx_block_mse_workspace_size(rows, k)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):
         _raise(mx_block_mse(x.data_ptr(), _DTYPES[x.dtype], codes.data_ptr(), scales.data_ptr(),
                             rows, k, bm.data_ptr() if bm is not None else None,
-                            sse.data_ptr(), ws.data_ptr(), ws_bytes, _stream(x.device)))
-    return bm, sse
+                            sums.data_ptr(), ws.data_ptr(), ws_bytes, _stream(x.device)))
+    return bm, sums
+
+
+# ---- MXFP8 (E4M3) tensor helpers ---------------------------------------------
+
+def quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor | None = None,
+                   scales: torch.Tensor | None = None):
+    """x [..., k] -> (codes uint8 [..., k] (E4M3 bytes), scales uint8 [..., k/32])."""
+    rows, k = _check_input(x)
+    if codes is None:
+        codes = torch.empty(tuple(x.shape), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(tuple(x.shape[:-1]) + (k // BLOCK,), dtype=torch.uint8,
+                             device=x.device)
+    if codes.numel() != x.numel() or scales.numel() * BLOCK != x.numel():
+        raise ValueError("output sizes do not match x")
+    with torch.cuda.device(x.device):
+        _raise(mx_quantize_mxfp8(x.data_ptr(), _DTYPES[x.dtype], rows, k, codes.data_ptr(),
+                                 scales.data_ptr(), _stream(x.device)))
+    return codes, scales
+
+
+def dequantize_mxfp8(codes: torch.Tensor, scales: torch.Tensor, dtype=torch.bfloat16,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """E4M3 codes [..., k] + scales [..., k/32] -> y [..., k] in dtype."""
+    if not codes.is_cuda or codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise ValueError("codes and scales must be uint8 GPU tensors")
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("codes and scales must be contiguous")
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
+    k = codes.shape[-1]
+    if k <= 0 or k % BLOCK:
+        raise ValueError("MXFP8 needs the last dimension to be a multiple of 32")
+    rows = codes.numel() // k if codes.numel() else 0
+    if scales.numel() * BLOCK != codes.numel():
+        raise ValueError("scales do not match codes")
+    if out is None:
+        out = torch.empty(tuple(codes.shape), dtype=dtype, device=codes.device)
+    with torch.cuda.device(codes.device):
+        _raise(mx_dequantize_mxfp8(codes.data_ptr(), scales.data_ptr(), rows, k, _DTYPES[dtype],
+                                   out.data_ptr(), _stream(codes.device)))
+    return out
+
+
+def fakequant_mxfp8(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """dequantize_mxfp8(quantize_mxfp8(x)) in x's dtype; out may be x."""
+    rows, k = _check_input(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.numel() != x.numel() or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    with torch.cuda.device(x.device):
+        _raise(mx_fakequant_mxfp8(x.data_ptr(), _DTYPES[x.dtype], rows, k, out.data_ptr(),
+                                  _stream(x.device)))
+    return out

@@ -25,7 +25,7 @@ mx_status_t check_shape(int64_t rows, int64_t k) {
 }
 
 bool dtype_ok(int d) { return d == MX_F32 || d == MX_BF16; }
-bool mode_ok(int m) { return m == MX_SCALE_OCP || m == MX_SCALE_OAS; }
+bool mode_ok(int m) { return m >= MX_SCALE_OCP && m <= MX_SCALE_OAS_NF; }
 int64_t elem_bytes(int d) { return d == MX_F32 ? 4 : 2; }
 
 // Half-open byte ranges [a, a+na) and [b, b+nb) intersect.
@@ -98,22 +98,22 @@ size_t mx_block_mse_workspace_size(int64_t rows, int64_t k) {
 
 mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype, const uint8_t *codes,
                          const uint8_t *scales, int64_t rows, int64_t k, float *block_mse,
-                         double *tensor_sse, void *workspace, size_t workspace_bytes,
+                         double *tensor_sums, void *workspace, size_t workspace_bytes,
                          void *stream) {
   if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;
   if (mx_status_t s = check_shape(rows, k)) return s;
-  if (!block_mse && !tensor_sse) return MX_ERR_NULL;
-  if (tensor_sse) {
-    if ((reinterpret_cast<uintptr_t>(tensor_sse) & 7u) != 0) return MX_ERR_ALIGN;
+  if (!block_mse && !tensor_sums) return MX_ERR_NULL;
+  if (tensor_sums) {
+    if ((reinterpret_cast<uintptr_t>(tensor_sums) & 7u) != 0) return MX_ERR_ALIGN;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0 ||
         workspace_bytes < mx_block_mse_workspace_size(rows, k))
       return MX_ERR_WORKSPACE;
-    if (overlap(tensor_sse, 8, workspace, (int64_t)workspace_bytes)) return MX_ERR_ALIAS;
+    if (overlap(tensor_sums, 16, workspace, (int64_t)workspace_bytes)) return MX_ERR_ALIAS;
   }
   if (rows == 0) {
     // an empty tensor has zero error; still a device write, so it is enqueued
-    if (!tensor_sse) return MX_OK;
-    return finish(mxi_launch_block_mse(nullptr, 0, nullptr, nullptr, 0, nullptr, tensor_sse,
+    if (!tensor_sums) return MX_OK;
+    return finish(mxi_launch_block_mse(nullptr, 0, nullptr, nullptr, 0, nullptr, tensor_sums,
                                        static_cast<double *>(workspace),
                                        static_cast<hipStream_t>(stream)));
   }
@@ -126,18 +126,61 @@ mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype, const uint8_t *codes
   if (block_mse && (overlap(block_mse, nbm, x, nx) || overlap(block_mse, nbm, codes, n / 2) ||
                     overlap(block_mse, nbm, scales, n / kBlock)))
     return MX_ERR_ALIAS;
-  if (tensor_sse) {
+  if (tensor_sums) {
     const int64_t nw = (int64_t)workspace_bytes;
-    if (overlap(tensor_sse, 8, x, nx) || overlap(tensor_sse, 8, codes, n / 2) ||
-        overlap(tensor_sse, 8, scales, n / kBlock) ||
-        (block_mse && overlap(tensor_sse, 8, block_mse, nbm)) || overlap(workspace, nw, x, nx) ||
+    if (overlap(tensor_sums, 16, x, nx) || overlap(tensor_sums, 16, codes, n / 2) ||
+        overlap(tensor_sums, 16, scales, n / kBlock) ||
+        (block_mse && overlap(tensor_sums, 16, block_mse, nbm)) || overlap(workspace, nw, x, nx) ||
         overlap(workspace, nw, codes, n / 2) || overlap(workspace, nw, scales, n / kBlock) ||
         (block_mse && overlap(workspace, nw, block_mse, nbm)))
       return MX_ERR_ALIAS;
   }
   return finish(mxi_launch_block_mse(x, x_dtype == MX_BF16, codes, scales, n / 8, block_mse,
-                                     tensor_sse, static_cast<double *>(workspace),
+                                     tensor_sums, static_cast<double *>(workspace),
                                      static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_quantize_mxfp8(const void *x, mx_dtype_t x_dtype, int64_t rows, int64_t k,
+                              uint8_t *codes, uint8_t *scales, void *stream) {
+  if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape(rows, k)) return s;
+  if (rows == 0) return MX_OK;
+  if (!x || !codes || !scales) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  const int64_t nx = n * elem_bytes(x_dtype);
+  if (overlap(x, nx, codes, n) || overlap(x, nx, scales, n / kBlock) ||
+      overlap(codes, n, scales, n / kBlock))
+    return MX_ERR_ALIAS;
+  return finish(mxi_launch_quantize8(x, x_dtype == MX_BF16, n / 8, codes, scales,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_dequantize_mxfp8(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                                int64_t k, mx_dtype_t y_dtype, void *y, void *stream) {
+  if (!dtype_ok(y_dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape(rows, k)) return s;
+  if (rows == 0) return MX_OK;
+  if (!codes || !scales || !y) return MX_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(y)) return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  const int64_t ny = n * elem_bytes(y_dtype);
+  if (overlap(y, ny, codes, n) || overlap(y, ny, scales, n / kBlock)) return MX_ERR_ALIAS;
+  return finish(mxi_launch_dequantize8(codes, scales, y_dtype == MX_BF16, n / 8, y,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_fakequant_mxfp8(const void *x, mx_dtype_t dtype, int64_t rows, int64_t k,
+                               void *y, void *stream) {
+  if (!dtype_ok(dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape(rows, k)) return s;
+  if (rows == 0) return MX_OK;
+  if (!x || !y) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return MX_ERR_ALIGN;
+  const int64_t nb = rows * k * elem_bytes(dtype);
+  if (x != y && overlap(x, nb, y, nb)) return MX_ERR_ALIAS;
+  return finish(mxi_launch_fakequant8(x, dtype == MX_BF16, rows * k / 8, y,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 const char *mx_status_string(mx_status_t s) {
@@ -146,7 +189,7 @@ const char *mx_status_string(mx_status_t s) {
     case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
     case MX_ERR_SHAPE: return "MX_ERR_SHAPE: need rows >= 0 and k a positive multiple of 32";
     case MX_ERR_DTYPE: return "MX_ERR_DTYPE: dtype must be MX_F32 or MX_BF16";
-    case MX_ERR_MODE: return "MX_ERR_MODE: mode must be MX_SCALE_OCP or MX_SCALE_OAS";
+    case MX_ERR_MODE: return "MX_ERR_MODE: mode must be an mx_scale_mode_t value (0..3)";
     case MX_ERR_ALIGN: return "MX_ERR_ALIGN: data pointers must be 16-byte aligned";
     case MX_ERR_HIP: return "MX_ERR_HIP: HIP launch failed";
     case MX_ERR_ALIAS: return "MX_ERR_ALIAS: an output overlaps an input";

@@ -18,5 +18,12 @@ hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, in
 size_t mxi_block_mse_partials(int64_t nitems);
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                                 const uint8_t *scales, int64_t nitems, float *block_mse,
-                                double *tensor_sse, double *partial, hipStream_t st);
+                                double *tensor_sums, double *partial, hipStream_t st);
+// MXFP8 (E4M3): codes are one byte per element.
+hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t nitems, uint8_t *codes,
+                                uint8_t *scales, hipStream_t st);
+hipError_t mxi_launch_dequantize8(const uint8_t *codes, const uint8_t *scales, int bf16,
+                                  int64_t nitems, void *y, hipStream_t st);
+hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *y,
+                                 hipStream_t st);
 #endif

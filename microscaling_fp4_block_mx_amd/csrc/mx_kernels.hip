@@ -39,6 +39,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #ifndef MX_UNROLL
 #define MX_UNROLL 4
@@ -289,23 +291,59 @@ __device__ __forceinline__ float lane_sse(const Item<BF16> &x, uint32_t c, uint3
 }
 
 // Block scale byte and this lane's 8 codes (all quad lanes agree on s).
+//
+// Modes (bytes as in include/mx.h): with s0 the OCP byte and v0 the block
+// maximum over 2^(s0-127) (in [4, 8) whenever the exponent field e of amax is
+// >= 2), the no-overflow byte is s0 + 1 exactly when v0 > 6, i.e. when amax's
+// mantissa field exceeds 0x400000; the page's halving test ((3, 3.5] under
+// the no-overflow scale) leaves s0 + 1 only when v0 > 7, i.e. mantissa field
+// > 0x600000. Both are capped at 252 so every code decodes finite.
+//
+// Error-driven modes compare a high byte h with h - 1 by the pinned fp32
+// SSE. h - 1 is evaluated only when it can win: at h - 1 the block maximum
+// (> 3 * 2^(h-127)) saturates to 3 * 2^(h-127), so that element alone
+// contributes fl(d * d) with d = amax - 3 * 2^(h-127) (exact in fp32), and the
+// pinned sum only grows as non-negative terms are added (rounding is
+// monotone). Hence SSE32(h - 1) >= fl(d * d); when SSE32(h) <= fl(d * d) the
+// strict test SSE32(h - 1) < SSE32(h) must fail and h is kept without
+// computing it. The decision is identical to evaluating both candidates.
 template <bool BF16, int MODE>
 __device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t &codes) {
-  const uint32_t s = ocp_scale_byte(quad_max_u32(item_amax_bits<BF16>(x)));
-  if (__builtin_expect(s == 255u, 0)) {
+  const uint32_t amax = quad_max_u32(item_amax_bits<BF16>(x));
+  const uint32_t s0 = ocp_scale_byte(amax);
+  if (__builtin_expect(s0 == 255u, 0)) {
     codes = sign_codes<BF16>(x);
+    return s0;
+  }
+  const uint32_t mant = amax & 0x7FFFFFu;
+  const bool normalized = (amax >> 23) >= 2u;  // v0 in [4, 8)
+  if constexpr (MODE == MX_SCALE_OCP || MODE == MX_SCALE_OAS_BITS) {
+    uint32_t s = s0;
+    if (MODE == MX_SCALE_OAS_BITS && normalized && mant > 0x600000u) s = min(s0 + 1u, 252u);
+    codes = encode_item<BF16>(x, s);
     return s;
+  } else {
+    uint32_t h = s0;
+    if (MODE == MX_SCALE_OAS_NF && normalized && mant > 0x400000u) h = min(s0 + 1u, 252u);
+    if (h == 0u) {
+      codes = encode_item<BF16>(x, h);
+      return h;
+    }
+    uint32_t c_hi;
+    const float sse_hi = quad_sum_f32(lane_sse<BF16>(x, h, c_hi));
+    const float d_top = __uint_as_float(amax) - __builtin_amdgcn_ldexpf(3.0f, (int)h - 127);
+    const float bound = d_top * d_top;
+    codes = c_hi;
+    if (sse_hi > bound) {  // uniform over the quad: same sums, same amax
+      uint32_t c_low;
+      const float sse_low = quad_sum_f32(lane_sse<BF16>(x, h - 1u, c_low));
+      if (sse_low < sse_hi) {  // strict: a tie keeps h
+        codes = c_low;
+        return h - 1u;
+      }
+    }
+    return h;
   }
-  if (MODE == MX_SCALE_OAS && s >= 1u) {
-    uint32_t c_ocp, c_low;
-    const float sse_ocp = quad_sum_f32(lane_sse<BF16>(x, s, c_ocp));
-    const float sse_low = quad_sum_f32(lane_sse<BF16>(x, s - 1u, c_low));
-    const bool low = sse_low < sse_ocp;  // strict: a tie keeps the OCP byte
-    codes = low ? c_low : c_ocp;
-    return low ? s - 1u : s;
-  }
-  codes = encode_item<BF16>(x, s);
-  return s;
 }
 
 // ---- kernels -----------------------------------------------------------------
@@ -388,19 +426,21 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restr
 }
 
 // Block error. Per block: SSE = sum (x - x_hat)^2 in fp64 (quad sum in a
-// fixed order), block_mse = (float)(SSE / 32). The tensor sum is taken in two
-// stages with fixed order and no atomics: each workgroup writes the sum of
-// its blocks' SSEs to partial[blockIdx.x] (lane sums, then a butterfly over
-// the wave, then the waves in order), and k_sum_partials adds the partials.
-template <bool BF16>
+// fixed order), block_mse = (float)(SSE / 32). The tensor sums (SSE and
+// sum x^2) are taken in two stages with fixed order and no atomics: each
+// workgroup writes its two sums to partial[2 * blockIdx.x + {0, 1}] (lane
+// sums, then a butterfly over the wave, then the waves in order), and
+// k_sum_partials adds the partials.
+template <bool BF16, bool SUMS>
 __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__ x,
                                                         const uint32_t *__restrict__ codes,
                                                         const uint8_t *__restrict__ scales,
                                                         float *__restrict__ block_mse,
                                                         double *__restrict__ partial,
                                                         int64_t nitems) {
-  __shared__ double wave_part[kThreads / 64];
-  double mine = 0.0;  // sum of the block SSEs this lane reports (q == 0 lanes)
+  __shared__ double wave_part[2][kThreads / 64];
+  double mine = 0.0;     // sum of the block SSEs this lane reports (q == 0 lanes)
+  double mine_sq = 0.0;  // sum of x^2 over this lane's elements
   Item<BF16> xv[kUnroll];
   uint32_t cw[kUnroll], sb[kUnroll];
   tile_loop(
@@ -413,45 +453,236 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
       [&](int u, int64_t it) {
         float q[8];
         decode_f32(cw[u], sb[u], q);
-        double acc = 0.0;
+        double acc = 0.0, acc_sq = 0.0;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-          const double d = (double)elem<BF16>(xv[u], i) - (double)q[i];
+          const double xi = (double)elem<BF16>(xv[u], i);
+          const double d = xi - (double)q[i];
           acc = __builtin_fma(d, d, acc);
+          if constexpr (SUMS) acc_sq = __builtin_fma(xi, xi, acc_sq);
+        }
+        if constexpr (SUMS) {
+          // materialize here, so the eight widened x values die now instead
+          // of living across the quad sum (keeps the kernel at full occupancy)
+          __asm__ volatile("" : "+v"(acc_sq));
+          mine_sq += acc_sq;
         }
         const double sse = quad_sum_f64(acc);
         if ((threadIdx.x & 3) == 0) {
           if (block_mse) st<false>(block_mse + (it >> 2), (float)(sse * (1.0 / 32.0)));
-          mine += sse;
+          if constexpr (SUMS) mine += sse;
         }
       });
-  if (partial) {
+  if constexpr (SUMS) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mine += __shfl_xor(mine, off, 64);
-    if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = mine;
+    for (int off = 32; off >= 1; off >>= 1) {
+      mine += __shfl_xor(mine, off, 64);
+      mine_sq += __shfl_xor(mine_sq, off, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      wave_part[0][threadIdx.x >> 6] = mine;
+      wave_part[1][threadIdx.x >> 6] = mine_sq;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < 2) {
       double t = 0.0;
-      for (int w = 0; w < kThreads / 64; w++) t += wave_part[w];
-      partial[blockIdx.x] = t;
+      for (int w = 0; w < kThreads / 64; w++) t += wave_part[threadIdx.x][w];
+      partial[2 * blockIdx.x + threadIdx.x] = t;
     }
   }
 }
 
-// One workgroup: out = sum of partial[0..n) (strided per thread, then a
-// fixed tree over the workgroup). n == 0 writes 0.
+// One workgroup: out[j] = sum over i of partial[2i + j] for j = 0, 1
+// (strided per thread, then a fixed tree over the workgroup). n == 0 writes 0.
 __global__ __launch_bounds__(kThreads) void k_sum_partials(const double *__restrict__ partial,
                                                            int n, double *__restrict__ out) {
-  __shared__ double part[kThreads];
-  double t = 0.0;
-  for (int i = threadIdx.x; i < n; i += kThreads) t += partial[i];
-  part[threadIdx.x] = t;
+  __shared__ double part[2][kThreads];
+  double t0 = 0.0, t1 = 0.0;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    t0 += partial[2 * i];
+    t1 += partial[2 * i + 1];
+  }
+  part[0][threadIdx.x] = t0;
+  part[1][threadIdx.x] = t1;
   __syncthreads();
   for (int w = kThreads / 2; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    if ((int)threadIdx.x < w) {
+      part[0][threadIdx.x] += part[0][threadIdx.x + w];
+      part[1][threadIdx.x] += part[1][threadIdx.x + w];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) *out = part[0];
+  if (threadIdx.x < 2) out[threadIdx.x] = part[threadIdx.x][0];
+}
+
+// ---- MXFP8 (E4M3 elements) --------------------------------------------------
+//
+// Same blocks and lane layout; one code byte per element, so an item's 8
+// codes are two 32-bit words (8 bytes per lane, 512 contiguous bytes per
+// wave). Scale: floor(log2 amax) - 8 + 127 = exponent field - 8 (0 below),
+// 255 for NaN/Inf blocks. Elements use the gfx950 scaled FP8 converts
+// (v_cvt_scalef32_pk_fp8_{bf16,f32}: two values / 2^(s-127) -> two E4M3
+// bytes, first value in the low byte, nearest-even; v_cvt_scalef32_pk_
+// {bf16,f32}_fp8 back). These matched the oracle on every finite bf16 value
+// at every scale byte the rule produces, and every code byte at every scale
+// byte, with two differences handled here: the encode does not saturate
+// (values past the 448 midpoint become NaN), so elements are first clamped
+// to +-448 * 2^(s-127) (an unsigned min of the |x| bit patterns, which order
+// like the values); and NaN decodes carry the sign bit, so NaN outputs are
+// rewritten to the canonical quiet NaN.
+
+__device__ __forceinline__ uint32_t mxfp8_scale_byte(uint32_t amax_bits) {
+  if (amax_bits >= 0x7F800000u) return 255u;
+  const uint32_t e = amax_bits >> 23;
+  return e > 8u ? e - 8u : 0u;
+}
+
+// 8 E4M3 codes of the item at scale byte s (finite block), element i in
+// byte i of the pair of words.
+template <bool BF16>
+__device__ __forceinline__ u32x2 encode8_item(const Item<BF16> &x, uint32_t s) {
+  const float sc = scale_operand(s);
+  s16x2 w0 = {0, 0}, w1 = {0, 0};
+  if constexpr (BF16) {
+    // 448 * 2^(s-127) as bf16 bits (exponent field s + 8 <= 254 for finite input)
+    const uint32_t lim = ((s + 8u) << 7) | 0x60u;
+    const u16x2 lim2 = {(uint16_t)lim, (uint16_t)lim};
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const u16x2 a = __builtin_bit_cast(u16x2, x.w[j] & 0x7FFF7FFFu);
+      c[j] = (x.w[j] & 0x80008000u) | __builtin_bit_cast(uint32_t, __builtin_elementwise_min(a, lim2));
+    }
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(w0, __builtin_bit_cast(bf16x2, c[0]), sc, false);
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(w0, __builtin_bit_cast(bf16x2, c[1]), sc, true);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(w1, __builtin_bit_cast(bf16x2, c[2]), sc, false);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(w1, __builtin_bit_cast(bf16x2, c[3]), sc, true);
+  } else {
+    const float lim = __uint_as_float(((s + 8u) << 23) | 0x600000u);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) f[i] = __builtin_amdgcn_fmed3f(__uint_as_float(x.w[i]), -lim, lim);
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, f[0], f[1], sc, false);
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, f[2], f[3], sc, true);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, f[4], f[5], sc, false);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, f[6], f[7], sc, true);
+  }
+  return u32x2{__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1)};
+}
+
+// Codes of a NaN/Inf block: the sign bit alone, one byte per element.
+template <bool BF16>
+__device__ __forceinline__ u32x2 sign_codes8(const Item<BF16> &x) {
+  uint32_t b[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t sgn = BF16 ? (x.w[i >> 1] >> ((i & 1) ? 31 : 15)) & 1u : x.w[i] >> 31;
+    b[i >> 2] |= (sgn << 7) << (8 * (i & 3));
+  }
+  return u32x2{b[0], b[1]};
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t quantize8_item(const Item<BF16> &x, u32x2 &codes) {
+  const uint32_t s = mxfp8_scale_byte(quad_max_u32(item_amax_bits<BF16>(x)));
+  if (__builtin_expect(s == 255u, 0)) {
+    codes = sign_codes8<BF16>(x);
+    return s;
+  }
+  codes = encode8_item<BF16>(x, s);
+  return s;
+}
+
+// Decode 8 E4M3 codes at byte s into output words (bf16: 4, fp32: 8). NaN
+// codes and byte 255 give the canonical quiet NaN.
+template <bool BF16>
+__device__ __forceinline__ void decode8_item(u32x2 c, uint32_t s, uint32_t (&y)[BF16 ? 4 : 8]) {
+  const float sc = scale_operand(s);
+  if constexpr (BF16) {
+    y[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, false));
+    y[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, true));
+    y[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, false));
+    y[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, true));
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      // a NaN half (exponent all ones, mantissa non-zero) loses its sign bit
+      const u16x2 a = __builtin_bit_cast(u16x2, y[j] & 0x7FFF7FFFu);
+      const s16x2 nan = a > (u16x2){0x7F80, 0x7F80};  // lanes: -1 where NaN
+      const uint32_t keep = ~(__builtin_bit_cast(uint32_t, nan) & 0x80008000u);
+      y[j] &= keep;
+    }
+    if (__builtin_expect(s == 255u, 0)) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) y[j] = kNaN16x2;
+    }
+  } else {
+    f32x2 v[4];
+    v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[0], sc, false);
+    v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[0], sc, true);
+    v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[1], sc, false);
+    v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[1], sc, true);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      y[2 * j] = __float_as_uint(v[j].x);
+      y[2 * j + 1] = __float_as_uint(v[j].y);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if ((y[i] & 0x7FFFFFFFu) > 0x7F800000u) y[i] = kNaN32;
+    if (__builtin_expect(s == 255u, 0)) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) y[i] = kNaN32;
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_quantize8(const void *__restrict__ x,
+                                                        u32x2 *__restrict__ codes,
+                                                        uint8_t *__restrict__ scales,
+                                                        int64_t nitems) {
+  Item<BF16> xv[kUnroll];
+  tile_loop(
+      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t it) {
+        u32x2 c;
+        const uint32_t s = quantize8_item<BF16>(xv[u], c);
+        st<false>(codes + it, c);
+        if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)s);
+      });
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_dequantize8(const u32x2 *__restrict__ codes,
+                                                          const uint8_t *__restrict__ scales,
+                                                          void *__restrict__ y, int64_t nitems) {
+  u32x2 cw[kUnroll];
+  uint32_t sb[kUnroll];
+  tile_loop(
+      nitems,
+      [&](int u, int64_t it) {
+        cw[u] = ld<false>(codes + it);
+        sb[u] = ld<false>(scales + (it >> 2));
+      },
+      [&](int u, int64_t it) {
+        uint32_t out[BF16 ? 4 : 8];
+        decode8_item<BF16>(cw[u], sb[u], out);
+        store_item<BF16>(y, it, out);
+      });
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_fakequant8(const void *x, void *y, int64_t nitems) {
+  Item<BF16> xv[kUnroll];
+  tile_loop(
+      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t it) {
+        u32x2 c;
+        const uint32_t s = quantize8_item<BF16>(xv[u], c);
+        uint32_t out[BF16 ? 4 : 8];
+        decode8_item<BF16>(c, s, out);
+        store_item<BF16>(y, it, out);
+      });
 }
 
 // ---- launchers -----------------------------------------------------------------
@@ -468,20 +699,30 @@ static unsigned grid_for(int64_t nitems, int64_t cap) {
 
 using namespace mxk;
 
+#define MX_DISPATCH_MODE(KERNEL, BF16, MODE, G, B, ST, ...)                               \
+  switch (MODE) {                                                                          \
+    case MX_SCALE_OAS:                                                                     \
+      hipLaunchKernelGGL((KERNEL<BF16, MX_SCALE_OAS>), G, B, 0, ST, __VA_ARGS__);          \
+      break;                                                                               \
+    case MX_SCALE_OAS_BITS:                                                                \
+      hipLaunchKernelGGL((KERNEL<BF16, MX_SCALE_OAS_BITS>), G, B, 0, ST, __VA_ARGS__);     \
+      break;                                                                               \
+    case MX_SCALE_OAS_NF:                                                                  \
+      hipLaunchKernelGGL((KERNEL<BF16, MX_SCALE_OAS_NF>), G, B, 0, ST, __VA_ARGS__);       \
+      break;                                                                               \
+    default:                                                                               \
+      hipLaunchKernelGGL((KERNEL<BF16, MX_SCALE_OCP>), G, B, 0, ST, __VA_ARGS__);          \
+      break;                                                                               \
+  }
+
 hipError_t mxi_launch_quantize(const void *x, int bf16, int mode, int64_t nitems,
                                uint8_t *codes, uint8_t *scales, hipStream_t st) {
   const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
   if (bf16) {
-    if (mode == MX_SCALE_OAS)
-      hipLaunchKernelGGL((k_quantize<true, MX_SCALE_OAS>), g, b, 0, st, x, c, scales, nitems);
-    else
-      hipLaunchKernelGGL((k_quantize<true, MX_SCALE_OCP>), g, b, 0, st, x, c, scales, nitems);
+    MX_DISPATCH_MODE(k_quantize, true, mode, g, b, st, x, c, scales, nitems)
   } else {
-    if (mode == MX_SCALE_OAS)
-      hipLaunchKernelGGL((k_quantize<false, MX_SCALE_OAS>), g, b, 0, st, x, c, scales, nitems);
-    else
-      hipLaunchKernelGGL((k_quantize<false, MX_SCALE_OCP>), g, b, 0, st, x, c, scales, nitems);
+    MX_DISPATCH_MODE(k_quantize, false, mode, g, b, st, x, c, scales, nitems)
   }
   return hipGetLastError();
 }
@@ -490,15 +731,9 @@ hipError_t mxi_launch_fakequant(const void *x, int bf16, int mode, int64_t nitem
                                 hipStream_t st) {
   const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
   if (bf16) {
-    if (mode == MX_SCALE_OAS)
-      hipLaunchKernelGGL((k_fakequant<true, MX_SCALE_OAS>), g, b, 0, st, x, y, nitems);
-    else
-      hipLaunchKernelGGL((k_fakequant<true, MX_SCALE_OCP>), g, b, 0, st, x, y, nitems);
+    MX_DISPATCH_MODE(k_fakequant, true, mode, g, b, st, x, y, nitems)
   } else {
-    if (mode == MX_SCALE_OAS)
-      hipLaunchKernelGGL((k_fakequant<false, MX_SCALE_OAS>), g, b, 0, st, x, y, nitems);
-    else
-      hipLaunchKernelGGL((k_fakequant<false, MX_SCALE_OCP>), g, b, 0, st, x, y, nitems);
+    MX_DISPATCH_MODE(k_fakequant, false, mode, g, b, st, x, y, nitems)
   }
   return hipGetLastError();
 }
@@ -518,28 +753,70 @@ hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, in
 #define MX_MSE_GRID_CAP 2048
 #endif
 
-size_t mxi_block_mse_partials(int64_t nitems) { return grid_for(nitems, MX_MSE_GRID_CAP); }
+size_t mxi_block_mse_partials(int64_t nitems) { return 2 * grid_for(nitems, MX_MSE_GRID_CAP); }
 
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                                 const uint8_t *scales, int64_t nitems, float *block_mse,
-                                double *tensor_sse, double *partial, hipStream_t st) {
+                                double *tensor_sums, double *partial, hipStream_t st) {
   const unsigned grid = grid_for(nitems, MX_MSE_GRID_CAP);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
-  double *part = tensor_sse ? partial : nullptr;
+  double *part = tensor_sums ? partial : nullptr;
   if (nitems > 0) {
-    if (bf16)
-      hipLaunchKernelGGL((k_block_mse<true>), dim3(grid), dim3(kThreads), 0, st, x, c, scales,
-                         block_mse, part, nitems);
-    else
-      hipLaunchKernelGGL((k_block_mse<false>), dim3(grid), dim3(kThreads), 0, st, x, c, scales,
-                         block_mse, part, nitems);
+    const dim3 g(grid), b(kThreads);
+    if (bf16) {
+      if (part)
+        hipLaunchKernelGGL((k_block_mse<true, true>), g, b, 0, st, x, c, scales, block_mse, part,
+                           nitems);
+      else
+        hipLaunchKernelGGL((k_block_mse<true, false>), g, b, 0, st, x, c, scales, block_mse,
+                           part, nitems);
+    } else {
+      if (part)
+        hipLaunchKernelGGL((k_block_mse<false, true>), g, b, 0, st, x, c, scales, block_mse,
+                           part, nitems);
+      else
+        hipLaunchKernelGGL((k_block_mse<false, false>), g, b, 0, st, x, c, scales, block_mse,
+                           part, nitems);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (tensor_sse) {
+  if (tensor_sums) {
     hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kThreads), 0, st, partial,
-                       nitems > 0 ? (int)grid : 0, tensor_sse);
+                       nitems > 0 ? (int)grid : 0, tensor_sums);
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t nitems, uint8_t *codes,
+                                uint8_t *scales, hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  u32x2 *c = reinterpret_cast<u32x2 *>(codes);
+  if (bf16)
+    hipLaunchKernelGGL((k_quantize8<true>), g, b, 0, st, x, c, scales, nitems);
+  else
+    hipLaunchKernelGGL((k_quantize8<false>), g, b, 0, st, x, c, scales, nitems);
+  return hipGetLastError();
+}
+
+hipError_t mxi_launch_dequantize8(const uint8_t *codes, const uint8_t *scales, int bf16,
+                                  int64_t nitems, void *y, hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const u32x2 *c = reinterpret_cast<const u32x2 *>(codes);
+  if (bf16)
+    hipLaunchKernelGGL((k_dequantize8<true>), g, b, 0, st, c, scales, y, nitems);
+  else
+    hipLaunchKernelGGL((k_dequantize8<false>), g, b, 0, st, c, scales, y, nitems);
+  return hipGetLastError();
+}
+
+hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *y,
+                                 hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  if (bf16)
+    hipLaunchKernelGGL((k_fakequant8<true>), g, b, 0, st, x, y, nitems);
+  else
+    hipLaunchKernelGGL((k_fakequant8<false>), g, b, 0, st, x, y, nitems);
+  return hipGetLastError();
 }

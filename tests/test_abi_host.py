@@ -60,7 +60,7 @@ def test_bad_shapes(lib, rows, k):
 
 def test_bad_dtype_and_mode(lib):
     assert mx.mx_quantize(A, 2, 1, 32, 0, B, C, None) == mx.MX_ERR_DTYPE
-    assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, 2, B, C, None) == mx.MX_ERR_MODE
+    assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, 4, B, C, None) == mx.MX_ERR_MODE
     assert mx.mx_quantize(A, mx.MX_BF16, 1, 32, -1, B, C, None) == mx.MX_ERR_MODE
     assert mx.mx_dequantize(B, C, 1, 32, 7, A, None) == mx.MX_ERR_DTYPE
     assert mx.mx_fakequant(A, -1, 1, 32, 0, B, None) == mx.MX_ERR_DTYPE
@@ -120,8 +120,8 @@ def test_aliasing(lib):
 
 def test_workspace(lib):
     need = mx.mx_block_mse_workspace_size(8192, 4096)
-    assert 8 <= need <= 16384 and need % 8 == 0
-    assert mx.mx_block_mse_workspace_size(0, 64) >= 8
+    assert 16 <= need <= 32768 and need % 16 == 0
+    assert mx.mx_block_mse_workspace_size(0, 64) >= 16
     # missing / small / misaligned workspace when the tensor sum is asked for
     assert mx.mx_block_mse(A, 1, B, C, 8192, 4096, None, W, None, 0, None) == mx.MX_ERR_WORKSPACE
     assert mx.mx_block_mse(A, 1, B, C, 8192, 4096, None, W, W + 64, need - 8, None) == \
@@ -147,3 +147,20 @@ def test_missing_library_fails_loudly(tmp_path):
             mx.load_library(str(tmp_path / "nope.so"))
     finally:
         mx._lib = saved
+
+
+def test_mxfp8_validation(lib):
+    assert mx.mx_quantize_mxfp8(A, 3, 1, 32, B, C, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_quantize_mxfp8(A, 1, 1, 48, B, C, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_quantize_mxfp8(None, 1, 1, 32, B, C, None) == mx.MX_ERR_NULL
+    assert mx.mx_quantize_mxfp8(A, 1, 1, 32, B + 8, C, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_quantize_mxfp8(A, 1, 0, 32, None, None, None) == mx.MX_OK
+    # codes are one byte per element: [rows, k]; a codes buffer starting
+    # inside x overlaps
+    assert mx.mx_quantize_mxfp8(A, 1, 4, 64, A + 256, C, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_quantize_mxfp8(A, 1, 4, 64, B, B + 128, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_dequantize_mxfp8(B, C, 1, 32, 9, A, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_dequantize_mxfp8(B, C, 4, 64, 0, B + 16, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_dequantize_mxfp8(B, C, -1, 64, 0, A, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_fakequant_mxfp8(A, 0, 4, 64, A + 16, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_fakequant_mxfp8(A, 0, 1, 32, None, None) == mx.MX_ERR_NULL

@@ -19,7 +19,7 @@ import microscaling_fp4_block_mx_amd as mx
 pytestmark = pytest.mark.gpu
 
 THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
-MODES = ("ocp", "oas")
+MODES = ("ocp", "oas", "oas_bits", "oas_nf")
 
 
 def say(msg):
@@ -77,17 +77,20 @@ def check_all_ops(x: torch.Tensor, label: str, modes=MODES, mse=True):
         assert_same_bits(y, oracle.fakequant(xh, mode, threads=THREADS),
                          f"{label} fakequant {mode}")
         if mse:
-            bm, sse = mx.block_mse(xd, c, s)
-            wbm, wsse = oracle.block_mse(xh, wc, ws, threads=THREADS)
+            bm, sums = mx.block_mse(xd, c, s)
+            wbm, wsse, wssq = oracle.block_mse(xh, wc, ws, threads=THREADS, with_energy=True)
             g = bm.cpu().numpy()
             np.testing.assert_array_equal(np.isnan(g), np.isnan(wbm))
             ok = ~np.isnan(wbm)
             np.testing.assert_allclose(g[ok], wbm[ok], rtol=1e-6, atol=0)
-            got = sse.item()
-            if np.isnan(wsse):
-                assert np.isnan(got)
-            else:
-                assert abs(got - wsse) <= 1e-6 * abs(wsse), (got, wsse)
+            got, got_sq = sums.tolist()
+            for a, b in ((got, wsse), (got_sq, wssq)):
+                if np.isnan(b):
+                    assert np.isnan(a)
+                elif np.isinf(b):
+                    assert a == b
+                else:
+                    assert abs(a - b) <= 1e-6 * abs(b), (a, b)
 
 
 # ---- exhaustive and special inputs ----------------------------------------
@@ -122,6 +125,36 @@ def test_fp32_subnormal_and_wide_range():
     check_all_ops(torch.from_numpy(x), "wide-f32")
 
 
+def test_oas_tie_prone_blocks():
+    """Blocks where the overflow-aware choices go both ways (and tie), so
+    both the evaluated and the bounded-out branch of the kernel run."""
+    x = workloads.oas_tie_prone_blocks(26, 200_000)
+    _, s0 = oracle.quantize(x, "ocp", threads=THREADS)
+    for mode in ("oas", "oas_nf"):
+        _, ws = oracle.quantize(x, mode, threads=THREADS)
+        assert (ws != s0).sum() > 1000  # the other candidate wins in many blocks
+    modes = ("oas", "oas_bits", "oas_nf")
+    check_all_ops(torch.from_numpy(x), "oas-tie-prone-f32", modes=modes)
+    check_all_ops(torch.from_numpy(x).to(torch.bfloat16), "oas-tie-prone-bf16", modes=modes)
+
+
+def test_page_modes_near_scale_ceiling():
+    """Block maxima near the largest finite values: the page modes cap the
+    scale byte at 252 and never decode to Inf."""
+    f = np.float32
+    top = [np.finfo(np.float32).max, f(7.9) * f(2.0 ** 125), f(6.5) * f(2.0 ** 125),
+           f(7.01) * f(2.0 ** 125), f(5.0) * f(2.0 ** 125), f(7.5) * f(2.0 ** -127),
+           f(6.5) * f(2.0 ** -127)]
+    rng = np.random.default_rng(27)
+    x = (rng.standard_normal((len(top), 64)) * 0.1).astype(np.float32)
+    for i, t in enumerate(top):
+        x[i] *= t
+        x[i, 3] = t
+    check_all_ops(torch.from_numpy(x), "near-ceiling-f32")
+    y = mx.fakequant(torch.from_numpy(x).cuda(), "oas_bits")
+    assert torch.isfinite(y).all()
+
+
 def test_dequantize_every_scale_byte():
     """Random codes at every scale byte 0..255 (253/254 overflow, 255 NaN)."""
     rng = np.random.default_rng(22)
@@ -133,7 +166,7 @@ def test_dequantize_every_scale_byte():
         assert_same_bits(y, oracle.dequantize(codes, scales, name), f"dequant-all-s {name}")
     # block error against user-made scales, including Inf / NaN reconstructions
     x = torch.from_numpy(rng.standard_normal((256, 128)).astype(np.float32))
-    bm, sse = mx.block_mse(x.cuda(), cd, sd)
+    bm, _ = mx.block_mse(x.cuda(), cd, sd)
     wbm, _ = oracle.block_mse(x.numpy(), codes, scales)
     g = bm.cpu().numpy()
     np.testing.assert_array_equal(np.isnan(g), np.isnan(wbm))
@@ -164,8 +197,8 @@ def test_leading_dims_and_empty():
     c, s = mx.quantize(e)
     assert c.shape == (0, 32) and s.shape == (0, 2)
     assert mx.fakequant(e).shape == (0, 64)
-    _, sse = mx.block_mse(e, c, s)
-    assert sse.item() == 0.0
+    _, sums = mx.block_mse(e, c, s)
+    assert sums.tolist() == [0.0, 0.0]
 
 
 def test_bad_arguments_raise_on_gpu():
@@ -207,22 +240,25 @@ def test_bf16_8192x4096_student_t_fakequant_full():
     check_all_ops(x, "student-t", modes=("ocp",))
 
 
-def test_bf16_16384x8192_laplace_ocp_and_oas_full():
+def test_bf16_16384x8192_laplace_all_modes_full():
     x = workloads.bf16_laplace_sparse_outliers(5)
     xh = host_view(x)
     xd = x.cuda()
-    mse = {}
+    mse, qsnr = {}, {}
     for mode in MODES:
         say(f"laplace quantize {mode}")
         c, s = mx.quantize(xd, mode)
         wc, ws = oracle.quantize(xh, mode, threads=THREADS)
         assert_same_bits(s, ws, f"laplace scales {mode}")
         assert_same_bits(c, wc, f"laplace codes {mode}")
-        _, sse = mx.block_mse(xd, c, s, per_block=False)
-        _, wsse = oracle.block_mse(xh, wc, ws, threads=THREADS)
-        assert abs(sse.item() - wsse) <= 1e-6 * wsse
-        mse[mode] = sse.item() / x.numel()
-    say(f"laplace tensor MSE ocp={mse['ocp']:.6g} oas={mse['oas']:.6g}")
+        _, sums = mx.block_mse(xd, c, s, per_block=False)
+        _, wsse, wssq = oracle.block_mse(xh, wc, ws, threads=THREADS, with_energy=True)
+        sse, ssq = sums.tolist()
+        assert abs(sse - wsse) <= 1e-6 * wsse and abs(ssq - wssq) <= 1e-6 * wssq
+        mse[mode] = sse / x.numel()
+        qsnr[mode] = 10 * np.log10(ssq / sse)
+    say("laplace tensor MSE " + " ".join(f"{m}={mse[m]:.6g}" for m in MODES))
+    say("laplace QSNR dB " + " ".join(f"{m}={qsnr[m]:.4f}" for m in MODES))
     assert mse["oas"] <= mse["ocp"] * (1 + 1e-9)
 
 
@@ -291,9 +327,10 @@ def test_deterministic():
         c1, s1 = mx.quantize(x, mode)
         c2, s2 = mx.quantize(x, mode)
         assert torch.equal(c1, c2) and torch.equal(s1, s2)
-        b1, _ = mx.block_mse(x, c1, s1)
-        b2, _ = mx.block_mse(x, c1, s1)
+        b1, t1 = mx.block_mse(x, c1, s1)
+        b2, t2 = mx.block_mse(x, c1, s1)
         assert torch.equal(b1.view(torch.int32), b2.view(torch.int32))
+        assert torch.equal(t1.view(torch.int64), t2.view(torch.int64))
 
 
 def test_side_stream():
