@@ -81,6 +81,14 @@ def _load():
         lib.mxref8_encode.restype = i32
         lib.mxref8_decode.argtypes = [i32, i32]
         lib.mxref8_decode.restype = ctypes.c_double
+        lib.mxrefnv_quantize.argtypes = [p, i32, i64, i64, p, p, p]
+        lib.mxrefnv_quantize.restype = i32
+        lib.mxrefnv_dequantize.argtypes = [p, p, i32, i64, i64, i32, p]
+        lib.mxrefnv_dequantize.restype = i32
+        lib.mxrefnv_tensor_exp.argtypes = [ctypes.c_double]
+        lib.mxrefnv_tensor_exp.restype = i32
+        lib.mxrefnv_decode.argtypes = [i32, i32, i32]
+        lib.mxrefnv_decode.restype = ctypes.c_double
         _lib = lib
     return _lib
 
@@ -238,3 +246,40 @@ def encode_e4m3(x: float, scale_byte: int) -> int:
 
 def decode_e4m3(code: int, scale_byte: int) -> float:
     return _load().mxref8_decode(int(code), int(scale_byte))
+
+
+# --- NVFP4 comparator (16-element blocks, E4M3 block scales) ---------------
+
+def quantize_nvfp4(x: np.ndarray):
+    """Return (codes uint8 [..., k/2], block_scales uint8 [..., k/16] (E4M3),
+    tensor_scale int (byte t + 127 of the factor 2^t))."""
+    x = np.ascontiguousarray(x)
+    rows, k = _shape2(x)
+    codes = np.empty(x.shape[:-1] + (k // 2,), np.uint8)
+    bs = np.empty(x.shape[:-1] + (k // 16,), np.uint8)
+    ts = np.zeros(1, np.uint8)
+    rc = _load().mxrefnv_quantize(_ptr(x), _dtype_code(x), rows, k, _ptr(codes), _ptr(bs), _ptr(ts))
+    if rc == -2:
+        raise ValueError("last dim must be a positive multiple of 16")
+    _check(rc)
+    return codes, bs, int(ts[0])
+
+
+def dequantize_nvfp4(codes: np.ndarray, block_scales: np.ndarray, tensor_scale: int,
+                     dtype: str = "bf16") -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    bs = np.ascontiguousarray(block_scales, dtype=np.uint8)
+    k = codes.shape[-1] * 2
+    rows = int(np.prod(codes.shape[:-1])) if codes.ndim > 1 else 1
+    y = np.empty(codes.shape[:-1] + (k,), np.float32 if dtype == "f32" else np.uint16)
+    _check(_load().mxrefnv_dequantize(_ptr(codes), _ptr(bs), int(tensor_scale), rows, k,
+                                      F32 if dtype == "f32" else BF16, _ptr(y)))
+    return y
+
+
+def nvfp4_tensor_exp(amax: float) -> int:
+    return _load().mxrefnv_tensor_exp(float(amax))
+
+
+def nvfp4_decode(code: int, block_scale: int, tensor_scale: int) -> float:
+    return _load().mxrefnv_decode(int(code), int(block_scale), int(tensor_scale))

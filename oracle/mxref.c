@@ -537,3 +537,121 @@ int mxref8_fakequant(const void *x, int dtype, int64_t rows, int64_t k, void *y,
   j.op = 2; j.x = x; j.dtype = dtype; j.k = k; j.y = y;
   return run8(j, rows, threads);
 }
+
+/* ======================================================================
+ * NVFP4 comparator ("Unveiling the Potential of Quantization with MXFP4",
+ * technical summary section 1: NVFP4 shares one scale per 16 elements and
+ * stores it as E4M3, i.e. with mantissa bits; Axolotl MXFP4 PR page: NVFP4
+ * uses group size 16). Readings where the pages stop:
+ *  - elements E2M1 as for MXFP4, two codes per byte, even element low;
+ *  - a per-tensor power of two S = 2^t, the largest with S * amax <= 6 * 448,
+ *    keeps the block scales inside E4M3's range; it is stored as the byte
+ *    t + 127 (clamped to [0, 254]); amax over finite elements, S = 1 if 0;
+ *  - block scale: E4M3 nearest-even of min((a_b / 6) * S, 448) in fp32 (the
+ *    division by 6 rounded to fp32 first);
+ *  - element code: nearest-even E2M1 (saturating) of x * r_b in fp32 with
+ *    r_b = S / s_b rounded to fp32 (0 when s_b == 0);
+ *  - decode: (E2M1 value * s_b) / S, exact before the output rounding;
+ *  - a block holding NaN/Inf gets block scale 0x7F (E4M3 NaN) and sign-only
+ *    codes, and decodes to NaN.
+ * ====================================================================== */
+
+#define NVB 16
+
+/* t of the tensor factor S = 2^t: the largest t with 2^t * amax <= 2688. */
+int mxrefnv_tensor_exp(double amax) {
+  if (amax == 0.0) return 0;
+  int t = 127;
+  while (t > -127 && ldexp(amax, t) > 2688.0) t--;
+  return t;
+}
+
+/* E2M1 code of float v (already divided by the block scale): nearest, ties
+ * to the even code, saturating; computed with the MXFP4 encoder at scale 1. */
+static int e2m1_code(float v) { return mxref_encode((double)v, 127); }
+
+static int e4m3_code_nonneg(float t) {
+  double v = t;
+  if (v >= 448.0) return 0x7E;
+  int lo = 0;
+  while (lo < 126 && e4m3_value(lo + 1) <= v) lo++;
+  int hi = lo + 1;
+  double mid = 0.5 * (e4m3_value(lo) + e4m3_value(hi));
+  if (v < mid) return lo;
+  if (v > mid) return hi;
+  return (lo % 2 == 0) ? lo : hi;
+}
+
+int mxrefnv_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
+                     uint8_t *block_scales, uint8_t *tensor_scale) {
+  if (rows < 0 || k <= 0 || k % NVB != 0) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (rows == 0) {
+    if (tensor_scale) *tensor_scale = 127;
+    return 0;
+  }
+  if (!x || !codes || !block_scales || !tensor_scale) return -1;
+  unsigned int csr = enter_ieee();
+  const int64_t n = rows * k;
+  double amax = 0.0;
+  for (int64_t i = 0; i < n; i++) {
+    double v = load_elem(x, dtype, i);
+    if (!isnan(v) && !isinf(v) && fabs(v) > amax) amax = fabs(v);
+  }
+  int t = mxrefnv_tensor_exp(amax);
+  *tensor_scale = (uint8_t)(t + 127);
+  const float S = (float)ldexp(1.0, t);
+  for (int64_t b = 0; b < n / NVB; b++) {
+    double xb[NVB], ab = 0.0;
+    int nonfinite = 0;
+    for (int i = 0; i < NVB; i++) {
+      xb[i] = load_elem(x, dtype, b * NVB + i);
+      if (isnan(xb[i]) || isinf(xb[i])) nonfinite = 1;
+      else if (fabs(xb[i]) > ab) ab = fabs(xb[i]);
+    }
+    int code[NVB];
+    if (nonfinite) {
+      block_scales[b] = 0x7F;
+      for (int i = 0; i < NVB; i++) code[i] = signbit(xb[i]) ? 8 : 0;
+    } else {
+      float q6 = (float)ab / 6.0f; /* fp32 division */
+      float tb = q6 * S;           /* exact: power of two, no overflow */
+      int sc = e4m3_code_nonneg(tb);
+      block_scales[b] = (uint8_t)sc;
+      float sv = (float)e4m3_value(sc);
+      float r = sv > 0.0f ? S / sv : 0.0f; /* fp32 division */
+      for (int i = 0; i < NVB; i++) {
+        float v = (float)xb[i] * r; /* fp32 multiply */
+        code[i] = (signbit(xb[i]) ? 8 : 0) | (e2m1_code(fabsf(v)) & 7);
+      }
+    }
+    for (int tt = 0; tt < NVB / 2; tt++)
+      codes[b * (NVB / 2) + tt] = (uint8_t)(code[2 * tt] | (code[2 * tt + 1] << 4));
+  }
+  leave_ieee(csr);
+  return 0;
+}
+
+double mxrefnv_decode(int code, int block_scale, int tensor_scale) {
+  if ((block_scale & 0x7F) == 0x7F) return NAN;
+  double v = kGrid[code & 7] * e4m3_value(block_scale & 0x7F) * ldexp(1.0, -(tensor_scale - 127));
+  if (block_scale & 0x80) v = -v; /* sign of the scale byte (never set by the quantizer) */
+  return (code & 8) ? -v : v;
+}
+
+int mxrefnv_dequantize(const uint8_t *codes, const uint8_t *block_scales, int tensor_scale,
+                       int64_t rows, int64_t k, int dtype, void *y) {
+  if (rows < 0 || k <= 0 || k % NVB != 0) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (rows == 0) return 0;
+  if (!codes || !block_scales || !y) return -1;
+  unsigned int csr = enter_ieee();
+  const int64_t n = rows * k;
+  for (int64_t i = 0; i < n; i++) {
+    uint8_t byte = codes[i / 2];
+    int c = (i % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+    store_elem(y, dtype, i, mxrefnv_decode(c, block_scales[i / NVB], tensor_scale));
+  }
+  leave_ieee(csr);
+  return 0;
+}

@@ -54,6 +54,16 @@ int mxref8_scale(double amax);
 int mxref8_encode(double x, int scale_byte);
 double mxref8_decode(int code, int scale_byte);
 
+/* NVFP4 comparator: 16-element blocks with E4M3 block scales and a per-tensor
+ * power-of-two factor 2^t stored as the byte t + 127. codes [rows, k/2],
+ * block_scales [rows, k/16] (E4M3 bytes), k % 16 == 0. Single-threaded. */
+int mxrefnv_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
+                     uint8_t *block_scales, uint8_t *tensor_scale);
+int mxrefnv_dequantize(const uint8_t *codes, const uint8_t *block_scales, int tensor_scale,
+                       int64_t rows, int64_t k, int dtype, void *y);
+int mxrefnv_tensor_exp(double amax);
+double mxrefnv_decode(int code, int block_scale, int tensor_scale);
+
 #ifdef __cplusplus
 }
 #endif
