@@ -46,6 +46,9 @@ EXTRA_BYTES_PER_ELEM = {
     "quantize_mxfp8": 2 + 1 + 1 / 32,
     "dequantize_mxfp8_bf16": 1 + 1 / 32 + 2,
     "fakequant_mxfp8": 4.0,
+    # NVFP4 comparator: quantize reads x twice (tensor maximum, then blocks)
+    "quantize_nvfp4": 2 + 2 + 0.5 + 1 / 16,
+    "dequantize_nvfp4_bf16": 0.5 + 1 / 16 + 2,
 }
 KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0>", "quantize_oas": "k_quantize<true, 1>",
              "dequantize_bf16": "k_dequantize<true>", "fakequant_ocp": "k_fakequant<true, 0>",
@@ -108,7 +111,7 @@ def main():
     x_host = workloads.bf16_student_t_outlier_channels(2)
     R_, K_ = x_host.shape
     n = x_host.numel()
-    per_set = n * (2 + 0.5 * 2 + 2 / 32 + 2 + 2 + 4 / 32 + 1 + 1 / 32)
+    per_set = n * (2 + 0.5 * 2 + 2 / 32 + 2 + 2 + 4 / 32 + 1 + 1 / 32 + 1 / 16)
     n_sets = max(2, int(np.ceil(args.rotate_gib * 2 ** 30 / per_set)))
 
     x0 = x_host.to(dev)
@@ -125,11 +128,15 @@ def main():
             bm=torch.empty((R_, K_ // 32), dtype=torch.float32, device=dev),
             c8=torch.empty((R_, K_), dtype=torch.uint8, device=dev),
             s8=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
+            bnv=torch.empty((R_, K_ // 16), dtype=torch.uint8, device=dev),
+            tnv=torch.full((1,), 127, dtype=torch.uint8, device=dev),
         ))
     del x0
     sums = torch.empty(2, dtype=torch.float64, device=dev)
     ws_bytes = mx.mx_block_mse_workspace_size(R_, K_)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsnv_bytes = mx.mx_nvfp4_workspace_size(R_, K_)
+    wsnv = torch.empty(wsnv_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
@@ -159,6 +166,14 @@ def main():
         elif op == "fakequant_mxfp8":
             st = mx.mx_fakequant_mxfp8(b["x"].data_ptr(), mx.MX_BF16, R_, K_,
                                        b["y_fq"].data_ptr(), sh)
+        elif op == "quantize_nvfp4":
+            st = mx.mx_quantize_nvfp4(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["c_oas"].data_ptr(),
+                                      b["bnv"].data_ptr(), b["tnv"].data_ptr(), wsnv.data_ptr(),
+                                      wsnv_bytes, sh)
+        elif op == "dequantize_nvfp4_bf16":
+            st = mx.mx_dequantize_nvfp4(b["c_oas"].data_ptr(), b["bnv"].data_ptr(),
+                                        b["tnv"].data_ptr(), R_, K_, mx.MX_BF16,
+                                        b["y_dq"].data_ptr(), sh)
         elif op in ("fakequant_oas", "fakequant_oas_nf"):
             mode = mx.MX_SCALE_OAS if op == "fakequant_oas" else mx.MX_SCALE_OAS_NF
             st = mx.mx_fakequant(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mode,
@@ -195,8 +210,9 @@ def main():
 
     # per-kernel launch time: each op alone, back to back over the rotating
     # sets, K * n_sets launches between two events on the same stream
-    for i in range(n_sets):  # codes for the MXFP8 dequantize
+    for i in range(n_sets):  # codes for the MXFP8 / NVFP4 dequantize
         run("quantize_mxfp8", sets[i])
+        run("quantize_nvfp4", sets[i])
     op_ms = {}
     for op in OPS + list(EXTRA_BYTES_PER_ELEM):
         for i in range(n_sets):
@@ -261,7 +277,12 @@ def main():
     sse8 = float(((xf - y8).double() ** 2).sum())
     quality["mxfp8"] = {"mse": sse8 / n,
                         "qsnr_db": round(10 * np.log10(float((xf.double() ** 2).sum()) / sse8), 4)}
-    del y8, xf
+    cn, bn, tn = mx.quantize_nvfp4(b["x"])
+    ynv = mx.dequantize_nvfp4(cn, bn, tn, torch.float32)
+    ssenv = float(((xf - ynv).double() ** 2).sum())
+    quality["nvfp4"] = {"mse": ssenv / n,
+                        "qsnr_db": round(10 * np.log10(float((xf.double() ** 2).sum()) / ssenv), 4)}
+    del y8, xf, ynv
 
     cpu = None
     if not args.no_cpu_baseline:

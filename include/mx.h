@@ -172,6 +172,34 @@ mx_status_t mx_dequantize_mxfp8(const uint8_t *codes, const uint8_t *scales,
 mx_status_t mx_fakequant_mxfp8(const void *x, mx_dtype_t dtype, int64_t rows,
                                int64_t k, void *y, void *stream);
 
+/* ---- NVFP4 comparator ---------------------------------------------------------
+ * For comparisons with the format MXFP4 is measured against ("Unveiling the
+ * Potential of Quantization with MXFP4", technical summary section 1: NVFP4
+ * shares one scale per 16 elements, stored as E4M3). Elements E2M1, codes
+ * uint8 [rows, k/2] (two per byte, even element low); block scales uint8
+ * [rows, k/16] as E4M3 bytes; k must be a multiple of 16. A per-tensor
+ * factor S = 2^t, the largest power of two with S * amax <= 6 * 448 (amax:
+ * largest finite |x|; t = 0 when it is 0; t <= 127), keeps the block scales
+ * inside E4M3; one device byte tensor_scale holds t + 127. Block scale:
+ * E4M3 nearest-even of min((a_b / 6) * S, 448) (fp32 division by 6);
+ * element: E2M1 nearest-even, saturating, of x * (S / s_b) in fp32 (the
+ * factor by IEEE fp32 division; 0 when s_b is 0). Decoding gives
+ * (E2M1 * s_b) / S exactly, then rounds to bf16 if asked. A block holding
+ * NaN/Inf gets block scale 0x7F and sign-only codes and decodes to NaN.
+ * Quantize reads x twice (tensor maximum, then the blocks) and needs a
+ * workspace of mx_nvfp4_workspace_size(rows, k) bytes (4-byte aligned).
+ * rows == 0 does nothing. Other conventions as above. */
+size_t mx_nvfp4_workspace_size(int64_t rows, int64_t k);
+mx_status_t mx_quantize_nvfp4(const void *x, mx_dtype_t x_dtype, int64_t rows,
+                              int64_t k, uint8_t *codes, uint8_t *block_scales,
+                              uint8_t *tensor_scale, void *workspace,
+                              size_t workspace_bytes, void *stream);
+mx_status_t mx_dequantize_nvfp4(const uint8_t *codes,
+                                const uint8_t *block_scales,
+                                const uint8_t *tensor_scale, int64_t rows,
+                                int64_t k, mx_dtype_t y_dtype, void *y,
+                                void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *mx_status_string(mx_status_t s);
 

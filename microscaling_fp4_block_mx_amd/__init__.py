@@ -37,7 +37,8 @@ MODES = tuple(_MODES)
 _DTYPES = {torch.float32: MX_F32, torch.bfloat16: MX_BF16}
 EXPORTS = ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
            "mx_block_mse_workspace_size", "mx_quantize_mxfp8", "mx_dequantize_mxfp8",
-           "mx_fakequant_mxfp8", "mx_status_string", "mx_last_error_detail")
+           "mx_fakequant_mxfp8", "mx_nvfp4_workspace_size", "mx_quantize_nvfp4",
+           "mx_dequantize_nvfp4", "mx_status_string", "mx_last_error_detail")
 
 _lib = None
 
@@ -61,8 +62,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mx_quantize_mxfp8.argtypes = [p, i32, i64, i64, p, p, p]
     lib.mx_dequantize_mxfp8.argtypes = [p, p, i64, i64, i32, p, p]
     lib.mx_fakequant_mxfp8.argtypes = [p, i32, i64, i64, p, p]
+    lib.mx_nvfp4_workspace_size.argtypes = [i64, i64]
+    lib.mx_nvfp4_workspace_size.restype = ctypes.c_size_t
+    lib.mx_quantize_nvfp4.argtypes = [p, i32, i64, i64, p, p, p, p, ctypes.c_size_t, p]
+    lib.mx_dequantize_nvfp4.argtypes = [p, p, p, i64, i64, i32, p, p]
     for f in ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
-              "mx_quantize_mxfp8", "mx_dequantize_mxfp8", "mx_fakequant_mxfp8"):
+              "mx_quantize_mxfp8", "mx_dequantize_mxfp8", "mx_fakequant_mxfp8",
+              "mx_quantize_nvfp4", "mx_dequantize_nvfp4"):
         getattr(lib, f).restype = i32
     lib.mx_status_string.argtypes = [i32]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -106,6 +112,21 @@ def mx_dequantize_mxfp8(codes, scales, rows, k, y_dtype, y, stream) -> int:
 
 def mx_fakequant_mxfp8(x, dtype, rows, k, y, stream) -> int:
     return load_library().mx_fakequant_mxfp8(x, dtype, rows, k, y, stream)
+
+
+def mx_nvfp4_workspace_size(rows, k) -> int:
+    return load_library().mx_nvfp4_workspace_size(rows, k)
+
+
+def mx_quantize_nvfp4(x, x_dtype, rows, k, codes, block_scales, tensor_scale, workspace,
+                      workspace_bytes, stream) -> int:
+    return load_library().mx_quantize_nvfp4(x, x_dtype, rows, k, codes, block_scales,
+                                            tensor_scale, workspace, workspace_bytes, stream)
+
+
+def mx_dequantize_nvfp4(codes, block_scales, tensor_scale, rows, k, y_dtype, y, stream) -> int:
+    return load_library().mx_dequantize_nvfp4(codes, block_scales, tensor_scale, rows, k,
+                                              y_dtype, y, stream)
 
 
 def mx_status_string(status: int) -> str:
@@ -275,3 +296,46 @@ def fakequant_mxfp8(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.T
         _raise(mx_fakequant_mxfp8(x.data_ptr(), _DTYPES[x.dtype], rows, k, out.data_ptr(),
                                   _stream(x.device)))
     return out
+
+
+# ---- NVFP4 comparator tensor helpers -----------------------------------------
+
+def quantize_nvfp4(x: torch.Tensor):
+    """x [..., k] (k % 16 == 0) -> (codes uint8 [..., k/2], block_scales uint8
+    [..., k/16] (E4M3 bytes), tensor_scale uint8 GPU tensor [1] (t + 127))."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype not in _DTYPES:
+        raise ValueError("need a float32/bfloat16 GPU tensor")
+    if x.dim() == 0 or not x.is_contiguous():
+        raise ValueError("need a contiguous tensor with at least one dimension")
+    k = x.shape[-1]
+    if k <= 0 or k % 16:
+        raise ValueError("NVFP4 needs the last dimension to be a multiple of 16")
+    rows = x.numel() // k if x.numel() else 0
+    codes = torch.empty(tuple(x.shape[:-1]) + (k // 2,), dtype=torch.uint8, device=x.device)
+    bs = torch.empty(tuple(x.shape[:-1]) + (k // 16,), dtype=torch.uint8, device=x.device)
+    ts = torch.full((1,), 127, dtype=torch.uint8, device=x.device)
+    wsb = mx_nvfp4_workspace_size(rows, k)
+    ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _raise(mx_quantize_nvfp4(x.data_ptr(), _DTYPES[x.dtype], rows, k, codes.data_ptr(),
+                                 bs.data_ptr(), ts.data_ptr(), ws.data_ptr(), wsb,
+                                 _stream(x.device)))
+    return codes, bs, ts
+
+
+def dequantize_nvfp4(codes: torch.Tensor, block_scales: torch.Tensor, tensor_scale: torch.Tensor,
+                     dtype=torch.bfloat16) -> torch.Tensor:
+    if not codes.is_cuda or codes.dtype != torch.uint8 or block_scales.dtype != torch.uint8:
+        raise ValueError("codes and block scales must be uint8 GPU tensors")
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
+    k = codes.shape[-1] * 2
+    rows = codes.numel() // (k // 2) if codes.numel() else 0
+    if block_scales.numel() * 16 != codes.numel() * 2:
+        raise ValueError("block scales do not match codes")
+    y = torch.empty(tuple(codes.shape[:-1]) + (k,), dtype=dtype, device=codes.device)
+    with torch.cuda.device(codes.device):
+        _raise(mx_dequantize_nvfp4(codes.data_ptr(), block_scales.data_ptr(),
+                                   tensor_scale.data_ptr(), rows, k, _DTYPES[dtype], y.data_ptr(),
+                                   _stream(codes.device)))
+    return y

@@ -24,6 +24,12 @@ mx_status_t check_shape(int64_t rows, int64_t k) {
   return MX_OK;
 }
 
+mx_status_t check_shape16(int64_t rows, int64_t k) {
+  if (rows < 0 || k <= 0 || k % 16 != 0) return MX_ERR_SHAPE;
+  if (rows > 0 && k > (INT64_MAX / 8) / rows) return MX_ERR_SHAPE;
+  return MX_OK;
+}
+
 bool dtype_ok(int d) { return d == MX_F32 || d == MX_BF16; }
 bool mode_ok(int m) { return m >= MX_SCALE_OCP && m <= MX_SCALE_OAS_NF; }
 int64_t elem_bytes(int d) { return d == MX_F32 ? 4 : 2; }
@@ -181,6 +187,53 @@ mx_status_t mx_fakequant_mxfp8(const void *x, mx_dtype_t dtype, int64_t rows, in
   if (x != y && overlap(x, nb, y, nb)) return MX_ERR_ALIAS;
   return finish(mxi_launch_fakequant8(x, dtype == MX_BF16, rows * k / 8, y,
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t mx_nvfp4_workspace_size(int64_t rows, int64_t k) {
+  if (check_shape16(rows, k) != MX_OK) return 0;
+  const size_t n = mxi_nvfp4_partials(rows * k / 8);
+  return (n > 0 ? n : 1) * sizeof(uint32_t);
+}
+
+mx_status_t mx_quantize_nvfp4(const void *x, mx_dtype_t x_dtype, int64_t rows, int64_t k,
+                              uint8_t *codes, uint8_t *block_scales, uint8_t *tensor_scale,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape16(rows, k)) return s;
+  if (rows == 0) return MX_OK;
+  if (!x || !codes || !block_scales || !tensor_scale) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(block_scales)) return MX_ERR_ALIGN;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 ||
+      workspace_bytes < mx_nvfp4_workspace_size(rows, k))
+    return MX_ERR_WORKSPACE;
+  const int64_t n = rows * k;
+  const int64_t nx = n * elem_bytes(x_dtype), nw = (int64_t)workspace_bytes;
+  if (overlap(x, nx, codes, n / 2) || overlap(x, nx, block_scales, n / 16) ||
+      overlap(codes, n / 2, block_scales, n / 16) || overlap(tensor_scale, 1, x, nx) ||
+      overlap(tensor_scale, 1, codes, n / 2) || overlap(tensor_scale, 1, block_scales, n / 16) ||
+      overlap(workspace, nw, x, nx) || overlap(workspace, nw, codes, n / 2) ||
+      overlap(workspace, nw, block_scales, n / 16) || overlap(workspace, nw, tensor_scale, 1))
+    return MX_ERR_ALIAS;
+  return finish(mxi_launch_quantize_nv(x, x_dtype == MX_BF16, n / 8, codes, block_scales,
+                                       tensor_scale, static_cast<uint32_t *>(workspace),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_dequantize_nvfp4(const uint8_t *codes, const uint8_t *block_scales,
+                                const uint8_t *tensor_scale, int64_t rows, int64_t k,
+                                mx_dtype_t y_dtype, void *y, void *stream) {
+  if (!dtype_ok(y_dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape16(rows, k)) return s;
+  if (rows == 0) return MX_OK;
+  if (!codes || !block_scales || !tensor_scale || !y) return MX_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(block_scales) || !aligned16(y)) return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  const int64_t ny = n * elem_bytes(y_dtype);
+  if (overlap(y, ny, codes, n / 2) || overlap(y, ny, block_scales, n / 16) ||
+      overlap(y, ny, tensor_scale, 1))
+    return MX_ERR_ALIAS;
+  return finish(mxi_launch_dequantize_nv(codes, block_scales, tensor_scale, y_dtype == MX_BF16,
+                                         n / 8, y, static_cast<hipStream_t>(stream)));
 }
 
 const char *mx_status_string(mx_status_t s) {

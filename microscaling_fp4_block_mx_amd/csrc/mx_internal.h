@@ -26,4 +26,12 @@ hipError_t mxi_launch_dequantize8(const uint8_t *codes, const uint8_t *scales, i
                                   int64_t nitems, void *y, hipStream_t st);
 hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *y,
                                  hipStream_t st);
+// NVFP4 comparator (nitems = rows * k / 8, even).
+size_t mxi_nvfp4_partials(int64_t nitems);
+hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t nitems, uint8_t *codes,
+                                  uint8_t *block_scales, uint8_t *tensor_scale,
+                                  uint32_t *partial, hipStream_t st);
+hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_scales,
+                                    const uint8_t *tensor_scale, int bf16, int64_t nitems, void *y,
+                                    hipStream_t st);
 #endif

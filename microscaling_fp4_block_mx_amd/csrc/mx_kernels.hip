@@ -685,6 +685,155 @@ __global__ __launch_bounds__(kThreads) void k_fakequant8(const void *x, void *y,
       });
 }
 
+// ---- NVFP4 comparator (16-element blocks, E4M3 block scales) ----------------
+//
+// Two lanes per 16-element block (an item is half a block); the pair's max
+// is one DPP step. A per-tensor power of two S = 2^t, the largest with
+// S * amax <= 2688 (6 * 448), keeps the block scales inside E4M3; amax is
+// the largest finite |x| of the tensor (first pass, per-workgroup maxima).
+// Block scale: E4M3 nearest-even of min((a_b / 6) * S, 448) (IEEE fp32
+// division, exact power-of-two product); element: nearest-even E2M1,
+// saturating, of x * (S / s_b) in fp32 (IEEE division for the reciprocal
+// factor). E4M3 and E2M1 rounding use the scaled converts at scale 1.
+
+// Largest finite |x| bit pattern of the item (non-finite lanes count as 0).
+template <bool BF16>
+__device__ __forceinline__ uint32_t item_finite_amax_bits(const Item<BF16> &x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t a = __float_as_uint(elem<BF16>(x, i)) & 0x7FFFFFFFu;
+    m = max(m, a < 0x7F800000u ? a : 0u);
+  }
+  return m;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_absmax_partials(const void *__restrict__ x,
+                                                              uint32_t *__restrict__ partial,
+                                                              int64_t nitems) {
+  __shared__ uint32_t wave_max[kThreads / 64];
+  uint32_t m = 0;
+  Item<BF16> xv[kUnroll];
+  tile_loop(
+      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t) { m = max(m, item_finite_amax_bits<BF16>(xv[u])); });
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kThreads / 64; w++) t = max(t, wave_max[w]);
+    partial[blockIdx.x] = t;
+  }
+}
+
+// t of S = 2^t from the tensor amax bits: with amax = (1 + f) 2^(e - 127),
+// 2^t * amax <= 1.3125 * 2^11 gives t = 138 - e when 1 + f <= 1.3125
+// (mantissa field <= 0x280000), else 137 - e; capped at 127 (tiny or
+// subnormal amax); amax == 0 gives t = 0.
+__device__ __forceinline__ int nv_tensor_exp(uint32_t amax_bits) {
+  if (amax_bits == 0u) return 0;
+  const int e = (int)(amax_bits >> 23);
+  const int t = (e == 0) ? 127 : ((amax_bits & 0x7FFFFFu) <= 0x280000u ? 138 - e : 137 - e);
+  return t > 127 ? 127 : t;
+}
+
+__device__ __forceinline__ uint32_t dpp_x1_max(uint32_t v) { return max(v, dpp_x1(v)); }
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *__restrict__ x,
+                                                          const uint32_t *__restrict__ partial,
+                                                          int npartial,
+                                                          uint32_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ block_scales,
+                                                          uint8_t *__restrict__ tensor_scale,
+                                                          int64_t nitems) {
+  // every workgroup reduces the first pass's maxima (order-free)
+  __shared__ uint32_t red[kThreads];
+  uint32_t a = 0;
+  for (int i = threadIdx.x; i < npartial; i += kThreads) a = max(a, partial[i]);
+  red[threadIdx.x] = a;
+  __syncthreads();
+  for (int w = kThreads / 2; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const int t = nv_tensor_exp(red[0]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = (uint8_t)(t + 127);
+  const float S = __uint_as_float((uint32_t)(t + 127) << 23);
+  const float one = 1.0f;  // scale operand of the converts: 2^0
+
+  Item<BF16> xv[kUnroll];
+  tile_loop(
+      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t it) {
+        const uint32_t ab = dpp_x1_max(item_amax_bits<BF16>(xv[u]));  // NaN/Inf sort above
+        uint32_t c;
+        uint32_t sbyte;
+        if (__builtin_expect(ab >= 0x7F800000u, 0)) {
+          sbyte = 0x7Fu;
+          c = sign_codes<BF16>(xv[u]);
+        } else {
+          const float q6 = __uint_as_float(ab) / 6.0f;
+          const float tb = fminf(q6 * S, 448.0f);
+          s16x2 w = {0, 0};
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, tb, tb, one, false);
+          sbyte = (uint32_t)w[0] & 0xFFu;
+          const float sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sbyte, one, false)[0];
+          const float r = sv > 0.0f ? S / sv : 0.0f;
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) v[i] = elem<BF16>(xv[u], i) * r;
+          c = 0;
+          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[0], v[1], one, 0);
+          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[2], v[3], one, 1);
+          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[4], v[5], one, 2);
+          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[6], v[7], one, 3);
+        }
+        st<false>(codes + it, c);
+        if ((threadIdx.x & 1) == 0) st<false>(block_scales + (it >> 1), (uint8_t)sbyte);
+      });
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_dequantize_nv(const uint32_t *__restrict__ codes,
+                                                            const uint8_t *__restrict__ block_scales,
+                                                            const uint8_t *__restrict__ tensor_scale,
+                                                            void *__restrict__ y, int64_t nitems) {
+  const int t = (int)*tensor_scale - 127;
+  const float inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t, scale operand
+  const float one = 1.0f;
+  uint32_t cw[kUnroll], sb[kUnroll];
+  tile_loop(
+      nitems,
+      [&](int u, int64_t it) {
+        cw[u] = ld<false>(codes + it);
+        sb[u] = ld<false>(block_scales + (it >> 1));
+      },
+      [&](int u, int64_t it) {
+        // s_b * 2^-t exactly (E4M3 decode with a power-of-two scale)
+        const float sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb[u], inv_s, false)[0];
+        float q[8];
+        decode_f32(cw[u], 127u, q);  // E2M1 values at scale 1
+        uint32_t out[BF16 ? 4 : 8];
+        const bool nan = (sb[u] & 0x7Fu) == 0x7Fu;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+            const b2 p = {(__bf16)(q[2 * j] * sv), (__bf16)(q[2 * j + 1] * sv)};
+            out[j] = nan ? kNaN16x2 : __builtin_bit_cast(uint32_t, p);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; i++) out[i] = nan ? kNaN32 : __float_as_uint(q[i] * sv);
+        }
+        store_item<BF16>(y, it, out);
+      });
+}
+
 // ---- launchers -----------------------------------------------------------------
 
 static unsigned grid_for(int64_t nitems, int64_t cap) {
@@ -818,5 +967,43 @@ hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *
     hipLaunchKernelGGL((k_fakequant8<true>), g, b, 0, st, x, y, nitems);
   else
     hipLaunchKernelGGL((k_fakequant8<false>), g, b, 0, st, x, y, nitems);
+  return hipGetLastError();
+}
+
+#ifndef MX_NV_GRID_CAP
+#define MX_NV_GRID_CAP 2048
+#endif
+
+size_t mxi_nvfp4_partials(int64_t nitems) { return grid_for(nitems, MX_NV_GRID_CAP); }
+
+hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t nitems, uint8_t *codes,
+                                  uint8_t *block_scales, uint8_t *tensor_scale,
+                                  uint32_t *partial, hipStream_t st) {
+  const unsigned gp = grid_for(nitems, MX_NV_GRID_CAP);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  uint32_t *c = reinterpret_cast<uint32_t *>(codes);
+  if (bf16) {
+    hipLaunchKernelGGL((k_absmax_partials<true>), dim3(gp), b, 0, st, x, partial, nitems);
+    hipLaunchKernelGGL((k_quantize_nv<true>), g, b, 0, st, x, partial, (int)gp, c, block_scales,
+                       tensor_scale, nitems);
+  } else {
+    hipLaunchKernelGGL((k_absmax_partials<false>), dim3(gp), b, 0, st, x, partial, nitems);
+    hipLaunchKernelGGL((k_quantize_nv<false>), g, b, 0, st, x, partial, (int)gp, c, block_scales,
+                       tensor_scale, nitems);
+  }
+  return hipGetLastError();
+}
+
+hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_scales,
+                                    const uint8_t *tensor_scale, int bf16, int64_t nitems, void *y,
+                                    hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
+  if (bf16)
+    hipLaunchKernelGGL((k_dequantize_nv<true>), g, b, 0, st, c, block_scales, tensor_scale, y,
+                       nitems);
+  else
+    hipLaunchKernelGGL((k_dequantize_nv<false>), g, b, 0, st, c, block_scales, tensor_scale, y,
+                       nitems);
   return hipGetLastError();
 }

@@ -164,3 +164,20 @@ def test_mxfp8_validation(lib):
     assert mx.mx_dequantize_mxfp8(B, C, -1, 64, 0, A, None) == mx.MX_ERR_SHAPE
     assert mx.mx_fakequant_mxfp8(A, 0, 4, 64, A + 16, None) == mx.MX_ERR_ALIAS
     assert mx.mx_fakequant_mxfp8(A, 0, 1, 32, None, None) == mx.MX_ERR_NULL
+
+
+def test_nvfp4_validation(lib):
+    need = mx.mx_nvfp4_workspace_size(8192, 4096)
+    assert 4 <= need <= 8192 * 4 and need % 4 == 0
+    assert mx.mx_nvfp4_workspace_size(1, 24) == 0
+    assert mx.mx_quantize_nvfp4(A, 1, 1, 24, B, C, W, W + 64, 64, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_quantize_nvfp4(A, 1, 0, 16, None, None, None, None, 0, None) == mx.MX_OK
+    assert mx.mx_quantize_nvfp4(A, 1, 1, 16, B, C, None, W + 64, 64, None) == mx.MX_ERR_NULL
+    assert mx.mx_quantize_nvfp4(A, 1, 1, 16, B, C, W, None, 0, None) == mx.MX_ERR_WORKSPACE
+    assert mx.mx_quantize_nvfp4(A, 1, 1, 16, B, C, W, W + 66, 64, None) == mx.MX_ERR_WORKSPACE
+    assert mx.mx_quantize_nvfp4(A, 1, 4, 64, B, C, A + 3, W + 64, 64, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_quantize_nvfp4(A, 1, 4, 64, B, B + 64, W, W + 64, 64, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_quantize_nvfp4(A, 4, 1, 16, B, C, W, W + 64, 64, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_dequantize_nvfp4(B, C, W, 1, 16, 0, None, None) == mx.MX_ERR_NULL
+    assert mx.mx_dequantize_nvfp4(B, C, W, 4, 64, 0, B + 32, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_dequantize_nvfp4(B, C, W, 1, 16, 0, A + 8, None) == mx.MX_ERR_ALIGN
