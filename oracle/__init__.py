@@ -89,6 +89,12 @@ def _load():
         lib.mxrefnv_tensor_exp.restype = i32
         lib.mxrefnv_decode.argtypes = [i32, i32, i32]
         lib.mxrefnv_decode.restype = ctypes.c_double
+        lib.mxrefmbs_quantize.argtypes = [p, i32, i64, i64, p, p, p]
+        lib.mxrefmbs_quantize.restype = i32
+        lib.mxrefmbs_dequantize.argtypes = [p, p, p, i64, i64, i32, p]
+        lib.mxrefmbs_dequantize.restype = i32
+        lib.mxrefmbs_macro_mantissa.argtypes = [ctypes.c_double]
+        lib.mxrefmbs_macro_mantissa.restype = i32
         _lib = lib
     return _lib
 
@@ -283,3 +289,35 @@ def nvfp4_tensor_exp(amax: float) -> int:
 
 def nvfp4_decode(code: int, block_scale: int, tensor_scale: int) -> float:
     return _load().mxrefnv_decode(int(code), int(block_scale), int(tensor_scale))
+
+
+# --- MBS-Static (16-element sub-blocks, 8-bit-mantissa macro factor) --------
+
+def quantize_mbs(x: np.ndarray):
+    """Return (codes [..., k/2], sub_scales [..., k/16] (E8M0 bytes),
+    macro_mant [..., k/128] (factor 1 + m/256))."""
+    x = np.ascontiguousarray(x)
+    rows, k = _shape2(x)
+    codes = np.empty(x.shape[:-1] + (k // 2,), np.uint8)
+    ss = np.empty(x.shape[:-1] + (k // 16,), np.uint8)
+    mm = np.empty(x.shape[:-1] + (k // 128,), np.uint8)
+    rc = _load().mxrefmbs_quantize(_ptr(x), _dtype_code(x), rows, k, _ptr(codes), _ptr(ss), _ptr(mm))
+    if rc == -2:
+        raise ValueError("last dim must be a positive multiple of 128")
+    _check(rc)
+    return codes, ss, mm
+
+
+def dequantize_mbs(codes, sub_scales, macro_mant, dtype: str = "bf16") -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    k = codes.shape[-1] * 2
+    rows = int(np.prod(codes.shape[:-1])) if codes.ndim > 1 else 1
+    y = np.empty(codes.shape[:-1] + (k,), np.float32 if dtype == "f32" else np.uint16)
+    _check(_load().mxrefmbs_dequantize(_ptr(codes), _ptr(np.ascontiguousarray(sub_scales, np.uint8)),
+                                       _ptr(np.ascontiguousarray(macro_mant, np.uint8)), rows, k,
+                                       F32 if dtype == "f32" else BF16, _ptr(y)))
+    return y
+
+
+def mbs_macro_mantissa(amax: float) -> int:
+    return _load().mxrefmbs_macro_mantissa(float(amax))

@@ -655,3 +655,93 @@ int mxrefnv_dequantize(const uint8_t *codes, const uint8_t *block_scales, int te
   leave_ieee(csr);
   return 0;
 }
+
+/* ======================================================================
+ * MBS-Static ("Unveiling the Potential of Quantization with MXFP4",
+ * technical summary section 2.B): MXFP4 quantization on 16-element base
+ * blocks, whose power-of-two scales are corrected by a high-precision
+ * factor with an 8-bit mantissa shared by each 128-element macro block;
+ * the static variant computes that factor by a cheap approximation.
+ * Readings where the page stops:
+ *  - macro factor f = 1 + m/256, m = the 8-bit mantissa of r = a_M / 6
+ *    (a_M = largest |x| of the macro block, division in fp32), rounded to
+ *    nearest even and capped at 255; m = 0 when a_M == 0. It carries the
+ *    part of a_M / 6 that a power of two cannot.
+ *  - y = fl32(x * fl32(1 / f)); each 16-element sub-block takes the OCP
+ *    byte of its largest |y| (floor(log2) - 2 + 127, clamped; 255 if it
+ *    holds NaN/Inf), and each element the E2M1 code of y at that byte.
+ *  - decode: E2M1 * 2^(s-127) * f, exact before the output rounding.
+ * Storage: codes [rows, k/2], sub-block bytes [rows, k/16], macro mantissas
+ * [rows, k/128]; k % 128 == 0.
+ * ====================================================================== */
+
+int mxrefmbs_macro_mantissa(double amax) {
+  if (amax == 0.0 || isnan(amax) || isinf(amax)) return 0;
+  float r = (float)amax / 6.0f; /* fp32 division */
+  int e;
+  double f = 2.0 * frexp((double)r, &e); /* [1, 2), exact */
+  double t = (f - 1.0) * 256.0;          /* exact */
+  double m = nearbyint(t);               /* round half even (default mode) */
+  if (m > 255.0) m = 255.0;
+  return (int)m;
+}
+
+int mxrefmbs_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
+                      uint8_t *sub_scales, uint8_t *macro_mant) {
+  if (rows < 0 || k <= 0 || k % 128 != 0) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (rows == 0) return 0;
+  if (!x || !codes || !sub_scales || !macro_mant) return -1;
+  unsigned int csr = enter_ieee();
+  const int64_t n = rows * k;
+  for (int64_t M = 0; M < n / 128; M++) {
+    double xm[128], aM = 0.0;
+    int nonfinite_macro = 0;
+    for (int i = 0; i < 128; i++) {
+      xm[i] = load_elem(x, dtype, M * 128 + i);
+      if (isnan(xm[i]) || isinf(xm[i])) nonfinite_macro = 1;
+      else if (fabs(xm[i]) > aM) aM = fabs(xm[i]);
+    }
+    int m = nonfinite_macro ? 0 : mxrefmbs_macro_mantissa(aM);
+    macro_mant[M] = (uint8_t)m;
+    const float f = 1.0f + (float)m / 256.0f;
+    const float inv = 1.0f / f; /* fp32 division */
+    for (int j = 0; j < 8; j++) {
+      float y[16];
+      double ay = 0.0;
+      int nonfinite = 0;
+      for (int i = 0; i < 16; i++) {
+        double v = xm[16 * j + i];
+        if (isnan(v) || isinf(v)) nonfinite = 1;
+        y[i] = (float)v * inv; /* fp32 multiply */
+        if (!isnan(y[i]) && fabs((double)y[i]) > ay) ay = fabs((double)y[i]);
+      }
+      int s = nonfinite ? 255 : mxref_ocp_scale(ay);
+      sub_scales[M * 8 + j] = (uint8_t)s;
+      int c[16];
+      for (int i = 0; i < 16; i++) c[i] = mxref_encode((double)y[i], s);
+      for (int t = 0; t < 8; t++)
+        codes[(M * 128 + 16 * j) / 2 + t] = (uint8_t)(c[2 * t] | (c[2 * t + 1] << 4));
+    }
+  }
+  leave_ieee(csr);
+  return 0;
+}
+
+int mxrefmbs_dequantize(const uint8_t *codes, const uint8_t *sub_scales,
+                        const uint8_t *macro_mant, int64_t rows, int64_t k, int dtype, void *y) {
+  if (rows < 0 || k <= 0 || k % 128 != 0) return -2;
+  if (dtype != MXREF_F32 && dtype != MXREF_BF16) return -3;
+  if (rows == 0) return 0;
+  if (!codes || !sub_scales || !macro_mant || !y) return -1;
+  unsigned int csr = enter_ieee();
+  const int64_t n = rows * k;
+  for (int64_t i = 0; i < n; i++) {
+    uint8_t byte = codes[i / 2];
+    int c = (i % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+    double f = 1.0 + macro_mant[i / 128] / 256.0;
+    store_elem(y, dtype, i, mxref_decode(c, sub_scales[i / 16]) * f);
+  }
+  leave_ieee(csr);
+  return 0;
+}

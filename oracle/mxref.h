@@ -64,6 +64,15 @@ int mxrefnv_dequantize(const uint8_t *codes, const uint8_t *block_scales, int te
 int mxrefnv_tensor_exp(double amax);
 double mxrefnv_decode(int code, int block_scale, int tensor_scale);
 
+/* MBS-Static: 16-element E8M0 sub-blocks corrected by an 8-bit-mantissa
+ * factor per 128-element macro block. codes [rows, k/2], sub_scales
+ * [rows, k/16], macro_mant [rows, k/128]; k % 128 == 0. Single-threaded. */
+int mxrefmbs_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
+                      uint8_t *sub_scales, uint8_t *macro_mant);
+int mxrefmbs_dequantize(const uint8_t *codes, const uint8_t *sub_scales,
+                        const uint8_t *macro_mant, int64_t rows, int64_t k, int dtype, void *y);
+int mxrefmbs_macro_mantissa(double amax);
+
 #ifdef __cplusplus
 }
 #endif
