@@ -719,7 +719,8 @@ int mxrefmbs_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t
       int s = nonfinite ? 255 : mxref_ocp_scale(ay);
       sub_scales[M * 8 + j] = (uint8_t)s;
       int c[16];
-      for (int i = 0; i < 16; i++) c[i] = mxref_encode((double)y[i], s);
+      for (int i = 0; i < 16; i++)  /* a NaN/Inf sub-block keeps the signs of x */
+        c[i] = (s == 255) ? (signbit(xm[16 * j + i]) ? 8 : 0) : mxref_encode((double)y[i], s);
       for (int t = 0; t < 8; t++)
         codes[(M * 128 + 16 * j) / 2 + t] = (uint8_t)(c[2 * t] | (c[2 * t + 1] << 4));
     }

@@ -105,6 +105,16 @@ def test_special_values_and_bf16(oracle_lib):
     assert s[0, 0] == 255 and s[0, 4] != 255
     y = oracle_lib.dequantize_mbs(c, s, m, "f32")
     assert (y[0, :16].view(np.uint32) == 0x7FC00000).all()
+    # a NaN/Inf sub-block stores only the signs of its inputs (as an MXFP4
+    # block with a NaN scale does), NaN signs included
+    x2 = np.zeros((1, 128), np.float32)
+    x2[0, 2], x2[0, 3], x2[0, 9] = -1.0, -np.inf, 5.0
+    x2.view(np.uint32)[0, 5] = 0xFFC00000  # -NaN
+    x2[0, 11] = -0.0
+    c2, s2, m2 = oracle_lib.quantize_mbs(x2)
+    assert s2[0, 0] == 255 and m2[0, 0] == 0
+    nib = np.stack([c2[0, :8] & 15, c2[0, :8] >> 4], 1).reshape(-1)
+    np.testing.assert_array_equal(nib, np.where(np.signbit(x2[0, :16]), 8, 0))
     xb = workloads.to_bf16_bits(torch.from_numpy(x[1:]).to(torch.bfloat16))
     cb, sb, mb = oracle_lib.quantize_mbs(xb)
     np.testing.assert_array_equal(oracle_lib.dequantize_mbs(cb, sb, mb, "bf16"),
