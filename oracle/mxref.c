@@ -678,6 +678,7 @@ int mxrefnv_dequantize(const uint8_t *codes, const uint8_t *block_scales, int te
 int mxrefmbs_macro_mantissa(double amax) {
   if (amax == 0.0 || isnan(amax) || isinf(amax)) return 0;
   float r = (float)amax / 6.0f; /* fp32 division */
+  if (r == 0.0f) return 0;      /* a_M / 6 underflows: no mantissa, factor 1 */
   int e;
   double f = 2.0 * frexp((double)r, &e); /* [1, 2), exact */
   double t = (f - 1.0) * 256.0;          /* exact */

@@ -32,6 +32,25 @@ def test_macro_mantissa_closed_form(oracle_lib):
     # above 1 + 255.5/256 the rounding would carry; capped at 255
     assert oracle_lib.mbs_macro_mantissa(6 * (1 + 255.75 / 256)) == 255
     assert oracle_lib.mbs_macro_mantissa(0.0) == 0
+    # a_M / 6 below half the smallest fp32 subnormal rounds to zero: factor 1
+    for n in (1, 2, 3):
+        assert oracle_lib.mbs_macro_mantissa(n * 2.0 ** -149) == 0
+    # 4 * 2^-149 / 6 rounds to 2^-149 = 1.0 * 2^-149: mantissa 0 as well
+    assert oracle_lib.mbs_macro_mantissa(4 * 2.0 ** -149) == 0
+    # 7 * 2^-149 / 6 rounds to 2^-149 too; 9 * 2^-149 / 6 -> 2 * 2^-149 (tie, even)
+    assert oracle_lib.mbs_macro_mantissa(7 * 2.0 ** -149) == 0
+    assert oracle_lib.mbs_macro_mantissa(9 * 2.0 ** -149) == 0
+    # 1.25 * 2^-140 * 6 is exact: subnormal a_M / 6 keeps its mantissa
+    assert oracle_lib.mbs_macro_mantissa(6 * 1.25 * 2.0 ** -140) == 64
+    x = np.zeros((1, 128), np.float32)
+    x.view(np.uint32)[0, 0] = 3  # 3 * 2^-149
+    x.view(np.uint32)[0, 1] = 0x80000001  # -2^-149
+    c, s, m = oracle_lib.quantize_mbs(x)
+    assert m[0, 0] == 0 and s[0, 0] == 0
+    y = oracle_lib.dequantize_mbs(c, s, m, "f32")
+    assert np.isfinite(y).all()
+    # at byte 0 the grid step is 2^-128, so both round to zero (signs kept)
+    assert (y[0, :2] == 0).all() and np.signbit(y[0, 1]) and not np.signbit(y[0, 0])
 
 
 def _rederive(x: np.ndarray):
