@@ -49,6 +49,9 @@ EXTRA_BYTES_PER_ELEM = {
     # NVFP4 comparator: quantize reads x twice (tensor maximum, then blocks)
     "quantize_nvfp4": 2 + 2 + 0.5 + 1 / 16,
     "dequantize_nvfp4_bf16": 0.5 + 1 / 16 + 2,
+    # MBS-Static: 16-element sub-block bytes plus one macro byte per 128
+    "quantize_mbs": 2 + 0.5 + 1 / 16 + 1 / 128,
+    "dequantize_mbs_bf16": 0.5 + 1 / 16 + 1 / 128 + 2,
 }
 KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0>", "quantize_oas": "k_quantize<true, 1>",
              "dequantize_bf16": "k_dequantize<true>", "fakequant_ocp": "k_fakequant<true, 0>",
@@ -111,7 +114,7 @@ def main():
     x_host = workloads.bf16_student_t_outlier_channels(2)
     R_, K_ = x_host.shape
     n = x_host.numel()
-    per_set = n * (2 + 0.5 * 2 + 2 / 32 + 2 + 2 + 4 / 32 + 1 + 1 / 32 + 1 / 16)
+    per_set = n * (2 + 0.5 * 2 + 2 / 32 + 2 + 2 + 4 / 32 + 1 + 1 / 32 + 1 / 16 + 1 / 16 + 1 / 128)
     n_sets = max(2, int(np.ceil(args.rotate_gib * 2 ** 30 / per_set)))
 
     x0 = x_host.to(dev)
@@ -130,6 +133,8 @@ def main():
             s8=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
             bnv=torch.empty((R_, K_ // 16), dtype=torch.uint8, device=dev),
             tnv=torch.full((1,), 127, dtype=torch.uint8, device=dev),
+            smb=torch.empty((R_, K_ // 16), dtype=torch.uint8, device=dev),
+            mmb=torch.empty((R_, K_ // 128), dtype=torch.uint8, device=dev),
         ))
     del x0
     sums = torch.empty(2, dtype=torch.float64, device=dev)
@@ -174,6 +179,13 @@ def main():
             st = mx.mx_dequantize_nvfp4(b["c_oas"].data_ptr(), b["bnv"].data_ptr(),
                                         b["tnv"].data_ptr(), R_, K_, mx.MX_BF16,
                                         b["y_dq"].data_ptr(), sh)
+        elif op == "quantize_mbs":  # codes land in c_oas; dequantize_mbs_bf16 runs next
+            st = mx.mx_quantize_mbs(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["c_oas"].data_ptr(),
+                                    b["smb"].data_ptr(), b["mmb"].data_ptr(), sh)
+        elif op == "dequantize_mbs_bf16":
+            st = mx.mx_dequantize_mbs(b["c_oas"].data_ptr(), b["smb"].data_ptr(),
+                                      b["mmb"].data_ptr(), R_, K_, mx.MX_BF16,
+                                      b["y_dq"].data_ptr(), sh)
         elif op in ("fakequant_oas", "fakequant_oas_nf"):
             mode = mx.MX_SCALE_OAS if op == "fakequant_oas" else mx.MX_SCALE_OAS_NF
             st = mx.mx_fakequant(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mode,
@@ -282,7 +294,12 @@ def main():
     ssenv = float(((xf - ynv).double() ** 2).sum())
     quality["nvfp4"] = {"mse": ssenv / n,
                         "qsnr_db": round(10 * np.log10(float((xf.double() ** 2).sum()) / ssenv), 4)}
-    del y8, xf, ynv
+    cm, sm, mm = mx.quantize_mbs(b["x"])
+    ymb = mx.dequantize_mbs(cm, sm, mm, torch.float32)
+    ssemb = float(((xf - ymb).double() ** 2).sum())
+    quality["mbs_static"] = {"mse": ssemb / n,
+                             "qsnr_db": round(10 * np.log10(float((xf.double() ** 2).sum()) / ssemb), 4)}
+    del y8, xf, ynv, ymb
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
   MX_OK = 0,
   MX_ERR_NULL = 1,   /* a required pointer is NULL                          */
-  MX_ERR_SHAPE = 2,  /* rows < 0, k <= 0, k % 32 != 0, or rows*k overflows   */
+  MX_ERR_SHAPE = 2,  /* rows < 0, k <= 0, k not a multiple of the block, or rows*k overflows */
   MX_ERR_DTYPE = 3,  /* dtype is not MX_F32 / MX_BF16                        */
   MX_ERR_MODE = 4,   /* mode is not an mx_scale_mode_t value                 */
   MX_ERR_ALIGN = 5,  /* a data pointer is not 16-byte aligned                */
@@ -199,6 +199,32 @@ mx_status_t mx_dequantize_nvfp4(const uint8_t *codes,
                                 const uint8_t *tensor_scale, int64_t rows,
                                 int64_t k, mx_dtype_t y_dtype, void *y,
                                 void *stream);
+
+/* ---- MBS-Static ------------------------------------------------------------
+ * "Unveiling the Potential of Quantization with MXFP4", technical summary
+ * section 2.B (Macro Block Scaling): E2M1 elements with one E8M0 scale per
+ * 16-element sub-block, corrected by an 8-bit mantissa factor per
+ * 128-element macro block; k must be a multiple of 128. Layouts: codes
+ * uint8 [rows, k/2] (two per byte, even element low), sub_scales uint8
+ * [rows, k/16] (E8M0 bytes), macro_mant uint8 [rows, k/128]. Per macro
+ * block with largest |x| a_M: m = the 8-bit mantissa of fl32(a_M / 6)
+ * rounded to nearest even and capped at 255 (0 for a zero or non-finite
+ * macro block, or where a_M / 6 underflows to zero); f = 1 + m/256;
+ * y = fl32(x * fl32(1/f)). Each sub-block takes the OCP byte of its largest
+ * |y| (floor(log2) - 2 + 127, clamped at 0) and the E2M1 codes of y at that
+ * byte (nearest, ties even, saturating at 6); a sub-block holding NaN/Inf
+ * gets byte 255 and the signs of x as codes. Decoding gives
+ * E2M1 * 2^(s-127) * f exactly, rounded to bf16 if asked; byte 255 decodes
+ * to the canonical quiet NaN. rows == 0 does nothing; same pointer,
+ * alignment (all four arrays 16-byte aligned), aliasing and error
+ * conventions as the MXFP4 entry points. */
+mx_status_t mx_quantize_mbs(const void *x, mx_dtype_t x_dtype, int64_t rows,
+                            int64_t k, uint8_t *codes, uint8_t *sub_scales,
+                            uint8_t *macro_mant, void *stream);
+mx_status_t mx_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
+                              const uint8_t *macro_mant, int64_t rows,
+                              int64_t k, mx_dtype_t y_dtype, void *y,
+                              void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *mx_status_string(mx_status_t s);

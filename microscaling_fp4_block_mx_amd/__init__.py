@@ -38,7 +38,8 @@ _DTYPES = {torch.float32: MX_F32, torch.bfloat16: MX_BF16}
 EXPORTS = ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
            "mx_block_mse_workspace_size", "mx_quantize_mxfp8", "mx_dequantize_mxfp8",
            "mx_fakequant_mxfp8", "mx_nvfp4_workspace_size", "mx_quantize_nvfp4",
-           "mx_dequantize_nvfp4", "mx_status_string", "mx_last_error_detail")
+           "mx_dequantize_nvfp4", "mx_quantize_mbs", "mx_dequantize_mbs", "mx_status_string",
+           "mx_last_error_detail")
 
 _lib = None
 
@@ -66,9 +67,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mx_nvfp4_workspace_size.restype = ctypes.c_size_t
     lib.mx_quantize_nvfp4.argtypes = [p, i32, i64, i64, p, p, p, p, ctypes.c_size_t, p]
     lib.mx_dequantize_nvfp4.argtypes = [p, p, p, i64, i64, i32, p, p]
+    lib.mx_quantize_mbs.argtypes = [p, i32, i64, i64, p, p, p, p]
+    lib.mx_dequantize_mbs.argtypes = [p, p, p, i64, i64, i32, p, p]
     for f in ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
               "mx_quantize_mxfp8", "mx_dequantize_mxfp8", "mx_fakequant_mxfp8",
-              "mx_quantize_nvfp4", "mx_dequantize_nvfp4"):
+              "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_quantize_mbs",
+              "mx_dequantize_mbs"):
         getattr(lib, f).restype = i32
     lib.mx_status_string.argtypes = [i32]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -127,6 +131,16 @@ def mx_quantize_nvfp4(x, x_dtype, rows, k, codes, block_scales, tensor_scale, wo
 def mx_dequantize_nvfp4(codes, block_scales, tensor_scale, rows, k, y_dtype, y, stream) -> int:
     return load_library().mx_dequantize_nvfp4(codes, block_scales, tensor_scale, rows, k,
                                               y_dtype, y, stream)
+
+
+def mx_quantize_mbs(x, x_dtype, rows, k, codes, sub_scales, macro_mant, stream) -> int:
+    return load_library().mx_quantize_mbs(x, x_dtype, rows, k, codes, sub_scales, macro_mant,
+                                          stream)
+
+
+def mx_dequantize_mbs(codes, sub_scales, macro_mant, rows, k, y_dtype, y, stream) -> int:
+    return load_library().mx_dequantize_mbs(codes, sub_scales, macro_mant, rows, k, y_dtype, y,
+                                            stream)
 
 
 def mx_status_string(status: int) -> str:
@@ -338,4 +352,46 @@ def dequantize_nvfp4(codes: torch.Tensor, block_scales: torch.Tensor, tensor_sca
         _raise(mx_dequantize_nvfp4(codes.data_ptr(), block_scales.data_ptr(),
                                    tensor_scale.data_ptr(), rows, k, _DTYPES[dtype], y.data_ptr(),
                                    _stream(codes.device)))
+    return y
+
+
+# ---- MBS-Static tensor helpers ------------------------------------------------
+
+def quantize_mbs(x: torch.Tensor):
+    """x [..., k] (k % 128 == 0) -> (codes uint8 [..., k/2], sub_scales uint8
+    [..., k/16] (E8M0 bytes), macro_mant uint8 [..., k/128])."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype not in _DTYPES:
+        raise ValueError("need a float32/bfloat16 GPU tensor")
+    if x.dim() == 0 or not x.is_contiguous():
+        raise ValueError("need a contiguous tensor with at least one dimension")
+    k = x.shape[-1]
+    if k <= 0 or k % 128:
+        raise ValueError("MBS-Static needs the last dimension to be a multiple of 128")
+    rows = x.numel() // k if x.numel() else 0
+    lead = tuple(x.shape[:-1])
+    codes = torch.empty(lead + (k // 2,), dtype=torch.uint8, device=x.device)
+    ss = torch.empty(lead + (k // 16,), dtype=torch.uint8, device=x.device)
+    mm = torch.empty(lead + (k // 128,), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _raise(mx_quantize_mbs(x.data_ptr(), _DTYPES[x.dtype], rows, k, codes.data_ptr(),
+                               ss.data_ptr(), mm.data_ptr(), _stream(x.device)))
+    return codes, ss, mm
+
+
+def dequantize_mbs(codes: torch.Tensor, sub_scales: torch.Tensor, macro_mant: torch.Tensor,
+                   dtype=torch.bfloat16) -> torch.Tensor:
+    for t in (codes, sub_scales, macro_mant):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.uint8 \
+                or not t.is_contiguous():
+            raise ValueError("codes, sub_scales and macro_mant must be contiguous uint8 GPU tensors")
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
+    k = codes.shape[-1] * 2
+    rows = codes.numel() // (k // 2) if codes.numel() else 0
+    if sub_scales.numel() * 16 != codes.numel() * 2 or macro_mant.numel() * 128 != codes.numel() * 2:
+        raise ValueError("sub_scales / macro_mant do not match codes")
+    y = torch.empty(tuple(codes.shape[:-1]) + (k,), dtype=dtype, device=codes.device)
+    with torch.cuda.device(codes.device):
+        _raise(mx_dequantize_mbs(codes.data_ptr(), sub_scales.data_ptr(), macro_mant.data_ptr(),
+                                 rows, k, _DTYPES[dtype], y.data_ptr(), _stream(codes.device)))
     return y

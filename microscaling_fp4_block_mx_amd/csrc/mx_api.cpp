@@ -24,11 +24,12 @@ mx_status_t check_shape(int64_t rows, int64_t k) {
   return MX_OK;
 }
 
-mx_status_t check_shape16(int64_t rows, int64_t k) {
-  if (rows < 0 || k <= 0 || k % 16 != 0) return MX_ERR_SHAPE;
+mx_status_t check_shape_n(int64_t rows, int64_t k, int64_t multiple) {
+  if (rows < 0 || k <= 0 || k % multiple != 0) return MX_ERR_SHAPE;
   if (rows > 0 && k > (INT64_MAX / 8) / rows) return MX_ERR_SHAPE;
   return MX_OK;
 }
+mx_status_t check_shape16(int64_t rows, int64_t k) { return check_shape_n(rows, k, 16); }
 
 bool dtype_ok(int d) { return d == MX_F32 || d == MX_BF16; }
 bool mode_ok(int m) { return m >= MX_SCALE_OCP && m <= MX_SCALE_OAS_NF; }
@@ -236,11 +237,49 @@ mx_status_t mx_dequantize_nvfp4(const uint8_t *codes, const uint8_t *block_scale
                                          n / 8, y, static_cast<hipStream_t>(stream)));
 }
 
+mx_status_t mx_quantize_mbs(const void *x, mx_dtype_t x_dtype, int64_t rows, int64_t k,
+                            uint8_t *codes, uint8_t *sub_scales, uint8_t *macro_mant,
+                            void *stream) {
+  if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape_n(rows, k, 128)) return s;
+  if (rows == 0) return MX_OK;
+  if (!x || !codes || !sub_scales || !macro_mant) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(sub_scales) || !aligned16(macro_mant))
+    return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  const int64_t nx = n * elem_bytes(x_dtype);
+  if (overlap(x, nx, codes, n / 2) || overlap(x, nx, sub_scales, n / 16) ||
+      overlap(x, nx, macro_mant, n / 128) || overlap(codes, n / 2, sub_scales, n / 16) ||
+      overlap(codes, n / 2, macro_mant, n / 128) ||
+      overlap(sub_scales, n / 16, macro_mant, n / 128))
+    return MX_ERR_ALIAS;
+  return finish(mxi_launch_quantize_mbs(x, x_dtype == MX_BF16, n / 8, codes, sub_scales,
+                                        macro_mant, static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
+                              const uint8_t *macro_mant, int64_t rows, int64_t k,
+                              mx_dtype_t y_dtype, void *y, void *stream) {
+  if (!dtype_ok(y_dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape_n(rows, k, 128)) return s;
+  if (rows == 0) return MX_OK;
+  if (!codes || !sub_scales || !macro_mant || !y) return MX_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(sub_scales) || !aligned16(macro_mant) || !aligned16(y))
+    return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  const int64_t ny = n * elem_bytes(y_dtype);
+  if (overlap(y, ny, codes, n / 2) || overlap(y, ny, sub_scales, n / 16) ||
+      overlap(y, ny, macro_mant, n / 128))
+    return MX_ERR_ALIAS;
+  return finish(mxi_launch_dequantize_mbs(codes, sub_scales, macro_mant, y_dtype == MX_BF16,
+                                          n / 8, y, static_cast<hipStream_t>(stream)));
+}
+
 const char *mx_status_string(mx_status_t s) {
   switch (s) {
     case MX_OK: return "MX_OK";
     case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
-    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: need rows >= 0 and k a positive multiple of 32";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: need rows >= 0 and k a positive multiple of the block (32; 16 for NVFP4; 128 for MBS-Static)";
     case MX_ERR_DTYPE: return "MX_ERR_DTYPE: dtype must be MX_F32 or MX_BF16";
     case MX_ERR_MODE: return "MX_ERR_MODE: mode must be an mx_scale_mode_t value (0..3)";
     case MX_ERR_ALIGN: return "MX_ERR_ALIGN: data pointers must be 16-byte aligned";

@@ -34,4 +34,10 @@ hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t nitems, uint8
 hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_scales,
                                     const uint8_t *tensor_scale, int bf16, int64_t nitems, void *y,
                                     hipStream_t st);
+// MBS-Static (nitems = rows * k / 8, a multiple of 16).
+hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint8_t *codes,
+                                   uint8_t *sub_scales, uint8_t *macro_mant, hipStream_t st);
+hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
+                                     const uint8_t *macro_mant, int bf16, int64_t nitems, void *y,
+                                     hipStream_t st);
 #endif

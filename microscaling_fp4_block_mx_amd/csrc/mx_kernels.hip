@@ -372,7 +372,7 @@ __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
     for (int u = 0; u < kUnroll; u++)
       if (base + u * kThreads < nitems) load(u, base + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++)  // whole quads drop out together
+    for (int u = 0; u < kUnroll; u++)  // whole quads (16-lane rows) drop out together
       if (base + u * kThreads < nitems) use(u, base + u * kThreads);
   }
 }
@@ -834,6 +834,112 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_nv(const uint32_t *__re
       });
 }
 
+// ---- MBS-Static (16-element sub-blocks, 8-bit-mantissa macro factor) ---------
+//
+// A 128-element macro block is one DPP row (16 lanes x 8 elements); a
+// 16-element sub-block is a lane pair. Macro factor f = 1 + m/256, m the
+// round-to-nearest-even 8-bit mantissa of fl32(a_M / 6) (capped at 255; 0 for
+// a zero or non-finite macro block); y = fl32(x * fl32(1/f)); each sub-block
+// takes the OCP byte of its largest |y| and the E2M1 codes of y at that
+// byte (scaled convert); decoding is E2M1 * 2^(s-127) * f, exact in fp32
+// (at most 2 + 9 significant bits). A sub-block holding NaN/Inf stores the
+// NaN byte and the signs of x, as a NaN MXFP4 block does.
+
+// rotate right by 4 / 8 lanes within each row of 16
+__device__ __forceinline__ uint32_t dpp_ror4(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_ror8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = quad_max_u32(v);
+  v = max(v, dpp_ror4(v));
+  v = max(v, dpp_ror8(v));
+  return v;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *__restrict__ x,
+                                                           uint32_t *__restrict__ codes,
+                                                           uint8_t *__restrict__ sub_scales,
+                                                           uint8_t *__restrict__ macro_mant,
+                                                           int64_t nitems) {
+  Item<BF16> xv[kUnroll];
+  tile_loop(
+      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t it) {
+        const uint32_t aM = row_max_u32(item_amax_bits<BF16>(xv[u]));
+        // m = 0 for a zero or non-finite macro block, and where a_M / 6
+        // underflows to zero (fp32 a_M below 4 * 2^-149): no mantissa.
+        uint32_t m = 0;
+        const float r = __uint_as_float(aM) / 6.0f;
+        if (aM < 0x7F800000u && r != 0.0f) {
+          const float f01 = 2.0f * __builtin_amdgcn_frexp_mantf(r);  // [1, 2), exact
+          m = min((uint32_t)__builtin_rintf((f01 - 1.0f) * 256.0f), 255u);
+        }
+        const float f = 1.0f + (float)m * (1.0f / 256.0f);  // exact
+        const float inv = 1.0f / f;
+        float y[8];
+        uint32_t ay = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          y[i] = elem<BF16>(xv[u], i) * inv;
+          ay = max(ay, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+        }
+        ay = max(ay, dpp_x1(ay));  // the sub-block's lane pair
+        const uint32_t s = ocp_scale_byte(ay);
+        uint32_t c;
+        if (__builtin_expect(s == 255u, 0)) {
+          c = sign_codes<BF16>(xv[u]);
+        } else {
+          const float sc = scale_operand(s);
+          c = 0;
+          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[0], y[1], sc, 0);
+          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[2], y[3], sc, 1);
+          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[4], y[5], sc, 2);
+          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[6], y[7], sc, 3);
+        }
+        st<false>(codes + it, c);
+        if ((threadIdx.x & 1) == 0) st<false>(sub_scales + (it >> 1), (uint8_t)s);
+        if ((threadIdx.x & 15) == 0) st<false>(macro_mant + (it >> 4), (uint8_t)m);
+      });
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_dequantize_mbs(const uint32_t *__restrict__ codes,
+                                                             const uint8_t *__restrict__ sub_scales,
+                                                             const uint8_t *__restrict__ macro_mant,
+                                                             void *__restrict__ y, int64_t nitems) {
+  uint32_t cw[kUnroll], sb[kUnroll], mb[kUnroll];
+  tile_loop(
+      nitems,
+      [&](int u, int64_t it) {
+        cw[u] = ld<false>(codes + it);
+        sb[u] = ld<false>(sub_scales + (it >> 1));
+        mb[u] = ld<false>(macro_mant + (it >> 4));
+      },
+      [&](int u, int64_t it) {
+        const float f = 1.0f + (float)mb[u] * (1.0f / 256.0f);
+        float q[8];
+        decode_f32(cw[u], sb[u], q);  // E2M1 * 2^(s-127); NaN for byte 255
+        uint32_t out[BF16 ? 4 : 8];
+        const bool nan = sb[u] == 255u;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+            const b2 p = {(__bf16)(q[2 * j] * f), (__bf16)(q[2 * j + 1] * f)};
+            out[j] = nan ? kNaN16x2 : __builtin_bit_cast(uint32_t, p);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; i++) out[i] = nan ? kNaN32 : __float_as_uint(q[i] * f);
+        }
+        store_item<BF16>(y, it, out);
+      });
+}
+
 // ---- launchers -----------------------------------------------------------------
 
 static unsigned grid_for(int64_t nitems, int64_t cap) {
@@ -1004,6 +1110,30 @@ hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_s
                        nitems);
   else
     hipLaunchKernelGGL((k_dequantize_nv<false>), g, b, 0, st, c, block_scales, tensor_scale, y,
+                       nitems);
+  return hipGetLastError();
+}
+
+hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint8_t *codes,
+                                   uint8_t *sub_scales, uint8_t *macro_mant, hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  uint32_t *c = reinterpret_cast<uint32_t *>(codes);
+  if (bf16)
+    hipLaunchKernelGGL((k_quantize_mbs<true>), g, b, 0, st, x, c, sub_scales, macro_mant, nitems);
+  else
+    hipLaunchKernelGGL((k_quantize_mbs<false>), g, b, 0, st, x, c, sub_scales, macro_mant, nitems);
+  return hipGetLastError();
+}
+
+hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
+                                     const uint8_t *macro_mant, int bf16, int64_t nitems, void *y,
+                                     hipStream_t st) {
+  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
+  if (bf16)
+    hipLaunchKernelGGL((k_dequantize_mbs<true>), g, b, 0, st, c, sub_scales, macro_mant, y, nitems);
+  else
+    hipLaunchKernelGGL((k_dequantize_mbs<false>), g, b, 0, st, c, sub_scales, macro_mant, y,
                        nitems);
   return hipGetLastError();
 }
