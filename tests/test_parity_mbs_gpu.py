@@ -110,7 +110,9 @@ def test_mbs_activations_full():
 def test_mbs_versus_mxfp4_qsnr():
     """MBS-Static's 16-element sub-blocks and macro factor recover accuracy
     that a block-32 power-of-two scale loses ("Unveiling the Potential of
-    Quantization with MXFP4", MBS section): higher QSNR than MXFP4 (OCP)."""
+    Quantization with MXFP4", MBS section): higher QSNR than MXFP4 (OCP). On
+    the outlier-channel activations it lands within 1 dB of NVFP4, the gap
+    the page's contributions section reports for its enhanced MXFP4."""
     for name, x in (("weights", workloads.bf16_normal(76, (4096, 4096))),
                     ("activations", workloads.bf16_student_t_outlier_channels(2))):
         xd = x.cuda()
@@ -118,8 +120,13 @@ def test_mbs_versus_mxfp4_qsnr():
         c, s, m = mx.quantize_mbs(xd)
         ymbs = mx.dequantize_mbs(c, s, m, torch.float32)
         ymx = mx.fakequant(xd).float()
+        cn, bn, tn = mx.quantize_nvfp4(xd)
+        ynv = mx.dequantize_nvfp4(cn, bn, tn, torch.float32)
         e = float((xf.double() ** 2).sum())
-        q_mbs = 10 * np.log10(e / float(((xf - ymbs).double() ** 2).sum()))
-        q_mx = 10 * np.log10(e / float(((xf - ymx).double() ** 2).sum()))
-        say(f"QSNR {name}: mbs-static {q_mbs:.3f} dB, mxfp4-ocp {q_mx:.3f} dB")
-        assert q_mbs > q_mx
+        q = {k: 10 * np.log10(e / float(((xf - y).double() ** 2).sum()))
+             for k, y in (("mbs", ymbs), ("mx", ymx), ("nv", ynv))}
+        say(f"QSNR {name}: mbs-static {q['mbs']:.3f} dB, mxfp4-ocp {q['mx']:.3f} dB, "
+            f"nvfp4 {q['nv']:.3f} dB")
+        assert q["mbs"] > q["mx"]
+        if name == "activations":
+            assert q["nv"] - q["mbs"] < 1.0
