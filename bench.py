@@ -9,6 +9,15 @@ HBM). Buffer sets rotate so the working set is >= 1 GiB and the 256 MB
 Infinity Cache cannot serve a step from the previous one.
 
 Prints ONE JSON line. --gpus N with N > 1 exits: this path runs on one GPU.
+
+--suite instead times each operation on the other workloads alone (fp32
+normal [1024, 4096]; the Llama-3.2-3B-shaped linear stack, per matrix and
+grouped by K; the 128-expert MoE weights; bf16 Laplace [16384, 8192] with
+sparse outliers), with per-launch HIP events (median, p10, p90), warm
+(cache-resident) and cold (rotated) figures where the tensor fits the cache,
+and for the small fp32 case the host-side single-launch latency and the
+per-launch time inside a replayed HIP graph. It prints one JSON line per
+measurement and a markdown table.
 """
 from __future__ import annotations
 
@@ -89,6 +98,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suite", action="store_true",
+                    help="time the operations on the other workloads instead of the step")
     return ap.parse_args()
 
 
@@ -108,6 +119,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.suite:
+        return suite(args, dev)
     torch.cuda.set_device(dev)
     mx.load_library()
 
@@ -365,6 +378,277 @@ def cpu_baseline(x_host, target_s):
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} step(s) over the first {rows} rows x 4096 of the same tensor "
                       f"({el:.1f} s)"}
+
+
+# ---- per-workload suite -----------------------------------------------------
+
+def _launch_stats(fn, n_timed, n_warm, stream):
+    """Per-launch HIP event times (us) of fn(i) on `stream`: median, p10,
+    p90, plus the mean of the same launches issued back to back."""
+    import numpy as np
+    import torch
+
+    for i in range(n_warm):
+        fn(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_timed)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for i in range(n_timed):
+        fn(i)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    return {"median_us": float(np.median(t)), "p10_us": float(np.percentile(t, 10)),
+            "p90_us": float(np.percentile(t, 90)),
+            "back_to_back_us": a0.elapsed_time(a1) * 1e3 / n_timed}
+
+
+def suite(args, dev):
+    import numpy as np
+    import torch
+
+    import microscaling_fp4_block_mx_amd as mx
+    import workloads
+
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    n_timed = max(100, args.steps)
+    n_warm = max(10, args.warmup)
+    results = []
+
+    def ok(st):
+        if st != mx.MX_OK:
+            raise RuntimeError(mx.mx_status_string(st))
+
+    def report(workload, op, nbytes, stats, **extra):
+        med = stats["median_us"]
+        row = {"workload": workload, "op": op, "bytes": int(nbytes),
+               **{k: round(v, 2) for k, v in stats.items()},
+               "GB/s": round(nbytes / med / 1e3, 1),
+               "frac_hbm": round(nbytes / med / 1e3 / HBM_PEAK_GBS, 4), **extra}
+        results.append(row)
+        print(json.dumps(row), flush=True)
+
+    def nsets_for(per_set):
+        return max(2, int(np.ceil(args.rotate_gib * 2 ** 30 / per_set)))
+
+    # -- fp32 normal [1024, 4096] (seed 1): quantize, dequantize -> fp32, block MSE
+    x1 = workloads.fp32_normal(1).to(dev)
+    R, K = x1.shape
+    n = x1.numel()
+    per_set = n * (4 + 0.5 + 1 / 32 + 4 + 4 / 32)
+    sets = []
+    for _ in range(nsets_for(per_set)):
+        sets.append(dict(x=x1.clone(),
+                         c=torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
+                         s=torch.empty((R, K // 32), dtype=torch.uint8, device=dev),
+                         y=torch.empty_like(x1),
+                         bm=torch.empty((R, K // 32), dtype=torch.float32, device=dev)))
+    wsb = mx.mx_block_mse_workspace_size(R, K)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    sums = torch.empty(2, dtype=torch.float64, device=dev)
+    W1 = "fp32 normal [1024, 4096] (seed 1)"
+
+    def q1(i, sh=sh):
+        b = sets[i % len(sets)]
+        ok(mx.mx_quantize(b["x"].data_ptr(), mx.MX_F32, R, K, mx.MX_SCALE_OCP,
+                          b["c"].data_ptr(), b["s"].data_ptr(), sh))
+
+    def dq1(i, sh=sh):
+        b = sets[i % len(sets)]
+        ok(mx.mx_dequantize(b["c"].data_ptr(), b["s"].data_ptr(), R, K, mx.MX_F32,
+                            b["y"].data_ptr(), sh))
+
+    def mse1(i, sh=sh):
+        b = sets[i % len(sets)]
+        ok(mx.mx_block_mse(b["x"].data_ptr(), mx.MX_F32, b["c"].data_ptr(), b["s"].data_ptr(),
+                           R, K, b["bm"].data_ptr(), sums.data_ptr(), ws.data_ptr(), wsb, sh))
+
+    for i in range(len(sets)):
+        q1(i)
+    for op, fn, bpe in (("quantize_ocp_f32", q1, 4 + 0.5 + 1 / 32),
+                        ("dequantize_f32", dq1, 0.5 + 1 / 32 + 4),
+                        ("block_mse_f32", mse1, 4 + 0.5 + 1 / 32 + 4 / 32)):
+        report(W1, op, bpe * n, _launch_stats(fn, n_timed, n_warm, stream),
+               cache=f"cold ({len(sets)} rotated sets)")
+        report(W1, op, bpe * n, _launch_stats(lambda i, fn=fn: fn(0), n_timed, n_warm, stream),
+               cache="warm (one set)")
+    # single-launch latency: host time of one quantize call until it has run
+    lat = []
+    for i in range(n_timed):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        q1(i)
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - t0) * 1e6)
+    lat = np.array(lat)
+    row = {"workload": W1, "op": "quantize_ocp_f32", "single_launch_host_us": {
+        "median": round(float(np.median(lat)), 2), "p10": round(float(np.percentile(lat, 10)), 2),
+        "p90": round(float(np.percentile(lat, 90)), 2)}}
+    results.append(row)
+    print(json.dumps(row), flush=True)
+    # the same launches captured in one HIP graph and replayed
+    gs = torch.cuda.Stream(dev)
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):
+        for i in range(len(sets)):
+            q1(i, gs.cuda_stream)
+    stream.wait_stream(gs)
+    torch.cuda.synchronize()
+    n_graph = 100
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(n_graph):
+            q1(i, cs)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    want_c = sets[0]["c"].clone()
+    reps = []
+    for _ in range(20):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        g.replay()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(a0.elapsed_time(a1) * 1e3 / n_graph)
+    q1(0)
+    torch.cuda.synchronize()
+    assert torch.equal(want_c, sets[0]["c"]), "graph replay changed the codes"
+    med = float(np.median(reps))
+    row = {"workload": W1, "op": "quantize_ocp_f32", "hip_graph_per_launch_us": round(med, 2),
+           "GB/s": round((4 + 0.5 + 1 / 32) * n / med / 1e3, 1),
+           "launches_per_graph": n_graph, "cache": f"cold ({len(sets)} rotated sets)"}
+    results.append(row)
+    print(json.dumps(row), flush=True)
+    del sets, x1, g, ws
+    torch.cuda.empty_cache()
+
+    # -- Laplace + sparse outliers bf16 [16384, 8192] (seed 5): quantize OCP /
+    #    OAS and block MSE of each
+    x5 = workloads.bf16_laplace_sparse_outliers(5).to(dev)
+    R, K = x5.shape
+    n = x5.numel()
+    per_set = n * (2 + 2 * (0.5 + 1 / 32) + 4 / 32)
+    sets = []
+    for _ in range(nsets_for(per_set)):
+        sets.append(dict(x=x5.clone(),
+                         c=[torch.empty((R, K // 2), dtype=torch.uint8, device=dev) for _ in range(2)],
+                         s=[torch.empty((R, K // 32), dtype=torch.uint8, device=dev) for _ in range(2)],
+                         bm=torch.empty((R, K // 32), dtype=torch.float32, device=dev)))
+    wsb = mx.mx_block_mse_workspace_size(R, K)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    W5 = "bf16 Laplace(0,1) [16384, 8192], 0.1% outliers +-U(20,200) (seed 5)"
+    for j, (mode, mname) in enumerate(((mx.MX_SCALE_OCP, "ocp"), (mx.MX_SCALE_OAS, "oas"))):
+        def q5(i, mode=mode, j=j):
+            b = sets[i % len(sets)]
+            ok(mx.mx_quantize(b["x"].data_ptr(), mx.MX_BF16, R, K, mode, b["c"][j].data_ptr(),
+                              b["s"][j].data_ptr(), sh))
+
+        def mse5(i, j=j):
+            b = sets[i % len(sets)]
+            ok(mx.mx_block_mse(b["x"].data_ptr(), mx.MX_BF16, b["c"][j].data_ptr(),
+                               b["s"][j].data_ptr(), R, K, b["bm"].data_ptr(), sums.data_ptr(),
+                               ws.data_ptr(), wsb, sh))
+        for op, fn, bpe in ((f"quantize_{mname}", q5, 2 + 0.5 + 1 / 32),
+                            (f"block_mse_{mname}", mse5, 2 + 0.5 + 1 / 32 + 4 / 32)):
+            report(W5, op, bpe * n, _launch_stats(fn, n_timed, n_warm, stream),
+                   cache=f"cold ({len(sets)} rotated sets)")
+            report(W5, op, bpe * n, _launch_stats(lambda i, fn=fn: fn(0), n_timed, n_warm, stream),
+                   cache="warm (one set)")
+        sse, ssq = sums.tolist()
+        row = {"workload": W5, "op": f"tensor_mse_{mname}", "mse": sse / n,
+               "qsnr_db": round(10 * np.log10(ssq / sse), 4)}
+        results.append(row)
+        print(json.dumps(row), flush=True)
+    del sets, x5, ws
+    torch.cuda.empty_cache()
+
+    # -- Llama-3.2-3B-shaped linear stack, bf16 N(0, 0.02): 196 per-matrix
+    #    quantize launches, and two launches grouped by K
+    a, b = workloads.llama32_3b_grouped(dev)
+    WL = "Llama-3.2-3B linears x28 layers, bf16 N(0,0.02)"
+    ca = torch.empty((a.shape[0], a.shape[1] // 2), dtype=torch.uint8, device=dev)
+    sa = torch.empty((a.shape[0], a.shape[1] // 32), dtype=torch.uint8, device=dev)
+    cb = torch.empty((b.shape[0], b.shape[1] // 2), dtype=torch.uint8, device=dev)
+    sb = torch.empty((b.shape[0], b.shape[1] // 32), dtype=torch.uint8, device=dev)
+    mats = []  # (tensor, codes, scales, row0, rows, k) in generation order
+    ra = rb = 0
+    for layer in range(workloads.LLAMA32_3B_LAYERS):
+        for which, (_, out_f, in_f) in enumerate(workloads.LLAMA32_3B_LINEARS):
+            if in_f == 8192:
+                mats.append((b, cb, sb, rb, out_f, in_f))
+                rb += out_f
+            else:
+                mats.append((a, ca, sa, ra, out_f, in_f))
+                ra += out_f
+    assert ra == a.shape[0] and rb == b.shape[0]
+    n = a.numel() + b.numel()
+    bytes_q = (2 + 0.5 + 1 / 32) * n
+
+    def per_matrix(_):
+        for t, c, s_, r0, rows, k in mats:
+            ok(mx.mx_quantize(t[r0].data_ptr(), mx.MX_BF16, rows, k, mx.MX_SCALE_OCP,
+                              c[r0].data_ptr(), s_[r0].data_ptr(), sh))
+
+    def grouped(_):
+        ok(mx.mx_quantize(a.data_ptr(), mx.MX_BF16, a.shape[0], a.shape[1], mx.MX_SCALE_OCP,
+                          ca.data_ptr(), sa.data_ptr(), sh))
+        ok(mx.mx_quantize(b.data_ptr(), mx.MX_BF16, b.shape[0], b.shape[1], mx.MX_SCALE_OCP,
+                          cb.data_ptr(), sb.data_ptr(), sh))
+
+    report(WL, "quantize_ocp (196 per-matrix launches)", bytes_q,
+           _launch_stats(per_matrix, 20, 3, stream), cache="exceeds cache")
+    report(WL, "quantize_ocp (2 launches grouped by K)", bytes_q,
+           _launch_stats(grouped, 20, 3, stream), cache="exceeds cache")
+    del a, b, ca, sa, cb, sb, mats
+    torch.cuda.empty_cache()
+
+    # -- MoE experts bf16 N(0, 0.02): quantize, then dequantize -> bf16
+    w13, w2 = workloads.moe_weights(dev)
+    WM = "MoE 128 experts w13 [128,3072,4096] + w2 [128,4096,1536], bf16 N(0,0.02)"
+    shapes = [(w, w.numel() // w.shape[-1], w.shape[-1]) for w in (w13, w2)]
+    cs = [torch.empty(w.numel() // 2, dtype=torch.uint8, device=dev) for w in (w13, w2)]
+    ss = [torch.empty(w.numel() // 32, dtype=torch.uint8, device=dev) for w in (w13, w2)]
+    ys = [torch.empty_like(w) for w in (w13, w2)]
+    n = w13.numel() + w2.numel()
+
+    def qm(_):
+        for (w, rows, k), c, s_ in zip(shapes, cs, ss):
+            ok(mx.mx_quantize(w.data_ptr(), mx.MX_BF16, rows, k, mx.MX_SCALE_OCP, c.data_ptr(),
+                              s_.data_ptr(), sh))
+
+    def dqm(_):
+        for (w, rows, k), c, s_, y in zip(shapes, cs, ss, ys):
+            ok(mx.mx_dequantize(c.data_ptr(), s_.data_ptr(), rows, k, mx.MX_BF16, y.data_ptr(), sh))
+
+    report(WM, "quantize_ocp (w13 + w2)", (2 + 0.5 + 1 / 32) * n,
+           _launch_stats(qm, 20, 3, stream), cache="exceeds cache")
+    report(WM, "dequantize_bf16 (w13 + w2)", (0.5 + 1 / 32 + 2) * n,
+           _launch_stats(dqm, 20, 3, stream), cache="exceeds cache")
+    del w13, w2, cs, ss, ys
+    torch.cuda.empty_cache()
+
+    # markdown summary
+    print("\n| workload | op | cache | bytes | median us | p10 | p90 | back-to-back us "
+          "| GB/s (median) | % of 8 TB/s |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for r in results:
+        if "median_us" in r:
+            print(f"| {r['workload']} | {r['op']} | {r['cache']} | {r['bytes']} | "
+                  f"{r['median_us']} | {r['p10_us']} | {r['p90_us']} | {r['back_to_back_us']} | "
+                  f"{r['GB/s']} | {100 * r['frac_hbm']:.1f} |")
+    for r in results:
+        if "median_us" not in r:
+            print("- " + json.dumps(r))
 
 
 if __name__ == "__main__":

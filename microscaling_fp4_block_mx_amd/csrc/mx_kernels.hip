@@ -492,27 +492,57 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
   }
 }
 
-// One workgroup: out[j] = sum over i of partial[2i + j] for j = 0, 1
-// (strided per thread, then a fixed tree over the workgroup). n == 0 writes 0.
+#ifndef MX_MSE_GRID_CAP
+#define MX_MSE_GRID_CAP 2048
+#endif
+constexpr int kSumPer = MX_MSE_GRID_CAP / kThreads;  // partial pairs per thread
+static_assert(kSumPer * kThreads == MX_MSE_GRID_CAP, "grid cap must be a multiple of 256");
+
+// One workgroup: out[j] = sum over i of partial[2i + j] for j = 0, 1, n <=
+// MX_MSE_GRID_CAP pairs. The kernel is latency-bound, so every thread issues
+// all of its loads (pairs t, t + 256, ...) before the first add; the sums then
+// run in a fixed order (per thread in pair order, a butterfly over the wave,
+// the four waves in order), so the result is deterministic. n == 0 writes 0.
 __global__ __launch_bounds__(kThreads) void k_sum_partials(const double *__restrict__ partial,
                                                            int n, double *__restrict__ out) {
-  __shared__ double part[2][kThreads];
+  __shared__ double wave_part[2][kThreads / 64];
+  if (n <= 0) {
+    if (threadIdx.x < 2) out[threadIdx.x] = 0.0;
+    return;
+  }
+  // unconditional loads of a clamped (in-bounds) index, so none waits on a
+  // branch; pairs past n are then replaced by zero
+  double v0[kSumPer], v1[kSumPer];
+#pragma unroll
+  for (int j = 0; j < kSumPer; j++) {
+    const int i = (int)threadIdx.x + j * kThreads;
+    const int ic = min(i, n - 1);
+    const double a = partial[2 * ic], b = partial[2 * ic + 1];
+    v0[j] = i < n ? a : 0.0;
+    v1[j] = i < n ? b : 0.0;
+  }
   double t0 = 0.0, t1 = 0.0;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    t0 += partial[2 * i];
-    t1 += partial[2 * i + 1];
+#pragma unroll
+  for (int j = 0; j < kSumPer; j++) {
+    t0 += v0[j];
+    t1 += v1[j];
   }
-  part[0][threadIdx.x] = t0;
-  part[1][threadIdx.x] = t1;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    t0 += __shfl_xor(t0, off, 64);
+    t1 += __shfl_xor(t1, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    wave_part[0][threadIdx.x >> 6] = t0;
+    wave_part[1][threadIdx.x >> 6] = t1;
+  }
   __syncthreads();
-  for (int w = kThreads / 2; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) {
-      part[0][threadIdx.x] += part[0][threadIdx.x + w];
-      part[1][threadIdx.x] += part[1][threadIdx.x + w];
-    }
-    __syncthreads();
+  if (threadIdx.x < 2) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; w++) t += wave_part[threadIdx.x][w];
+    out[threadIdx.x] = t;
   }
-  if (threadIdx.x < 2) out[threadIdx.x] = part[threadIdx.x][0];
 }
 
 // ---- MXFP8 (E4M3 elements) --------------------------------------------------
@@ -859,35 +889,54 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
   return v;
 }
 
+// fl32(a / 6) for the non-negative fp32 pattern a. From 2^-125 up, the
+// product with fl32(1/6) plus one fma residual correction is the correctly
+// rounded quotient (checked against IEEE division for every fp32 value in
+// that range); below it, where the quotient is subnormal, IEEE division.
+__device__ __forceinline__ float div6(uint32_t a_bits) {
+  const float a = __uint_as_float(a_bits);
+  if (__builtin_expect(a_bits < 0x01000000u, 0)) return a / 6.0f;
+  constexpr float kSixth = 1.0f / 6.0f;
+  const float q0 = a * kSixth;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, a), kSixth, q0);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *__restrict__ x,
                                                            uint32_t *__restrict__ codes,
                                                            uint8_t *__restrict__ sub_scales,
                                                            uint8_t *__restrict__ macro_mant,
                                                            int64_t nitems) {
+  // fl32(1 / f) for every macro mantissa m (f = 1 + m/256): IEEE division,
+  // once per workgroup, so the per-item cost is one LDS read
+  static_assert(kThreads == 256, "one table entry per thread");
+  __shared__ float inv_tab[256];
+  inv_tab[threadIdx.x] = 1.0f / (1.0f + (float)threadIdx.x * (1.0f / 256.0f));
+  __syncthreads();
   Item<BF16> xv[kUnroll];
   tile_loop(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t it) {
-        const uint32_t aM = row_max_u32(item_amax_bits<BF16>(xv[u]));
+        const uint32_t a8 = item_amax_bits<BF16>(xv[u]);
+        const uint32_t aS = max(a8, dpp_x1(a8));  // the sub-block's lane pair
+        uint32_t aM = max(aS, dpp_x2(aS));
+        aM = max(aM, dpp_ror4(aM));
+        aM = max(aM, dpp_ror8(aM));
         // m = 0 for a zero or non-finite macro block, and where a_M / 6
         // underflows to zero (fp32 a_M below 4 * 2^-149): no mantissa.
         uint32_t m = 0;
-        const float r = __uint_as_float(aM) / 6.0f;
+        const float r = div6(aM);
         if (aM < 0x7F800000u && r != 0.0f) {
           const float f01 = 2.0f * __builtin_amdgcn_frexp_mantf(r);  // [1, 2), exact
           m = min((uint32_t)__builtin_rintf((f01 - 1.0f) * 256.0f), 255u);
         }
-        const float f = 1.0f + (float)m * (1.0f / 256.0f);  // exact
-        const float inv = 1.0f / f;
+        const float inv = inv_tab[m];
         float y[8];
-        uint32_t ay = 0;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-          y[i] = elem<BF16>(xv[u], i) * inv;
-          ay = max(ay, __float_as_uint(y[i]) & 0x7FFFFFFFu);
-        }
-        ay = max(ay, dpp_x1(ay));  // the sub-block's lane pair
+        for (int i = 0; i < 8; i++) y[i] = elem<BF16>(xv[u], i) * inv;
+        // largest |y| of the sub-block: rounding is monotone, so it equals
+        // fl(max |x| * inv); NaN/Inf stay NaN/Inf and give byte 255
+        const uint32_t ay = __float_as_uint(__uint_as_float(aS) * inv);
         const uint32_t s = ocp_scale_byte(ay);
         uint32_t c;
         if (__builtin_expect(s == 255u, 0)) {
@@ -1003,10 +1052,6 @@ hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, in
     hipLaunchKernelGGL((k_dequantize<false>), g, b, 0, st, c, scales, y, nitems);
   return hipGetLastError();
 }
-
-#ifndef MX_MSE_GRID_CAP
-#define MX_MSE_GRID_CAP 2048
-#endif
 
 size_t mxi_block_mse_partials(int64_t nitems) { return 2 * grid_for(nitems, MX_MSE_GRID_CAP); }
 

@@ -1,0 +1,83 @@
+"""The entry points under HIP graph capture: one graph holds quantize (OAS),
+dequantize, block MSE with tensor sums, fake-quant, MXFP8 fake-quant, NVFP4
+quantize and MBS-Static quantize on static buffers. Every replay, with new
+inputs copied in and the outputs overwritten by eager work in between, must
+reproduce the eager results bit for bit (the path records no memset and
+allocates nothing, so it is capturable as is)."""
+import pytest
+import torch
+
+import workloads
+import microscaling_fp4_block_mx_amd as mx
+
+pytestmark = pytest.mark.gpu
+
+
+def _ok(st):
+    assert st == mx.MX_OK, mx.mx_status_string(st)
+
+
+def test_graph_replays_match_eager():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    R, K = 512, 4096
+    xf = torch.empty((R, K), dtype=torch.float32, device=dev)
+    xb = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    c, s = torch.empty((R, K // 2), **u8), torch.empty((R, K // 32), **u8)
+    y = torch.empty_like(xf)
+    bm = torch.empty((R, K // 32), dtype=torch.float32, device=dev)
+    sums = torch.empty(2, dtype=torch.float64, device=dev)
+    wsb = mx.mx_block_mse_workspace_size(R, K)
+    ws = torch.empty(wsb, **u8)
+    fq, fq8 = torch.empty_like(xb), torch.empty_like(xb)
+    cn, bn, tn = torch.empty((R, K // 2), **u8), torch.empty((R, K // 16), **u8), torch.empty(1, **u8)
+    wsnb = mx.mx_nvfp4_workspace_size(R, K)
+    wsn = torch.empty(wsnb, **u8)
+    cm, sm, mm = torch.empty((R, K // 2), **u8), torch.empty((R, K // 16), **u8), torch.empty((R, K // 128), **u8)
+    outs = (c, s, y, bm, sums, fq, fq8, cn, bn, tn, cm, sm, mm)
+
+    def seq(h):
+        _ok(mx.mx_quantize(xf.data_ptr(), mx.MX_F32, R, K, mx.MX_SCALE_OAS, c.data_ptr(),
+                           s.data_ptr(), h))
+        _ok(mx.mx_dequantize(c.data_ptr(), s.data_ptr(), R, K, mx.MX_F32, y.data_ptr(), h))
+        _ok(mx.mx_block_mse(xf.data_ptr(), mx.MX_F32, c.data_ptr(), s.data_ptr(), R, K,
+                            bm.data_ptr(), sums.data_ptr(), ws.data_ptr(), wsb, h))
+        _ok(mx.mx_fakequant(xb.data_ptr(), mx.MX_BF16, R, K, mx.MX_SCALE_OCP, fq.data_ptr(), h))
+        _ok(mx.mx_fakequant_mxfp8(xb.data_ptr(), mx.MX_BF16, R, K, fq8.data_ptr(), h))
+        _ok(mx.mx_quantize_nvfp4(xb.data_ptr(), mx.MX_BF16, R, K, cn.data_ptr(), bn.data_ptr(),
+                                 tn.data_ptr(), wsn.data_ptr(), wsnb, h))
+        _ok(mx.mx_quantize_mbs(xb.data_ptr(), mx.MX_BF16, R, K, cm.data_ptr(), sm.data_ptr(),
+                               mm.data_ptr(), h))
+
+    def load(seed):
+        xf.copy_(workloads.fp32_normal(seed, (R, K)).to(dev) * (seed % 5 + 1))
+        xb.copy_(workloads.bf16_student_t_outlier_channels(seed, (R, K)).to(dev))
+
+    main = torch.cuda.current_stream(dev)
+    load(100)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        seq(side.cuda_stream)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+
+    for seed in (101, 102, 103, 104):
+        load(seed)
+        seq(main.cuda_stream)  # eager reference on the same buffers
+        torch.cuda.synchronize()
+        want = [t.clone() for t in outs]
+        for t in outs:  # eager work between replays: clobber every output
+            t.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, want)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+                f"replay for seed {seed}: output {i} differs from eager"
