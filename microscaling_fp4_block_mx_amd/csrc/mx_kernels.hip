@@ -348,42 +348,50 @@ __device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t 
 
 // ---- kernels -----------------------------------------------------------------
 
-// Grid-stride over tiles of kThreads * kUnroll items; each thread's kUnroll
-// items are spaced kThreads apart so every load instruction is coalesced,
-// and all loads of a tile are issued before any is consumed. Full tiles run
-// without bounds checks; the one partial tile (if any) is handled by the
-// workgroup whose stride lands on it, with per-item checks.
-template <typename Load, typename Use>
+// Grid-stride over tiles of kThreads * U items; each thread's U items are
+// spaced kThreads apart so every load instruction is coalesced, and all loads
+// of a tile are issued before any is consumed. Full tiles run without bounds
+// checks; the one partial tile (if any) is handled by the workgroup whose
+// stride lands on it, with per-item checks.
+template <int U, typename Load, typename Use>
 __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
-  const int64_t tile = (int64_t)kThreads * kUnroll;
+  const int64_t tile = (int64_t)kThreads * U;
   const int64_t nfull = nitems / tile;
   int64_t t = blockIdx.x;
   for (; t < nfull; t += gridDim.x) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) load(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) load(u, base + u * kThreads);
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) use(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) use(u, base + u * kThreads);
   }
   if (t == nfull && nfull * tile < nitems) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++)
+    for (int u = 0; u < U; u++)
       if (base + u * kThreads < nitems) load(u, base + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++)  // whole quads (16-lane rows) drop out together
+    for (int u = 0; u < U; u++)  // whole quads (16-lane rows) drop out together
       if (base + u * kThreads < nitems) use(u, base + u * kThreads);
   }
 }
+
+// Items per thread per tile for the streaming kernels: an fp32 item is two
+// 16-byte accesses, so fp32 takes half as many items, which keeps the bytes
+// in flight per lane equal and doubles the workgroups on small tensors.
+// (Kernels whose workspace size is fixed per shape, whatever the dtype, keep
+// kUnroll for both.)
+template <bool BF16>
+constexpr int kU = BF16 ? kUnroll : (kUnroll > 1 ? kUnroll / 2 : 1);
 
 template <bool BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ x,
                                                        uint32_t *__restrict__ codes,
                                                        uint8_t *__restrict__ scales,
                                                        int64_t nitems) {
-  Item<BF16> xv[kUnroll];
-  tile_loop(
+  Item<BF16> xv[kU<BF16>];
+  tile_loop<kU<BF16>>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t it) {
         uint32_t c;
@@ -395,8 +403,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ 
 
 template <bool BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_fakequant(const void *x, void *y, int64_t nitems) {
-  Item<BF16> xv[kUnroll];
-  tile_loop(
+  Item<BF16> xv[kU<BF16>];
+  tile_loop<kU<BF16>>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t it) {
         uint32_t c;
@@ -411,8 +419,8 @@ template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restrict__ codes,
                                                          const uint8_t *__restrict__ scales,
                                                          void *__restrict__ y, int64_t nitems) {
-  uint32_t cw[kUnroll], sb[kUnroll];
-  tile_loop(
+  uint32_t cw[kU<BF16>], sb[kU<BF16>];
+  tile_loop<kU<BF16>>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
@@ -443,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
   double mine_sq = 0.0;  // sum of x^2 over this lane's elements
   Item<BF16> xv[kUnroll];
   uint32_t cw[kUnroll], sb[kUnroll];
-  tile_loop(
+  tile_loop<kUnroll>(
       nitems,
       [&](int u, int64_t it) {
         load_item<BF16>(x, it, xv[u]);
@@ -671,8 +679,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize8(const void *__restrict__
                                                         u32x2 *__restrict__ codes,
                                                         uint8_t *__restrict__ scales,
                                                         int64_t nitems) {
-  Item<BF16> xv[kUnroll];
-  tile_loop(
+  Item<BF16> xv[kU<BF16>];
+  tile_loop<kU<BF16>>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t it) {
         u32x2 c;
@@ -686,9 +694,9 @@ template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_dequantize8(const u32x2 *__restrict__ codes,
                                                           const uint8_t *__restrict__ scales,
                                                           void *__restrict__ y, int64_t nitems) {
-  u32x2 cw[kUnroll];
-  uint32_t sb[kUnroll];
-  tile_loop(
+  u32x2 cw[kU<BF16>];
+  uint32_t sb[kU<BF16>];
+  tile_loop<kU<BF16>>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
@@ -703,8 +711,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize8(const u32x2 *__restric
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_fakequant8(const void *x, void *y, int64_t nitems) {
-  Item<BF16> xv[kUnroll];
-  tile_loop(
+  Item<BF16> xv[kU<BF16>];
+  tile_loop<kU<BF16>>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t it) {
         u32x2 c;
@@ -745,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void k_absmax_partials(const void *__rest
   __shared__ uint32_t wave_max[kThreads / 64];
   uint32_t m = 0;
   Item<BF16> xv[kUnroll];
-  tile_loop(
+  tile_loop<kUnroll>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) { m = max(m, item_finite_amax_bits<BF16>(xv[u])); });
 #pragma unroll
@@ -796,7 +804,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *__restrict
   const float one = 1.0f;  // scale operand of the converts: 2^0
 
   Item<BF16> xv[kUnroll];
-  tile_loop(
+  tile_loop<kUnroll>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t it) {
         const uint32_t ab = dpp_x1_max(item_amax_bits<BF16>(xv[u]));  // NaN/Inf sort above
@@ -835,8 +843,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_nv(const uint32_t *__re
   const int t = (int)*tensor_scale - 127;
   const float inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t, scale operand
   const float one = 1.0f;
-  uint32_t cw[kUnroll], sb[kUnroll];
-  tile_loop(
+  uint32_t cw[kU<BF16>], sb[kU<BF16>];
+  tile_loop<kU<BF16>>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
@@ -913,8 +921,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *__restric
   __shared__ float inv_tab[256];
   inv_tab[threadIdx.x] = 1.0f / (1.0f + (float)threadIdx.x * (1.0f / 256.0f));
   __syncthreads();
-  Item<BF16> xv[kUnroll];
-  tile_loop(
+  Item<BF16> xv[kU<BF16>];
+  tile_loop<kU<BF16>>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t it) {
         const uint32_t a8 = item_amax_bits<BF16>(xv[u]);
@@ -960,8 +968,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_mbs(const uint32_t *__r
                                                              const uint8_t *__restrict__ sub_scales,
                                                              const uint8_t *__restrict__ macro_mant,
                                                              void *__restrict__ y, int64_t nitems) {
-  uint32_t cw[kUnroll], sb[kUnroll], mb[kUnroll];
-  tile_loop(
+  uint32_t cw[kU<BF16>], sb[kU<BF16>], mb[kU<BF16>];
+  tile_loop<kU<BF16>>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
@@ -991,8 +999,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_mbs(const uint32_t *__r
 
 // ---- launchers -----------------------------------------------------------------
 
-static unsigned grid_for(int64_t nitems, int64_t cap) {
-  const int64_t tile = (int64_t)kThreads * kUnroll;
+static unsigned grid_for(int64_t nitems, int64_t cap, int unroll = kUnroll) {
+  const int64_t tile = (int64_t)kThreads * unroll;
   int64_t g = (nitems + tile - 1) / tile;
   if (g > cap) g = cap;
   if (g < 1) g = 1;
@@ -1021,7 +1029,7 @@ using namespace mxk;
 
 hipError_t mxi_launch_quantize(const void *x, int bf16, int mode, int64_t nitems,
                                uint8_t *codes, uint8_t *scales, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
   if (bf16) {
     MX_DISPATCH_MODE(k_quantize, true, mode, g, b, st, x, c, scales, nitems)
@@ -1033,7 +1041,7 @@ hipError_t mxi_launch_quantize(const void *x, int bf16, int mode, int64_t nitems
 
 hipError_t mxi_launch_fakequant(const void *x, int bf16, int mode, int64_t nitems, void *y,
                                 hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   if (bf16) {
     MX_DISPATCH_MODE(k_fakequant, true, mode, g, b, st, x, y, nitems)
   } else {
@@ -1044,7 +1052,7 @@ hipError_t mxi_launch_fakequant(const void *x, int bf16, int mode, int64_t nitem
 
 hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, int bf16,
                                  int64_t nitems, void *y, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
   if (bf16)
     hipLaunchKernelGGL((k_dequantize<true>), g, b, 0, st, c, scales, y, nitems);
@@ -1091,7 +1099,7 @@ hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
 
 hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                 uint8_t *scales, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   u32x2 *c = reinterpret_cast<u32x2 *>(codes);
   if (bf16)
     hipLaunchKernelGGL((k_quantize8<true>), g, b, 0, st, x, c, scales, nitems);
@@ -1102,7 +1110,7 @@ hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t nitems, uint8_t
 
 hipError_t mxi_launch_dequantize8(const uint8_t *codes, const uint8_t *scales, int bf16,
                                   int64_t nitems, void *y, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   const u32x2 *c = reinterpret_cast<const u32x2 *>(codes);
   if (bf16)
     hipLaunchKernelGGL((k_dequantize8<true>), g, b, 0, st, c, scales, y, nitems);
@@ -1113,7 +1121,7 @@ hipError_t mxi_launch_dequantize8(const uint8_t *codes, const uint8_t *scales, i
 
 hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *y,
                                  hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   if (bf16)
     hipLaunchKernelGGL((k_fakequant8<true>), g, b, 0, st, x, y, nitems);
   else
@@ -1148,7 +1156,7 @@ hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t nitems, uint8
 hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_scales,
                                     const uint8_t *tensor_scale, int bf16, int64_t nitems, void *y,
                                     hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
   if (bf16)
     hipLaunchKernelGGL((k_dequantize_nv<true>), g, b, 0, st, c, block_scales, tensor_scale, y,
@@ -1161,7 +1169,7 @@ hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_s
 
 hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                    uint8_t *sub_scales, uint8_t *macro_mant, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
   if (bf16)
     hipLaunchKernelGGL((k_quantize_mbs<true>), g, b, 0, st, x, c, sub_scales, macro_mant, nitems);
@@ -1173,7 +1181,7 @@ hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint
 hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
                                      const uint8_t *macro_mant, int bf16, int64_t nitems, void *y,
                                      hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
   if (bf16)
     hipLaunchKernelGGL((k_dequantize_mbs<true>), g, b, 0, st, c, sub_scales, macro_mant, y, nitems);
