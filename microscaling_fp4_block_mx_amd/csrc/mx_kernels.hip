@@ -190,6 +190,19 @@ __device__ __forceinline__ uint32_t ocp_scale_byte(uint32_t amax_bits) {
 // Scale operand of the converts for byte s.
 __device__ __forceinline__ float scale_operand(uint32_t s) { return __uint_as_float(s << 23); }
 
+// fl32(a / 6) for the non-negative fp32 pattern a. From 2^-125 up, the
+// product with fl32(1/6) plus one fma residual correction is the correctly
+// rounded quotient (checked against IEEE division for every fp32 value in
+// that range); below it, where the quotient is subnormal, IEEE division.
+__device__ __forceinline__ float div6(uint32_t a_bits) {
+  const float a = __uint_as_float(a_bits);
+  if (__builtin_expect(a_bits < 0x01000000u, 0)) return a / 6.0f;
+  constexpr float kSixth = 1.0f / 6.0f;
+  const float q0 = a * kSixth;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, a), kSixth, q0);
+}
+
+
 // 8 codes of the item at scale byte s (finite block), packed in one word,
 // element i in nibble i.
 template <bool BF16>
@@ -734,9 +747,19 @@ __global__ __launch_bounds__(kThreads) void k_fakequant8(const void *x, void *y,
 // saturating, of x * (S / s_b) in fp32 (IEEE division for the reciprocal
 // factor). E4M3 and E2M1 rounding use the scaled converts at scale 1.
 
-// Largest finite |x| bit pattern of the item (non-finite lanes count as 0).
+#ifndef MX_NV_GRID_CAP
+#define MX_NV_GRID_CAP 2048
+#endif
+constexpr int kNvPer = MX_NV_GRID_CAP / kThreads;  // first-pass maxima per thread
+static_assert(kNvPer * kThreads == MX_NV_GRID_CAP, "grid cap must be a multiple of 256");
+
+// Largest finite |x| bit pattern of the item (non-finite elements count as
+// 0): the plain maximum when the item holds no NaN/Inf, else element by
+// element.
 template <bool BF16>
 __device__ __forceinline__ uint32_t item_finite_amax_bits(const Item<BF16> &x) {
+  const uint32_t all = item_amax_bits<BF16>(x);
+  if (__builtin_expect(all < 0x7F800000u, 1)) return all;
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -788,20 +811,32 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *__restrict
                                                           uint8_t *__restrict__ block_scales,
                                                           uint8_t *__restrict__ tensor_scale,
                                                           int64_t nitems) {
-  // every workgroup reduces the first pass's maxima (order-free)
-  __shared__ uint32_t red[kThreads];
-  uint32_t a = 0;
-  for (int i = threadIdx.x; i < npartial; i += kThreads) a = max(a, partial[i]);
-  red[threadIdx.x] = a;
-  __syncthreads();
-  for (int w = kThreads / 2; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + w]);
-    __syncthreads();
+  // every workgroup reduces the first pass's maxima (max is order-free and
+  // idempotent, so clamped duplicate loads are harmless; all loads are issued
+  // before the first use), and fills a table of fl32(1 / v) for the E4M3
+  // values v (code 0 -> 0; code 0x7F is NaN and never looked up)
+  __shared__ uint32_t wave_max[kThreads / 64];
+  __shared__ float rcp_e4m3[128];
+  const float one = 1.0f;  // scale operand of the converts: 2^0
+  uint32_t pv[kNvPer];
+#pragma unroll
+  for (int j = 0; j < kNvPer; j++) pv[j] = partial[min((int)threadIdx.x + j * kThreads, npartial - 1)];
+  if (threadIdx.x < 128) {
+    const float v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(threadIdx.x, one, false)[0];
+    rcp_e4m3[threadIdx.x] = threadIdx.x == 0 ? 0.0f : 1.0f / v;
   }
-  const int t = nv_tensor_exp(red[0]);
+  uint32_t a = 0;
+#pragma unroll
+  for (int j = 0; j < kNvPer; j++) a = max(a, pv[j]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off, 64));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = a;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; w++) a = max(a, wave_max[w]);
+  const int t = nv_tensor_exp(a);
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = (uint8_t)(t + 127);
   const float S = __uint_as_float((uint32_t)(t + 127) << 23);
-  const float one = 1.0f;  // scale operand of the converts: 2^0
 
   Item<BF16> xv[kUnroll];
   tile_loop<kUnroll>(
@@ -814,13 +849,15 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *__restrict
           sbyte = 0x7Fu;
           c = sign_codes<BF16>(xv[u]);
         } else {
-          const float q6 = __uint_as_float(ab) / 6.0f;
+          const float q6 = div6(ab);
           const float tb = fminf(q6 * S, 448.0f);
           s16x2 w = {0, 0};
           w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, tb, tb, one, false);
           sbyte = (uint32_t)w[0] & 0xFFu;
-          const float sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sbyte, one, false)[0];
-          const float r = sv > 0.0f ? S / sv : 0.0f;
+          // S / s_b = 2^t * fl32(1 / s_b) exactly: scaling by a power of two
+          // commutes with rounding, and 2^t / s_b is never subnormal (t >= -117,
+          // s_b <= 448); both overflow to Inf together
+          const float r = rcp_e4m3[sbyte] * S;
           float v[8];
 #pragma unroll
           for (int i = 0; i < 8; i++) v[i] = elem<BF16>(xv[u], i) * r;
@@ -895,18 +932,6 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
   v = max(v, dpp_ror4(v));
   v = max(v, dpp_ror8(v));
   return v;
-}
-
-// fl32(a / 6) for the non-negative fp32 pattern a. From 2^-125 up, the
-// product with fl32(1/6) plus one fma residual correction is the correctly
-// rounded quotient (checked against IEEE division for every fp32 value in
-// that range); below it, where the quotient is subnormal, IEEE division.
-__device__ __forceinline__ float div6(uint32_t a_bits) {
-  const float a = __uint_as_float(a_bits);
-  if (__builtin_expect(a_bits < 0x01000000u, 0)) return a / 6.0f;
-  constexpr float kSixth = 1.0f / 6.0f;
-  const float q0 = a * kSixth;
-  return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, a), kSixth, q0);
 }
 
 template <bool BF16>
@@ -1129,17 +1154,13 @@ hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *
   return hipGetLastError();
 }
 
-#ifndef MX_NV_GRID_CAP
-#define MX_NV_GRID_CAP 2048
-#endif
-
 size_t mxi_nvfp4_partials(int64_t nitems) { return grid_for(nitems, MX_NV_GRID_CAP); }
 
 hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                   uint8_t *block_scales, uint8_t *tensor_scale,
                                   uint32_t *partial, hipStream_t st) {
   const unsigned gp = grid_for(nitems, MX_NV_GRID_CAP);
-  const dim3 g(grid_for(nitems, MX_GRID_CAP)), b(kThreads);
+  const dim3 g(gp), b(kThreads);
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
   if (bf16) {
     hipLaunchKernelGGL((k_absmax_partials<true>), dim3(gp), b, 0, st, x, partial, nitems);
