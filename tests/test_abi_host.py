@@ -181,3 +181,26 @@ def test_nvfp4_validation(lib):
     assert mx.mx_dequantize_nvfp4(B, C, W, 1, 16, 0, None, None) == mx.MX_ERR_NULL
     assert mx.mx_dequantize_nvfp4(B, C, W, 4, 64, 0, B + 32, None) == mx.MX_ERR_ALIAS
     assert mx.mx_dequantize_nvfp4(B, C, W, 1, 16, 0, A + 8, None) == mx.MX_ERR_ALIGN
+
+
+def test_mbs_validation(lib):
+    # k must be a multiple of the 128-element macro block
+    assert mx.mx_quantize_mbs(A, 1, 1, 64, B, C, W, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_dequantize_mbs(B, C, W, 1, 96, 1, A, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_quantize_mbs(A, 1, -1, 128, B, C, W, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_quantize_mbs(A, 2, 1, 128, B, C, W, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_dequantize_mbs(B, C, W, 1, 128, 7, A, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_quantize_mbs(A, 1, 0, 128, None, None, None, None) == mx.MX_OK
+    assert mx.mx_dequantize_mbs(None, None, None, 0, 128, 0, None, None) == mx.MX_OK
+    assert mx.mx_quantize_mbs(A, 1, 1, 128, B, C, None, None) == mx.MX_ERR_NULL
+    assert mx.mx_dequantize_mbs(B, None, W, 1, 128, 0, A, None) == mx.MX_ERR_NULL
+    for bad in ((A + 8, B, C, W), (A, B + 4, C, W), (A, B, C + 1, W), (A, B, C, W + 2)):
+        assert mx.mx_quantize_mbs(bad[0], 1, 1, 128, *bad[1:], None) == mx.MX_ERR_ALIGN
+    assert mx.mx_dequantize_mbs(B, C, W, 1, 128, 0, A + 4, None) == mx.MX_ERR_ALIGN
+    # codes [rows, k/2], sub-scales [rows, k/16], macro bytes [rows, k/128]
+    assert mx.mx_quantize_mbs(A, 1, 4, 256, A + 1024, C, W, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_quantize_mbs(A, 1, 4, 256, B, B + 496, W, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_quantize_mbs(A, 1, 4, 256, B, C, C + 48, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_quantize_mbs(A, 1, 4, 256, B, C, B + 16, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_dequantize_mbs(B, C, W, 4, 256, 0, B + 256, None) == mx.MX_ERR_ALIAS
+    assert mx.mx_dequantize_mbs(B, C, W, 4, 256, 1, W - 16, None) == mx.MX_ERR_ALIAS
