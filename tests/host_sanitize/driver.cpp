@@ -1,0 +1,161 @@
+// Host-only exercise of the C ABI (mx_api.cpp) against recording launcher
+// stubs: every entry point's accepted calls reach the right launcher with
+// the right item count, dtype, mode and pointers; rejected calls reach none;
+// a failing launch turns into MX_ERR_HIP with a per-thread detail string.
+// Built and run under sanitizers by tests/test_host_sanitizers.py.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <thread>
+
+#include "mx.h"
+#include "stubs.h"
+
+static int g_fail = 0;
+#define CHECK(c)                                                    \
+  do {                                                              \
+    if (!(c)) {                                                     \
+      fprintf(stderr, "%s:%d: CHECK failed: %s\n", __FILE__, __LINE__, #c); \
+      g_fail++;                                                     \
+    }                                                               \
+  } while (0)
+
+static void *P(uintptr_t a) { return reinterpret_cast<void *>(a); }
+static const uintptr_t X = 1ull << 32, Cd = 2ull << 32, Sc = 3ull << 32, Y = 4ull << 32,
+                       Ws = 5ull << 32, Ts = 6ull << 32;
+
+// an accepted call: exactly one launch, of `name`, with `nitems`
+static void expect_launch(mx_status_t st, const char *name, int64_t nitems, int before) {
+  CHECK(st == MX_OK);
+  CHECK(g_calls == before + 1);
+  CHECK(g_last.name && strcmp(g_last.name, name) == 0);
+  CHECK(g_last.nitems == nitems);
+}
+
+static void mxfp4() {
+  int n0 = g_calls;
+  expect_launch(mx_quantize(P(X), MX_BF16, 64, 4096, MX_SCALE_OAS_NF, (uint8_t *)P(Cd),
+                            (uint8_t *)P(Sc), nullptr),
+                "quantize", 64 * 4096 / 8, n0);
+  CHECK(g_last.bf16 == 1 && g_last.mode == MX_SCALE_OAS_NF && g_last.p[0] == P(X) &&
+        g_last.p[1] == P(Cd) && g_last.p[2] == P(Sc));
+  n0 = g_calls;
+  expect_launch(mx_dequantize((uint8_t *)P(Cd), (uint8_t *)P(Sc), 3, 96, MX_F32, P(Y), nullptr),
+                "dequantize", 3 * 96 / 8, n0);
+  CHECK(g_last.bf16 == 0 && g_last.p[2] == P(Y));
+  n0 = g_calls;
+  expect_launch(mx_fakequant(P(X), MX_F32, 5, 32, MX_SCALE_OCP, P(X), nullptr), "fakequant",
+                5 * 32 / 8, n0);  // in place is allowed
+  n0 = g_calls;
+  const size_t wsb = mx_block_mse_workspace_size(1000, 4096);
+  CHECK(wsb >= 16 && wsb % 8 == 0);
+  expect_launch(mx_block_mse(P(X), MX_BF16, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 1000, 4096,
+                             (float *)P(Y), (double *)P(Ts), P(Ws), wsb, nullptr),
+                "block_mse", 1000 * 4096 / 8, n0);
+  CHECK(g_last.p[4] == P(Ts) && g_last.p[5] == P(Ws));
+  // rows == 0: nothing launched, except block_mse's zero write of the sums
+  n0 = g_calls;
+  CHECK(mx_quantize(nullptr, MX_BF16, 0, 32, MX_SCALE_OCP, nullptr, nullptr, nullptr) == MX_OK);
+  CHECK(mx_dequantize(nullptr, nullptr, 0, 32, MX_F32, nullptr, nullptr) == MX_OK);
+  CHECK(g_calls == n0);
+  expect_launch(mx_block_mse(nullptr, MX_BF16, nullptr, nullptr, 0, 32, nullptr, (double *)P(Ts),
+                             P(Ws), 16, nullptr),
+                "block_mse", 0, n0);
+  // rejected calls launch nothing
+  n0 = g_calls;
+  CHECK(mx_quantize(P(X), MX_BF16, 1, 48, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr) == MX_ERR_SHAPE);
+  CHECK(mx_quantize(P(X), MX_BF16, INT64_MAX, 32, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr) == MX_ERR_SHAPE);
+  CHECK(mx_quantize(P(X), MX_BF16, INT64_MAX / 2, INT64_MAX / 64 * 32, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr) == MX_ERR_SHAPE);
+  CHECK(mx_quantize(P(X), (mx_dtype_t)7, 1, 32, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr) == MX_ERR_DTYPE);
+  CHECK(mx_quantize(P(X), MX_BF16, 1, 32, (mx_scale_mode_t)4, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr) == MX_ERR_MODE);
+  CHECK(mx_quantize(P(X), MX_BF16, 1, 32, (mx_scale_mode_t)-1, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr) == MX_ERR_MODE);
+  CHECK(mx_quantize(P(X + 2), MX_BF16, 1, 32, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr) == MX_ERR_ALIGN);
+  CHECK(mx_quantize(P(X), MX_BF16, 4, 64, MX_SCALE_OCP, (uint8_t *)P(X + 64), (uint8_t *)P(Sc), nullptr) == MX_ERR_ALIAS);
+  CHECK(mx_fakequant(P(X), MX_BF16, 4, 64, MX_SCALE_OCP, P(X + 16), nullptr) == MX_ERR_ALIAS);
+  CHECK(mx_block_mse(P(X), MX_BF16, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 1, 32, nullptr, nullptr, nullptr, 0, nullptr) == MX_ERR_NULL);
+  CHECK(mx_block_mse(P(X), MX_BF16, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 1, 32, nullptr, (double *)P(Ts), P(Ws), 8, nullptr) == MX_ERR_WORKSPACE);
+  CHECK(g_calls == n0);
+}
+
+static void mxfp8_nvfp4_mbs() {
+  int n0 = g_calls;
+  expect_launch(mx_quantize_mxfp8(P(X), MX_F32, 7, 64, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr),
+                "quantize8", 7 * 64 / 8, n0);
+  n0 = g_calls;
+  expect_launch(mx_dequantize_mxfp8((uint8_t *)P(Cd), (uint8_t *)P(Sc), 7, 64, MX_BF16, P(Y), nullptr),
+                "dequantize8", 7 * 64 / 8, n0);
+  n0 = g_calls;
+  expect_launch(mx_fakequant_mxfp8(P(X), MX_BF16, 2, 32, P(Y), nullptr), "fakequant8", 8, n0);
+  n0 = g_calls;
+  const size_t nvb = mx_nvfp4_workspace_size(9, 48);
+  CHECK(nvb >= 4 && nvb % 4 == 0);
+  expect_launch(mx_quantize_nvfp4(P(X), MX_BF16, 9, 48, (uint8_t *)P(Cd), (uint8_t *)P(Sc),
+                                  (uint8_t *)P(Ts), P(Ws), nvb, nullptr),
+                "quantize_nv", 9 * 48 / 8, n0);
+  CHECK(g_last.p[4] == P(Ts) && g_last.p[5] == P(Ws));
+  n0 = g_calls;
+  expect_launch(mx_dequantize_nvfp4((uint8_t *)P(Cd), (uint8_t *)P(Sc), (uint8_t *)P(Ts), 9, 48,
+                                    MX_F32, P(Y), nullptr),
+                "dequantize_nv", 9 * 48 / 8, n0);
+  n0 = g_calls;
+  expect_launch(mx_quantize_mbs(P(X), MX_F32, 3, 384, (uint8_t *)P(Cd), (uint8_t *)P(Sc),
+                                (uint8_t *)P(Ts), nullptr),
+                "quantize_mbs", 3 * 384 / 8, n0);
+  CHECK(g_last.p[3] == P(Ts) && g_last.bf16 == 0);
+  n0 = g_calls;
+  expect_launch(mx_dequantize_mbs((uint8_t *)P(Cd), (uint8_t *)P(Sc), (uint8_t *)P(Ts), 3, 384,
+                                  MX_BF16, P(Y), nullptr),
+                "dequantize_mbs", 3 * 384 / 8, n0);
+  n0 = g_calls;
+  CHECK(mx_quantize_mbs(P(X), MX_F32, 3, 320, (uint8_t *)P(Cd), (uint8_t *)P(Sc), (uint8_t *)P(Ts), nullptr) == MX_ERR_SHAPE);
+  CHECK(mx_quantize_nvfp4(P(X), MX_BF16, 9, 40, (uint8_t *)P(Cd), (uint8_t *)P(Sc), (uint8_t *)P(Ts), P(Ws), nvb, nullptr) == MX_ERR_SHAPE);
+  CHECK(mx_quantize_nvfp4(P(X), MX_BF16, 9, 48, (uint8_t *)P(Cd), (uint8_t *)P(Sc), (uint8_t *)P(Ts), P(Ws + 2), nvb, nullptr) == MX_ERR_WORKSPACE);
+  CHECK(g_calls == n0);
+}
+
+// a failing launch reports MX_ERR_HIP; the detail string is per thread
+static void hip_errors() {
+  const int64_t k = 8 * kFailItems;  // one row whose item count makes the stub fail
+  CHECK(mx_quantize(P(X), MX_BF16, 1, k, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr) == MX_ERR_HIP);
+  CHECK(strcmp(mx_last_error_detail(), "stubbed launch failure") == 0);
+  CHECK(mx_quantize_mbs(P(X), MX_BF16, 1, k, (uint8_t *)P(Cd), (uint8_t *)P(Sc), (uint8_t *)P(Ts), nullptr) == MX_ERR_HIP);
+  bool other_clean = false;
+  std::thread t([&] { other_clean = mx_last_error_detail()[0] == '\0'; });
+  t.join();
+  CHECK(other_clean);
+  for (int s = 0; s <= 8; s++) CHECK(strncmp(mx_status_string((mx_status_t)s), "MX_", 3) == 0);
+  CHECK(strstr(mx_status_string((mx_status_t)99), "unknown") != nullptr);
+}
+
+// many threads validating and launching at once (shared state would race)
+static void threads() {
+  std::thread ts[8];
+  int bad[8] = {};
+  for (int i = 0; i < 8; i++) {
+    ts[i] = std::thread([i, &bad] {
+      for (int r = 0; r < 2000; r++) {
+        const bool fail = (r + i) % 3 == 0;
+        const int64_t k = fail ? 8 * kFailItems : 32 * (1 + r % 7);
+        const mx_status_t st = mx_quantize(P(X), MX_BF16, 1, k, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc), nullptr);
+        if (st != (fail ? MX_ERR_HIP : MX_OK)) bad[i]++;
+        if (g_last.nitems != k / 8) bad[i]++;
+      }
+    });
+  }
+  for (auto &t : ts) t.join();
+  for (int i = 0; i < 8; i++) CHECK(bad[i] == 0);
+}
+
+int main() {
+  mxfp4();
+  mxfp8_nvfp4_mbs();
+  hip_errors();
+  threads();
+  if (g_fail) {
+    fprintf(stderr, "%d check(s) failed\n", g_fail);
+    return 1;
+  }
+  printf("host ABI checks passed\n");
+  return 0;
+}
