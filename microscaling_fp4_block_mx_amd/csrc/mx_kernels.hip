@@ -99,9 +99,10 @@ __device__ __forceinline__ double quad_sum_f64(double p) {
 // accesses cover 1 KiB contiguously, so bf16 tensors are read and written
 // with the non-temporal hint (no reuse; fewer dirty L2 lines to write back
 // at the end of the kernel). fp32 items take two 16-byte accesses whose
-// per-instruction footprint is strided (32-byte lane pitch): those, and the
-// small code/scale accesses, stay on the default cache policy, which
-// measured faster for them.
+// per-instruction footprint is strided (32-byte lane pitch): fp32 loads,
+// and the small code/scale accesses, stay on the default cache policy,
+// which measured faster for them; fp32 stores are regrouped through LDS into
+// contiguous non-temporal stores (store_item).
 template <bool NT, typename T>
 __device__ __forceinline__ T ld(const T *p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -122,6 +123,9 @@ struct Item {
   uint32_t w[BF16 ? 4 : 8];
 };
 
+// One item's 8 elements. (fp32 items are read directly, two 16-byte loads
+// per lane: a variant that read 1 KiB-contiguous units and swapped them into
+// place through LDS measured no faster, unlike the stores below.)
 template <bool BF16>
 __device__ __forceinline__ void load_item(const void *base, int64_t it, Item<BF16> &x) {
   if constexpr (BF16) {
@@ -140,6 +144,15 @@ __device__ __forceinline__ void load_item(const void *base, int64_t it, Item<BF1
 }
 
 // Store the output words of one item (bf16: 4 words, fp32: 8 words).
+//
+// An fp32 item is 32 bytes, so two direct 16-byte stores per lane leave
+// every store instruction writing half of each 32-byte span (lane pitch 32
+// bytes). When the whole wave is active its 64 items are consecutive, so
+// the wave first passes its 2 KiB through LDS: lane j writes its two
+// 16-byte halves to units 2j and 2j+1, then lane L stores units L and
+// 64 + L, and each store instruction writes 1 KiB contiguously with the
+// non-temporal hint (measured: fp32 dequantize 29.4 -> 22.5 us on 32 Mi
+// elements). A partly active wave (the ragged tail) stores directly.
 template <bool BF16>
 __device__ __forceinline__ void store_item(void *base, int64_t it,
                                            const uint32_t (&y)[BF16 ? 4 : 8]) {
@@ -147,8 +160,30 @@ __device__ __forceinline__ void store_item(void *base, int64_t it,
     st<true>(reinterpret_cast<u32x4 *>(base) + it, u32x4{y[0], y[1], y[2], y[3]});
   } else {
     u32x4 *p = reinterpret_cast<u32x4 *>(base) + 2 * it;
-    st<false>(p, u32x4{y[0], y[1], y[2], y[3]});
-    st<false>(p + 1, u32x4{y[4], y[5], y[6], y[7]});
+    const u32x4 lo = {y[0], y[1], y[2], y[3]}, hi = {y[4], y[5], y[6], y[7]};
+    if (__builtin_amdgcn_read_exec() == ~0ull) {
+      __shared__ u32x4 xpose[kThreads / 64][128];
+      u32x4 *w = xpose[threadIdx.x >> 6];
+      const int lane = (int)(threadIdx.x & 63);
+      w[2 * lane] = lo;
+      w[2 * lane + 1] = hi;
+      // the other lanes' writes must land before the reads (one wave: LDS
+      // runs its instructions in order; the fences keep the compiler's order)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const u32x4 a = w[lane], b = w[64 + lane];
+      // and every read here before the next item's writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      u32x4 *q = p - 2 * lane;  // the wave's first item
+      st<true>(q + lane, a);
+      st<true>(q + 64 + lane, b);
+    } else {
+      st<false>(p, lo);
+      st<false>(p + 1, hi);
+    }
   }
 }
 
