@@ -45,8 +45,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef MX_UNROLL
 #define MX_UNROLL 4
 #endif
+// Most workgroups a streaming launch uses (beyond it, workgroups loop over
+// tiles). Measured on a 2.1e9-element bf16 tensor: 196,608 (768 per CU)
+// beat 65,536 by 5 % (quantize) and 3 % (dequantize) with fake-quant level,
+// while 8,192-32,768 were slower. Tensors below ~200 M elements get one tile
+// per workgroup either way.
 #ifndef MX_GRID_CAP
-#define MX_GRID_CAP 65536
+#define MX_GRID_CAP 196608
 #endif
 constexpr int kThreads = 256;
 constexpr int kUnroll = MX_UNROLL;  // items per thread per grid-stride step
