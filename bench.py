@@ -316,7 +316,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x_host, args.cpu_seconds)
+        cpu = cpu_baseline(x_host, args.cpu_seconds, sets[0]["x"])
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -336,48 +336,95 @@ def main():
         "quality": quality,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "env": {"device": torch.cuda.get_device_name(dev), "torch": torch.__version__,
+                "hip": torch.version.hip},
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(x_host, target_s):
-    """The oracle as it stands, on the host cores, over a bounded sample of
-    the same workload (leading rows), running the same step."""
-    import numpy as np
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def cpu_baseline(x_host, target_s, x_dev):
+    """The oracle as it stands, on the host cores, over a bounded sample of
+    the same workload (leading rows), running the same step: first on every
+    core, then on one thread over a smaller sample. The first sample's oracle
+    outputs are also compared with the library's on the same rows (codes and
+    scales of both modes, dequantize, fake-quant bit for bit; block MSE and
+    tensor sums to a relative 1e-6)."""
+    import numpy as np
+    import torch
+
+    import microscaling_fp4_block_mx_amd as mx
     import oracle
     import workloads
 
     oracle.build(force=not os.path.exists(os.path.join(ROOT, "oracle", "libmxref.so")))
     cores = max(1, len(os.sched_getaffinity(0)))
     xs_full = workloads.to_bf16_bits(x_host)
-    rows = 256
-    xs = np.ascontiguousarray(xs_full[:rows])
-    n = xs.size
-    bytes_step = sum(BYTES_PER_ELEM[o] for o in OPS) * n
-    done, t0 = 0, time.perf_counter()
-    while True:
-        c, s = oracle.quantize(xs, "ocp", threads=cores)
-        oracle.quantize(xs, "oas", threads=cores)
-        oracle.dequantize(c, s, "bf16", threads=cores)
-        oracle.fakequant(xs, "ocp", threads=cores)
-        oracle.block_mse(xs, c, s, threads=cores)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= target_s:
-            break
-        if done == 1:  # size the sample so the loop lands near the target
-            rows_next = int(min(xs_full.shape[0], rows * max(1.0, target_s / max(el, 1e-3) / 3)))
-            if rows_next > rows:
-                rows = rows_next
-                xs = np.ascontiguousarray(xs_full[:rows])
-                n = xs.size
-                bytes_step = sum(BYTES_PER_ELEM[o] for o in OPS) * n
-                done, t0 = 0, time.perf_counter()
-    gbs = done * bytes_step / el / 1e9
+    k = xs_full.shape[1]
+
+    def step(xs, threads):
+        c, s = oracle.quantize(xs, "ocp", threads=threads)
+        c2, s2 = oracle.quantize(xs, "oas", threads=threads)
+        y = oracle.dequantize(c, s, "bf16", threads=threads)
+        f = oracle.fakequant(xs, "ocp", threads=threads)
+        bm = oracle.block_mse(xs, c, s, threads=threads, with_energy=True)
+        return c, s, c2, s2, y, f, bm
+
+    def timed(rows, threads, budget):
+        xs = np.ascontiguousarray(xs_full[:rows])
+        done, t0, out = 0, time.perf_counter(), None
+        while True:
+            out = step(xs, threads)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return rows, done, el, out
+            if done == 1 and rows < xs_full.shape[0]:  # size the sample to land near the budget
+                grow = int(min(xs_full.shape[0], rows * max(1.0, budget / max(el, 1e-3) / 3)))
+                if grow > rows:
+                    rows = grow
+                    xs = np.ascontiguousarray(xs_full[:rows])
+                    done, t0 = 0, time.perf_counter()
+
+    bpe = sum(BYTES_PER_ELEM[o] for o in OPS)
+    rows, done, el, out = timed(256, cores, 0.7 * target_s)
+    gbs = done * bpe * rows * k / el / 1e9
+    rows1, done1, el1, _ = timed(16, 1, 0.3 * target_s)
+    gbs1 = done1 * bpe * rows1 * k / el1 / 1e9
+
+    # the library on the same rows
+    c, s, c2, s2, y, f, (wbm, wsse, wssq) = out
+    xd = x_dev[:rows].contiguous()
+    gc, gs = mx.quantize(xd, "ocp")
+    gc2, gs2 = mx.quantize(xd, "oas")
+    gy = mx.dequantize(gc, gs, torch.bfloat16)
+    gf = mx.fakequant(xd, "ocp")
+    gbm, gsums = mx.block_mse(xd, gc, gs)
+    sse, ssq = gsums.tolist()
+    same = {
+        "codes_scales_ocp": bool(np.array_equal(gc.cpu().numpy(), c) and np.array_equal(gs.cpu().numpy(), s)),
+        "codes_scales_oas": bool(np.array_equal(gc2.cpu().numpy(), c2) and np.array_equal(gs2.cpu().numpy(), s2)),
+        "dequantize": bool(np.array_equal(workloads.to_bf16_bits(gy), y)),
+        "fakequant": bool(np.array_equal(workloads.to_bf16_bits(gf), f)),
+        "block_mse_rel_1e-6": bool(np.allclose(gbm.cpu().numpy(), wbm, rtol=1e-6, atol=0)
+                                   and abs(sse - wsse) <= 1e-6 * wsse and abs(ssq - wssq) <= 1e-6 * wssq),
+    }
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} step(s) over the first {rows} rows x 4096 of the same tensor "
-                      f"({el:.1f} s)"}
+            "sample": f"{done} step(s) over the first {rows} rows x {k} of the same tensor "
+                      f"({el:.1f} s, {cores} threads)",
+            "single_thread": {"value": round(gbs1, 3), "unit": "GB/s",
+                              "sample": f"{done1} step(s) over the first {rows1} rows ({el1:.1f} s)"},
+            "cpu_model": cpu_model(),
+            "sample_matches_library": same}
 
 
 # ---- per-workload suite -----------------------------------------------------
