@@ -11,9 +11,10 @@ Infinity Cache cannot serve a step from the previous one.
 Prints ONE JSON line. --gpus N with N > 1 exits: this path runs on one GPU.
 
 --suite instead times each operation on the other workloads alone (fp32
-normal [1024, 4096]; the Llama-3.2-3B-shaped linear stack, per matrix and
-grouped by K; the 128-expert MoE weights; bf16 Laplace [16384, 8192] with
-sparse outliers), with per-launch HIP events (median, p10, p90), warm
+normal [1024, 4096]; the Llama-3.2-3B-shaped linear stack, per matrix, as one
+multi-tensor call and grouped by K; the 128-expert MoE weights; bf16 Laplace
+[16384, 8192] with sparse outliers), with per-launch HIP events (median, p10,
+p90), warm
 (cache-resident) and cold (rotated) figures where the tensor fits the cache,
 and for the small fp32 case the host-side single-launch latency and the
 per-launch time inside a replayed HIP graph. It prints one JSON line per
@@ -652,8 +653,17 @@ def suite(args, dev):
         ok(mx.mx_quantize(b.data_ptr(), mx.MX_BF16, b.shape[0], b.shape[1], mx.MX_SCALE_OCP,
                           cb.data_ptr(), sb.data_ptr(), sh))
 
+    descs = (mx.MxTensor * len(mats))()
+    for i, (t, c, s_, r0, rows, k) in enumerate(mats):
+        descs[i] = mx.MxTensor(t[r0].data_ptr(), None, c[r0].data_ptr(), s_[r0].data_ptr(), rows, k)
+
+    def multi(_):
+        ok(mx.mx_quantize_multi(descs, len(mats), mx.MX_BF16, mx.MX_SCALE_OCP, sh))
+
     report(WL, "quantize_ocp (196 per-matrix launches)", bytes_q,
            _launch_stats(per_matrix, 20, 3, stream), cache="exceeds cache")
+    report(WL, "quantize_ocp (196 matrices, one multi-tensor call)", bytes_q,
+           _launch_stats(multi, 20, 3, stream), cache="exceeds cache")
     report(WL, "quantize_ocp (2 launches grouped by K)", bytes_q,
            _launch_stats(grouped, 20, 3, stream), cache="exceeds cache")
     del a, b, ca, sa, cb, sb, mats

@@ -226,10 +226,46 @@ mx_status_t mx_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
                               int64_t k, mx_dtype_t y_dtype, void *y,
                               void *stream);
 
+/* ---- Many tensors in one call ---------------------------------------------
+ * QAT fake-quantizes every Linear weight on each forward pass and a
+ * converted checkpoint quantizes every one of them (Axolotl MXFP4 QAT page,
+ * QATConfig section: weights of each Linear layer); vLLM's online path does
+ * the same for each expert's weights ("MXFP4: 4-bit MoE" section). These
+ * entry points take a list of separate tensors and cover them with one
+ * launch per MX_MULTI_MAX (48) tensors instead of one per tensor, with
+ * results identical to the single-tensor calls.
+ *
+ * `tensors` is a HOST array of `count` descriptors, read during the call
+ * only; every pointer inside is a device pointer, 16-byte aligned. All
+ * tensors share `dtype` and `mode`; each has its own rows and k (k % 32 ==
+ * 0; rows == 0 skips it). mx_quantize_multi uses x, codes [rows, k/2] and
+ * scales [rows, k/32]; mx_fakequant_multi uses x and y [rows, k] (y may
+ * equal x). No output may overlap another tensor's input or output
+ * (inputs may be shared): MX_ERR_ALIAS. count == 0 does nothing; count < 0
+ * is MX_ERR_SHAPE. On a per-tensor validation error nothing is launched and
+ * mx_last_error_detail() names the tensor. Validation compares every output
+ * range with every other range, so its host cost grows with count^2. */
+typedef struct {
+  const void *x;   /* input [rows, k] */
+  void *y;         /* mx_fakequant_multi: output [rows, k]; else unused */
+  uint8_t *codes;  /* mx_quantize_multi: [rows, k/2]; else unused */
+  uint8_t *scales; /* mx_quantize_multi: [rows, k/32]; else unused */
+  int64_t rows;
+  int64_t k;
+} mx_tensor_t;
+mx_status_t mx_quantize_multi(const mx_tensor_t *tensors, int count,
+                              mx_dtype_t dtype, mx_scale_mode_t mode,
+                              void *stream);
+mx_status_t mx_fakequant_multi(const mx_tensor_t *tensors, int count,
+                               mx_dtype_t dtype, mx_scale_mode_t mode,
+                               void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *mx_status_string(mx_status_t s);
 
-/* Detail of the last MX_ERR_HIP on the calling thread ("" if none). */
+/* Detail of the calling thread's most recent failure that recorded one
+ * ("" if none): the HIP error text of an MX_ERR_HIP, or which tensor of a
+ * multi-tensor call failed validation. */
 const char *mx_last_error_detail(void);
 
 #ifdef __cplusplus

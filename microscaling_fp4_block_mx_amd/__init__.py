@@ -38,8 +38,8 @@ _DTYPES = {torch.float32: MX_F32, torch.bfloat16: MX_BF16}
 EXPORTS = ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
            "mx_block_mse_workspace_size", "mx_quantize_mxfp8", "mx_dequantize_mxfp8",
            "mx_fakequant_mxfp8", "mx_nvfp4_workspace_size", "mx_quantize_nvfp4",
-           "mx_dequantize_nvfp4", "mx_quantize_mbs", "mx_dequantize_mbs", "mx_status_string",
-           "mx_last_error_detail")
+           "mx_dequantize_nvfp4", "mx_quantize_mbs", "mx_dequantize_mbs", "mx_quantize_multi",
+           "mx_fakequant_multi", "mx_status_string", "mx_last_error_detail")
 
 _lib = None
 
@@ -69,10 +69,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mx_dequantize_nvfp4.argtypes = [p, p, p, i64, i64, i32, p, p]
     lib.mx_quantize_mbs.argtypes = [p, i32, i64, i64, p, p, p, p]
     lib.mx_dequantize_mbs.argtypes = [p, p, p, i64, i64, i32, p, p]
+    lib.mx_quantize_multi.argtypes = [p, i32, i32, i32, p]
+    lib.mx_fakequant_multi.argtypes = [p, i32, i32, i32, p]
     for f in ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
               "mx_quantize_mxfp8", "mx_dequantize_mxfp8", "mx_fakequant_mxfp8",
               "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_quantize_mbs",
-              "mx_dequantize_mbs"):
+              "mx_dequantize_mbs", "mx_quantize_multi", "mx_fakequant_multi"):
         getattr(lib, f).restype = i32
     lib.mx_status_string.argtypes = [i32]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -143,18 +145,38 @@ def mx_dequantize_mbs(codes, sub_scales, macro_mant, rows, k, y_dtype, y, stream
                                             stream)
 
 
+class MxTensor(ctypes.Structure):
+    """mx_tensor_t of include/mx.h (pointers as integers)."""
+    _fields_ = [("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("rows", ctypes.c_int64), ("k", ctypes.c_int64)]
+
+
+def mx_quantize_multi(tensors, count, dtype, mode, stream) -> int:
+    return load_library().mx_quantize_multi(tensors, count, dtype, mode, stream)
+
+
+def mx_fakequant_multi(tensors, count, dtype, mode, stream) -> int:
+    return load_library().mx_fakequant_multi(tensors, count, dtype, mode, stream)
+
+
 def mx_status_string(status: int) -> str:
     return load_library().mx_status_string(status).decode()
 
 
+def mx_last_error_detail() -> str:
+    return load_library().mx_last_error_detail().decode()
+
+
 # ---- tensor helpers --------------------------------------------------------
 
-def _raise(status: int):
+def _raise(status: int, with_detail: bool = False):
     if status == MX_OK:
         return
     msg = mx_status_string(status)
     if status == MX_ERR_HIP:
         raise RuntimeError(msg + ": " + load_library().mx_last_error_detail().decode())
+    if with_detail:
+        msg += " (" + load_library().mx_last_error_detail().decode() + ")"
     raise ValueError(msg)
 
 
@@ -395,3 +417,62 @@ def dequantize_mbs(codes: torch.Tensor, sub_scales: torch.Tensor, macro_mant: to
         _raise(mx_dequantize_mbs(codes.data_ptr(), sub_scales.data_ptr(), macro_mant.data_ptr(),
                                  rows, k, _DTYPES[dtype], y.data_ptr(), _stream(codes.device)))
     return y
+
+
+# ---- many tensors in one call --------------------------------------------------
+
+def _multi_inputs(xs):
+    xs = list(xs)
+    if not xs:
+        return xs, None, None
+    dev, dt = xs[0].device, xs[0].dtype
+    for x in xs:
+        _check_input(x)
+        if x.device != dev or x.dtype != dt:
+            raise ValueError("all tensors must share one device and dtype")
+    return xs, dev, dt
+
+
+def quantize_multi(xs, mode: str = "ocp"):
+    """[x_i [..., k_i]] -> [(codes_i, scales_i)], as quantize() per tensor,
+    with one launch per 48 tensors."""
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {MODES}")
+    xs, dev, dt = _multi_inputs(xs)
+    outs = []
+    arr = (MxTensor * max(1, len(xs)))()
+    for i, x in enumerate(xs):
+        k = x.shape[-1]
+        rows = x.numel() // k if x.numel() else 0
+        c = torch.empty(tuple(x.shape[:-1]) + (k // 2,), dtype=torch.uint8, device=dev)
+        s = torch.empty(tuple(x.shape[:-1]) + (k // BLOCK,), dtype=torch.uint8, device=dev)
+        outs.append((c, s))
+        arr[i] = MxTensor(x.data_ptr(), None, c.data_ptr(), s.data_ptr(), rows, k)
+    if xs:
+        with torch.cuda.device(dev):
+            _raise(mx_quantize_multi(arr, len(xs), _DTYPES[dt], _MODES[mode], _stream(dev)), True)
+    return outs
+
+
+def fakequant_multi(xs, mode: str = "ocp", out=None):
+    """[x_i] -> [y_i], as fakequant() per tensor, with one launch per 48
+    tensors; out may be a list of preallocated outputs (or the inputs, in
+    place)."""
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {MODES}")
+    xs, dev, dt = _multi_inputs(xs)
+    ys = list(out) if out is not None else [torch.empty_like(x) for x in xs]
+    if len(ys) != len(xs):
+        raise ValueError("out must have one tensor per input")
+    arr = (MxTensor * max(1, len(xs)))()
+    for i, (x, y) in enumerate(zip(xs, ys)):
+        if y.dtype != x.dtype or y.numel() != x.numel() or not y.is_contiguous() \
+                or y.device != x.device:
+            raise ValueError("each out tensor must be a contiguous tensor like its input")
+        k = x.shape[-1]
+        rows = x.numel() // k if x.numel() else 0
+        arr[i] = MxTensor(x.data_ptr(), y.data_ptr(), None, None, rows, k)
+    if xs:
+        with torch.cuda.device(dev):
+            _raise(mx_fakequant_multi(arr, len(xs), _DTYPES[dt], _MODES[mode], _stream(dev)), True)
+    return ys

@@ -3,7 +3,10 @@
 // Every check here runs before any HIP call, so the error paths can be
 // exercised on a machine without a GPU.
 #include <stdint.h>
+#include <stdio.h>
 #include <string.h>
+
+#include <vector>
 
 #include <hip/hip_runtime.h>
 
@@ -273,6 +276,108 @@ mx_status_t mx_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
     return MX_ERR_ALIAS;
   return finish(mxi_launch_dequantize_mbs(codes, sub_scales, macro_mant, y_dtype == MX_BF16,
                                           n / 8, y, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Byte range one tensor of a multi call reads (in) or writes (out).
+struct Span {
+  const void *p;
+  int64_t n;
+  int owner;
+  bool out;
+};
+
+void set_detail_tensor(int i, const char *what) {
+  snprintf(g_detail, sizeof g_detail, "tensor %d: %s", i, what);
+}
+
+mx_status_t multi(const mx_tensor_t *tensors, int count, mx_dtype_t dtype,
+                  mx_scale_mode_t mode, bool fakequant, void *stream) {
+  if (!dtype_ok(dtype)) return MX_ERR_DTYPE;
+  if (!mode_ok(mode)) return MX_ERR_MODE;
+  if (count < 0) return MX_ERR_SHAPE;
+  if (count == 0) return MX_OK;
+  if (!tensors) return MX_ERR_NULL;
+  std::vector<MxiTensor> launch;
+  std::vector<Span> spans;
+  launch.reserve(count);
+  for (int i = 0; i < count; i++) {
+    const mx_tensor_t &t = tensors[i];
+    if (mx_status_t s = check_shape(t.rows, t.k)) {
+      set_detail_tensor(i, "shape");
+      return s;
+    }
+    if (t.rows == 0) continue;
+    const int64_t n = t.rows * t.k;
+    const int64_t nx = n * elem_bytes(dtype);
+    if (fakequant) {
+      if (!t.x || !t.y) {
+        set_detail_tensor(i, "NULL pointer");
+        return MX_ERR_NULL;
+      }
+      if (!aligned16(t.x) || !aligned16(t.y)) {
+        set_detail_tensor(i, "alignment");
+        return MX_ERR_ALIGN;
+      }
+      if (t.x != t.y && overlap(t.x, nx, t.y, nx)) {
+        set_detail_tensor(i, "y partially overlaps x");
+        return MX_ERR_ALIAS;
+      }
+      spans.push_back({t.x, nx, i, false});
+      spans.push_back({t.y, nx, i, true});
+      launch.push_back({t.x, t.y, nullptr, n / 8});
+    } else {
+      if (!t.x || !t.codes || !t.scales) {
+        set_detail_tensor(i, "NULL pointer");
+        return MX_ERR_NULL;
+      }
+      if (!aligned16(t.x) || !aligned16(t.codes) || !aligned16(t.scales)) {
+        set_detail_tensor(i, "alignment");
+        return MX_ERR_ALIGN;
+      }
+      if (overlap(t.x, nx, t.codes, n / 2) || overlap(t.x, nx, t.scales, n / kBlock) ||
+          overlap(t.codes, n / 2, t.scales, n / kBlock)) {
+        set_detail_tensor(i, "an output overlaps an input");
+        return MX_ERR_ALIAS;
+      }
+      spans.push_back({t.x, nx, i, false});
+      spans.push_back({t.codes, n / 2, i, true});
+      spans.push_back({t.scales, n / kBlock, i, true});
+      launch.push_back({t.x, t.codes, t.scales, n / 8});
+    }
+  }
+  // no tensor's output may touch another tensor's input or output (inputs
+  // may be shared)
+  for (size_t a = 0; a < spans.size(); a++) {
+    if (!spans[a].out) continue;
+    for (size_t b = 0; b < spans.size(); b++) {
+      if (spans[b].owner == spans[a].owner) continue;
+      if (overlap(spans[a].p, spans[a].n, spans[b].p, spans[b].n)) {
+        set_detail_tensor(spans[a].owner, "an output overlaps another tensor's data");
+        return MX_ERR_ALIAS;
+      }
+    }
+  }
+  if (launch.empty()) return MX_OK;
+  return finish(mxi_launch_multi(launch.data(), (int)launch.size(), dtype == MX_BF16, mode,
+                                 fakequant ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status_t mx_quantize_multi(const mx_tensor_t *tensors, int count, mx_dtype_t dtype,
+                              mx_scale_mode_t mode, void *stream) {
+  return multi(tensors, count, dtype, mode, false, stream);
+}
+
+mx_status_t mx_fakequant_multi(const mx_tensor_t *tensors, int count, mx_dtype_t dtype,
+                               mx_scale_mode_t mode, void *stream) {
+  return multi(tensors, count, dtype, mode, true, stream);
 }
 
 const char *mx_status_string(mx_status_t s) {

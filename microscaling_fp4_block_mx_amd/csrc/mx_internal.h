@@ -40,4 +40,16 @@ hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint
 hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
                                      const uint8_t *macro_mant, int bf16, int64_t nitems, void *y,
                                      hipStream_t st);
+// Many tensors in one launch per MX_MULTI_MAX of them (empty ones skipped).
+#ifndef MX_MULTI_MAX
+#define MX_MULTI_MAX 48
+#endif
+struct MxiTensor {
+  const void *x;
+  void *out;        // quantize: codes; fake-quant: y
+  uint8_t *scales;  // quantize only
+  int64_t nitems;   // rows * k / 8
+};
+hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, int fakequant,
+                            hipStream_t st);
 #endif

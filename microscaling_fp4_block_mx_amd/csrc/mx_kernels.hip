@@ -468,6 +468,85 @@ __global__ __launch_bounds__(kThreads) void k_fakequant(const void *x, void *y, 
       });
 }
 
+// ---- many tensors in one launch ------------------------------------------------
+//
+// A list of separate tensors (say every Linear weight of a model) quantized
+// or fake-quantized by one launch: a launch per tensor pays the per-kernel
+// ramp-up and drain each time (a 3 Mi-element weight runs at a quarter of the
+// streaming rate on its own). The descriptors travel by value in the kernel
+// arguments (no device table, nothing to copy or allocate; capturable). Tile
+// t of the launch belongs to the tensor whose first tile is the largest
+// tile0 <= t (a binary search on uniform values, so scalar work); a
+// tensor's last tile may be partial and takes the per-item checks.
+
+template <int U, typename Load, typename Use>
+__device__ __forceinline__ void tile_at(int64_t t, int64_t nitems, Load load, Use use) {
+  const int64_t tile = (int64_t)kThreads * U;
+  const int64_t base = t * tile + threadIdx.x;
+  if ((t + 1) * tile <= nitems) {
+#pragma unroll
+    for (int u = 0; u < U; u++) load(u, base + u * kThreads);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; u++) use(u, base + u * kThreads);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (base + u * kThreads < nitems) load(u, base + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; u++)  // whole quads drop out together
+      if (base + u * kThreads < nitems) use(u, base + u * kThreads);
+  }
+}
+
+struct MultiDesc {
+  const void *x;    // input [rows, k]
+  void *out;        // quantize: codes; fake-quant: y
+  uint8_t *scales;  // quantize: scales; fake-quant: unused
+  int64_t nitems;   // rows * k / 8
+  int64_t tile0;    // first tile of this tensor in the launch
+};
+struct MultiArgs {
+  int count;
+  int64_t ntiles;  // tiles of the whole launch
+  MultiDesc d[MX_MULTI_MAX];
+};
+
+__device__ __forceinline__ int multi_find(const MultiArgs &a, int64_t t) {
+  int lo = 0, hi = a.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.d[mid].tile0 <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool BF16, int MODE, bool FQ>
+__global__ __launch_bounds__(kThreads) void k_multi(const MultiArgs a) {
+  constexpr int U = kU<BF16>;
+  Item<BF16> xv[U];
+  for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+    const int j = multi_find(a, t);
+    const MultiDesc &d = a.d[j];
+    const void *x = d.x;
+    tile_at<U>(
+        t - d.tile0, d.nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+        [&](int u, int64_t it) {
+          uint32_t c;
+          const uint32_t s = quantize_item<BF16, MODE>(xv[u], c);
+          if constexpr (FQ) {
+            uint32_t out[BF16 ? 4 : 8];
+            decode_item<BF16>(c, s, out);
+            store_item<BF16>(d.out, it, out);
+          } else {
+            st<false>(static_cast<uint32_t *>(d.out) + it, c);
+            if ((threadIdx.x & 3) == 0) st<false>(d.scales + (it >> 2), (uint8_t)s);
+          }
+        });
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restrict__ codes,
                                                          const uint8_t *__restrict__ scales,
@@ -1076,6 +1155,22 @@ static unsigned grid_for(int64_t nitems, int64_t cap, int unroll = kUnroll) {
 
 using namespace mxk;
 
+#define MX_DISPATCH_MULTI(BF16, FQ, MODE, G, B, ST, ARGS)                                 \
+  switch (MODE) {                                                                          \
+    case MX_SCALE_OAS:                                                                     \
+      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OAS, FQ>), G, B, 0, ST, ARGS);            \
+      break;                                                                               \
+    case MX_SCALE_OAS_BITS:                                                                \
+      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OAS_BITS, FQ>), G, B, 0, ST, ARGS);       \
+      break;                                                                               \
+    case MX_SCALE_OAS_NF:                                                                  \
+      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OAS_NF, FQ>), G, B, 0, ST, ARGS);         \
+      break;                                                                               \
+    default:                                                                               \
+      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OCP, FQ>), G, B, 0, ST, ARGS);            \
+      break;                                                                               \
+  }
+
 #define MX_DISPATCH_MODE(KERNEL, BF16, MODE, G, B, ST, ...)                               \
   switch (MODE) {                                                                          \
     case MX_SCALE_OAS:                                                                     \
@@ -1250,4 +1345,39 @@ hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_sc
     hipLaunchKernelGGL((k_dequantize_mbs<false>), g, b, 0, st, c, sub_scales, macro_mant, y,
                        nitems);
   return hipGetLastError();
+}
+
+hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, int fakequant,
+                            hipStream_t st) {
+  // chunks of at most MX_MULTI_MAX non-empty tensors, one launch each
+  int i = 0;
+  while (i < count) {
+    MultiArgs a;
+    a.count = 0;
+    int64_t tiles = 0;
+    const int64_t tile = (int64_t)kThreads * (bf16 ? kU<true> : kU<false>);
+    for (; i < count && a.count < MX_MULTI_MAX; i++) {
+      if (t[i].nitems <= 0) continue;
+      MultiDesc &d = a.d[a.count++];
+      d.x = t[i].x;
+      d.out = t[i].out;
+      d.scales = t[i].scales;
+      d.nitems = t[i].nitems;
+      d.tile0 = tiles;
+      tiles += (t[i].nitems + tile - 1) / tile;
+    }
+    if (a.count == 0) break;
+    a.ntiles = tiles;
+    const dim3 g((unsigned)(tiles < MX_GRID_CAP ? tiles : MX_GRID_CAP)), b(kThreads);
+    if (bf16) {
+      if (fakequant) { MX_DISPATCH_MULTI(true, true, mode, g, b, st, a) }
+      else { MX_DISPATCH_MULTI(true, false, mode, g, b, st, a) }
+    } else {
+      if (fakequant) { MX_DISPATCH_MULTI(false, true, mode, g, b, st, a) }
+      else { MX_DISPATCH_MULTI(false, false, mode, g, b, st, a) }
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }

@@ -114,6 +114,50 @@ static void mxfp8_nvfp4_mbs() {
   CHECK(g_calls == n0);
 }
 
+// many tensors in one call: empty ones are dropped, the rest reach the
+// launcher in order; a bad tensor or a cross-tensor overlap launches nothing
+static void multi() {
+  mx_tensor_t t[5] = {};
+  for (int i = 0; i < 5; i++) {
+    t[i].x = P(X + (uintptr_t)i * (1u << 24));
+    t[i].codes = (uint8_t *)P(Cd + (uintptr_t)i * (1u << 24));
+    t[i].scales = (uint8_t *)P(Sc + (uintptr_t)i * (1u << 24));
+    t[i].y = P(Y + (uintptr_t)i * (1u << 24));
+    t[i].rows = 3 + i;
+    t[i].k = 64;
+  }
+  t[2].rows = 0;
+  int n0 = g_calls;
+  int64_t items = 0;
+  for (int i = 0; i < 5; i++) items += t[i].rows * t[i].k / 8;
+  expect_launch(mx_quantize_multi(t, 5, MX_BF16, MX_SCALE_OAS, nullptr), "quantize_multi", items, n0);
+  CHECK(g_last.p[5] == P(4) && g_last.mode == MX_SCALE_OAS);
+  n0 = g_calls;
+  expect_launch(mx_fakequant_multi(t, 5, MX_F32, MX_SCALE_OCP, nullptr), "fakequant_multi", items, n0);
+  CHECK(g_last.bf16 == 0);
+  n0 = g_calls;
+  t[3].k = 40;
+  CHECK(mx_quantize_multi(t, 5, MX_BF16, MX_SCALE_OCP, nullptr) == MX_ERR_SHAPE);
+  CHECK(strcmp(mx_last_error_detail(), "tensor 3: shape") == 0);
+  t[3].k = 64;
+  t[4].codes = t[1].codes;  // two tensors writing the same codes
+  CHECK(mx_quantize_multi(t, 5, MX_BF16, MX_SCALE_OCP, nullptr) == MX_ERR_ALIAS);
+  t[4].codes = (uint8_t *)P(Cd + 4u * (1u << 24));
+  t[4].y = const_cast<void *>(t[0].x);  // fake-quant output over another tensor's input
+  CHECK(mx_fakequant_multi(t, 5, MX_BF16, MX_SCALE_OCP, nullptr) == MX_ERR_ALIAS);
+  CHECK(mx_quantize_multi(nullptr, 3, MX_BF16, MX_SCALE_OCP, nullptr) == MX_ERR_NULL);
+  CHECK(mx_quantize_multi(t, -2, MX_BF16, MX_SCALE_OCP, nullptr) == MX_ERR_SHAPE);
+  CHECK(g_calls == n0);
+  t[4].y = const_cast<void *>(t[4].x);  // in place is fine
+  expect_launch(mx_fakequant_multi(t, 5, MX_BF16, MX_SCALE_OCP, nullptr), "fakequant_multi", items, n0);
+  n0 = g_calls;
+  t[4].x = t[0].x;  // two tensors may read one input, but not write over it
+  t[4].y = const_cast<void *>(t[0].x);
+  CHECK(mx_fakequant_multi(t, 5, MX_BF16, MX_SCALE_OCP, nullptr) == MX_ERR_ALIAS);
+  t[4].y = P(Y + 4u * (1u << 24));
+  expect_launch(mx_fakequant_multi(t, 5, MX_BF16, MX_SCALE_OCP, nullptr), "fakequant_multi", items, n0);
+}
+
 // a failing launch reports MX_ERR_HIP; the detail string is per thread
 static void hip_errors() {
   const int64_t k = 8 * kFailItems;  // one row whose item count makes the stub fail
@@ -150,6 +194,7 @@ static void threads() {
 int main() {
   mxfp4();
   mxfp8_nvfp4_mbs();
+  multi();
   hip_errors();
   threads();
   if (g_fail) {

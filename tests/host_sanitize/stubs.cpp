@@ -77,3 +77,12 @@ hipError_t mxi_launch_dequantize_mbs(const uint8_t *c, const uint8_t *ss, const 
                                      int bf16, int64_t n, void *y, hipStream_t) {
   return rec("dequantize_mbs", n, bf16, -1, c, ss, mm, y);
 }
+hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, int fakequant,
+                            hipStream_t) {
+  int64_t total = 0;
+  for (int i = 0; i < count; i++) total += t[i].nitems;  // reads every descriptor
+  g_last.p[4] = t;
+  g_last.p[5] = reinterpret_cast<const void *>(static_cast<intptr_t>(count));
+  return rec(fakequant ? "fakequant_multi" : "quantize_multi", total, bf16, mode, t[0].x,
+             t[0].out, t[0].scales, nullptr);
+}

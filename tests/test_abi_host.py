@@ -204,3 +204,48 @@ def test_mbs_validation(lib):
     assert mx.mx_quantize_mbs(A, 1, 4, 256, B, C, B + 16, None) == mx.MX_ERR_ALIAS
     assert mx.mx_dequantize_mbs(B, C, W, 4, 256, 0, B + 256, None) == mx.MX_ERR_ALIAS
     assert mx.mx_dequantize_mbs(B, C, W, 4, 256, 1, W - 16, None) == mx.MX_ERR_ALIAS
+
+
+def test_multi_validation(lib):
+    T = mx.MxTensor
+    arr = (T * 4)()
+    arr[0] = T(A, None, B, C, 4, 64)
+    arr[1] = T(A + 4096, None, B + 1024, C + 1024, 4, 48)  # k not a multiple of 32
+    assert mx.mx_quantize_multi(arr, 2, 1, 0, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_last_error_detail() == "tensor 1: shape"
+    assert mx.mx_quantize_multi(arr, 0, 1, 0, None) == mx.MX_OK
+    assert mx.mx_quantize_multi(arr, -1, 1, 0, None) == mx.MX_ERR_SHAPE
+    assert mx.mx_quantize_multi(None, 1, 1, 0, None) == mx.MX_ERR_NULL
+    assert mx.mx_quantize_multi(arr, 1, 5, 0, None) == mx.MX_ERR_DTYPE
+    assert mx.mx_quantize_multi(arr, 1, 1, 4, None) == mx.MX_ERR_MODE
+    assert mx.mx_fakequant_multi(arr, 1, 1, 0, None) == mx.MX_ERR_NULL  # y missing
+    arr[1] = T(A + 4096, None, B + 1024, C + 1028, 4, 64)
+    assert mx.mx_quantize_multi(arr, 2, 1, 0, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_last_error_detail() == "tensor 1: alignment"
+    # tensor 1's codes overlap tensor 0's codes
+    arr[1] = T(A + 4096, None, B + 64, C + 1024, 4, 64)
+    assert mx.mx_quantize_multi(arr, 2, 1, 0, None) == mx.MX_ERR_ALIAS
+    # tensor 1's scales overlap tensor 0's input
+    arr[1] = T(A + 4096, None, B + 1024, A + 16, 4, 64)
+    assert mx.mx_quantize_multi(arr, 2, 1, 0, None) == mx.MX_ERR_ALIAS
+    # in-place fake-quant of tensor 0 while tensor 1 reads inside it
+    arr[0] = T(A, A, None, None, 4, 64)
+    arr[1] = T(A + 256, B, None, None, 4, 64)
+    assert mx.mx_fakequant_multi(arr, 2, 0, 0, None) == mx.MX_ERR_ALIAS
+    # y partially overlapping its own x
+    arr[0] = T(A, A + 16, None, None, 4, 64)
+    assert mx.mx_fakequant_multi(arr, 1, 0, 0, None) == mx.MX_ERR_ALIAS
+    # empty tensors only: nothing to launch
+    arr[0] = T(None, None, None, None, 0, 64)
+    arr[1] = T(None, None, None, None, 0, 32)
+    assert mx.mx_quantize_multi(arr, 2, 1, 0, None) == mx.MX_OK
+    assert mx.mx_fakequant_multi(arr, 2, 1, 3, None) == mx.MX_OK
+
+
+def test_multi_helpers_refuse_bad_lists(lib):
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        mx.quantize_multi([torch.zeros(4, 32)])  # CPU tensor
+    with pytest.raises(ValueError):
+        mx.fakequant_multi([], mode="nope")
+    assert mx.quantize_multi([]) == [] and mx.fakequant_multi([]) == []

@@ -1,0 +1,87 @@
+"""GPU parity of the many-tensors-in-one-call entry points: every tensor's
+codes, scales and fake-quant output equal the oracle's (and the single-
+tensor calls'), across ragged shapes, empty tensors, more tensors than one
+launch takes, every scale mode and both dtypes; plus the 196 Llama-3.2-3B-
+shaped weights as separate tensors. Expected values from oracle/ only."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import microscaling_fp4_block_mx_amd as mx
+from test_parity_gpu import assert_same_bits, host_view, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mx.load_library()
+    oracle.build(force=not os.path.exists(os.path.join(os.path.dirname(oracle.__file__),
+                                                       "libmxref.so")))
+    yield
+    torch.cuda.synchronize()
+
+
+def ragged_list(seed: int, n: int, dtype):
+    rng = np.random.default_rng(seed)
+    xs = []
+    for i in range(n):
+        rows = int(rng.choice([0, 1, 2, 3, 7, 64, 257, 1000]))
+        k = 32 * int(rng.choice([1, 2, 3, 5, 33, 96, 128]))
+        x = rng.standard_t(3, (rows, k)) * np.exp(rng.normal(0, 2, (rows, k // 32))).repeat(32, 1)
+        xs.append(torch.from_numpy(x.astype(np.float32)).to(dtype))
+    return xs
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("mode", mx.MODES)
+def test_multi_ragged_vs_oracle(dtype, mode):
+    xs = ragged_list(11 + mx.MODES.index(mode), 120, dtype)  # > 2 launches of 48
+    xd = [x.cuda() for x in xs]
+    say(f"multi {mode} {dtype}: {len(xs)} tensors")
+    qs = mx.quantize_multi(xd, mode)
+    fs = mx.fakequant_multi(xd, mode)
+    name = "bf16" if dtype == torch.bfloat16 else "f32"
+    for i, (x, (c, s), f) in enumerate(zip(xs, qs, fs)):
+        xh = host_view(x)
+        wc, ws = oracle.quantize(xh, mode)
+        assert_same_bits(c, wc, f"tensor {i} codes {mode}")
+        assert_same_bits(s, ws, f"tensor {i} scales {mode}")
+        assert_same_bits(f, oracle.fakequant(xh, mode), f"tensor {i} fake-quant {mode}")
+
+
+def test_multi_in_place_and_leading_dims():
+    xs = [workloads.bf16_student_t_outlier_channels(20 + i, shape=(2, 3, 64 * (i + 1))).cuda()
+          for i in range(5)]
+    want = [mx.fakequant(x) for x in xs]
+    got = mx.fakequant_multi(xs, out=xs)  # in place
+    for w, g, x in zip(want, got, xs):
+        assert g.data_ptr() == x.data_ptr()
+        assert torch.equal(w.view(torch.int16), g.view(torch.int16))
+
+
+def test_multi_llama32_3b_separate_weights():
+    """The 196 weights as separate tensors, one call: bit-equal to one
+    quantize call per matrix (5 launches instead of 196)."""
+    say("generating llama weights on device")
+    ms = [workloads.llama32_3b_matrix(layer, which, "cuda")
+          for layer in range(workloads.LLAMA32_3B_LAYERS)
+          for which in range(len(workloads.LLAMA32_3B_LINEARS))]
+    qs = mx.quantize_multi(ms)
+    for i, (m, (c, s)) in enumerate(zip(ms, qs)):
+        c1, s1 = mx.quantize(m)
+        assert torch.equal(c, c1) and torch.equal(s, s1), f"matrix {i}"
+    # and the oracle on sampled rows of a few of them
+    rng = np.random.default_rng(77)
+    for i in (0, 1, 4, 6, 195):
+        rows = np.sort(rng.choice(ms[i].shape[0], 64, replace=False))
+        idx = torch.from_numpy(rows).cuda()
+        wc, ws = oracle.quantize(host_view(ms[i].index_select(0, idx)), "ocp")
+        assert_same_bits(qs[i][0].index_select(0, idx), wc, f"matrix {i} codes (sampled rows)")
+        assert_same_bits(qs[i][1].index_select(0, idx), ws, f"matrix {i} scales (sampled rows)")
