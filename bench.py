@@ -14,11 +14,10 @@ Prints ONE JSON line. --gpus N with N > 1 exits: this path runs on one GPU.
 normal [1024, 4096]; the Llama-3.2-3B-shaped linear stack, per matrix, as one
 multi-tensor call and grouped by K; the 128-expert MoE weights; bf16 Laplace
 [16384, 8192] with sparse outliers), with per-launch HIP events (median, p10,
-p90), warm
-(cache-resident) and cold (rotated) figures where the tensor fits the cache,
-and for the small fp32 case the host-side single-launch latency and the
-per-launch time inside a replayed HIP graph. It prints one JSON line per
-measurement and a markdown table.
+p90), warm (cache-resident) and cold (rotated) figures where the tensor fits
+the cache, and for the small fp32 case the host-side single-launch latency
+and the per-launch time inside a replayed HIP graph. It prints one JSON line
+per measurement and a markdown table.
 """
 from __future__ import annotations
 
