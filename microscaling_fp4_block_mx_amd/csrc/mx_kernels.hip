@@ -234,12 +234,15 @@ __device__ __forceinline__ float scale_operand(uint32_t s) { return __uint_as_fl
 // product with fl32(1/6) plus one fma residual correction is the correctly
 // rounded quotient (checked against IEEE division for every fp32 value in
 // that range); below it, where the quotient is subnormal, IEEE division.
-__device__ __forceinline__ float div6(uint32_t a_bits) {
-  const float a = __uint_as_float(a_bits);
-  if (__builtin_expect(a_bits < 0x01000000u, 0)) return a / 6.0f;
+__device__ __forceinline__ float div6_fast(float a) {
   constexpr float kSixth = 1.0f / 6.0f;
   const float q0 = a * kSixth;
   return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, a), kSixth, q0);
+}
+__device__ __forceinline__ float div6(uint32_t a_bits) {
+  const float a = __uint_as_float(a_bits);
+  if (__builtin_expect(a_bits < 0x01000000u, 0)) return a / 6.0f;
+  return div6_fast(a);
 }
 
 
@@ -1053,6 +1056,80 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
   return v;
 }
 
+// The U items of one tile, in phases across the items (every item's macro
+// maximum, then every factor, then every table read, then the codes) so the
+// scheduler can overlap their long dependency chains; the rare cases (a
+// subnormal quotient, a NaN/Inf sub-block) are patched afterwards under a
+// branch that a wave without them skips.
+template <bool BF16, int U>
+__device__ __forceinline__ void mbs_tile(const Item<BF16> (&xv)[U], const float *inv_tab,
+                                         uint32_t *__restrict__ codes,
+                                         uint8_t *__restrict__ sub_scales,
+                                         uint8_t *__restrict__ macro_mant, int64_t base,
+                                         int64_t nitems, bool full) {
+  uint32_t aS[U], aM[U], m[U], s[U], c[U];
+  float inv[U];
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const uint32_t a8 = item_amax_bits<BF16>(xv[u]);
+    aS[u] = max(a8, dpp_x1(a8));  // the sub-block's lane pair
+    uint32_t v = max(aS[u], dpp_x2(aS[u]));
+    v = max(v, dpp_ror4(v));
+    aM[u] = max(v, dpp_ror8(v));  // the macro block's row of 16 lanes
+  }
+  // a_M / 6: the exact fast form (div6_fast) everywhere, then IEEE division
+  // for the lanes below its range, under a branch taken only when a wave has
+  // any (a macro maximum below 2^-125)
+  float r[U];
+  bool small = false;
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    r[u] = div6_fast(__uint_as_float(aM[u]));
+    small |= aM[u] - 1u < 0x00FFFFFFu;  // 0 < a_M < 2^-125
+  }
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(small) != 0, 0)) {
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (aM[u] - 1u < 0x00FFFFFFu) r[u] = __uint_as_float(aM[u]) / 6.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    // m = 0 for a zero or non-finite macro block, and where a_M / 6
+    // underflows to zero (fp32 a_M below 4 * 2^-149): no mantissa
+    const float t = __builtin_rintf((2.0f * __builtin_amdgcn_frexp_mantf(r[u]) - 1.0f) * 256.0f);
+    const float tc = __builtin_fminf(__builtin_fmaxf(t, 0.0f), 255.0f);  // NaN -> 0
+    m[u] = (aM[u] < 0x7F800000u && r[u] != 0.0f) ? (uint32_t)tc : 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < U; u++) inv[u] = inv_tab[m[u]];
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    // largest |y| of the sub-block: rounding is monotone, so it equals
+    // fl(max |x| * inv); NaN/Inf stay NaN/Inf and give byte 255
+    s[u] = ocp_scale_byte(__float_as_uint(__uint_as_float(aS[u]) * inv[u]));
+    const float sc = scale_operand(s[u]);
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) y[i] = elem<BF16>(xv[u], i) * inv[u];
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], sc, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], sc, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], sc, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], sc, 3);
+    c[u] = w;
+  }
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    if (__builtin_expect(s[u] == 255u, 0)) c[u] = sign_codes<BF16>(xv[u]);
+    const int64_t it = base + u * kThreads;
+    if (full || it < nitems) {  // whole rows of 16 lanes drop out together
+      st<false>(codes + it, c[u]);
+      if ((threadIdx.x & 1) == 0) st<false>(sub_scales + (it >> 1), (uint8_t)s[u]);
+      if ((threadIdx.x & 15) == 0) st<false>(macro_mant + (it >> 4), (uint8_t)m[u]);
+    }
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *__restrict__ x,
                                                            uint32_t *__restrict__ codes,
@@ -1065,46 +1142,27 @@ __global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *__restric
   __shared__ float inv_tab[256];
   inv_tab[threadIdx.x] = 1.0f / (1.0f + (float)threadIdx.x * (1.0f / 256.0f));
   __syncthreads();
-  Item<BF16> xv[kU<BF16>];
-  tile_loop<kU<BF16>>(
-      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
-      [&](int u, int64_t it) {
-        const uint32_t a8 = item_amax_bits<BF16>(xv[u]);
-        const uint32_t aS = max(a8, dpp_x1(a8));  // the sub-block's lane pair
-        uint32_t aM = max(aS, dpp_x2(aS));
-        aM = max(aM, dpp_ror4(aM));
-        aM = max(aM, dpp_ror8(aM));
-        // m = 0 for a zero or non-finite macro block, and where a_M / 6
-        // underflows to zero (fp32 a_M below 4 * 2^-149): no mantissa.
-        uint32_t m = 0;
-        const float r = div6(aM);
-        if (aM < 0x7F800000u && r != 0.0f) {
-          const float f01 = 2.0f * __builtin_amdgcn_frexp_mantf(r);  // [1, 2), exact
-          m = min((uint32_t)__builtin_rintf((f01 - 1.0f) * 256.0f), 255u);
-        }
-        const float inv = inv_tab[m];
-        float y[8];
+  constexpr int U = kU<BF16>;
+  const int64_t tile = (int64_t)kThreads * U;
+  const int64_t nfull = nitems / tile;
+  Item<BF16> xv[U];
+  int64_t t = blockIdx.x;
+  for (; t < nfull; t += gridDim.x) {
+    const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < 8; i++) y[i] = elem<BF16>(xv[u], i) * inv;
-        // largest |y| of the sub-block: rounding is monotone, so it equals
-        // fl(max |x| * inv); NaN/Inf stay NaN/Inf and give byte 255
-        const uint32_t ay = __float_as_uint(__uint_as_float(aS) * inv);
-        const uint32_t s = ocp_scale_byte(ay);
-        uint32_t c;
-        if (__builtin_expect(s == 255u, 0)) {
-          c = sign_codes<BF16>(xv[u]);
-        } else {
-          const float sc = scale_operand(s);
-          c = 0;
-          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[0], y[1], sc, 0);
-          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[2], y[3], sc, 1);
-          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[4], y[5], sc, 2);
-          c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[6], y[7], sc, 3);
-        }
-        st<false>(codes + it, c);
-        if ((threadIdx.x & 1) == 0) st<false>(sub_scales + (it >> 1), (uint8_t)s);
-        if ((threadIdx.x & 15) == 0) st<false>(macro_mant + (it >> 4), (uint8_t)m);
-      });
+    for (int u = 0; u < U; u++) load_item<BF16>(x, base + u * kThreads, xv[u]);
+    __builtin_amdgcn_sched_barrier(0);
+    mbs_tile<BF16, U>(xv, inv_tab, codes, sub_scales, macro_mant, base, nitems, true);
+  }
+  if (t == nfull && nfull * tile < nitems) {
+    const int64_t base = t * tile + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (base + u * kThreads < nitems) load_item<BF16>(x, base + u * kThreads, xv[u]);
+      else xv[u] = Item<BF16>{};  // zeros: finite, so lanes past the end stay quiet
+    }
+    mbs_tile<BF16, U>(xv, inv_tab, codes, sub_scales, macro_mant, base, nitems, false);
+  }
 }
 
 template <bool BF16>

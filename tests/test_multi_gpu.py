@@ -85,3 +85,50 @@ def test_multi_llama32_3b_separate_weights():
         wc, ws = oracle.quantize(host_view(ms[i].index_select(0, idx)), "ocp")
         assert_same_bits(qs[i][0].index_select(0, idx), wc, f"matrix {i} codes (sampled rows)")
         assert_same_bits(qs[i][1].index_select(0, idx), ws, f"matrix {i} scales (sampled rows)")
+
+
+def test_other_formats_past_2_31_elements():
+    """MXFP8, NVFP4 and MBS-Static on one bf16 tensor of 2^31 + 2^20
+    elements (64-bit indexing in every kernel), checked on sampled rows
+    including the last ones."""
+    rows, k = (1 << 31) // 4096 + 256, 4096
+    say(f"big tensor [{rows}, {k}]")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(91)
+    x = torch.empty((rows, k), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, 65536):
+        r1 = min(rows, r0 + 65536)
+        x[r0:r1] = (torch.randn((r1 - r0, k), generator=g, device="cuda") * 3).to(torch.bfloat16)
+    # sampled rows: the first and last ones, random ones, and the row holding
+    # the tensor's largest |x| (so the NVFP4 tensor factor of the sample is
+    # the whole tensor's)
+    top = int(torch.argmax(x.view(-1).abs()).item()) // k
+    pick = np.unique(np.concatenate([np.arange(4), np.random.default_rng(92).choice(rows, 60, replace=False),
+                                     np.arange(rows - 4, rows), [top]]))
+    idx = torch.from_numpy(pick).cuda()
+    xs = host_view(x.index_select(0, idx))
+    say("mxfp8")
+    c, s = mx.quantize_mxfp8(x)
+    wc, ws = oracle.quantize_mxfp8(xs)
+    assert_same_bits(c.index_select(0, idx), wc, "mxfp8 codes (sampled rows)")
+    assert_same_bits(s.index_select(0, idx), ws, "mxfp8 scales (sampled rows)")
+    del c, s
+    say("mbs-static")
+    c, s, m = mx.quantize_mbs(x)
+    wc, ws, wm = oracle.quantize_mbs(xs)
+    assert_same_bits(c.index_select(0, idx), wc, "mbs codes (sampled rows)")
+    assert_same_bits(s.index_select(0, idx), ws, "mbs sub-scales (sampled rows)")
+    assert_same_bits(m.index_select(0, idx), wm, "mbs macro bytes (sampled rows)")
+    y = mx.dequantize_mbs(c, s, m, torch.bfloat16)
+    assert_same_bits(y.index_select(0, idx), oracle.dequantize_mbs(wc, ws, wm, "bf16"),
+                     "mbs dequant (sampled rows)")
+    del c, s, m, y
+    say("nvfp4")
+    c, b, t = mx.quantize_nvfp4(x)
+    wc, wb, wt = oracle.quantize_nvfp4(xs)
+    assert int(t.item()) == wt, "nvfp4 tensor factor byte"
+    assert_same_bits(c.index_select(0, idx), wc, "nvfp4 codes (sampled rows)")
+    assert_same_bits(b.index_select(0, idx), wb, "nvfp4 block scales (sampled rows)")
+    y = mx.dequantize_nvfp4(c, b, t, torch.bfloat16)
+    assert_same_bits(y.index_select(0, idx), oracle.dequantize_nvfp4(wc, wb, wt, "bf16"),
+                     "nvfp4 dequant (sampled rows)")
