@@ -195,6 +195,23 @@ def _check_input(x: torch.Tensor):
     return x.numel() // k if x.numel() else 0, k
 
 
+def _need(t, name: str, device, dtype=None, numel=None):
+    """A tensor the kernels will read or write: on `device`, contiguous, of
+    `dtype` and `numel` when given. Anything else is refused here, before a
+    pointer reaches the GPU."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t
+
+
 def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -215,8 +232,8 @@ def quantize(x: torch.Tensor, mode: str = "ocp", codes: torch.Tensor | None = No
         codes = torch.empty(lead + (k // 2,), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(lead + (k // BLOCK,), dtype=torch.uint8, device=x.device)
-    if codes.numel() * 2 != x.numel() or scales.numel() * BLOCK != x.numel():
-        raise ValueError("output sizes do not match x")
+    _need(codes, "codes", x.device, torch.uint8, x.numel() // 2)
+    _need(scales, "scales", x.device, torch.uint8, x.numel() // BLOCK)
     with torch.cuda.device(x.device):
         _raise(mx_quantize(x.data_ptr(), _DTYPES[x.dtype], rows, k, _mode(mode),
                            codes.data_ptr(), scales.data_ptr(), _stream(x.device)))
@@ -226,10 +243,8 @@ def quantize(x: torch.Tensor, mode: str = "ocp", codes: torch.Tensor | None = No
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, dtype=torch.bfloat16,
                out: torch.Tensor | None = None) -> torch.Tensor:
     """codes [..., k/2] + scales [..., k/32] -> y [..., k] in dtype."""
-    if not codes.is_cuda or codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
-        raise ValueError("codes and scales must be uint8 GPU tensors")
-    if not (codes.is_contiguous() and scales.is_contiguous()):
-        raise ValueError("codes and scales must be contiguous")
+    _need(codes, "codes", getattr(codes, "device", None), torch.uint8)
+    _need(scales, "scales", codes.device, torch.uint8)
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
     k = codes.shape[-1] * 2
@@ -238,6 +253,7 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, dtype=torch.bfloat16,
         raise ValueError("scales do not match codes")
     if out is None:
         out = torch.empty(tuple(codes.shape[:-1]) + (k,), dtype=dtype, device=codes.device)
+    _need(out, "out", codes.device, dtype, codes.numel() * 2)
     with torch.cuda.device(codes.device):
         _raise(mx_dequantize(codes.data_ptr(), scales.data_ptr(), rows, k, _DTYPES[dtype],
                              out.data_ptr(), _stream(codes.device)))
@@ -249,8 +265,7 @@ def fakequant(x: torch.Tensor, mode: str = "ocp", out: torch.Tensor | None = Non
     rows, k = _check_input(x)
     if out is None:
         out = torch.empty_like(x)
-    if out.dtype != x.dtype or out.numel() != x.numel() or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like x")
+    _need(out, "out", x.device, x.dtype, x.numel())
     with torch.cuda.device(x.device):
         _raise(mx_fakequant(x.data_ptr(), _DTYPES[x.dtype], rows, k, _mode(mode),
                             out.data_ptr(), _stream(x.device)))
@@ -263,8 +278,8 @@ def block_mse(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     with sums[0] = sum (x - x_hat)^2 and sums[1] = sum x^2. Tensor MSE =
     sums[0] / x.numel(); QSNR = 10 log10(sums[1] / sums[0]) dB."""
     rows, k = _check_input(x)
-    if codes.numel() * 2 != x.numel() or scales.numel() * BLOCK != x.numel():
-        raise ValueError("codes/scales do not match x")
+    _need(codes, "codes", x.device, torch.uint8, x.numel() // 2)
+    _need(scales, "scales", x.device, torch.uint8, x.numel() // BLOCK)
     bm = None
     if per_block:
         bm = torch.empty(tuple(x.shape[:-1]) + (k // BLOCK,), dtype=torch.float32,
@@ -290,8 +305,8 @@ def quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor | None = None,
     if scales is None:
         scales = torch.empty(tuple(x.shape[:-1]) + (k // BLOCK,), dtype=torch.uint8,
                              device=x.device)
-    if codes.numel() != x.numel() or scales.numel() * BLOCK != x.numel():
-        raise ValueError("output sizes do not match x")
+    _need(codes, "codes", x.device, torch.uint8, x.numel())
+    _need(scales, "scales", x.device, torch.uint8, x.numel() // BLOCK)
     with torch.cuda.device(x.device):
         _raise(mx_quantize_mxfp8(x.data_ptr(), _DTYPES[x.dtype], rows, k, codes.data_ptr(),
                                  scales.data_ptr(), _stream(x.device)))
@@ -301,10 +316,8 @@ def quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor | None = None,
 def dequantize_mxfp8(codes: torch.Tensor, scales: torch.Tensor, dtype=torch.bfloat16,
                      out: torch.Tensor | None = None) -> torch.Tensor:
     """E4M3 codes [..., k] + scales [..., k/32] -> y [..., k] in dtype."""
-    if not codes.is_cuda or codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
-        raise ValueError("codes and scales must be uint8 GPU tensors")
-    if not (codes.is_contiguous() and scales.is_contiguous()):
-        raise ValueError("codes and scales must be contiguous")
+    _need(codes, "codes", getattr(codes, "device", None), torch.uint8)
+    _need(scales, "scales", codes.device, torch.uint8)
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
     k = codes.shape[-1]
@@ -315,6 +328,7 @@ def dequantize_mxfp8(codes: torch.Tensor, scales: torch.Tensor, dtype=torch.bflo
         raise ValueError("scales do not match codes")
     if out is None:
         out = torch.empty(tuple(codes.shape), dtype=dtype, device=codes.device)
+    _need(out, "out", codes.device, dtype, codes.numel())
     with torch.cuda.device(codes.device):
         _raise(mx_dequantize_mxfp8(codes.data_ptr(), scales.data_ptr(), rows, k, _DTYPES[dtype],
                                    out.data_ptr(), _stream(codes.device)))
@@ -326,8 +340,7 @@ def fakequant_mxfp8(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.T
     rows, k = _check_input(x)
     if out is None:
         out = torch.empty_like(x)
-    if out.dtype != x.dtype or out.numel() != x.numel() or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like x")
+    _need(out, "out", x.device, x.dtype, x.numel())
     with torch.cuda.device(x.device):
         _raise(mx_fakequant_mxfp8(x.data_ptr(), _DTYPES[x.dtype], rows, k, out.data_ptr(),
                                   _stream(x.device)))
@@ -361,8 +374,9 @@ def quantize_nvfp4(x: torch.Tensor):
 
 def dequantize_nvfp4(codes: torch.Tensor, block_scales: torch.Tensor, tensor_scale: torch.Tensor,
                      dtype=torch.bfloat16) -> torch.Tensor:
-    if not codes.is_cuda or codes.dtype != torch.uint8 or block_scales.dtype != torch.uint8:
-        raise ValueError("codes and block scales must be uint8 GPU tensors")
+    _need(codes, "codes", getattr(codes, "device", None), torch.uint8)
+    _need(block_scales, "block_scales", codes.device, torch.uint8)
+    _need(tensor_scale, "tensor_scale", codes.device, torch.uint8, 1)
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
     k = codes.shape[-1] * 2
@@ -402,10 +416,9 @@ def quantize_mbs(x: torch.Tensor):
 
 def dequantize_mbs(codes: torch.Tensor, sub_scales: torch.Tensor, macro_mant: torch.Tensor,
                    dtype=torch.bfloat16) -> torch.Tensor:
-    for t in (codes, sub_scales, macro_mant):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.uint8 \
-                or not t.is_contiguous():
-            raise ValueError("codes, sub_scales and macro_mant must be contiguous uint8 GPU tensors")
+    _need(codes, "codes", getattr(codes, "device", None), torch.uint8)
+    _need(sub_scales, "sub_scales", codes.device, torch.uint8)
+    _need(macro_mant, "macro_mant", codes.device, torch.uint8)
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
     k = codes.shape[-1] * 2

@@ -137,6 +137,17 @@ def test_tensor_helpers_refuse_cpu_tensors(lib):
         mx.quantize(x)
     with pytest.raises(ValueError):
         mx.fakequant(x)
+    u8 = torch.zeros(2, 32, dtype=torch.uint8)
+    for f in (lambda: mx.dequantize(u8, u8[:, :2].contiguous()),
+              lambda: mx.dequantize_mxfp8(torch.zeros(2, 64, dtype=torch.uint8), u8[:, :2].contiguous()),
+              lambda: mx.dequantize_nvfp4(u8, u8[:, :4].contiguous(), u8[0, :1].contiguous()),
+              lambda: mx.dequantize_mbs(torch.zeros(2, 64, dtype=torch.uint8), u8[:, :8].contiguous(),
+                                        u8[:, :1].contiguous()),
+              lambda: mx.quantize_mxfp8(x), lambda: mx.quantize_nvfp4(x),
+              lambda: mx.quantize_mbs(torch.zeros(2, 128, dtype=torch.bfloat16)),
+              lambda: mx.quantize_multi([x]), lambda: mx.fakequant_multi([x])):
+        with pytest.raises(ValueError):
+            f()
 
 
 def test_missing_library_fails_loudly(tmp_path):

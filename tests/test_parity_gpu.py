@@ -214,6 +214,42 @@ def test_bad_arguments_raise_on_gpu():
         mx.quantize(x, mode="nope")
 
 
+def test_helpers_refuse_host_or_mismatched_tensors_before_launch():
+    """A CPU, wrong-dtype, wrong-size or strided tensor handed to any helper
+    is refused on the host, so no host pointer ever reaches a kernel."""
+    x = torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda")
+    c, s = mx.quantize(x)
+    cpu_c, cpu_s = c.cpu(), s.cpu()
+    cases = [
+        lambda: mx.quantize(x, codes=cpu_c),
+        lambda: mx.quantize(x, scales=torch.empty(4, 4, dtype=torch.int32, device="cuda")),
+        lambda: mx.quantize(x, codes=torch.empty(4, 63, dtype=torch.uint8, device="cuda")),
+        lambda: mx.dequantize(c, cpu_s),
+        lambda: mx.dequantize(c, s, out=torch.empty(4, 128, dtype=torch.bfloat16)),
+        lambda: mx.dequantize(c, s, torch.float32, out=torch.empty(4, 128, dtype=torch.bfloat16,
+                                                                   device="cuda")),
+        lambda: mx.fakequant(x, out=torch.empty(4, 128, dtype=torch.bfloat16)),
+        lambda: mx.fakequant(x, out=torch.empty(128, 4, dtype=torch.bfloat16, device="cuda").t()),
+        lambda: mx.block_mse(x, cpu_c, s),
+        lambda: mx.block_mse(x, c, s[:, :2].contiguous()),
+        lambda: mx.quantize_mxfp8(x, codes=torch.empty(4, 64, dtype=torch.uint8, device="cuda")),
+        lambda: mx.dequantize_mxfp8(torch.zeros(4, 128, dtype=torch.uint8, device="cuda"), cpu_s),
+        lambda: mx.fakequant_mxfp8(x, out=torch.empty(4, 128, dtype=torch.bfloat16)),
+        lambda: mx.dequantize_nvfp4(c, torch.zeros(4, 8, dtype=torch.uint8, device="cuda"),
+                                    torch.zeros(1, dtype=torch.uint8)),
+        lambda: mx.dequantize_nvfp4(c, torch.zeros(4, 8, dtype=torch.uint8),
+                                    torch.zeros(1, dtype=torch.uint8, device="cuda")),
+        lambda: mx.dequantize_mbs(c, torch.zeros(4, 8, dtype=torch.uint8, device="cuda"),
+                                  torch.zeros(4, 1, dtype=torch.uint8)),
+        lambda: mx.fakequant_multi([x], out=[torch.empty(4, 128, dtype=torch.bfloat16)]),
+        lambda: mx.quantize_multi([x, x.float()]),
+    ]
+    for i, f in enumerate(cases):
+        with pytest.raises(ValueError):
+            f()
+    torch.cuda.synchronize()
+
+
 def test_fakequant_in_place():
     x = workloads.bf16_student_t_outlier_channels(seed=24, shape=(256, 4096)).cuda()
     want = mx.fakequant(x)
