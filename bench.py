@@ -66,20 +66,35 @@ KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0>", "quantize_oas": "k_quantize<
              "dequantize_bf16": "k_dequantize<true>", "fakequant_ocp": "k_fakequant<true, 0>",
              "block_mse": "k_block_mse<true, true>"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mx_bf16_8192x4096_hbm_traffic.md")
-KERNEL_SRC = os.path.join(ROOT, "microscaling_fp4_block_mx_amd", "csrc", "mx_kernels.hip")
+KERNEL_SRCS = (os.path.join(ROOT, "microscaling_fp4_block_mx_amd", "csrc", "mx_kernels.hip"),
+               os.path.join(ROOT, "microscaling_fp4_block_mx_amd", "csrc", "mx_internal.h"))
+
+
+def kernel_code_hash() -> str:
+    """sha256 prefix of the kernel sources (mx_kernels.hip, mx_internal.h)
+    with comments and whitespace removed: a comment edit keeps the profiled
+    traffic figures valid, any code edit does not."""
+    import hashlib
+    import re
+    text = ""
+    for path in KERNEL_SRCS:
+        text += open(path).read() + "\n"
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def measured_traffic(op):
     """HBM bytes per launch of op's kernel from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, or None if that summary was taken on a
-    different kernel source than the one built here."""
-    import hashlib
+    FETCH_SIZE/WRITE_SIZE summary, or None if that summary was taken on
+    different kernel code than the one built here."""
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
-        h = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+        h = kernel_code_hash()
     except OSError:
         return None
-    if ("source_sha256_prefix " + h) not in lines:
+    if ("kernel_code_sha256_prefix " + h) not in lines:
         return None
     key = "traffic_bytes " + KERNEL_OF[op] + " "
     for ln in lines:

@@ -27,7 +27,9 @@
 //
 // Format facts (E2M1 grid 0, .5, 1, 1.5, 2, 3, 4, 6; E8M0 scale 2^(s-127);
 // two codes per byte, even element low) are stated with their sources in
-// include/mx.h.
+// include/mx.h. Later sections hold the other formats on the same item
+// layout (MXFP8, the NVFP4 comparator, MBS-Static) and the multi-tensor
+// launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1049,13 +1051,6 @@ __device__ __forceinline__ uint32_t dpp_ror4(uint32_t v) {
 __device__ __forceinline__ uint32_t dpp_ror8(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
 }
-__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
-  v = quad_max_u32(v);
-  v = max(v, dpp_ror4(v));
-  v = max(v, dpp_ror8(v));
-  return v;
-}
-
 // The U items of one tile, in phases across the items (every item's macro
 // maximum, then every factor, then every table read, then the codes) so the
 // scheduler can overlap their long dependency chains; the rare cases (a
