@@ -243,8 +243,8 @@ mx_status_t mx_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
  * equal x). No output may overlap another tensor's input or output
  * (inputs may be shared): MX_ERR_ALIAS. count == 0 does nothing; count < 0
  * is MX_ERR_SHAPE. On a per-tensor validation error nothing is launched and
- * mx_last_error_detail() names the tensor. Validation compares every output
- * range with every other range, so its host cost grows with count^2. */
+ * mx_last_error_detail() names the tensor (for an overlap, one of the two).
+ * Validation sorts the byte ranges: host cost O(count log count). */
 typedef struct {
   const void *x;   /* input [rows, k] */
   void *y;         /* mx_fakequant_multi: output [rows, k]; else unused */

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -290,6 +291,49 @@ struct Span {
   bool out;
 };
 
+// The latest-ending earlier span, and the latest-ending one of any other
+// owner: enough to tell whether some earlier span of an owner other than o
+// reaches past a point.
+struct Reach {
+  uintptr_t end1 = 0, end2 = 0;
+  int owner1 = -1;
+  void add(uintptr_t end, int owner) {
+    if (owner == owner1) {
+      end1 = end > end1 ? end : end1;
+    } else if (end > end1) {
+      end2 = end1;
+      end1 = end;
+      owner1 = owner;
+    } else if (end > end2) {
+      end2 = end;
+    }
+  }
+  bool other_reaches(uintptr_t point, int o) const {
+    return (owner1 != o ? end1 : end2) > point;
+  }
+};
+
+// A tensor one of whose spans overlaps another tensor's output (or whose
+// output overlaps another tensor's span), or -1. Sorted by
+// start, every overlapping pair is seen when its later-starting member
+// arrives: an output is checked against every earlier span, an input
+// against every earlier output. O(n log n).
+int cross_overlap(std::vector<Span> &spans) {
+  std::sort(spans.begin(), spans.end(), [](const Span &a, const Span &b) {
+    return reinterpret_cast<uintptr_t>(a.p) < reinterpret_cast<uintptr_t>(b.p);
+  });
+  Reach any, outs;
+  for (const Span &q : spans) {
+    const uintptr_t start = reinterpret_cast<uintptr_t>(q.p);
+    if (q.out && any.other_reaches(start, q.owner)) return q.owner;
+    if (!q.out && outs.other_reaches(start, q.owner)) return q.owner;
+    const uintptr_t end = start + (uintptr_t)q.n;
+    any.add(end, q.owner);
+    if (q.out) outs.add(end, q.owner);
+  }
+  return -1;
+}
+
 void set_detail_tensor(int i, const char *what) {
   snprintf(g_detail, sizeof g_detail, "tensor %d: %s", i, what);
 }
@@ -351,15 +395,9 @@ mx_status_t multi(const mx_tensor_t *tensors, int count, mx_dtype_t dtype,
   }
   // no tensor's output may touch another tensor's input or output (inputs
   // may be shared)
-  for (size_t a = 0; a < spans.size(); a++) {
-    if (!spans[a].out) continue;
-    for (size_t b = 0; b < spans.size(); b++) {
-      if (spans[b].owner == spans[a].owner) continue;
-      if (overlap(spans[a].p, spans[a].n, spans[b].p, spans[b].n)) {
-        set_detail_tensor(spans[a].owner, "an output overlaps another tensor's data");
-        return MX_ERR_ALIAS;
-      }
-    }
+  if (int bad = cross_overlap(spans); bad >= 0) {
+    set_detail_tensor(bad, "overlaps another tensor's output, or its output another tensor's data");
+    return MX_ERR_ALIAS;
   }
   if (launch.empty()) return MX_OK;
   return finish(mxi_launch_multi(launch.data(), (int)launch.size(), dtype == MX_BF16, mode,

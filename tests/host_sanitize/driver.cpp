@@ -158,6 +158,69 @@ static void multi() {
   expect_launch(mx_fakequant_multi(t, 5, MX_BF16, MX_SCALE_OCP, nullptr), "fakequant_multi", items, n0);
 }
 
+// the overlap rule against a brute-force check on random layouts: tensors
+// of 32 elements (bf16: x and y 64 B, codes 16 B, scales 1 B, all at 16-byte
+// steps) scattered over a small window so that ranges often collide
+static uint64_t g_rng = 0x9E3779B97F4A7C15ull;
+static uint32_t rnd(uint32_t n) {
+  g_rng ^= g_rng << 13;
+  g_rng ^= g_rng >> 7;
+  g_rng ^= g_rng << 17;
+  return (uint32_t)(g_rng % n);
+}
+static bool ov(uintptr_t a, int64_t na, uintptr_t b, int64_t nb) {
+  return a < b + (uintptr_t)nb && b < a + (uintptr_t)na;
+}
+static void multi_random() {
+  for (int trial = 0; trial < 4000; trial++) {
+    const bool fq = trial & 1;
+    const int n = 1 + (int)rnd(7);
+    mx_tensor_t t[8] = {};
+    for (int i = 0; i < n; i++) {
+      t[i].rows = 1;
+      t[i].k = 32;
+      t[i].x = P(X + 16 * rnd(40));
+      t[i].codes = (uint8_t *)P(X + 16 * rnd(40));
+      t[i].scales = (uint8_t *)P(X + 16 * rnd(40));
+      t[i].y = rnd(4) == 0 ? const_cast<void *>(t[i].x) : P(X + 16 * rnd(40));
+    }
+    // brute force: own ranges first (as the single-tensor calls), then every
+    // output against every other tensor's ranges
+    mx_status_t want = MX_OK;
+    struct R { uintptr_t p; int64_t n; int o; bool out; } r[24];
+    int nr = 0;
+    for (int i = 0; i < n && want == MX_OK; i++) {
+      const uintptr_t x = (uintptr_t)t[i].x;
+      if (fq) {
+        const uintptr_t y = (uintptr_t)t[i].y;
+        if (x != y && ov(x, 64, y, 64)) want = MX_ERR_ALIAS;
+        r[nr++] = {x, 64, i, false};
+        r[nr++] = {y, 64, i, true};
+      } else {
+        const uintptr_t c = (uintptr_t)t[i].codes, sc = (uintptr_t)t[i].scales;
+        if (ov(x, 64, c, 16) || ov(x, 64, sc, 1) || ov(c, 16, sc, 1)) want = MX_ERR_ALIAS;
+        r[nr++] = {x, 64, i, false};
+        r[nr++] = {c, 16, i, true};
+        r[nr++] = {sc, 1, i, true};
+      }
+    }
+    for (int a = 0; a < nr && want == MX_OK; a++)
+      for (int b = 0; b < nr; b++)
+        if (r[a].out && r[a].o != r[b].o && ov(r[a].p, r[a].n, r[b].p, r[b].n)) {
+          want = MX_ERR_ALIAS;
+          break;
+        }
+    const mx_status_t got = fq ? mx_fakequant_multi(t, n, MX_BF16, MX_SCALE_OCP, nullptr)
+                               : mx_quantize_multi(t, n, MX_BF16, MX_SCALE_OCP, nullptr);
+    if (got != want) {
+      fprintf(stderr, "random layout %d (%s, %d tensors): got %d, want %d\n", trial,
+              fq ? "fakequant" : "quantize", n, (int)got, (int)want);
+      g_fail++;
+      return;
+    }
+  }
+}
+
 // a failing launch reports MX_ERR_HIP; the detail string is per thread
 static void hip_errors() {
   const int64_t k = 8 * kFailItems;  // one row whose item count makes the stub fail
@@ -195,6 +258,7 @@ int main() {
   mxfp4();
   mxfp8_nvfp4_mbs();
   multi();
+  multi_random();
   hip_errors();
   threads();
   if (g_fail) {
