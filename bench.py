@@ -61,6 +61,9 @@ EXTRA_BYTES_PER_ELEM = {
     # MBS-Static: 16-element sub-block bytes plus one macro byte per 128
     "quantize_mbs": 2 + 0.5 + 1 / 16 + 1 / 128,
     "dequantize_mbs_bf16": 0.5 + 1 / 16 + 1 / 128 + 2,
+    # fused fake-quant of the comparators (NVFP4 reads x twice)
+    "fakequant_nvfp4": 2 + 2 + 2,
+    "fakequant_mbs": 2 + 2,
 }
 KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0>", "quantize_oas": "k_quantize<true, 1>",
              "dequantize_bf16": "k_dequantize<true>", "fakequant_ocp": "k_fakequant<true, 0>",
@@ -214,6 +217,11 @@ def main():
             st = mx.mx_dequantize_mbs(b["c_oas"].data_ptr(), b["smb"].data_ptr(),
                                       b["mmb"].data_ptr(), R_, K_, mx.MX_BF16,
                                       b["y_dq"].data_ptr(), sh)
+        elif op == "fakequant_nvfp4":
+            st = mx.mx_fakequant_nvfp4(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["y_fq"].data_ptr(),
+                                       wsnv.data_ptr(), wsnv_bytes, sh)
+        elif op == "fakequant_mbs":
+            st = mx.mx_fakequant_mbs(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["y_fq"].data_ptr(), sh)
         elif op in ("fakequant_oas", "fakequant_oas_nf"):
             mode = mx.MX_SCALE_OAS if op == "fakequant_oas" else mx.MX_SCALE_OAS_NF
             st = mx.mx_fakequant(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mode,

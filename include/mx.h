@@ -190,6 +190,14 @@ mx_status_t mx_fakequant_mxfp8(const void *x, mx_dtype_t dtype, int64_t rows,
  * workspace of mx_nvfp4_workspace_size(rows, k) bytes (4-byte aligned).
  * rows == 0 does nothing. Other conventions as above. */
 size_t mx_nvfp4_workspace_size(int64_t rows, int64_t k);
+/* y = mx_dequantize_nvfp4(mx_quantize_nvfp4(x)) in x's dtype, fused (x is
+ * still read twice: the tensor maximum, then the blocks); y may equal x.
+ * Same workspace as mx_quantize_nvfp4. For quantization-aware training
+ * in this format, which the Axolotl MXFP4 QAT page's quantization-config
+ * section lists beside MXFP4 (NVFP4 with a group size of 16). */
+mx_status_t mx_fakequant_nvfp4(const void *x, mx_dtype_t dtype, int64_t rows,
+                               int64_t k, void *y, void *workspace,
+                               size_t workspace_bytes, void *stream);
 mx_status_t mx_quantize_nvfp4(const void *x, mx_dtype_t x_dtype, int64_t rows,
                               int64_t k, uint8_t *codes, uint8_t *block_scales,
                               uint8_t *tensor_scale, void *workspace,
@@ -221,6 +229,10 @@ mx_status_t mx_dequantize_nvfp4(const uint8_t *codes,
 mx_status_t mx_quantize_mbs(const void *x, mx_dtype_t x_dtype, int64_t rows,
                             int64_t k, uint8_t *codes, uint8_t *sub_scales,
                             uint8_t *macro_mant, void *stream);
+/* y = mx_dequantize_mbs(mx_quantize_mbs(x)) in x's dtype, fused; y may
+ * equal x. */
+mx_status_t mx_fakequant_mbs(const void *x, mx_dtype_t dtype, int64_t rows,
+                             int64_t k, void *y, void *stream);
 mx_status_t mx_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
                               const uint8_t *macro_mant, int64_t rows,
                               int64_t k, mx_dtype_t y_dtype, void *y,

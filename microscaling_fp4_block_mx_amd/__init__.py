@@ -39,7 +39,8 @@ EXPORTS = ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
            "mx_block_mse_workspace_size", "mx_quantize_mxfp8", "mx_dequantize_mxfp8",
            "mx_fakequant_mxfp8", "mx_nvfp4_workspace_size", "mx_quantize_nvfp4",
            "mx_dequantize_nvfp4", "mx_quantize_mbs", "mx_dequantize_mbs", "mx_quantize_multi",
-           "mx_fakequant_multi", "mx_status_string", "mx_last_error_detail")
+           "mx_fakequant_multi", "mx_fakequant_nvfp4", "mx_fakequant_mbs", "mx_status_string",
+           "mx_last_error_detail")
 
 _lib = None
 
@@ -69,12 +70,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mx_dequantize_nvfp4.argtypes = [p, p, p, i64, i64, i32, p, p]
     lib.mx_quantize_mbs.argtypes = [p, i32, i64, i64, p, p, p, p]
     lib.mx_dequantize_mbs.argtypes = [p, p, p, i64, i64, i32, p, p]
+    lib.mx_fakequant_nvfp4.argtypes = [p, i32, i64, i64, p, p, ctypes.c_size_t, p]
+    lib.mx_fakequant_mbs.argtypes = [p, i32, i64, i64, p, p]
     lib.mx_quantize_multi.argtypes = [p, i32, i32, i32, p]
     lib.mx_fakequant_multi.argtypes = [p, i32, i32, i32, p]
     for f in ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
               "mx_quantize_mxfp8", "mx_dequantize_mxfp8", "mx_fakequant_mxfp8",
               "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_quantize_mbs",
-              "mx_dequantize_mbs", "mx_quantize_multi", "mx_fakequant_multi"):
+              "mx_dequantize_mbs", "mx_quantize_multi", "mx_fakequant_multi",
+              "mx_fakequant_nvfp4", "mx_fakequant_mbs"):
         getattr(lib, f).restype = i32
     lib.mx_status_string.argtypes = [i32]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -143,6 +147,15 @@ def mx_quantize_mbs(x, x_dtype, rows, k, codes, sub_scales, macro_mant, stream) 
 def mx_dequantize_mbs(codes, sub_scales, macro_mant, rows, k, y_dtype, y, stream) -> int:
     return load_library().mx_dequantize_mbs(codes, sub_scales, macro_mant, rows, k, y_dtype, y,
                                             stream)
+
+
+def mx_fakequant_nvfp4(x, dtype, rows, k, y, workspace, workspace_bytes, stream) -> int:
+    return load_library().mx_fakequant_nvfp4(x, dtype, rows, k, y, workspace, workspace_bytes,
+                                             stream)
+
+
+def mx_fakequant_mbs(x, dtype, rows, k, y, stream) -> int:
+    return load_library().mx_fakequant_mbs(x, dtype, rows, k, y, stream)
 
 
 class MxTensor(ctypes.Structure):
@@ -372,6 +385,31 @@ def quantize_nvfp4(x: torch.Tensor):
     return codes, bs, ts
 
 
+def _check_input_n(x, multiple: int, what: str):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype not in _DTYPES:
+        raise ValueError("need a float32/bfloat16 GPU tensor")
+    if x.dim() == 0 or not x.is_contiguous():
+        raise ValueError("need a contiguous tensor with at least one dimension")
+    k = x.shape[-1]
+    if k <= 0 or k % multiple:
+        raise ValueError(f"{what} needs the last dimension to be a multiple of {multiple}")
+    return x.numel() // k if x.numel() else 0, k
+
+
+def fakequant_nvfp4(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """dequantize_nvfp4(quantize_nvfp4(x)) in x's dtype, fused; out may be x."""
+    rows, k = _check_input_n(x, 16, "NVFP4")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.device, x.dtype, x.numel())
+    wsb = mx_nvfp4_workspace_size(rows, k)
+    ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _raise(mx_fakequant_nvfp4(x.data_ptr(), _DTYPES[x.dtype], rows, k, out.data_ptr(),
+                                  ws.data_ptr(), wsb, _stream(x.device)))
+    return out
+
+
 def dequantize_nvfp4(codes: torch.Tensor, block_scales: torch.Tensor, tensor_scale: torch.Tensor,
                      dtype=torch.bfloat16) -> torch.Tensor:
     _need(codes, "codes", getattr(codes, "device", None), torch.uint8)
@@ -412,6 +450,18 @@ def quantize_mbs(x: torch.Tensor):
         _raise(mx_quantize_mbs(x.data_ptr(), _DTYPES[x.dtype], rows, k, codes.data_ptr(),
                                ss.data_ptr(), mm.data_ptr(), _stream(x.device)))
     return codes, ss, mm
+
+
+def fakequant_mbs(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """dequantize_mbs(quantize_mbs(x)) in x's dtype, fused; out may be x."""
+    rows, k = _check_input_n(x, 128, "MBS-Static")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.device, x.dtype, x.numel())
+    with torch.cuda.device(x.device):
+        _raise(mx_fakequant_mbs(x.data_ptr(), _DTYPES[x.dtype], rows, k, out.data_ptr(),
+                                _stream(x.device)))
+    return out
 
 
 def dequantize_mbs(codes: torch.Tensor, sub_scales: torch.Tensor, macro_mant: torch.Tensor,

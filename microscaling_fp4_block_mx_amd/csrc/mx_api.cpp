@@ -220,7 +220,7 @@ mx_status_t mx_quantize_nvfp4(const void *x, mx_dtype_t x_dtype, int64_t rows, i
       overlap(workspace, nw, block_scales, n / 16) || overlap(workspace, nw, tensor_scale, 1))
     return MX_ERR_ALIAS;
   return finish(mxi_launch_quantize_nv(x, x_dtype == MX_BF16, n / 8, codes, block_scales,
-                                       tensor_scale, static_cast<uint32_t *>(workspace),
+                                       tensor_scale, static_cast<uint32_t *>(workspace), nullptr,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -258,7 +258,39 @@ mx_status_t mx_quantize_mbs(const void *x, mx_dtype_t x_dtype, int64_t rows, int
       overlap(sub_scales, n / 16, macro_mant, n / 128))
     return MX_ERR_ALIAS;
   return finish(mxi_launch_quantize_mbs(x, x_dtype == MX_BF16, n / 8, codes, sub_scales,
-                                        macro_mant, static_cast<hipStream_t>(stream)));
+                                        macro_mant, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_fakequant_nvfp4(const void *x, mx_dtype_t dtype, int64_t rows, int64_t k,
+                               void *y, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!dtype_ok(dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape16(rows, k)) return s;
+  if (rows == 0) return MX_OK;
+  if (!x || !y) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return MX_ERR_ALIGN;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 ||
+      workspace_bytes < mx_nvfp4_workspace_size(rows, k))
+    return MX_ERR_WORKSPACE;
+  const int64_t nb = rows * k * elem_bytes(dtype), nw = (int64_t)workspace_bytes;
+  if ((x != y && overlap(x, nb, y, nb)) || overlap(workspace, nw, x, nb) ||
+      overlap(workspace, nw, y, nb))
+    return MX_ERR_ALIAS;
+  return finish(mxi_launch_quantize_nv(x, dtype == MX_BF16, rows * k / 8, nullptr, nullptr,
+                                       nullptr, static_cast<uint32_t *>(workspace), y,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_fakequant_mbs(const void *x, mx_dtype_t dtype, int64_t rows, int64_t k, void *y,
+                             void *stream) {
+  if (!dtype_ok(dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape_n(rows, k, 128)) return s;
+  if (rows == 0) return MX_OK;
+  if (!x || !y) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return MX_ERR_ALIGN;
+  const int64_t nb = rows * k * elem_bytes(dtype);
+  if (x != y && overlap(x, nb, y, nb)) return MX_ERR_ALIAS;
+  return finish(mxi_launch_quantize_mbs(x, dtype == MX_BF16, rows * k / 8, nullptr, nullptr,
+                                        nullptr, y, static_cast<hipStream_t>(stream)));
 }
 
 mx_status_t mx_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,

@@ -28,15 +28,18 @@ hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *
                                  hipStream_t st);
 // NVFP4 comparator (nitems = rows * k / 8, even).
 size_t mxi_nvfp4_partials(int64_t nitems);
+// y != NULL: fused fake-quant into y (codes, block_scales, tensor_scale unused).
 hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                   uint8_t *block_scales, uint8_t *tensor_scale,
-                                  uint32_t *partial, hipStream_t st);
+                                  uint32_t *partial, void *y, hipStream_t st);
 hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_scales,
                                     const uint8_t *tensor_scale, int bf16, int64_t nitems, void *y,
                                     hipStream_t st);
 // MBS-Static (nitems = rows * k / 8, a multiple of 16).
+// y != NULL: fused fake-quant into y (codes, sub_scales, macro_mant unused).
 hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint8_t *codes,
-                                   uint8_t *sub_scales, uint8_t *macro_mant, hipStream_t st);
+                                   uint8_t *sub_scales, uint8_t *macro_mant, void *y,
+                                   hipStream_t st);
 hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
                                      const uint8_t *macro_mant, int bf16, int64_t nitems, void *y,
                                      hipStream_t st);

@@ -927,14 +927,22 @@ __device__ __forceinline__ int nv_tensor_exp(uint32_t amax_bits) {
 
 __device__ __forceinline__ uint32_t dpp_x1_max(uint32_t v) { return max(v, dpp_x1(v)); }
 
+// Decoding used by the fused fake-quant below (defined with the dequantize
+// kernel).
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *__restrict__ x,
+__device__ __forceinline__ void nv_decode_item(uint32_t c, uint32_t sbyte, float inv_s,
+                                               uint32_t (&out)[BF16 ? 4 : 8]);
+
+// FQ: fake-quant (y = dequantize(quantize(x)) in x's dtype; y may be x)
+// instead of writing codes, block scales and the tensor byte.
+template <bool BF16, bool FQ>
+__global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *x,
                                                           const uint32_t *__restrict__ partial,
                                                           int npartial,
                                                           uint32_t *__restrict__ codes,
                                                           uint8_t *__restrict__ block_scales,
                                                           uint8_t *__restrict__ tensor_scale,
-                                                          int64_t nitems) {
+                                                          void *y, int64_t nitems) {
   // every workgroup reduces the first pass's maxima (max is order-free and
   // idempotent, so clamped duplicate loads are harmless; all loads are issued
   // before the first use), and fills a table of fl32(1 / v) for the E4M3
@@ -959,8 +967,9 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *__restrict
 #pragma unroll
   for (int w = 0; w < kThreads / 64; w++) a = max(a, wave_max[w]);
   const int t = nv_tensor_exp(a);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = (uint8_t)(t + 127);
+  if (!FQ && blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = (uint8_t)(t + 127);
   const float S = __uint_as_float((uint32_t)(t + 127) << 23);
+  const float inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t
 
   Item<BF16> xv[kUnroll];
   tile_loop<kUnroll>(
@@ -991,9 +1000,39 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *__restrict
           c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[4], v[5], one, 2);
           c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[6], v[7], one, 3);
         }
-        st<false>(codes + it, c);
-        if ((threadIdx.x & 1) == 0) st<false>(block_scales + (it >> 1), (uint8_t)sbyte);
+        if constexpr (FQ) {
+          uint32_t out[BF16 ? 4 : 8];
+          nv_decode_item<BF16>(c, sbyte, inv_s, out);
+          store_item<BF16>(y, it, out);
+        } else {
+          st<false>(codes + it, c);
+          if ((threadIdx.x & 1) == 0) st<false>(block_scales + (it >> 1), (uint8_t)sbyte);
+        }
       });
+}
+
+// Decoded values of one item: E2M1 code * s_b * 2^-t, exact in fp32 (at
+// most 2 + 4 significant bits), rounded to bf16 if asked; block scale byte
+// 0x7F (NaN) gives the canonical NaN.
+template <bool BF16>
+__device__ __forceinline__ void nv_decode_item(uint32_t c, uint32_t sbyte, float inv_s,
+                                               uint32_t (&out)[BF16 ? 4 : 8]) {
+  // s_b * 2^-t exactly (E4M3 decode with a power-of-two scale)
+  const float sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sbyte, inv_s, false)[0];
+  float q[8];
+  decode_f32(c, 127u, q);  // E2M1 values at scale 1
+  const bool nan = (sbyte & 0x7Fu) == 0x7Fu;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+      const b2 p = {(__bf16)(q[2 * j] * sv), (__bf16)(q[2 * j + 1] * sv)};
+      out[j] = nan ? kNaN16x2 : __builtin_bit_cast(uint32_t, p);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = nan ? kNaN32 : __float_as_uint(q[i] * sv);
+  }
 }
 
 template <bool BF16>
@@ -1003,7 +1042,6 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_nv(const uint32_t *__re
                                                             void *__restrict__ y, int64_t nitems) {
   const int t = (int)*tensor_scale - 127;
   const float inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t, scale operand
-  const float one = 1.0f;
   uint32_t cw[kU<BF16>], sb[kU<BF16>];
   tile_loop<kU<BF16>>(
       nitems,
@@ -1012,23 +1050,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_nv(const uint32_t *__re
         sb[u] = ld<false>(block_scales + (it >> 1));
       },
       [&](int u, int64_t it) {
-        // s_b * 2^-t exactly (E4M3 decode with a power-of-two scale)
-        const float sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb[u], inv_s, false)[0];
-        float q[8];
-        decode_f32(cw[u], 127u, q);  // E2M1 values at scale 1
         uint32_t out[BF16 ? 4 : 8];
-        const bool nan = (sb[u] & 0x7Fu) == 0x7Fu;
-        if constexpr (BF16) {
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-            const b2 p = {(__bf16)(q[2 * j] * sv), (__bf16)(q[2 * j + 1] * sv)};
-            out[j] = nan ? kNaN16x2 : __builtin_bit_cast(uint32_t, p);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; i++) out[i] = nan ? kNaN32 : __float_as_uint(q[i] * sv);
-        }
+        nv_decode_item<BF16>(cw[u], sb[u], inv_s, out);
         store_item<BF16>(y, it, out);
       });
 }
@@ -1051,16 +1074,39 @@ __device__ __forceinline__ uint32_t dpp_ror4(uint32_t v) {
 __device__ __forceinline__ uint32_t dpp_ror8(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
 }
+// Decoded values of one item: E2M1 * 2^(s-127) * (1 + m/256), exact in fp32
+// (at most 2 + 9 significant bits), rounded to bf16 if asked; sub-block byte
+// 255 gives the canonical NaN.
+template <bool BF16>
+__device__ __forceinline__ void mbs_decode_item(uint32_t c, uint32_t s, uint32_t m,
+                                                uint32_t (&out)[BF16 ? 4 : 8]) {
+  const float f = 1.0f + (float)m * (1.0f / 256.0f);
+  float q[8];
+  decode_f32(c, s, q);  // E2M1 * 2^(s-127); NaN for byte 255
+  const bool nan = s == 255u;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+      const b2 p = {(__bf16)(q[2 * j] * f), (__bf16)(q[2 * j + 1] * f)};
+      out[j] = nan ? kNaN16x2 : __builtin_bit_cast(uint32_t, p);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = nan ? kNaN32 : __float_as_uint(q[i] * f);
+  }
+}
+
 // The U items of one tile, in phases across the items (every item's macro
 // maximum, then every factor, then every table read, then the codes) so the
 // scheduler can overlap their long dependency chains; the rare cases (a
 // subnormal quotient, a NaN/Inf sub-block) are patched afterwards under a
 // branch that a wave without them skips.
-template <bool BF16, int U>
+template <bool BF16, int U, bool FQ>
 __device__ __forceinline__ void mbs_tile(const Item<BF16> (&xv)[U], const float *inv_tab,
                                          uint32_t *__restrict__ codes,
                                          uint8_t *__restrict__ sub_scales,
-                                         uint8_t *__restrict__ macro_mant, int64_t base,
+                                         uint8_t *__restrict__ macro_mant, void *y, int64_t base,
                                          int64_t nitems, bool full) {
   uint32_t aS[U], aM[U], m[U], s[U], c[U];
   float inv[U];
@@ -1118,19 +1164,27 @@ __device__ __forceinline__ void mbs_tile(const Item<BF16> (&xv)[U], const float 
     if (__builtin_expect(s[u] == 255u, 0)) c[u] = sign_codes<BF16>(xv[u]);
     const int64_t it = base + u * kThreads;
     if (full || it < nitems) {  // whole rows of 16 lanes drop out together
-      st<false>(codes + it, c[u]);
-      if ((threadIdx.x & 1) == 0) st<false>(sub_scales + (it >> 1), (uint8_t)s[u]);
-      if ((threadIdx.x & 15) == 0) st<false>(macro_mant + (it >> 4), (uint8_t)m[u]);
+      if constexpr (FQ) {
+        uint32_t out[BF16 ? 4 : 8];
+        mbs_decode_item<BF16>(c[u], s[u], m[u], out);
+        store_item<BF16>(y, it, out);
+      } else {
+        st<false>(codes + it, c[u]);
+        if ((threadIdx.x & 1) == 0) st<false>(sub_scales + (it >> 1), (uint8_t)s[u]);
+        if ((threadIdx.x & 15) == 0) st<false>(macro_mant + (it >> 4), (uint8_t)m[u]);
+      }
     }
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *__restrict__ x,
+// FQ: fake-quant (y = dequantize(quantize(x)) in x's dtype; y may be x)
+// instead of writing codes and bytes.
+template <bool BF16, bool FQ>
+__global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *x,
                                                            uint32_t *__restrict__ codes,
                                                            uint8_t *__restrict__ sub_scales,
                                                            uint8_t *__restrict__ macro_mant,
-                                                           int64_t nitems) {
+                                                           void *y, int64_t nitems) {
   // fl32(1 / f) for every macro mantissa m (f = 1 + m/256): IEEE division,
   // once per workgroup, so the per-item cost is one LDS read
   static_assert(kThreads == 256, "one table entry per thread");
@@ -1147,7 +1201,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *__restric
 #pragma unroll
     for (int u = 0; u < U; u++) load_item<BF16>(x, base + u * kThreads, xv[u]);
     __builtin_amdgcn_sched_barrier(0);
-    mbs_tile<BF16, U>(xv, inv_tab, codes, sub_scales, macro_mant, base, nitems, true);
+    mbs_tile<BF16, U, FQ>(xv, inv_tab, codes, sub_scales, macro_mant, y, base, nitems, true);
   }
   if (t == nfull && nfull * tile < nitems) {
     const int64_t base = t * tile + threadIdx.x;
@@ -1156,7 +1210,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *__restric
       if (base + u * kThreads < nitems) load_item<BF16>(x, base + u * kThreads, xv[u]);
       else xv[u] = Item<BF16>{};  // zeros: finite, so lanes past the end stay quiet
     }
-    mbs_tile<BF16, U>(xv, inv_tab, codes, sub_scales, macro_mant, base, nitems, false);
+    mbs_tile<BF16, U, FQ>(xv, inv_tab, codes, sub_scales, macro_mant, y, base, nitems, false);
   }
 }
 
@@ -1174,22 +1228,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_mbs(const uint32_t *__r
         mb[u] = ld<false>(macro_mant + (it >> 4));
       },
       [&](int u, int64_t it) {
-        const float f = 1.0f + (float)mb[u] * (1.0f / 256.0f);
-        float q[8];
-        decode_f32(cw[u], sb[u], q);  // E2M1 * 2^(s-127); NaN for byte 255
         uint32_t out[BF16 ? 4 : 8];
-        const bool nan = sb[u] == 255u;
-        if constexpr (BF16) {
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-            const b2 p = {(__bf16)(q[2 * j] * f), (__bf16)(q[2 * j + 1] * f)};
-            out[j] = nan ? kNaN16x2 : __builtin_bit_cast(uint32_t, p);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; i++) out[i] = nan ? kNaN32 : __float_as_uint(q[i] * f);
-        }
+        mbs_decode_item<BF16>(cw[u], sb[u], mb[u], out);
         store_item<BF16>(y, it, out);
       });
 }
@@ -1346,18 +1386,26 @@ size_t mxi_nvfp4_partials(int64_t nitems) { return grid_for(nitems, MX_NV_GRID_C
 
 hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                   uint8_t *block_scales, uint8_t *tensor_scale,
-                                  uint32_t *partial, hipStream_t st) {
+                                  uint32_t *partial, void *y, hipStream_t st) {
   const unsigned gp = grid_for(nitems, MX_NV_GRID_CAP);
   const dim3 g(gp), b(kThreads);
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
   if (bf16) {
     hipLaunchKernelGGL((k_absmax_partials<true>), dim3(gp), b, 0, st, x, partial, nitems);
-    hipLaunchKernelGGL((k_quantize_nv<true>), g, b, 0, st, x, partial, (int)gp, c, block_scales,
-                       tensor_scale, nitems);
+    if (y)
+      hipLaunchKernelGGL((k_quantize_nv<true, true>), g, b, 0, st, x, partial, (int)gp, c,
+                         block_scales, tensor_scale, y, nitems);
+    else
+      hipLaunchKernelGGL((k_quantize_nv<true, false>), g, b, 0, st, x, partial, (int)gp, c,
+                         block_scales, tensor_scale, y, nitems);
   } else {
     hipLaunchKernelGGL((k_absmax_partials<false>), dim3(gp), b, 0, st, x, partial, nitems);
-    hipLaunchKernelGGL((k_quantize_nv<false>), g, b, 0, st, x, partial, (int)gp, c, block_scales,
-                       tensor_scale, nitems);
+    if (y)
+      hipLaunchKernelGGL((k_quantize_nv<false, true>), g, b, 0, st, x, partial, (int)gp, c,
+                         block_scales, tensor_scale, y, nitems);
+    else
+      hipLaunchKernelGGL((k_quantize_nv<false, false>), g, b, 0, st, x, partial, (int)gp, c,
+                         block_scales, tensor_scale, y, nitems);
   }
   return hipGetLastError();
 }
@@ -1377,13 +1425,25 @@ hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_s
 }
 
 hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint8_t *codes,
-                                   uint8_t *sub_scales, uint8_t *macro_mant, hipStream_t st) {
+                                   uint8_t *sub_scales, uint8_t *macro_mant, void *y,
+                                   hipStream_t st) {
   const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
-  if (bf16)
-    hipLaunchKernelGGL((k_quantize_mbs<true>), g, b, 0, st, x, c, sub_scales, macro_mant, nitems);
-  else
-    hipLaunchKernelGGL((k_quantize_mbs<false>), g, b, 0, st, x, c, sub_scales, macro_mant, nitems);
+  if (bf16) {
+    if (y)
+      hipLaunchKernelGGL((k_quantize_mbs<true, true>), g, b, 0, st, x, c, sub_scales, macro_mant,
+                         y, nitems);
+    else
+      hipLaunchKernelGGL((k_quantize_mbs<true, false>), g, b, 0, st, x, c, sub_scales,
+                         macro_mant, y, nitems);
+  } else {
+    if (y)
+      hipLaunchKernelGGL((k_quantize_mbs<false, true>), g, b, 0, st, x, c, sub_scales,
+                         macro_mant, y, nitems);
+    else
+      hipLaunchKernelGGL((k_quantize_mbs<false, false>), g, b, 0, st, x, c, sub_scales,
+                         macro_mant, y, nitems);
+  }
   return hipGetLastError();
 }
 

@@ -108,6 +108,21 @@ static void mxfp8_nvfp4_mbs() {
                                   MX_BF16, P(Y), nullptr),
                 "dequantize_mbs", 3 * 384 / 8, n0);
   n0 = g_calls;
+  expect_launch(mx_fakequant_nvfp4(P(X), MX_BF16, 9, 48, P(Y), P(Ws), nvb, nullptr),
+                "fakequant_nv", 9 * 48 / 8, n0);
+  CHECK(g_last.p[1] == P(Y) && g_last.p[5] == P(Ws));
+  n0 = g_calls;
+  expect_launch(mx_fakequant_nvfp4(P(X), MX_F32, 9, 48, P(X), P(Ws), nvb, nullptr),
+                "fakequant_nv", 9 * 48 / 8, n0);  // in place
+  n0 = g_calls;
+  expect_launch(mx_fakequant_mbs(P(X), MX_BF16, 2, 256, P(Y), nullptr), "fakequant_mbs", 64, n0);
+  n0 = g_calls;
+  CHECK(mx_fakequant_nvfp4(P(X), MX_BF16, 9, 48, P(X + 16), P(Ws), nvb, nullptr) == MX_ERR_ALIAS);
+  CHECK(mx_fakequant_nvfp4(P(X), MX_BF16, 9, 48, P(Y), P(Y + 32), nvb, nullptr) == MX_ERR_ALIAS);
+  CHECK(mx_fakequant_nvfp4(P(X), MX_BF16, 9, 48, P(Y), nullptr, 0, nullptr) == MX_ERR_WORKSPACE);
+  CHECK(mx_fakequant_mbs(P(X), MX_BF16, 2, 192, P(Y), nullptr) == MX_ERR_SHAPE);
+  CHECK(mx_fakequant_mbs(P(X), MX_BF16, 2, 256, P(X + 32), nullptr) == MX_ERR_ALIAS);
+  CHECK(g_calls == n0);
   CHECK(mx_quantize_mbs(P(X), MX_F32, 3, 320, (uint8_t *)P(Cd), (uint8_t *)P(Sc), (uint8_t *)P(Ts), nullptr) == MX_ERR_SHAPE);
   CHECK(mx_quantize_nvfp4(P(X), MX_BF16, 9, 40, (uint8_t *)P(Cd), (uint8_t *)P(Sc), (uint8_t *)P(Ts), P(Ws), nvb, nullptr) == MX_ERR_SHAPE);
   CHECK(mx_quantize_nvfp4(P(X), MX_BF16, 9, 48, (uint8_t *)P(Cd), (uint8_t *)P(Sc), (uint8_t *)P(Ts), P(Ws + 2), nvb, nullptr) == MX_ERR_WORKSPACE);

@@ -60,18 +60,20 @@ hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t n, void *y, hi
 }
 size_t mxi_nvfp4_partials(int64_t n) { return n > 0 ? (size_t)((n + 1023) / 1024 > 2048 ? 2048 : (n + 1023) / 1024) : 1; }
 hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t n, uint8_t *c, uint8_t *bs,
-                                  uint8_t *ts, uint32_t *part, hipStream_t) {
+                                  uint8_t *ts, uint32_t *part, void *y, hipStream_t) {
   g_last.p[4] = ts;
   g_last.p[5] = part;
-  return rec("quantize_nv", n, bf16, -1, x, c, bs, nullptr);
+  return rec(y ? "fakequant_nv" : "quantize_nv", n, bf16, -1, x, y ? y : (const void *)c, bs,
+             nullptr);
 }
 hipError_t mxi_launch_dequantize_nv(const uint8_t *c, const uint8_t *bs, const uint8_t *ts,
                                     int bf16, int64_t n, void *y, hipStream_t) {
   return rec("dequantize_nv", n, bf16, -1, c, bs, ts, y);
 }
 hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t n, uint8_t *c, uint8_t *ss,
-                                   uint8_t *mm, hipStream_t) {
-  return rec("quantize_mbs", n, bf16, -1, x, c, ss, mm);
+                                   uint8_t *mm, void *y, hipStream_t) {
+  return rec(y ? "fakequant_mbs" : "quantize_mbs", n, bf16, -1, x, y ? y : (const void *)c, ss,
+             mm);
 }
 hipError_t mxi_launch_dequantize_mbs(const uint8_t *c, const uint8_t *ss, const uint8_t *mm,
                                      int bf16, int64_t n, void *y, hipStream_t) {

@@ -38,6 +38,10 @@ def check_mbs(x: torch.Tensor, label: str):
     for dt, name in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
         assert_same_bits(mx.dequantize_mbs(c, s, m, dt), oracle.dequantize_mbs(wc, ws, wm, name),
                          f"{label} mbs dequant {name}")
+    # fused fake-quant: the oracle's quantize then dequantize, in x's dtype
+    name = "bf16" if x.dtype == torch.bfloat16 else "f32"
+    assert_same_bits(mx.fakequant_mbs(x.cuda()), oracle.dequantize_mbs(wc, ws, wm, name),
+                     f"{label} mbs fake-quant")
 
 
 def test_mbs_golden_macro_block():
@@ -130,3 +134,12 @@ def test_mbs_versus_mxfp4_qsnr():
         assert q["mbs"] > q["mx"]
         if name == "activations":
             assert q["nv"] - q["mbs"] < 1.0
+
+
+def test_mbs_fakequant_in_place():
+    x = workloads.bf16_student_t_outlier_channels(32, shape=(512, 4096)).cuda()
+    want = mx.fakequant_mbs(x)
+    y = x.clone()
+    got = mx.fakequant_mbs(y, out=y)
+    assert got.data_ptr() == y.data_ptr()
+    assert torch.equal(want.view(torch.int16), got.view(torch.int16))

@@ -37,6 +37,10 @@ def check_nv(x: torch.Tensor, label: str):
     for dt, name in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
         assert_same_bits(mx.dequantize_nvfp4(c, b, t, dt), oracle.dequantize_nvfp4(wc, wb, wt, name),
                          f"{label} nvfp4 dequant {name}")
+    # fused fake-quant: the oracle's quantize then dequantize, in x's dtype
+    name = "bf16" if x.dtype == torch.bfloat16 else "f32"
+    assert_same_bits(mx.fakequant_nvfp4(x.cuda()), oracle.dequantize_nvfp4(wc, wb, wt, name),
+                     f"{label} nvfp4 fake-quant")
 
 
 def test_nvfp4_golden_blocks():
@@ -94,3 +98,12 @@ def test_nvfp4_versus_mxfp4_qsnr():
         q_mx = 10 * np.log10(e / float(((xf - ymx).double() ** 2).sum()))
         say(f"QSNR {name}: nvfp4 {q_nv:.3f} dB, mxfp4-ocp {q_mx:.3f} dB")
         assert q_nv > q_mx
+
+
+def test_nvfp4_fakequant_in_place():
+    x = workloads.bf16_student_t_outlier_channels(31, shape=(512, 4096)).cuda()
+    want = mx.fakequant_nvfp4(x)
+    y = x.clone()
+    got = mx.fakequant_nvfp4(y, out=y)
+    assert got.data_ptr() == y.data_ptr()
+    assert torch.equal(want.view(torch.int16), got.view(torch.int16))
