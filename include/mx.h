@@ -33,8 +33,9 @@
  *     (pointers may then be NULL); only mx_block_mse still enqueues the
  *     write of 0 to tensor_sums.
  *   - x, y, codes and scales must be 16-byte aligned (MX_ERR_ALIGN).
- *   - Outputs must not overlap inputs, except that mx_fakequant accepts
- *     y == x exactly (in place). Partial overlap is MX_ERR_ALIAS.
+ *   - Outputs must not overlap inputs, except that every fake-quant entry
+ *     point accepts y == x exactly (in place). Partial overlap is
+ *     MX_ERR_ALIAS.
  *   - On any error nothing is launched and no output is touched.
  */
 #ifndef MX_H
