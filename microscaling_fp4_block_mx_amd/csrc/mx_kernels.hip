@@ -865,8 +865,9 @@ __global__ __launch_bounds__(kThreads) void k_dequantize8(const u32x2 *__restric
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_fakequant8(const void *x, void *y, int64_t nitems) {
-  Item<BF16> xv[kU<BF16>];
-  tile_loop<kU<BF16>>(
+  constexpr int U = unroll_of(BF16, 0, kKindFakequant);  // as MXFP4 fake-quant (3 % faster)
+  Item<BF16> xv[U];
+  tile_loop<U>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t it) {
         u32x2 c;
@@ -1391,7 +1392,7 @@ hipError_t mxi_launch_dequantize8(const uint8_t *codes, const uint8_t *scales, i
 
 hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *y,
                                  hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, unroll_of(bf16, 0, kKindFakequant))), b(kThreads);
   if (bf16)
     hipLaunchKernelGGL((k_fakequant8<true>), g, b, 0, st, x, y, nitems);
   else
