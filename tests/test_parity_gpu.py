@@ -369,6 +369,44 @@ def test_deterministic():
         assert torch.equal(t1.view(torch.int64), t2.view(torch.int64))
 
 
+def test_deterministic_other_formats():
+    x = workloads.bf16_laplace_sparse_outliers(7, shape=(2048, 8192)).cuda()
+    runs = []
+    for _ in range(2):
+        runs.append([t.clone() for t in (*mx.quantize_mxfp8(x), *mx.quantize_nvfp4(x),
+                                         *mx.quantize_mbs(x), mx.fakequant_nvfp4(x),
+                                         mx.fakequant_mbs(x), mx.fakequant_mxfp8(x))])
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_concurrent_streams():
+    """Two streams at once, each with its own buffers and workspace: results
+    equal the same calls made one after another (the library keeps no
+    shared state between calls)."""
+    xa = workloads.bf16_student_t_outlier_channels(41, shape=(4096, 4096)).cuda()
+    xb = workloads.bf16_laplace_sparse_outliers(42, shape=(2048, 8192)).cuda()
+    want = []
+    for x in (xa, xb):
+        c, s = mx.quantize(x, "oas")
+        bm, sums = mx.block_mse(x, c, s)
+        want.append((c, s, bm, sums, mx.fakequant_nvfp4(x), mx.fakequant(x, "oas_nf")))
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    got = [None, None]
+    for _ in range(3):
+        for i, (x, st) in enumerate(((xa, sa), (xb, sb))):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                c, s = mx.quantize(x, "oas")
+                bm, sums = mx.block_mse(x, c, s)
+                got[i] = (c, s, bm, sums, mx.fakequant_nvfp4(x), mx.fakequant(x, "oas_nf"))
+        torch.cuda.synchronize()
+        for w, g in zip(want, got):
+            for a, b in zip(w, g):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
 def test_side_stream():
     """Work is enqueued on torch's current stream."""
     x = workloads.bf16_normal(25, (2048, 4096), std=1.0).cuda()
