@@ -61,6 +61,9 @@ EXTRA_BYTES_PER_ELEM = {
     # MBS-Static: 16-element sub-block bytes plus one macro byte per 128
     "quantize_mbs": 2 + 0.5 + 1 / 16 + 1 / 128,
     "dequantize_mbs_bf16": 0.5 + 1 / 16 + 1 / 128 + 2,
+    # one pass: codes + scales + y + block MSE + tensor sums (quantize,
+    # dequantize and block MSE of the step fused; x read once)
+    "quantize_fused": 2 + 0.5 + 1 / 32 + 2 + 4 / 32,
     # fused fake-quant of the comparators (NVFP4 reads x twice)
     "fakequant_nvfp4": 2 + 2 + 2,
     "fakequant_mbs": 2 + 2,
@@ -217,6 +220,11 @@ def main():
             st = mx.mx_dequantize_mbs(b["c_oas"].data_ptr(), b["smb"].data_ptr(),
                                       b["mmb"].data_ptr(), R_, K_, mx.MX_BF16,
                                       b["y_dq"].data_ptr(), sh)
+        elif op == "quantize_fused":
+            st = mx.mx_quantize_fused(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP,
+                                      b["c_oas"].data_ptr(), b["s_oas"].data_ptr(),
+                                      b["y_fq"].data_ptr(), b["bm"].data_ptr(), sums.data_ptr(),
+                                      ws.data_ptr(), ws_bytes, sh)
         elif op == "fakequant_nvfp4":
             st = mx.mx_fakequant_nvfp4(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["y_fq"].data_ptr(),
                                        wsnv.data_ptr(), wsnv_bytes, sh)
@@ -541,11 +549,19 @@ def suite(args, dev):
         ok(mx.mx_block_mse(b["x"].data_ptr(), mx.MX_F32, b["c"].data_ptr(), b["s"].data_ptr(),
                            R, K, b["bm"].data_ptr(), sums.data_ptr(), ws.data_ptr(), wsb, sh))
 
+    def fused1(i, sh=sh):
+        b = sets[i % len(sets)]
+        ok(mx.mx_quantize_fused(b["x"].data_ptr(), mx.MX_F32, R, K, mx.MX_SCALE_OCP,
+                                b["c"].data_ptr(), b["s"].data_ptr(), b["y"].data_ptr(),
+                                b["bm"].data_ptr(), sums.data_ptr(), ws.data_ptr(), wsb, sh))
+
     for i in range(len(sets)):
         q1(i)
     for op, fn, bpe in (("quantize_ocp_f32", q1, 4 + 0.5 + 1 / 32),
                         ("dequantize_f32", dq1, 0.5 + 1 / 32 + 4),
-                        ("block_mse_f32", mse1, 4 + 0.5 + 1 / 32 + 4 / 32)):
+                        ("block_mse_f32", mse1, 4 + 0.5 + 1 / 32 + 4 / 32),
+                        ("quantize_fused_f32 (the three above in one pass)", fused1,
+                         4 + 0.5 + 1 / 32 + 4 + 4 / 32)):
         report(W1, op, bpe * n, _launch_stats(fn, n_timed, n_warm, stream),
                cache=f"cold ({len(sets)} rotated sets)")
         report(W1, op, bpe * n, _launch_stats(lambda i, fn=fn: fn(0), n_timed, n_warm, stream),

@@ -149,6 +149,23 @@ mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype,
  * asked for tensor_sums (at most 32 KiB); 0 for an invalid shape. */
 size_t mx_block_mse_workspace_size(int64_t rows, int64_t k);
 
+/* One pass over x for the QAT / calibration loop that quantizes and then
+ * measures what it lost (the MXFP4 wiki page's example 2 quantizes, then
+ * dequantizes and reports the MSE): codes and scales as mx_quantize, plus,
+ * when the pointers are not NULL, y [rows, k] in x's dtype as
+ * mx_dequantize of those codes (= mx_fakequant), block_mse and tensor_sums
+ * as mx_block_mse of those codes. x is read once instead of three times.
+ * codes, scales, y and block_mse equal the separate calls bit for bit;
+ * tensor_sums equal them to a relative 1e-6 (the summation order of the
+ * partial sums may differ). Workspace, alignment and error conventions as
+ * mx_quantize and mx_block_mse; no written range may overlap x, another
+ * output or the workspace. */
+mx_status_t mx_quantize_fused(const void *x, mx_dtype_t x_dtype, int64_t rows,
+                              int64_t k, mx_scale_mode_t mode, uint8_t *codes,
+                              uint8_t *scales, void *y, float *block_mse,
+                              double *tensor_sums, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* ---- MXFP8 (E4M3 elements) ------------------------------------------------
  * vLLM MXFP8/MXFP4 page, "MXFP8: Block-32 scaling" section: online MXFP8
  * quantization produces FP8 values plus one uint8 scale per 32 elements of

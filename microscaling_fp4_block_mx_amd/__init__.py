@@ -39,8 +39,8 @@ EXPORTS = ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
            "mx_block_mse_workspace_size", "mx_quantize_mxfp8", "mx_dequantize_mxfp8",
            "mx_fakequant_mxfp8", "mx_nvfp4_workspace_size", "mx_quantize_nvfp4",
            "mx_dequantize_nvfp4", "mx_quantize_mbs", "mx_dequantize_mbs", "mx_quantize_multi",
-           "mx_fakequant_multi", "mx_fakequant_nvfp4", "mx_fakequant_mbs", "mx_status_string",
-           "mx_last_error_detail")
+           "mx_fakequant_multi", "mx_fakequant_nvfp4", "mx_fakequant_mbs", "mx_quantize_fused",
+           "mx_status_string", "mx_last_error_detail")
 
 _lib = None
 
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mx_dequantize_nvfp4.argtypes = [p, p, p, i64, i64, i32, p, p]
     lib.mx_quantize_mbs.argtypes = [p, i32, i64, i64, p, p, p, p]
     lib.mx_dequantize_mbs.argtypes = [p, p, p, i64, i64, i32, p, p]
+    lib.mx_quantize_fused.argtypes = [p, i32, i64, i64, i32, p, p, p, p, p, p, ctypes.c_size_t, p]
     lib.mx_fakequant_nvfp4.argtypes = [p, i32, i64, i64, p, p, ctypes.c_size_t, p]
     lib.mx_fakequant_mbs.argtypes = [p, i32, i64, i64, p, p]
     lib.mx_quantize_multi.argtypes = [p, i32, i32, i32, p]
@@ -78,7 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
               "mx_quantize_mxfp8", "mx_dequantize_mxfp8", "mx_fakequant_mxfp8",
               "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_quantize_mbs",
               "mx_dequantize_mbs", "mx_quantize_multi", "mx_fakequant_multi",
-              "mx_fakequant_nvfp4", "mx_fakequant_mbs"):
+              "mx_fakequant_nvfp4", "mx_fakequant_mbs", "mx_quantize_fused"):
         getattr(lib, f).restype = i32
     lib.mx_status_string.argtypes = [i32]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -146,6 +147,13 @@ def mx_quantize_mbs(x, x_dtype, rows, k, codes, sub_scales, macro_mant, stream) 
 
 def mx_dequantize_mbs(codes, sub_scales, macro_mant, rows, k, y_dtype, y, stream) -> int:
     return load_library().mx_dequantize_mbs(codes, sub_scales, macro_mant, rows, k, y_dtype, y,
+                                            stream)
+
+
+def mx_quantize_fused(x, x_dtype, rows, k, mode, codes, scales, y, block_mse, tensor_sums,
+                      workspace, workspace_bytes, stream) -> int:
+    return load_library().mx_quantize_fused(x, x_dtype, rows, k, mode, codes, scales, y,
+                                            block_mse, tensor_sums, workspace, workspace_bytes,
                                             stream)
 
 
@@ -305,6 +313,30 @@ def block_mse(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                             rows, k, bm.data_ptr() if bm is not None else None,
                             sums.data_ptr(), ws.data_ptr(), ws_bytes, _stream(x.device)))
     return bm, sums
+
+
+def quantize_fused(x: torch.Tensor, mode: str = "ocp", want_y: bool = True,
+                   want_block_mse: bool = True, want_sums: bool = True):
+    """One pass: -> (codes, scales, y or None, block_mse or None, sums or
+    None), equal to quantize(), then dequantize() in x's dtype, then
+    block_mse() (sums to a relative 1e-6)."""
+    rows, k = _check_input(x)
+    lead = tuple(x.shape[:-1])
+    codes = torch.empty(lead + (k // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(lead + (k // BLOCK,), dtype=torch.uint8, device=x.device)
+    y = torch.empty_like(x) if want_y else None
+    bm = (torch.empty(lead + (k // BLOCK,), dtype=torch.float32, device=x.device)
+          if want_block_mse else None)
+    sums = torch.empty(2, dtype=torch.float64, device=x.device) if want_sums else None
+    ws_bytes = mx_block_mse_workspace_size(rows, k) if want_sums else 0
+    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=x.device)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    with torch.cuda.device(x.device):
+        _raise(mx_quantize_fused(x.data_ptr(), _DTYPES[x.dtype], rows, k, _mode(mode),
+                                 codes.data_ptr(), scales.data_ptr(), ptr(y), ptr(bm), ptr(sums),
+                                 ws.data_ptr() if want_sums else None, ws_bytes,
+                                 _stream(x.device)))
+    return codes, scales, y, bm, sums
 
 
 # ---- MXFP8 (E4M3) tensor helpers ---------------------------------------------

@@ -151,6 +151,53 @@ mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype, const uint8_t *codes
                                      static_cast<hipStream_t>(stream)));
 }
 
+mx_status_t mx_quantize_fused(const void *x, mx_dtype_t x_dtype, int64_t rows, int64_t k,
+                              mx_scale_mode_t mode, uint8_t *codes, uint8_t *scales, void *y,
+                              float *block_mse, double *tensor_sums, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;
+  if (!mode_ok(mode)) return MX_ERR_MODE;
+  if (mx_status_t s = check_shape(rows, k)) return s;
+  if (tensor_sums) {
+    if ((reinterpret_cast<uintptr_t>(tensor_sums) & 7u) != 0) return MX_ERR_ALIGN;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0 ||
+        workspace_bytes < mx_block_mse_workspace_size(rows, k))
+      return MX_ERR_WORKSPACE;
+  }
+  if (rows == 0) {
+    if (!tensor_sums) return MX_OK;
+    if (overlap(tensor_sums, 16, workspace, (int64_t)workspace_bytes)) return MX_ERR_ALIAS;
+    return finish(mxi_launch_quantize_fused(nullptr, 0, 0, 0, nullptr, nullptr, nullptr, nullptr,
+                                            tensor_sums, static_cast<double *>(workspace),
+                                            static_cast<hipStream_t>(stream)));
+  }
+  if (!x || !codes || !scales) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || (y && !aligned16(y)))
+    return MX_ERR_ALIGN;
+  if (block_mse && (reinterpret_cast<uintptr_t>(block_mse) & 3u) != 0) return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  const int64_t nx = n * elem_bytes(x_dtype);
+  // every written range against x and against each other
+  struct R {
+    const void *p;
+    int64_t n;
+  } out[5] = {{codes, n / 2}, {scales, n / kBlock}, {y, nx}, {block_mse, 4 * (n / kBlock)},
+              {tensor_sums, 16}};
+  for (int i = 0; i < 5; i++) {
+    if (!out[i].p) continue;
+    if (overlap(out[i].p, out[i].n, x, nx)) return MX_ERR_ALIAS;
+    if (tensor_sums && overlap(out[i].p, out[i].n, workspace, (int64_t)workspace_bytes))
+      return MX_ERR_ALIAS;
+    for (int j = i + 1; j < 5; j++)
+      if (out[j].p && overlap(out[i].p, out[i].n, out[j].p, out[j].n)) return MX_ERR_ALIAS;
+  }
+  if (tensor_sums && overlap(workspace, (int64_t)workspace_bytes, x, nx)) return MX_ERR_ALIAS;
+  return finish(mxi_launch_quantize_fused(x, x_dtype == MX_BF16, mode, n / 8, codes, scales, y,
+                                          block_mse, tensor_sums,
+                                          tensor_sums ? static_cast<double *>(workspace) : nullptr,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 mx_status_t mx_quantize_mxfp8(const void *x, mx_dtype_t x_dtype, int64_t rows, int64_t k,
                               uint8_t *codes, uint8_t *scales, void *stream) {
   if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;

@@ -19,6 +19,11 @@ size_t mxi_block_mse_partials(int64_t nitems);
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                                 const uint8_t *scales, int64_t nitems, float *block_mse,
                                 double *tensor_sums, double *partial, hipStream_t st);
+// Quantize plus, optionally, y (x's dtype), block MSE and tensor sums in
+// one pass; partial sums as mxi_launch_block_mse (same count).
+hipError_t mxi_launch_quantize_fused(const void *x, int bf16, int mode, int64_t nitems,
+                                     uint8_t *codes, uint8_t *scales, void *y, float *block_mse,
+                                     double *tensor_sums, double *partial, hipStream_t st);
 // MXFP8 (E4M3): codes are one byte per element.
 hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                 uint8_t *scales, hipStream_t st);

@@ -593,6 +593,60 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restr
 // workgroup writes its two sums to partial[2 * blockIdx.x + {0, 1}] (lane
 // sums, then a butterfly over the wave, then the waves in order), and
 // k_sum_partials adds the partials.
+// Block error of one item against (c, s): the fp64 SSE of the quad's block,
+// summed in a fixed order (per lane, then quad_sum_f64), written as
+// block_mse[block] = SSE / 32 by the quad's lane 0 when block_mse is set;
+// lane 0 also adds the SSE to `mine`, and every lane adds its sum of x^2 to
+// `mine_sq` (tensor sums).
+template <bool BF16, bool SUMS>
+__device__ __forceinline__ void mse_item(const Item<BF16> &x, uint32_t c, uint32_t s, int64_t it,
+                                         float *__restrict__ block_mse, double &mine,
+                                         double &mine_sq) {
+  float q[8];
+  decode_f32(c, s, q);
+  double acc = 0.0, acc_sq = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const double xi = (double)elem<BF16>(x, i);
+    const double d = xi - (double)q[i];
+    acc = __builtin_fma(d, d, acc);
+    if constexpr (SUMS) acc_sq = __builtin_fma(xi, xi, acc_sq);
+  }
+  if constexpr (SUMS) {
+    // materialize here, so the eight widened x values die now instead
+    // of living across the quad sum (keeps the kernel at full occupancy)
+    __asm__ volatile("" : "+v"(acc_sq));
+    mine_sq += acc_sq;
+  }
+  const double sse = quad_sum_f64(acc);
+  if ((threadIdx.x & 3) == 0) {
+    if (block_mse) st<false>(block_mse + (it >> 2), (float)(sse * (1.0 / 32.0)));
+    if constexpr (SUMS) mine += sse;
+  }
+}
+
+// The workgroup's two tensor sums, in a fixed order (butterfly over each
+// wave, then the waves in turn), to partial[2 * blockIdx.x + {0, 1}].
+__device__ __forceinline__ void write_partials(double mine, double mine_sq,
+                                               double *__restrict__ partial) {
+  __shared__ double wave_part[2][kThreads / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mine += __shfl_xor(mine, off, 64);
+    mine_sq += __shfl_xor(mine_sq, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    wave_part[0][threadIdx.x >> 6] = mine;
+    wave_part[1][threadIdx.x >> 6] = mine_sq;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    double t = 0.0;
+    for (int w = 0; w < kThreads / 64; w++) t += wave_part[threadIdx.x][w];
+    partial[2 * blockIdx.x + threadIdx.x] = t;
+  }
+}
+
 template <bool BF16, bool SUMS>
 __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__ x,
                                                         const uint32_t *__restrict__ codes,
@@ -600,7 +654,6 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
                                                         float *__restrict__ block_mse,
                                                         double *__restrict__ partial,
                                                         int64_t nitems) {
-  __shared__ double wave_part[2][kThreads / 64];
   double mine = 0.0;     // sum of the block SSEs this lane reports (q == 0 lanes)
   double mine_sq = 0.0;  // sum of x^2 over this lane's elements
   Item<BF16> xv[kUnroll];
@@ -613,45 +666,46 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
         sb[u] = ld<false>(scales + (it >> 2));
       },
       [&](int u, int64_t it) {
-        float q[8];
-        decode_f32(cw[u], sb[u], q);
-        double acc = 0.0, acc_sq = 0.0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-          const double xi = (double)elem<BF16>(xv[u], i);
-          const double d = xi - (double)q[i];
-          acc = __builtin_fma(d, d, acc);
-          if constexpr (SUMS) acc_sq = __builtin_fma(xi, xi, acc_sq);
-        }
-        if constexpr (SUMS) {
-          // materialize here, so the eight widened x values die now instead
-          // of living across the quad sum (keeps the kernel at full occupancy)
-          __asm__ volatile("" : "+v"(acc_sq));
-          mine_sq += acc_sq;
-        }
-        const double sse = quad_sum_f64(acc);
-        if ((threadIdx.x & 3) == 0) {
-          if (block_mse) st<false>(block_mse + (it >> 2), (float)(sse * (1.0 / 32.0)));
-          if constexpr (SUMS) mine += sse;
-        }
+        mse_item<BF16, SUMS>(xv[u], cw[u], sb[u], it, block_mse, mine, mine_sq);
       });
-  if constexpr (SUMS) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      mine += __shfl_xor(mine, off, 64);
-      mine_sq += __shfl_xor(mine_sq, off, 64);
-    }
-    if ((threadIdx.x & 63) == 0) {
-      wave_part[0][threadIdx.x >> 6] = mine;
-      wave_part[1][threadIdx.x >> 6] = mine_sq;
-    }
-    __syncthreads();
-    if (threadIdx.x < 2) {
-      double t = 0.0;
-      for (int w = 0; w < kThreads / 64; w++) t += wave_part[threadIdx.x][w];
-      partial[2 * blockIdx.x + threadIdx.x] = t;
-    }
-  }
+  if constexpr (SUMS) write_partials(mine, mine_sq, partial);
+}
+
+// One pass: quantize, and optionally the dequantized tensor y (x's dtype)
+// and the block / tensor error of the new codes, all from the x already in
+// registers. Same item code as k_quantize, k_fakequant and k_block_mse, so
+// the outputs equal those three calls in sequence (the tensor sums up to
+// their summation order: this launch's grid is the block-MSE grid).
+template <bool BF16, int MODE, bool SUMS>
+__global__ __launch_bounds__(kThreads) void k_quantize_fused(const void *__restrict__ x,
+                                                             uint32_t *__restrict__ codes,
+                                                             uint8_t *__restrict__ scales,
+                                                             void *__restrict__ y,
+                                                             float *__restrict__ block_mse,
+                                                             double *__restrict__ partial,
+                                                             int64_t nitems) {
+  double mine = 0.0, mine_sq = 0.0;
+  const bool err = block_mse != nullptr || SUMS;
+  // (the grid is the block-MSE grid, sized with kUnroll items per thread;
+  // the grid stride makes any per-thread count correct, and fp32 items take
+  // two per thread here as in the streaming kernels)
+  constexpr int U = kU<BF16>;
+  Item<BF16> xv[U];
+  tile_loop<U>(
+      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t it) {
+        uint32_t c;
+        const uint32_t s = quantize_item<BF16, MODE>(xv[u], c);
+        st<false>(codes + it, c);
+        if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)s);
+        if (y) {  // uniform
+          uint32_t out[BF16 ? 4 : 8];
+          decode_item<BF16>(c, s, out);
+          store_item<BF16>(y, it, out);
+        }
+        if (err) mse_item<BF16, SUMS>(xv[u], c, s, it, block_mse, mine, mine_sq);
+      });
+  if constexpr (SUMS) write_partials(mine, mine_sq, partial);
 }
 
 #ifndef MX_MSE_GRID_CAP
@@ -1510,6 +1564,51 @@ hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, i
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+#define MX_DISPATCH_FUSED(BF16, SUMS, MODE, G, B, ST, ...)                                 \
+  switch (MODE) {                                                                          \
+    case MX_SCALE_OAS:                                                                     \
+      hipLaunchKernelGGL((k_quantize_fused<BF16, MX_SCALE_OAS, SUMS>), G, B, 0, ST, __VA_ARGS__); \
+      break;                                                                               \
+    case MX_SCALE_OAS_BITS:                                                                \
+      hipLaunchKernelGGL((k_quantize_fused<BF16, MX_SCALE_OAS_BITS, SUMS>), G, B, 0, ST,   \
+                         __VA_ARGS__);                                                     \
+      break;                                                                               \
+    case MX_SCALE_OAS_NF:                                                                  \
+      hipLaunchKernelGGL((k_quantize_fused<BF16, MX_SCALE_OAS_NF, SUMS>), G, B, 0, ST,     \
+                         __VA_ARGS__);                                                     \
+      break;                                                                               \
+    default:                                                                               \
+      hipLaunchKernelGGL((k_quantize_fused<BF16, MX_SCALE_OCP, SUMS>), G, B, 0, ST, __VA_ARGS__); \
+      break;                                                                               \
+  }
+
+hipError_t mxi_launch_quantize_fused(const void *x, int bf16, int mode, int64_t nitems,
+                                     uint8_t *codes, uint8_t *scales, void *y, float *block_mse,
+                                     double *tensor_sums, double *partial, hipStream_t st) {
+  // the block-MSE grid, so the partial sums fit mx_block_mse_workspace_size
+  const unsigned grid = grid_for(nitems, MX_MSE_GRID_CAP);
+  uint32_t *c = reinterpret_cast<uint32_t *>(codes);
+  double *part = tensor_sums ? partial : nullptr;
+  if (nitems > 0) {
+    const dim3 g(grid), b(kThreads);
+    if (bf16) {
+      if (part) { MX_DISPATCH_FUSED(true, true, mode, g, b, st, x, c, scales, y, block_mse, part, nitems) }
+      else { MX_DISPATCH_FUSED(true, false, mode, g, b, st, x, c, scales, y, block_mse, part, nitems) }
+    } else {
+      if (part) { MX_DISPATCH_FUSED(false, true, mode, g, b, st, x, c, scales, y, block_mse, part, nitems) }
+      else { MX_DISPATCH_FUSED(false, false, mode, g, b, st, x, c, scales, y, block_mse, part, nitems) }
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (tensor_sums) {
+    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kThreads), 0, st, partial,
+                       nitems > 0 ? (int)grid : 0, tensor_sums);
+    return hipGetLastError();
   }
   return hipSuccess;
 }

@@ -54,6 +54,27 @@ static void mxfp4() {
                              (float *)P(Y), (double *)P(Ts), P(Ws), wsb, nullptr),
                 "block_mse", 1000 * 4096 / 8, n0);
   CHECK(g_last.p[4] == P(Ts) && g_last.p[5] == P(Ws));
+  n0 = g_calls;
+  expect_launch(mx_quantize_fused(P(X), MX_BF16, 1000, 4096, MX_SCALE_OAS, (uint8_t *)P(Cd),
+                                  (uint8_t *)P(Sc), P(Y), (float *)P(Ws + (1u << 24)),
+                                  (double *)P(Ts), P(Ws), wsb, nullptr),
+                "quantize_fused_y", 1000 * 4096 / 8, n0);
+  CHECK(g_last.mode == MX_SCALE_OAS && g_last.p[4] == P(Ts) && g_last.p[5] == P(Ws));
+  n0 = g_calls;
+  expect_launch(mx_quantize_fused(P(X), MX_F32, 4, 64, MX_SCALE_OCP, (uint8_t *)P(Cd),
+                                  (uint8_t *)P(Sc), nullptr, nullptr, nullptr, nullptr, 0, nullptr),
+                "quantize_fused", 32, n0);
+  CHECK(g_last.p[5] == nullptr);
+  n0 = g_calls;
+  CHECK(mx_quantize_fused(P(X), MX_BF16, 4, 64, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc),
+                          P(Cd + 64), nullptr, nullptr, nullptr, 0, nullptr) == MX_ERR_ALIAS);
+  CHECK(mx_quantize_fused(P(X), MX_BF16, 4, 64, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc),
+                          P(Y), nullptr, (double *)P(Ts), P(Ws), 8, nullptr) == MX_ERR_WORKSPACE);
+  CHECK(mx_quantize_fused(P(X), MX_BF16, 4, 64, MX_SCALE_OCP, (uint8_t *)P(Cd), (uint8_t *)P(Sc),
+                          P(Y), (float *)P(Y + 32), nullptr, nullptr, 0, nullptr) == MX_ERR_ALIAS);
+  CHECK(mx_quantize_fused(P(X), MX_BF16, 4, 64, (mx_scale_mode_t)9, (uint8_t *)P(Cd),
+                          (uint8_t *)P(Sc), nullptr, nullptr, nullptr, nullptr, 0, nullptr) == MX_ERR_MODE);
+  CHECK(g_calls == n0);
   // rows == 0: nothing launched, except block_mse's zero write of the sums
   n0 = g_calls;
   CHECK(mx_quantize(nullptr, MX_BF16, 0, 32, MX_SCALE_OCP, nullptr, nullptr, nullptr) == MX_OK);

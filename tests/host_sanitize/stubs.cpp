@@ -47,6 +47,13 @@ hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *c, const
   g_last.p[5] = part;
   return rec("block_mse", n, bf16, -1, x, c, s, bm);
 }
+hipError_t mxi_launch_quantize_fused(const void *x, int bf16, int mode, int64_t n, uint8_t *c,
+                                     uint8_t *s, void *y, float *bm, double *sums, double *part,
+                                     hipStream_t) {
+  g_last.p[4] = sums;
+  g_last.p[5] = part;
+  return rec(y ? "quantize_fused_y" : "quantize_fused", n, bf16, mode, x, c, s, bm);
+}
 hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t n, uint8_t *c, uint8_t *s,
                                 hipStream_t) {
   return rec("quantize8", n, bf16, -1, x, c, s, nullptr);

@@ -1,0 +1,86 @@
+"""GPU parity of mx_quantize_fused (one pass: codes, scales, y, block MSE,
+tensor sums) with the separate calls and with the oracle: codes, scales, y
+and block MSE bit for bit, tensor sums to a relative 1e-6, in every scale
+mode, both dtypes, ragged shapes, with each optional output on or off."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import microscaling_fp4_block_mx_amd as mx
+from test_parity_gpu import assert_same_bits, host_view, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mx.load_library()
+    oracle.build(force=not os.path.exists(os.path.join(os.path.dirname(oracle.__file__),
+                                                       "libmxref.so")))
+    yield
+    torch.cuda.synchronize()
+
+
+def check_fused(x: torch.Tensor, mode: str, label: str):
+    xd = x.cuda()
+    say(f"{label} fused {mode} {tuple(x.shape)} {x.dtype}")
+    c, s, y, bm, sums = mx.quantize_fused(xd, mode)
+    c1, s1 = mx.quantize(xd, mode)
+    y1 = mx.dequantize(c1, s1, xd.dtype)
+    bm1, sums1 = mx.block_mse(xd, c1, s1)
+    assert torch.equal(c, c1) and torch.equal(s, s1), f"{label}: codes/scales differ from quantize"
+    assert torch.equal(y.view(torch.uint8), y1.view(torch.uint8)), f"{label}: y differs"
+    assert torch.equal(bm.view(torch.int32), bm1.view(torch.int32)), f"{label}: block MSE differs"
+    a, b = sums.tolist(), sums1.tolist()
+    for u, v in zip(a, b):
+        assert u == v or abs(u - v) <= 1e-6 * abs(v), f"{label}: sums {a} vs {b}"
+    # and the oracle
+    xh = host_view(x)
+    wc, ws = oracle.quantize(xh, mode)
+    assert_same_bits(c, wc, f"{label} codes")
+    assert_same_bits(s, ws, f"{label} scales")
+    assert_same_bits(y, oracle.fakequant(xh, mode), f"{label} y")
+    wbm, wsse, wssq = oracle.block_mse(xh, wc, ws, with_energy=True)
+    assert np.allclose(bm.cpu().numpy(), wbm, rtol=1e-6, atol=0, equal_nan=True)
+    for got, want in zip(a, (wsse, wssq)):
+        assert got == want or abs(got - want) <= 1e-6 * abs(want)
+
+
+@pytest.mark.parametrize("mode", mx.MODES)
+def test_fused_ragged(mode):
+    rng = np.random.default_rng(61 + mx.MODES.index(mode))
+    for rows, k in ((1, 32), (3, 96), (257, 160), (1000, 4096), (4099, 64)):
+        x = rng.standard_t(3, (rows, k)) * np.exp(rng.normal(0, 2, (rows, k // 32))).repeat(32, 1)
+        xt = torch.from_numpy(x.astype(np.float32))
+        check_fused(xt, mode, f"f32 {rows}x{k}")
+        check_fused(xt.to(torch.bfloat16), mode, f"bf16 {rows}x{k}")
+
+
+def test_fused_bench_tensor_and_fp32_config():
+    check_fused(workloads.bf16_student_t_outlier_channels(2), "oas", "student-t 8192x4096")
+    check_fused(workloads.fp32_normal(1), "ocp", "fp32 normal 1024x4096")
+
+
+def test_fused_optional_outputs():
+    x = workloads.bf16_student_t_outlier_channels(62, shape=(512, 4096)).cuda()
+    c, s, y, bm, sums = mx.quantize_fused(x, "ocp")
+    for wy, wb, wsum in ((False, False, False), (True, False, False), (False, True, False),
+                         (False, False, True), (False, True, True)):
+        c2, s2, y2, bm2, sums2 = mx.quantize_fused(x, "ocp", wy, wb, wsum)
+        assert torch.equal(c2, c) and torch.equal(s2, s)
+        assert (y2 is None) != wy and (bm2 is None) != wb and (sums2 is None) != wsum
+        if wy:
+            assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
+        if wb:
+            assert torch.equal(bm2.view(torch.int32), bm.view(torch.int32))
+        if wsum:
+            assert torch.equal(sums2.view(torch.int64), sums.view(torch.int64))
+    # empty tensor: sums written as zeros
+    _, _, _, _, z = mx.quantize_fused(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"))
+    assert z.tolist() == [0.0, 0.0]
