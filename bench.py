@@ -732,6 +732,9 @@ def suite(args, dev):
     del w13, w2, cs, ss, ys
     torch.cuda.empty_cache()
 
+    quality = suite_quality(dev)
+    results.extend(quality)
+
     # markdown summary
     print("\n| workload | op | cache | bytes | median us | p10 | p90 | back-to-back us "
           "| GB/s (median) | % of 8 TB/s |")
@@ -742,8 +745,103 @@ def suite(args, dev):
                   f"{r['median_us']} | {r['p10_us']} | {r['p90_us']} | {r['back_to_back_us']} | "
                   f"{r['GB/s']} | {100 * r['frac_hbm']:.1f} |")
     for r in results:
-        if "median_us" not in r:
+        if "median_us" not in r and r.get("op") != "qsnr_db":
             print("- " + json.dumps(r))
+    fmts = list(quality[0]["qsnr_db"])
+    print("\nQSNR dB = 10 log10(sum x^2 / sum (x - x_hat)^2) over the whole workload:\n")
+    print("| workload | " + " | ".join(fmts) + " |")
+    print("|---|" + "---|" * len(fmts))
+    for r in quality:
+        print(f"| {r['workload']} | " + " | ".join(f"{r['qsnr_db'][f]:.2f}" for f in fmts) + " |")
+
+
+QUALITY_FORMATS = ("mxfp4_ocp", "mxfp4_oas", "mxfp4_oas_bits", "mxfp4_oas_nf", "mxfp8",
+                   "nvfp4", "mbs_static")
+
+
+def suite_quality(dev, chunk_elems: int = 1 << 27):
+    """QSNR of every format and MXFP4 scale mode on each workload, from the
+    library's outputs (bit-identical to the oracle's by the parity tests).
+    MXFP4 error sums come from the one-pass call; the other formats are
+    fake-quantized and differenced in fp64. Block formats are row-local, so
+    big tensors go through in row chunks; NVFP4's per-tensor factor is taken
+    per weight matrix (per expert for MoE) and per activation tensor."""
+    import numpy as np
+    import torch
+
+    import microscaling_fp4_block_mx_amd as mx
+    import workloads
+
+    mx.load_library()
+
+    def sums_rowwise(x2, acc):
+        rows_per = max(1, chunk_elems // x2.shape[1])
+        for r0 in range(0, x2.shape[0], rows_per):
+            xc = x2[r0:r0 + rows_per]
+            xd = xc.double()
+            ssq = float((xd * xd).sum())
+            for mode in mx.MODES:
+                _, _, _, _, sums = mx.quantize_fused(xc, mode, want_y=False,
+                                                     want_block_mse=False, want_sums=True)
+                acc["mxfp4_" + mode][0] += float(sums[0])
+                acc["mxfp4_" + mode][1] += float(sums[1])
+            for name, fq in (("mxfp8", mx.fakequant_mxfp8), ("mbs_static", mx.fakequant_mbs)):
+                d = fq(xc).double() - xd
+                acc[name][0] += float((d * d).sum())
+                acc[name][1] += ssq
+            del xd
+
+    def sums_nvfp4(x2, acc):
+        d = mx.fakequant_nvfp4(x2).double() - x2.double()
+        acc["nvfp4"][0] += float((d * d).sum())
+        acc["nvfp4"][1] += float((x2.double() ** 2).sum())
+
+    rows = []
+
+    def finish(name, acc):
+        q = {f: round(10 * np.log10(acc[f][1] / acc[f][0]), 2) for f in QUALITY_FORMATS}
+        row = {"workload": name, "op": "qsnr_db", "qsnr_db": q}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+
+    new = lambda: {f: [0.0, 0.0] for f in QUALITY_FORMATS}  # noqa: E731
+    for name, x in (("C1 fp32 N(0,1) [1024, 4096]", workloads.fp32_normal(1)),
+                    ("C2 bf16 Student-t(3) + 20 outlier channels [8192, 4096]",
+                     workloads.bf16_student_t_outlier_channels(2)),
+                    ("C5 bf16 Laplace + 0.1% outliers [16384, 8192]",
+                     workloads.bf16_laplace_sparse_outliers(5))):
+        x = x.to(dev)
+        acc = new()
+        sums_rowwise(x, acc)
+        sums_nvfp4(x, acc)
+        finish(name, acc)
+        del x
+    a, b = workloads.llama32_3b_grouped(dev)
+    acc = new()
+    sums_rowwise(a, acc)
+    sums_rowwise(b, acc)
+    ra = rb = 0
+    for layer in range(workloads.LLAMA32_3B_LAYERS):
+        for _, out_f, in_f in workloads.LLAMA32_3B_LINEARS:
+            if in_f == 8192:
+                sums_nvfp4(b[rb:rb + out_f], acc)
+                rb += out_f
+            else:
+                sums_nvfp4(a[ra:ra + out_f], acc)
+                ra += out_f
+    finish("C3 Llama-3.2-3B linears x28, bf16 N(0,0.02)", acc)
+    del a, b
+    torch.cuda.empty_cache()
+    w13, w2 = workloads.moe_weights(dev)
+    acc = new()
+    for w in (w13, w2):
+        sums_rowwise(w.reshape(-1, w.shape[-1]), acc)
+        for e in range(w.shape[0]):
+            sums_nvfp4(w[e], acc)
+    finish("C4 MoE w13 + w2, 128 experts, bf16 N(0,0.02)", acc)
+    del w13, w2
+    torch.cuda.empty_cache()
+    return rows
 
 
 if __name__ == "__main__":
