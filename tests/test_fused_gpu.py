@@ -84,3 +84,39 @@ def test_fused_optional_outputs():
     # empty tensor: sums written as zeros
     _, _, _, _, z = mx.quantize_fused(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"))
     assert z.tolist() == [0.0, 0.0]
+
+
+def test_fused_past_2_31_elements():
+    """One bf16 tensor of 2^31 + 2^20 elements in OAS mode: every output
+    against the separate calls in full, and against the oracle on sampled
+    rows including the last ones (64-bit indexing in the one-pass kernel)."""
+    rows, k = (1 << 31) // 4096 + 256, 4096
+    say(f"fused big tensor [{rows}, {k}]")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(93)
+    x = torch.empty((rows, k), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, 65536):
+        r1 = min(rows, r0 + 65536)
+        x[r0:r1] = (torch.randn((r1 - r0, k), generator=g, device="cuda") * 3).to(torch.bfloat16)
+    c, s, y, bm, sums = mx.quantize_fused(x, "oas")
+    c1, s1 = mx.quantize(x, "oas")
+    assert torch.equal(c, c1) and torch.equal(s, s1)
+    del c1, s1
+    y1 = mx.dequantize(c, s, torch.bfloat16)
+    assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+    del y1
+    bm1, sums1 = mx.block_mse(x, c, s)
+    assert torch.equal(bm.view(torch.int32), bm1.view(torch.int32))
+    for u, v in zip(sums.tolist(), sums1.tolist()):
+        assert abs(u - v) <= 1e-6 * abs(v)
+    del bm1
+    pick = np.unique(np.concatenate([np.arange(4), np.random.default_rng(94).choice(rows, 60, replace=False),
+                                     np.arange(rows - 4, rows)]))
+    idx = torch.from_numpy(pick).cuda()
+    xs = host_view(x.index_select(0, idx))
+    wc, ws = oracle.quantize(xs, "oas")
+    assert_same_bits(c.index_select(0, idx), wc, "fused codes (sampled rows)")
+    assert_same_bits(s.index_select(0, idx), ws, "fused scales (sampled rows)")
+    assert_same_bits(y.index_select(0, idx), oracle.fakequant(xs, "oas"), "fused y (sampled rows)")
+    wbm, _, _ = oracle.block_mse(xs, wc, ws, with_energy=True)
+    assert np.allclose(bm.index_select(0, idx).cpu().numpy(), wbm, rtol=1e-6, atol=0)
