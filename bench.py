@@ -127,8 +127,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; every MX block is independent, "
-              "so the path shards by rows with no exchange (see DESIGN.md). "
+        print("bench.py: this benchmark measures one GPU only; every MX block is independent, "
+              "so the path shards by rows with no exchange. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
