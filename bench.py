@@ -805,10 +805,10 @@ def suite_quality(dev, chunk_elems: int = 1 << 27):
         print(json.dumps(row), flush=True)
 
     new = lambda: {f: [0.0, 0.0] for f in QUALITY_FORMATS}  # noqa: E731
-    for name, x in (("C1 fp32 N(0,1) [1024, 4096]", workloads.fp32_normal(1)),
-                    ("C2 bf16 Student-t(3) + 20 outlier channels [8192, 4096]",
+    for name, x in (("fp32 N(0,1) [1024, 4096]", workloads.fp32_normal(1)),
+                    ("bf16 Student-t(3) + 20 outlier channels [8192, 4096]",
                      workloads.bf16_student_t_outlier_channels(2)),
-                    ("C5 bf16 Laplace + 0.1% outliers [16384, 8192]",
+                    ("bf16 Laplace + 0.1% outliers [16384, 8192]",
                      workloads.bf16_laplace_sparse_outliers(5))):
         x = x.to(dev)
         acc = new()
@@ -829,7 +829,7 @@ def suite_quality(dev, chunk_elems: int = 1 << 27):
             else:
                 sums_nvfp4(a[ra:ra + out_f], acc)
                 ra += out_f
-    finish("C3 Llama-3.2-3B linears x28, bf16 N(0,0.02)", acc)
+    finish("Llama-3.2-3B linears x28, bf16 N(0,0.02)", acc)
     del a, b
     torch.cuda.empty_cache()
     w13, w2 = workloads.moe_weights(dev)
@@ -838,7 +838,7 @@ def suite_quality(dev, chunk_elems: int = 1 << 27):
         sums_rowwise(w.reshape(-1, w.shape[-1]), acc)
         for e in range(w.shape[0]):
             sums_nvfp4(w[e], acc)
-    finish("C4 MoE w13 + w2, 128 experts, bf16 N(0,0.02)", acc)
+    finish("MoE w13 + w2, 128 experts, bf16 N(0,0.02)", acc)
     del w13, w2
     torch.cuda.empty_cache()
     return rows
