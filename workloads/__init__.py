@@ -33,12 +33,12 @@ import torch
 
 # ---- shapes ----------------------------------------------------------------
 
-C1_SHAPE = (1024, 4096)
-C2_SHAPE = (8192, 4096)
-C5_SHAPE = (16384, 8192)
-C2_OUTLIER_CHANNELS = 20
-C2_OUTLIER_GAIN = 50.0
-C5_OUTLIER_COUNT = 134218  # round(0.001 * 16384 * 8192)
+FP32_NORMAL_SHAPE = (1024, 4096)
+STUDENT_T_SHAPE = (8192, 4096)
+LAPLACE_SHAPE = (16384, 8192)
+STUDENT_T_OUTLIER_CHANNELS = 20
+STUDENT_T_OUTLIER_GAIN = 50.0
+LAPLACE_OUTLIER_COUNT = 134218  # round(0.001 * 16384 * 8192)
 
 LLAMA32_3B_LAYERS = 28
 # (name, out_features, in_features); quantization runs along in_features
@@ -67,14 +67,14 @@ def _bf16(a: np.ndarray) -> torch.Tensor:
 
 # ---- host-generated workloads ---------------------------------------------
 
-def fp32_normal(seed: int = 1, shape=C1_SHAPE) -> torch.Tensor:
+def fp32_normal(seed: int = 1, shape=FP32_NORMAL_SHAPE) -> torch.Tensor:
     rng = np.random.default_rng(seed)
     return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32))
 
 
-def bf16_student_t_outlier_channels(seed: int = 2, shape=C2_SHAPE,
-                                    n_channels: int = C2_OUTLIER_CHANNELS,
-                                    gain: float = C2_OUTLIER_GAIN) -> torch.Tensor:
+def bf16_student_t_outlier_channels(seed: int = 2, shape=STUDENT_T_SHAPE,
+                                    n_channels: int = STUDENT_T_OUTLIER_CHANNELS,
+                                    gain: float = STUDENT_T_OUTLIER_GAIN) -> torch.Tensor:
     rng = np.random.default_rng(seed)
     body = rng.standard_t(3.0, size=shape).astype(np.float32)
     chans = rng.choice(shape[-1], n_channels, replace=False)
@@ -82,7 +82,7 @@ def bf16_student_t_outlier_channels(seed: int = 2, shape=C2_SHAPE,
     return _bf16(body)
 
 
-def bf16_laplace_sparse_outliers(seed: int = 5, shape=C5_SHAPE,
+def bf16_laplace_sparse_outliers(seed: int = 5, shape=LAPLACE_SHAPE,
                                  n_outliers: int | None = None) -> torch.Tensor:
     rng = np.random.default_rng(seed)
     n = int(np.prod(shape))
