@@ -27,6 +27,14 @@ def _setup():
     torch.cuda.synchronize()
 
 
+def same_sum(got: float, want: float) -> bool:
+    """Tensor sums agree: both NaN, equal (infinities included), or within a
+    relative 1e-6."""
+    if np.isnan(want) or np.isnan(got):
+        return bool(np.isnan(want) and np.isnan(got))
+    return got == want or abs(got - want) <= 1e-6 * abs(want)
+
+
 def check_fused(x: torch.Tensor, mode: str, label: str):
     xd = x.cuda()
     say(f"{label} fused {mode} {tuple(x.shape)} {x.dtype}")
@@ -39,7 +47,7 @@ def check_fused(x: torch.Tensor, mode: str, label: str):
     assert torch.equal(bm.view(torch.int32), bm1.view(torch.int32)), f"{label}: block MSE differs"
     a, b = sums.tolist(), sums1.tolist()
     for u, v in zip(a, b):
-        assert u == v or abs(u - v) <= 1e-6 * abs(v), f"{label}: sums {a} vs {b}"
+        assert same_sum(u, v), f"{label}: sums {a} vs {b}"
     # and the oracle
     xh = host_view(x)
     wc, ws = oracle.quantize(xh, mode)
@@ -49,7 +57,7 @@ def check_fused(x: torch.Tensor, mode: str, label: str):
     wbm, wsse, wssq = oracle.block_mse(xh, wc, ws, with_energy=True)
     assert np.allclose(bm.cpu().numpy(), wbm, rtol=1e-6, atol=0, equal_nan=True)
     for got, want in zip(a, (wsse, wssq)):
-        assert got == want or abs(got - want) <= 1e-6 * abs(want)
+        assert same_sum(got, want), f"{label}: sums {a} vs oracle {(wsse, wssq)}"
 
 
 @pytest.mark.parametrize("mode", mx.MODES)
