@@ -63,11 +63,16 @@ constexpr uint32_t kNaN16x2 = 0x7FC07FC0u;
 // ---- cross-lane helpers (quad = 4 adjacent lanes) --------------------------
 
 // quad_perm [1,0,3,2] and [2,3,0,1]: exchange with lane^1 and lane^2.
+// bound_ctrl is set on every DPP move here: the source lane always lies in
+// the same quad (or 16-lane row), and quads and rows enter and leave the
+// ragged tail whole, so no lane reads a missing or inactive one and the
+// flag changes no result; it lets the compiler fold the move into the ALU
+// op that uses it (one DPP op instead of a move, a wait state and the op).
 __device__ __forceinline__ uint32_t dpp_x1(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
 }
 __device__ __forceinline__ uint32_t dpp_x2(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
@@ -1141,10 +1146,10 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_nv(const uint32_t *__re
 
 // rotate right by 4 / 8 lanes within each row of 16
 __device__ __forceinline__ uint32_t dpp_ror4(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true);
 }
 __device__ __forceinline__ uint32_t dpp_ror8(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);
 }
 // Decoded values of one item: E2M1 * 2^(s-127) * (1 + m/256), exact in fp32
 // (at most 2 + 9 significant bits), rounded to bf16 if asked; sub-block byte
