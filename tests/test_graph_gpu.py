@@ -1,6 +1,8 @@
 """The entry points under HIP graph capture: one graph holds quantize (OAS),
 dequantize, block MSE with tensor sums, fake-quant, MXFP8 fake-quant, NVFP4
-quantize and MBS-Static quantize on static buffers. Every replay, with new
+quantize / dequantize / fake-quant, MBS-Static quantize / dequantize /
+fake-quant, the one-pass call with every output, and a multi-tensor
+quantize, on static buffers. Every replay, with new
 inputs copied in and the outputs overwritten by eager work in between, must
 reproduce the eager results bit for bit (the path records no memset and
 allocates nothing, so it is capturable as is)."""
@@ -36,7 +38,18 @@ def test_graph_replays_match_eager():
     wsnb = mx.mx_nvfp4_workspace_size(R, K)
     wsn = torch.empty(wsnb, **u8)
     cm, sm, mm = torch.empty((R, K // 2), **u8), torch.empty((R, K // 16), **u8), torch.empty((R, K // 128), **u8)
-    outs = (c, s, y, bm, sums, fq, fq8, cn, bn, tn, cm, sm, mm)
+    ynv, ymb, fqnv, fqmb = (torch.empty_like(xb) for _ in range(4))
+    wsn2 = torch.empty(wsnb, **u8)
+    c1, s1, y1 = torch.empty((R, K // 2), **u8), torch.empty((R, K // 32), **u8), torch.empty_like(xb)
+    bm1, sums1, ws1 = torch.empty_like(bm), torch.empty_like(sums), torch.empty(wsb, **u8)
+    cq, sq = torch.empty((R, K // 2), **u8), torch.empty((R, K // 32), **u8)
+    half = R // 2
+    descs = (mx.MxTensor * 2)()
+    descs[0] = mx.MxTensor(xb.data_ptr(), None, cq.data_ptr(), sq.data_ptr(), half, K)
+    descs[1] = mx.MxTensor(xb[half].data_ptr(), None, cq[half].data_ptr(), sq[half].data_ptr(),
+                           R - half, K)
+    outs = (c, s, y, bm, sums, fq, fq8, cn, bn, tn, cm, sm, mm, ynv, ymb, fqnv, fqmb,
+            c1, s1, y1, bm1, sums1, cq, sq)
 
     def seq(h):
         _ok(mx.mx_quantize(xf.data_ptr(), mx.MX_F32, R, K, mx.MX_SCALE_OAS, c.data_ptr(),
@@ -50,6 +63,17 @@ def test_graph_replays_match_eager():
                                  tn.data_ptr(), wsn.data_ptr(), wsnb, h))
         _ok(mx.mx_quantize_mbs(xb.data_ptr(), mx.MX_BF16, R, K, cm.data_ptr(), sm.data_ptr(),
                                mm.data_ptr(), h))
+        _ok(mx.mx_dequantize_nvfp4(cn.data_ptr(), bn.data_ptr(), tn.data_ptr(), R, K, mx.MX_BF16,
+                                   ynv.data_ptr(), h))
+        _ok(mx.mx_dequantize_mbs(cm.data_ptr(), sm.data_ptr(), mm.data_ptr(), R, K, mx.MX_BF16,
+                                 ymb.data_ptr(), h))
+        _ok(mx.mx_fakequant_nvfp4(xb.data_ptr(), mx.MX_BF16, R, K, fqnv.data_ptr(),
+                                  wsn2.data_ptr(), wsnb, h))
+        _ok(mx.mx_fakequant_mbs(xb.data_ptr(), mx.MX_BF16, R, K, fqmb.data_ptr(), h))
+        _ok(mx.mx_quantize_fused(xb.data_ptr(), mx.MX_BF16, R, K, mx.MX_SCALE_OAS_NF,
+                                 c1.data_ptr(), s1.data_ptr(), y1.data_ptr(), bm1.data_ptr(),
+                                 sums1.data_ptr(), ws1.data_ptr(), wsb, h))
+        _ok(mx.mx_quantize_multi(descs, 2, mx.MX_BF16, mx.MX_SCALE_OAS_BITS, h))
 
     def load(seed):
         xf.copy_(workloads.fp32_normal(seed, (R, K)).to(dev) * (seed % 5 + 1))
