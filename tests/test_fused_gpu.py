@@ -128,3 +128,14 @@ def test_fused_past_2_31_elements():
     assert_same_bits(y.index_select(0, idx), oracle.fakequant(xs, "oas"), "fused y (sampled rows)")
     wbm, _, _ = oracle.block_mse(xs, wc, ws, with_energy=True)
     assert np.allclose(bm.index_select(0, idx).cpu().numpy(), wbm, rtol=1e-6, atol=0)
+
+
+def test_fused_deterministic():
+    """Repeated calls give the same bits, tensor sums included (fixed-order
+    partial sums, no atomics)."""
+    x = workloads.bf16_student_t_outlier_channels(63, shape=(2048, 4096)).cuda()
+    first = mx.quantize_fused(x, "oas")
+    for _ in range(3):
+        again = mx.quantize_fused(x, "oas")
+        for a, b in zip(first, again):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
