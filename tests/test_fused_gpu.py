@@ -11,7 +11,7 @@ import torch
 import oracle
 import workloads
 import microscaling_fp4_block_mx_amd as mx
-from test_parity_gpu import assert_same_bits, host_view, say
+from test_parity_gpu import THREADS, assert_same_bits, host_view, say
 
 pytestmark = pytest.mark.gpu
 
@@ -128,6 +128,17 @@ def test_fused_past_2_31_elements():
     assert_same_bits(y.index_select(0, idx), oracle.fakequant(xs, "oas"), "fused y (sampled rows)")
     wbm, _, _ = oracle.block_mse(xs, wc, ws, with_energy=True)
     assert np.allclose(bm.index_select(0, idx).cpu().numpy(), wbm, rtol=1e-6, atol=0)
+    # the whole tensor: the oracle quantizes all 2^31 + 2^20 elements itself;
+    # codes and scales equal everywhere, and the tensor sums agree
+    say("fused big tensor: oracle over the whole tensor")
+    del y
+    xh = host_view(x)
+    wc_all, ws_all = oracle.quantize(xh, "oas", threads=THREADS)
+    assert_same_bits(s, ws_all, "fused scales (whole tensor)")
+    assert_same_bits(c, wc_all, "fused codes (whole tensor)")
+    _, wsse, wssq = oracle.block_mse(xh, wc_all, ws_all, threads=THREADS, with_energy=True)
+    got = sums.tolist()
+    assert same_sum(got[0], wsse) and same_sum(got[1], wssq), (got, wsse, wssq)
 
 
 def test_fused_deterministic():
