@@ -440,26 +440,28 @@ __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
   }
 }
 
-// Items per thread per tile for the streaming kernels: an fp32 item is two
-// 16-byte accesses, so fp32 takes half as many items, which keeps the bytes
-// in flight per lane equal and doubles the workgroups on small tensors.
-// (Kernels whose workspace size is fixed per shape, whatever the dtype, keep
-// kUnroll for both.)
+// Items per thread per tile for the streaming kernels: kUnroll bf16 items,
+// a quarter as many fp32 items (an fp32 item is two 16-byte accesses). One
+// fp32 item per thread doubles the workgroups in flight, which measured
+// 2-4 % faster than two for fp32 quantize, dequantize and MXFP8 on both a
+// 4 Mi-element and a 32 Mi-element tensor. (Kernels whose workspace size is
+// fixed per shape, whatever the dtype, keep kUnroll for both.)
 template <bool BF16>
-constexpr int kU = BF16 ? kUnroll : (kUnroll > 1 ? kUnroll / 2 : 1);
+constexpr int kU = BF16 ? kUnroll : (kUnroll >= 4 ? kUnroll / 4 : 1);
 
 // Items per thread for the MXFP4 kernels, by what the kernel does (measured
-// on bf16 8192x4096, each op alone): quantize in the OCP, OAS and OAS_BITS
-// modes keeps kU (two items per thread was 7 % slower), while fake-quant,
-// dequantize and OAS_NF quantize take two (2-12 % faster: fewer registers
-// and more workgroups in flight for the longer per-item work or the
-// write-heavy stream). The multi-tensor launch uses the same numbers; its
-// tile offsets depend on them.
+// each op alone): bf16 quantize in the OCP, OAS and OAS_BITS modes keeps kU
+// (two items per thread was 7 % slower on 8192x4096), while bf16 dequantize
+// and OAS_NF quantize take two (2-12 % faster: fewer registers and more
+// workgroups in flight for the longer per-item work or the write-heavy
+// stream). Fake-quant takes two items in both dtypes (one fp32 item was 5 %
+// slower on fp32 1024x4096). The multi-tensor launch uses the same numbers;
+// its tile offsets depend on them.
 enum { kKindQuantize = 0, kKindFakequant = 1, kKindDequantize = 2 };
 constexpr int unroll_of(bool bf16, int mode, int kind) {
-  return kind == kKindQuantize && mode != MX_SCALE_OAS_NF
-             ? (bf16 ? kU<true> : kU<false>)
-             : kU<false>;
+  if (kind == kKindFakequant) return 2;
+  if (!bf16) return kU<false>;
+  return kind == kKindQuantize && mode != MX_SCALE_OAS_NF ? kU<true> : 2;
 }
 
 template <bool BF16, int MODE>
