@@ -72,6 +72,9 @@ KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0>", "quantize_oas": "k_quantize<
              "dequantize_bf16": "k_dequantize<true>", "fakequant_ocp": "k_fakequant<true, 0>",
              "block_mse": "k_block_mse<true, true>"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mx_bf16_8192x4096_hbm_traffic.md")
+# launches per timing of the multi-GB suite workloads: warm-up, then timed
+# twice (per-launch events, then back to back)
+BIG_TIMED, BIG_WARM = 20, 3
 KERNEL_SRCS = (os.path.join(ROOT, "microscaling_fp4_block_mx_amd", "csrc", "mx_kernels.hip"),
                os.path.join(ROOT, "microscaling_fp4_block_mx_amd", "csrc", "mx_internal.h"))
 
@@ -121,11 +124,16 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true",
                     help="time the operations on the other workloads instead of the step")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from the rocprofv3 csv files in DIR "
+                         "(trace_*, fetch_*, write_*, suite_*) and exit; needs no GPU")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        return summarize_profiles(args.summarize_profiles)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this benchmark measures one GPU only; every MX block is independent, "
               "so the path shards by rows with no exchange. "
@@ -699,11 +707,11 @@ def suite(args, dev):
         ok(mx.mx_quantize_multi(descs, len(mats), mx.MX_BF16, mx.MX_SCALE_OCP, sh))
 
     report(WL, "quantize_ocp (196 per-matrix launches)", bytes_q,
-           _launch_stats(per_matrix, 20, 3, stream), cache="exceeds cache")
+           _launch_stats(per_matrix, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     report(WL, "quantize_ocp (196 matrices, one multi-tensor call)", bytes_q,
-           _launch_stats(multi, 20, 3, stream), cache="exceeds cache")
+           _launch_stats(multi, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     report(WL, "quantize_ocp (2 launches grouped by K)", bytes_q,
-           _launch_stats(grouped, 20, 3, stream), cache="exceeds cache")
+           _launch_stats(grouped, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     del a, b, ca, sa, cb, sb, mats
     torch.cuda.empty_cache()
 
@@ -726,9 +734,9 @@ def suite(args, dev):
             ok(mx.mx_dequantize(c.data_ptr(), s_.data_ptr(), rows, k, mx.MX_BF16, y.data_ptr(), sh))
 
     report(WM, "quantize_ocp (w13 + w2)", (2 + 0.5 + 1 / 32) * n,
-           _launch_stats(qm, 20, 3, stream), cache="exceeds cache")
+           _launch_stats(qm, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     report(WM, "dequantize_bf16 (w13 + w2)", (0.5 + 1 / 32 + 2) * n,
-           _launch_stats(dqm, 20, 3, stream), cache="exceeds cache")
+           _launch_stats(dqm, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     del w13, w2, cs, ss, ys
     torch.cuda.empty_cache()
 
@@ -753,6 +761,242 @@ def suite(args, dev):
     print("|---|" + "---|" * len(fmts))
     for r in quality:
         print(f"| {r['workload']} | " + " | ".join(f"{r['qsnr_db'][f]:.2f}" for f in fmts) + " |")
+
+
+# ---- rocprofv3 summaries ------------------------------------------------------
+
+# Algorithmic bytes per element of each kernel on the bf16 bench tensor, by
+# the name rocprofv3 prints (NVFP4 quantize is two kernels: the tensor-maximum
+# pass reads x, the block pass reads it again and writes codes and scales).
+KERNEL_BYTES_PER_ELEM = {
+    "k_quantize<true, 0>": BYTES_PER_ELEM["quantize_ocp"],
+    "k_quantize<true, 1>": BYTES_PER_ELEM["quantize_oas"],
+    "k_quantize<true, 2>": EXTRA_BYTES_PER_ELEM["quantize_oas_bits"],
+    "k_quantize<true, 3>": EXTRA_BYTES_PER_ELEM["quantize_oas_nf"],
+    "k_dequantize<true>": BYTES_PER_ELEM["dequantize_bf16"],
+    "k_fakequant<true, 0>": BYTES_PER_ELEM["fakequant_ocp"],
+    "k_fakequant<true, 1>": EXTRA_BYTES_PER_ELEM["fakequant_oas"],
+    "k_fakequant<true, 3>": EXTRA_BYTES_PER_ELEM["fakequant_oas_nf"],
+    "k_block_mse<true, true>": BYTES_PER_ELEM["block_mse"],
+    "k_quantize8<true>": EXTRA_BYTES_PER_ELEM["quantize_mxfp8"],
+    "k_dequantize8<true>": EXTRA_BYTES_PER_ELEM["dequantize_mxfp8_bf16"],
+    "k_fakequant8<true>": EXTRA_BYTES_PER_ELEM["fakequant_mxfp8"],
+    "k_absmax_partials<true>": 2.0,
+    "k_quantize_nv<true, false>": EXTRA_BYTES_PER_ELEM["quantize_nvfp4"] - 2.0,
+    "k_quantize_nv<true, true>": EXTRA_BYTES_PER_ELEM["fakequant_nvfp4"] - 2.0,
+    "k_dequantize_nv<true>": EXTRA_BYTES_PER_ELEM["dequantize_nvfp4_bf16"],
+    "k_quantize_mbs<true, false>": EXTRA_BYTES_PER_ELEM["quantize_mbs"],
+    "k_quantize_mbs<true, true>": EXTRA_BYTES_PER_ELEM["fakequant_mbs"],
+    "k_dequantize_mbs<true>": EXTRA_BYTES_PER_ELEM["dequantize_mbs_bf16"],
+    "k_quantize_fused<true, 0, true>": EXTRA_BYTES_PER_ELEM["quantize_fused"],
+    "__amd_rocclr_copyBuffer": 4.0,  # the reference copy: 2 B in + 2 B out
+}
+BENCH_ELEMS = 8192 * 4096
+
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT -o trace -- \\\n"
+             "    python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT -o fetch -- \\\n"
+             "    python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT -o write -- \\\n"
+             "    python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
+    "suite": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT -o suite -- \\\n"
+             "    python3 $R/bench.py --suite",
+}
+PROFILE_HOW = ("Each rocprofv3 command runs on its own, from a scratch working directory "
+               "(`cd /tmp`), with `$R` the repository root and `$OUT` an output directory; "
+               "`python3 $R/bench.py --summarize-profiles $OUT` then writes this file.")
+
+
+def _kernel_short(name: str) -> str:
+    for k in KERNEL_BYTES_PER_ELEM:
+        if k in name:
+            return k
+    return name.split("(")[0].replace("void ", "").replace("mxk::", "")
+
+
+def summarize_profiles(d: str, out_dir: str = os.path.join(ROOT, "profiles")) -> None:
+    """The three profiles/ summaries from rocprofv3 csv output in d: the
+    bench step's kernel trace, its HBM traffic (FETCH_SIZE and WRITE_SIZE,
+    calibrated on the reference copy), and the suite's kernel trace (when d
+    holds one), written to out_dir."""
+    import collections
+    import csv
+
+    h = kernel_code_hash()
+    code = ("Kernel code (`csrc/mx_kernels.hip` + `csrc/mx_internal.h`, comments and whitespace "
+            f"stripped; `bench.kernel_code_hash`) sha256 prefix: `{h}`\n")
+    alg = {k: int(v * BENCH_ELEMS) for k, v in KERNEL_BYTES_PER_ELEM.items()}
+    pct = lambda b, us: b / us / 1e3 / HBM_PEAK_GBS * 100  # noqa: E731
+
+    # kernel trace of the bench run
+    out = ["# Kernel trace: MXFP4 hot-path kernels, bf16 8192x4096 (bench.py step)\n",
+           PROFILE_HOW + "\n", "```\n" + PROFILE_CMDS["trace"] + "\n```\n",
+           "Step kernels: `k_quantize<true, 0>` (OCP), `k_quantize<true, 1>` (OAS), "
+           "`k_dequantize<true>`, `k_fakequant<true, 0>`, `k_block_mse<true, true>` + "
+           "`k_sum_partials`; the rest run beside the step (modes 2/3 = OAS_BITS/OAS_NF, `*8` = "
+           "MXFP8, `*_nv` / `k_absmax_partials` = NVFP4, `*_mbs` = MBS-Static; a `true` second "
+           "template argument of those two is the fused fake-quant; `k_quantize_fused` = quantize "
+           "+ dequantized output + block MSE + tensor sums in one pass). bf16 in, 8192x4096.\n",
+           code,
+           "| kernel | calls | avg us | min us | max us | algorithmic bytes | GB/s at avg "
+           "| % of 8 TB/s |", "|---|---|---|---|---|---|---|---|"]
+    with open(os.path.join(d, "trace_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            k = _kernel_short(r["Name"])
+            if k not in alg and k != "k_sum_partials":
+                continue
+            avg = float(r["AverageNs"]) / 1e3
+            b = alg.get(k)
+            out.append(f"| `{k}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                       f"{float(r['MaxNs']) / 1e3:.2f} | {b if b else '-'} | "
+                       f"{f'{b / avg / 1e3:.0f}' if b else '-'} | "
+                       f"{f'{pct(b, avg):.1f}' if b else '-'} |")
+    with open(os.path.join(out_dir, "mx_bf16_8192x4096_kernel_trace.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+
+    # HBM traffic: the reference copy (64 MiB read + 64 MiB written, the
+    # largest copyBuffer dispatch) calibrates both counters
+    copy = "__amd_rocclr_copyBuffer"
+    with open(os.path.join(d, "write_counter_collection.csv")) as f:
+        wr = [r for r in csv.DictReader(f) if _kernel_short(r["Kernel_Name"]) == copy]
+    ref_grid = max(wr, key=lambda r: float(r["Counter_Value"]))["Grid_Size"]
+    per = {}
+    for fn, ctr in (("fetch_counter_collection.csv", "FETCH_SIZE"),
+                    ("write_counter_collection.csv", "WRITE_SIZE")):
+        agg = collections.defaultdict(list)
+        with open(os.path.join(d, fn)) as f:
+            for r in csv.DictReader(f):
+                k = _kernel_short(r["Kernel_Name"])
+                if k == copy and r["Grid_Size"] != ref_grid:
+                    continue
+                agg[k].append(float(r["Counter_Value"]))
+        per[ctr] = {k: sum(v) / len(v) for k, v in agg.items()}
+    cal_f = 65536.0 / per["FETCH_SIZE"][copy]
+    cal_w = 65536.0 / per["WRITE_SIZE"][copy]
+    out = ["# HBM traffic: MXFP4 hot-path kernels, bf16 8192x4096 (bench.py step)\n",
+           PROFILE_HOW + "\n",
+           "```\n" + PROFILE_CMDS["fetch"] + "\n" + PROFILE_CMDS["write"] + "\n```\n", code,
+           f"Calibration: the device copy bench.py runs (`{copy}`, 64 MiB read + 64 MiB written "
+           f"per dispatch) reads FETCH_SIZE {per['FETCH_SIZE'][copy]:.1f} KiB and WRITE_SIZE "
+           f"{per['WRITE_SIZE'][copy]:.1f} KiB, so FETCH_SIZE is scaled by {cal_f:.4f} and "
+           f"WRITE_SIZE by {cal_w:.4f}.\n",
+           "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled traffic bytes | algorithmic bytes "
+           "| traffic / algorithmic |", "|---|---|---|---|---|---|"]
+    machine = []
+    for k in KERNEL_BYTES_PER_ELEM:
+        if k not in per["FETCH_SIZE"] or k not in per["WRITE_SIZE"]:
+            continue
+        fk, wk = per["FETCH_SIZE"][k], per["WRITE_SIZE"][k]
+        t = (fk * cal_f + wk * cal_w) * 1024
+        out.append(f"| `{k}` | {fk:.1f} | {wk:.1f} | {t:.0f} | {alg[k]} | {t / alg[k]:.4f} |")
+        machine.append(f"traffic_bytes {k} {t:.0f}")
+    out += ["\nMachine-readable (read by bench.py while the source hash matches):\n",
+            "```\nkernel_code_sha256_prefix " + h] + machine + ["```"]
+    with open(os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
+        f.write("\n".join(out) + "\n")
+    if os.path.exists(os.path.join(d, "suite_kernel_trace.csv")):
+        _summarize_suite(os.path.join(d, "suite_kernel_trace.csv"), code, out_dir)
+
+
+def _summarize_suite(path: str, code: str, out_dir: str) -> None:
+    """Per-workload kernel times of `bench.py --suite` from its kernel trace.
+    Launches are told apart by kernel, dtype and grid size; the two
+    196,608-workgroup groups by dispatch order (see the note written out)."""
+    import collections
+    import csv
+
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    short = lambda n: n.split("(")[0].replace("void ", "").replace("mxk::", "")  # noqa: E731
+    c1, c5 = 1024 * 4096, 16384 * 8192
+    l3072, l8192 = 688128 * 3072, 86016 * 8192
+    m13, m2 = 128 * 3072 * 4096, 128 * 4096 * 1536
+    passes = 2 * BIG_TIMED + BIG_WARM  # dispatches of one big-workload timing
+    per_matrix = {384: ("k/v [1024, 3072]", 1024 * 3072), 1152: ("q/o [3072, 3072]", 3072 * 3072),
+                  3072: ("gate/up [8192, 3072] and down [3072, 8192]", 8192 * 3072)}
+
+    def bytes_for(kernel, n, f32):
+        if kernel.startswith(("k_quantize<", "k_dequantize<")):
+            return n * (4.53125 if f32 else 2.53125)
+        if kernel.startswith("k_block_mse<"):
+            return n * (4.65625 if f32 else 2.65625)
+        if kernel.startswith("k_quantize_fused<"):
+            return n * (8.65625 if f32 else 4.65625)
+        return None
+
+    # the timed part ends with the MoE dequantize launches; the QSNR pass
+    # that follows is not timed and is left out
+    last = max(i for i, r in enumerate(rows)
+               if short(r["Kernel_Name"]) == "k_dequantize<true>"
+               and int(r["Grid_Size_X"]) // 256 in (196608, 98304))
+    groups = collections.OrderedDict()
+    seen196 = 0
+    for r in rows[:last + 1]:
+        k = short(r["Kernel_Name"])
+        if not k.startswith("k_"):
+            continue
+        grid = int(r["Grid_Size_X"]) // 256
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if k.startswith("k_multi"):
+            key = ("MULTI", k, None)
+        elif k == "k_sum_partials":
+            key = ("tensor-sum pass of block MSE (all workloads)", k, None)
+        elif "<false" in k:
+            key = ("fp32 normal [1024, 4096]", k, c1)
+        elif grid == 16384 or k.startswith("k_block_mse"):
+            key = ("bf16 Laplace [16384, 8192]", k, c5)
+        elif grid in per_matrix and k.startswith("k_quantize<"):
+            key = ("Llama-3.2-3B per-matrix launches: " + per_matrix[grid][0], k,
+                   per_matrix[grid][1])
+        elif grid == 86016:
+            key = ("Llama-3.2-3B grouped by K: K=8192 [86016, 8192]", k, l8192)
+        elif grid == 98304:
+            key = ("MoE w2 [128x4096, 1536]", k, m2)
+        elif grid == 196608 and k.startswith("k_quantize<"):
+            seen196 += 1
+            key = (("Llama-3.2-3B grouped by K: K=3072 [688128, 3072]", k, l3072)
+                   if seen196 <= passes else ("MoE w13 [128x3072, 4096]", k, m13))
+        elif grid == 196608 and k.startswith("k_dequantize<"):
+            key = ("MOEDQ", k, None)
+        elif grid == 196608:
+            key = ("MoE w13 [128x3072, 4096]", k, m13)
+        else:
+            key = (f"unattributed (grid {grid})", k, None)
+        groups.setdefault(key, []).append(dur)
+    multi = groups.pop(("MULTI", "k_multi<true, 0, false>", None), None)
+    moedq = groups.pop(("MOEDQ", "k_dequantize<true>", None), None)
+    if moedq:  # w13 and w2 alternate
+        groups[("MoE w13 [128x3072, 4096]", "k_dequantize<true>", m13)] = moedq[0::2]
+        groups[("MoE w2 [128x4096, 1536]", "k_dequantize<true>", m2)] = moedq[1::2]
+    out = ["# Kernel trace: the other workloads (`bench.py --suite`)\n", PROFILE_HOW + "\n",
+           "```\n" + PROFILE_CMDS["suite"] + "\n```\n", code,
+           "Durations are the GPU's own per-dispatch times from the trace (under the profiler the "
+           "host-side event figures of the small fp32 case are inflated by per-dispatch overhead; "
+           "these are not). Launches are attributed to their workload by grid size; the K=3072 "
+           "Llama group and the MoE w13 tensor both run 196,608 workgroups and are told apart by "
+           f"dispatch order (the suite runs the Llama launches first, {passes} of each), and the "
+           "MoE dequantize launches (both 196,608 workgroups) alternate w13, w2. Per-matrix Llama "
+           "launches are grouped by shape. The suite's QSNR pass, which runs after the timed "
+           "launches, is left out.\n",
+           "| workload | kernel | dispatches | avg us | min us | max us | algorithmic bytes "
+           "| GB/s at avg | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for (wl, k, n), v in groups.items():
+        avg = sum(v) / len(v)
+        b = bytes_for(k, n, "<false" in k) if n else None
+        out.append(f"| {wl} | `{k}` | {len(v)} | {avg:.2f} | {min(v):.2f} | {max(v):.2f} | "
+                   f"{int(b) if b else '-'} | {f'{b / avg / 1e3:.0f}' if b else '-'} | "
+                   f"{f'{b / avg / 1e3 / HBM_PEAK_GBS * 100:.1f}' if b else '-'} |")
+    if multi:
+        per_pass = sum(multi) / passes
+        b = (l3072 + l8192) * 2.53125
+        out.append(f"| Llama-3.2-3B, the 196 weights as separate tensors: one `mx_quantize_multi` "
+                   f"call per pass ({len(multi) // passes} launches) | `k_multi<true, 0, false>` | "
+                   f"{len(multi)} | {per_pass:.2f} per pass | {min(multi):.2f} | {max(multi):.2f} "
+                   f"| {int(b)} | {b / per_pass / 1e3:.0f} | "
+                   f"{b / per_pass / 1e3 / HBM_PEAK_GBS * 100:.1f} |")
+    with open(os.path.join(out_dir, "mx_workloads_suite_kernel_trace.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
 
 
 QUALITY_FORMATS = ("mxfp4_ocp", "mxfp4_oas", "mxfp4_oas_bits", "mxfp4_oas_nf", "mxfp8",
