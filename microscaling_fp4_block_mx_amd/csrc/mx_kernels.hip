@@ -694,8 +694,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_fused(const void *__restr
   double mine = 0.0, mine_sq = 0.0;
   const bool err = block_mse != nullptr || SUMS;
   // (the grid is the block-MSE grid, sized with kUnroll items per thread;
-  // the grid stride makes any per-thread count correct, and fp32 items take
-  // two per thread here as in the streaming kernels)
+  // the grid stride makes any per-thread count correct, and the items per
+  // thread here are the streaming kernels' kU)
   constexpr int U = kU<BF16>;
   Item<BF16> xv[U];
   tile_loop<U>(
