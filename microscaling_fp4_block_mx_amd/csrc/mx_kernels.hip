@@ -412,8 +412,11 @@ __device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t 
 // ---- kernels -----------------------------------------------------------------
 
 // Grid-stride over tiles of kThreads * U items; each thread's U items are
-// spaced kThreads apart so every load instruction is coalesced, and all loads
-// of a tile are issued before any is consumed. Full tiles run without bounds
+// spaced kThreads apart so every load instruction is coalesced, and the loads
+// of a tile come ahead of its arithmetic (the backend may still sink a load
+// whose value is first used past a divergent branch below the first item's
+// work: OAS quantize issues one load, then three, which measured faster than
+// forcing all four ahead). Full tiles run without bounds
 // checks; the one partial tile (if any) is handled by the workgroup whose
 // stride lands on it, with per-item checks.
 template <int U, typename Load, typename Use>
