@@ -329,13 +329,12 @@ def quantize_fused(x: torch.Tensor, mode: str = "ocp", want_y: bool = True,
           if want_block_mse else None)
     sums = torch.empty(2, dtype=torch.float64, device=x.device) if want_sums else None
     ws_bytes = mx_block_mse_workspace_size(rows, k) if want_sums else 0
-    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=x.device)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if want_sums else None
     ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     with torch.cuda.device(x.device):
         _raise(mx_quantize_fused(x.data_ptr(), _DTYPES[x.dtype], rows, k, _mode(mode),
                                  codes.data_ptr(), scales.data_ptr(), ptr(y), ptr(bm), ptr(sums),
-                                 ws.data_ptr() if want_sums else None, ws_bytes,
-                                 _stream(x.device)))
+                                 ptr(ws), ws_bytes, _stream(x.device)))
     return codes, scales, y, bm, sums
 
 
