@@ -27,9 +27,10 @@
 //
 // Format facts (E2M1 grid 0, .5, 1, 1.5, 2, 3, 4, 6; E8M0 scale 2^(s-127);
 // two codes per byte, even element low) are stated with their sources in
-// include/mx.h. Later sections hold the other formats on the same item
-// layout (MXFP8, the NVFP4 comparator, MBS-Static) and the multi-tensor
-// launch.
+// include/mx.h. The MXFP4 kernels (quantize, fake-quant, dequantize, block
+// error, and the one pass that does all of them from one read of x) come
+// first; later sections hold the multi-tensor launch and the other formats
+// on the same item layout (MXFP8, the NVFP4 comparator, MBS-Static).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
