@@ -63,3 +63,12 @@ def test_kernel_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.kernel_code_hash() == h1
     src.write_text("int a; int c;\n")
     assert bench.kernel_code_hash() != h1
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
