@@ -665,8 +665,9 @@ int mxrefnv_dequantize(const uint8_t *codes, const uint8_t *block_scales, int te
  * Readings where the page stops:
  *  - macro factor f = 1 + m/256, m = the 8-bit mantissa of r = a_M / 6
  *    (a_M = largest |x| of the macro block, division in fp32), rounded to
- *    nearest even and capped at 255; m = 0 when a_M == 0. It carries the
- *    part of a_M / 6 that a power of two cannot.
+ *    nearest even and capped at 255; m = 0 when a_M is 0 or not finite, or
+ *    when a_M / 6 underflows to zero in fp32. It carries the part of a_M / 6
+ *    that a power of two cannot.
  *  - y = fl32(x * fl32(1 / f)); each 16-element sub-block takes the OCP
  *    byte of its largest |y| (floor(log2) - 2 + 127, clamped; 255 if it
  *    holds NaN/Inf), and each element the E2M1 code of y at that byte.
