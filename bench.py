@@ -802,7 +802,13 @@ PROFILE_CMDS = {
              "    python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
     "suite": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT -o suite -- \\\n"
              "    python3 $R/bench.py --suite",
+    "sq": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR \\\n"
+          "    SQ_INSTS_LDS SQ_BUSY_CYCLES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $OUT -o sq -- \\\n"
+          "    python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
 }
+# VALU issue model for the instruction-mix summary: a wave64 VALU instruction
+# holds its 16-lane SIMD for 4 cycles; 256 CUs x 4 SIMDs at 2.4 GHz
+SIMDS, CLOCK_GHZ, VALU_CYCLES = 1024, 2.4, 4
 PROFILE_HOW = ("Each rocprofv3 command runs on its own, from a scratch working directory "
                "(`cd /tmp`), with `$R` the repository root and `$OUT` an output directory; "
                "`python3 $R/bench.py --summarize-profiles $OUT` then writes this file.")
@@ -897,6 +903,54 @@ def summarize_profiles(d: str, out_dir: str = os.path.join(ROOT, "profiles")) ->
         f.write("\n".join(out) + "\n")
     if os.path.exists(os.path.join(d, "suite_kernel_trace.csv")):
         _summarize_suite(os.path.join(d, "suite_kernel_trace.csv"), code, out_dir)
+    if os.path.exists(os.path.join(d, "sq_counter_collection.csv")):
+        _summarize_instruction_mix(d, code, out_dir)
+
+
+def _summarize_instruction_mix(d: str, code: str, out_dir: str) -> None:
+    """Instructions per wave-item (one item = 8 elements per lane, 64 lanes)
+    of each kernel from the SQ counters, and the time its VALU instructions
+    take at full issue rate next to the kernel's traced duration."""
+    import collections
+    import csv
+
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(os.path.join(d, "sq_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            agg[_kernel_short(r["Kernel_Name"])][r["Counter_Name"]].append(
+                float(r["Counter_Value"]))
+    avg_us = {}
+    trace = os.path.join(d, "trace_kernel_stats.csv")
+    if os.path.exists(trace):
+        with open(trace) as f:
+            for r in csv.DictReader(f):
+                avg_us[_kernel_short(r["Name"])] = float(r["AverageNs"]) / 1e3
+    wave_items = BENCH_ELEMS / (8 * 64)
+    out = ["# Instruction mix: MXFP4 hot-path kernels, bf16 8192x4096 (bench.py step)\n",
+           PROFILE_HOW + "\n", "```\n" + PROFILE_CMDS["sq"] + "\n```\n", code,
+           "Counts are chip totals per dispatch (SQ_WAVES equals the waves launched), "
+           "averaged over the dispatches of each kernel, per wave-item: one item is 8 "
+           "elements in each of a wave's 64 lanes, so the bench tensor is "
+           f"{int(wave_items)} wave-items. VALU issue time = SQ_INSTS_VALU x {VALU_CYCLES} "
+           f"cycles / ({SIMDS} SIMDs x {CLOCK_GHZ} GHz), the time the kernel's vector "
+           "instructions need if every SIMD issued one each cycle slot with nothing else "
+           "in the way; kernel time from the kernel trace of the same code.\n",
+           "| kernel | waves | VALU / wave-item | SALU / wave-item | VMEM rd / wave-item "
+           "| VMEM wr / wave-item | LDS / wave-item | VALU issue us | kernel us | VALU issue / "
+           "kernel |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for k in KERNEL_BYTES_PER_ELEM:
+        if k not in agg or k == "__amd_rocclr_copyBuffer":
+            continue
+        c = {n: sum(v) / len(v) for n, v in agg[k].items()}
+        per = lambda n: c.get(n, 0.0) / wave_items  # noqa: E731
+        valu_us = c.get("SQ_INSTS_VALU", 0.0) * VALU_CYCLES / (SIMDS * CLOCK_GHZ * 1e3)
+        t = avg_us.get(k)
+        out.append(f"| `{k}` | {int(c.get('SQ_WAVES', 0))} | {per('SQ_INSTS_VALU'):.1f} | "
+                   f"{per('SQ_INSTS_SALU'):.1f} | {per('SQ_INSTS_VMEM_RD'):.2f} | "
+                   f"{per('SQ_INSTS_VMEM_WR'):.2f} | {per('SQ_INSTS_LDS'):.2f} | {valu_us:.2f} | "
+                   f"{f'{t:.2f}' if t else '-'} | {f'{valu_us / t:.2f}' if t else '-'} |")
+    with open(os.path.join(out_dir, "mx_bf16_8192x4096_instruction_mix.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
 
 
 def _summarize_suite(path: str, code: str, out_dir: str) -> None:
