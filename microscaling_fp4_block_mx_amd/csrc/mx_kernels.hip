@@ -658,6 +658,11 @@ __device__ __forceinline__ void write_partials(double mine, double mine_sq,
   }
 }
 
+// Items per thread of the block-MSE kernel, both dtypes (it sizes the grid,
+// hence the workspace, per shape): two measured 3 % faster than four on bf16
+// 8192x4096 with the same per-block results.
+constexpr int kMseU = 2;
+
 template <bool BF16, bool SUMS>
 __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__ x,
                                                         const uint32_t *__restrict__ codes,
@@ -667,9 +672,9 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
                                                         int64_t nitems) {
   double mine = 0.0;     // sum of the block SSEs this lane reports (q == 0 lanes)
   double mine_sq = 0.0;  // sum of x^2 over this lane's elements
-  Item<BF16> xv[kUnroll];
-  uint32_t cw[kUnroll], sb[kUnroll];
-  tile_loop<kUnroll>(
+  Item<BF16> xv[kMseU];
+  uint32_t cw[kMseU], sb[kMseU];
+  tile_loop<kMseU>(
       nitems,
       [&](int u, int64_t it) {
         load_item<BF16>(x, it, xv[u]);
@@ -697,9 +702,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize_fused(const void *__restr
                                                              int64_t nitems) {
   double mine = 0.0, mine_sq = 0.0;
   const bool err = block_mse != nullptr || SUMS;
-  // (the grid is the block-MSE grid, sized with kUnroll items per thread;
-  // the grid stride makes any per-thread count correct, and the items per
-  // thread here are the streaming kernels' kU)
+  // (the grid is sized like the block-MSE grid but with kUnroll items per
+  // thread, so the block-MSE workspace holds its partials; the grid stride
+  // makes any per-thread count correct, and the items per thread here are
+  // the streaming kernels' kU)
   constexpr int U = kU<BF16>;
   Item<BF16> xv[U];
   tile_loop<U>(
@@ -1397,12 +1403,16 @@ hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, in
   return hipGetLastError();
 }
 
-size_t mxi_block_mse_partials(int64_t nitems) { return 2 * grid_for(nitems, MX_MSE_GRID_CAP); }
+// (the one-pass kernel's grid, sized with kUnroll items per thread, is
+// never larger than this one, so the same workspace serves it)
+size_t mxi_block_mse_partials(int64_t nitems) {
+  return 2 * grid_for(nitems, MX_MSE_GRID_CAP, kMseU);
+}
 
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                                 const uint8_t *scales, int64_t nitems, float *block_mse,
                                 double *tensor_sums, double *partial, hipStream_t st) {
-  const unsigned grid = grid_for(nitems, MX_MSE_GRID_CAP);
+  const unsigned grid = grid_for(nitems, MX_MSE_GRID_CAP, kMseU);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
   double *part = tensor_sums ? partial : nullptr;
   if (nitems > 0) {

@@ -40,7 +40,7 @@ hipError_t mxi_launch_dequantize(const uint8_t *c, const uint8_t *s, int bf16, i
                                  hipStream_t) {
   return rec("dequantize", n, bf16, -1, c, s, y, nullptr);
 }
-size_t mxi_block_mse_partials(int64_t n) { return n > 0 ? 2 * (size_t)((n + 1023) / 1024 > 2048 ? 2048 : (n + 1023) / 1024) : 2; }
+size_t mxi_block_mse_partials(int64_t n) { return n > 0 ? 2 * (size_t)((n + 511) / 512 > 2048 ? 2048 : (n + 511) / 512) : 2; }
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *c, const uint8_t *s,
                                 int64_t n, float *bm, double *sums, double *part, hipStream_t) {
   g_last.p[4] = sums;
