@@ -1308,8 +1308,10 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_mbs(const uint32_t *__r
                                                              const uint8_t *__restrict__ sub_scales,
                                                              const uint8_t *__restrict__ macro_mant,
                                                              void *__restrict__ y, int64_t nitems) {
-  uint32_t cw[kU<BF16>], sb[kU<BF16>], mb[kU<BF16>];
-  tile_loop<kU<BF16>>(
+  // items per thread as MXFP4 dequantize (two for bf16: 2.5 % faster here)
+  constexpr int U = unroll_of(BF16, 0, kKindDequantize);
+  uint32_t cw[U], sb[U], mb[U];
+  tile_loop<U>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
@@ -1543,7 +1545,8 @@ hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint
 hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
                                      const uint8_t *macro_mant, int bf16, int64_t nitems, void *y,
                                      hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, unroll_of(bf16, 0, kKindDequantize))),
+      b(kThreads);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
   if (bf16)
     hipLaunchKernelGGL((k_dequantize_mbs<true>), g, b, 0, st, c, sub_scales, macro_mant, y, nitems);
