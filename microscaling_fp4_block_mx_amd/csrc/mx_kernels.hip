@@ -704,9 +704,9 @@ __global__ __launch_bounds__(kThreads) void k_quantize_fused(const void *__restr
   const bool err = block_mse != nullptr || SUMS;
   // (the grid is sized like the block-MSE grid but with kUnroll items per
   // thread, so the block-MSE workspace holds its partials; the grid stride
-  // makes any per-thread count correct, and the items per thread here are
-  // the streaming kernels' kU)
-  constexpr int U = kU<BF16>;
+  // makes any per-thread count correct. Two bf16 items per thread, as for
+  // fake-quant: 2.4 % faster than four on 8192x4096.)
+  constexpr int U = BF16 ? 2 : kU<false>;
   Item<BF16> xv[U];
   tile_loop<U>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
