@@ -455,7 +455,7 @@ constexpr int kU = BF16 ? kUnroll : (kUnroll >= 4 ? kUnroll / 4 : 1);
 
 // Items per thread for the MXFP4 kernels, by what the kernel does (measured
 // each op alone): bf16 quantize in the OCP, OAS and OAS_BITS modes keeps kU
-// (two items per thread was 7 % slower on 8192x4096), while bf16 dequantize
+// (two items per thread was 7 % slower on 8192x4096, eight 3-13 % slower), while bf16 dequantize
 // and OAS_NF quantize take two (2-12 % faster: fewer registers and more
 // workgroups in flight for the longer per-item work or the write-heavy
 // stream). Fake-quant takes two items in both dtypes (one fp32 item was 5 %
