@@ -72,10 +72,12 @@ typedef enum {
      top values saturate when that lowers the error). With s0 the OCP byte,
      a block with s0 >= 1 takes s0 - 1 when its squared error at s0 - 1 is
      strictly smaller than at s0; ties keep s0. The squared error is computed
-     in fp32 in one fixed order: elements 8g..8g+7 form group g (g = 0..3);
-     within a group one accumulator takes the even positions and one the odd
-     positions, each acc = fma(d, d, acc) with d = x - x_hat (fp32); group =
-     even + odd; total = (g0 + g1) + (g2 + g3). */
+     in fp32, in units of the larger candidate's scale 2^(s0-127) (so the
+     choice does not depend on the block's magnitude), in one fixed order:
+     each element error is d = (x - x_hat) * 2^(127-s0), exact, rounded once
+     to fp32; elements 8g..8g+7 form group g (g = 0..3); within a group one
+     accumulator takes the even positions and one the odd positions, each
+     acc = fma(d, d, acc); group = even + odd; total = (g0 + g1) + (g2 + g3). */
   MX_SCALE_OAS = 1,
   /* Overflow-aware scaling in the page's own form ("Unveiling...", technical
      summary section 2.A): start from the no-overflow byte s_nf, the smallest
@@ -86,8 +88,8 @@ typedef enum {
      the OCP byte it is s0 + 1 when amax / 2^(s0-127) > 7, else s0. */
   MX_SCALE_OAS_BITS = 2,
   /* Error-driven form around the no-overflow byte: the block takes s_nf - 1
-     when its squared error (the fp32 order above) is strictly smaller than at
-     s_nf; ties keep s_nf. */
+     when its squared error (the fp32 arithmetic above, in units of
+     2^(s_nf-127)) is strictly smaller than at s_nf; ties keep s_nf. */
   MX_SCALE_OAS_NF = 3
   /* In the two page modes the scale byte never exceeds 252, the largest byte
      at which every code decodes to a finite fp32/bf16 value. */

@@ -103,10 +103,10 @@ def mx_fakequant(x, dtype, rows, k, mode, y, stream) -> int:
     return load_library().mx_fakequant(x, dtype, rows, k, mode, y, stream)
 
 
-def mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse, tensor_sse, workspace,
+def mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse, tensor_sums, workspace,
                  workspace_bytes, stream) -> int:
     return load_library().mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse,
-                                       tensor_sse, workspace, workspace_bytes, stream)
+                                       tensor_sums, workspace, workspace_bytes, stream)
 
 
 def mx_block_mse_workspace_size(rows, k) -> int:

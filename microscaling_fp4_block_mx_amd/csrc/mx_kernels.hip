@@ -335,19 +335,24 @@ __device__ __forceinline__ void decode_f32(uint32_t c, uint32_t s, float (&q)[8]
   q[4] = v2.x; q[5] = v2.y; q[6] = v3.x; q[7] = v3.y;
 }
 
-// Lane share of the pinned fp32 block squared error at scale byte c:
-// d = x - x_hat in fp32, even positions in one fma accumulator, odd in
-// another, lane share = even + odd. Returns the candidate's codes too.
+// Lane share of the pinned fp32 block squared error at candidate byte c,
+// measured in units of the larger candidate's scale 2^(h-127) (h >= c): each
+// element error is d = x * 2^(127-h) - x_hat * 2^(127-h), formed exactly and
+// rounded once by one fma (x_hat is decoded straight at byte 127 + c - h);
+// even positions go to one fma accumulator and odd to another, lane share =
+// even + odd. Returns the candidate's codes too.
 template <bool BF16>
-__device__ __forceinline__ float lane_sse(const Item<BF16> &x, uint32_t c, uint32_t &codes) {
+__device__ __forceinline__ float lane_sse(const Item<BF16> &x, uint32_t c, uint32_t h,
+                                          uint32_t &codes) {
   codes = encode_item<BF16>(x, c);
   float q[8];
-  decode_f32(codes, c, q);
+  decode_f32(codes, 127u + c - h, q);
+  const float unit = __uint_as_float((254u - h) << 23);  // 2^(127-h), 1 <= h <= 252
   float acc_e = 0.0f, acc_o = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i += 2) {
-    const float d0 = elem<BF16>(x, i) - q[i];
-    const float d1 = elem<BF16>(x, i + 1) - q[i + 1];
+    const float d0 = __builtin_fmaf(elem<BF16>(x, i), unit, -q[i]);
+    const float d1 = __builtin_fmaf(elem<BF16>(x, i + 1), unit, -q[i + 1]);
     acc_e = __builtin_fmaf(d0, d0, acc_e);
     acc_o = __builtin_fmaf(d1, d1, acc_o);
   }
@@ -364,9 +369,10 @@ __device__ __forceinline__ float lane_sse(const Item<BF16> &x, uint32_t c, uint3
 // > 0x600000. Both are capped at 252 so every code decodes finite.
 //
 // Error-driven modes compare a high byte h with h - 1 by the pinned fp32
-// SSE. h - 1 is evaluated only when it can win: at h - 1 the block maximum
-// (> 3 * 2^(h-127)) saturates to 3 * 2^(h-127), so that element alone
-// contributes fl(d * d) with d = amax - 3 * 2^(h-127) (exact in fp32), and the
+// SSE (errors in units of 2^(h-127)). h - 1 is evaluated only when it can
+// win: at h - 1 the block maximum (> 3 * 2^(h-127)) saturates to
+// 3 * 2^(h-127), so that element alone contributes fl(d * d) with
+// d = fl(amax * 2^(127-h) - 3), the same d the sum takes for it, and the
 // pinned sum only grows as non-negative terms are added (rounding is
 // monotone). Hence SSE32(h - 1) >= fl(d * d); when SSE32(h) <= fl(d * d) the
 // strict test SSE32(h - 1) < SSE32(h) must fail and h is kept without
@@ -394,13 +400,14 @@ __device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t 
       return h;
     }
     uint32_t c_hi;
-    const float sse_hi = quad_sum_f32(lane_sse<BF16>(x, h, c_hi));
-    const float d_top = __uint_as_float(amax) - __builtin_amdgcn_ldexpf(3.0f, (int)h - 127);
+    const float sse_hi = quad_sum_f32(lane_sse<BF16>(x, h, h, c_hi));
+    const float d_top =
+        __builtin_fmaf(__uint_as_float(amax), __uint_as_float((254u - h) << 23), -3.0f);
     const float bound = d_top * d_top;
     codes = c_hi;
     if (sse_hi > bound) {  // uniform over the quad: same sums, same amax
       uint32_t c_low;
-      const float sse_low = quad_sum_f32(lane_sse<BF16>(x, h - 1u, c_low));
+      const float sse_low = quad_sum_f32(lane_sse<BF16>(x, h - 1u, h, c_low));
       if (sse_low < sse_hi) {  // strict: a tie keeps h
         codes = c_low;
         return h - 1u;

@@ -68,7 +68,7 @@ def _load():
         lib.mxref_encode.restype = i32
         lib.mxref_decode.argtypes = [i32, i32]
         lib.mxref_decode.restype = ctypes.c_double
-        lib.mxref_oas_sse32.argtypes = [ctypes.POINTER(ctypes.c_double), i32]
+        lib.mxref_oas_sse32.argtypes = [ctypes.POINTER(ctypes.c_double), i32, i32]
         lib.mxref_oas_sse32.restype = ctypes.c_float
         lib.mxref8_quantize.argtypes = [p, i32, i64, i64, p, p, i32]
         lib.mxref8_dequantize.argtypes = [p, p, i64, i64, i32, p, i32]
@@ -200,11 +200,15 @@ def decode(code: int, scale_byte: int) -> float:
     return _load().mxref_decode(int(code), int(scale_byte))
 
 
-def oas_sse32(block: np.ndarray, scale_byte: int) -> float:
+def oas_sse32(block: np.ndarray, scale_byte: int, unit_byte: int | None = None) -> float:
+    """Pinned fp32 squared error of a 32-element block at candidate byte
+    scale_byte, measured in units of 2^(unit_byte - 127) (unit_byte: the
+    larger of the two candidates; default scale_byte)."""
     b = np.ascontiguousarray(block, dtype=np.float64)
     assert b.shape == (32,)
+    h = int(scale_byte) if unit_byte is None else int(unit_byte)
     return float(_load().mxref_oas_sse32(b.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                                         int(scale_byte)))
+                                         int(scale_byte), h))
 
 
 # --- MXFP8 (E4M3 elements, one byte each) ----------------------------------

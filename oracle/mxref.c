@@ -36,7 +36,8 @@
  *
  * Arithmetic is C double throughout (exact for every quantity here: x/2^k,
  * grid midpoints, decoded values), except the overflow-aware decision, which
- * both this oracle and the device take in float in one fixed order.
+ * both this oracle and the device take in float in one fixed order, with
+ * each error measured in units of the larger candidate scale.
  * Build with -O2 -ffp-contract=off, never -ffast-math.
  */
 #include "mxref.h"
@@ -136,18 +137,24 @@ double mxref_decode(int c, int s) {
   return (c & 8) ? -mag : mag;
 }
 
-/* Block squared error at scale byte s, in float, in the fixed order the
- * device uses: four groups of eight consecutive elements; inside a group one
- * accumulator takes the even positions and one the odd positions, each by
- * fused multiply-add; then group = even + odd, total = (g0 + g1) + (g2 + g3). */
-float mxref_oas_sse32(const double *xb, int s) {
+/* Block squared error at candidate byte c, in float, measured in units of
+ * the larger candidate's scale 2^(h-127) (h >= c): each element's error is
+ * d = (x - x_hat) * 2^(127-h), exact in double and rounded once to float, so
+ * the comparison between the two candidates does not depend on the block's
+ * magnitude (no overflow of d*d for huge blocks, no underflow for tiny ones).
+ * The terms are summed in a fixed order: four groups of eight consecutive
+ * elements; inside a group one accumulator takes the even positions and one
+ * the odd positions, each by fused multiply-add; then group = even + odd,
+ * total = (g0 + g1) + (g2 + g3). */
+float mxref_oas_sse32(const double *xb, int c, int h) {
+  const double unit = ldexp(1.0, 127 - h); /* exact power of two */
   float grp[4];
   for (int g = 0; g < 4; g++) {
     float acc_even = 0.0f, acc_odd = 0.0f;
     for (int t = 0; t < 4; t++) {
       int i = 8 * g + 2 * t;
-      float d0 = (float)xb[i] - (float)mxref_decode(mxref_encode(xb[i], s), s);
-      float d1 = (float)xb[i + 1] - (float)mxref_decode(mxref_encode(xb[i + 1], s), s);
+      float d0 = (float)((xb[i] - mxref_decode(mxref_encode(xb[i], c), c)) * unit);
+      float d1 = (float)((xb[i + 1] - mxref_decode(mxref_encode(xb[i + 1], c), c)) * unit);
       acc_even = fmaf(d0, d0, acc_even);
       acc_odd = fmaf(d1, d1, acc_odd);
     }
@@ -176,8 +183,8 @@ static int block_scale(const double *xb, int mode) {
   if (mode == MXREF_OCP || mode == MXREF_OAS) {
     int s0 = mxref_ocp_scale(amax);
     if (mode == MXREF_OAS && s0 >= 1) {
-      float sse_ocp = mxref_oas_sse32(xb, s0);
-      float sse_low = mxref_oas_sse32(xb, s0 - 1);
+      float sse_ocp = mxref_oas_sse32(xb, s0, s0);
+      float sse_low = mxref_oas_sse32(xb, s0 - 1, s0);
       if (sse_low < sse_ocp) return s0 - 1; /* strict: a tie keeps the OCP byte */
     }
     return s0;
@@ -193,8 +200,8 @@ static int block_scale(const double *xb, int mode) {
   }
   /* MXREF_OAS_NF: the smaller of the two errors, ties keep snf */
   if (snf >= 1) {
-    float sse_nf = mxref_oas_sse32(xb, snf);
-    float sse_low = mxref_oas_sse32(xb, snf - 1);
+    float sse_nf = mxref_oas_sse32(xb, snf, snf);
+    float sse_low = mxref_oas_sse32(xb, snf - 1, snf);
     if (sse_low < sse_nf) return snf - 1;
   }
   return snf;

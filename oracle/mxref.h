@@ -41,7 +41,7 @@ int mxref_block_mse(const void *x, int dtype, const uint8_t *codes,
 int mxref_ocp_scale(double amax);                 /* E8M0 byte of the OCP rule */
 int mxref_encode(double x, int scale_byte);       /* 4-bit code of one element */
 double mxref_decode(int code, int scale_byte);    /* exact value of one code   */
-float mxref_oas_sse32(const double *x32, int scale_byte); /* pinned fp32 SSE */
+float mxref_oas_sse32(const double *x32, int c, int h); /* pinned fp32 SSE at c in units of 2^(h-127) */
 
 /* MXFP8 with E4M3 elements: codes [rows, k] uint8 (one byte per element),
  * scales [rows, k/32] as above. OCP scale only. */

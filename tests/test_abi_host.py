@@ -44,7 +44,7 @@ def test_status_strings(lib):
 A = 1 << 20  # fake, 16-byte aligned addresses: validation fails before any use
 B = 2 << 30
 C = 3 << 30
-W = 5 << 30  # fake workspace / tensor_sse region
+W = 5 << 30  # fake workspace / tensor_sums region
 
 
 @pytest.mark.parametrize("rows,k", [(-1, 32), (1, 0), (1, -32), (4, 48), (2, 33),
@@ -114,7 +114,7 @@ def test_aliasing(lib):
         mx.MX_ERR_ALIAS
     # workspace over the input
     assert mx.mx_block_mse(A, 0, B, C, 4, 64, None, W, A + 32, 64, None) == mx.MX_ERR_ALIAS
-    # tensor_sse inside the workspace
+    # tensor_sums inside the workspace
     assert mx.mx_block_mse(A, 0, B, C, 4, 64, None, W + 8, W, 64, None) == mx.MX_ERR_ALIAS
 
 

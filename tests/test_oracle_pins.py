@@ -311,8 +311,9 @@ def test_oas_worked_blocks_golden(oracle_lib):
         x = np.zeros(32, np.float32)
         x[0] = 4.0
         x[1:1 + int(n)] = 0.75
-        assert oracle_lib.oas_sse32(x.astype(np.float64), 127) == float(sse0)
-        assert oracle_lib.oas_sse32(x.astype(np.float64), 126) == float(sse1)
+        # both errors in units of the larger candidate's scale (here 1)
+        assert oracle_lib.oas_sse32(x.astype(np.float64), 127, 127) == float(sse0)
+        assert oracle_lib.oas_sse32(x.astype(np.float64), 126, 127) == float(sse1)
         _, s = oracle_lib.quantize(x[None], "oas")
         assert int(s[0, 0]) == int(byte), name
         _, s = oracle_lib.quantize(x[None], "ocp")
