@@ -147,6 +147,26 @@ mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype,
                          double *tensor_sums, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/* mx_block_mse without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The partial sums behind tensor_sums live
+ * in a fixed 32 KiB device array inside the library (2 x 2048 doubles; the
+ * block-error launch never uses more than 2048 workgroups, so every shape
+ * fits; a larger need would be MX_ERR_WORKSPACE). Each GPU holds its own copy
+ * from the first call on that GPU (the device of `stream`, or the current
+ * device for the null stream) until the process ends. The call allocates
+ * nothing; outputs equal mx_block_mse's bit for bit. Every call on a GPU
+ * shares that GPU's array, which keeps the last call's contents (nothing in
+ * it needs clearing: a call writes each partial before reading it): calls
+ * that may run at the same time on one GPU (unordered streams) race and can
+ * return wrong tensor_sums, so order them on one stream. A call with
+ * tensor_sums == NULL does not use the array. Other arguments, alignment,
+ * aliasing and error conventions as mx_block_mse. */
+mx_status_t mx_block_mse_noalloc(const void *x, mx_dtype_t x_dtype,
+                                 const uint8_t *codes, const uint8_t *scales,
+                                 int64_t rows, int64_t k, float *block_mse,
+                                 double *tensor_sums, void *stream);
+
 /* Bytes of workspace mx_block_mse needs for a [rows, k] tensor when it is
  * asked for tensor_sums (at most 32 KiB); 0 for an invalid shape. */
 size_t mx_block_mse_workspace_size(int64_t rows, int64_t k);

@@ -40,7 +40,7 @@ EXPORTS = ("mx_quantize", "mx_dequantize", "mx_fakequant", "mx_block_mse",
            "mx_fakequant_mxfp8", "mx_nvfp4_workspace_size", "mx_quantize_nvfp4",
            "mx_dequantize_nvfp4", "mx_quantize_mbs", "mx_dequantize_mbs", "mx_quantize_multi",
            "mx_fakequant_multi", "mx_fakequant_nvfp4", "mx_fakequant_mbs", "mx_quantize_fused",
-           "mx_status_string", "mx_last_error_detail")
+           "mx_block_mse_noalloc", "mx_status_string", "mx_last_error_detail")
 
 _lib = None
 
@@ -60,6 +60,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mx_fakequant.argtypes = [p, i32, i64, i64, i32, p, p]
     lib.mx_block_mse.argtypes = [p, i32, p, p, i64, i64, p, p, p, ctypes.c_size_t, p]
     lib.mx_block_mse_workspace_size.argtypes = [i64, i64]
+    lib.mx_block_mse_noalloc.argtypes = [p, i32, p, p, i64, i64, p, p, p]
     lib.mx_block_mse_workspace_size.restype = ctypes.c_size_t
     lib.mx_quantize_mxfp8.argtypes = [p, i32, i64, i64, p, p, p]
     lib.mx_dequantize_mxfp8.argtypes = [p, p, i64, i64, i32, p, p]
@@ -79,7 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
               "mx_quantize_mxfp8", "mx_dequantize_mxfp8", "mx_fakequant_mxfp8",
               "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_quantize_mbs",
               "mx_dequantize_mbs", "mx_quantize_multi", "mx_fakequant_multi",
-              "mx_fakequant_nvfp4", "mx_fakequant_mbs", "mx_quantize_fused"):
+              "mx_fakequant_nvfp4", "mx_fakequant_mbs", "mx_quantize_fused",
+              "mx_block_mse_noalloc"):
         getattr(lib, f).restype = i32
     lib.mx_status_string.argtypes = [i32]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -111,6 +113,12 @@ def mx_block_mse(x, x_dtype, codes, scales, rows, k, block_mse, tensor_sums, wor
 
 def mx_block_mse_workspace_size(rows, k) -> int:
     return load_library().mx_block_mse_workspace_size(rows, k)
+
+
+def mx_block_mse_noalloc(x, x_dtype, codes, scales, rows, k, block_mse, tensor_sums,
+                         stream) -> int:
+    return load_library().mx_block_mse_noalloc(x, x_dtype, codes, scales, rows, k, block_mse,
+                                               tensor_sums, stream)
 
 
 def mx_quantize_mxfp8(x, x_dtype, rows, k, codes, scales, stream) -> int:

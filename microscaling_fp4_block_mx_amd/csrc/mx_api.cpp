@@ -151,6 +151,54 @@ mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype, const uint8_t *codes
                                      static_cast<hipStream_t>(stream)));
 }
 
+mx_status_t mx_block_mse_noalloc(const void *x, mx_dtype_t x_dtype, const uint8_t *codes,
+                                 const uint8_t *scales, int64_t rows, int64_t k, float *block_mse,
+                                 double *tensor_sums, void *stream) {
+  if (!dtype_ok(x_dtype)) return MX_ERR_DTYPE;
+  if (mx_status_t s = check_shape(rows, k)) return s;
+  if (!block_mse && !tensor_sums) return MX_ERR_NULL;
+  if (tensor_sums && (reinterpret_cast<uintptr_t>(tensor_sums) & 7u) != 0) return MX_ERR_ALIGN;
+  const int64_t n = rows * k;
+  if (rows > 0) {
+    if (!x || !codes || !scales) return MX_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGN;
+    if (block_mse && (reinterpret_cast<uintptr_t>(block_mse) & 3u) != 0) return MX_ERR_ALIGN;
+    const int64_t nx = n * elem_bytes(x_dtype);
+    const int64_t nbm = 4 * (n / kBlock);
+    if (block_mse && (overlap(block_mse, nbm, x, nx) || overlap(block_mse, nbm, codes, n / 2) ||
+                      overlap(block_mse, nbm, scales, n / kBlock)))
+      return MX_ERR_ALIAS;
+    if (tensor_sums && (overlap(tensor_sums, 16, x, nx) || overlap(tensor_sums, 16, codes, n / 2) ||
+                        overlap(tensor_sums, 16, scales, n / kBlock) ||
+                        (block_mse && overlap(tensor_sums, 16, block_mse, nbm))))
+      return MX_ERR_ALIAS;
+  } else if (!tensor_sums) {
+    return MX_OK;
+  }
+  double *partial = nullptr;
+  if (tensor_sums) {
+    // every shape's partial sums fit the fixed scratch (the launch's grid is
+    // capped); the check guards that bound
+    const size_t need = mxi_block_mse_partials(n / 8);
+    if (need > mxi_scratch_partials()) {
+      snprintf(g_detail, sizeof g_detail,
+               "block error needs %zu partial sums, the fixed scratch holds %zu", need,
+               mxi_scratch_partials());
+      return MX_ERR_WORKSPACE;
+    }
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                          : hipGetDevice(&dev);
+    if (e == hipSuccess) e = mxi_scratch_address(dev, &partial);
+    if (e != hipSuccess) return finish(e);
+  }
+  if (rows == 0)  // an empty tensor has zero error; still a device write
+    return finish(mxi_launch_block_mse(nullptr, 0, nullptr, nullptr, 0, nullptr, tensor_sums,
+                                       partial, static_cast<hipStream_t>(stream)));
+  return finish(mxi_launch_block_mse(x, x_dtype == MX_BF16, codes, scales, n / 8, block_mse,
+                                     tensor_sums, partial, static_cast<hipStream_t>(stream)));
+}
+
 mx_status_t mx_quantize_fused(const void *x, mx_dtype_t x_dtype, int64_t rows, int64_t k,
                               mx_scale_mode_t mode, uint8_t *codes, uint8_t *scales, void *y,
                               float *block_mse, double *tensor_sums, void *workspace,

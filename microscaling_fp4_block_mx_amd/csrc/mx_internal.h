@@ -19,6 +19,11 @@ size_t mxi_block_mse_partials(int64_t nitems);
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                                 const uint8_t *scales, int64_t nitems, float *block_mse,
                                 double *tensor_sums, double *partial, hipStream_t st);
+// The library's fixed device scratch for block-error partial sums: its size
+// in doubles (every launch's partials fit), and its address on device dev
+// (looked up once per device).
+size_t mxi_scratch_partials();
+hipError_t mxi_scratch_address(int dev, double **out);
 // Quantize plus, optionally, y (x's dtype), block MSE and tensor sums in
 // one pass; partial sums as mxi_launch_block_mse (same count).
 hipError_t mxi_launch_quantize_fused(const void *x, int bf16, int mode, int64_t nitems,

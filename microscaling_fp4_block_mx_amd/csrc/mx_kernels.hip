@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mx_internal.h"
 
 namespace mxk {
@@ -1449,6 +1451,48 @@ hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                        nitems > 0 ? (int)grid : 0, tensor_sums);
     return hipGetLastError();
   }
+  return hipSuccess;
+}
+
+// ---- fixed device scratch (block error without a workspace) -------------------
+//
+// The tensor sums of the block-error launch go through per-workgroup partial
+// sums: two doubles per workgroup, and that launch never uses more than
+// MX_MSE_GRID_CAP workgroups, so 2 * MX_MSE_GRID_CAP doubles (32 KiB) hold
+// them for every tensor size. mx_block_mse_noalloc keeps them here instead of
+// in a caller workspace. Each GPU the library runs on holds its own copy, at
+// its own address, until the process ends; every call on a GPU shares it. A
+// launch writes every partial slot it reads before the sum kernel reads it,
+// so nothing has to start at zero.
+constexpr size_t kScratchDoubles = 2 * (size_t)MX_MSE_GRID_CAP;
+static __device__ __align__(256) double scratch[kScratchDoubles];
+
+size_t mxi_scratch_partials() { return kScratchDoubles; }
+
+// Device address of `scratch` on device `dev`. In host code the array's name
+// is a host-side stand-in, not a device address, so it is looked up with
+// hipGetSymbolAddress, with that device current, once per device, and only
+// the looked-up address is handed to kernels.
+hipError_t mxi_scratch_address(int dev, double **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static double *addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<double *>(p);
+  }
+  *out = addr[dev];
   return hipSuccess;
 }
 

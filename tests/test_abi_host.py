@@ -130,6 +130,26 @@ def test_workspace(lib):
         mx.MX_ERR_WORKSPACE
 
 
+def test_block_mse_noalloc_validation(lib):
+    """The entry point without a workspace: the same argument checks as
+    mx_block_mse, all before any HIP call (the scratch address is looked up
+    only after them)."""
+    f = mx.mx_block_mse_noalloc
+    for rows, k in ((-1, 32), (1, 0), (4, 48), (1 << 40, 1 << 30)):
+        assert f(A, mx.MX_F32, B, C, rows, k, A + (64 << 30), None, None) == mx.MX_ERR_SHAPE
+    assert f(A, 5, B, C, 1, 32, None, W, None) == mx.MX_ERR_DTYPE
+    assert f(A, 0, B, C, 1, 32, None, None, None) == mx.MX_ERR_NULL      # no output asked
+    assert f(None, 0, B, C, 1, 32, A + 64, None, None) == mx.MX_ERR_NULL
+    assert f(A, 0, None, C, 1, 32, None, W, None) == mx.MX_ERR_NULL
+    assert f(A + 2, 0, B, C, 1, 32, None, W, None) == mx.MX_ERR_ALIGN
+    assert f(A, 0, B, C, 1, 32, A + (1 << 25) + 2, None, None) == mx.MX_ERR_ALIGN
+    assert f(A, 0, B, C, 1, 32, None, W + 4, None) == mx.MX_ERR_ALIGN
+    assert f(A, 0, B, C, 4, 64, A, None, None) == mx.MX_ERR_ALIAS        # block_mse over x
+    assert f(A, 0, B, C, 4, 64, None, B + 64, None) == mx.MX_ERR_ALIAS   # sums over codes
+    # empty tensor, block MSE only: nothing to write, nothing launched
+    assert f(None, 1, None, None, 0, 64, A, None, None) == mx.MX_OK
+
+
 def test_tensor_helpers_refuse_cpu_tensors(lib):
     import torch
     x = torch.zeros(2, 64, dtype=torch.bfloat16)
