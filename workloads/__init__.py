@@ -131,6 +131,29 @@ def llama32_3b_grouped(device, seed: int = 3):
     return a, b
 
 
+def llama32_3b_arena(device, seed: int = 3):
+    """The 196 matrices laid end to end in one contiguous bf16 buffer, layer
+    by layer in the order q, k, v, o, gate, up, down (the same values as
+    llama32_3b_matrix), and the (offset, out_features, in_features) of each.
+    Every matrix starts at a multiple of 3072 * 1024 elements and holds a
+    whole number of 32-element blocks per row, so the flat buffer is a run
+    of MX blocks in which no block straddles two matrices: quantizing it as
+    [n / 3072, 3072] gives every matrix's codes and scales at its offset."""
+    total = LLAMA32_3B_LAYERS * sum(o * i for _, o, i in LLAMA32_3B_LINEARS)
+    arena = torch.empty(total, dtype=torch.bfloat16, device=device)
+    layout = []
+    off = 0
+    for layer in range(LLAMA32_3B_LAYERS):
+        for which, (_, out_f, in_f) in enumerate(LLAMA32_3B_LINEARS):
+            m = llama32_3b_matrix(layer, which, device, seed)
+            arena[off:off + m.numel()].copy_(m.view(-1))
+            layout.append((off, out_f, in_f))
+            off += m.numel()
+            del m
+    assert off == total
+    return arena, layout
+
+
 def moe_weights(device, seed: int = 4):
     """(w13 [128, 3072, 4096], w2 [128, 4096, 1536]) bf16, one stream per expert."""
     w13 = torch.empty(MOE_W13_SHAPE, dtype=torch.bfloat16, device=device)
