@@ -1,29 +1,45 @@
 """Benchmark of the MXFP4 hot path on one MI355X.
 
-One step = every operation of the path over one batch of bf16 activations
-[8192 tokens, 4096 hidden] (Student-t(3) body, 20 outlier channels x50):
+One step = every operation of the path over one batch of the largest
+workload, the Llama-3.2-3B-shaped linear weights: 28 layers x {q, k, v, o,
+gate, up, down}, bf16 N(0, 0.02), the 196 matrices end to end in one buffer
+(2,818,572,288 elements, 5.6 GB), each matrix quantized along its input
+dimension. The operations, one launch each over the whole buffer:
   quantize (OCP scale), quantize (overflow-aware scale), dequantize -> bf16,
-  fused fake-quant (OCP), per-block MSE of the OCP result.
-Throughput = algorithmic bytes of the step / step time (inputs resident in
-HBM). Buffer sets rotate so the working set is >= 1 GiB and the 256 MB
-Infinity Cache cannot serve a step from the previous one.
+  fused fake-quant (OCP), per-block MSE of the OCP result (+ its tensor sums).
+Throughput = algorithmic bytes of the step / step time, inputs resident in
+HBM; the 5.6 GB input is 22x the 256 MB Infinity Cache, so no step is served
+from the previous one.
+
+Beside the step, the same run times (rotated buffer sets of >= 1.5 GiB, so
+cold): fake-quant of bf16 activations [8192, 4096] (Student-t(3), 20
+outlier channels x50) and the other formats and modes on that tensor;
+quantize (OCP and overflow-aware) of bf16 activations [16384, 8192]
+(Laplace + 0.1 % outliers); and reference streaming kernels with the
+quantize kernel's tiling on the step's buffer (a quantize-shaped skeleton
+with no arithmetic, a copy, a read and a write) that show what HBM allows.
 
 Prints ONE JSON line. --gpus N with N > 1 exits: this path runs on one GPU.
+--only step|beside runs one part alone (for profiling).
 
 --suite instead times each operation on the other workloads alone (fp32
 normal [1024, 4096]; the Llama-3.2-3B-shaped linear stack, per matrix, as one
-multi-tensor call and grouped by K; the 128-expert MoE weights; bf16 Laplace
-[16384, 8192] with sparse outliers), with per-launch HIP events (median, p10,
-p90), warm (cache-resident) and cold (rotated) figures where the tensor fits
-the cache, and for the small fp32 case the host-side single-launch latency
-and the per-launch time inside a replayed HIP graph. It prints one JSON line
+multi-tensor call, grouped by K and as one buffer; the 128-expert MoE
+weights; bf16 Laplace [16384, 8192] with sparse outliers), with per-launch
+HIP events (median, p10, p90), warm (cache-resident) and cold (rotated)
+figures where the tensor fits the cache, and for the small fp32 case the
+host-side single-launch latency, the per-launch time inside a replayed HIP
+graph, an empty launch and a copy of the same size. It prints one JSON line
 per measurement and a markdown table.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
+import math
 import os
+import subprocess
 import sys
 import time
 
@@ -32,8 +48,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "MXFP4 quantize/fake-quant GB/s (bf16 in) and % of HBM peak, 1× MI355X"
-WORKLOAD = ("bf16 activations 8192 tokens x 4096 hidden, Student-t(nu=3), "
-            "20 outlier channels x50 (seed 2)")
+WORKLOAD = ("Llama-3.2-3B-shaped linear weights, bf16 N(0,0.02), 28 layers x {q 3072x3072, "
+            "k 1024x3072, v 1024x3072, o 3072x3072, gate 8192x3072, up 8192x3072, down "
+            "3072x8192}: the 196 matrices end to end in one buffer, each quantized along its "
+            "input dimension (seed 3)")
+STEP_K = 3072            # the buffer is launched as [n / 3072, 3072]; blocks never straddle a matrix
+STEP_ELEMS = 2818572288  # 28 layers x 100,663,296
+C2_WORKLOAD = ("bf16 activations 8192 tokens x 4096 hidden, Student-t(nu=3), 20 outlier "
+               "channels x50 (seed 2)")
+C2_ELEMS = 8192 * 4096
+C5_WORKLOAD = "bf16 activations 16384 x 8192, Laplace(0,1), 0.1% outliers +-U(20,200) (seed 5)"
+C5_ELEMS = 16384 * 8192
 
 # algorithmic bytes per element (bf16 input): what each op must move
 BYTES_PER_ELEM = {
@@ -44,9 +69,11 @@ BYTES_PER_ELEM = {
     "block_mse": 2 + 0.5 + 1 / 32 + 4 / 32,  # x, codes, scales in; fp32/block out
 }
 OPS = list(BYTES_PER_ELEM)
-# measured beside the step (not part of it): the page-faithful
-# overflow-aware variants and fake-quant in the overflow-aware modes
+# measured beside the step on the Student-t activations: fake-quant (OCP),
+# the page-faithful overflow-aware variants, fake-quant in the
+# overflow-aware modes, and the other formats
 EXTRA_BYTES_PER_ELEM = {
+    "fakequant_ocp": 4.0,
     "quantize_oas_bits": 2 + 0.5 + 1 / 32,
     "quantize_oas_nf": 2 + 0.5 + 1 / 32,
     "fakequant_oas": 4.0,
@@ -62,21 +89,30 @@ EXTRA_BYTES_PER_ELEM = {
     "quantize_mbs": 2 + 0.5 + 1 / 16 + 1 / 128,
     "dequantize_mbs_bf16": 0.5 + 1 / 16 + 1 / 128 + 2,
     # one pass: codes + scales + y + block MSE + tensor sums (quantize,
-    # dequantize and block MSE of the step fused; x read once)
+    # dequantize and block MSE fused; x read once)
     "quantize_fused": 2 + 0.5 + 1 / 32 + 2 + 4 / 32,
     # fused fake-quant of the comparators (NVFP4 reads x twice)
     "fakequant_nvfp4": 2 + 2 + 2,
     "fakequant_mbs": 2 + 2,
 }
+# on the Laplace activations
+C5_BYTES_PER_ELEM = {"quantize_ocp": 2 + 0.5 + 1 / 32, "quantize_oas": 2 + 0.5 + 1 / 32}
+# reference kernels (bench_ceiling.hip) on the step's buffer
+CEILING_BYTES_PER_ELEM = {"quantize_shape": 2 + 0.5 + 1 / 32, "copy": 4.0, "read": 2.0,
+                          "write": 2.0}
 KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0>", "quantize_oas": "k_quantize<true, 1>",
              "dequantize_bf16": "k_dequantize<true>", "fakequant_ocp": "k_fakequant<true, 0>",
              "block_mse": "k_block_mse<true, true>"}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mx_bf16_8192x4096_hbm_traffic.md")
+PROFILE_STEM = {"step": "mx_llama32_3b_linears",
+                "beside": "mx_student_t_8192x4096_laplace_16384x8192"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", PROFILE_STEM["step"] + "_hbm_traffic.md")
 # launches per timing of the multi-GB suite workloads: warm-up, then timed
 # twice (per-launch events, then back to back)
 BIG_TIMED, BIG_WARM = 20, 3
 KERNEL_SRCS = (os.path.join(ROOT, "microscaling_fp4_block_mx_amd", "csrc", "mx_kernels.hip"),
                os.path.join(ROOT, "microscaling_fp4_block_mx_amd", "csrc", "mx_internal.h"))
+CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
+CEILING_LIB = os.path.join(ROOT, "libmxceiling.so")
 
 
 def kernel_code_hash() -> str:
@@ -95,9 +131,9 @@ def kernel_code_hash() -> str:
 
 
 def measured_traffic(op):
-    """HBM bytes per launch of op's kernel from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, or None if that summary was taken on
-    different kernel code than the one built here."""
+    """HBM bytes per launch of op's kernel on the step's buffer from the
+    committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None if that
+    summary was taken on different kernel code than the one built here."""
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
         h = kernel_code_hash()
@@ -112,64 +148,236 @@ def measured_traffic(op):
     return None
 
 
+def build_ceiling(verbose: bool = False) -> str:
+    """Compile the reference streaming kernels (bench_ceiling.hip) for gfx950
+    into libmxceiling.so beside this file."""
+    from microscaling_fp4_block_mx_amd import build as mxbuild
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [mxbuild.hipcc(), f"--offload-arch={mxbuild.ARCH}", "-O3", "-std=c++17", "-fPIC",
+           "-shared", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-command-line-argument", "-o", tmp, CEILING_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libmxceiling.so")
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
+
+
+def ceiling_lib() -> ctypes.CDLL:
+    if not os.path.exists(CEILING_LIB):
+        build_ceiling()
+    lib = ctypes.CDLL(CEILING_LIB)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.mxc_quantize_shape.argtypes = [p, i64, p, p, p]
+    lib.mxc_copy.argtypes = [p, p, i64, p]
+    lib.mxc_read.argtypes = [p, i64, p, p]
+    lib.mxc_write.argtypes = [p, i64, p]
+    lib.mxc_empty.argtypes = [p]
+    for f in ("mxc_quantize_shape", "mxc_copy", "mxc_read", "mxc_write", "mxc_empty"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate-gib", type=float, default=1.5,
-                    help="minimum working set across rotated buffer sets")
+                    help="minimum working set across rotated buffer sets (the activations "
+                         "beside the step)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=("step", "beside"),
+                    help="run only the step (with its reference kernels) or only the "
+                         "measurements beside it; no quality or CPU baseline")
     ap.add_argument("--suite", action="store_true",
                     help="time the operations on the other workloads instead of the step")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from the rocprofv3 csv files in DIR "
-                         "(trace_*, fetch_*, write_*, suite_*) and exit; needs no GPU")
+                         "(trace_*, fetch_*, write_*, sq_*, suite_*) and exit; needs no GPU")
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.summarize_profiles:
-        return summarize_profiles(args.summarize_profiles)
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this benchmark measures one GPU only; every MX block is independent, "
-              "so the path shards by rows with no exchange. "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def _ok(mx, st):
+    if st != mx.MX_OK:
+        raise RuntimeError(mx.mx_status_string(st) + " " + mx.mx_last_error_detail())
 
+
+def _timed_launches(fn, m, stream):
+    """Mean time (ms) of m calls of fn(i) issued back to back between two
+    events on `stream`."""
+    import torch
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for i in range(m):
+        fn(i)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    return a0.elapsed_time(a1) / m
+
+
+def _row(nbytes, ms, **extra):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": int(nbytes), **extra}
+
+
+def run_step(args, dev, stream):
+    """The step on the Llama-3.2-3B linear buffer, each op alone, and the
+    reference kernels on the same buffer."""
+    import torch
+
+    import microscaling_fp4_block_mx_amd as mx
+    import workloads
+
+    sh = stream.cuda_stream
+    arena, _ = workloads.llama32_3b_arena(dev)
+    x = arena.view(-1, STEP_K)
+    R_, K_ = x.shape
+    n = x.numel()
+    assert n == STEP_ELEMS
+    b = dict(c_ocp=torch.empty((R_, K_ // 2), dtype=torch.uint8, device=dev),
+             s_ocp=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
+             c_oas=torch.empty((R_, K_ // 2), dtype=torch.uint8, device=dev),
+             s_oas=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
+             y_dq=torch.empty_like(x), y_fq=torch.empty_like(x),
+             bm=torch.empty((R_, K_ // 32), dtype=torch.float32, device=dev))
+    sums = torch.empty(2, dtype=torch.float64, device=dev)
+    ws_bytes = mx.mx_block_mse_workspace_size(R_, K_)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    xp = x.data_ptr()
+
+    def run(op):
+        if op == "quantize_ocp":
+            st = mx.mx_quantize(xp, mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP, b["c_ocp"].data_ptr(),
+                                b["s_ocp"].data_ptr(), sh)
+        elif op == "quantize_oas":
+            st = mx.mx_quantize(xp, mx.MX_BF16, R_, K_, mx.MX_SCALE_OAS, b["c_oas"].data_ptr(),
+                                b["s_oas"].data_ptr(), sh)
+        elif op == "dequantize_bf16":
+            st = mx.mx_dequantize(b["c_ocp"].data_ptr(), b["s_ocp"].data_ptr(), R_, K_,
+                                  mx.MX_BF16, b["y_dq"].data_ptr(), sh)
+        elif op == "fakequant_ocp":
+            st = mx.mx_fakequant(xp, mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP, b["y_fq"].data_ptr(),
+                                 sh)
+        else:
+            st = mx.mx_block_mse(xp, mx.MX_BF16, b["c_ocp"].data_ptr(), b["s_ocp"].data_ptr(),
+                                 R_, K_, b["bm"].data_ptr(), sums.data_ptr(), ws.data_ptr(),
+                                 ws_bytes, sh)
+        _ok(mx, st)
+
+    def step():
+        for op in OPS:
+            run(op)
+
+    for _ in range(max(1, args.warmup)):  # also produces the codes dequantize / block MSE read
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps between two events on the launch stream
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / K
+
+    # each op alone: m launches back to back between two events on the same
+    # stream (the average launch duration of its kernel; block MSE is its
+    # kernel plus the one-workgroup tensor-sum kernel)
+    m = max(K, 10)
+    op_ms = {op: _timed_launches(lambda i, op=op: run(op), m, stream) for op in OPS}
+
+    # reference kernels with the quantize kernel's tiling, on the same buffer
+    cl = ceiling_lib()
+    nit = n // 8
+    sink = torch.empty(196608, dtype=torch.int32, device=dev)
+    ceil_fn = {
+        "quantize_shape": lambda i: cl.mxc_quantize_shape(xp, nit, b["c_oas"].data_ptr(),
+                                                          b["s_oas"].data_ptr(), sh),
+        "copy": lambda i: cl.mxc_copy(xp, b["y_fq"].data_ptr(), nit, sh),
+        "read": lambda i: cl.mxc_read(xp, nit, sink.data_ptr(), sh),
+        "write": lambda i: cl.mxc_write(b["y_fq"].data_ptr(), nit, sh),
+    }
+    ceil_ms = {}
+    for name, fn in ceil_fn.items():
+        fn(0)
+        torch.cuda.synchronize()
+        ceil_ms[name] = _timed_launches(fn, m, stream)
+    ceilings = {name: _row(CEILING_BYTES_PER_ELEM[name] * n, ceil_ms[name]) for name in ceil_fn}
+    ceilings["quantize_ocp_vs_quantize_shape"] = round(ceil_ms["quantize_shape"]
+                                                       / op_ms["quantize_ocp"], 4)
+    ceilings["fakequant_ocp_vs_copy"] = round(ceil_ms["copy"] / op_ms["fakequant_ocp"], 4)
+    ceilings["kernels"] = "bench_ceiling.hip (k_ceiling_*): the quantize kernel's tiling, no format arithmetic"
+
+    bytes_op = {op: BYTES_PER_ELEM[op] * n for op in OPS}
+    bytes_step = sum(bytes_op.values())
+    breakdown = {op: _row(bytes_op[op], op_ms[op]) for op in OPS}
+    dom = max(OPS, key=lambda o: op_ms[o])
+    dom_gbs = bytes_op[dom] / (op_ms[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": KERNEL_OF[dom], "op": dom, "achieved": round(dom_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom),
+                "bytes_per_launch": int(bytes_op[dom]),
+                "avg_launch_us": round(op_ms[dom] * 1e3, 2)}
+
+    # quality of the step's outputs (outside the timed region)
+    run("block_mse")
+    torch.cuda.synchronize()
+    sse, ssq = sums.tolist()
+    quality = {"mxfp4_ocp": {"mse": sse / n, "qsnr_db": round(10 * math.log10(ssq / sse), 4)}}
+    run("quantize_oas")  # the reference kernels wrote over the overflow-aware codes
+    _ok(mx, mx.mx_block_mse(xp, mx.MX_BF16, b["c_oas"].data_ptr(), b["s_oas"].data_ptr(), R_, K_,
+                            None, sums.data_ptr(), ws.data_ptr(), ws_bytes, sh))
+    torch.cuda.synchronize()
+    sse2, ssq2 = sums.tolist()
+    quality["mxfp4_oas"] = {"mse": sse2 / n,
+                            "qsnr_db": round(10 * math.log10(ssq2 / sse2), 4)}
+    del b, ws, sink
+    torch.cuda.empty_cache()
+    return dict(x=x, n=n, ms_per_step=ms_per_step, wall=wall, bytes_step=bytes_step,
+                breakdown=breakdown, roofline=roofline, ceilings=ceilings, quality=quality,
+                copy_us=ceil_ms["copy"] * 1e3)
+
+
+def run_beside(args, dev, stream):
+    """Fake-quant and the other formats on the Student-t activations, and
+    quantize (both modes) on the Laplace activations; rotated buffer sets,
+    each op m launches back to back."""
     import numpy as np
     import torch
 
     import microscaling_fp4_block_mx_amd as mx
     import workloads
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    if args.suite:
-        return suite(args, dev)
-    torch.cuda.set_device(dev)
-    mx.load_library()
+    sh = stream.cuda_stream
+    K = args.steps
+    out = {}
 
+    # -- Student-t activations [8192, 4096]
     x_host = workloads.bf16_student_t_outlier_channels(2)
     R_, K_ = x_host.shape
     n = x_host.numel()
     per_set = n * (2 + 0.5 * 2 + 2 / 32 + 2 + 2 + 4 / 32 + 1 + 1 / 32 + 1 / 16 + 1 / 16 + 1 / 128)
     n_sets = max(2, int(np.ceil(args.rotate_gib * 2 ** 30 / per_set)))
-
     x0 = x_host.to(dev)
     sets = []
     for _ in range(n_sets):
         sets.append(dict(
             x=x0.clone(),
-            c_ocp=torch.empty((R_, K_ // 2), dtype=torch.uint8, device=dev),
-            s_ocp=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
-            c_oas=torch.empty((R_, K_ // 2), dtype=torch.uint8, device=dev),
-            s_oas=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
-            y_dq=torch.empty_like(x0),
-            y_fq=torch.empty_like(x0),
+            c=torch.empty((R_, K_ // 2), dtype=torch.uint8, device=dev),
+            s=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
+            y_dq=torch.empty_like(x0), y_fq=torch.empty_like(x0),
             bm=torch.empty((R_, K_ // 32), dtype=torch.float32, device=dev),
             c8=torch.empty((R_, K_), dtype=torch.uint8, device=dev),
             s8=torch.empty((R_, K_ // 32), dtype=torch.uint8, device=dev),
@@ -184,200 +392,192 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     wsnv_bytes = mx.mx_nvfp4_workspace_size(R_, K_)
     wsnv = torch.empty(wsnv_bytes, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
 
     def run(op, b):
-        if op == "quantize_ocp":
-            st = mx.mx_quantize(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP,
-                                b["c_ocp"].data_ptr(), b["s_ocp"].data_ptr(), sh)
-        elif op == "quantize_oas":
-            st = mx.mx_quantize(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mx.MX_SCALE_OAS,
-                                b["c_oas"].data_ptr(), b["s_oas"].data_ptr(), sh)
-        elif op == "dequantize_bf16":
-            st = mx.mx_dequantize(b["c_ocp"].data_ptr(), b["s_ocp"].data_ptr(), R_, K_,
-                                  mx.MX_BF16, b["y_dq"].data_ptr(), sh)
-        elif op == "fakequant_ocp":
-            st = mx.mx_fakequant(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP,
-                                 b["y_fq"].data_ptr(), sh)
+        xp = b["x"].data_ptr()
+        if op in ("fakequant_ocp", "fakequant_oas", "fakequant_oas_nf"):
+            mode = {"fakequant_ocp": mx.MX_SCALE_OCP, "fakequant_oas": mx.MX_SCALE_OAS,
+                    "fakequant_oas_nf": mx.MX_SCALE_OAS_NF}[op]
+            st = mx.mx_fakequant(xp, mx.MX_BF16, R_, K_, mode, b["y_fq"].data_ptr(), sh)
         elif op in ("quantize_oas_bits", "quantize_oas_nf"):
             mode = mx.MX_SCALE_OAS_BITS if op.endswith("bits") else mx.MX_SCALE_OAS_NF
-            st = mx.mx_quantize(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mode,
-                                b["c_oas"].data_ptr(), b["s_oas"].data_ptr(), sh)
+            st = mx.mx_quantize(xp, mx.MX_BF16, R_, K_, mode, b["c"].data_ptr(),
+                                b["s"].data_ptr(), sh)
         elif op == "quantize_mxfp8":
-            st = mx.mx_quantize_mxfp8(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["c8"].data_ptr(),
+            st = mx.mx_quantize_mxfp8(xp, mx.MX_BF16, R_, K_, b["c8"].data_ptr(),
                                       b["s8"].data_ptr(), sh)
         elif op == "dequantize_mxfp8_bf16":
             st = mx.mx_dequantize_mxfp8(b["c8"].data_ptr(), b["s8"].data_ptr(), R_, K_, mx.MX_BF16,
                                         b["y_dq"].data_ptr(), sh)
         elif op == "fakequant_mxfp8":
-            st = mx.mx_fakequant_mxfp8(b["x"].data_ptr(), mx.MX_BF16, R_, K_,
-                                       b["y_fq"].data_ptr(), sh)
+            st = mx.mx_fakequant_mxfp8(xp, mx.MX_BF16, R_, K_, b["y_fq"].data_ptr(), sh)
         elif op == "quantize_nvfp4":
-            st = mx.mx_quantize_nvfp4(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["c_oas"].data_ptr(),
+            st = mx.mx_quantize_nvfp4(xp, mx.MX_BF16, R_, K_, b["c"].data_ptr(),
                                       b["bnv"].data_ptr(), b["tnv"].data_ptr(), wsnv.data_ptr(),
                                       wsnv_bytes, sh)
         elif op == "dequantize_nvfp4_bf16":
-            st = mx.mx_dequantize_nvfp4(b["c_oas"].data_ptr(), b["bnv"].data_ptr(),
+            st = mx.mx_dequantize_nvfp4(b["c"].data_ptr(), b["bnv"].data_ptr(),
                                         b["tnv"].data_ptr(), R_, K_, mx.MX_BF16,
                                         b["y_dq"].data_ptr(), sh)
-        elif op == "quantize_mbs":  # codes land in c_oas; dequantize_mbs_bf16 runs next
-            st = mx.mx_quantize_mbs(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["c_oas"].data_ptr(),
+        elif op == "quantize_mbs":  # codes land in c; dequantize_mbs_bf16 runs next
+            st = mx.mx_quantize_mbs(xp, mx.MX_BF16, R_, K_, b["c"].data_ptr(),
                                     b["smb"].data_ptr(), b["mmb"].data_ptr(), sh)
         elif op == "dequantize_mbs_bf16":
-            st = mx.mx_dequantize_mbs(b["c_oas"].data_ptr(), b["smb"].data_ptr(),
+            st = mx.mx_dequantize_mbs(b["c"].data_ptr(), b["smb"].data_ptr(),
                                       b["mmb"].data_ptr(), R_, K_, mx.MX_BF16,
                                       b["y_dq"].data_ptr(), sh)
         elif op == "quantize_fused":
-            st = mx.mx_quantize_fused(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP,
-                                      b["c_oas"].data_ptr(), b["s_oas"].data_ptr(),
+            st = mx.mx_quantize_fused(xp, mx.MX_BF16, R_, K_, mx.MX_SCALE_OCP,
+                                      b["c"].data_ptr(), b["s"].data_ptr(),
                                       b["y_fq"].data_ptr(), b["bm"].data_ptr(), sums.data_ptr(),
                                       ws.data_ptr(), ws_bytes, sh)
         elif op == "fakequant_nvfp4":
-            st = mx.mx_fakequant_nvfp4(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["y_fq"].data_ptr(),
+            st = mx.mx_fakequant_nvfp4(xp, mx.MX_BF16, R_, K_, b["y_fq"].data_ptr(),
                                        wsnv.data_ptr(), wsnv_bytes, sh)
         elif op == "fakequant_mbs":
-            st = mx.mx_fakequant_mbs(b["x"].data_ptr(), mx.MX_BF16, R_, K_, b["y_fq"].data_ptr(), sh)
-        elif op in ("fakequant_oas", "fakequant_oas_nf"):
-            mode = mx.MX_SCALE_OAS if op == "fakequant_oas" else mx.MX_SCALE_OAS_NF
-            st = mx.mx_fakequant(b["x"].data_ptr(), mx.MX_BF16, R_, K_, mode,
-                                 b["y_fq"].data_ptr(), sh)
+            st = mx.mx_fakequant_mbs(xp, mx.MX_BF16, R_, K_, b["y_fq"].data_ptr(), sh)
         else:
-            st = mx.mx_block_mse(b["x"].data_ptr(), mx.MX_BF16, b["c_ocp"].data_ptr(),
-                                 b["s_ocp"].data_ptr(), R_, K_, b["bm"].data_ptr(),
-                                 sums.data_ptr(), ws.data_ptr(), ws_bytes, sh)
-        if st != mx.MX_OK:
-            raise RuntimeError(mx.mx_status_string(st))
+            raise KeyError(op)
+        _ok(mx, st)
 
-    def step(i):
-        b = sets[i % n_sets]
-        for op in OPS:
-            run(op, b)
-
-    # warmup (also produces the codes each set's dequantize / block_mse read)
-    for i in range(max(args.warmup, n_sets)):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: K whole steps between two events on the launch stream
-    K = args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(K):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / K
-
-    # per-kernel launch time: each op alone, back to back over the rotating
-    # sets, K * n_sets launches between two events on the same stream
-    for i in range(n_sets):  # codes for the MXFP8 / NVFP4 dequantize
-        run("quantize_mxfp8", sets[i])
-        run("quantize_nvfp4", sets[i])
-    op_ms = {}
-    for op in OPS + list(EXTRA_BYTES_PER_ELEM):
-        for i in range(n_sets):
-            run(op, sets[i])
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        m = max(K, 2 * n_sets)
-        a0.record(stream)
-        for i in range(m):
-            run(op, sets[i % n_sets])
-        a1.record(stream)
-        torch.cuda.synchronize()
-        op_ms[op] = a0.elapsed_time(a1) / m
-
-    # reference: a plain device copy of the same bf16 tensor (read n*2 bytes,
-    # write n*2 bytes) timed the same way; it is also the calibration kernel
-    # for the HBM traffic counters
-    for i in range(n_sets):
-        sets[i]["y_fq"].copy_(sets[i]["x"])
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     m = max(K, 2 * n_sets)
-    c0.record(stream)
-    for i in range(m):
-        sets[i % n_sets]["y_fq"].copy_(sets[i % n_sets]["x"])
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_us = c0.elapsed_time(c1) * 1e3 / m
-
-    bytes_op = {op: BYTES_PER_ELEM[op] * n for op in OPS}
-    bytes_step = sum(bytes_op.values())
-    value = bytes_step / (ms_per_step * 1e-3) / 1e9
-
-    breakdown = {}
-    for op in OPS:
-        gbs = bytes_op[op] / (op_ms[op] * 1e-3) / 1e9
-        breakdown[op] = {"us": round(op_ms[op] * 1e3, 2), "GB/s": round(gbs, 1),
-                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                         "bytes": int(bytes_op[op])}
-    extra = {}
     for op, bpe in EXTRA_BYTES_PER_ELEM.items():
-        gbs = bpe * n / (op_ms[op] * 1e-3) / 1e9
-        extra[op] = {"us": round(op_ms[op] * 1e3, 2), "GB/s": round(gbs, 1),
-                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(bpe * n)}
-    dom = max(OPS, key=lambda o: op_ms[o])
-    dom_gbs = bytes_op[dom] / (op_ms[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom),
-                "bytes_per_launch": int(bytes_op[dom]),
-                "avg_launch_us": round(op_ms[dom] * 1e3, 2)}
+        for i in range(n_sets):  # warm the code paths; produce the codes the decoders read
+            run(op, sets[i])
+        torch.cuda.synchronize()
+        ms = _timed_launches(lambda i, op=op: run(op, sets[i % n_sets]), m, stream)
+        out[f"{op} [8192, 4096]"] = _row(bpe * n, ms, workload=C2_WORKLOAD,
+                                         cache=f"cold ({n_sets} rotated sets)")
+    # the reference copy of the same tensor, timed the same way (and the
+    # counter calibration kernel of this part's profiles)
+    cl = ceiling_lib()
+    ms = _timed_launches(lambda i: cl.mxc_copy(sets[i % n_sets]["x"].data_ptr(),
+                                               sets[i % n_sets]["y_fq"].data_ptr(), n // 8, sh),
+                         m, stream)
+    out["reference_copy [8192, 4096]"] = _row(4.0 * n, ms, workload=C2_WORKLOAD,
+                                              cache=f"cold ({n_sets} rotated sets)")
+    del sets, ws, wsnv
+    torch.cuda.empty_cache()
 
-    # quantization quality of the bench tensor per scale mode (outside the
-    # timed region): tensor MSE and QSNR from the block-error kernel
-    quality = {}
-    b = sets[0]
+    # -- Laplace activations [16384, 8192]: quantize in both modes
+    x5 = workloads.bf16_laplace_sparse_outliers(5).to(dev)
+    R5, K5 = x5.shape
+    n5 = x5.numel()
+    per_set = n5 * (2 + 0.5 + 1 / 32)
+    n_sets = max(2, int(np.ceil(args.rotate_gib * 2 ** 30 / per_set)))
+    sets = [dict(x=x5.clone(), c=torch.empty((R5, K5 // 2), dtype=torch.uint8, device=dev),
+                 s=torch.empty((R5, K5 // 32), dtype=torch.uint8, device=dev))
+            for _ in range(n_sets)]
+    del x5
+    m = max(K, 2 * n_sets)
+    for op, mode in (("quantize_ocp", mx.MX_SCALE_OCP), ("quantize_oas", mx.MX_SCALE_OAS)):
+        def q5(i, mode=mode):
+            b = sets[i % n_sets]
+            _ok(mx, mx.mx_quantize(b["x"].data_ptr(), mx.MX_BF16, R5, K5, mode,
+                                   b["c"].data_ptr(), b["s"].data_ptr(), sh))
+        for i in range(n_sets):
+            q5(i)
+        torch.cuda.synchronize()
+        out[f"{op} [16384, 8192]"] = _row(C5_BYTES_PER_ELEM[op] * n5, _timed_launches(q5, m, stream),
+                                          workload=C5_WORKLOAD,
+                                          cache=f"cold ({n_sets} rotated sets)")
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def quality_beside(dev):
+    """Tensor MSE and QSNR of every format and MXFP4 mode on the Student-t
+    activations, and of both step modes on the Laplace activations."""
+    import numpy as np
+    import torch
+
+    import microscaling_fp4_block_mx_amd as mx
+    import workloads
+
+    q = {}
+    x = workloads.bf16_student_t_outlier_channels(2).to(dev)
+    n = x.numel()
     for mode in mx.MODES:
-        c, sc = mx.quantize(b["x"], mode)
-        _, sums = mx.block_mse(b["x"], c, sc, per_block=False)
+        c, sc = mx.quantize(x, mode)
+        _, sums = mx.block_mse(x, c, sc, per_block=False)
         sse, ssq = sums.tolist()
-        quality["mxfp4_" + mode] = {"mse": sse / n, "qsnr_db": round(10 * np.log10(ssq / sse), 4)}
-    y8 = mx.fakequant_mxfp8(b["x"]).float()
-    xf = b["x"].float()
-    sse8 = float(((xf - y8).double() ** 2).sum())
-    quality["mxfp8"] = {"mse": sse8 / n,
-                        "qsnr_db": round(10 * np.log10(float((xf.double() ** 2).sum()) / sse8), 4)}
-    cn, bn, tn = mx.quantize_nvfp4(b["x"])
-    ynv = mx.dequantize_nvfp4(cn, bn, tn, torch.float32)
-    ssenv = float(((xf - ynv).double() ** 2).sum())
-    quality["nvfp4"] = {"mse": ssenv / n,
-                        "qsnr_db": round(10 * np.log10(float((xf.double() ** 2).sum()) / ssenv), 4)}
-    cm, sm, mm = mx.quantize_mbs(b["x"])
-    ymb = mx.dequantize_mbs(cm, sm, mm, torch.float32)
-    ssemb = float(((xf - ymb).double() ** 2).sum())
-    quality["mbs_static"] = {"mse": ssemb / n,
-                             "qsnr_db": round(10 * np.log10(float((xf.double() ** 2).sum()) / ssemb), 4)}
-    del y8, xf, ynv, ymb
+        q["mxfp4_" + mode] = {"mse": sse / n, "qsnr_db": round(10 * np.log10(ssq / sse), 4)}
+    xf = x.float()
+    e = float((xf.double() ** 2).sum())
+    for name, y in (("mxfp8", mx.fakequant_mxfp8(x).float()),
+                    ("nvfp4", mx.dequantize_nvfp4(*mx.quantize_nvfp4(x), torch.float32)),
+                    ("mbs_static", mx.dequantize_mbs(*mx.quantize_mbs(x), torch.float32))):
+        sse = float(((xf - y).double() ** 2).sum())
+        q[name] = {"mse": sse / n, "qsnr_db": round(10 * np.log10(e / sse), 4)}
+    out = {"student_t_8192x4096": q}
+    x5 = workloads.bf16_laplace_sparse_outliers(5).to(dev)
+    q5 = {}
+    for mode in ("ocp", "oas"):
+        c, sc = mx.quantize(x5, mode)
+        _, sums = mx.block_mse(x5, c, sc, per_block=False)
+        sse, ssq = sums.tolist()
+        q5["mxfp4_" + mode] = {"mse": sse / x5.numel(), "qsnr_db": round(10 * np.log10(ssq / sse), 4)}
+    out["laplace_16384x8192"] = q5
+    return out
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x_host, args.cpu_seconds, sets[0]["x"])
 
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOAD, "rows": R_, "k": K_, "step": OPS,
-                   "bytes_per_step": int(bytes_step),
-                   "elements_per_s": round(n / (ms_per_step * 1e-3), 1),
-                   "rotation_sets": n_sets,
-                   "working_set_gib": round(n_sets * per_set / 2 ** 30, 2),
-                   "wall_s_timed": round(wall, 4),
-                   "device_copy_reference": {"bytes": 4 * n, "us": round(copy_us, 2),
-                                             "GB/s": round(4 * n / copy_us / 1e3, 1)}},
-        "breakdown": breakdown,
-        "beside_the_step": extra,
-        "quality": quality,
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "env": {"device": torch.cuda.get_device_name(dev), "torch": torch.__version__,
-                "hip": torch.version.hip},
-    }
+def main():
+    args = parse()
+    if args.summarize_profiles:
+        return summarize_profiles(args.summarize_profiles)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this benchmark measures one GPU only; every MX block is independent, "
+              "so the path shards by rows with no exchange. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import microscaling_fp4_block_mx_amd as mx
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    if args.suite:
+        return suite(args, dev)
+    torch.cuda.set_device(dev)
+    mx.load_library()
+    stream = torch.cuda.current_stream(dev)
+
+    step = run_step(args, dev, stream) if args.only in (None, "step") else None
+    beside = run_beside(args, dev, stream) if args.only in (None, "beside") else None
+    quality = cpu = None
+    if args.only is None:
+        quality = {"llama32_3b_linears": step["quality"], **quality_beside(dev)}
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(step["x"], args.cpu_seconds)
+
+    out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if step:
+        n = step["n"]
+        out.update({
+            "value": round(step["bytes_step"] / (step["ms_per_step"] * 1e-3) / 1e9, 1),
+            "ms_per_step": round(step["ms_per_step"], 5),
+            "config": {"workload": WORKLOAD, "rows": n // STEP_K, "k": STEP_K, "elements": n,
+                       "step": OPS, "launches_per_step": len(OPS) + 1,
+                       "bytes_per_step": int(step["bytes_step"]),
+                       "elements_per_s": round(n / (step["ms_per_step"] * 1e-3), 1),
+                       "wall_s_timed": round(step["wall"], 4),
+                       "cache": "input 22x the 256 MB Infinity Cache; no rotation needed"},
+            "breakdown": step["breakdown"],
+            "ceilings": step["ceilings"],
+            "roofline": step["roofline"],
+        })
+    if beside:
+        out["beside_the_step"] = beside
+    if quality:
+        out["quality"] = quality
+    if cpu:
+        out["cpu_baseline"] = cpu
+    out["env"] = {"device": torch.cuda.get_device_name(dev), "torch": torch.__version__,
+                  "hip": torch.version.hip}
     print(json.dumps(out), flush=True)
 
 
@@ -391,13 +591,14 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(x_host, target_s, x_dev):
+def cpu_baseline(x_dev, target_s):
     """The oracle as it stands, on the host cores, over a bounded sample of
-    the same workload (leading rows), running the same step: first on every
-    core, then on one thread over a smaller sample. The first sample's oracle
-    outputs are also compared with the library's on the same rows (codes and
-    scales of both modes, dequantize, fake-quant bit for bit; block MSE and
-    tensor sums to a relative 1e-6)."""
+    the step's buffer (its leading rows of 3072, i.e. the first matrices),
+    running the same step: first on every core, then on one thread over a
+    smaller sample. The first sample's oracle outputs are also compared with
+    the library's on the same rows (codes and scales of both modes,
+    dequantize, fake-quant bit for bit; block MSE and tensor sums to a
+    relative 1e-6)."""
     import numpy as np
     import torch
 
@@ -407,8 +608,15 @@ def cpu_baseline(x_host, target_s, x_dev):
 
     oracle.build(force=not os.path.exists(os.path.join(ROOT, "oracle", "libmxref.so")))
     cores = max(1, len(os.sched_getaffinity(0)))
-    xs_full = workloads.to_bf16_bits(x_host)
-    k = xs_full.shape[1]
+    k = x_dev.shape[1]
+    max_rows = min(x_dev.shape[0], 131072)  # at most 403 M elements on the host
+    cache = {}
+
+    def host_rows(rows):
+        if cache.get("rows", 0) < rows:
+            cache["x"] = workloads.to_bf16_bits(x_dev[:rows])
+            cache["rows"] = rows
+        return np.ascontiguousarray(cache["x"][:rows])
 
     def step(xs, threads):
         c, s = oracle.quantize(xs, "ocp", threads=threads)
@@ -419,7 +627,7 @@ def cpu_baseline(x_host, target_s, x_dev):
         return c, s, c2, s2, y, f, bm
 
     def timed(rows, threads, budget):
-        xs = np.ascontiguousarray(xs_full[:rows])
+        xs = host_rows(rows)
         done, t0, out = 0, time.perf_counter(), None
         while True:
             out = step(xs, threads)
@@ -427,11 +635,11 @@ def cpu_baseline(x_host, target_s, x_dev):
             el = time.perf_counter() - t0
             if el >= budget:
                 return rows, done, el, out
-            if done == 1 and rows < xs_full.shape[0]:  # size the sample to land near the budget
-                grow = int(min(xs_full.shape[0], rows * max(1.0, budget / max(el, 1e-3) / 3)))
+            if done == 1 and rows < max_rows:  # size the sample to land near the budget
+                grow = int(min(max_rows, rows * max(1.0, budget / max(el, 1e-3) / 3)))
                 if grow > rows:
                     rows = grow
-                    xs = np.ascontiguousarray(xs_full[:rows])
+                    xs = host_rows(rows)
                     done, t0 = 0, time.perf_counter()
 
     bpe = sum(BYTES_PER_ELEM[o] for o in OPS)
@@ -458,8 +666,8 @@ def cpu_baseline(x_host, target_s, x_dev):
                                    and abs(sse - wsse) <= 1e-6 * wsse and abs(ssq - wssq) <= 1e-6 * wssq),
     }
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} step(s) over the first {rows} rows x {k} of the same tensor "
-                      f"({el:.1f} s, {cores} threads)",
+            "sample": f"{done} step(s) over the first {rows} rows x {k} of the same buffer "
+                      f"({rows * k} elements, the first matrices; {el:.1f} s, {cores} threads)",
             "single_thread": {"value": round(gbs1, 3), "unit": "GB/s",
                               "sample": f"{done1} step(s) over the first {rows1} rows ({el1:.1f} s)"},
             "cpu_model": cpu_model(),
@@ -574,6 +782,16 @@ def suite(args, dev):
                cache=f"cold ({len(sets)} rotated sets)")
         report(W1, op, bpe * n, _launch_stats(lambda i, fn=fn: fn(0), n_timed, n_warm, stream),
                cache="warm (one set)")
+    # the floor of a launch of this size: an empty kernel, and a copy of the
+    # fp32 input with the quantize kernel's tiling (16 MiB read + 16 MiB written)
+    cl = ceiling_lib()
+    report(W1, "empty launch (one workgroup)", 0, _launch_stats(lambda i: cl.mxc_empty(sh),
+                                                                 n_timed, n_warm, stream),
+           cache="-")
+    report(W1, "reference copy of the fp32 input (bench_ceiling.hip)", 8 * n,
+           _launch_stats(lambda i: cl.mxc_copy(sets[i % len(sets)]["x"].data_ptr(),
+                                               sets[i % len(sets)]["y"].data_ptr(), n // 4, sh),
+                         n_timed, n_warm, stream), cache=f"cold ({len(sets)} rotated sets)")
     # single-launch latency: host time of one quantize call until it has run
     lat = []
     for i in range(n_timed):
@@ -714,6 +932,19 @@ def suite(args, dev):
            _launch_stats(grouped, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     del a, b, ca, sa, cb, sb, mats
     torch.cuda.empty_cache()
+    # the same 196 matrices end to end in one buffer: one launch (the step's form)
+    arena, _ = workloads.llama32_3b_arena(dev)
+    xa = arena.view(-1, STEP_K)
+    ca = torch.empty((xa.shape[0], STEP_K // 2), dtype=torch.uint8, device=dev)
+    sa = torch.empty((xa.shape[0], STEP_K // 32), dtype=torch.uint8, device=dev)
+
+    def one_buffer(_):
+        ok(mx.mx_quantize(xa.data_ptr(), mx.MX_BF16, xa.shape[0], STEP_K, mx.MX_SCALE_OCP,
+                          ca.data_ptr(), sa.data_ptr(), sh))
+    report(WL, "quantize_ocp (one launch over the 196 matrices end to end)", bytes_q,
+           _launch_stats(one_buffer, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    del arena, xa, ca, sa
+    torch.cuda.empty_cache()
 
     # -- MoE experts bf16 N(0, 0.02): quantize, then dequantize -> bf16
     w13, w2 = workloads.moe_weights(dev)
@@ -765,9 +996,9 @@ def suite(args, dev):
 
 # ---- rocprofv3 summaries ------------------------------------------------------
 
-# Algorithmic bytes per element of each kernel on the bf16 bench tensor, by
-# the name rocprofv3 prints (NVFP4 quantize is two kernels: the tensor-maximum
-# pass reads x, the block pass reads it again and writes codes and scales).
+# Algorithmic bytes per element of each kernel (bf16 in), by the name
+# rocprofv3 prints. NVFP4 quantize is two kernels: the tensor-maximum pass
+# reads x, the block pass reads it again and writes codes and scales.
 KERNEL_BYTES_PER_ELEM = {
     "k_quantize<true, 0>": BYTES_PER_ELEM["quantize_ocp"],
     "k_quantize<true, 1>": BYTES_PER_ELEM["quantize_oas"],
@@ -789,22 +1020,35 @@ KERNEL_BYTES_PER_ELEM = {
     "k_quantize_mbs<true, true>": EXTRA_BYTES_PER_ELEM["fakequant_mbs"],
     "k_dequantize_mbs<true>": EXTRA_BYTES_PER_ELEM["dequantize_mbs_bf16"],
     "k_quantize_fused<true, 0, true>": EXTRA_BYTES_PER_ELEM["quantize_fused"],
-    "__amd_rocclr_copyBuffer": 4.0,  # the reference copy: 2 B in + 2 B out
+    "k_ceiling_quantize_shape": CEILING_BYTES_PER_ELEM["quantize_shape"],
+    "k_ceiling_copy": CEILING_BYTES_PER_ELEM["copy"],
+    "k_ceiling_read": CEILING_BYTES_PER_ELEM["read"],
+    "k_ceiling_write": CEILING_BYTES_PER_ELEM["write"],
 }
-BENCH_ELEMS = 8192 * 4096
-
+CALIBRATION_KERNEL = "k_ceiling_copy"  # reads and writes 2 bytes per element, known exactly
+# The two parts of bench.py that are profiled, each on its own (--only):
+# elements a dispatch covers, from its grid (workgroups). In the part beside
+# the step only the Laplace quantize launches run 16,384 workgroups.
+PHASES = {
+    "step": {"title": "Llama-3.2-3B linears, 196 matrices end to end, bf16 [917504, 3072] "
+                      "(bench.py step)",
+             "elems": lambda grid: STEP_ELEMS},
+    "beside": {"title": "bf16 Student-t activations [8192, 4096] and Laplace activations "
+                        "[16384, 8192] (bench.py, beside the step)",
+               "elems": lambda grid: C5_ELEMS if grid == 16384 else C2_ELEMS},
+}
 PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT -o trace -- \\\n"
-             "    python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT -o fetch -- \\\n"
-             "    python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT -o write -- \\\n"
-             "    python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT -o {p}_trace -- \\\n"
+             "    python3 $R/bench.py --only {p} --steps 20 --warmup 5",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT -o {p}_fetch -- \\\n"
+             "    python3 $R/bench.py --only {p} --steps 3 --warmup 2",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT -o {p}_write -- \\\n"
+             "    python3 $R/bench.py --only {p} --steps 3 --warmup 2",
+    "sq": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR \\\n"
+          "    SQ_INSTS_LDS SQ_BUSY_CYCLES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $OUT \\\n"
+          "    -o {p}_sq -- python3 $R/bench.py --only {p} --steps 3 --warmup 2",
     "suite": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT -o suite -- \\\n"
              "    python3 $R/bench.py --suite",
-    "sq": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR \\\n"
-          "    SQ_INSTS_LDS SQ_BUSY_CYCLES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $OUT -o sq -- \\\n"
-          "    python3 $R/bench.py --steps 3 --warmup 2 --no-cpu-baseline",
 }
 # VALU issue model for the instruction-mix summary: a wave64 VALU instruction
 # holds its 16-lane SIMD for 4 cycles; 256 CUs x 4 SIMDs at 2.4 GHz
@@ -818,138 +1062,147 @@ def _kernel_short(name: str) -> str:
     for k in KERNEL_BYTES_PER_ELEM:
         if k in name:
             return k
-    return name.split("(")[0].replace("void ", "").replace("mxk::", "")
+    return name.split("(")[0].replace("void ", "").replace("mxk::", "").replace(
+        "(anonymous namespace)::", "")
+
+
+def _dispatch_groups(path: str, elems):
+    """(kernel, workgroups, elements) -> list of durations in us, from a
+    rocprofv3 kernel-trace csv."""
+    import collections
+    import csv
+    groups = collections.OrderedDict()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = _kernel_short(r["Kernel_Name"])
+            grid = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault((k, grid, elems(grid)), []).append(dur)
+    return groups
+
+
+def _counter_groups(path: str, elems):
+    """(kernel, workgroups, elements) -> {counter: mean value per dispatch}."""
+    import collections
+    import csv
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = _kernel_short(r["Kernel_Name"])
+            grid = int(r["Grid_Size"]) // max(1, int(r.get("Workgroup_Size", 256) or 256))
+            agg[(k, grid, elems(grid))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {key: {c: sum(v) / len(v) for c, v in d.items()} for key, d in agg.items()}
 
 
 def summarize_profiles(d: str, out_dir: str = os.path.join(ROOT, "profiles")) -> None:
-    """The three profiles/ summaries from rocprofv3 csv output in d: the
-    bench step's kernel trace, its HBM traffic (FETCH_SIZE and WRITE_SIZE,
-    calibrated on the reference copy), and the suite's kernel trace (when d
-    holds one), written to out_dir."""
-    import collections
-    import csv
-
+    """The profiles/ summaries from rocprofv3 csv output in d: per profiled
+    part of bench.py (the step; beside the step) its kernel trace, its HBM
+    traffic (FETCH_SIZE and WRITE_SIZE, calibrated on the reference copy
+    kernel) and its instruction mix (SQ counters), and the suite's kernel
+    trace, for whichever raw files d holds."""
     h = kernel_code_hash()
     code = ("Kernel code (`csrc/mx_kernels.hip` + `csrc/mx_internal.h`, comments and whitespace "
             f"stripped; `bench.kernel_code_hash`) sha256 prefix: `{h}`\n")
-    alg = {k: int(v * BENCH_ELEMS) for k, v in KERNEL_BYTES_PER_ELEM.items()}
     pct = lambda b, us: b / us / 1e3 / HBM_PEAK_GBS * 100  # noqa: E731
-
-    # kernel trace of the bench run
-    out = ["# Kernel trace: MXFP4 hot-path kernels, bf16 8192x4096 (bench.py step)\n",
-           PROFILE_HOW + "\n", "```\n" + PROFILE_CMDS["trace"] + "\n```\n",
-           "Step kernels: `k_quantize<true, 0>` (OCP), `k_quantize<true, 1>` (OAS), "
-           "`k_dequantize<true>`, `k_fakequant<true, 0>`, `k_block_mse<true, true>` + "
-           "`k_sum_partials`; the rest run beside the step (modes 2/3 = OAS_BITS/OAS_NF, `*8` = "
-           "MXFP8, `*_nv` / `k_absmax_partials` = NVFP4, `*_mbs` = MBS-Static; a `true` second "
-           "template argument of those two is the fused fake-quant; `k_quantize_fused` = quantize "
-           "+ dequantized output + block MSE + tensor sums in one pass). bf16 in, 8192x4096.\n",
-           code,
-           "| kernel | calls | avg us | min us | max us | algorithmic bytes | GB/s at avg "
-           "| % of 8 TB/s |", "|---|---|---|---|---|---|---|---|"]
-    with open(os.path.join(d, "trace_kernel_stats.csv")) as f:
-        for r in csv.DictReader(f):
-            k = _kernel_short(r["Name"])
-            if k not in alg and k != "k_sum_partials":
-                continue
-            avg = float(r["AverageNs"]) / 1e3
-            b = alg.get(k)
-            out.append(f"| `{k}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-                       f"{float(r['MaxNs']) / 1e3:.2f} | {b if b else '-'} | "
-                       f"{f'{b / avg / 1e3:.0f}' if b else '-'} | "
-                       f"{f'{pct(b, avg):.1f}' if b else '-'} |")
-    with open(os.path.join(out_dir, "mx_bf16_8192x4096_kernel_trace.md"), "w") as f:
-        f.write("\n".join(out) + "\n")
-
-    # HBM traffic: the reference copy (64 MiB read + 64 MiB written, the
-    # largest copyBuffer dispatch) calibrates both counters
-    copy = "__amd_rocclr_copyBuffer"
-    with open(os.path.join(d, "write_counter_collection.csv")) as f:
-        wr = [r for r in csv.DictReader(f) if _kernel_short(r["Kernel_Name"]) == copy]
-    ref_grid = max(wr, key=lambda r: float(r["Counter_Value"]))["Grid_Size"]
-    per = {}
-    for fn, ctr in (("fetch_counter_collection.csv", "FETCH_SIZE"),
-                    ("write_counter_collection.csv", "WRITE_SIZE")):
-        agg = collections.defaultdict(list)
-        with open(os.path.join(d, fn)) as f:
-            for r in csv.DictReader(f):
-                k = _kernel_short(r["Kernel_Name"])
-                if k == copy and r["Grid_Size"] != ref_grid:
+    for p, ph in PHASES.items():
+        stem = os.path.join(out_dir, PROFILE_STEM[p])
+        cmd = {k: v.format(p=p) for k, v in PROFILE_CMDS.items()}
+        trace = os.path.join(d, f"{p}_trace_kernel_trace.csv")
+        avg_us = {}
+        if os.path.exists(trace):
+            out = [f"# Kernel trace: {ph['title']}\n", PROFILE_HOW + "\n",
+                   "```\n" + cmd["trace"] + "\n```\n", code,
+                   "Per-dispatch GPU times from the trace, grouped by kernel and grid "
+                   "(workgroups); algorithmic bytes = the op's bytes per element x the elements "
+                   "one launch covers. `k_ceiling_*` are the reference kernels of "
+                   "`bench_ceiling.hip` (the quantize kernel's tiling, no format arithmetic).\n",
+                   "| kernel | workgroups | elements | dispatches | avg us | min us | max us "
+                   "| algorithmic bytes | GB/s at avg | % of 8 TB/s |",
+                   "|---|---|---|---|---|---|---|---|---|---|"]
+            for (k, grid, n), v in _dispatch_groups(trace, ph["elems"]).items():
+                avg = sum(v) / len(v)
+                avg_us[(k, grid)] = avg
+                bpe = KERNEL_BYTES_PER_ELEM.get(k)
+                if bpe is None and k != "k_sum_partials":
                     continue
-                agg[k].append(float(r["Counter_Value"]))
-        per[ctr] = {k: sum(v) / len(v) for k, v in agg.items()}
-    cal_f = 65536.0 / per["FETCH_SIZE"][copy]
-    cal_w = 65536.0 / per["WRITE_SIZE"][copy]
-    out = ["# HBM traffic: MXFP4 hot-path kernels, bf16 8192x4096 (bench.py step)\n",
-           PROFILE_HOW + "\n",
-           "```\n" + PROFILE_CMDS["fetch"] + "\n" + PROFILE_CMDS["write"] + "\n```\n", code,
-           f"Calibration: the device copy bench.py runs (`{copy}`, 64 MiB read + 64 MiB written "
-           f"per dispatch) reads FETCH_SIZE {per['FETCH_SIZE'][copy]:.1f} KiB and WRITE_SIZE "
-           f"{per['WRITE_SIZE'][copy]:.1f} KiB, so FETCH_SIZE is scaled by {cal_f:.4f} and "
-           f"WRITE_SIZE by {cal_w:.4f}.\n",
-           "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled traffic bytes | algorithmic bytes "
-           "| traffic / algorithmic |", "|---|---|---|---|---|---|"]
-    machine = []
-    for k in KERNEL_BYTES_PER_ELEM:
-        if k not in per["FETCH_SIZE"] or k not in per["WRITE_SIZE"]:
-            continue
-        fk, wk = per["FETCH_SIZE"][k], per["WRITE_SIZE"][k]
-        t = (fk * cal_f + wk * cal_w) * 1024
-        out.append(f"| `{k}` | {fk:.1f} | {wk:.1f} | {t:.0f} | {alg[k]} | {t / alg[k]:.4f} |")
-        machine.append(f"traffic_bytes {k} {t:.0f}")
-    out += ["\nMachine-readable (read by bench.py while the source hash matches):\n",
-            "```\nkernel_code_sha256_prefix " + h] + machine + ["```"]
-    with open(os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
-        f.write("\n".join(out) + "\n")
-    if os.path.exists(os.path.join(d, "suite_kernel_trace.csv")):
-        _summarize_suite(os.path.join(d, "suite_kernel_trace.csv"), code, out_dir)
-    if os.path.exists(os.path.join(d, "sq_counter_collection.csv")):
-        _summarize_instruction_mix(d, code, out_dir)
+                b = int(bpe * n) if bpe else None
+                out.append(f"| `{k}` | {grid} | {n if bpe else '-'} | {len(v)} | {avg:.2f} | "
+                           f"{min(v):.2f} | {max(v):.2f} | {b if b else '-'} | "
+                           f"{f'{b / avg / 1e3:.0f}' if b else '-'} | "
+                           f"{f'{pct(b, avg):.1f}' if b else '-'} |")
+            with open(stem + "_kernel_trace.md", "w") as f:
+                f.write("\n".join(out) + "\n")
+        fetch = os.path.join(d, f"{p}_fetch_counter_collection.csv")
+        write = os.path.join(d, f"{p}_write_counter_collection.csv")
+        if os.path.exists(fetch) and os.path.exists(write):
+            cf = _counter_groups(fetch, ph["elems"])
+            cw = _counter_groups(write, ph["elems"])
+            cal = [key for key in cf if key[0] == CALIBRATION_KERNEL and key in cw]
+            ref = max(cal, key=lambda key: key[2])
+            ref_kib = ref[2] * 2.0 / 1024  # the copy reads and writes 2 bytes per element
+            cal_f = ref_kib / cf[ref]["FETCH_SIZE"]
+            cal_w = ref_kib / cw[ref]["WRITE_SIZE"]
+            out = [f"# HBM traffic: {ph['title']}\n", PROFILE_HOW + "\n",
+                   "```\n" + cmd["fetch"] + "\n" + cmd["write"] + "\n```\n", code,
+                   f"Calibration: the reference copy kernel (`{CALIBRATION_KERNEL}`, "
+                   f"{ref[2] * 2} bytes read and as many written per dispatch) reads FETCH_SIZE "
+                   f"{cf[ref]['FETCH_SIZE']:.1f} KiB and WRITE_SIZE {cw[ref]['WRITE_SIZE']:.1f} "
+                   f"KiB, so FETCH_SIZE is scaled by {cal_f:.4f} and WRITE_SIZE by {cal_w:.4f}.\n",
+                   "| kernel | workgroups | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled traffic bytes "
+                   "| algorithmic bytes | traffic / algorithmic |",
+                   "|---|---|---|---|---|---|---|"]
+            machine = []
+            for key in cf:
+                k, grid, n = key
+                bpe = KERNEL_BYTES_PER_ELEM.get(k)
+                if bpe is None or key not in cw:
+                    continue
+                fk, wk = cf[key]["FETCH_SIZE"], cw[key]["WRITE_SIZE"]
+                t = (fk * cal_f + wk * cal_w) * 1024
+                alg = bpe * n
+                out.append(f"| `{k}` | {grid} | {fk:.1f} | {wk:.1f} | {t:.0f} | {alg:.0f} | "
+                           f"{t / alg:.4f} |")
+                machine.append(f"traffic_bytes {k} {t:.0f}")
+            out += ["\nMachine-readable (read by bench.py while the source hash matches):\n",
+                    "```\nkernel_code_sha256_prefix " + h] + machine + ["```"]
+            with open(stem + "_hbm_traffic.md", "w") as f:
+                f.write("\n".join(out) + "\n")
+        sq = os.path.join(d, f"{p}_sq_counter_collection.csv")
+        if os.path.exists(sq):
+            _summarize_instruction_mix(sq, avg_us, ph, cmd["sq"], code, stem)
+    suite_csv = os.path.join(d, "suite_kernel_trace.csv")
+    if os.path.exists(suite_csv):
+        _summarize_suite(suite_csv, code, out_dir)
 
 
-def _summarize_instruction_mix(d: str, code: str, out_dir: str) -> None:
+def _summarize_instruction_mix(path: str, avg_us: dict, ph: dict, cmd: str, code: str,
+                               stem: str) -> None:
     """Instructions per wave-item (one item = 8 elements per lane, 64 lanes)
     of each kernel from the SQ counters, and the time its VALU instructions
     take at full issue rate next to the kernel's traced duration."""
-    import collections
-    import csv
-
-    agg = collections.defaultdict(lambda: collections.defaultdict(list))
-    with open(os.path.join(d, "sq_counter_collection.csv")) as f:
-        for r in csv.DictReader(f):
-            agg[_kernel_short(r["Kernel_Name"])][r["Counter_Name"]].append(
-                float(r["Counter_Value"]))
-    avg_us = {}
-    trace = os.path.join(d, "trace_kernel_stats.csv")
-    if os.path.exists(trace):
-        with open(trace) as f:
-            for r in csv.DictReader(f):
-                avg_us[_kernel_short(r["Name"])] = float(r["AverageNs"]) / 1e3
-    wave_items = BENCH_ELEMS / (8 * 64)
-    out = ["# Instruction mix: MXFP4 hot-path kernels, bf16 8192x4096 (bench.py step)\n",
-           PROFILE_HOW + "\n", "```\n" + PROFILE_CMDS["sq"] + "\n```\n", code,
+    out = [f"# Instruction mix: {ph['title']}\n", PROFILE_HOW + "\n", "```\n" + cmd + "\n```\n",
+           code,
            "Counts are chip totals per dispatch (SQ_WAVES equals the waves launched), "
-           "averaged over the dispatches of each kernel, per wave-item: one item is 8 "
-           "elements in each of a wave's 64 lanes, so the bench tensor is "
-           f"{int(wave_items)} wave-items. VALU issue time = SQ_INSTS_VALU x {VALU_CYCLES} "
-           f"cycles / ({SIMDS} SIMDs x {CLOCK_GHZ} GHz), the time the kernel's vector "
-           "instructions need if every SIMD issued one each cycle slot with nothing else "
+           "averaged over the dispatches of each kernel and grid, per wave-item: one item is 8 "
+           "elements in each of a wave's 64 lanes. VALU issue time = SQ_INSTS_VALU x "
+           f"{VALU_CYCLES} cycles / ({SIMDS} SIMDs x {CLOCK_GHZ} GHz), the time the kernel's "
+           "vector instructions need if every SIMD issued one each cycle slot with nothing else "
            "in the way; kernel time from the kernel trace of the same code.\n",
-           "| kernel | waves | VALU / wave-item | SALU / wave-item | VMEM rd / wave-item "
-           "| VMEM wr / wave-item | LDS / wave-item | VALU issue us | kernel us | VALU issue / "
-           "kernel |", "|---|---|---|---|---|---|---|---|---|---|"]
-    for k in KERNEL_BYTES_PER_ELEM:
-        if k not in agg or k == "__amd_rocclr_copyBuffer":
+           "| kernel | workgroups | waves | VALU / wave-item | SALU / wave-item | VMEM rd / "
+           "wave-item | VMEM wr / wave-item | LDS / wave-item | VALU issue us | kernel us | "
+           "VALU issue / kernel |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (k, grid, n), c in _counter_groups(path, ph["elems"]).items():
+        if k not in KERNEL_BYTES_PER_ELEM:
             continue
-        c = {n: sum(v) / len(v) for n, v in agg[k].items()}
-        per = lambda n: c.get(n, 0.0) / wave_items  # noqa: E731
+        wave_items = n / (8 * 64)
+        per = lambda name: c.get(name, 0.0) / wave_items  # noqa: E731
         valu_us = c.get("SQ_INSTS_VALU", 0.0) * VALU_CYCLES / (SIMDS * CLOCK_GHZ * 1e3)
-        t = avg_us.get(k)
-        out.append(f"| `{k}` | {int(c.get('SQ_WAVES', 0))} | {per('SQ_INSTS_VALU'):.1f} | "
+        t = avg_us.get((k, grid))
+        out.append(f"| `{k}` | {grid} | {int(c.get('SQ_WAVES', 0))} | {per('SQ_INSTS_VALU'):.1f} | "
                    f"{per('SQ_INSTS_SALU'):.1f} | {per('SQ_INSTS_VMEM_RD'):.2f} | "
                    f"{per('SQ_INSTS_VMEM_WR'):.2f} | {per('SQ_INSTS_LDS'):.2f} | {valu_us:.2f} | "
                    f"{f'{t:.2f}' if t else '-'} | {f'{valu_us / t:.2f}' if t else '-'} |")
-    with open(os.path.join(out_dir, "mx_bf16_8192x4096_instruction_mix.md"), "w") as f:
+    with open(stem + "_instruction_mix.md", "w") as f:
         f.write("\n".join(out) + "\n")
 
 
@@ -971,6 +1224,8 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
                   3072: ("gate/up [8192, 3072] and down [3072, 8192]", 8192 * 3072)}
 
     def bytes_for(kernel, n, f32):
+        if kernel == "k_ceiling_copy":  # the fp32 input copied: 4 bytes in, 4 out
+            return n * 8.0
         if kernel.startswith(("k_quantize<", "k_dequantize<")):
             return n * (4.53125 if f32 else 2.53125)
         if kernel.startswith("k_block_mse<"):
@@ -986,20 +1241,29 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
                and int(r["Grid_Size_X"]) // 256 in (196608, 98304))
     groups = collections.OrderedDict()
     seen196 = 0
+    seen_c5 = collections.Counter()
+    per_timing = 10 + 2 * 100  # dispatches of one _launch_stats call at the suite's defaults
     for r in rows[:last + 1]:
-        k = short(r["Kernel_Name"])
+        k = short(r["Kernel_Name"]).replace("(anonymous namespace)::", "")
         if not k.startswith("k_"):
             continue
-        grid = int(r["Grid_Size_X"]) // 256
+        grid = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         if k.startswith("k_multi"):
             key = ("MULTI", k, None)
         elif k == "k_sum_partials":
             key = ("tensor-sum pass of block MSE (all workloads)", k, None)
+        elif k.startswith("k_ceiling"):
+            key = ("fp32 normal [1024, 4096]: reference kernels", k, c1)
         elif "<false" in k:
             key = ("fp32 normal [1024, 4096]", k, c1)
         elif grid == 16384 or k.startswith("k_block_mse"):
-            key = ("bf16 Laplace [16384, 8192]", k, c5)
+            # each op is timed cold (rotated sets), then warm (one set): runs
+            # of per_timing dispatches alternate
+            cold = (seen_c5[k] // per_timing) % 2 == 0
+            seen_c5[k] += 1
+            key = ("bf16 Laplace [16384, 8192], " + ("cold (rotated sets)" if cold
+                                                     else "warm (one set, cache-resident)"), k, c5)
         elif grid in per_matrix and k.startswith("k_quantize<"):
             key = ("Llama-3.2-3B per-matrix launches: " + per_matrix[grid][0], k,
                    per_matrix[grid][1])
@@ -1009,8 +1273,13 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
             key = ("MoE w2 [128x4096, 1536]", k, m2)
         elif grid == 196608 and k.startswith("k_quantize<"):
             seen196 += 1
-            key = (("Llama-3.2-3B grouped by K: K=3072 [688128, 3072]", k, l3072)
-                   if seen196 <= passes else ("MoE w13 [128x3072, 4096]", k, m13))
+            if seen196 <= passes:
+                key = ("Llama-3.2-3B grouped by K: K=3072 [688128, 3072]", k, l3072)
+            elif seen196 <= 2 * passes:
+                key = ("Llama-3.2-3B, 196 matrices end to end: one launch [917504, 3072]", k,
+                       STEP_ELEMS)
+            else:
+                key = ("MoE w13 [128x3072, 4096]", k, m13)
         elif grid == 196608 and k.startswith("k_dequantize<"):
             key = ("MOEDQ", k, None)
         elif grid == 196608:
@@ -1028,11 +1297,14 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
            "Durations are the GPU's own per-dispatch times from the trace (under the profiler the "
            "host-side event figures of the small fp32 case are inflated by per-dispatch overhead; "
            "these are not). Launches are attributed to their workload by grid size; the K=3072 "
-           "Llama group and the MoE w13 tensor both run 196,608 workgroups and are told apart by "
-           f"dispatch order (the suite runs the Llama launches first, {passes} of each), and the "
-           "MoE dequantize launches (both 196,608 workgroups) alternate w13, w2. Per-matrix Llama "
-           "launches are grouped by shape. The suite's QSNR pass, which runs after the timed "
-           "launches, is left out.\n",
+           "Llama group, the 196 Llama matrices as one buffer and the MoE w13 tensor all run "
+           "196,608 workgroups and are told apart by dispatch order (the suite runs them in that "
+           f"order, {passes} of each), and the MoE dequantize launches (both 196,608 workgroups) "
+           "alternate w13, w2. The Laplace launches are split into the cold (rotated sets) and "
+           f"warm (one set) timings by dispatch order ({per_timing} dispatches each). "
+           "Per-matrix Llama launches are grouped by shape. The fp32 rows mix cold, warm, "
+           "single-launch and graph-replayed dispatches. The suite's QSNR pass, which runs after "
+           "the timed launches, is left out.\n",
            "| workload | kernel | dispatches | avg us | min us | max us | algorithmic bytes "
            "| GB/s at avg | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
     for (wl, k, n), v in groups.items():

@@ -133,7 +133,8 @@ mx_status_t mx_fakequant(const void *x, mx_dtype_t dtype, int64_t rows,
  * both in fp64. Either output may be NULL (both NULL is MX_ERR_NULL).
  * block_mse must be 4-byte aligned and tensor_sums 8-byte aligned. Both
  * outputs are deterministic: the tensor sums are taken in a fixed order
- * (per-workgroup partial sums, then one ordered reduction), never with atomics.
+ * (per-workgroup partial sums, then ordered sums of them in one or two
+ * levels), never with atomics.
  * workspace: device scratch for those partial sums, needed only when
  * tensor_sums != NULL; at least mx_block_mse_workspace_size(rows, k) bytes,
  * 8-byte aligned, not overlapping any argument. Its contents on entry do not
@@ -150,16 +151,19 @@ mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype,
 /* mx_block_mse without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc. The partial sums behind tensor_sums live
- * in a fixed 32 KiB device array inside the library (2 x 2048 doubles; the
- * block-error launch never uses more than 2048 workgroups, so every shape
- * fits; a larger need would be MX_ERR_WORKSPACE). Each GPU holds its own copy
- * from the first call on that GPU (the device of `stream`, or the current
- * device for the null stream) until the process ends. The call allocates
- * nothing; outputs equal mx_block_mse's bit for bit. Every call on a GPU
- * shares that GPU's array, which keeps the last call's contents (nothing in
- * it needs clearing: a call writes each partial before reading it): calls
- * that may run at the same time on one GPU (unordered streams) race and can
- * return wrong tensor_sums, so order them on one stream. A call with
+ * in a fixed 32 KiB device array inside the library (2 x 2048 doubles); the
+ * launch caps its grid at 2048 workgroups so that every shape fits (larger
+ * tensors loop over their tiles, which is slower than mx_block_mse on
+ * tensors above ~1.7e7 elements). Each GPU holds its own copy from the first
+ * call on that GPU (the device of `stream`, or the current device for the
+ * null stream) until the process ends. The call allocates nothing.
+ * block_mse equals mx_block_mse's bit for bit; tensor_sums too up to
+ * 16,777,216 elements (the same grid), and to a relative 1e-6 above (the
+ * partial sums fall on other workgroups). Every call on a GPU shares that
+ * GPU's array, which keeps the last call's contents (nothing in it needs
+ * clearing: a call writes each partial before reading it): calls that may
+ * run at the same time on one GPU (unordered streams) race and can return
+ * wrong tensor_sums, so order them on one stream. A call with
  * tensor_sums == NULL does not use the array. Other arguments, alignment,
  * aliasing and error conventions as mx_block_mse. */
 mx_status_t mx_block_mse_noalloc(const void *x, mx_dtype_t x_dtype,
@@ -167,8 +171,12 @@ mx_status_t mx_block_mse_noalloc(const void *x, mx_dtype_t x_dtype,
                                  int64_t rows, int64_t k, float *block_mse,
                                  double *tensor_sums, void *stream);
 
-/* Bytes of workspace mx_block_mse needs for a [rows, k] tensor when it is
- * asked for tensor_sums (at most 32 KiB); 0 for an invalid shape. */
+/* Bytes of workspace mx_block_mse (and mx_quantize_fused) needs for a
+ * [rows, k] tensor when asked for tensor_sums: 16 bytes per 4096 elements
+ * (one partial pair per workgroup), plus 16 bytes per 2048 of those pairs
+ * when there are more than 2048 (a second summing level); e.g. 131,136
+ * bytes for 8192 x 4096 and 11,015,424 bytes for 2.8e9 elements (0.4 % of a
+ * bf16 input). 0 for an invalid shape. */
 size_t mx_block_mse_workspace_size(int64_t rows, int64_t k);
 
 /* One pass over x for the QAT / calibration loop that quantizes and then

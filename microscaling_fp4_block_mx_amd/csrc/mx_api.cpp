@@ -126,6 +126,7 @@ mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype, const uint8_t *codes
     if (!tensor_sums) return MX_OK;
     return finish(mxi_launch_block_mse(nullptr, 0, nullptr, nullptr, 0, nullptr, tensor_sums,
                                        static_cast<double *>(workspace),
+                                       (int64_t)(workspace_bytes / sizeof(double)),
                                        static_cast<hipStream_t>(stream)));
   }
   if (!x || !codes || !scales) return MX_ERR_NULL;
@@ -148,6 +149,7 @@ mx_status_t mx_block_mse(const void *x, mx_dtype_t x_dtype, const uint8_t *codes
   }
   return finish(mxi_launch_block_mse(x, x_dtype == MX_BF16, codes, scales, n / 8, block_mse,
                                      tensor_sums, static_cast<double *>(workspace),
+                                     (int64_t)(workspace_bytes / sizeof(double)),
                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -177,15 +179,8 @@ mx_status_t mx_block_mse_noalloc(const void *x, mx_dtype_t x_dtype, const uint8_
   }
   double *partial = nullptr;
   if (tensor_sums) {
-    // every shape's partial sums fit the fixed scratch (the launch's grid is
-    // capped); the check guards that bound
-    const size_t need = mxi_block_mse_partials(n / 8);
-    if (need > mxi_scratch_partials()) {
-      snprintf(g_detail, sizeof g_detail,
-               "block error needs %zu partial sums, the fixed scratch holds %zu", need,
-               mxi_scratch_partials());
-      return MX_ERR_WORKSPACE;
-    }
+    // every shape's partial sums fit the fixed scratch: with less space than
+    // its fastest grid needs, the launch caps its grid at one sum group
     int dev = 0;
     hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
                           : hipGetDevice(&dev);
@@ -194,9 +189,11 @@ mx_status_t mx_block_mse_noalloc(const void *x, mx_dtype_t x_dtype, const uint8_
   }
   if (rows == 0)  // an empty tensor has zero error; still a device write
     return finish(mxi_launch_block_mse(nullptr, 0, nullptr, nullptr, 0, nullptr, tensor_sums,
-                                       partial, static_cast<hipStream_t>(stream)));
+                                       partial, (int64_t)mxi_scratch_partials(),
+                                       static_cast<hipStream_t>(stream)));
   return finish(mxi_launch_block_mse(x, x_dtype == MX_BF16, codes, scales, n / 8, block_mse,
-                                     tensor_sums, partial, static_cast<hipStream_t>(stream)));
+                                     tensor_sums, partial, (int64_t)mxi_scratch_partials(),
+                                     static_cast<hipStream_t>(stream)));
 }
 
 mx_status_t mx_quantize_fused(const void *x, mx_dtype_t x_dtype, int64_t rows, int64_t k,
@@ -217,6 +214,7 @@ mx_status_t mx_quantize_fused(const void *x, mx_dtype_t x_dtype, int64_t rows, i
     if (overlap(tensor_sums, 16, workspace, (int64_t)workspace_bytes)) return MX_ERR_ALIAS;
     return finish(mxi_launch_quantize_fused(nullptr, 0, 0, 0, nullptr, nullptr, nullptr, nullptr,
                                             tensor_sums, static_cast<double *>(workspace),
+                                            (int64_t)(workspace_bytes / sizeof(double)),
                                             static_cast<hipStream_t>(stream)));
   }
   if (!x || !codes || !scales) return MX_ERR_NULL;
@@ -243,6 +241,7 @@ mx_status_t mx_quantize_fused(const void *x, mx_dtype_t x_dtype, int64_t rows, i
   return finish(mxi_launch_quantize_fused(x, x_dtype == MX_BF16, mode, n / 8, codes, scales, y,
                                           block_mse, tensor_sums,
                                           tensor_sums ? static_cast<double *>(workspace) : nullptr,
+                                          (int64_t)(workspace_bytes / sizeof(double)),
                                           static_cast<hipStream_t>(stream)));
 }
 

@@ -14,11 +14,16 @@ hipError_t mxi_launch_fakequant(const void *x, int bf16, int mode, int64_t nitem
                                 hipStream_t st);
 hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, int bf16,
                                  int64_t nitems, void *y, hipStream_t st);
-// Number of fp64 partial sums the block-error launch writes for nitems.
+// Doubles of partial-sum space an error launch over nitems items needs for
+// its fastest grid (the workspace size).
 size_t mxi_block_mse_partials(int64_t nitems);
+// partial: the partial-sum space (partial_space doubles; a smaller space
+// than mxi_block_mse_partials caps the grid, still correct as long as it
+// holds the 2 * 2048 doubles of one sum group).
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                                 const uint8_t *scales, int64_t nitems, float *block_mse,
-                                double *tensor_sums, double *partial, hipStream_t st);
+                                double *tensor_sums, double *partial, int64_t partial_space,
+                                hipStream_t st);
 // The library's fixed device scratch for block-error partial sums: its size
 // in doubles (every launch's partials fit), and its address on device dev
 // (looked up once per device).
@@ -28,7 +33,8 @@ hipError_t mxi_scratch_address(int dev, double **out);
 // one pass; partial sums as mxi_launch_block_mse (same count).
 hipError_t mxi_launch_quantize_fused(const void *x, int bf16, int mode, int64_t nitems,
                                      uint8_t *codes, uint8_t *scales, void *y, float *block_mse,
-                                     double *tensor_sums, double *partial, hipStream_t st);
+                                     double *tensor_sums, double *partial, int64_t partial_space,
+                                     hipStream_t st);
 // MXFP8 (E4M3): codes are one byte per element.
 hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                 uint8_t *scales, hipStream_t st);

@@ -50,11 +50,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef MX_UNROLL
 #define MX_UNROLL 4
 #endif
-// Most workgroups a streaming launch uses (beyond it, workgroups loop over
-// tiles). Measured on a 2.1e9-element bf16 tensor: 196,608 (768 per CU)
-// beat 65,536 by 5 % (quantize) and 3 % (dequantize) with fake-quant level,
-// while 8,192-32,768 were slower. Tensors below ~200 M elements get one tile
-// per workgroup either way.
+// Most workgroups a launch of the other formats' kernels and of the
+// multi-tensor launch uses (beyond it, workgroups loop over tiles). Measured
+// on a 2.1e9-element bf16 tensor with four items per thread: 196,608 (768
+// per CU) beat 65,536 by 5 % (quantize) and 3 % (dequantize), while
+// 8,192-32,768 were slower. The MXFP4 single-tensor kernels are not capped
+// (see kGridLimit). Tensors below ~200 M elements get one tile per workgroup
+// either way.
 #ifndef MX_GRID_CAP
 #define MX_GRID_CAP 196608
 #endif
@@ -422,15 +424,22 @@ __device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t 
 // ---- kernels -----------------------------------------------------------------
 
 // Grid-stride over tiles of kThreads * U items; each thread's U items are
-// spaced kThreads apart so every load instruction is coalesced, and the loads
-// of a tile come ahead of its arithmetic (the backend may still sink a load
-// whose value is first used past a divergent branch below the first item's
-// work: OAS quantize issues one load, then three, which measured faster than
-// forcing all four ahead). Full tiles run without bounds
-// checks; the one partial tile (if any) is handled by the workgroup whose
-// stride lands on it, with per-item checks.
-template <int U, typename Load, typename Use>
-__device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
+// spaced kThreads apart so every load instruction is coalesced. A tile runs
+// in three phases: every item's loads, every item's arithmetic (results kept
+// in registers), every item's stores. The vector memory counter that a wave
+// waits on for its loads also counts its stores, so a store issued between
+// the loads of a tile and the wait for a later item's data makes that wait
+// cover the store as well: storing each item before the next item's
+// arithmetic stalled every wave on its own stores (block MSE on the 2.8e9-
+// element weight set: 1465 us with the per-item store, 1188 us without any
+// store). The backend may still sink a load whose value is first used past a
+// divergent branch below the first item's arithmetic (OAS quantize issues one
+// load, then three, which measured faster than forcing all four ahead). Full
+// tiles run without bounds checks; the one partial tile (if any) is handled
+// by the workgroup whose stride lands on it, with per-item checks.
+template <int U, typename Load, typename Compute, typename Store>
+__device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Compute compute,
+                                          Store store) {
   const int64_t tile = (int64_t)kThreads * U;
   const int64_t nfull = nitems / tile;
   int64_t t = blockIdx.x;
@@ -438,9 +447,12 @@ __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
     for (int u = 0; u < U; u++) load(u, base + u * kThreads);
-    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
+    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
 #pragma unroll
-    for (int u = 0; u < U; u++) use(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) compute(u, base + u * kThreads);
+    __builtin_amdgcn_sched_barrier(0);  // every item's arithmetic ahead of the stores
+#pragma unroll
+    for (int u = 0; u < U; u++) store(u, base + u * kThreads);
   }
   if (t == nfull && nfull * tile < nitems) {
     const int64_t base = t * tile + threadIdx.x;
@@ -449,8 +461,17 @@ __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
       if (base + u * kThreads < nitems) load(u, base + u * kThreads);
 #pragma unroll
     for (int u = 0; u < U; u++)  // whole quads (16-lane rows) drop out together
-      if (base + u * kThreads < nitems) use(u, base + u * kThreads);
+      if (base + u * kThreads < nitems) compute(u, base + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (base + u * kThreads < nitems) store(u, base + u * kThreads);
   }
+}
+
+// The same walk for a kernel that stores nothing per item.
+template <int U, typename Load, typename Use>
+__device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
+  tile_loop<U>(nitems, load, use, [](int, int64_t) {});
 }
 
 // Items per thread per tile for the streaming kernels: kUnroll bf16 items,
@@ -462,51 +483,65 @@ __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
 template <bool BF16>
 constexpr int kU = BF16 ? kUnroll : (kUnroll >= 4 ? kUnroll / 4 : 1);
 
-// Items per thread for the MXFP4 kernels, by what the kernel does (measured
-// each op alone): bf16 quantize in the OCP, OAS and OAS_BITS modes keeps kU
-// (two items per thread was 7 % slower on 8192x4096, eight 3-13 % slower), while bf16 dequantize
-// and OAS_NF quantize take two (2-12 % faster: fewer registers and more
-// workgroups in flight for the longer per-item work or the write-heavy
-// stream). Fake-quant takes two items in both dtypes (one fp32 item was 5 %
-// slower on fp32 1024x4096). The multi-tensor launch uses the same numbers;
-// its tile offsets depend on them.
+// Items per thread for the MXFP4 kernels, by what the kernel does and by
+// tensor size (each op measured alone). Up to kLargeItems items (tensors up
+// to ~1e9 elements, which the 256 MB Infinity Cache may partly hold): bf16
+// quantize in every mode keeps kU (two items per thread was 7 % slower on
+// 8192x4096 for OCP and OAS, and 7 % slower on 16384x8192 for OAS_NF; eight
+// 3-13 % slower), while bf16 dequantize and fake-quant take two (fewer
+// registers and more workgroups in flight for the write-heavy stream; one
+// fp32 fake-quant item was 5 % slower on fp32 1024x4096). Beyond it (multi-GB
+// weight sets streamed once from HBM) fewer items per thread keep the memory
+// that the resident workgroups touch at one time compact: on the 2.8e9-element
+// Llama-3.2-3B weight set, quantize OCP with one item per thread was 3.5 %
+// faster than four, overflow-aware quantize with two 3.6 % faster, fake-quant
+// with one 5 % faster than two; OAS_NF quantize keeps four and dequantize two.
+// The multi-tensor launch uses the small-tensor numbers (its tile offsets
+// depend on them).
+#ifndef MX_LARGE_ITEMS
+#define MX_LARGE_ITEMS (int64_t(3) << 23)
+#endif
+constexpr int64_t kLargeItems = MX_LARGE_ITEMS;
 enum { kKindQuantize = 0, kKindFakequant = 1, kKindDequantize = 2 };
-constexpr int unroll_of(bool bf16, int mode, int kind) {
+constexpr int unroll_of(bool bf16, int mode, int kind, bool large = false) {
+  if (bf16 && large) {
+    if (kind == kKindFakequant) return 1;
+    if (kind == kKindDequantize) return 2;
+    return mode == MX_SCALE_OAS_NF ? kU<true> : mode == MX_SCALE_OAS ? 2 : 1;
+  }
   if (kind == kKindFakequant) return 2;
   if (!bf16) return kU<false>;
-  return kind == kKindQuantize && mode != MX_SCALE_OAS_NF ? kU<true> : 2;
+  return kind == kKindQuantize ? kU<true> : 2;
 }
 
-template <bool BF16, int MODE>
+template <bool BF16, int MODE, int U>
 __global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ x,
                                                        uint32_t *__restrict__ codes,
                                                        uint8_t *__restrict__ scales,
                                                        int64_t nitems) {
-  constexpr int U = unroll_of(BF16, MODE, kKindQuantize);
   Item<BF16> xv[U];
+  uint32_t cw[U], sv[U];
   tile_loop<U>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t) { sv[u] = quantize_item<BF16, MODE>(xv[u], cw[u]); },
       [&](int u, int64_t it) {
-        uint32_t c;
-        const uint32_t s = quantize_item<BF16, MODE>(xv[u], c);
-        st<false>(codes + it, c);
-        if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)s);
+        st<false>(codes + it, cw[u]);
+        if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)sv[u]);
       });
 }
 
-template <bool BF16, int MODE>
+template <bool BF16, int MODE, int U>
 __global__ __launch_bounds__(kThreads) void k_fakequant(const void *x, void *y, int64_t nitems) {
-  constexpr int U = unroll_of(BF16, MODE, kKindFakequant);
   Item<BF16> xv[U];
+  uint32_t out[U][BF16 ? 4 : 8];
   tile_loop<U>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
-      [&](int u, int64_t it) {
+      [&](int u, int64_t) {
         uint32_t c;
         const uint32_t s = quantize_item<BF16, MODE>(xv[u], c);
-        uint32_t out[BF16 ? 4 : 8];
-        decode_item<BF16>(c, s, out);
-        store_item<BF16>(y, it, out);
-      });
+        decode_item<BF16>(c, s, out[u]);
+      },
+      [&](int u, int64_t it) { store_item<BF16>(y, it, out[u]); });
 }
 
 // ---- many tensors in one launch ------------------------------------------------
@@ -520,8 +555,9 @@ __global__ __launch_bounds__(kThreads) void k_fakequant(const void *x, void *y, 
 // tile0 <= t (a binary search on uniform values, so scalar work); a
 // tensor's last tile may be partial and takes the per-item checks.
 
-template <int U, typename Load, typename Use>
-__device__ __forceinline__ void tile_at(int64_t t, int64_t nitems, Load load, Use use) {
+template <int U, typename Load, typename Compute, typename Store>
+__device__ __forceinline__ void tile_at(int64_t t, int64_t nitems, Load load, Compute compute,
+                                        Store store) {
   const int64_t tile = (int64_t)kThreads * U;
   const int64_t base = t * tile + threadIdx.x;
   if ((t + 1) * tile <= nitems) {
@@ -529,14 +565,20 @@ __device__ __forceinline__ void tile_at(int64_t t, int64_t nitems, Load load, Us
     for (int u = 0; u < U; u++) load(u, base + u * kThreads);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; u++) use(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) compute(u, base + u * kThreads);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; u++) store(u, base + u * kThreads);
   } else {
 #pragma unroll
     for (int u = 0; u < U; u++)
       if (base + u * kThreads < nitems) load(u, base + u * kThreads);
 #pragma unroll
     for (int u = 0; u < U; u++)  // whole quads drop out together
-      if (base + u * kThreads < nitems) use(u, base + u * kThreads);
+      if (base + u * kThreads < nitems) compute(u, base + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (base + u * kThreads < nitems) store(u, base + u * kThreads);
   }
 }
 
@@ -567,44 +609,42 @@ template <bool BF16, int MODE, bool FQ>
 __global__ __launch_bounds__(kThreads) void k_multi(const MultiArgs a) {
   constexpr int U = unroll_of(BF16, MODE, FQ ? kKindFakequant : kKindQuantize);
   Item<BF16> xv[U];
+  uint32_t cw[U], sv[U], out[U][FQ ? (BF16 ? 4 : 8) : 1];
   for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
     const int j = multi_find(a, t);
     const MultiDesc &d = a.d[j];
     const void *x = d.x;
     tile_at<U>(
         t - d.tile0, d.nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+        [&](int u, int64_t) {
+          sv[u] = quantize_item<BF16, MODE>(xv[u], cw[u]);
+          if constexpr (FQ) decode_item<BF16>(cw[u], sv[u], out[u]);
+        },
         [&](int u, int64_t it) {
-          uint32_t c;
-          const uint32_t s = quantize_item<BF16, MODE>(xv[u], c);
           if constexpr (FQ) {
-            uint32_t out[BF16 ? 4 : 8];
-            decode_item<BF16>(c, s, out);
-            store_item<BF16>(d.out, it, out);
+            store_item<BF16>(d.out, it, out[u]);
           } else {
-            st<false>(static_cast<uint32_t *>(d.out) + it, c);
-            if ((threadIdx.x & 3) == 0) st<false>(d.scales + (it >> 2), (uint8_t)s);
+            st<false>(static_cast<uint32_t *>(d.out) + it, cw[u]);
+            if ((threadIdx.x & 3) == 0) st<false>(d.scales + (it >> 2), (uint8_t)sv[u]);
           }
         });
   }
 }
 
-template <bool BF16>
+template <bool BF16, int U>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restrict__ codes,
                                                          const uint8_t *__restrict__ scales,
                                                          void *__restrict__ y, int64_t nitems) {
-  constexpr int U = unroll_of(BF16, 0, kKindDequantize);
   uint32_t cw[U], sb[U];
+  uint32_t out[U][BF16 ? 4 : 8];
   tile_loop<U>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
         sb[u] = ld<false>(scales + (it >> 2));
       },
-      [&](int u, int64_t it) {
-        uint32_t out[BF16 ? 4 : 8];
-        decode_item<BF16>(cw[u], sb[u], out);
-        store_item<BF16>(y, it, out);
-      });
+      [&](int u, int64_t) { decode_item<BF16>(cw[u], sb[u], out[u]); },
+      [&](int u, int64_t it) { store_item<BF16>(y, it, out[u]); });
 }
 
 // Block error. Per block: SSE = sum (x - x_hat)^2 in fp64 (quad sum in a
@@ -614,14 +654,13 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restr
 // sums, then a butterfly over the wave, then the waves in order), and
 // k_sum_partials adds the partials.
 // Block error of one item against (c, s): the fp64 SSE of the quad's block,
-// summed in a fixed order (per lane, then quad_sum_f64), written as
-// block_mse[block] = SSE / 32 by the quad's lane 0 when block_mse is set;
-// lane 0 also adds the SSE to `mine`, and every lane adds its sum of x^2 to
-// `mine_sq` (tensor sums).
+// summed in a fixed order (per lane, then quad_sum_f64); returns the block's
+// MSE, SSE / 32 as fp32, on every lane of the quad (the caller stores it
+// from lane 0). Lane 0 of the quad also adds the SSE to `mine`, and every
+// lane adds its sum of x^2 to `mine_sq` (tensor sums).
 template <bool BF16, bool SUMS>
-__device__ __forceinline__ void mse_item(const Item<BF16> &x, uint32_t c, uint32_t s, int64_t it,
-                                         float *__restrict__ block_mse, double &mine,
-                                         double &mine_sq) {
+__device__ __forceinline__ float mse_item(const Item<BF16> &x, uint32_t c, uint32_t s,
+                                          double &mine, double &mine_sq) {
   float q[8];
   decode_f32(c, s, q);
   double acc = 0.0, acc_sq = 0.0;
@@ -639,10 +678,8 @@ __device__ __forceinline__ void mse_item(const Item<BF16> &x, uint32_t c, uint32
     mine_sq += acc_sq;
   }
   const double sse = quad_sum_f64(acc);
-  if ((threadIdx.x & 3) == 0) {
-    if (block_mse) st<false>(block_mse + (it >> 2), (float)(sse * (1.0 / 32.0)));
-    if constexpr (SUMS) mine += sse;
-  }
+  if constexpr (SUMS) mine += (threadIdx.x & 3) == 0 ? sse : 0.0;
+  return (float)(sse * (1.0 / 32.0));
 }
 
 // The workgroup's two tensor sums, in a fixed order (butterfly over each
@@ -667,12 +704,19 @@ __device__ __forceinline__ void write_partials(double mine, double mine_sq,
   }
 }
 
-// Items per thread of the block-MSE kernel, both dtypes (it sizes the grid,
-// hence the workspace, per shape): two measured 3 % faster than four on bf16
-// 8192x4096 with the same per-block results.
-constexpr int kMseU = 2;
+// Items per thread of the block-MSE kernel, by tensor size only (the grid
+// sizes the partial-sum workspace, which the caller sizes without a dtype):
+// four up to kLargeItems items, two beyond. With one tile per workgroup
+// (see mxi_launch_block_mse) four measured fastest on bf16 8192x4096 and
+// 16384x8192 (74.6 % and 79.4 % of 8 TB/s without the tensor sums, against
+// 71.1 % and 76.7 % with two), two on the 2.8e9-element weight set (77.5 %,
+// against 73.8 % with four and 72.5 % with one).
+constexpr int mse_unroll(bool large) { return large ? 2 : 4; }
+// Items per thread of the one-pass kernel, both dtypes (it sizes the same
+// workspace).
+constexpr int kFusedU = 2;
 
-template <bool BF16, bool SUMS>
+template <bool BF16, bool SUMS, int U>
 __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__ x,
                                                         const uint32_t *__restrict__ codes,
                                                         const uint8_t *__restrict__ scales,
@@ -681,17 +725,19 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
                                                         int64_t nitems) {
   double mine = 0.0;     // sum of the block SSEs this lane reports (q == 0 lanes)
   double mine_sq = 0.0;  // sum of x^2 over this lane's elements
-  Item<BF16> xv[kMseU];
-  uint32_t cw[kMseU], sb[kMseU];
-  tile_loop<kMseU>(
+  Item<BF16> xv[U];
+  uint32_t cw[U], sb[U];
+  float bm[U];
+  tile_loop<U>(
       nitems,
       [&](int u, int64_t it) {
         load_item<BF16>(x, it, xv[u]);
         cw[u] = ld<false>(codes + it);
         sb[u] = ld<false>(scales + (it >> 2));
       },
+      [&](int u, int64_t) { bm[u] = mse_item<BF16, SUMS>(xv[u], cw[u], sb[u], mine, mine_sq); },
       [&](int u, int64_t it) {
-        mse_item<BF16, SUMS>(xv[u], cw[u], sb[u], it, block_mse, mine, mine_sq);
+        if (block_mse && (threadIdx.x & 3) == 0) st<false>(block_mse + (it >> 2), bm[u]);
       });
   if constexpr (SUMS) write_partials(mine, mine_sq, partial);
 }
@@ -711,57 +757,70 @@ __global__ __launch_bounds__(kThreads) void k_quantize_fused(const void *__restr
                                                              int64_t nitems) {
   double mine = 0.0, mine_sq = 0.0;
   const bool err = block_mse != nullptr || SUMS;
-  // (the grid is sized like the block-MSE grid but with kUnroll items per
-  // thread, so the block-MSE workspace holds its partials; the grid stride
-  // makes any per-thread count correct. Two bf16 items per thread, as for
-  // fake-quant: 2.4 % faster than four on 8192x4096.)
-  constexpr int U = BF16 ? 2 : kU<false>;
+  // two items per thread in both dtypes (as for fake-quant: 2.4 % faster
+  // than four on bf16 8192x4096); its grid is the largest an error launch
+  // uses, which sizes the partial-sum workspace
+  constexpr int U = kFusedU;
   Item<BF16> xv[U];
+  uint32_t cw[U], sv[U], out[U][BF16 ? 4 : 8];
+  float bm[U];
   tile_loop<U>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t) {
+        sv[u] = quantize_item<BF16, MODE>(xv[u], cw[u]);
+        if (y) decode_item<BF16>(cw[u], sv[u], out[u]);  // uniform
+        if (err) bm[u] = mse_item<BF16, SUMS>(xv[u], cw[u], sv[u], mine, mine_sq);
+      },
       [&](int u, int64_t it) {
-        uint32_t c;
-        const uint32_t s = quantize_item<BF16, MODE>(xv[u], c);
-        st<false>(codes + it, c);
-        if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)s);
-        if (y) {  // uniform
-          uint32_t out[BF16 ? 4 : 8];
-          decode_item<BF16>(c, s, out);
-          store_item<BF16>(y, it, out);
-        }
-        if (err) mse_item<BF16, SUMS>(xv[u], c, s, it, block_mse, mine, mine_sq);
+        st<false>(codes + it, cw[u]);
+        if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)sv[u]);
+        if (y) store_item<BF16>(y, it, out[u]);
+        if (block_mse && (threadIdx.x & 3) == 0) st<false>(block_mse + (it >> 2), bm[u]);
       });
   if constexpr (SUMS) write_partials(mine, mine_sq, partial);
 }
 
-#ifndef MX_MSE_GRID_CAP
-#define MX_MSE_GRID_CAP 2048
+// Partial sums of the tensor error: each workgroup of an error launch writes
+// two (SSE, sum of x^2); one workgroup of k_sum_partials adds up to
+// kSumGroup pairs in a fixed order. An error launch uses at most
+// kSumGroup^2 workgroups (beyond, workgroups loop over tiles), so at most two
+// sum levels run: up to kSumGroup partial pairs go straight to the result,
+// more go through one pair per kSumGroup first.
+#ifndef MX_SUM_GROUP
+#define MX_SUM_GROUP 2048
 #endif
-constexpr int kSumPer = MX_MSE_GRID_CAP / kThreads;  // partial pairs per thread
-static_assert(kSumPer * kThreads == MX_MSE_GRID_CAP, "grid cap must be a multiple of 256");
+constexpr int64_t kSumGroup = MX_SUM_GROUP;
+constexpr int kSumPer = (int)(kSumGroup / kThreads);  // partial pairs per thread
+static_assert(kSumPer * kThreads == kSumGroup, "sum group must be a multiple of 256");
+constexpr int64_t kPartialCap = kSumGroup * kSumGroup;
 
-// One workgroup: out[j] = sum over i of partial[2i + j] for j = 0, 1, n <=
-// MX_MSE_GRID_CAP pairs. The kernel is latency-bound, so every thread issues
-// all of its loads (pairs t, t + 256, ...) before the first add; the sums then
-// run in a fixed order (per thread in pair order, a butterfly over the wave,
-// the four waves in order), so the result is deterministic. n == 0 writes 0.
+// Workgroup b: out[2b + j] = sum over i of partial[2(b kSumGroup + i) + j]
+// for j = 0, 1 and the (up to kSumGroup) pairs i of its group; n pairs in
+// all. The kernel is latency-bound, so every thread issues all of its loads
+// (pairs t, t + 256, ...) before the first add; the sums then run in a fixed
+// order (per thread in pair order, a butterfly over the wave, the four waves
+// in order), so the result is deterministic. n == 0 writes 0.
 __global__ __launch_bounds__(kThreads) void k_sum_partials(const double *__restrict__ partial,
-                                                           int n, double *__restrict__ out) {
+                                                           int64_t n, double *__restrict__ out) {
   __shared__ double wave_part[2][kThreads / 64];
-  if (n <= 0) {
-    if (threadIdx.x < 2) out[threadIdx.x] = 0.0;
+  const int64_t first = (int64_t)blockIdx.x * kSumGroup;
+  const int m = (int)(n - first < kSumGroup ? n - first : kSumGroup);  // pairs of this group
+  double *o = out + 2 * blockIdx.x;
+  if (m <= 0) {
+    if (threadIdx.x < 2) o[threadIdx.x] = 0.0;
     return;
   }
+  const double *p = partial + 2 * first;
   // unconditional loads of a clamped (in-bounds) index, so none waits on a
-  // branch; pairs past n are then replaced by zero
+  // branch; pairs past m are then replaced by zero
   double v0[kSumPer], v1[kSumPer];
 #pragma unroll
   for (int j = 0; j < kSumPer; j++) {
     const int i = (int)threadIdx.x + j * kThreads;
-    const int ic = min(i, n - 1);
-    const double a = partial[2 * ic], b = partial[2 * ic + 1];
-    v0[j] = i < n ? a : 0.0;
-    v1[j] = i < n ? b : 0.0;
+    const int ic = min(i, m - 1);
+    const double a = p[2 * ic], b = p[2 * ic + 1];
+    v0[j] = i < m ? a : 0.0;
+    v1[j] = i < m ? b : 0.0;
   }
   double t0 = 0.0, t1 = 0.0;
 #pragma unroll
@@ -783,7 +842,7 @@ __global__ __launch_bounds__(kThreads) void k_sum_partials(const double *__restr
     double t = 0.0;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; w++) t += wave_part[threadIdx.x][w];
-    out[threadIdx.x] = t;
+    o[threadIdx.x] = t;
   }
 }
 
@@ -914,13 +973,14 @@ __global__ __launch_bounds__(kThreads) void k_quantize8(const void *__restrict__
                                                         uint8_t *__restrict__ scales,
                                                         int64_t nitems) {
   Item<BF16> xv[kU<BF16>];
+  u32x2 cw[kU<BF16>];
+  uint32_t sv[kU<BF16>];
   tile_loop<kU<BF16>>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t) { sv[u] = quantize8_item<BF16>(xv[u], cw[u]); },
       [&](int u, int64_t it) {
-        u32x2 c;
-        const uint32_t s = quantize8_item<BF16>(xv[u], c);
-        st<false>(codes + it, c);
-        if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)s);
+        st<false>(codes + it, cw[u]);
+        if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)sv[u]);
       });
 }
 
@@ -930,32 +990,30 @@ __global__ __launch_bounds__(kThreads) void k_dequantize8(const u32x2 *__restric
                                                           void *__restrict__ y, int64_t nitems) {
   u32x2 cw[kU<BF16>];
   uint32_t sb[kU<BF16>];
+  uint32_t out[kU<BF16>][BF16 ? 4 : 8];
   tile_loop<kU<BF16>>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
         sb[u] = ld<false>(scales + (it >> 2));
       },
-      [&](int u, int64_t it) {
-        uint32_t out[BF16 ? 4 : 8];
-        decode8_item<BF16>(cw[u], sb[u], out);
-        store_item<BF16>(y, it, out);
-      });
+      [&](int u, int64_t) { decode8_item<BF16>(cw[u], sb[u], out[u]); },
+      [&](int u, int64_t it) { store_item<BF16>(y, it, out[u]); });
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_fakequant8(const void *x, void *y, int64_t nitems) {
   constexpr int U = unroll_of(BF16, 0, kKindFakequant);  // as MXFP4 fake-quant (3 % faster)
   Item<BF16> xv[U];
+  uint32_t out[U][BF16 ? 4 : 8];
   tile_loop<U>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
-      [&](int u, int64_t it) {
+      [&](int u, int64_t) {
         u32x2 c;
         const uint32_t s = quantize8_item<BF16>(xv[u], c);
-        uint32_t out[BF16 ? 4 : 8];
-        decode8_item<BF16>(c, s, out);
-        store_item<BF16>(y, it, out);
-      });
+        decode8_item<BF16>(c, s, out[u]);
+      },
+      [&](int u, int64_t it) { store_item<BF16>(y, it, out[u]); });
 }
 
 // ---- NVFP4 comparator (16-element blocks, E4M3 block scales) ----------------
@@ -1070,9 +1128,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *x,
   const float inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t
 
   Item<BF16> xv[kUnroll];
+  uint32_t cw[kUnroll], sv[kUnroll], out[kUnroll][FQ ? (BF16 ? 4 : 8) : 1];
   tile_loop<kUnroll>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
-      [&](int u, int64_t it) {
+      [&](int u, int64_t) {
         const uint32_t ab = dpp_x1_max(item_amax_bits<BF16>(xv[u]));  // NaN/Inf sort above
         uint32_t c;
         uint32_t sbyte;
@@ -1098,13 +1157,16 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *x,
           c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[4], v[5], one, 2);
           c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[6], v[7], one, 3);
         }
+        if constexpr (FQ) nv_decode_item<BF16>(c, sbyte, inv_s, out[u]);
+        cw[u] = c;
+        sv[u] = sbyte;
+      },
+      [&](int u, int64_t it) {
         if constexpr (FQ) {
-          uint32_t out[BF16 ? 4 : 8];
-          nv_decode_item<BF16>(c, sbyte, inv_s, out);
-          store_item<BF16>(y, it, out);
+          store_item<BF16>(y, it, out[u]);
         } else {
-          st<false>(codes + it, c);
-          if ((threadIdx.x & 1) == 0) st<false>(block_scales + (it >> 1), (uint8_t)sbyte);
+          st<false>(codes + it, cw[u]);
+          if ((threadIdx.x & 1) == 0) st<false>(block_scales + (it >> 1), (uint8_t)sv[u]);
         }
       });
 }
@@ -1141,17 +1203,15 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_nv(const uint32_t *__re
   const int t = (int)*tensor_scale - 127;
   const float inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t, scale operand
   uint32_t cw[kU<BF16>], sb[kU<BF16>];
+  uint32_t out[kU<BF16>][BF16 ? 4 : 8];
   tile_loop<kU<BF16>>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
         sb[u] = ld<false>(block_scales + (it >> 1));
       },
-      [&](int u, int64_t it) {
-        uint32_t out[BF16 ? 4 : 8];
-        nv_decode_item<BF16>(cw[u], sb[u], inv_s, out);
-        store_item<BF16>(y, it, out);
-      });
+      [&](int u, int64_t) { nv_decode_item<BF16>(cw[u], sb[u], inv_s, out[u]); },
+      [&](int u, int64_t it) { store_item<BF16>(y, it, out[u]); });
 }
 
 // ---- MBS-Static (16-element sub-blocks, 8-bit-mantissa macro factor) ---------
@@ -1320,6 +1380,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_mbs(const uint32_t *__r
   // items per thread as MXFP4 dequantize (two for bf16: 2.5 % faster here)
   constexpr int U = unroll_of(BF16, 0, kKindDequantize);
   uint32_t cw[U], sb[U], mb[U];
+  uint32_t out[U][BF16 ? 4 : 8];
   tile_loop<U>(
       nitems,
       [&](int u, int64_t it) {
@@ -1327,11 +1388,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_mbs(const uint32_t *__r
         sb[u] = ld<false>(sub_scales + (it >> 1));
         mb[u] = ld<false>(macro_mant + (it >> 4));
       },
-      [&](int u, int64_t it) {
-        uint32_t out[BF16 ? 4 : 8];
-        mbs_decode_item<BF16>(cw[u], sb[u], mb[u], out);
-        store_item<BF16>(y, it, out);
-      });
+      [&](int u, int64_t) { mbs_decode_item<BF16>(cw[u], sb[u], mb[u], out[u]); },
+      [&](int u, int64_t it) { store_item<BF16>(y, it, out[u]); });
 }
 
 // ---- launchers -----------------------------------------------------------------
@@ -1364,107 +1422,189 @@ using namespace mxk;
       break;                                                                               \
   }
 
-#define MX_DISPATCH_MODE(KERNEL, BF16, MODE, G, B, ST, ...)                               \
+// The MXFP4 streaming kernels launch one tile per workgroup (a grid stride
+// only past the launch limit): on the 2.8e9-element weight set a cap of
+// 196,608 workgroups, whose second round of tiles streams a second region of
+// memory at the same time, was 1-5 % slower than no cap.
+constexpr int64_t kGridLimit = 0x7FFFFFFF;
+
+template <bool BF16, int MODE>
+static void launch_quantize_t(const void *x, uint32_t *c, uint8_t *s, int64_t nitems,
+                              hipStream_t st) {
+  if (nitems >= kLargeItems) {
+    constexpr int U = unroll_of(BF16, MODE, kKindQuantize, true);
+    hipLaunchKernelGGL((k_quantize<BF16, MODE, U>), dim3(grid_for(nitems, kGridLimit, U)),
+                       dim3(kThreads), 0, st, x, c, s, nitems);
+  } else {
+    constexpr int U = unroll_of(BF16, MODE, kKindQuantize, false);
+    hipLaunchKernelGGL((k_quantize<BF16, MODE, U>), dim3(grid_for(nitems, kGridLimit, U)),
+                       dim3(kThreads), 0, st, x, c, s, nitems);
+  }
+}
+
+template <bool BF16, int MODE>
+static void launch_fakequant_t(const void *x, void *y, int64_t nitems, hipStream_t st) {
+  if (nitems >= kLargeItems) {
+    constexpr int U = unroll_of(BF16, MODE, kKindFakequant, true);
+    hipLaunchKernelGGL((k_fakequant<BF16, MODE, U>), dim3(grid_for(nitems, kGridLimit, U)),
+                       dim3(kThreads), 0, st, x, y, nitems);
+  } else {
+    constexpr int U = unroll_of(BF16, MODE, kKindFakequant, false);
+    hipLaunchKernelGGL((k_fakequant<BF16, MODE, U>), dim3(grid_for(nitems, kGridLimit, U)),
+                       dim3(kThreads), 0, st, x, y, nitems);
+  }
+}
+
+template <bool BF16>
+static void launch_dequantize_t(const uint32_t *c, const uint8_t *s, void *y, int64_t nitems,
+                                hipStream_t st) {
+  if (nitems >= kLargeItems) {
+    constexpr int U = unroll_of(BF16, 0, kKindDequantize, true);
+    hipLaunchKernelGGL((k_dequantize<BF16, U>), dim3(grid_for(nitems, kGridLimit, U)),
+                       dim3(kThreads), 0, st, c, s, y, nitems);
+  } else {
+    constexpr int U = unroll_of(BF16, 0, kKindDequantize, false);
+    hipLaunchKernelGGL((k_dequantize<BF16, U>), dim3(grid_for(nitems, kGridLimit, U)),
+                       dim3(kThreads), 0, st, c, s, y, nitems);
+  }
+}
+
+#define MX_MODE_SWITCH(FN, BF16, MODE, ...)                                                 \
   switch (MODE) {                                                                          \
-    case MX_SCALE_OAS:                                                                     \
-      hipLaunchKernelGGL((KERNEL<BF16, MX_SCALE_OAS>), G, B, 0, ST, __VA_ARGS__);          \
-      break;                                                                               \
-    case MX_SCALE_OAS_BITS:                                                                \
-      hipLaunchKernelGGL((KERNEL<BF16, MX_SCALE_OAS_BITS>), G, B, 0, ST, __VA_ARGS__);     \
-      break;                                                                               \
-    case MX_SCALE_OAS_NF:                                                                  \
-      hipLaunchKernelGGL((KERNEL<BF16, MX_SCALE_OAS_NF>), G, B, 0, ST, __VA_ARGS__);       \
-      break;                                                                               \
-    default:                                                                               \
-      hipLaunchKernelGGL((KERNEL<BF16, MX_SCALE_OCP>), G, B, 0, ST, __VA_ARGS__);          \
-      break;                                                                               \
+    case MX_SCALE_OAS: FN<BF16, MX_SCALE_OAS>(__VA_ARGS__); break;                         \
+    case MX_SCALE_OAS_BITS: FN<BF16, MX_SCALE_OAS_BITS>(__VA_ARGS__); break;               \
+    case MX_SCALE_OAS_NF: FN<BF16, MX_SCALE_OAS_NF>(__VA_ARGS__); break;                   \
+    default: FN<BF16, MX_SCALE_OCP>(__VA_ARGS__); break;                                   \
   }
 
 hipError_t mxi_launch_quantize(const void *x, int bf16, int mode, int64_t nitems,
                                uint8_t *codes, uint8_t *scales, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, unroll_of(bf16, mode, kKindQuantize))), b(kThreads);
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
   if (bf16) {
-    MX_DISPATCH_MODE(k_quantize, true, mode, g, b, st, x, c, scales, nitems)
+    MX_MODE_SWITCH(launch_quantize_t, true, mode, x, c, scales, nitems, st)
   } else {
-    MX_DISPATCH_MODE(k_quantize, false, mode, g, b, st, x, c, scales, nitems)
+    MX_MODE_SWITCH(launch_quantize_t, false, mode, x, c, scales, nitems, st)
   }
   return hipGetLastError();
 }
 
 hipError_t mxi_launch_fakequant(const void *x, int bf16, int mode, int64_t nitems, void *y,
                                 hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, unroll_of(bf16, mode, kKindFakequant))), b(kThreads);
   if (bf16) {
-    MX_DISPATCH_MODE(k_fakequant, true, mode, g, b, st, x, y, nitems)
+    MX_MODE_SWITCH(launch_fakequant_t, true, mode, x, y, nitems, st)
   } else {
-    MX_DISPATCH_MODE(k_fakequant, false, mode, g, b, st, x, y, nitems)
+    MX_MODE_SWITCH(launch_fakequant_t, false, mode, x, y, nitems, st)
   }
   return hipGetLastError();
 }
 
 hipError_t mxi_launch_dequantize(const uint8_t *codes, const uint8_t *scales, int bf16,
                                  int64_t nitems, void *y, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, unroll_of(bf16, 0, kKindDequantize))), b(kThreads);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
   if (bf16)
-    hipLaunchKernelGGL((k_dequantize<true>), g, b, 0, st, c, scales, y, nitems);
+    launch_dequantize_t<true>(c, scales, y, nitems, st);
   else
-    hipLaunchKernelGGL((k_dequantize<false>), g, b, 0, st, c, scales, y, nitems);
+    launch_dequantize_t<false>(c, scales, y, nitems, st);
   return hipGetLastError();
 }
 
-// (the one-pass kernel's grid, sized with kUnroll items per thread, is
-// never larger than this one, so the same workspace serves it)
+// Doubles of partial-sum space an error launch with `grid` workgroups
+// writes: its pairs, and the second-level pairs when there are more than
+// one group of them.
+static int64_t partial_doubles(int64_t grid) {
+  return 2 * (grid + (grid > kSumGroup ? (grid + kSumGroup - 1) / kSumGroup : 0));
+}
+
+// The workspace an error launch over nitems items needs for one tile per
+// workgroup: the one-pass grid (two items per thread) is the largest.
 size_t mxi_block_mse_partials(int64_t nitems) {
-  return 2 * grid_for(nitems, MX_MSE_GRID_CAP, kMseU);
+  return (size_t)partial_doubles(grid_for(nitems, kPartialCap, kFusedU));
+}
+
+// Grid of an error launch: one tile per workgroup (a wave never waits for a
+// store of its own: the stores of each workgroup's one tile come last) when
+// the partial space holds that grid's sums, else one sum group of
+// workgroups looping over the tiles (the fixed scratch of the call without
+// a workspace). Without tensor sums there are no partials.
+static unsigned error_grid(int64_t nitems, int u, bool sums, int64_t partial_space) {
+  const unsigned g = grid_for(nitems, kPartialCap, u);
+  if (!sums || partial_doubles(g) <= partial_space) return g;
+  return grid_for(nitems, kSumGroup, u);
+}
+
+// Adds the `grid` partial pairs at `partial` into out[0..1]: one sum launch,
+// or two when there are more than kSumGroup pairs (the second-level pairs go
+// right after the first-level ones).
+static hipError_t sum_partials(double *partial, int64_t grid, double *out, hipStream_t st) {
+  if (grid <= kSumGroup) {
+    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kThreads), 0, st, partial, grid, out);
+    return hipGetLastError();
+  }
+  const int64_t groups = (grid + kSumGroup - 1) / kSumGroup;
+  double *second = partial + 2 * grid;
+  hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)groups), dim3(kThreads), 0, st, partial,
+                     grid, second);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kThreads), 0, st, second, groups, out);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool SUMS, int U>
+static void launch_block_mse_t(const void *x, const uint32_t *c, const uint8_t *scales,
+                               float *block_mse, double *part, unsigned grid, int64_t nitems,
+                               hipStream_t st) {
+  hipLaunchKernelGGL((k_block_mse<BF16, SUMS, U>), dim3(grid), dim3(kThreads), 0, st, x, c,
+                     scales, block_mse, part, nitems);
+}
+
+template <bool BF16, bool SUMS>
+static void launch_block_mse_u(bool large, const void *x, const uint32_t *c,
+                               const uint8_t *scales, float *block_mse, double *part,
+                               unsigned grid, int64_t nitems, hipStream_t st) {
+  if (large)
+    launch_block_mse_t<BF16, SUMS, mse_unroll(true)>(x, c, scales, block_mse, part, grid, nitems,
+                                                     st);
+  else
+    launch_block_mse_t<BF16, SUMS, mse_unroll(false)>(x, c, scales, block_mse, part, grid,
+                                                      nitems, st);
 }
 
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
                                 const uint8_t *scales, int64_t nitems, float *block_mse,
-                                double *tensor_sums, double *partial, hipStream_t st) {
-  const unsigned grid = grid_for(nitems, MX_MSE_GRID_CAP, kMseU);
+                                double *tensor_sums, double *partial, int64_t partial_space,
+                                hipStream_t st) {
+  const bool large = nitems >= kLargeItems;
+  const unsigned grid = error_grid(nitems, mse_unroll(large), tensor_sums != nullptr,
+                                   partial_space);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
   double *part = tensor_sums ? partial : nullptr;
   if (nitems > 0) {
-    const dim3 g(grid), b(kThreads);
     if (bf16) {
-      if (part)
-        hipLaunchKernelGGL((k_block_mse<true, true>), g, b, 0, st, x, c, scales, block_mse, part,
-                           nitems);
-      else
-        hipLaunchKernelGGL((k_block_mse<true, false>), g, b, 0, st, x, c, scales, block_mse,
-                           part, nitems);
+      if (part) launch_block_mse_u<true, true>(large, x, c, scales, block_mse, part, grid, nitems, st);
+      else launch_block_mse_u<true, false>(large, x, c, scales, block_mse, part, grid, nitems, st);
     } else {
-      if (part)
-        hipLaunchKernelGGL((k_block_mse<false, true>), g, b, 0, st, x, c, scales, block_mse,
-                           part, nitems);
-      else
-        hipLaunchKernelGGL((k_block_mse<false, false>), g, b, 0, st, x, c, scales, block_mse,
-                           part, nitems);
+      if (part) launch_block_mse_u<false, true>(large, x, c, scales, block_mse, part, grid, nitems, st);
+      else launch_block_mse_u<false, false>(large, x, c, scales, block_mse, part, grid, nitems, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (tensor_sums) {
-    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kThreads), 0, st, partial,
-                       nitems > 0 ? (int)grid : 0, tensor_sums);
-    return hipGetLastError();
-  }
+  if (tensor_sums) return sum_partials(partial, nitems > 0 ? grid : 0, tensor_sums, st);
   return hipSuccess;
 }
 
 // ---- fixed device scratch (block error without a workspace) -------------------
 //
 // The tensor sums of the block-error launch go through per-workgroup partial
-// sums: two doubles per workgroup, and that launch never uses more than
-// MX_MSE_GRID_CAP workgroups, so 2 * MX_MSE_GRID_CAP doubles (32 KiB) hold
-// them for every tensor size. mx_block_mse_noalloc keeps them here instead of
-// in a caller workspace. Each GPU the library runs on holds its own copy, at
-// its own address, until the process ends; every call on a GPU shares it. A
-// launch writes every partial slot it reads before the sum kernel reads it,
-// so nothing has to start at zero.
-constexpr size_t kScratchDoubles = 2 * (size_t)MX_MSE_GRID_CAP;
+// sums, two doubles per workgroup. mx_block_mse_noalloc keeps them here
+// instead of in a caller workspace: one sum group's worth, 2 * kSumGroup
+// doubles (32 KiB), which holds every tensor size because that call's
+// launch is capped at kSumGroup workgroups (see error_grid). Each GPU the
+// library runs on holds its own copy, at its own address, until the process
+// ends; every call on a GPU shares it. A launch writes every partial slot it
+// reads before the sum kernel reads it, so nothing has to start at zero.
+constexpr size_t kScratchDoubles = 2 * (size_t)kSumGroup;
 static __device__ __align__(256) double scratch[kScratchDoubles];
 
 size_t mxi_scratch_partials() { return kScratchDoubles; }
@@ -1663,9 +1803,9 @@ hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, i
 
 hipError_t mxi_launch_quantize_fused(const void *x, int bf16, int mode, int64_t nitems,
                                      uint8_t *codes, uint8_t *scales, void *y, float *block_mse,
-                                     double *tensor_sums, double *partial, hipStream_t st) {
-  // the block-MSE grid, so the partial sums fit mx_block_mse_workspace_size
-  const unsigned grid = grid_for(nitems, MX_MSE_GRID_CAP);
+                                     double *tensor_sums, double *partial, int64_t partial_space,
+                                     hipStream_t st) {
+  const unsigned grid = error_grid(nitems, kFusedU, tensor_sums != nullptr, partial_space);
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
   double *part = tensor_sums ? partial : nullptr;
   if (nitems > 0) {
@@ -1680,10 +1820,6 @@ hipError_t mxi_launch_quantize_fused(const void *x, int bf16, int mode, int64_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (tensor_sums) {
-    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kThreads), 0, st, partial,
-                       nitems > 0 ? (int)grid : 0, tensor_sums);
-    return hipGetLastError();
-  }
+  if (tensor_sums) return sum_partials(partial, nitems > 0 ? grid : 0, tensor_sums, st);
   return hipSuccess;
 }

@@ -53,7 +53,38 @@ static void mxfp4() {
   expect_launch(mx_block_mse(P(X), MX_BF16, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 1000, 4096,
                              (float *)P(Y), (double *)P(Ts), P(Ws), wsb, nullptr),
                 "block_mse", 1000 * 4096 / 8, n0);
-  CHECK(g_last.p[4] == P(Ts) && g_last.p[5] == P(Ws));
+  CHECK(g_last.p[4] == P(Ts) && g_last.p[5] == P(Ws) && g_last.space == (int64_t)(wsb / 8));
+  // the call without a workspace: its partial sums go to the fixed scratch
+  // of the stream's device (the current device for the null stream)
+  n0 = g_calls;
+  expect_launch(mx_block_mse_noalloc(P(X), MX_BF16, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 1000,
+                                     4096, (float *)P(Y), (double *)P(Ts), nullptr),
+                "block_mse", 1000 * 4096 / 8, n0);
+  CHECK(g_last.p[4] == P(Ts) && g_last.p[5] == stub_scratch(0) && g_last.space == 4096);
+  n0 = g_calls;
+  expect_launch(mx_block_mse_noalloc(P(X), MX_F32, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 8, 64,
+                                     nullptr, (double *)P(Ts), P(Ws)),
+                "block_mse", 8 * 64 / 8, n0);
+  CHECK(g_last.p[5] == stub_scratch(1) && g_last.bf16 == 0);
+  n0 = g_calls;
+  expect_launch(mx_block_mse_noalloc(P(X), MX_BF16, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 8, 64,
+                                     (float *)P(Y), nullptr, nullptr),
+                "block_mse", 8 * 64 / 8, n0);
+  CHECK(g_last.p[4] == nullptr && g_last.p[5] == nullptr);
+  n0 = g_calls;
+  expect_launch(mx_block_mse_noalloc(nullptr, MX_BF16, nullptr, nullptr, 0, 32, nullptr,
+                                     (double *)P(Ts), nullptr),
+                "block_mse", 0, n0);
+  n0 = g_calls;
+  CHECK(mx_block_mse_noalloc(nullptr, MX_BF16, nullptr, nullptr, 0, 32, (float *)P(Y), nullptr,
+                             nullptr) == MX_OK);
+  CHECK(mx_block_mse_noalloc(P(X), MX_BF16, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 1, 48, nullptr,
+                             (double *)P(Ts), nullptr) == MX_ERR_SHAPE);
+  CHECK(mx_block_mse_noalloc(P(X + 4), MX_BF16, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 1, 32, nullptr,
+                             (double *)P(Ts), nullptr) == MX_ERR_ALIGN);
+  CHECK(mx_block_mse_noalloc(P(X), MX_BF16, (uint8_t *)P(Cd), (uint8_t *)P(Sc), 4, 64, nullptr,
+                             (double *)P(Cd + 8), nullptr) == MX_ERR_ALIAS);
+  CHECK(g_calls == n0);
   n0 = g_calls;
   expect_launch(mx_quantize_fused(P(X), MX_BF16, 1000, 4096, MX_SCALE_OAS, (uint8_t *)P(Cd),
                                   (uint8_t *)P(Sc), P(Y), (float *)P(Ws + (1u << 24)),

@@ -40,19 +40,40 @@ hipError_t mxi_launch_dequantize(const uint8_t *c, const uint8_t *s, int bf16, i
                                  hipStream_t) {
   return rec("dequantize", n, bf16, -1, c, s, y, nullptr);
 }
-size_t mxi_block_mse_partials(int64_t n) { return n > 0 ? 2 * (size_t)((n + 511) / 512 > 2048 ? 2048 : (n + 511) / 512) : 2; }
+size_t mxi_block_mse_partials(int64_t n) {  // one pair per 512 items, a second level past 2048
+  int64_t g = n > 0 ? (n + 511) / 512 : 1;
+  if (g > 2048 * 2048) g = 2048 * 2048;
+  return 2 * (size_t)(g + (g > 2048 ? (g + 2047) / 2048 : 0));
+}
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *c, const uint8_t *s,
-                                int64_t n, float *bm, double *sums, double *part, hipStream_t) {
+                                int64_t n, float *bm, double *sums, double *part,
+                                int64_t space, hipStream_t) {
   g_last.p[4] = sums;
   g_last.p[5] = part;
+  g_last.space = space;
   return rec("block_mse", n, bf16, -1, x, c, s, bm);
 }
 hipError_t mxi_launch_quantize_fused(const void *x, int bf16, int mode, int64_t n, uint8_t *c,
                                      uint8_t *s, void *y, float *bm, double *sums, double *part,
-                                     hipStream_t) {
+                                     int64_t space, hipStream_t) {
   g_last.p[4] = sums;
   g_last.p[5] = part;
+  g_last.space = space;
   return rec(y ? "quantize_fused_y" : "quantize_fused", n, bf16, mode, x, c, s, bm);
+}
+size_t mxi_scratch_partials() { return 4096; }
+hipError_t mxi_scratch_address(int dev, double **out) {
+  *out = static_cast<double *>(const_cast<void *>(stub_scratch(dev)));
+  return hipSuccess;
+}
+// the device of a stream: device 1 for any non-null stream in these tests
+extern "C" hipError_t hipGetDevice(int *d) {
+  *d = 0;
+  return hipSuccess;
+}
+extern "C" hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t *d) {
+  *d = 1;
+  return hipSuccess;
 }
 hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t n, uint8_t *c, uint8_t *s,
                                 hipStream_t) {

@@ -20,38 +20,57 @@ def test_traffic_summary_calibration(tmp_path):
     d.mkdir()
     out = tmp_path / "out"
     out.mkdir()
-    copy = "__amd_rocclr_copyBuffer"
+    n = bench.STEP_ELEMS
+    copy = "void (anonymous namespace)::k_ceiling_copy(u32x4 const*, u32x4*, long)"
     fq = "void mxk::k_fakequant<true, 0>(void const*, void*, long)"
-    _write(d / "trace_kernel_stats.csv", ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
-           [[fq, 10, 22000.0, 21000.0, 23000.0], [copy, 5, 26000.0, 25000.0, 27000.0]])
-    # the copy moves 64 MiB each way; FETCH_SIZE sees half of its reads
-    hdr = ["Kernel_Name", "Grid_Size", "Counter_Value"]
-    _write(d / "fetch_counter_collection.csv", hdr,
-           [[copy, 4096, 32768.0], [copy, 64, 1.0], [fq, 8192, 32768.0]])
-    _write(d / "write_counter_collection.csv", hdr,
-           [[copy, 4096, 65536.0], [copy, 64, 2.0], [fq, 8192, 65536.0]])
+    wg = 256
+    grid = 196608 * wg  # work-items
+    # two fake-quant dispatches of 1000 us and 1100 us, one copy of 900 us
+    _write(d / "step_trace_kernel_trace.csv",
+           ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"],
+           [[fq, grid, wg, 0, 1_000_000], [fq, grid, wg, 2_000_000, 3_100_000],
+            [copy, grid, wg, 4_000_000, 4_900_000]])
+    # the copy moves 2n bytes each way; FETCH_SIZE sees half of its reads
+    kib = 2 * n / 1024
+    hdr = ["Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name", "Counter_Value"]
+    _write(d / "step_fetch_counter_collection.csv", hdr,
+           [[copy, grid, wg, "FETCH_SIZE", kib / 2], [fq, grid, wg, "FETCH_SIZE", kib / 2]])
+    _write(d / "step_write_counter_collection.csv", hdr,
+           [[copy, grid, wg, "WRITE_SIZE", kib], [fq, grid, wg, "WRITE_SIZE", kib]])
     bench.summarize_profiles(str(d), str(out))
     text = (out / os.path.basename(bench.TRAFFIC_FILE)).read_text()
     assert "FETCH_SIZE is scaled by 2.0000 and WRITE_SIZE by 1.0000" in text
-    # fake-quant: 32768 KiB fetched x 2 + 65536 KiB written = 128 MiB, its
+    # fake-quant: 2n bytes fetched (after scaling) + 2n written = 4n, its
     # algorithmic bytes exactly
-    assert f"traffic_bytes k_fakequant<true, 0> {128 << 20}" in text
+    assert f"traffic_bytes k_fakequant<true, 0> {4 * n}" in text
     assert "kernel_code_sha256_prefix " + bench.kernel_code_hash() in text
-    trace = (out / "mx_bf16_8192x4096_kernel_trace.md").read_text()
+    trace = (out / (bench.PROFILE_STEM["step"] + "_kernel_trace.md")).read_text()
     row = next(ln for ln in trace.splitlines() if ln.startswith("| `k_fakequant<true, 0>`"))
-    # 134217728 bytes in 22 us = 6101 GB/s = 76.3 % of 8 TB/s
-    assert "| 22.00 |" in row and "| 134217728 | 6101 | 76.3 |" in row
+    # 4n bytes in 1050 us on average
+    gbs = 4 * n / 1050e-6 / 1e9
+    assert f"| 196608 | {n} | 2 | 1050.00 | 1000.00 | 1100.00 | {4 * n} | {gbs:.0f} |" in row
+    assert f"{gbs / 80:.1f} |" in row
 
 
 def test_algorithmic_bytes_agree_with_the_step():
-    n = bench.BENCH_ELEMS
+    n = bench.STEP_ELEMS
     for op, k in bench.KERNEL_OF.items():
         assert bench.KERNEL_BYTES_PER_ELEM[k] == bench.BYTES_PER_ELEM[op]
     # NVFP4 quantize is its two kernels
     assert (bench.KERNEL_BYTES_PER_ELEM["k_absmax_partials<true>"]
             + bench.KERNEL_BYTES_PER_ELEM["k_quantize_nv<true, false>"]) * n \
         == bench.EXTRA_BYTES_PER_ELEM["quantize_nvfp4"] * n
-    assert bench.BYTES_PER_ELEM["fakequant_ocp"] * n == 134217728
+    # the step's buffer: 196 matrices, 2,818,572,288 elements
+    assert n == bench.__dict__["STEP_ELEMS"] == 28 * sum(
+        o * i for o, i in ((3072, 3072), (1024, 3072), (1024, 3072), (3072, 3072),
+                           (8192, 3072), (8192, 3072), (3072, 8192)))
+    assert bench.BYTES_PER_ELEM["fakequant_ocp"] * n == 11274289152
+    assert bench.BYTES_PER_ELEM["quantize_ocp"] * n == 7134511104
+
+
+def test_beside_phase_attributes_by_grid():
+    elems = bench.PHASES["beside"]["elems"]
+    assert elems(16384) == 16384 * 8192 and elems(4096) == 8192 * 4096
 
 
 def test_kernel_hash_ignores_comments_only(tmp_path, monkeypatch):

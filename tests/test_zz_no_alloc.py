@@ -1,8 +1,11 @@
 """mx_block_mse_noalloc (the block error without a workspace, for callers that
-cannot allocate) against mx_block_mse through the C ABI: per-block MSE and
-tensor sums bit for bit, on two calls in a row whose second tensor is
-smaller, in both dtypes, and with each output alone. Nothing here allocates
-between the calls it compares except the test's own output tensors."""
+cannot allocate) against mx_block_mse through the C ABI, on two calls in a
+row whose second tensor is smaller, in both dtypes, and with each output
+alone: per-block MSE bit for bit; tensor sums bit for bit where the
+workspace call's grid fits the fixed scratch (at most 2048 workgroups),
+else within a relative 1e-6 (the no-alloc launch caps its grid, so its
+partial sums fall on other workgroups). Nothing here allocates between the
+calls it compares except the test's own output tensors."""
 import os
 import sys
 
@@ -78,8 +81,12 @@ def test_noalloc_matches_workspace_call_twice_shrinking():
             _noalloc(x, c, s, got_bm, got_sums, stream)
             torch.cuda.synchronize()
             assert torch.equal(got_bm.view(torch.int32), want_bm.view(torch.int32))
-            assert torch.equal(got_sums.view(torch.int64), want_sums.view(torch.int64)), \
-                (got_sums.tolist(), want_sums.tolist())
+            if R * K <= 2048 * 1024 * 8:  # the workspace call's grid fits the scratch
+                assert torch.equal(got_sums.view(torch.int64), want_sums.view(torch.int64)), \
+                    (got_sums.tolist(), want_sums.tolist())
+            else:
+                for g, w in zip(got_sums.tolist(), want_sums.tolist()):
+                    assert abs(g - w) <= 1e-6 * abs(w), (g, w)
 
 
 def test_noalloc_each_output_alone_and_against_oracle():
@@ -125,4 +132,4 @@ def test_noalloc_on_a_side_stream():
     _noalloc(x, c, s, got_bm, got_sums, side.cuda_stream)
     side.synchronize()
     assert torch.equal(got_bm.view(torch.int32), want_bm.view(torch.int32))
-    assert torch.equal(got_sums.view(torch.int64), want_sums.view(torch.int64))
+    assert torch.equal(got_sums.view(torch.int64), want_sums.view(torch.int64))  # 512 workgroups
