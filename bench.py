@@ -301,7 +301,7 @@ def run_step(args, dev, stream):
     # reference kernels with the quantize kernel's tiling, on the same buffer
     cl = ceiling_lib()
     nit = n // 8
-    sink = torch.empty(196608, dtype=torch.int32, device=dev)
+    sink = torch.empty(-(-nit // 256), dtype=torch.int32, device=dev)  # a word per workgroup
     ceil_fn = {
         "quantize_shape": lambda i: cl.mxc_quantize_shape(xp, nit, b["c_oas"].data_ptr(),
                                                           b["s_oas"].data_ptr(), sh),
@@ -318,7 +318,8 @@ def run_step(args, dev, stream):
     ceilings["quantize_ocp_vs_quantize_shape"] = round(ceil_ms["quantize_shape"]
                                                        / op_ms["quantize_ocp"], 4)
     ceilings["fakequant_ocp_vs_copy"] = round(ceil_ms["copy"] / op_ms["fakequant_ocp"], 4)
-    ceilings["kernels"] = "bench_ceiling.hip (k_ceiling_*): the quantize kernel's tiling, no format arithmetic"
+    ceilings["kernels"] = ("bench_ceiling.hip (k_ceiling_*): one 16-byte item per thread, one tile "
+                           "per workgroup, no format arithmetic")
 
     bytes_op = {op: BYTES_PER_ELEM[op] * n for op in OPS}
     bytes_step = sum(bytes_op.values())

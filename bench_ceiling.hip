@@ -2,10 +2,12 @@
 // the MXFP4 kernels, to show what HBM allows for the same traffic shape on
 // this part. They are not part of the library and compute nothing of the
 // format: each moves exactly the bytes of one MXFP4 operation with as little
-// arithmetic as the compiler allows, on the tiling of the library's quantize
-// kernel (256-thread workgroups, 4 items of 16 bytes per thread spaced 256
-// apart, at most 196,608 workgroups with a grid stride, non-temporal 16-byte
-// loads and stores).
+// arithmetic as the compiler allows, in the streaming form that measured
+// fastest for these traffic shapes on multi-GB tensors: 256-thread
+// workgroups, one item of 16 bytes per thread, one tile per workgroup (no
+// grid cap), non-temporal 16-byte loads and stores. (On the 5.6 GB weight
+// buffer a copy ran at 81 % of 8 TB/s with one item per thread and 70 % with
+// four on a grid capped at 196,608 workgroups.)
 //
 //   mxc_quantize_shape: per 16-byte item read, one 4-byte word written (the
 //     code word) and, for every 4th item, one byte (the scale byte): the
@@ -20,8 +22,8 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
-constexpr int kItems = 4;
-constexpr int64_t kGridCap = 196608;
+constexpr int kItems = 1;
+constexpr int64_t kGridCap = 0x7FFFFFFF;
 
 unsigned grid_for(int64_t nitems) {
   const int64_t tile = (int64_t)kThreads * kItems;
@@ -122,7 +124,7 @@ int mxc_copy(const void *x, void *y, int64_t nitems, void *stream) {
   return (int)hipGetLastError();
 }
 
-// sink: at least as many 4-byte words as workgroups (196,608 at most).
+// sink: at least as many 4-byte words as workgroups (nitems / 256, rounded up).
 int mxc_read(const void *x, int64_t nitems, void *sink, void *stream) {
   hipLaunchKernelGGL(k_ceiling_read, dim3(grid_for(nitems)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(x),

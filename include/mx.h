@@ -173,9 +173,9 @@ mx_status_t mx_block_mse_noalloc(const void *x, mx_dtype_t x_dtype,
 
 /* Bytes of workspace mx_block_mse (and mx_quantize_fused) needs for a
  * [rows, k] tensor when asked for tensor_sums: 16 bytes per 4096 elements
- * (one partial pair per workgroup), plus 16 bytes per 2048 of those pairs
- * when there are more than 2048 (a second summing level); e.g. 131,136
- * bytes for 8192 x 4096 and 11,015,424 bytes for 2.8e9 elements (0.4 % of a
+ * (one partial pair per workgroup), plus 16 bytes per 8192 of those pairs
+ * when there are more than 8192 (a second summing level); e.g. 131,072
+ * bytes for 8192 x 4096 and 11,011,392 bytes for 2.8e9 elements (0.4 % of a
  * bf16 input). 0 for an invalid shape. */
 size_t mx_block_mse_workspace_size(int64_t rows, int64_t k);
 

@@ -781,28 +781,33 @@ __global__ __launch_bounds__(kThreads) void k_quantize_fused(const void *__restr
 }
 
 // Partial sums of the tensor error: each workgroup of an error launch writes
-// two (SSE, sum of x^2); one workgroup of k_sum_partials adds up to
-// kSumGroup pairs in a fixed order. An error launch uses at most
+// two (SSE, sum of x^2); one workgroup of k_sum_partials (1024 threads) adds
+// up to kSumGroup pairs in a fixed order. An error launch uses at most
 // kSumGroup^2 workgroups (beyond, workgroups loop over tiles), so at most two
-// sum levels run: up to kSumGroup partial pairs go straight to the result,
-// more go through one pair per kSumGroup first.
+// sum levels run: up to kSumGroup partial pairs (tensors up to ~3.4e7
+// elements) go straight to the result, more go through one pair per
+// kSumGroup first. (Groups of 2048 pairs put a second, dependent launch on
+// the 8192x4096 one-pass call: 3.5 us more than its earlier 2048-workgroup
+// grid.)
 #ifndef MX_SUM_GROUP
-#define MX_SUM_GROUP 2048
+#define MX_SUM_GROUP 8192
 #endif
 constexpr int64_t kSumGroup = MX_SUM_GROUP;
-constexpr int kSumPer = (int)(kSumGroup / kThreads);  // partial pairs per thread
-static_assert(kSumPer * kThreads == kSumGroup, "sum group must be a multiple of 256");
+constexpr int kSumThreads = 1024;
+constexpr int kSumPer = (int)(kSumGroup / kSumThreads);  // partial pairs per thread
+static_assert(kSumPer * kSumThreads == kSumGroup, "sum group must be a multiple of 1024");
 constexpr int64_t kPartialCap = kSumGroup * kSumGroup;
 
 // Workgroup b: out[2b + j] = sum over i of partial[2(b kSumGroup + i) + j]
 // for j = 0, 1 and the (up to kSumGroup) pairs i of its group; n pairs in
 // all. The kernel is latency-bound, so every thread issues all of its loads
-// (pairs t, t + 256, ...) before the first add; the sums then run in a fixed
-// order (per thread in pair order, a butterfly over the wave, the four waves
-// in order), so the result is deterministic. n == 0 writes 0.
-__global__ __launch_bounds__(kThreads) void k_sum_partials(const double *__restrict__ partial,
-                                                           int64_t n, double *__restrict__ out) {
-  __shared__ double wave_part[2][kThreads / 64];
+// (pairs t, t + 1024, ...) before the first add; the sums then run in a
+// fixed order (per thread in pair order, a butterfly over the wave, the
+// sixteen waves in order), so the result is deterministic. n == 0 writes 0.
+__global__ __launch_bounds__(kSumThreads) void k_sum_partials(const double *__restrict__ partial,
+                                                              int64_t n,
+                                                              double *__restrict__ out) {
+  __shared__ double wave_part[2][kSumThreads / 64];
   const int64_t first = (int64_t)blockIdx.x * kSumGroup;
   const int m = (int)(n - first < kSumGroup ? n - first : kSumGroup);  // pairs of this group
   double *o = out + 2 * blockIdx.x;
@@ -816,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void k_sum_partials(const double *__restr
   double v0[kSumPer], v1[kSumPer];
 #pragma unroll
   for (int j = 0; j < kSumPer; j++) {
-    const int i = (int)threadIdx.x + j * kThreads;
+    const int i = (int)threadIdx.x + j * kSumThreads;
     const int ic = min(i, m - 1);
     const double a = p[2 * ic], b = p[2 * ic + 1];
     v0[j] = i < m ? a : 0.0;
@@ -841,7 +846,7 @@ __global__ __launch_bounds__(kThreads) void k_sum_partials(const double *__restr
   if (threadIdx.x < 2) {
     double t = 0.0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; w++) t += wave_part[threadIdx.x][w];
+    for (int w = 0; w < kSumThreads / 64; w++) t += wave_part[threadIdx.x][w];
     o[threadIdx.x] = t;
   }
 }
@@ -1529,7 +1534,7 @@ size_t mxi_block_mse_partials(int64_t nitems) {
 static unsigned error_grid(int64_t nitems, int u, bool sums, int64_t partial_space) {
   const unsigned g = grid_for(nitems, kPartialCap, u);
   if (!sums || partial_doubles(g) <= partial_space) return g;
-  return grid_for(nitems, kSumGroup, u);
+  return grid_for(nitems, partial_space / 2 < kSumGroup ? partial_space / 2 : kSumGroup, u);
 }
 
 // Adds the `grid` partial pairs at `partial` into out[0..1]: one sum launch,
@@ -1537,16 +1542,16 @@ static unsigned error_grid(int64_t nitems, int u, bool sums, int64_t partial_spa
 // right after the first-level ones).
 static hipError_t sum_partials(double *partial, int64_t grid, double *out, hipStream_t st) {
   if (grid <= kSumGroup) {
-    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kThreads), 0, st, partial, grid, out);
+    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kSumThreads), 0, st, partial, grid, out);
     return hipGetLastError();
   }
   const int64_t groups = (grid + kSumGroup - 1) / kSumGroup;
   double *second = partial + 2 * grid;
-  hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)groups), dim3(kThreads), 0, st, partial,
+  hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)groups), dim3(kSumThreads), 0, st, partial,
                      grid, second);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kThreads), 0, st, second, groups, out);
+  hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kSumThreads), 0, st, second, groups, out);
   return hipGetLastError();
 }
 
@@ -1598,13 +1603,13 @@ hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *codes,
 //
 // The tensor sums of the block-error launch go through per-workgroup partial
 // sums, two doubles per workgroup. mx_block_mse_noalloc keeps them here
-// instead of in a caller workspace: one sum group's worth, 2 * kSumGroup
-// doubles (32 KiB), which holds every tensor size because that call's
-// launch is capped at kSumGroup workgroups (see error_grid). Each GPU the
-// library runs on holds its own copy, at its own address, until the process
-// ends; every call on a GPU shares it. A launch writes every partial slot it
-// reads before the sum kernel reads it, so nothing has to start at zero.
-constexpr size_t kScratchDoubles = 2 * (size_t)kSumGroup;
+// instead of in a caller workspace: 2 * 2048 doubles (32 KiB), which holds
+// every tensor size because that call's launch is capped at 2048 workgroups
+// when its fastest grid needs more (see error_grid). Each GPU the library
+// runs on holds its own copy, at its own address, until the process ends;
+// every call on a GPU shares it. A launch writes every partial slot it reads
+// before the sum kernel reads it, so nothing has to start at zero.
+constexpr size_t kScratchDoubles = 2 * 2048;
 static __device__ __align__(256) double scratch[kScratchDoubles];
 
 size_t mxi_scratch_partials() { return kScratchDoubles; }

@@ -40,10 +40,10 @@ hipError_t mxi_launch_dequantize(const uint8_t *c, const uint8_t *s, int bf16, i
                                  hipStream_t) {
   return rec("dequantize", n, bf16, -1, c, s, y, nullptr);
 }
-size_t mxi_block_mse_partials(int64_t n) {  // one pair per 512 items, a second level past 2048
+size_t mxi_block_mse_partials(int64_t n) {  // one pair per 512 items, a second level past 8192
   int64_t g = n > 0 ? (n + 511) / 512 : 1;
-  if (g > 2048 * 2048) g = 2048 * 2048;
-  return 2 * (size_t)(g + (g > 2048 ? (g + 2047) / 2048 : 0));
+  if (g > 8192LL * 8192) g = 8192LL * 8192;
+  return 2 * (size_t)(g + (g > 8192 ? (g + 8191) / 8192 : 0));
 }
 hipError_t mxi_launch_block_mse(const void *x, int bf16, const uint8_t *c, const uint8_t *s,
                                 int64_t n, float *bm, double *sums, double *part,

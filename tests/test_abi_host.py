@@ -120,21 +120,21 @@ def test_aliasing(lib):
 
 def _expected_workspace(rows, k):
     """16 bytes per workgroup of the one-pass grid (512 items = 4096 elements
-    each, at most 2048^2 of them), plus 16 per group of 2048 partial pairs
+    each, at most 8192^2 of them), plus 16 per group of 8192 partial pairs
     when there is more than one group."""
     items = rows * k // 8
-    grid = max(1, min(-(-items // 512), 2048 * 2048))
-    groups = -(-grid // 2048) if grid > 2048 else 0
+    grid = max(1, min(-(-items // 512), 8192 * 8192))
+    groups = -(-grid // 8192) if grid > 8192 else 0
     return 16 * (grid + groups)
 
 
 def test_workspace(lib):
     need = mx.mx_block_mse_workspace_size(8192, 4096)
-    assert need == _expected_workspace(8192, 4096) == 16 * (8192 + 4)
+    assert need == _expected_workspace(8192, 4096) == 16 * 8192
     for rows, k in ((0, 64), (1, 32), (16, 4096), (917504, 3072), (1 << 26, 4096)):
         assert mx.mx_block_mse_workspace_size(rows, k) == _expected_workspace(rows, k), (rows, k)
     # the 2.8e9-element weight set: 11 MB, 0.4 % of the bf16 input
-    assert mx.mx_block_mse_workspace_size(917504, 3072) == 16 * (688128 + 336)
+    assert mx.mx_block_mse_workspace_size(917504, 3072) == 16 * (688128 + 84)
     # missing / small / misaligned workspace when the tensor sum is asked for
     assert mx.mx_block_mse(A, 1, B, C, 8192, 4096, None, W, None, 0, None) == mx.MX_ERR_WORKSPACE
     assert mx.mx_block_mse(A, 1, B, C, 8192, 4096, None, W, W + 64, need - 8, None) == \
