@@ -39,6 +39,7 @@ import ctypes
 import json
 import math
 import os
+import re
 import subprocess
 import sys
 import time
@@ -100,9 +101,15 @@ C5_BYTES_PER_ELEM = {"quantize_ocp": 2 + 0.5 + 1 / 32, "quantize_oas": 2 + 0.5 +
 # reference kernels (bench_ceiling.hip) on the step's buffer
 CEILING_BYTES_PER_ELEM = {"quantize_shape": 2 + 0.5 + 1 / 32, "copy": 4.0, "read": 2.0,
                           "write": 2.0}
-KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0>", "quantize_oas": "k_quantize<true, 1>",
-             "dequantize_bf16": "k_dequantize<true>", "fakequant_ocp": "k_fakequant<true, 0>",
-             "block_mse": "k_block_mse<true, true>"}
+# Kernel family of each op (the kernels' last template argument, U, is the
+# number of 8-element items per thread, which the library picks by size)
+KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0, U>", "quantize_oas": "k_quantize<true, 1, U>",
+             "dequantize_bf16": "k_dequantize<true, U>",
+             "fakequant_ocp": "k_fakequant<true, 0, U>", "block_mse": "k_block_mse<true, true, U>"}
+# kernels with items-per-thread as their last template argument, and one
+# tile (256 threads x U items x 8 elements) per workgroup at these sizes
+U_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize", "k_block_mse")
+FUSED_ITEMS = 2  # items per thread of k_quantize_fused
 PROFILE_STEM = {"step": "mx_llama32_3b_linears",
                 "beside": "mx_student_t_8192x4096_laplace_16384x8192"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", PROFILE_STEM["step"] + "_hbm_traffic.md")
@@ -130,9 +137,27 @@ def kernel_code_hash() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
+def kernel_family(k: str) -> str:
+    """k_quantize<true, 0, 1> -> k_quantize<true, 0, U>; other names as they are."""
+    m = re.fullmatch(r"(k_\w+)<(.*), (\d+)>", k)
+    if m and m.group(1) in U_KERNELS:
+        return f"{m.group(1)}<{m.group(2)}, U>"
+    return k
+
+
+def items_per_thread(k: str):
+    """U of a kernel whose grid is one tile per workgroup, else None."""
+    m = re.fullmatch(r"(k_\w+)<.*, (\d+)>", k)
+    if m and m.group(1) in U_KERNELS:
+        return int(m.group(2))
+    if k.startswith("k_quantize_fused<"):
+        return FUSED_ITEMS
+    return None
+
+
 def measured_traffic(op):
-    """HBM bytes per launch of op's kernel on the step's buffer from the
-    committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None if that
+    """(kernel, HBM bytes per launch) of op's kernel on the step's buffer from
+    the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None if that
     summary was taken on different kernel code than the one built here."""
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
@@ -141,10 +166,10 @@ def measured_traffic(op):
         return None
     if ("kernel_code_sha256_prefix " + h) not in lines:
         return None
-    key = "traffic_bytes " + KERNEL_OF[op] + " "
     for ln in lines:
-        if ln.startswith(key):
-            return int(ln.split()[-1])
+        f = ln.split(" ")
+        if f[0] == "traffic_bytes" and kernel_family(" ".join(f[1:-1])) == KERNEL_OF[op]:
+            return " ".join(f[1:-1]), int(f[-1])
     return None
 
 
@@ -326,9 +351,11 @@ def run_step(args, dev, stream):
     breakdown = {op: _row(bytes_op[op], op_ms[op]) for op in OPS}
     dom = max(OPS, key=lambda o: op_ms[o])
     dom_gbs = bytes_op[dom] / (op_ms[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": KERNEL_OF[dom], "op": dom, "achieved": round(dom_gbs, 1),
+    mt = measured_traffic(dom)
+    roofline = {"bound": "hbm", "kernel": mt[0] if mt else KERNEL_OF[dom], "op": dom,
+                "achieved": round(dom_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom),
+                "traffic": mt[1] if mt else None,
                 "bytes_per_launch": int(bytes_op[dom]),
                 "avg_launch_us": round(op_ms[dom] * 1e3, 2)}
 
@@ -1001,15 +1028,15 @@ def suite(args, dev):
 # rocprofv3 prints. NVFP4 quantize is two kernels: the tensor-maximum pass
 # reads x, the block pass reads it again and writes codes and scales.
 KERNEL_BYTES_PER_ELEM = {
-    "k_quantize<true, 0>": BYTES_PER_ELEM["quantize_ocp"],
-    "k_quantize<true, 1>": BYTES_PER_ELEM["quantize_oas"],
-    "k_quantize<true, 2>": EXTRA_BYTES_PER_ELEM["quantize_oas_bits"],
-    "k_quantize<true, 3>": EXTRA_BYTES_PER_ELEM["quantize_oas_nf"],
-    "k_dequantize<true>": BYTES_PER_ELEM["dequantize_bf16"],
-    "k_fakequant<true, 0>": BYTES_PER_ELEM["fakequant_ocp"],
-    "k_fakequant<true, 1>": EXTRA_BYTES_PER_ELEM["fakequant_oas"],
-    "k_fakequant<true, 3>": EXTRA_BYTES_PER_ELEM["fakequant_oas_nf"],
-    "k_block_mse<true, true>": BYTES_PER_ELEM["block_mse"],
+    "k_quantize<true, 0, U>": BYTES_PER_ELEM["quantize_ocp"],
+    "k_quantize<true, 1, U>": BYTES_PER_ELEM["quantize_oas"],
+    "k_quantize<true, 2, U>": EXTRA_BYTES_PER_ELEM["quantize_oas_bits"],
+    "k_quantize<true, 3, U>": EXTRA_BYTES_PER_ELEM["quantize_oas_nf"],
+    "k_dequantize<true, U>": BYTES_PER_ELEM["dequantize_bf16"],
+    "k_fakequant<true, 0, U>": BYTES_PER_ELEM["fakequant_ocp"],
+    "k_fakequant<true, 1, U>": EXTRA_BYTES_PER_ELEM["fakequant_oas"],
+    "k_fakequant<true, 3, U>": EXTRA_BYTES_PER_ELEM["fakequant_oas_nf"],
+    "k_block_mse<true, true, U>": BYTES_PER_ELEM["block_mse"],
     "k_quantize8<true>": EXTRA_BYTES_PER_ELEM["quantize_mxfp8"],
     "k_dequantize8<true>": EXTRA_BYTES_PER_ELEM["dequantize_mxfp8_bf16"],
     "k_fakequant8<true>": EXTRA_BYTES_PER_ELEM["fakequant_mxfp8"],
@@ -1027,16 +1054,31 @@ KERNEL_BYTES_PER_ELEM = {
     "k_ceiling_write": CEILING_BYTES_PER_ELEM["write"],
 }
 CALIBRATION_KERNEL = "k_ceiling_copy"  # reads and writes 2 bytes per element, known exactly
+
+
+def kernel_bytes_per_elem(k: str):
+    """Algorithmic bytes per element of kernel k (a name as _kernel_short gives)."""
+    return KERNEL_BYTES_PER_ELEM.get(kernel_family(k))
+
+
+def tile_elems(k: str, grid: int):
+    """Elements a dispatch of k covers when it runs one tile per workgroup
+    (256 threads x U items x 8 elements), else None."""
+    u = items_per_thread(k)
+    return grid * 256 * u * 8 if u else None
+
+
 # The two parts of bench.py that are profiled, each on its own (--only):
-# elements a dispatch covers, from its grid (workgroups). In the part beside
-# the step only the Laplace quantize launches run 16,384 workgroups.
+# elements a dispatch covers, from its kernel and grid (workgroups). Beside
+# the step only the Laplace quantize launches cover C5_ELEMS.
 PHASES = {
     "step": {"title": "Llama-3.2-3B linears, 196 matrices end to end, bf16 [917504, 3072] "
                       "(bench.py step)",
-             "elems": lambda grid: STEP_ELEMS},
+             "elems": lambda k, grid: STEP_ELEMS},
     "beside": {"title": "bf16 Student-t activations [8192, 4096] and Laplace activations "
                         "[16384, 8192] (bench.py, beside the step)",
-               "elems": lambda grid: C5_ELEMS if grid == 16384 else C2_ELEMS},
+               "elems": lambda k, grid: C5_ELEMS if tile_elems(k, grid) == C5_ELEMS
+               else C2_ELEMS},
 }
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT -o {p}_trace -- \\\n"
@@ -1060,11 +1102,9 @@ PROFILE_HOW = ("Each rocprofv3 command runs on its own, from a scratch working d
 
 
 def _kernel_short(name: str) -> str:
-    for k in KERNEL_BYTES_PER_ELEM:
-        if k in name:
-            return k
-    return name.split("(")[0].replace("void ", "").replace("mxk::", "").replace(
-        "(anonymous namespace)::", "")
+    """'void mxk::k_quantize<true, 0, 1>(void const*, ...)' -> 'k_quantize<true, 0, 1>'."""
+    m = re.search(r"\b(k_\w+(?:<[^()]*>)?)\(", name)
+    return m.group(1) if m else name.split("(")[0]
 
 
 def _dispatch_groups(path: str, elems):
@@ -1078,7 +1118,7 @@ def _dispatch_groups(path: str, elems):
             k = _kernel_short(r["Kernel_Name"])
             grid = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            groups.setdefault((k, grid, elems(grid)), []).append(dur)
+            groups.setdefault((k, grid, elems(k, grid)), []).append(dur)
     return groups
 
 
@@ -1091,7 +1131,7 @@ def _counter_groups(path: str, elems):
         for r in csv.DictReader(f):
             k = _kernel_short(r["Kernel_Name"])
             grid = int(r["Grid_Size"]) // max(1, int(r.get("Workgroup_Size", 256) or 256))
-            agg[(k, grid, elems(grid))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            agg[(k, grid, elems(k, grid))][r["Counter_Name"]].append(float(r["Counter_Value"]))
     return {key: {c: sum(v) / len(v) for c, v in d.items()} for key, d in agg.items()}
 
 
@@ -1123,7 +1163,7 @@ def summarize_profiles(d: str, out_dir: str = os.path.join(ROOT, "profiles")) ->
             for (k, grid, n), v in _dispatch_groups(trace, ph["elems"]).items():
                 avg = sum(v) / len(v)
                 avg_us[(k, grid)] = avg
-                bpe = KERNEL_BYTES_PER_ELEM.get(k)
+                bpe = kernel_bytes_per_elem(k)
                 if bpe is None and k != "k_sum_partials":
                     continue
                 b = int(bpe * n) if bpe else None
@@ -1155,7 +1195,7 @@ def summarize_profiles(d: str, out_dir: str = os.path.join(ROOT, "profiles")) ->
             machine = []
             for key in cf:
                 k, grid, n = key
-                bpe = KERNEL_BYTES_PER_ELEM.get(k)
+                bpe = kernel_bytes_per_elem(k)
                 if bpe is None or key not in cw:
                     continue
                 fk, wk = cf[key]["FETCH_SIZE"], cw[key]["WRITE_SIZE"]
@@ -1193,7 +1233,7 @@ def _summarize_instruction_mix(path: str, avg_us: dict, ph: dict, cmd: str, code
            "wave-item | VMEM wr / wave-item | LDS / wave-item | VALU issue us | kernel us | "
            "VALU issue / kernel |", "|---|---|---|---|---|---|---|---|---|---|---|"]
     for (k, grid, n), c in _counter_groups(path, ph["elems"]).items():
-        if k not in KERNEL_BYTES_PER_ELEM:
+        if kernel_bytes_per_elem(k) is None:
             continue
         wave_items = n / (8 * 64)
         per = lambda name: c.get(name, 0.0) / wave_items  # noqa: E731
@@ -1209,20 +1249,27 @@ def _summarize_instruction_mix(path: str, avg_us: dict, ph: dict, cmd: str, code
 
 def _summarize_suite(path: str, code: str, out_dir: str) -> None:
     """Per-workload kernel times of `bench.py --suite` from its kernel trace.
-    Launches are told apart by kernel, dtype and grid size; the two
-    196,608-workgroup groups by dispatch order (see the note written out)."""
+    Launches are told apart by kernel, dtype and the elements their grid
+    covers (one tile per workgroup); the Laplace launches' cold and warm
+    timings by dispatch order."""
     import collections
     import csv
 
     with open(path) as f:
         rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
-    short = lambda n: n.split("(")[0].replace("void ", "").replace("mxk::", "")  # noqa: E731
     c1, c5 = 1024 * 4096, 16384 * 8192
     l3072, l8192 = 688128 * 3072, 86016 * 8192
     m13, m2 = 128 * 3072 * 4096, 128 * 4096 * 1536
+    by_elems = {
+        c5: "bf16 Laplace [16384, 8192]",
+        1024 * 3072: "Llama-3.2-3B per-matrix launches: k/v [1024, 3072]",
+        3072 * 3072: "Llama-3.2-3B per-matrix launches: q/o [3072, 3072]",
+        8192 * 3072: "Llama-3.2-3B per-matrix launches: gate/up [8192, 3072] and down [3072, 8192]",
+        l3072: "Llama-3.2-3B grouped by K: K=3072 [688128, 3072]",
+        l8192: "Llama-3.2-3B grouped by K: K=8192 [86016, 8192]",
+        STEP_ELEMS: "Llama-3.2-3B, 196 matrices end to end: one launch [917504, 3072]",
+        m13: "MoE w13 [128x3072, 4096]", m2: "MoE w2 [128x4096, 1536]"}
     passes = 2 * BIG_TIMED + BIG_WARM  # dispatches of one big-workload timing
-    per_matrix = {384: ("k/v [1024, 3072]", 1024 * 3072), 1152: ("q/o [3072, 3072]", 3072 * 3072),
-                  3072: ("gate/up [8192, 3072] and down [3072, 8192]", 8192 * 3072)}
 
     def bytes_for(kernel, n, f32):
         if kernel == "k_ceiling_copy":  # the fp32 input copied: 4 bytes in, 4 out
@@ -1237,19 +1284,20 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
 
     # the timed part ends with the MoE dequantize launches; the QSNR pass
     # that follows is not timed and is left out
+    grid_of = lambda r: int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))  # noqa: E731
     last = max(i for i, r in enumerate(rows)
-               if short(r["Kernel_Name"]) == "k_dequantize<true>"
-               and int(r["Grid_Size_X"]) // 256 in (196608, 98304))
+               if _kernel_short(r["Kernel_Name"]).startswith("k_dequantize<true,")
+               and tile_elems(_kernel_short(r["Kernel_Name"]), grid_of(r)) in (m13, m2))
     groups = collections.OrderedDict()
-    seen196 = 0
     seen_c5 = collections.Counter()
     per_timing = 10 + 2 * 100  # dispatches of one _launch_stats call at the suite's defaults
     for r in rows[:last + 1]:
-        k = short(r["Kernel_Name"]).replace("(anonymous namespace)::", "")
+        k = _kernel_short(r["Kernel_Name"])
         if not k.startswith("k_"):
             continue
-        grid = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        grid = grid_of(r)
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        n = tile_elems(k, grid)
         if k.startswith("k_multi"):
             key = ("MULTI", k, None)
         elif k == "k_sum_partials":
@@ -1258,50 +1306,26 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
             key = ("fp32 normal [1024, 4096]: reference kernels", k, c1)
         elif "<false" in k:
             key = ("fp32 normal [1024, 4096]", k, c1)
-        elif grid == 16384 or k.startswith("k_block_mse"):
+        elif n == c5:
             # each op is timed cold (rotated sets), then warm (one set): runs
             # of per_timing dispatches alternate
             cold = (seen_c5[k] // per_timing) % 2 == 0
             seen_c5[k] += 1
-            key = ("bf16 Laplace [16384, 8192], " + ("cold (rotated sets)" if cold
-                                                     else "warm (one set, cache-resident)"), k, c5)
-        elif grid in per_matrix and k.startswith("k_quantize<"):
-            key = ("Llama-3.2-3B per-matrix launches: " + per_matrix[grid][0], k,
-                   per_matrix[grid][1])
-        elif grid == 86016:
-            key = ("Llama-3.2-3B grouped by K: K=8192 [86016, 8192]", k, l8192)
-        elif grid == 98304:
-            key = ("MoE w2 [128x4096, 1536]", k, m2)
-        elif grid == 196608 and k.startswith("k_quantize<"):
-            seen196 += 1
-            if seen196 <= passes:
-                key = ("Llama-3.2-3B grouped by K: K=3072 [688128, 3072]", k, l3072)
-            elif seen196 <= 2 * passes:
-                key = ("Llama-3.2-3B, 196 matrices end to end: one launch [917504, 3072]", k,
-                       STEP_ELEMS)
-            else:
-                key = ("MoE w13 [128x3072, 4096]", k, m13)
-        elif grid == 196608 and k.startswith("k_dequantize<"):
-            key = ("MOEDQ", k, None)
-        elif grid == 196608:
-            key = ("MoE w13 [128x3072, 4096]", k, m13)
+            key = (by_elems[c5] + (", cold (rotated sets)" if cold
+                                   else ", warm (one set, cache-resident)"), k, c5)
+        elif n in by_elems:
+            key = (by_elems[n], k, n)
         else:
             key = (f"unattributed (grid {grid})", k, None)
         groups.setdefault(key, []).append(dur)
     multi = groups.pop(("MULTI", "k_multi<true, 0, false>", None), None)
-    moedq = groups.pop(("MOEDQ", "k_dequantize<true>", None), None)
-    if moedq:  # w13 and w2 alternate
-        groups[("MoE w13 [128x3072, 4096]", "k_dequantize<true>", m13)] = moedq[0::2]
-        groups[("MoE w2 [128x4096, 1536]", "k_dequantize<true>", m2)] = moedq[1::2]
     out = ["# Kernel trace: the other workloads (`bench.py --suite`)\n", PROFILE_HOW + "\n",
            "```\n" + PROFILE_CMDS["suite"] + "\n```\n", code,
            "Durations are the GPU's own per-dispatch times from the trace (under the profiler the "
            "host-side event figures of the small fp32 case are inflated by per-dispatch overhead; "
-           "these are not). Launches are attributed to their workload by grid size; the K=3072 "
-           "Llama group, the 196 Llama matrices as one buffer and the MoE w13 tensor all run "
-           "196,608 workgroups and are told apart by dispatch order (the suite runs them in that "
-           f"order, {passes} of each), and the MoE dequantize launches (both 196,608 workgroups) "
-           "alternate w13, w2. The Laplace launches are split into the cold (rotated sets) and "
+           "these are not). Launches are attributed to their workload by the elements their grid "
+           "covers (256 threads x U items x 8 elements per workgroup, U the kernel's last "
+           "template argument; the workloads' sizes all differ). The Laplace launches are split into the cold (rotated sets) and "
            f"warm (one set) timings by dispatch order ({per_timing} dispatches each). "
            "Per-matrix Llama launches are grouped by shape. The fp32 rows mix cold, warm, "
            "single-launch and graph-replayed dispatches. The suite's QSNR pass, which runs after "

@@ -80,6 +80,14 @@ __device__ __forceinline__ uint32_t dpp_x2(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
 }
 
+// rotate right by 4 / 8 lanes within each row of 16
+__device__ __forceinline__ uint32_t dpp_ror4(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t dpp_ror8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);
+}
+
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
   v = max(v, dpp_x1(v));
   v = max(v, dpp_x2(v));
@@ -107,6 +115,19 @@ __device__ __forceinline__ double dpp_x2_f64(double v) {
 __device__ __forceinline__ double quad_sum_f64(double p) {
   p = p + dpp_x1_f64(p);
   p = p + dpp_x2_f64(p);
+  return p;
+}
+
+// Sum of the 16 lanes of a row on every lane of the row: the quad sums, then
+// the other quads' sums rotated in (4 lanes, then 8), in one fixed order.
+__device__ __forceinline__ double row_sum_f64(double p) {
+  p = quad_sum_f64(p);
+  uint64_t u = __double_as_longlong(p);
+  p = p + __longlong_as_double(((uint64_t)dpp_ror4((uint32_t)(u >> 32)) << 32) |
+                               dpp_ror4((uint32_t)u));
+  u = __double_as_longlong(p);
+  p = p + __longlong_as_double(((uint64_t)dpp_ror8((uint32_t)(u >> 32)) << 32) |
+                               dpp_ror8((uint32_t)u));
   return p;
 }
 
@@ -484,20 +505,22 @@ template <bool BF16>
 constexpr int kU = BF16 ? kUnroll : (kUnroll >= 4 ? kUnroll / 4 : 1);
 
 // Items per thread for the MXFP4 kernels, by what the kernel does and by
-// tensor size (each op measured alone). Up to kLargeItems items (tensors up
-// to ~1e9 elements, which the 256 MB Infinity Cache may partly hold): bf16
-// quantize in every mode keeps kU (two items per thread was 7 % slower on
-// 8192x4096 for OCP and OAS, and 7 % slower on 16384x8192 for OAS_NF; eight
-// 3-13 % slower), while bf16 dequantize and fake-quant take two (fewer
-// registers and more workgroups in flight for the write-heavy stream; one
-// fp32 fake-quant item was 5 % slower on fp32 1024x4096). Beyond it (multi-GB
-// weight sets streamed once from HBM) fewer items per thread keep the memory
-// that the resident workgroups touch at one time compact: on the 2.8e9-element
-// Llama-3.2-3B weight set, quantize OCP with one item per thread was 3.5 %
-// faster than four, overflow-aware quantize with two 3.6 % faster, fake-quant
-// with one 5 % faster than two; OAS_NF quantize keeps four and dequantize two.
-// The multi-tensor launch uses the small-tensor numbers (its tile offsets
-// depend on them).
+// tensor size (each op measured alone, with the three-phase tile loop).
+// Below kLargeItems items (tensors below ~2e8 elements, 400 MB of bf16, which
+// the 256 MB Infinity Cache may partly hold): bf16 quantize keeps kU in OCP,
+// OAS and OAS_BITS (OAS with two items per thread was 2 % slower on
+// 8192x4096, equal on 16384x8192), while OAS_NF quantize takes two (4 % faster on
+// 8192x4096, where its two error evaluations per block make it
+// arithmetic-bound; equal on 16384x8192); bf16 dequantize and fake-quant take
+// two (fewer registers and more workgroups in flight for the write-heavy
+// stream; one fp32 fake-quant item was 5 % slower on fp32 1024x4096). Beyond
+// it (multi-GB weight sets streamed once from HBM) fewer items per thread keep
+// the memory that the resident workgroups touch at one time compact: on the
+// 2.8e9-element Llama-3.2-3B weight set, quantize OCP with one item per thread
+// was 3.5 % faster than four, overflow-aware quantize with two 3.6 % faster,
+// fake-quant with one 5 % faster than two; OAS_NF quantize keeps four and
+// dequantize two. The multi-tensor launch uses the small-tensor numbers (its
+// tile offsets depend on them).
 #ifndef MX_LARGE_ITEMS
 #define MX_LARGE_ITEMS (int64_t(3) << 23)
 #endif
@@ -511,7 +534,8 @@ constexpr int unroll_of(bool bf16, int mode, int kind, bool large = false) {
   }
   if (kind == kKindFakequant) return 2;
   if (!bf16) return kU<false>;
-  return kind == kKindQuantize ? kU<true> : 2;
+  if (kind == kKindQuantize) return mode == MX_SCALE_OAS_NF ? 2 : kU<true>;
+  return 2;
 }
 
 template <bool BF16, int MODE, int U>
@@ -682,24 +706,23 @@ __device__ __forceinline__ float mse_item(const Item<BF16> &x, uint32_t c, uint3
   return (float)(sse * (1.0 / 32.0));
 }
 
-// The workgroup's two tensor sums, in a fixed order (butterfly over each
-// wave, then the waves in turn), to partial[2 * blockIdx.x + {0, 1}].
+// The workgroup's two tensor sums, in a fixed order (DPP sums over each row
+// of 16 lanes, then the rows in turn), to partial[2 * blockIdx.x + {0, 1}].
+// Row sums through LDS cost fewer instructions than a 64-lane butterfly of
+// cross-lane shuffles; every lane is active here.
 __device__ __forceinline__ void write_partials(double mine, double mine_sq,
                                                double *__restrict__ partial) {
-  __shared__ double wave_part[2][kThreads / 64];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    mine += __shfl_xor(mine, off, 64);
-    mine_sq += __shfl_xor(mine_sq, off, 64);
-  }
-  if ((threadIdx.x & 63) == 0) {
-    wave_part[0][threadIdx.x >> 6] = mine;
-    wave_part[1][threadIdx.x >> 6] = mine_sq;
+  __shared__ double row_part[2][kThreads / 16];
+  mine = row_sum_f64(mine);
+  mine_sq = row_sum_f64(mine_sq);
+  if ((threadIdx.x & 15) == 0) {
+    row_part[0][threadIdx.x >> 4] = mine;
+    row_part[1][threadIdx.x >> 4] = mine_sq;
   }
   __syncthreads();
   if (threadIdx.x < 2) {
     double t = 0.0;
-    for (int w = 0; w < kThreads / 64; w++) t += wave_part[threadIdx.x][w];
+    for (int r = 0; r < kThreads / 16; r++) t += row_part[threadIdx.x][r];
     partial[2 * blockIdx.x + threadIdx.x] = t;
   }
 }
@@ -1230,13 +1253,6 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_nv(const uint32_t *__re
 // (at most 2 + 9 significant bits). A sub-block holding NaN/Inf stores the
 // NaN byte and the signs of x, as a NaN MXFP4 block does.
 
-// rotate right by 4 / 8 lanes within each row of 16
-__device__ __forceinline__ uint32_t dpp_ror4(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true);
-}
-__device__ __forceinline__ uint32_t dpp_ror8(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);
-}
 // Decoded values of one item: E2M1 * 2^(s-127) * (1 + m/256), exact in fp32
 // (at most 2 + 9 significant bits), rounded to bf16 if asked; sub-block byte
 // 255 gives the canonical NaN.
