@@ -155,22 +155,73 @@ def items_per_thread(k: str):
     return None
 
 
-def measured_traffic(op):
-    """(kernel, HBM bytes per launch) of op's kernel on the step's buffer from
-    the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None if that
-    summary was taken on different kernel code than the one built here."""
+def _traffic_lines(path):
+    """{kernel: HBM bytes per launch} from a committed rocprofv3 traffic
+    summary, or None if it was taken on different kernel code than the one
+    built here."""
     try:
-        lines = open(TRAFFIC_FILE).read().splitlines()
+        lines = open(path).read().splitlines()
         h = kernel_code_hash()
     except OSError:
         return None
     if ("kernel_code_sha256_prefix " + h) not in lines:
         return None
+    out = {}
     for ln in lines:
         f = ln.split(" ")
-        if f[0] == "traffic_bytes" and kernel_family(" ".join(f[1:-1])) == KERNEL_OF[op]:
-            return " ".join(f[1:-1]), int(f[-1])
+        if f[0] == "traffic_bytes":
+            out[" ".join(f[1:-1])] = int(f[-1])
+    return out
+
+
+def measured_traffic(op, path=None, family=None):
+    """(kernel, HBM bytes per launch) of op's kernel (or of the kernel family
+    given) from the committed FETCH_SIZE/WRITE_SIZE summary of the step (or
+    of path), or None while that summary belongs to other kernel code."""
+    t = _traffic_lines(path or TRAFFIC_FILE)
+    if t is None:
+        return None
+    fam = family or KERNEL_OF[op]
+    for k, b in t.items():
+        if kernel_family(k) == fam:
+            return k, b
     return None
+
+
+# Kernel families of the ops timed beside the step (one instantiation each
+# there), for their measured traffic; NVFP4 quantize is two kernels.
+BESIDE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", PROFILE_STEM["beside"] + "_hbm_traffic.md")
+BESIDE_KERNELS = {
+    "fakequant_ocp": ["k_fakequant<true, 0, U>"], "fakequant_oas": ["k_fakequant<true, 1, U>"],
+    "fakequant_oas_nf": ["k_fakequant<true, 3, U>"],
+    "quantize_oas_bits": ["k_quantize<true, 2, U>"], "quantize_oas_nf": ["k_quantize<true, 3, U>"],
+    "quantize_mxfp8": ["k_quantize8<true>"], "dequantize_mxfp8_bf16": ["k_dequantize8<true>"],
+    "fakequant_mxfp8": ["k_fakequant8<true>"],
+    "quantize_nvfp4": ["k_absmax_partials<true>", "k_quantize_nv<true, false>"],
+    "dequantize_nvfp4_bf16": ["k_dequantize_nv<true>"],
+    "fakequant_nvfp4": ["k_absmax_partials<true>", "k_quantize_nv<true, true>"],
+    "quantize_mbs": ["k_quantize_mbs<true, false>"], "dequantize_mbs_bf16": ["k_dequantize_mbs<true>"],
+    "fakequant_mbs": ["k_quantize_mbs<true, true>"],
+    "quantize_fused": ["k_quantize_fused<true, 0, true>"],
+    "reference_copy": ["k_ceiling_copy"],
+    "quantize_ocp": ["k_quantize<true, 0, U>"], "quantize_oas": ["k_quantize<true, 1, U>"],
+}
+
+
+def beside_roofline(op, row):
+    """Roofline fields of one op timed beside the step: its achieved rate
+    against the 8 TB/s peak, and the HBM bytes its kernels moved per call
+    in the committed profile of this part (None while stale)."""
+    traffic = 0
+    for fam in BESIDE_KERNELS[op]:
+        mt = measured_traffic(op, BESIDE_TRAFFIC_FILE, fam)
+        if mt is None:
+            traffic = None
+            break
+        traffic += mt[1]
+    return {"bound": "hbm", "achieved": row["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": row["frac_hbm"], "traffic": traffic, "bytes_per_launch": row["bytes"],
+            "avg_launch_us": row["us"]}
 
 
 def build_ceiling(verbose: bool = False) -> str:
@@ -373,7 +424,11 @@ def run_step(args, dev, stream):
                             "qsnr_db": round(10 * math.log10(ssq2 / sse2), 4)}
     del b, ws, sink
     torch.cuda.empty_cache()
+    # block MSE's summing launches: a second level when the workspace holds
+    # more than one pair per 4096 elements (16 bytes per 8192 partials)
+    sum_launches = 1 + int(ws_bytes // 16 > -(-n // 4096))
     return dict(x=x, n=n, ms_per_step=ms_per_step, wall=wall, bytes_step=bytes_step,
+                sum_launches=sum_launches,
                 breakdown=breakdown, roofline=roofline, ceilings=ceilings, quality=quality,
                 copy_us=ceil_ms["copy"] * 1e3)
 
@@ -474,16 +529,18 @@ def run_beside(args, dev, stream):
             run(op, sets[i])
         torch.cuda.synchronize()
         ms = _timed_launches(lambda i, op=op: run(op, sets[i % n_sets]), m, stream)
-        out[f"{op} [8192, 4096]"] = _row(bpe * n, ms, workload=C2_WORKLOAD,
-                                         cache=f"cold ({n_sets} rotated sets)")
+        row = _row(bpe * n, ms, workload=C2_WORKLOAD, cache=f"cold ({n_sets} rotated sets)")
+        row["roofline"] = beside_roofline(op, row)
+        out[f"{op} [8192, 4096]"] = row
     # the reference copy of the same tensor, timed the same way (and the
     # counter calibration kernel of this part's profiles)
     cl = ceiling_lib()
     ms = _timed_launches(lambda i: cl.mxc_copy(sets[i % n_sets]["x"].data_ptr(),
                                                sets[i % n_sets]["y_fq"].data_ptr(), n // 8, sh),
                          m, stream)
-    out["reference_copy [8192, 4096]"] = _row(4.0 * n, ms, workload=C2_WORKLOAD,
-                                              cache=f"cold ({n_sets} rotated sets)")
+    row = _row(4.0 * n, ms, workload=C2_WORKLOAD, cache=f"cold ({n_sets} rotated sets)")
+    row["roofline"] = beside_roofline("reference_copy", row)
+    out["reference_copy [8192, 4096]"] = row
     del sets, ws, wsnv
     torch.cuda.empty_cache()
 
@@ -506,9 +563,10 @@ def run_beside(args, dev, stream):
         for i in range(n_sets):
             q5(i)
         torch.cuda.synchronize()
-        out[f"{op} [16384, 8192]"] = _row(C5_BYTES_PER_ELEM[op] * n5, _timed_launches(q5, m, stream),
-                                          workload=C5_WORKLOAD,
-                                          cache=f"cold ({n_sets} rotated sets)")
+        row = _row(C5_BYTES_PER_ELEM[op] * n5, _timed_launches(q5, m, stream),
+                   workload=C5_WORKLOAD, cache=f"cold ({n_sets} rotated sets)")
+        row["roofline"] = beside_roofline(op, row)
+        out[f"{op} [16384, 8192]"] = row
     del sets
     torch.cuda.empty_cache()
     return out
@@ -589,7 +647,7 @@ def main():
             "value": round(step["bytes_step"] / (step["ms_per_step"] * 1e-3) / 1e9, 1),
             "ms_per_step": round(step["ms_per_step"], 5),
             "config": {"workload": WORKLOAD, "rows": n // STEP_K, "k": STEP_K, "elements": n,
-                       "step": OPS, "launches_per_step": len(OPS) + 1,
+                       "step": OPS, "launches_per_step": len(OPS) + step["sum_launches"],
                        "bytes_per_step": int(step["bytes_step"]),
                        "elements_per_s": round(n / (step["ms_per_step"] * 1e-3), 1),
                        "wall_s_timed": round(step["wall"], 4),

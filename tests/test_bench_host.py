@@ -152,3 +152,16 @@ def test_suite_attribution_by_elements(tmp_path):
                   "MoE w2 [128x4096, 1536] | `k_dequantize<true, 2>`"):
         assert label in text, label
     assert "| bf16 Laplace" not in text and "unattributed" not in text
+
+
+def test_every_op_beside_the_step_has_roofline_kernels():
+    # every op run_beside times maps to the kernels whose traffic it reads
+    for op in list(bench.EXTRA_BYTES_PER_ELEM) + ["reference_copy", "quantize_ocp",
+                                                 "quantize_oas"]:
+        fams = bench.BESIDE_KERNELS[op]
+        assert fams and all(bench.kernel_bytes_per_elem(f.replace(", U>", ", 4>")) is not None
+                            or f == "k_ceiling_copy" for f in fams), op
+        row = {"GB/s": 1.0, "frac_hbm": 0.5, "bytes": 10, "us": 1.0}
+        r = bench.beside_roofline(op, row)
+        assert r["bound"] == "hbm" and r["peak"] == bench.HBM_PEAK_GBS and r["frac"] == 0.5
+        assert r["traffic"] is None or r["traffic"] > 0
