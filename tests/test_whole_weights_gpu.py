@@ -8,8 +8,9 @@ MoE experts (vLLM MXFP8/MXFP4 page, "MXFP4: 4-bit MoE": packed w13
 per tensor. Codes, scales and dequantized values are compared with the oracle
 bit for bit over the whole tensors (2,818,572,288 + 2,415,919,104 elements),
 streamed through host memory in chunks; block MSE and tensor sums to a
-relative 1e-6; fake-quant against dequantize(quantize) on the device; and
-each matrix's or expert's own launch against its slice of the big launch.
+relative 1e-6; fake-quant against dequantize(quantize) on the device; each
+matrix's or expert's own launch, and the 196 matrices as separate tensors
+through the multi-tensor calls, against their slices of the big launch.
 """
 import os
 import sys
@@ -110,6 +111,25 @@ def test_llama32_3b_linears_whole():
         assert torch.equal(cm.view(-1), cf[off // 2:(off + out_f * in_f) // 2]), off
         assert torch.equal(sm.view(-1), sf[off // 32:(off + out_f * in_f) // 32]), off
     del cm, sm
+    # the 196 matrices as separate tensors through the multi-tensor calls
+    # (chunks of 48 matrices, ~7e8 elements each: the large-tensor tiling)
+    say("196 matrices through quantize_multi (OCP, OAS) and fakequant_multi (OCP)")
+    mats = [arena[off:off + out_f * in_f].view(out_f, in_f) for off, out_f, in_f in layout]
+    cf2, sf2 = c2.view(-1), s2.view(-1)
+    for mode, (cw, sw) in (("ocp", (cf, sf)), ("oas", (cf2, sf2))):
+        outs = mx.quantize_multi(mats, mode)
+        for (off, out_f, in_f), (cm, sm) in zip(layout, outs):
+            n = out_f * in_f
+            assert torch.equal(cm.view(-1), cw[off // 2:(off + n) // 2]), (mode, off)
+            assert torch.equal(sm.view(-1), sw[off // 32:(off + n) // 32]), (mode, off)
+        del outs
+    yf = y.view(-1)
+    fqs = mx.fakequant_multi(mats)
+    for (off, out_f, in_f), fm in zip(layout, fqs):
+        assert torch.equal(fm.view(-1).view(torch.int16),
+                           yf[off:off + out_f * in_f].view(torch.int16)), ("fakequant_multi", off)
+    del fqs, mats
+    torch.cuda.empty_cache()
     check_whole(x, "llama", {"ocp": {"codes": c, "scales": s, "y": y, "bm": bm, "sums": sums},
                              "oas": {"codes": c2, "scales": s2}})
 
