@@ -675,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restr
 // fixed order), block_mse = (float)(SSE / 32). The tensor sums (SSE and
 // sum x^2) are taken in two stages with fixed order and no atomics: each
 // workgroup writes its two sums to partial[2 * blockIdx.x + {0, 1}] (lane
-// sums, then a butterfly over the wave, then the waves in order), and
+// sums, then DPP sums within each 16-lane row, then the rows in order), and
 // k_sum_partials adds the partials.
 // Block error of one item against (c, s): the fp64 SSE of the quad's block,
 // summed in a fixed order (per lane, then quad_sum_f64); returns the block's
