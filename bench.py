@@ -108,7 +108,8 @@ KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0, U>", "quantize_oas": "k_quanti
              "fakequant_ocp": "k_fakequant<true, 0, U>", "block_mse": "k_block_mse<true, true, U>"}
 # kernels with items-per-thread as their last template argument, and one
 # tile (256 threads x U items x 8 elements) per workgroup at these sizes
-U_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize", "k_block_mse")
+U_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize", "k_block_mse", "k_quantize_pair")
+ITEM_ELEMS = {"k_quantize_pair": 16}  # elements per item where not 8 (two lanes per block)
 FUSED_ITEMS = 2  # items per thread of k_quantize_fused
 PROFILE_STEM = {"step": "mx_llama32_3b_linears",
                 "beside": "mx_student_t_8192x4096_laplace_16384x8192"}
@@ -189,12 +190,14 @@ def measured_traffic(op, path=None, family=None):
 
 
 # Kernel families of the ops timed beside the step (one instantiation each
-# there), for their measured traffic; NVFP4 quantize is two kernels.
+# there), for their measured traffic; NVFP4 quantize is two kernels, and a
+# tuple lists the kernels the library chooses between by tensor size.
 BESIDE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", PROFILE_STEM["beside"] + "_hbm_traffic.md")
 BESIDE_KERNELS = {
     "fakequant_ocp": ["k_fakequant<true, 0, U>"], "fakequant_oas": ["k_fakequant<true, 1, U>"],
     "fakequant_oas_nf": ["k_fakequant<true, 3, U>"],
-    "quantize_oas_bits": ["k_quantize<true, 2, U>"], "quantize_oas_nf": ["k_quantize<true, 3, U>"],
+    "quantize_oas_bits": ["k_quantize<true, 2, U>"],
+    "quantize_oas_nf": [("k_quantize_pair<3, U>", "k_quantize<true, 3, U>")],
     "quantize_mxfp8": ["k_quantize8<true>"], "dequantize_mxfp8_bf16": ["k_dequantize8<true>"],
     "fakequant_mxfp8": ["k_fakequant8<true>"],
     "quantize_nvfp4": ["k_absmax_partials<true>", "k_quantize_nv<true, false>"],
@@ -213,8 +216,10 @@ def beside_roofline(op, row):
     against the 8 TB/s peak, and the HBM bytes its kernels moved per call
     in the committed profile of this part (None while stale)."""
     traffic = 0
-    for fam in BESIDE_KERNELS[op]:
-        mt = measured_traffic(op, BESIDE_TRAFFIC_FILE, fam)
+    for fams in BESIDE_KERNELS[op]:  # a tuple: the kernels the library may pick by size
+        mt = None
+        for fam in (fams if isinstance(fams, tuple) else (fams,)):
+            mt = mt or measured_traffic(op, BESIDE_TRAFFIC_FILE, fam)
         if mt is None:
             traffic = None
             break
@@ -1090,6 +1095,7 @@ KERNEL_BYTES_PER_ELEM = {
     "k_quantize<true, 1, U>": BYTES_PER_ELEM["quantize_oas"],
     "k_quantize<true, 2, U>": EXTRA_BYTES_PER_ELEM["quantize_oas_bits"],
     "k_quantize<true, 3, U>": EXTRA_BYTES_PER_ELEM["quantize_oas_nf"],
+    "k_quantize_pair<3, U>": EXTRA_BYTES_PER_ELEM["quantize_oas_nf"],
     "k_dequantize<true, U>": BYTES_PER_ELEM["dequantize_bf16"],
     "k_fakequant<true, 0, U>": BYTES_PER_ELEM["fakequant_ocp"],
     "k_fakequant<true, 1, U>": EXTRA_BYTES_PER_ELEM["fakequant_oas"],
@@ -1121,9 +1127,10 @@ def kernel_bytes_per_elem(k: str):
 
 def tile_elems(k: str, grid: int):
     """Elements a dispatch of k covers when it runs one tile per workgroup
-    (256 threads x U items x 8 elements), else None."""
+    (256 threads x U items x 8 elements, 16 for the two-lanes-per-block
+    kernel), else None."""
     u = items_per_thread(k)
-    return grid * 256 * u * 8 if u else None
+    return grid * 256 * u * ITEM_ELEMS.get(k.split("<")[0], 8) if u else None
 
 
 # The two parts of bench.py that are profiled, each on its own (--only):

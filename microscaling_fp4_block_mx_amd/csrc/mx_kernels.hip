@@ -384,7 +384,14 @@ __device__ __forceinline__ float lane_sse(const Item<BF16> &x, uint32_t c, uint3
   return acc_e + acc_o;
 }
 
-// Block scale byte and this lane's 8 codes (all quad lanes agree on s).
+// Block scale byte and this lane's codes, for either lane layout of a block
+// (four lanes of 8 elements, or two lanes of 16). amax is the block's largest
+// |x| bit pattern, held by every lane of the block; encode(s) returns this
+// lane's codes at byte s, sign() its codes for a NaN/Inf block, and
+// block_sse(c, h, codes) stores its codes at candidate byte c and returns the
+// block's pinned fp32 error at c in units of 2^(h-127), summed over the
+// block's lanes in the fixed order (every lane of the block gets the same
+// bits, so the branches below are uniform over the block).
 //
 // Modes (bytes as in include/mx.h): with s0 the OCP byte and v0 the block
 // maximum over 2^(s0-127) (in [4, 8) whenever the exponent field e of amax is
@@ -402,12 +409,12 @@ __device__ __forceinline__ float lane_sse(const Item<BF16> &x, uint32_t c, uint3
 // monotone). Hence SSE32(h - 1) >= fl(d * d); when SSE32(h) <= fl(d * d) the
 // strict test SSE32(h - 1) < SSE32(h) must fail and h is kept without
 // computing it. The decision is identical to evaluating both candidates.
-template <bool BF16, int MODE>
-__device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t &codes) {
-  const uint32_t amax = quad_max_u32(item_amax_bits<BF16>(x));
+template <int MODE, typename Codes, typename Encode, typename Sign, typename BlockSse>
+__device__ __forceinline__ uint32_t choose_scale(uint32_t amax, Codes &codes, Encode encode,
+                                                 Sign sign, BlockSse block_sse) {
   const uint32_t s0 = ocp_scale_byte(amax);
   if (__builtin_expect(s0 == 255u, 0)) {
-    codes = sign_codes<BF16>(x);
+    codes = sign();
     return s0;
   }
   const uint32_t mant = amax & 0x7FFFFFu;
@@ -415,24 +422,24 @@ __device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t 
   if constexpr (MODE == MX_SCALE_OCP || MODE == MX_SCALE_OAS_BITS) {
     uint32_t s = s0;
     if (MODE == MX_SCALE_OAS_BITS && normalized && mant > 0x600000u) s = min(s0 + 1u, 252u);
-    codes = encode_item<BF16>(x, s);
+    codes = encode(s);
     return s;
   } else {
     uint32_t h = s0;
     if (MODE == MX_SCALE_OAS_NF && normalized && mant > 0x400000u) h = min(s0 + 1u, 252u);
     if (h == 0u) {
-      codes = encode_item<BF16>(x, h);
+      codes = encode(h);
       return h;
     }
-    uint32_t c_hi;
-    const float sse_hi = quad_sum_f32(lane_sse<BF16>(x, h, h, c_hi));
+    Codes c_hi;
+    const float sse_hi = block_sse(h, h, c_hi);
     const float d_top =
         __builtin_fmaf(__uint_as_float(amax), __uint_as_float((254u - h) << 23), -3.0f);
     const float bound = d_top * d_top;
     codes = c_hi;
-    if (sse_hi > bound) {  // uniform over the quad: same sums, same amax
-      uint32_t c_low;
-      const float sse_low = quad_sum_f32(lane_sse<BF16>(x, h - 1u, h, c_low));
+    if (sse_hi > bound) {  // uniform over the block: same sums, same amax
+      Codes c_low;
+      const float sse_low = block_sse(h - 1u, h, c_low);
       if (sse_low < sse_hi) {  // strict: a tie keeps h
         codes = c_low;
         return h - 1u;
@@ -440,6 +447,81 @@ __device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t 
     }
     return h;
   }
+}
+
+// Block scale byte and this lane's 8 codes, four lanes per block (all quad
+// lanes agree on the byte).
+template <bool BF16, int MODE>
+__device__ __forceinline__ uint32_t quantize_item(const Item<BF16> &x, uint32_t &codes) {
+  return choose_scale<MODE>(
+      quad_max_u32(item_amax_bits<BF16>(x)), codes,
+      [&](uint32_t s) { return encode_item<BF16>(x, s); },
+      [&]() { return sign_codes<BF16>(x); },
+      [&](uint32_t c, uint32_t h, uint32_t &out) {
+        return quad_sum_f32(lane_sse<BF16>(x, c, h, out));
+      });
+}
+
+// ---- two lanes per block (bf16) ----------------------------------------------
+//
+// A lane pair owns a block: 16 bf16 elements (32 bytes, two 16-byte loads)
+// per lane, 8 code bytes out. The per-block work (maximum, byte, bound,
+// decision) then runs on two lanes instead of four, which pays where the two
+// error evaluations of OAS_NF make quantize arithmetic-bound; its loads are
+// 16 bytes at a 32-byte lane pitch per instruction, which costs more than the
+// quad layout's contiguous ones on larger tensors (see launch_quantize_t).
+// The pinned error keeps its order: the even lane of the pair holds groups 0
+// and 1, the odd lane groups 2 and 3, each lane forms (g0 + g1) or (g2 + g3)
+// from its two groups (each even + odd accumulator as in lane_sse), and one
+// pair exchange adds the two (fp32 addition commutes, so both lanes hold the
+// same bits).
+struct PairItem {
+  uint32_t w[8];  // element 2j in the low half of w[j]
+};
+__device__ __forceinline__ void load_pair_item(const void *base, int64_t pit, PairItem &x) {
+  const u32x4 *q = reinterpret_cast<const u32x4 *>(base) + 2 * pit;
+  const u32x4 a = ld<true>(q), b = ld<true>(q + 1);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    x.w[j] = a[j];
+    x.w[4 + j] = b[j];
+  }
+}
+__device__ __forceinline__ uint32_t pair_amax_bits(const PairItem &x) {
+  u16x2 m = __builtin_bit_cast(u16x2, x.w[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int j = 1; j < 8; j++)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, x.w[j] & 0x7FFF7FFFu));
+  return (uint32_t)max(m.x, m.y) << 16;
+}
+// the lane's two 8-element halves as quad-layout items
+__device__ __forceinline__ Item<true> pair_half(const PairItem &x, int half) {
+  Item<true> r;
+#pragma unroll
+  for (int j = 0; j < 4; j++) r.w[j] = x.w[4 * half + j];
+  return r;
+}
+__device__ __forceinline__ float pair_lane_sse(const PairItem &x, uint32_t c, uint32_t h,
+                                               u32x2 &codes) {
+  uint32_t c0, c1;
+  const float ga = lane_sse<true>(pair_half(x, 0), c, h, c0);  // group 2 (lane & 1)
+  const float gb = lane_sse<true>(pair_half(x, 1), c, h, c1);  // group 2 (lane & 1) + 1
+  codes = u32x2{c0, c1};
+  return ga + gb;
+}
+template <int MODE>
+__device__ __forceinline__ uint32_t quantize_pair(const PairItem &x, u32x2 &codes) {
+  const uint32_t a = pair_amax_bits(x);
+  return choose_scale<MODE>(
+      max(a, dpp_x1(a)), codes,
+      [&](uint32_t s) {
+        return u32x2{encode_item<true>(pair_half(x, 0), s), encode_item<true>(pair_half(x, 1), s)};
+      },
+      [&]() { return u32x2{sign_codes<true>(pair_half(x, 0)), sign_codes<true>(pair_half(x, 1))}; },
+      [&](uint32_t c, uint32_t h, u32x2 &out) {
+        const float p = pair_lane_sse(x, c, h, out);
+        return p + __uint_as_float(dpp_x1(__float_as_uint(p)));
+      });
 }
 
 // ---- kernels -----------------------------------------------------------------
@@ -554,6 +636,23 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ 
       });
 }
 
+// bf16 quantize with two lanes per block (npitems = elements / 16).
+template <int MODE, int U>
+__global__ __launch_bounds__(kThreads) void k_quantize_pair(const void *__restrict__ x,
+                                                            uint32_t *__restrict__ codes,
+                                                            uint8_t *__restrict__ scales,
+                                                            int64_t npitems) {
+  PairItem xv[U];
+  u32x2 cw[U];
+  uint32_t sv[U];
+  tile_loop<U>(
+      npitems, [&](int u, int64_t pit) { load_pair_item(x, pit, xv[u]); },
+      [&](int u, int64_t) { sv[u] = quantize_pair<MODE>(xv[u], cw[u]); },
+      [&](int u, int64_t pit) {
+        st<false>(reinterpret_cast<u32x2 *>(codes) + pit, cw[u]);
+        if ((threadIdx.x & 1) == 0) st<false>(scales + (pit >> 1), (uint8_t)sv[u]);
+      });
+}
 template <bool BF16, int MODE, int U>
 __global__ __launch_bounds__(kThreads) void k_fakequant(const void *x, void *y, int64_t nitems) {
   Item<BF16> xv[U];
@@ -1448,10 +1547,24 @@ using namespace mxk;
 // 196,608 workgroups, whose second round of tiles streams a second region of
 // memory at the same time, was 1-5 % slower than no cap.
 constexpr int64_t kGridLimit = 0x7FFFFFFF;
+// bf16 OAS_NF quantize takes the two-lanes-per-block layout up to this many
+// items (67,108,864 elements). On Student-t activations (8.4e6 to 2.0e8
+// elements, rotated buffers) it was 6-9 % faster up to 3.4e7 elements, 2 %
+// at 6.7e7, and 1-5 % slower from 1.0e8 up; for OAS quantize it was slower at
+// every size measured.
+constexpr int64_t kPairItems = int64_t(1) << 23;
 
 template <bool BF16, int MODE>
 static void launch_quantize_t(const void *x, uint32_t *c, uint8_t *s, int64_t nitems,
                               hipStream_t st) {
+  if constexpr (BF16 && MODE == MX_SCALE_OAS_NF) {
+    if (nitems <= kPairItems) {  // nitems is a multiple of 4 (k % 32 == 0)
+      const int64_t np = nitems / 2;
+      hipLaunchKernelGGL((k_quantize_pair<MODE, 1>), dim3(grid_for(np, kGridLimit, 1)),
+                         dim3(kThreads), 0, st, x, c, s, np);
+      return;
+    }
+  }
   if (nitems >= kLargeItems) {
     constexpr int U = unroll_of(BF16, MODE, kKindQuantize, true);
     hipLaunchKernelGGL((k_quantize<BF16, MODE, U>), dim3(grid_for(nitems, kGridLimit, U)),

@@ -78,6 +78,10 @@ def test_kernel_names_and_families():
     assert bench.items_per_thread("k_fakequant<true, 1, 2>") == 2
     assert bench.items_per_thread("k_quantize_fused<true, 0, true>") == bench.FUSED_ITEMS
     assert bench.items_per_thread("k_quantize8<true>") is None
+    # the two-lanes-per-block kernel: 16 elements per item
+    assert bench.kernel_family("k_quantize_pair<3, 1>") == "k_quantize_pair<3, U>"
+    assert bench.tile_elems("k_quantize_pair<3, 1>", 8192) == 8192 * 4096
+    assert bench.tile_elems("k_quantize<true, 3, 2>", 8192) == 8192 * 4096
     assert bench.kernel_bytes_per_elem("k_quantize<true, 0, 1>") == 2 + 0.5 + 1 / 32
     assert bench.kernel_bytes_per_elem("k_ceiling_read") == 2.0
 
@@ -158,7 +162,7 @@ def test_every_op_beside_the_step_has_roofline_kernels():
     # every op run_beside times maps to the kernels whose traffic it reads
     for op in list(bench.EXTRA_BYTES_PER_ELEM) + ["reference_copy", "quantize_ocp",
                                                  "quantize_oas"]:
-        fams = bench.BESIDE_KERNELS[op]
+        fams = [f for g in bench.BESIDE_KERNELS[op] for f in (g if isinstance(g, tuple) else (g,))]
         assert fams and all(bench.kernel_bytes_per_elem(f.replace(", U>", ", 4>")) is not None
                             or f == "k_ceiling_copy" for f in fams), op
         row = {"GB/s": 1.0, "frac_hbm": 0.5, "bytes": 10, "us": 1.0}

@@ -278,6 +278,31 @@ def test_bf16_8192x4096_student_t_fakequant_full():
                          f"student-t fakequant {mode}")
     say("student-t quantize/dequant/mse")
     check_all_ops(x, "student-t", modes=("ocp",))
+    # the error-driven modes' codes and scales over the whole tensor (OAS_NF
+    # runs the two-lanes-per-block layout at this size)
+    for mode in ("oas", "oas_nf"):
+        say(f"student-t quantize {mode}")
+        c, s = mx.quantize(xd, mode)
+        wc, ws = oracle.quantize(xh, mode, threads=THREADS)
+        assert_same_bits(s, ws, f"student-t scales {mode}")
+        assert_same_bits(c, wc, f"student-t codes {mode}")
+
+
+@pytest.mark.parametrize("rows", [16384, 16385])
+def test_oas_nf_layout_threshold(rows):
+    # bf16 OAS_NF quantize changes lane layout above 2^23 items (2^26
+    # elements): 16384 x 4096 is the largest tensor of the two-lanes-per-block
+    # layout, 16385 x 4096 the smallest of the four-lanes one
+    rng = np.random.default_rng(31 + rows)
+    body = rng.standard_t(3.0, size=(rows, 4096)).astype(np.float32)
+    body[:, rng.choice(4096, 20, replace=False)] *= np.float32(50.0)
+    x = torch.from_numpy(body).to(torch.bfloat16)
+    xh = host_view(x)
+    say(f"oas_nf layout threshold {rows}x4096")
+    c, s = mx.quantize(x.cuda(), "oas_nf")
+    wc, ws = oracle.quantize(xh, "oas_nf", threads=THREADS)
+    assert_same_bits(s, ws, f"threshold scales {rows}")
+    assert_same_bits(c, wc, f"threshold codes {rows}")
 
 
 def test_bf16_16384x8192_laplace_all_modes_full():
