@@ -320,12 +320,18 @@ mx_status_t mx_fakequant_multi(const mx_tensor_t *tensors, int count,
                                mx_dtype_t dtype, mx_scale_mode_t mode,
                                void *stream);
 
-/* Static, human-readable name of a status code. */
+/* Error reporting of this interface (no operation of the method, so no
+ * passage defines it): the pages describe no error conventions; these two
+ * calls only report the mx_status_t values above. */
+
+/* Static, human-readable name of a status code (never NULL; unknown values
+ * give "unknown mx_status_t"). The string is owned by the library. */
 const char *mx_status_string(mx_status_t s);
 
 /* Detail of the calling thread's most recent failure that recorded one
  * ("" if none): the HIP error text of an MX_ERR_HIP, or which tensor of a
- * multi-tensor call failed validation. */
+ * multi-tensor call failed validation. The string is owned by the library
+ * and valid until that thread's next call. */
 const char *mx_last_error_detail(void);
 
 #ifdef __cplusplus
