@@ -1094,15 +1094,21 @@ __device__ __forceinline__ void decode8_item(u32x2 c, uint32_t s, uint32_t (&y)[
   }
 }
 
+// Items per thread of MXFP8 quantize: two for bf16 (with the three-phase
+// tile loop, 2.8 % faster than four on 8192x4096 activations; one was 6 %
+// slower), kU for fp32.
+template <bool BF16>
+constexpr int kU8 = BF16 ? 2 : kU<false>;
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_quantize8(const void *__restrict__ x,
                                                         u32x2 *__restrict__ codes,
                                                         uint8_t *__restrict__ scales,
                                                         int64_t nitems) {
-  Item<BF16> xv[kU<BF16>];
-  u32x2 cw[kU<BF16>];
-  uint32_t sv[kU<BF16>];
-  tile_loop<kU<BF16>>(
+  Item<BF16> xv[kU8<BF16>];
+  u32x2 cw[kU8<BF16>];
+  uint32_t sv[kU8<BF16>];
+  tile_loop<kU8<BF16>>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) { sv[u] = quantize8_item<BF16>(xv[u], cw[u]); },
       [&](int u, int64_t it) {
@@ -1772,7 +1778,7 @@ hipError_t mxi_scratch_address(int dev, double **out) {
 
 hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                 uint8_t *scales, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
+  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU8<true> : kU8<false>)), b(kThreads);
   u32x2 *c = reinterpret_cast<u32x2 *>(codes);
   if (bf16)
     hipLaunchKernelGGL((k_quantize8<true>), g, b, 0, st, x, c, scales, nitems);
