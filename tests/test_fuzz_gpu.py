@@ -38,7 +38,7 @@ def random_tensor(rng: np.random.Generator) -> torch.Tensor:
     return torch.from_numpy(x.reshape(rows, k))
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(24))
 def test_fuzz_every_entry_point(seed):
     rng = np.random.default_rng(7000 + seed)
     for case in range(10):
