@@ -6,7 +6,9 @@
 // handled by a quad of 4 adjacent lanes; lane q of the quad owns elements
 // 8q..8q+7 ("item" = 8 elements = one 16-byte bf16 load, one 32-bit code
 // word). A wave64 covers 16 blocks per item step: 1 KiB of bf16 in, 256 B of
-// codes and 16 B of scales out, all contiguous.
+// codes and 16 B of scales out, all contiguous. (OAS_NF quantize of smaller
+// bf16 tensors gives each block to a lane pair instead; see "two lanes per
+// block".)
 //
 // Cross-lane work inside a quad (block amax, block squared error) uses DPP
 // quad permutations, so quads must always be whole: every launch covers a
@@ -55,8 +57,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // on a 2.1e9-element bf16 tensor with four items per thread: 196,608 (768
 // per CU) beat 65,536 by 5 % (quantize) and 3 % (dequantize), while
 // 8,192-32,768 were slower. The MXFP4 single-tensor kernels are not capped
-// (see kGridLimit). Tensors below ~200 M elements get one tile per workgroup
-// either way.
+// (see kGridLimit). Below the cap every workgroup takes one tile: tensors up
+// to ~1.6e9 elements with four items per thread, ~4e8 with one.
 #ifndef MX_GRID_CAP
 #define MX_GRID_CAP 196608
 #endif
@@ -593,7 +595,8 @@ constexpr int kU = BF16 ? kUnroll : (kUnroll >= 4 ? kUnroll / 4 : 1);
 // OAS and OAS_BITS (OAS with two items per thread was 2 % slower on
 // 8192x4096, equal on 16384x8192), while OAS_NF quantize takes two (4 % faster on
 // 8192x4096, where its two error evaluations per block make it
-// arithmetic-bound; equal on 16384x8192); bf16 dequantize and fake-quant take
+// arithmetic-bound; equal on 16384x8192; up to kPairItems items it runs the
+// two-lanes-per-block kernel instead); bf16 dequantize and fake-quant take
 // two (fewer registers and more workgroups in flight for the write-heavy
 // stream; one fp32 fake-quant item was 5 % slower on fp32 1024x4096). Beyond
 // it (multi-GB weight sets streamed once from HBM) fewer items per thread keep
