@@ -12,6 +12,9 @@
 //   mxc_quantize_shape: per 16-byte item read, one 4-byte word written (the
 //     code word) and, for every 4th item, one byte (the scale byte): the
 //     traffic of bf16 quantize, 2 + 1/2 + 1/32 bytes per element.
+//   mxc_dequantize_shape: the reverse, per item one 4-byte word and the
+//     byte of its group of 4 items read (every lane loads it, as dequantize
+//     does), 16 bytes written: the traffic of bf16 dequantize.
 //   mxc_copy: 16 bytes read and 16 bytes written per item.
 //   mxc_read / mxc_write: only the loads / only the stores of a copy.
 //   mxc_empty: one workgroup that does nothing (the launch floor).
@@ -71,6 +74,22 @@ __global__ __launch_bounds__(kThreads) void k_ceiling_quantize_shape(
       });
 }
 
+__global__ __launch_bounds__(kThreads) void k_ceiling_dequantize_shape(
+    const uint32_t *__restrict__ words, const uint8_t *__restrict__ bytes,
+    u32x4 *__restrict__ y, int64_t nitems) {
+  uint32_t w[kItems], b[kItems];
+  tiles(
+      nitems,
+      [&](int u, int64_t it) {
+        w[u] = words[it];
+        b[u] = bytes[it >> 2];
+      },
+      [&](int u, int64_t it) {
+        const uint32_t v = w[u] ^ b[u];
+        __builtin_nontemporal_store(u32x4{v, v, v, v}, y + it);
+      });
+}
+
 __global__ __launch_bounds__(kThreads) void k_ceiling_copy(const u32x4 *__restrict__ x,
                                                            u32x4 *__restrict__ y,
                                                            int64_t nitems) {
@@ -114,6 +133,15 @@ int mxc_quantize_shape(const void *x, int64_t nitems, void *words, void *bytes, 
   hipLaunchKernelGGL(k_ceiling_quantize_shape, dim3(grid_for(nitems)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(x),
                      static_cast<uint32_t *>(words), static_cast<uint8_t *>(bytes), nitems);
+  return (int)hipGetLastError();
+}
+
+// words: nitems 4-byte words; bytes: nitems / 4 bytes; y: nitems 16-byte items.
+int mxc_dequantize_shape(const void *words, const void *bytes, int64_t nitems, void *y,
+                         void *stream) {
+  hipLaunchKernelGGL(k_ceiling_dequantize_shape, dim3(grid_for(nitems)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint32_t *>(words),
+                     static_cast<const uint8_t *>(bytes), static_cast<u32x4 *>(y), nitems);
   return (int)hipGetLastError();
 }
 
