@@ -100,6 +100,7 @@ EXTRA_BYTES_PER_ELEM = {
 C5_BYTES_PER_ELEM = {"quantize_ocp": 2 + 0.5 + 1 / 32, "quantize_oas": 2 + 0.5 + 1 / 32}
 # reference kernels (bench_ceiling.hip) on the step's buffer
 CEILING_BYTES_PER_ELEM = {"quantize_shape": 2 + 0.5 + 1 / 32, "dequantize_shape": 0.5 + 1 / 32 + 2,
+                          "block_mse_shape": 2 + 0.5 + 1 / 32 + 1 / 8,
                           "copy": 4.0, "read": 2.0,
                           "write": 2.0}
 # Kernel family of each op (the kernels' last template argument, U, is the
@@ -255,12 +256,13 @@ def ceiling_lib() -> ctypes.CDLL:
     p, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.mxc_quantize_shape.argtypes = [p, i64, p, p, p]
     lib.mxc_dequantize_shape.argtypes = [p, p, i64, p, p]
+    lib.mxc_block_mse_shape.argtypes = [p, p, p, i64, p, p]
     lib.mxc_copy.argtypes = [p, p, i64, p]
     lib.mxc_read.argtypes = [p, i64, p, p]
     lib.mxc_write.argtypes = [p, i64, p]
     lib.mxc_empty.argtypes = [p]
-    for f in ("mxc_quantize_shape", "mxc_dequantize_shape", "mxc_copy", "mxc_read", "mxc_write",
-              "mxc_empty"):
+    for f in ("mxc_quantize_shape", "mxc_dequantize_shape", "mxc_block_mse_shape", "mxc_copy",
+              "mxc_read", "mxc_write", "mxc_empty"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -392,6 +394,9 @@ def run_step(args, dev, stream):
         "dequantize_shape": lambda i: cl.mxc_dequantize_shape(b["c_ocp"].data_ptr(),
                                                               b["s_ocp"].data_ptr(), nit,
                                                               b["y_dq"].data_ptr(), sh),
+        "block_mse_shape": lambda i: cl.mxc_block_mse_shape(xp, b["c_ocp"].data_ptr(),
+                                                            b["s_ocp"].data_ptr(), nit,
+                                                            b["bm"].data_ptr(), sh),
         "copy": lambda i: cl.mxc_copy(xp, b["y_fq"].data_ptr(), nit, sh),
         "read": lambda i: cl.mxc_read(xp, nit, sink.data_ptr(), sh),
         "write": lambda i: cl.mxc_write(b["y_fq"].data_ptr(), nit, sh),
@@ -406,6 +411,8 @@ def run_step(args, dev, stream):
                                                        / op_ms["quantize_ocp"], 4)
     ceilings["dequantize_bf16_vs_dequantize_shape"] = round(ceil_ms["dequantize_shape"]
                                                             / op_ms["dequantize_bf16"], 4)
+    ceilings["block_mse_vs_block_mse_shape"] = round(ceil_ms["block_mse_shape"]
+                                                     / op_ms["block_mse"], 4)
     ceilings["fakequant_ocp_vs_copy"] = round(ceil_ms["copy"] / op_ms["fakequant_ocp"], 4)
     ceilings["kernels"] = ("bench_ceiling.hip (k_ceiling_*): one 16-byte item per thread, one tile "
                            "per workgroup, no format arithmetic")
@@ -1122,6 +1129,7 @@ KERNEL_BYTES_PER_ELEM = {
     "k_quantize_fused<true, 0, true>": EXTRA_BYTES_PER_ELEM["quantize_fused"],
     "k_ceiling_quantize_shape": CEILING_BYTES_PER_ELEM["quantize_shape"],
     "k_ceiling_dequantize_shape": CEILING_BYTES_PER_ELEM["dequantize_shape"],
+    "k_ceiling_block_mse_shape": CEILING_BYTES_PER_ELEM["block_mse_shape"],
     "k_ceiling_copy": CEILING_BYTES_PER_ELEM["copy"],
     "k_ceiling_read": CEILING_BYTES_PER_ELEM["read"],
     "k_ceiling_write": CEILING_BYTES_PER_ELEM["write"],

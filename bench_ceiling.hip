@@ -15,6 +15,10 @@
 //   mxc_dequantize_shape: the reverse, per item one 4-byte word and the
 //     byte of its group of 4 items read (every lane loads it, as dequantize
 //     does), 16 bytes written: the traffic of bf16 dequantize.
+//   mxc_block_mse_shape: per item 16 bytes, one 4-byte word and the byte of
+//     its group read, and for every 4th item one 4-byte word written: the
+//     traffic of bf16 block MSE with its per-block output, 2 + 1/2 + 1/32 +
+//     1/8 bytes per element.
 //   mxc_copy: 16 bytes read and 16 bytes written per item.
 //   mxc_read / mxc_write: only the loads / only the stores of a copy.
 //   mxc_empty: one workgroup that does nothing (the launch floor).
@@ -90,6 +94,23 @@ __global__ __launch_bounds__(kThreads) void k_ceiling_dequantize_shape(
       });
 }
 
+__global__ __launch_bounds__(kThreads) void k_ceiling_block_mse_shape(
+    const u32x4 *__restrict__ x, const uint32_t *__restrict__ words,
+    const uint8_t *__restrict__ bytes, uint32_t *__restrict__ out, int64_t nitems) {
+  u32x4 v[kItems];
+  uint32_t w[kItems], b[kItems];
+  tiles(
+      nitems,
+      [&](int u, int64_t it) {
+        v[u] = __builtin_nontemporal_load(x + it);
+        w[u] = words[it];
+        b[u] = bytes[it >> 2];
+      },
+      [&](int u, int64_t it) {
+        if ((threadIdx.x & 3) == 0) out[it >> 2] = v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3] ^ w[u] ^ b[u];
+      });
+}
+
 __global__ __launch_bounds__(kThreads) void k_ceiling_copy(const u32x4 *__restrict__ x,
                                                            u32x4 *__restrict__ y,
                                                            int64_t nitems) {
@@ -142,6 +163,17 @@ int mxc_dequantize_shape(const void *words, const void *bytes, int64_t nitems, v
   hipLaunchKernelGGL(k_ceiling_dequantize_shape, dim3(grid_for(nitems)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint32_t *>(words),
                      static_cast<const uint8_t *>(bytes), static_cast<u32x4 *>(y), nitems);
+  return (int)hipGetLastError();
+}
+
+// x: nitems 16-byte items; words: nitems 4-byte words; bytes: nitems / 4
+// bytes; out: nitems / 4 4-byte words.
+int mxc_block_mse_shape(const void *x, const void *words, const void *bytes, int64_t nitems,
+                        void *out, void *stream) {
+  hipLaunchKernelGGL(k_ceiling_block_mse_shape, dim3(grid_for(nitems)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(x),
+                     static_cast<const uint32_t *>(words), static_cast<const uint8_t *>(bytes),
+                     static_cast<uint32_t *>(out), nitems);
   return (int)hipGetLastError();
 }
 
