@@ -1,8 +1,9 @@
-"""The entry points under HIP graph capture: one graph holds quantize (OAS),
-dequantize, block MSE with tensor sums, fake-quant, MXFP8 fake-quant, NVFP4
-quantize / dequantize / fake-quant, MBS-Static quantize / dequantize /
-fake-quant, the one-pass call with every output, and a multi-tensor
-quantize, on static buffers. Every replay, with new
+"""The entry points under HIP graph capture: one graph holds quantize (OAS;
+and bf16 OAS_NF, the two-lanes-per-block kernel), dequantize, block MSE with
+tensor sums (with a workspace, and the no-alloc entry point on the bf16
+codes), fake-quant, MXFP8 fake-quant, NVFP4 quantize / dequantize /
+fake-quant, MBS-Static quantize / dequantize / fake-quant, the one-pass call
+with every output, and a multi-tensor quantize, on static buffers. Every replay, with new
 inputs copied in and the outputs overwritten by eager work in between, must
 reproduce the eager results bit for bit (the path records no memset and
 allocates nothing, so it is capturable as is)."""
@@ -43,13 +44,15 @@ def test_graph_replays_match_eager():
     c1, s1, y1 = torch.empty((R, K // 2), **u8), torch.empty((R, K // 32), **u8), torch.empty_like(xb)
     bm1, sums1, ws1 = torch.empty_like(bm), torch.empty_like(sums), torch.empty(wsb, **u8)
     cq, sq = torch.empty((R, K // 2), **u8), torch.empty((R, K // 32), **u8)
+    cnf, snf = torch.empty((R, K // 2), **u8), torch.empty((R, K // 32), **u8)
+    bmna, sumsna = torch.empty_like(bm), torch.empty_like(sums)
     half = R // 2
     descs = (mx.MxTensor * 2)()
     descs[0] = mx.MxTensor(xb.data_ptr(), None, cq.data_ptr(), sq.data_ptr(), half, K)
     descs[1] = mx.MxTensor(xb[half].data_ptr(), None, cq[half].data_ptr(), sq[half].data_ptr(),
                            R - half, K)
     outs = (c, s, y, bm, sums, fq, fq8, cn, bn, tn, cm, sm, mm, ynv, ymb, fqnv, fqmb,
-            c1, s1, y1, bm1, sums1, cq, sq)
+            c1, s1, y1, bm1, sums1, cq, sq, cnf, snf, bmna, sumsna)
 
     def seq(h):
         _ok(mx.mx_quantize(xf.data_ptr(), mx.MX_F32, R, K, mx.MX_SCALE_OAS, c.data_ptr(),
@@ -74,6 +77,10 @@ def test_graph_replays_match_eager():
                                  c1.data_ptr(), s1.data_ptr(), y1.data_ptr(), bm1.data_ptr(),
                                  sums1.data_ptr(), ws1.data_ptr(), wsb, h))
         _ok(mx.mx_quantize_multi(descs, 2, mx.MX_BF16, mx.MX_SCALE_OAS_BITS, h))
+        _ok(mx.mx_quantize(xb.data_ptr(), mx.MX_BF16, R, K, mx.MX_SCALE_OAS_NF, cnf.data_ptr(),
+                           snf.data_ptr(), h))
+        _ok(mx.mx_block_mse_noalloc(xb.data_ptr(), mx.MX_BF16, cnf.data_ptr(), snf.data_ptr(), R,
+                                    K, bmna.data_ptr(), sumsna.data_ptr(), h))
 
     def load(seed):
         xf.copy_(workloads.fp32_normal(seed, (R, K)).to(dev) * (seed % 5 + 1))
