@@ -423,6 +423,10 @@ def run_step(args, dev, stream):
     dom = max(OPS, key=lambda o: op_ms[o])
     dom_gbs = bytes_op[dom] / (op_ms[dom] * 1e-3) / 1e9
     mt = measured_traffic(dom)
+    if mt is None:
+        print(f"bench.py: roofline.traffic is null: {os.path.relpath(TRAFFIC_FILE, ROOT)} was "
+              "taken on other kernel code (python bench.py --summarize-profiles DIR rewrites it)",
+              file=sys.stderr)
     roofline = {"bound": "hbm", "kernel": mt[0] if mt else KERNEL_OF[dom], "op": dom,
                 "achieved": round(dom_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
