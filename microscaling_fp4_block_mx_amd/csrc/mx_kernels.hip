@@ -542,12 +542,24 @@ __device__ __forceinline__ uint32_t quantize_pair(const PairItem &x, u32x2 &code
 // load, then three, which measured faster than forcing all four ahead). Full
 // tiles run without bounds checks; the one partial tile (if any) is handled
 // by the workgroup whose stride lands on it, with per-item checks.
-template <int U, typename Load, typename Compute, typename Store>
+//
+// XCD_CHUNKS: workgroups are dispatched round-robin over the eight XCDs
+// (workgroup b on XCD b mod 8), so by default each XCD walks tiles spaced
+// eight apart across the whole tensor; with XCD_CHUNKS (and a grid that is a
+// multiple of 8) workgroup b takes tile (b mod 8) G/8 + b/8 instead, so each
+// XCD walks one contiguous eighth of the tensor (a bijection on the tiles,
+// so the results do not change). On the 2.8e9-element weight set this made
+// dequantize 2.5-3.3 % faster (also on the MoE experts), left fake-quant
+// unchanged and made quantize 8 % slower; runs of four tiles per XCD were
+// slower for all three.
+template <int U, bool XCD_CHUNKS = false, typename Load, typename Compute, typename Store>
 __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Compute compute,
                                           Store store) {
   const int64_t tile = (int64_t)kThreads * U;
   const int64_t nfull = nitems / tile;
   int64_t t = blockIdx.x;
+  if (XCD_CHUNKS && gridDim.x % 8u == 0u)
+    t = (int64_t)(blockIdx.x % 8u) * (gridDim.x / 8u) + blockIdx.x / 8u;
   for (; t < nfull; t += gridDim.x) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
@@ -763,7 +775,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restr
                                                          void *__restrict__ y, int64_t nitems) {
   uint32_t cw[U], sb[U];
   uint32_t out[U][BF16 ? 4 : 8];
-  tile_loop<U>(
+  tile_loop<U, true>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
