@@ -550,8 +550,8 @@ __device__ __forceinline__ uint32_t quantize_pair(const PairItem &x, u32x2 &code
 // XCD walks one contiguous eighth of the tensor (a bijection on the tiles,
 // so the results do not change). On the 2.8e9-element weight set this made
 // dequantize 2.5-3.3 % faster (also on the MoE experts), left fake-quant
-// unchanged and made quantize 8 % slower; runs of four tiles per XCD were
-// slower for all three.
+// unchanged and made quantize 8 % and block MSE 4 % slower; runs of four
+// tiles per XCD were slower for all of them.
 template <int U, bool XCD_CHUNKS = false, typename Load, typename Compute, typename Store>
 __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Compute compute,
                                           Store store) {
