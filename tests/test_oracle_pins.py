@@ -397,6 +397,17 @@ def test_mse_matches_mean_of_squares(oracle_lib):
     d2 = (x.astype(np.float64) - y) ** 2
     np.testing.assert_allclose(bm, d2.reshape(x.shape[0], -1, 32).mean(-1), rtol=1e-7)
     assert abs(sse - d2.sum()) <= 1e-12 * d2.sum()
+    # the energy beside it (QSNR's numerator): every element's square, once
+    _, sse2, ssq = oracle_lib.block_mse(x, c, s, with_energy=True)
+    x2 = x.astype(np.float64) ** 2
+    assert sse2 == sse and abs(ssq - x2.sum()) <= 1e-12 * x2.sum()
+    # and per row: a tensor of one nonzero row carries exactly that row's energy
+    for r in (0, x.shape[0] - 1):
+        xr = np.zeros_like(x)
+        xr[r] = x[r]
+        cr, sr = oracle_lib.quantize(xr)
+        _, _, ssq_r = oracle_lib.block_mse(xr, cr, sr, with_energy=True)
+        assert abs(ssq_r - x2[r].sum()) <= 1e-12 * x2[r].sum()
 
 
 def test_footprint_closed_form():
