@@ -105,6 +105,25 @@ def test_invariants(oracle_lib):
     assert np.all(np.abs(y - x) <= np.abs(x).reshape(-1, 16).max(1).repeat(16).reshape(x.shape) * 0.25 + 1e-30)
 
 
+
+def test_decode_every_block_scale_byte(oracle_lib):
+    """Decoding reads the block scale as a full E4M3 byte, sign included
+    (the quantizer never writes a negative one), against torch's own
+    float8_e4m3fn reading of the byte: 0x7F and 0xFF are NaN."""
+    rng = np.random.default_rng(77)
+    bs = np.arange(256, dtype=np.uint8).reshape(16, 16)
+    codes = rng.integers(0, 256, (16, 128), dtype=np.uint8)
+    for t in (127, 135, 100):
+        y = oracle_lib.dequantize_nvfp4(codes, bs, t, "f32")
+        cc = np.empty((16, 256), np.int64)
+        cc[:, 0::2] = codes & 0xF
+        cc[:, 1::2] = codes >> 4
+        sv = torch.from_numpy(bs).view(torch.float8_e4m3fn).float().numpy().astype(np.float64).repeat(16, 1)
+        want = (np.where(cc & 8, -1, 1) * G[cc & 7] * sv / 2.0 ** (t - 127)).astype(np.float32)
+        nan = np.isnan(sv)
+        assert nan.sum() == 2 * 16 and np.isnan(y[nan]).all()
+        np.testing.assert_array_equal(y[~nan], want[~nan])
+
 def test_nonfinite_block_and_bf16(oracle_lib):
     x = np.zeros((2, 32), np.float32)
     x[0, 3] = np.nan

@@ -110,6 +110,10 @@ def test_scale_range_ends(oracle_lib):
     assert oracle_lib.ocp_scale(math.ldexp(1.0, -125)) == 0
     assert oracle_lib.ocp_scale(math.ldexp(1.0, -124)) == 1
     assert oracle_lib.ocp_scale(0.0) == 0
+    # past fp32's range (a double argument) the byte stops at E8M0's largest
+    # finite scale 2^127; byte 255 is E8M0's NaN, never a clamp
+    for e in (128, 129, 130, 131, 200, 1000):
+        assert oracle_lib.ocp_scale(math.ldexp(1.0, e)) == min(e - 2 + 127, 254), e
 
 
 # ---- rounding --------------------------------------------------------------
@@ -388,6 +392,23 @@ def test_mse_closed_form(oracle_lib):
         want = np.float32(X * X / 32) if X * X / 32 < 2.0 ** 128 else np.float32(np.inf)
         assert sse == X * X and bm[0, 0] == want
 
+
+
+def test_mse_reconstruction_overflows_like_fp32(oracle_lib):
+    """The error is taken against the value an fp32 dequantize returns: at
+    byte 254 a code of magnitude 2 or more decodes past fp32's largest finite
+    value (2^128 > (2 - 2^-23) * 2^127), so the reconstruction is +Inf and so
+    is the tensor SSE; one byte lower it is 2^127, finite."""
+    for dt in ("f32", "bf16"):
+        x = np.ones((1, 32), np.float32)
+        if dt == "bf16":
+            x = workloads.to_bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+        codes = np.full((1, 16), 0x44, np.uint8)          # every element: +2.0
+        for byte, want in ((253, 32 * 2.0 ** 254), (254, math.inf)):
+            bm, sse = oracle_lib.block_mse(x, codes, np.full((1, 1), byte, np.uint8))
+            # d = 1 - 2^127 rounds to -2^127 in fp64: SSE = 32 * 2^254 exactly
+            assert sse == want, (dt, byte, sse)
+            assert bm[0, 0] == np.float32(np.inf)           # 2^254 is past fp32 either way
 
 def test_mse_matches_mean_of_squares(oracle_lib):
     x = _rand(8)
