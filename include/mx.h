@@ -291,9 +291,10 @@ mx_status_t mx_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
  * converted checkpoint quantizes every one of them (Axolotl MXFP4 QAT page,
  * QATConfig section: weights of each Linear layer); vLLM's online path does
  * the same for each expert's weights ("MXFP4: 4-bit MoE" section). These
- * entry points take a list of separate tensors and cover them with one
- * launch per MX_MULTI_MAX (48) tensors instead of one per tensor, with
- * results identical to the single-tensor calls.
+ * entry points take a list of separate tensors and cover them with a few
+ * launches instead of one per tensor (tensors of similar size share one, at
+ * most MX_MULTI_MAX = 60 per launch), with results identical to the
+ * single-tensor calls.
  *
  * `tensors` is a HOST array of `count` descriptors, read during the call
  * only; every pointer inside is a device pointer, 16-byte aligned. All

@@ -537,7 +537,7 @@ def _multi_inputs(xs):
 
 def quantize_multi(xs, mode: str = "ocp"):
     """[x_i [..., k_i]] -> [(codes_i, scales_i)], as quantize() per tensor,
-    with one launch per 48 tensors."""
+    with one launch per group of up to 60 tensors of similar size."""
     if mode not in _MODES:
         raise ValueError(f"mode must be one of {MODES}")
     xs, dev, dt = _multi_inputs(xs)

@@ -59,9 +59,11 @@ hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint
 hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
                                      const uint8_t *macro_mant, int bf16, int64_t nitems, void *y,
                                      hipStream_t st);
-// Many tensors in one launch per MX_MULTI_MAX of them (empty ones skipped).
+// Many tensors in one call: launches of at most MX_MULTI_MAX tensors of
+// similar size (empty ones skipped); 60 descriptors are 1,920 bytes of
+// kernel arguments.
 #ifndef MX_MULTI_MAX
-#define MX_MULTI_MAX 48
+#define MX_MULTI_MAX 60
 #endif
 struct MxiTensor {
   const void *x;

@@ -36,7 +36,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "mx_internal.h"
 
@@ -52,8 +54,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef MX_UNROLL
 #define MX_UNROLL 4
 #endif
-// Most workgroups a launch of the other formats' kernels and of the
-// multi-tensor launch uses (beyond it, workgroups loop over tiles). Measured
+// Most workgroups a launch of the other formats' kernels uses (beyond it,
+// workgroups loop over tiles). Measured
 // on a 2.1e9-element bf16 tensor with four items per thread: 196,608 (768
 // per CU) beat 65,536 by 5 % (quantize) and 3 % (dequantize), while
 // 8,192-32,768 were slower. The MXFP4 single-tensor kernels are not capped
@@ -616,8 +618,8 @@ constexpr int kU = BF16 ? kUnroll : (kUnroll >= 4 ? kUnroll / 4 : 1);
 // 2.8e9-element Llama-3.2-3B weight set, quantize OCP with one item per thread
 // was 3.5 % faster than four, overflow-aware quantize with two 3.6 % faster,
 // fake-quant with one 5 % faster than two; OAS_NF quantize keeps four and
-// dequantize two. The multi-tensor launch uses the small-tensor numbers (its
-// tile offsets depend on them).
+// dequantize two. The multi-tensor launch picks by the items of the whole
+// call.
 #ifndef MX_LARGE_ITEMS
 #define MX_LARGE_ITEMS (int64_t(3) << 23)
 #endif
@@ -725,48 +727,41 @@ struct MultiDesc {
   void *out;        // quantize: codes; fake-quant: y
   uint8_t *scales;  // quantize: scales; fake-quant: unused
   int64_t nitems;   // rows * k / 8
-  int64_t tile0;    // first tile of this tensor in the launch
 };
 struct MultiArgs {
-  int count;
-  int64_t ntiles;  // tiles of the whole launch
   MultiDesc d[MX_MULTI_MAX];
 };
 
-__device__ __forceinline__ int multi_find(const MultiArgs &a, int64_t t) {
-  int lo = 0, hi = a.count - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.d[mid].tile0 <= t) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
-template <bool BF16, int MODE, bool FQ>
+// Many tensors in one launch: workgroup (x, y) takes tile x of tensor y, so
+// no workgroup searches for its tensor; tiles past a tensor's end do nothing
+// (the host groups tensors of similar size into one launch). On the 196
+// Llama-3.2-3B matrices this ran 3 % (quantize OCP) and 5 % (fake-quant)
+// faster than one 1-D grid whose workgroups found their tensor by a binary
+// search over the tensors' first tiles, with four items per thread: with
+// one item per thread that search cost 10 % more, since every tile waits
+// on it before its loads issue; a 64-lane compare of the first tiles
+// (one vector load) cost 25 %, a scalar compare of all of them 70 %.
+template <bool BF16, int MODE, bool FQ, bool LARGE>
 __global__ __launch_bounds__(kThreads) void k_multi(const MultiArgs a) {
-  constexpr int U = unroll_of(BF16, MODE, FQ ? kKindFakequant : kKindQuantize);
+  constexpr int U = unroll_of(BF16, MODE, FQ ? kKindFakequant : kKindQuantize, LARGE);
   Item<BF16> xv[U];
   uint32_t cw[U], sv[U], out[U][FQ ? (BF16 ? 4 : 8) : 1];
-  for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
-    const int j = multi_find(a, t);
-    const MultiDesc &d = a.d[j];
-    const void *x = d.x;
-    tile_at<U>(
-        t - d.tile0, d.nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
-        [&](int u, int64_t) {
-          sv[u] = quantize_item<BF16, MODE>(xv[u], cw[u]);
-          if constexpr (FQ) decode_item<BF16>(cw[u], sv[u], out[u]);
-        },
-        [&](int u, int64_t it) {
-          if constexpr (FQ) {
-            store_item<BF16>(d.out, it, out[u]);
-          } else {
-            st<false>(static_cast<uint32_t *>(d.out) + it, cw[u]);
-            if ((threadIdx.x & 3) == 0) st<false>(d.scales + (it >> 2), (uint8_t)sv[u]);
-          }
-        });
-  }
+  const MultiDesc &d = a.d[blockIdx.y];
+  const void *x = d.x;
+  tile_at<U>(
+      blockIdx.x, d.nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+      [&](int u, int64_t) {
+        sv[u] = quantize_item<BF16, MODE>(xv[u], cw[u]);
+        if constexpr (FQ) decode_item<BF16>(cw[u], sv[u], out[u]);
+      },
+      [&](int u, int64_t it) {
+        if constexpr (FQ) {
+          store_item<BF16>(d.out, it, out[u]);
+        } else {
+          st<false>(static_cast<uint32_t *>(d.out) + it, cw[u]);
+          if ((threadIdx.x & 3) == 0) st<false>(d.scales + (it >> 2), (uint8_t)sv[u]);
+        }
+      });
 }
 
 template <bool BF16, int U>
@@ -1547,19 +1542,19 @@ static unsigned grid_for(int64_t nitems, int64_t cap, int unroll = kUnroll) {
 
 using namespace mxk;
 
-#define MX_DISPATCH_MULTI(BF16, FQ, MODE, G, B, ST, ARGS)                                 \
+#define MX_DISPATCH_MULTI(BF16, FQ, L, MODE, G, B, ST, ARGS)                              \
   switch (MODE) {                                                                          \
     case MX_SCALE_OAS:                                                                     \
-      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OAS, FQ>), G, B, 0, ST, ARGS);            \
+      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OAS, FQ, L>), G, B, 0, ST, ARGS);         \
       break;                                                                               \
     case MX_SCALE_OAS_BITS:                                                                \
-      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OAS_BITS, FQ>), G, B, 0, ST, ARGS);       \
+      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OAS_BITS, FQ, L>), G, B, 0, ST, ARGS);    \
       break;                                                                               \
     case MX_SCALE_OAS_NF:                                                                  \
-      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OAS_NF, FQ>), G, B, 0, ST, ARGS);         \
+      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OAS_NF, FQ, L>), G, B, 0, ST, ARGS);      \
       break;                                                                               \
     default:                                                                               \
-      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OCP, FQ>), G, B, 0, ST, ARGS);            \
+      hipLaunchKernelGGL((k_multi<BF16, MX_SCALE_OCP, FQ, L>), G, B, 0, ST, ARGS);         \
       break;                                                                               \
   }
 
@@ -1904,33 +1899,46 @@ hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_sc
 
 hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, int fakequant,
                             hipStream_t st) {
-  // chunks of at most MX_MULTI_MAX non-empty tensors, one launch each
-  int i = 0;
-  while (i < count) {
+  const int kind = fakequant ? kKindFakequant : kKindQuantize;
+  // the large-tensor tiling when the call as a whole streams that much
+  int64_t total = 0;
+  std::vector<int> order;
+  order.reserve(count);
+  for (int i = 0; i < count; i++) {
+    if (t[i].nitems <= 0) continue;
+    total += t[i].nitems;
+    order.push_back(i);
+  }
+  const bool large = bf16 && total >= kLargeItems;
+  const int64_t tile = (int64_t)kThreads * (large ? unroll_of(true, mode, kind, true)
+                                                  : unroll_of(bf16, mode, kind));
+  // largest first; each launch takes up to MX_MULTI_MAX tensors of at least
+  // 7/8 of its first one's tiles, so at most 1/8 of its workgroups are idle
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int p, int q) { return t[p].nitems > t[q].nitems; });
+  size_t i = 0;
+  while (i < order.size()) {
+    const int64_t gx = (t[order[i]].nitems + tile - 1) / tile;
+    if (gx > kGridLimit) return hipErrorInvalidValue;
     MultiArgs a;
-    a.count = 0;
-    int64_t tiles = 0;
-    const int64_t tile =
-        (int64_t)kThreads * unroll_of(bf16, mode, fakequant ? kKindFakequant : kKindQuantize);
-    for (; i < count && a.count < MX_MULTI_MAX; i++) {
-      if (t[i].nitems <= 0) continue;
-      MultiDesc &d = a.d[a.count++];
-      d.x = t[i].x;
-      d.out = t[i].out;
-      d.scales = t[i].scales;
-      d.nitems = t[i].nitems;
-      d.tile0 = tiles;
-      tiles += (t[i].nitems + tile - 1) / tile;
+    int n = 0;
+    for (; i < order.size() && n < MX_MULTI_MAX; i++, n++) {
+      const MxiTensor &q = t[order[i]];
+      if (8 * ((q.nitems + tile - 1) / tile) < 7 * gx) break;
+      a.d[n] = {q.x, q.out, q.scales, q.nitems};
     }
-    if (a.count == 0) break;
-    a.ntiles = tiles;
-    const dim3 g((unsigned)(tiles < MX_GRID_CAP ? tiles : MX_GRID_CAP)), b(kThreads);
+    const dim3 g((unsigned)gx, (unsigned)n), b(kThreads);
     if (bf16) {
-      if (fakequant) { MX_DISPATCH_MULTI(true, true, mode, g, b, st, a) }
-      else { MX_DISPATCH_MULTI(true, false, mode, g, b, st, a) }
+      if (large) {
+        if (fakequant) { MX_DISPATCH_MULTI(true, true, true, mode, g, b, st, a) }
+        else { MX_DISPATCH_MULTI(true, false, true, mode, g, b, st, a) }
+      } else {
+        if (fakequant) { MX_DISPATCH_MULTI(true, true, false, mode, g, b, st, a) }
+        else { MX_DISPATCH_MULTI(true, false, false, mode, g, b, st, a) }
+      }
     } else {
-      if (fakequant) { MX_DISPATCH_MULTI(false, true, mode, g, b, st, a) }
-      else { MX_DISPATCH_MULTI(false, false, mode, g, b, st, a) }
+      if (fakequant) { MX_DISPATCH_MULTI(false, true, false, mode, g, b, st, a) }
+      else { MX_DISPATCH_MULTI(false, false, false, mode, g, b, st, a) }
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

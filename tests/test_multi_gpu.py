@@ -42,7 +42,7 @@ def ragged_list(seed: int, n: int, dtype):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("mode", mx.MODES)
 def test_multi_ragged_vs_oracle(dtype, mode):
-    xs = ragged_list(11 + mx.MODES.index(mode), 120, dtype)  # > 2 launches of 48
+    xs = ragged_list(11 + mx.MODES.index(mode), 120, dtype)  # > 60 tensors of many sizes
     xd = [x.cuda() for x in xs]
     say(f"multi {mode} {dtype}: {len(xs)} tensors")
     qs = mx.quantize_multi(xd, mode)
@@ -68,7 +68,7 @@ def test_multi_in_place_and_leading_dims():
 
 def test_multi_llama32_3b_separate_weights():
     """The 196 weights as separate tensors, one call: bit-equal to one
-    quantize call per matrix (5 launches instead of 196)."""
+    quantize call per matrix (4 launches instead of 196)."""
     say("generating llama weights on device")
     ms = [workloads.llama32_3b_matrix(layer, which, "cuda")
           for layer in range(workloads.LLAMA32_3B_LAYERS)
