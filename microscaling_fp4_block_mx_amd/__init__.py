@@ -557,9 +557,9 @@ def quantize_multi(xs, mode: str = "ocp"):
 
 
 def fakequant_multi(xs, mode: str = "ocp", out=None):
-    """[x_i] -> [y_i], as fakequant() per tensor, with one launch per 48
-    tensors; out may be a list of preallocated outputs (or the inputs, in
-    place)."""
+    """[x_i] -> [y_i], as fakequant() per tensor, with one launch per group
+    of up to 60 tensors of similar size; out may be a list of preallocated
+    outputs (or the inputs, in place)."""
     if mode not in _MODES:
         raise ValueError(f"mode must be one of {MODES}")
     xs, dev, dt = _multi_inputs(xs)

@@ -66,6 +66,30 @@ def test_multi_in_place_and_leading_dims():
         assert torch.equal(w.view(torch.int16), g.view(torch.int16))
 
 
+@pytest.mark.parametrize("mode", ["ocp", "oas", "oas_nf"])
+def test_multi_large_tiling_unequal_sizes(mode):
+    """A call past the large-tensor size (the tiling of multi-GB weight
+    sets) whose tensors differ in size by less than 1/8, so they share a
+    launch and the smaller ones leave tiles of the 2-D grid idle; plus small
+    and empty tensors in their own launches. Bit-equal to one call per
+    tensor, in both directions of the size order."""
+    # 2.2e8 elements in all (past 2^24 * 12 = 2.0e8); the seven large ones
+    # are within 7/8 of the largest
+    shapes = [(8192, 4096), (7680, 4096), (8000, 4096), (7424, 4096), (7200, 4096),
+              (0, 4096), (3, 96), (8192, 4096), (7900, 4096), (1, 32)]
+    xs = [workloads.bf16_student_t_outlier_channels(40 + i, shape=sh).cuda() if sh[0] else
+          torch.empty(sh, dtype=torch.bfloat16, device="cuda") for i, sh in enumerate(shapes)]
+    for order in (xs, xs[::-1]):
+        say(f"multi large {mode}: {[tuple(x.shape) for x in order]}")
+        qs = mx.quantize_multi(order, mode)
+        fs = mx.fakequant_multi(order, mode)
+        for i, (x, (c, s), f) in enumerate(zip(order, qs, fs)):
+            c1, s1 = mx.quantize(x, mode)
+            assert torch.equal(c, c1) and torch.equal(s, s1), f"tensor {i} {tuple(x.shape)}"
+            assert torch.equal(f.view(torch.int16), mx.fakequant(x, mode).view(torch.int16)), \
+                f"tensor {i} {tuple(x.shape)} fake-quant"
+
+
 def test_multi_llama32_3b_separate_weights():
     """The 196 weights as separate tensors, one call: bit-equal to one
     quantize call per matrix (4 launches instead of 196)."""
