@@ -419,7 +419,8 @@ def run_step(args, dev, stream):
 
     bytes_op = {op: BYTES_PER_ELEM[op] * n for op in OPS}
     bytes_step = sum(bytes_op.values())
-    breakdown = {op: _row(bytes_op[op], op_ms[op]) for op in OPS}
+    breakdown = {op: _row(bytes_op[op], op_ms[op], elements_per_s=round(n / (op_ms[op] * 1e-3), 1))
+                 for op in OPS}
     dom = max(OPS, key=lambda o: op_ms[o])
     dom_gbs = bytes_op[dom] / (op_ms[dom] * 1e-3) / 1e9
     mt = measured_traffic(dom)
