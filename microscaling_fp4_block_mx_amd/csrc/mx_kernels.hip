@@ -690,9 +690,7 @@ __global__ __launch_bounds__(kThreads) void k_fakequant(const void *x, void *y, 
 // or fake-quantized by one launch: a launch per tensor pays the per-kernel
 // ramp-up and drain each time (a 3 Mi-element weight runs at a quarter of the
 // streaming rate on its own). The descriptors travel by value in the kernel
-// arguments (no device table, nothing to copy or allocate; capturable). Tile
-// t of the launch belongs to the tensor whose first tile is the largest
-// tile0 <= t (a binary search on uniform values, so scalar work); a
+// arguments (no device table, nothing to copy or allocate; capturable). A
 // tensor's last tile may be partial and takes the per-item checks.
 
 template <int U, typename Load, typename Compute, typename Store>
