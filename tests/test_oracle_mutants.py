@@ -86,21 +86,40 @@ MUTANTS = [
      "double qf = q;"),
     ("energy_drops_an_element", "ssq += xv * xv;", "ssq += xv * xv * (i % 32 != 31);"),
     ("sse_drops_an_element", "sse += d * d;", "sse += d * d * (i % 32 != 5);"),
+    ("oas_skipped_at_byte_1", "if (mode == MXREF_OAS && s0 >= 1)", "if (mode == MXREF_OAS && s0 >= 2)"),
+    ("nf_skipped_at_byte_1", "  if (snf >= 1) {\n    float sse_nf", "  if (snf >= 2) {\n    float sse_nf"),
+    ("tensor_sse_in_fp32", "j->sse += (long double)sse;", "j->sse += (long double)(float)sse;"),
+    ("decode_scale_off_by_one", "double mag = kGrid[c & 7] * ldexp(1.0, s - 127);",
+     "double mag = kGrid[c & 7] * ldexp(1.0, s - 128);"),
+    # element stores
+    ("bf16_ties_away", "return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)((u + 0x8000u) >> 16);"),
+    ("negative_canonical_nan", "uint32_t q = 0x7FC00000u; /* canonical quiet NaN */",
+     "uint32_t q = 0xFFC00000u; /* canonical quiet NaN */"),
     # MXFP8 (E4M3 elements, emax 8)
     ("mxfp8_bias_off_by_one", "int s = (e2 - 1) - 8 + 127;", "int s = (e2 - 1) - 7 + 127;"),
     ("mxfp8_saturates_to_nan", "if (v >= 448.0) return sign | 0x7E;", "if (v >= 448.0) return sign | 0x7F;"),
     ("mxfp8_subnormal_scale", "if (e == 0) return ldexp((double)m / 8.0, -6);",
      "if (e == 0) return ldexp((double)m / 8.0, -7);"),
+    ("mxfp8_ties_up", "    c = (lo % 2 == 0) ? lo : hi;\n  return sign | c;", "    c = hi;\n  return sign | c;"),
+    ("mxfp8_nan_code_decoded", "if (s == 255 || (c & 0x7F) == 0x7F) return NAN;", "if (s == 255) return NAN;"),
     # NVFP4 comparator
     ("nvfp4_tensor_bound_inclusive", "ldexp(amax, t) > 2688.0) t--;", "ldexp(amax, t) >= 2688.0) t--;"),
     ("nvfp4_block_over_4", "float q6 = (float)ab / 6.0f;", "float q6 = (float)ab / 4.0f;"),
     ("nvfp4_decode_scale_sign_lost", "if (block_scale & 0x80) v = -v;", "if (block_scale & 0x100) v = -v;"),
+    ("nvfp4_scale_saturates_to_nan", "  if (v >= 448.0) return 0x7E;\n  int lo = 0;\n  while",
+     "  if (v >= 448.0) return 0x7F;\n  int lo = 0;\n  while"),
+    ("nvfp4_negative_zero_loses_sign", "code[i] = (signbit(xb[i]) ? 8 : 0) | (e2m1_code(fabsf(v)) & 7);",
+     "code[i] = (xb[i] < 0 ? 8 : 0) | (e2m1_code(fabsf(v)) & 7);"),
+    ("nvfp4_block_ties_up", "  if (v > mid) return hi;\n  return (lo % 2 == 0) ? lo : hi;\n}\n\nint mxrefnv",
+     "  if (v > mid) return hi;\n  return hi;\n}\n\nint mxrefnv"),
     # MBS-Static
     ("mbs_mantissa_truncated", "double m = nearbyint(t);", "double m = floor(t);"),
     ("mbs_decode_factor_128", "double f = 1.0 + macro_mant[i / 128] / 256.0;",
      "double f = 1.0 + macro_mant[i / 128] / 128.0;"),
     ("mbs_sub_block_uses_x", "y[i] = (float)v * inv; /* fp32 multiply */",
      "y[i] = (float)v; /* fp32 multiply */"),
+    ("mbs_mantissa_not_capped", "  if (m > 255.0) m = 255.0;\n", "\n"),
+    ("mbs_sub_block_16_to_32", "codes[(M * 128 + 16 * j) / 2 + t]", "codes[(M * 128 + 16 * j) / 2 + (t ^ 1)]"),
 ]
 
 

@@ -165,4 +165,26 @@ def test_block_scale_tie_and_tensor_boundary(oracle_lib):
     assert oracle_lib.nvfp4_tensor_exp(5.25 * (1 + 2.0 ** -20)) == 8
     z = np.zeros((1, 16), np.float32)
     z[0, 2] = 5.25
-    assert oracle_lib.quantize_nvfp4(z)[2] == 136
+    cz, bz, tz = oracle_lib.quantize_nvfp4(z)
+    assert tz == 136
+    # 5.25 * 2^9 = 2688 = 6 * 448 exactly: the block scale is E4M3's largest
+    # finite value (torch reads byte 0x7E as 448) and the maximum is code 7
+    assert bz[0, 0] == 0x7E
+    assert torch.tensor([0x7E], dtype=torch.uint8).view(torch.float8_e4m3fn).float().item() == 448.0
+    assert (cz[0, 1] & 0xF) == 7
+    assert oracle_lib.dequantize_nvfp4(cz, bz, tz, "f32")[0, 2] == 5.25
+
+
+def test_signed_zero(oracle_lib):
+    """E2M1's sign bit carries the sign of zero: -0.0 encodes to code 8 and
+    decodes to -0.0 (fp32 bits 0x80000000), +0.0 to code 0, in a block
+    with other values and in an all-zero block."""
+    x = np.zeros((2, 16), np.float32)
+    x[0, :4] = [-0.0, 0.0, 1.5, -0.0]
+    x[1, :2] = [-0.0, 0.0]
+    c, b, t = oracle_lib.quantize_nvfp4(x)
+    assert (c[0, 0] & 0xF) == 8 and (c[0, 0] >> 4) == 0 and (c[0, 1] >> 4) == 8
+    assert (c[1, 0] & 0xF) == 8 and (c[1, 0] >> 4) == 0
+    y = oracle_lib.dequantize_nvfp4(c, b, t, "f32").view(np.uint32)
+    assert y[0, 0] == 0x80000000 and y[0, 1] == 0 and y[0, 3] == 0x80000000
+    assert y[1, 0] == 0x80000000 and y[1, 1] == 0

@@ -324,6 +324,41 @@ def test_oas_worked_blocks_golden(oracle_lib):
         assert int(s[0, 0]) == 127
 
 
+def test_overflow_aware_choice_at_the_ends_of_the_byte_range(oracle_lib):
+    """The worked blocks of tests/golden/oas_worked_blocks.txt (A: 4 and
+    sixteen 0.75, a tie, keeps the OCP byte; B: seventeen 0.75 takes one
+    byte less) scaled by 2^(s-127) down to the smallest byte that has a
+    smaller candidate (s = 1, where the 0.75 * 2^-126 elements are fp32
+    subnormals, still exact) and up to the largest (252): every term of
+    both errors is the same in units of the larger candidate, so the choice
+    is the worked one. Likewise block C = {3.25, five 0.75} for the
+    no-overflow pair: at its no-overflow byte 3.25 rounds to 3 (error 0.25)
+    and each 0.75 ties to 1 (0.25), SSE 0.375; one byte lower 6.5
+    saturates to 6 (0.25 in the same units) and 1.5 is exact, SSE 0.0625:
+    the smaller byte wins, also at no-overflow byte 1."""
+    for s in (1, 2, 127, 251, 252):
+        for n, want in ((16, s), (17, s - 1)):
+            x = np.zeros((1, 32), np.float32)
+            x[0, 0] = 4.0
+            x[0, 1:1 + n] = 0.75
+            x = (x * np.float32(2.0 ** (s - 127))).astype(np.float32)
+            assert Fraction(float(x[0, 0])) == 4 * Fraction(2) ** (s - 127)
+            assert Fraction(float(x[0, 1])) == Fraction(3, 4) * Fraction(2) ** (s - 127)
+            _, so = oracle_lib.quantize(x, "ocp")
+            _, sa = oracle_lib.quantize(x, "oas")
+            assert int(so[0, 0]) == s and int(sa[0, 0]) == want, (s, n)
+    for s in (1, 2, 127, 252):
+        x = np.zeros((1, 32), np.float32)
+        x[0, 3] = 3.25
+        x[0, 10:15] = 0.75
+        x = (x * np.float32(2.0 ** (s - 127))).astype(np.float32)
+        assert Fraction(float(x[0, 3])) == Fraction(13, 4) * Fraction(2) ** (s - 127)
+        assert Fraction(float(x[0, 10])) == Fraction(3, 4) * Fraction(2) ** (s - 127)
+        _, sn = oracle_lib.quantize(x, "oas_nf")
+        _, sb = oracle_lib.quantize(x, "oas_bits")
+        assert int(sn[0, 0]) == s - 1 and int(sb[0, 0]) == s - 1, s
+
+
 def test_oas_never_worse_than_ocp(oracle_lib):
     x = workloads.to_bf16_bits(workloads.bf16_laplace_sparse_outliers(seed=9, shape=(64, 4096)))
     co, so = oracle_lib.quantize(x, "ocp")

@@ -68,6 +68,13 @@ def test_nvfp4_ragged_and_scales(rows, k, scale):
 def test_nvfp4_special_tensors():
     x = np.zeros((4, 64), np.float32)
     check_nv(torch.from_numpy(x), "all-zero")
+    sz = np.zeros((3, 32), np.float32)
+    sz[0, [0, 2, 5]] = -0.0          # signed zeros in an all-zero block
+    sz[1, :] = -0.0
+    sz[2, :] = np.linspace(-1, 1, 32)
+    sz[2, [3, 17]] = -0.0            # and beside nonzero values
+    check_nv(torch.from_numpy(sz), "signed zeros")
+    check_nv(torch.from_numpy(sz).to(torch.bfloat16), "signed zeros")
     x[1, 5] = np.nan
     x[2, 40] = -np.inf
     x[3, :] = np.linspace(-3, 3, 64)
