@@ -142,6 +142,43 @@ def test_oas_tie_prone_blocks():
     check_all_ops(torch.from_numpy(x).to(torch.bfloat16), "oas-tie-prone-bf16", modes=modes)
 
 
+def test_overflow_aware_at_the_ends_of_the_byte_range():
+    """Tie-prone blocks moved so that their OCP byte (and, for half of them,
+    their no-overflow byte) is 1, 2, 251 or 252: the smallest and largest
+    bytes that have a smaller candidate, where the blocks' small elements are
+    fp32 subnormals or the top ones near fp32's largest values. Both
+    outcomes of each choice occur; the hand-worked blocks (4 with sixteen or
+    seventeen 0.75; 3.25 with five 0.75) ride along at each byte."""
+    x = workloads.oas_tie_prone_blocks(28, 4000).astype(np.float64)
+    amax = np.abs(x).max(1, keepdims=True)
+    x = x / 2.0 ** np.floor(np.log2(amax))          # block maximum in [1, 2)
+    rng = np.random.default_rng(29)
+    s = rng.choice([1, 2, 251, 252], (x.shape[0], 1))
+    # normalized maximum in [4, 8) for the OCP byte s (half the blocks), or
+    # in (3, 6] for the no-overflow byte s
+    nf = rng.random((x.shape[0], 1)) < 0.5
+    x = x * np.where(nf, 3.0, 4.0)
+    x = (x * 2.0 ** (s - 127)).astype(np.float32)
+    worked = []
+    for b in (1, 2, 251, 252):
+        for n in (16, 17):
+            w = np.zeros(32)
+            w[0], w[1:1 + n] = 4.0, 0.75
+            worked.append(w * 2.0 ** (b - 127))
+        w = np.zeros(32)
+        w[3], w[10:15] = 3.25, 0.75
+        worked.append(w * 2.0 ** (b - 127))
+    x = np.concatenate([x, np.array(worked, np.float32)])
+    assert np.isfinite(x).all()
+    _, s0 = oracle.quantize(x, "ocp", threads=THREADS)
+    assert set(np.unique(s0)) >= {1, 2, 251, 252}
+    for mode in ("oas", "oas_nf"):
+        _, ws = oracle.quantize(x, mode, threads=THREADS)
+        assert (ws.astype(int) < s0.astype(int)).any() and (ws == s0).any(), mode
+    check_all_ops(torch.from_numpy(x), "byte-range-ends-f32")
+    check_all_ops(torch.from_numpy(x).to(torch.bfloat16), "byte-range-ends-bf16")
+
+
 def test_page_modes_near_scale_ceiling():
     """Block maxima near the largest finite values: the page modes cap the
     scale byte at 252 and never decode to Inf."""
