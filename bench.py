@@ -103,14 +103,17 @@ CEILING_BYTES_PER_ELEM = {"quantize_shape": 2 + 0.5 + 1 / 32, "dequantize_shape"
                           "block_mse_shape": 2 + 0.5 + 1 / 32 + 1 / 8,
                           "copy": 4.0, "read": 2.0,
                           "write": 2.0}
-# Kernel family of each op (the kernels' last template argument, U, is the
-# number of 8-element items per thread, which the library picks by size)
+# Kernel family of each op (the kernels' template argument U is the number of
+# 8-element items per thread, which the library picks by size; the quantize,
+# fake-quant and dequantize kernels take the threads per workgroup after it)
 KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0, U>", "quantize_oas": "k_quantize<true, 1, U>",
              "dequantize_bf16": "k_dequantize<true, U>",
              "fakequant_ocp": "k_fakequant<true, 0, U>", "block_mse": "k_block_mse<true, true, U>"}
-# kernels with items-per-thread as their last template argument, and one
-# tile (256 threads x U items x 8 elements) per workgroup at these sizes
+# kernels with items-per-thread as their last template argument (or, for
+# NT_KERNELS, U then the threads per workgroup NT), and one tile (NT threads
+# x U items x 8 elements; NT = 256 where not given) per workgroup at these sizes
 U_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize", "k_block_mse", "k_quantize_pair")
+NT_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize")
 ITEM_ELEMS = {"k_quantize_pair": 16}  # elements per item where not 8 (two lanes per block)
 FUSED_ITEMS = 2  # items per thread of k_quantize_fused
 PROFILE_STEM = {"step": "mx_llama32_3b_linears",
@@ -140,22 +143,40 @@ def kernel_code_hash() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def kernel_family(k: str) -> str:
-    """k_quantize<true, 0, 1> -> k_quantize<true, 0, U>; other names as they are."""
+def _u_nt(k: str):
+    """(name, leading template arguments, U, NT) of a kernel in U_KERNELS,
+    else None."""
+    m = re.fullmatch(r"(k_\w+)<(.*), (\d+), (\d+)>", k)
+    if m and m.group(1) in NT_KERNELS:
+        return m.group(1), m.group(2), int(m.group(3)), int(m.group(4))
     m = re.fullmatch(r"(k_\w+)<(.*), (\d+)>", k)
-    if m and m.group(1) in U_KERNELS:
-        return f"{m.group(1)}<{m.group(2)}, U>"
-    return k
+    if m and m.group(1) in U_KERNELS and m.group(1) not in NT_KERNELS:
+        return m.group(1), m.group(2), int(m.group(3)), 256
+    return None
+
+
+def kernel_family(k: str) -> str:
+    """k_quantize<true, 0, 1, 256> -> k_quantize<true, 0, U>,
+    k_block_mse<true, true, 2> -> k_block_mse<true, true, U>; other names
+    as they are."""
+    p = _u_nt(k)
+    return f"{p[0]}<{p[1]}, U>" if p else k
 
 
 def items_per_thread(k: str):
     """U of a kernel whose grid is one tile per workgroup, else None."""
-    m = re.fullmatch(r"(k_\w+)<.*, (\d+)>", k)
-    if m and m.group(1) in U_KERNELS:
-        return int(m.group(2))
+    p = _u_nt(k)
+    if p:
+        return p[2]
     if k.startswith("k_quantize_fused<"):
         return FUSED_ITEMS
     return None
+
+
+def threads_per_group(k: str) -> int:
+    """Threads per workgroup of kernel k (256 unless its name gives NT)."""
+    p = _u_nt(k)
+    return p[3] if p else 256
 
 
 def _traffic_lines(path):
@@ -1149,10 +1170,10 @@ def kernel_bytes_per_elem(k: str):
 
 def tile_elems(k: str, grid: int):
     """Elements a dispatch of k covers when it runs one tile per workgroup
-    (256 threads x U items x 8 elements, 16 for the two-lanes-per-block
+    (NT threads x U items x 8 elements, 16 for the two-lanes-per-block
     kernel), else None."""
     u = items_per_thread(k)
-    return grid * 256 * u * ITEM_ELEMS.get(k.split("<")[0], 8) if u else None
+    return grid * threads_per_group(k) * u * ITEM_ELEMS.get(k.split("<")[0], 8) if u else None
 
 
 # The two parts of bench.py that are profiled, each on its own (--only):
@@ -1414,8 +1435,8 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
            "Durations are the GPU's own per-dispatch times from the trace (under the profiler the "
            "host-side event figures of the small fp32 case are inflated by per-dispatch overhead; "
            "these are not). Launches are attributed to their workload by the elements their grid "
-           "covers (256 threads x U items x 8 elements per workgroup, U the kernel's last "
-           "template argument; the workloads' sizes all differ). The Laplace launches are split into the cold (rotated sets) and "
+           "covers (NT threads x U items x 8 elements per workgroup, from the kernel's template "
+           "arguments; the workloads' sizes all differ). The Laplace launches are split into the cold (rotated sets) and "
            f"warm (one set) timings by dispatch order ({per_timing} dispatches each). "
            "Per-matrix Llama launches are grouped by shape. The fp32 rows mix cold, warm, "
            "single-launch and graph-replayed dispatches. The suite's QSNR pass, which runs after "

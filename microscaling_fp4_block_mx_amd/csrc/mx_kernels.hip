@@ -530,8 +530,9 @@ __device__ __forceinline__ uint32_t quantize_pair(const PairItem &x, u32x2 &code
 
 // ---- kernels -----------------------------------------------------------------
 
-// Grid-stride over tiles of kThreads * U items; each thread's U items are
-// spaced kThreads apart so every load instruction is coalesced. A tile runs
+// Grid-stride over tiles of NT * U items (NT threads per workgroup); each
+// thread's U items are spaced NT apart so every load instruction is
+// coalesced. A tile runs
 // in three phases: every item's loads, every item's arithmetic (results kept
 // in registers), every item's stores. The vector memory counter that a wave
 // waits on for its loads also counts its stores, so a store issued between
@@ -554,10 +555,11 @@ __device__ __forceinline__ uint32_t quantize_pair(const PairItem &x, u32x2 &code
 // dequantize 2.5-3.3 % faster (also on the MoE experts), left fake-quant
 // unchanged and made quantize 8 % and block MSE 4 % slower; runs of four
 // tiles per XCD were slower for all of them.
-template <int U, bool XCD_CHUNKS = false, typename Load, typename Compute, typename Store>
+template <int U, bool XCD_CHUNKS = false, int NT = kThreads, typename Load, typename Compute,
+          typename Store>
 __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Compute compute,
                                           Store store) {
-  const int64_t tile = (int64_t)kThreads * U;
+  const int64_t tile = (int64_t)NT * U;
   const int64_t nfull = nitems / tile;
   int64_t t = blockIdx.x;
   if (XCD_CHUNKS && gridDim.x % 8u == 0u)
@@ -565,25 +567,25 @@ __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Compute com
   for (; t < nfull; t += gridDim.x) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < U; u++) load(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) load(u, base + u * NT);
     __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
 #pragma unroll
-    for (int u = 0; u < U; u++) compute(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) compute(u, base + u * NT);
     __builtin_amdgcn_sched_barrier(0);  // every item's arithmetic ahead of the stores
 #pragma unroll
-    for (int u = 0; u < U; u++) store(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) store(u, base + u * NT);
   }
   if (t == nfull && nfull * tile < nitems) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (base + u * kThreads < nitems) load(u, base + u * kThreads);
+      if (base + u * NT < nitems) load(u, base + u * NT);
 #pragma unroll
     for (int u = 0; u < U; u++)  // whole quads (16-lane rows) drop out together
-      if (base + u * kThreads < nitems) compute(u, base + u * kThreads);
+      if (base + u * NT < nitems) compute(u, base + u * NT);
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (base + u * kThreads < nitems) store(u, base + u * kThreads);
+      if (base + u * NT < nitems) store(u, base + u * NT);
   }
 }
 
@@ -637,14 +639,29 @@ constexpr int unroll_of(bool bf16, int mode, int kind, bool large = false) {
   return 2;
 }
 
-template <bool BF16, int MODE, int U>
-__global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ x,
-                                                       uint32_t *__restrict__ codes,
-                                                       uint8_t *__restrict__ scales,
-                                                       int64_t nitems) {
+// Threads per workgroup of the bf16 quantize, fake-quant and dequantize
+// kernels on multi-GB tensors (one tile per workgroup, so this is also the
+// tile's width); everything else keeps kThreads. Measured on the 2.8e9-
+// element Llama-3.2-3B weight set against 256 threads: overflow-aware
+// quantize with 128 4 % faster (64: 3 % slower, 512: 3 % slower),
+// dequantize with 64 2.4 % faster and fake-quant with 64 1.6 % faster (128
+// and 512 slower or equal), while quantize OCP keeps 256 (64: 5 % slower,
+// 128: 4 %, 512: 1.5 %). A plain copy of the same buffer ran 3.4 % faster
+// with 64 than with 256.
+constexpr int threads_of(bool bf16, int mode, int kind, bool large = false) {
+  if (!bf16 || !large) return kThreads;
+  if (kind == kKindFakequant || kind == kKindDequantize) return 64;
+  if (kind == kKindQuantize && mode == MX_SCALE_OAS) return 128;
+  return kThreads;
+}
+
+template <bool BF16, int MODE, int U, int NT>
+__global__ __launch_bounds__(NT) void k_quantize(const void *__restrict__ x,
+                                                 uint32_t *__restrict__ codes,
+                                                 uint8_t *__restrict__ scales, int64_t nitems) {
   Item<BF16> xv[U];
   uint32_t cw[U], sv[U];
-  tile_loop<U>(
+  tile_loop<U, false, NT>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) { sv[u] = quantize_item<BF16, MODE>(xv[u], cw[u]); },
       [&](int u, int64_t it) {
@@ -670,11 +687,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pair(const void *__restri
         if ((threadIdx.x & 1) == 0) st<false>(scales + (pit >> 1), (uint8_t)sv[u]);
       });
 }
-template <bool BF16, int MODE, int U>
-__global__ __launch_bounds__(kThreads) void k_fakequant(const void *x, void *y, int64_t nitems) {
+template <bool BF16, int MODE, int U, int NT>
+__global__ __launch_bounds__(NT) void k_fakequant(const void *x, void *y, int64_t nitems) {
   Item<BF16> xv[U];
   uint32_t out[U][BF16 ? 4 : 8];
-  tile_loop<U>(
+  tile_loop<U, false, NT>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) {
         uint32_t c;
@@ -693,30 +710,30 @@ __global__ __launch_bounds__(kThreads) void k_fakequant(const void *x, void *y, 
 // arguments (no device table, nothing to copy or allocate; capturable). A
 // tensor's last tile may be partial and takes the per-item checks.
 
-template <int U, typename Load, typename Compute, typename Store>
+template <int U, int NT, typename Load, typename Compute, typename Store>
 __device__ __forceinline__ void tile_at(int64_t t, int64_t nitems, Load load, Compute compute,
                                         Store store) {
-  const int64_t tile = (int64_t)kThreads * U;
+  const int64_t tile = (int64_t)NT * U;
   const int64_t base = t * tile + threadIdx.x;
   if ((t + 1) * tile <= nitems) {
 #pragma unroll
-    for (int u = 0; u < U; u++) load(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) load(u, base + u * NT);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; u++) compute(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) compute(u, base + u * NT);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; u++) store(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) store(u, base + u * NT);
   } else {
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (base + u * kThreads < nitems) load(u, base + u * kThreads);
+      if (base + u * NT < nitems) load(u, base + u * NT);
 #pragma unroll
     for (int u = 0; u < U; u++)  // whole quads drop out together
-      if (base + u * kThreads < nitems) compute(u, base + u * kThreads);
+      if (base + u * NT < nitems) compute(u, base + u * NT);
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (base + u * kThreads < nitems) store(u, base + u * kThreads);
+      if (base + u * NT < nitems) store(u, base + u * NT);
   }
 }
 
@@ -732,21 +749,24 @@ struct MultiArgs {
 
 // Many tensors in one launch: workgroup (x, y) takes tile x of tensor y, so
 // no workgroup searches for its tensor; tiles past a tensor's end do nothing
-// (the host groups tensors of similar size into one launch). On the 196
+// (the host groups tensors of similar size into one launch). Items per
+// thread and threads per workgroup follow the single-tensor kernels for the
+// size of the whole call. On the 196
 // Llama-3.2-3B matrices this ran 3 % (quantize OCP) and 5 % (fake-quant)
 // faster than one 1-D grid whose workgroups found their tensor by a binary
 // search over the tensors' first tiles, with four items per thread: with
 // one item per thread that search cost 10 % more, since every tile waits
 // on it before its loads issue; a 64-lane compare of the first tiles
 // (one vector load) cost 25 %, a scalar compare of all of them 70 %.
-template <bool BF16, int MODE, bool FQ, bool LARGE>
-__global__ __launch_bounds__(kThreads) void k_multi(const MultiArgs a) {
+template <bool BF16, int MODE, bool FQ, bool LARGE,
+          int NT = threads_of(BF16, MODE, FQ ? kKindFakequant : kKindQuantize, LARGE)>
+__global__ __launch_bounds__(NT) void k_multi(const MultiArgs a) {
   constexpr int U = unroll_of(BF16, MODE, FQ ? kKindFakequant : kKindQuantize, LARGE);
   Item<BF16> xv[U];
   uint32_t cw[U], sv[U], out[U][FQ ? (BF16 ? 4 : 8) : 1];
   const MultiDesc &d = a.d[blockIdx.y];
   const void *x = d.x;
-  tile_at<U>(
+  tile_at<U, NT>(
       blockIdx.x, d.nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) {
         sv[u] = quantize_item<BF16, MODE>(xv[u], cw[u]);
@@ -762,13 +782,13 @@ __global__ __launch_bounds__(kThreads) void k_multi(const MultiArgs a) {
       });
 }
 
-template <bool BF16, int U>
-__global__ __launch_bounds__(kThreads) void k_dequantize(const uint32_t *__restrict__ codes,
-                                                         const uint8_t *__restrict__ scales,
-                                                         void *__restrict__ y, int64_t nitems) {
+template <bool BF16, int U, int NT>
+__global__ __launch_bounds__(NT) void k_dequantize(const uint32_t *__restrict__ codes,
+                                                   const uint8_t *__restrict__ scales,
+                                                   void *__restrict__ y, int64_t nitems) {
   uint32_t cw[U], sb[U];
   uint32_t out[U][BF16 ? 4 : 8];
-  tile_loop<U, true>(
+  tile_loop<U, true, NT>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
@@ -1528,8 +1548,8 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_mbs(const uint32_t *__r
 
 // ---- launchers -----------------------------------------------------------------
 
-static unsigned grid_for(int64_t nitems, int64_t cap, int unroll = kUnroll) {
-  const int64_t tile = (int64_t)kThreads * unroll;
+static unsigned grid_for(int64_t nitems, int64_t cap, int unroll = kUnroll, int nt = kThreads) {
+  const int64_t tile = (int64_t)nt * unroll;
   int64_t g = (nitems + tile - 1) / tile;
   if (g > cap) g = cap;
   if (g < 1) g = 1;
@@ -1581,12 +1601,14 @@ static void launch_quantize_t(const void *x, uint32_t *c, uint8_t *s, int64_t ni
   }
   if (nitems >= kLargeItems) {
     constexpr int U = unroll_of(BF16, MODE, kKindQuantize, true);
-    hipLaunchKernelGGL((k_quantize<BF16, MODE, U>), dim3(grid_for(nitems, kGridLimit, U)),
-                       dim3(kThreads), 0, st, x, c, s, nitems);
+    constexpr int NT = threads_of(BF16, MODE, kKindQuantize, true);
+    hipLaunchKernelGGL((k_quantize<BF16, MODE, U, NT>), dim3(grid_for(nitems, kGridLimit, U, NT)),
+                       dim3(NT), 0, st, x, c, s, nitems);
   } else {
     constexpr int U = unroll_of(BF16, MODE, kKindQuantize, false);
-    hipLaunchKernelGGL((k_quantize<BF16, MODE, U>), dim3(grid_for(nitems, kGridLimit, U)),
-                       dim3(kThreads), 0, st, x, c, s, nitems);
+    constexpr int NT = threads_of(BF16, MODE, kKindQuantize, false);
+    hipLaunchKernelGGL((k_quantize<BF16, MODE, U, NT>), dim3(grid_for(nitems, kGridLimit, U, NT)),
+                       dim3(NT), 0, st, x, c, s, nitems);
   }
 }
 
@@ -1594,12 +1616,14 @@ template <bool BF16, int MODE>
 static void launch_fakequant_t(const void *x, void *y, int64_t nitems, hipStream_t st) {
   if (nitems >= kLargeItems) {
     constexpr int U = unroll_of(BF16, MODE, kKindFakequant, true);
-    hipLaunchKernelGGL((k_fakequant<BF16, MODE, U>), dim3(grid_for(nitems, kGridLimit, U)),
-                       dim3(kThreads), 0, st, x, y, nitems);
+    constexpr int NT = threads_of(BF16, MODE, kKindFakequant, true);
+    hipLaunchKernelGGL((k_fakequant<BF16, MODE, U, NT>), dim3(grid_for(nitems, kGridLimit, U, NT)),
+                       dim3(NT), 0, st, x, y, nitems);
   } else {
     constexpr int U = unroll_of(BF16, MODE, kKindFakequant, false);
-    hipLaunchKernelGGL((k_fakequant<BF16, MODE, U>), dim3(grid_for(nitems, kGridLimit, U)),
-                       dim3(kThreads), 0, st, x, y, nitems);
+    constexpr int NT = threads_of(BF16, MODE, kKindFakequant, false);
+    hipLaunchKernelGGL((k_fakequant<BF16, MODE, U, NT>), dim3(grid_for(nitems, kGridLimit, U, NT)),
+                       dim3(NT), 0, st, x, y, nitems);
   }
 }
 
@@ -1608,12 +1632,14 @@ static void launch_dequantize_t(const uint32_t *c, const uint8_t *s, void *y, in
                                 hipStream_t st) {
   if (nitems >= kLargeItems) {
     constexpr int U = unroll_of(BF16, 0, kKindDequantize, true);
-    hipLaunchKernelGGL((k_dequantize<BF16, U>), dim3(grid_for(nitems, kGridLimit, U)),
-                       dim3(kThreads), 0, st, c, s, y, nitems);
+    constexpr int NT = threads_of(BF16, 0, kKindDequantize, true);
+    hipLaunchKernelGGL((k_dequantize<BF16, U, NT>), dim3(grid_for(nitems, kGridLimit, U, NT)),
+                       dim3(NT), 0, st, c, s, y, nitems);
   } else {
     constexpr int U = unroll_of(BF16, 0, kKindDequantize, false);
-    hipLaunchKernelGGL((k_dequantize<BF16, U>), dim3(grid_for(nitems, kGridLimit, U)),
-                       dim3(kThreads), 0, st, c, s, y, nitems);
+    constexpr int NT = threads_of(BF16, 0, kKindDequantize, false);
+    hipLaunchKernelGGL((k_dequantize<BF16, U, NT>), dim3(grid_for(nitems, kGridLimit, U, NT)),
+                       dim3(NT), 0, st, c, s, y, nitems);
   }
 }
 
@@ -1908,8 +1934,9 @@ hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, i
     order.push_back(i);
   }
   const bool large = bf16 && total >= kLargeItems;
-  const int64_t tile = (int64_t)kThreads * (large ? unroll_of(true, mode, kind, true)
-                                                  : unroll_of(bf16, mode, kind));
+  const int nt = large ? threads_of(true, mode, kind, true) : threads_of(bf16, mode, kind);
+  const int64_t tile = (int64_t)nt * (large ? unroll_of(true, mode, kind, true)
+                                            : unroll_of(bf16, mode, kind));
   // largest first; each launch takes up to MX_MULTI_MAX tensors of at least
   // 7/8 of its first one's tiles, so at most 1/8 of its workgroups are idle
   std::stable_sort(order.begin(), order.end(),
@@ -1925,7 +1952,7 @@ hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, i
       if (8 * ((q.nitems + tile - 1) / tile) < 7 * gx) break;
       a.d[n] = {q.x, q.out, q.scales, q.nitems};
     }
-    const dim3 g((unsigned)gx, (unsigned)n), b(kThreads);
+    const dim3 g((unsigned)gx, (unsigned)n), b((unsigned)nt);
     if (bf16) {
       if (large) {
         if (fakequant) { MX_DISPATCH_MULTI(true, true, true, mode, g, b, st, a) }

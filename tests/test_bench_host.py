@@ -22,7 +22,7 @@ def test_traffic_summary_calibration(tmp_path):
     out.mkdir()
     n = bench.STEP_ELEMS
     copy = "void (anonymous namespace)::k_ceiling_copy(u32x4 const*, u32x4*, long)"
-    fq = "void mxk::k_fakequant<true, 0, 1>(void const*, void*, long)"
+    fq = "void mxk::k_fakequant<true, 0, 1, 64>(void const*, void*, long)"
     wg = 256
     grid = n // 2048 * wg  # work-items: one tile of 256 x 8 elements per workgroup
     # two fake-quant dispatches of 1000 us and 1100 us, one copy of 900 us
@@ -42,10 +42,10 @@ def test_traffic_summary_calibration(tmp_path):
     assert "FETCH_SIZE is scaled by 2.0000 and WRITE_SIZE by 1.0000" in text
     # fake-quant: 2n bytes fetched (after scaling) + 2n written = 4n, its
     # algorithmic bytes exactly
-    assert f"traffic_bytes k_fakequant<true, 0, 1> {4 * n}" in text
+    assert f"traffic_bytes k_fakequant<true, 0, 1, 64> {4 * n}" in text
     assert "kernel_code_sha256_prefix " + bench.kernel_code_hash() in text
     trace = (out / (bench.PROFILE_STEM["step"] + "_kernel_trace.md")).read_text()
-    row = next(ln for ln in trace.splitlines() if ln.startswith("| `k_fakequant<true, 0, 1>`"))
+    row = next(ln for ln in trace.splitlines() if ln.startswith("| `k_fakequant<true, 0, 1, 64>`"))
     # 4n bytes in 1050 us on average
     gbs = 4 * n / 1050e-6 / 1e9
     assert f"| {n // 2048} | {n} | 2 | 1050.00 | 1000.00 | 1100.00 | {4 * n} | {gbs:.0f} |" in row
@@ -56,7 +56,7 @@ def test_traffic_summary_calibration(tmp_path):
     old = bench.TRAFFIC_FILE
     try:
         bench.TRAFFIC_FILE = str(monkey_file)
-        assert bench.measured_traffic("fakequant_ocp") == ("k_fakequant<true, 0, 1>", 4 * n)
+        assert bench.measured_traffic("fakequant_ocp") == ("k_fakequant<true, 0, 1, 64>", 4 * n)
         assert bench.measured_traffic("quantize_ocp") is None
     finally:
         bench.TRAFFIC_FILE = old
@@ -64,25 +64,30 @@ def test_traffic_summary_calibration(tmp_path):
 
 def test_kernel_names_and_families():
     short = bench._kernel_short
-    assert short("void mxk::k_quantize<true, 3, 4>(void const*, unsigned int*, unsigned char*, "
-                 "long)") == "k_quantize<true, 3, 4>"
+    assert short("void mxk::k_quantize<true, 3, 4, 256>(void const*, unsigned int*, unsigned char*, "
+                 "long)") == "k_quantize<true, 3, 4, 256>"
     assert short("(anonymous namespace)::k_ceiling_copy(u32x4 const*, u32x4*, long) [clone .kd]"
                  ) == "k_ceiling_copy"
     assert short("mxk::k_sum_partials(double const*, long, double*)") == "k_sum_partials"
     fam = bench.kernel_family
-    assert fam("k_quantize<true, 3, 4>") == "k_quantize<true, 3, U>"
-    assert fam("k_dequantize<true, 2>") == "k_dequantize<true, U>"
+    assert fam("k_quantize<true, 3, 4, 256>") == "k_quantize<true, 3, U>"
+    assert fam("k_quantize<true, 1, 2, 128>") == "k_quantize<true, 1, U>"
+    assert fam("k_dequantize<true, 2, 64>") == "k_dequantize<true, U>"
     assert fam("k_block_mse<true, true, 2>") == "k_block_mse<true, true, U>"
     assert fam("k_quantize_nv<true, false>") == "k_quantize_nv<true, false>"
     assert fam("k_quantize_fused<true, 0, true>") == "k_quantize_fused<true, 0, true>"
-    assert bench.items_per_thread("k_fakequant<true, 1, 2>") == 2
+    assert bench.items_per_thread("k_fakequant<true, 1, 2, 256>") == 2
+    assert bench.items_per_thread("k_fakequant<true, 0, 1, 64>") == 1
+    assert bench.threads_per_group("k_fakequant<true, 0, 1, 64>") == 64
+    assert bench.threads_per_group("k_block_mse<true, true, 2>") == 256
     assert bench.items_per_thread("k_quantize_fused<true, 0, true>") == bench.FUSED_ITEMS
     assert bench.items_per_thread("k_quantize8<true>") is None
     # the two-lanes-per-block kernel: 16 elements per item
     assert bench.kernel_family("k_quantize_pair<3, 1>") == "k_quantize_pair<3, U>"
     assert bench.tile_elems("k_quantize_pair<3, 1>", 8192) == 8192 * 4096
-    assert bench.tile_elems("k_quantize<true, 3, 2>", 8192) == 8192 * 4096
-    assert bench.kernel_bytes_per_elem("k_quantize<true, 0, 1>") == 2 + 0.5 + 1 / 32
+    assert bench.tile_elems("k_quantize<true, 3, 2, 256>", 8192) == 8192 * 4096
+    assert bench.tile_elems("k_dequantize<true, 2, 64>", 32768) == 32768 * 1024
+    assert bench.kernel_bytes_per_elem("k_quantize<true, 0, 1, 256>") == 2 + 0.5 + 1 / 32
     assert bench.kernel_bytes_per_elem("k_ceiling_read") == 2.0
 
 
@@ -90,7 +95,9 @@ def test_algorithmic_bytes_agree_with_the_step():
     n = bench.STEP_ELEMS
     for op, k in bench.KERNEL_OF.items():
         assert bench.KERNEL_BYTES_PER_ELEM[k] == bench.BYTES_PER_ELEM[op]
-        assert bench.kernel_family(k.replace(", U>", ", 1>")) == k
+        name = k.split("<")[0]
+        assert bench.kernel_family(k.replace(", U>", ", 1, 64>" if name in bench.NT_KERNELS
+                                              else ", 1>")) == k
     # NVFP4 quantize is its two kernels
     assert (bench.KERNEL_BYTES_PER_ELEM["k_absmax_partials<true>"]
             + bench.KERNEL_BYTES_PER_ELEM["k_quantize_nv<true, false>"]) * n \
@@ -105,9 +112,9 @@ def test_algorithmic_bytes_agree_with_the_step():
 
 def test_beside_phase_attributes_by_grid():
     elems = bench.PHASES["beside"]["elems"]
-    assert elems("k_quantize<true, 0, 4>", 16384) == 16384 * 8192
-    assert elems("k_quantize<true, 3, 4>", 4096) == 8192 * 4096
-    assert elems("k_fakequant<true, 0, 2>", 8192) == 8192 * 4096
+    assert elems("k_quantize<true, 0, 4, 256>", 16384) == 16384 * 8192
+    assert elems("k_quantize<true, 3, 4, 256>", 4096) == 8192 * 4096
+    assert elems("k_fakequant<true, 0, 2, 256>", 8192) == 8192 * 4096
     assert elems("k_quantize_fused<true, 0, true>", 8192) == 8192 * 4096
     assert elems("k_quantize8<true>", 4096) == 8192 * 4096
 
@@ -136,12 +143,12 @@ def test_suite_attribution_by_elements(tmp_path):
     # one dispatch per workload shape; the run ends with the MoE dequantize
     # launches and the untimed QSNR pass after them is left out
     wg = 256
-    disp = [("k_quantize<true, 0, 1>", 688128 * 3072 // 2048),
-            ("k_quantize<true, 0, 1>", bench.STEP_ELEMS // 2048),
-            ("k_quantize<true, 0, 4>", 3072 * 3072 // 8192),
-            ("k_quantize<true, 0, 1>", 128 * 3072 * 4096 // 2048),
-            ("k_dequantize<true, 2>", 128 * 4096 * 1536 // 4096),
-            ("k_dequantize<true, 2>", 16384 * 8192 // 4096)]
+    disp = [("k_quantize<true, 0, 1, 256>", 688128 * 3072 // 2048),
+            ("k_quantize<true, 0, 1, 256>", bench.STEP_ELEMS // 2048),
+            ("k_quantize<true, 0, 4, 256>", 3072 * 3072 // 8192),
+            ("k_quantize<true, 0, 1, 256>", 128 * 3072 * 4096 // 2048),
+            ("k_dequantize<true, 2, 64>", 128 * 4096 * 1536 // 1024),
+            ("k_dequantize<true, 2, 256>", 16384 * 8192 // 4096)]
     rows = [[f"void mxk::{k}(void const*, long)", g * wg, wg, 10 * i * 1000, (10 * i + 1) * 1000]
             for i, (k, g) in enumerate(disp)]
     _write(tmp_path / "suite_kernel_trace.csv",
@@ -149,11 +156,11 @@ def test_suite_attribution_by_elements(tmp_path):
            rows)
     bench._summarize_suite(str(tmp_path / "suite_kernel_trace.csv"), "", str(tmp_path))
     text = (tmp_path / "mx_workloads_suite_kernel_trace.md").read_text()
-    for label in ("K=3072 [688128, 3072] | `k_quantize<true, 0, 1>`",
-                  "one launch [917504, 3072] | `k_quantize<true, 0, 1>`",
-                  "q/o [3072, 3072] | `k_quantize<true, 0, 4>`",
-                  "MoE w13 [128x3072, 4096] | `k_quantize<true, 0, 1>`",
-                  "MoE w2 [128x4096, 1536] | `k_dequantize<true, 2>`"):
+    for label in ("K=3072 [688128, 3072] | `k_quantize<true, 0, 1, 256>`",
+                  "one launch [917504, 3072] | `k_quantize<true, 0, 1, 256>`",
+                  "q/o [3072, 3072] | `k_quantize<true, 0, 4, 256>`",
+                  "MoE w13 [128x3072, 4096] | `k_quantize<true, 0, 1, 256>`",
+                  "MoE w2 [128x4096, 1536] | `k_dequantize<true, 2, 64>`"):
         assert label in text, label
     assert "| bf16 Laplace" not in text and "unattributed" not in text
 
@@ -163,8 +170,10 @@ def test_every_op_beside_the_step_has_roofline_kernels():
     for op in list(bench.EXTRA_BYTES_PER_ELEM) + ["reference_copy", "quantize_ocp",
                                                  "quantize_oas"]:
         fams = [f for g in bench.BESIDE_KERNELS[op] for f in (g if isinstance(g, tuple) else (g,))]
-        assert fams and all(bench.kernel_bytes_per_elem(f.replace(", U>", ", 4>")) is not None
-                            or f == "k_ceiling_copy" for f in fams), op
+        full = [f.replace(", U>", ", 4, 256>" if f.split("<")[0] in bench.NT_KERNELS else ", 4>")
+                for f in fams]
+        assert fams and all(bench.kernel_bytes_per_elem(f) is not None
+                            or f == "k_ceiling_copy" for f in full), op
         row = {"GB/s": 1.0, "frac_hbm": 0.5, "bytes": 10, "us": 1.0}
         r = bench.beside_roofline(op, row)
         assert r["bound"] == "hbm" and r["peak"] == bench.HBM_PEAK_GBS and r["frac"] == 0.5
