@@ -642,12 +642,12 @@ constexpr int unroll_of(bool bf16, int mode, int kind, bool large = false) {
 // Threads per workgroup of the bf16 quantize, fake-quant and dequantize
 // kernels on multi-GB tensors (one tile per workgroup, so this is also the
 // tile's width); everything else keeps kThreads. Measured on the 2.8e9-
-// element Llama-3.2-3B weight set against 256 threads: overflow-aware
-// quantize with 128 4 % faster (64: 3 % slower, 512: 3 % slower),
-// dequantize with 64 2.4 % faster and fake-quant with 64 1.6 % faster (128
-// and 512 slower or equal), while quantize OCP keeps 256 (64: 5 % slower,
-// 128: 4 %, 512: 1.5 %). A plain copy of the same buffer ran 3.4 % faster
-// with 64 than with 256.
+// element Llama-3.2-3B weight set against 256 threads: OAS quantize with
+// 128 4-6 % faster (64: up to 3 % slower, 512: 3 % slower), dequantize with
+// 64 2.4 % faster and fake-quant with 64 faster in every mode (OCP 1.6-1.8 %,
+// OAS 4 %, OAS_BITS 1.7 %, OAS_NF 5 %; 128 and 512 slower or equal), while
+// quantize OCP, OAS_BITS and OAS_NF keep 256 (64 and 128: 2-5 % slower). A
+// plain copy of the same buffer ran 3.4 % faster with 64 than with 256.
 constexpr int threads_of(bool bf16, int mode, int kind, bool large = false) {
   if (!bf16 || !large) return kThreads;
   if (kind == kKindFakequant || kind == kKindDequantize) return 64;
