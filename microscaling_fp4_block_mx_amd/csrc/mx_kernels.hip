@@ -619,8 +619,9 @@ constexpr int kU = BF16 ? kUnroll : (kUnroll >= 4 ? kUnroll / 4 : 1);
 // the memory that the resident workgroups touch at one time compact: on the
 // 2.8e9-element Llama-3.2-3B weight set, quantize OCP with one item per thread
 // was 3.5 % faster than four, overflow-aware quantize with two 3.6 % faster,
-// fake-quant with one 5 % faster than two; OAS_NF quantize keeps four and
-// dequantize two. The multi-tensor launch picks by the items of the whole
+// fake-quant with one 5 % faster than two, dequantize keeps two; OAS_NF
+// quantize takes two with 128-thread workgroups (see threads_of: 3.6-5 %
+// faster than four items with 256). The multi-tensor launch picks by the items of the whole
 // call.
 #ifndef MX_LARGE_ITEMS
 #define MX_LARGE_ITEMS (int64_t(3) << 23)
@@ -631,7 +632,7 @@ constexpr int unroll_of(bool bf16, int mode, int kind, bool large = false) {
   if (bf16 && large) {
     if (kind == kKindFakequant) return 1;
     if (kind == kKindDequantize) return 2;
-    return mode == MX_SCALE_OAS_NF ? kU<true> : mode == MX_SCALE_OAS ? 2 : 1;
+    return mode == MX_SCALE_OAS_NF || mode == MX_SCALE_OAS ? 2 : 1;
   }
   if (kind == kKindFakequant) return 2;
   if (!bf16) return kU<false>;
@@ -645,13 +646,15 @@ constexpr int unroll_of(bool bf16, int mode, int kind, bool large = false) {
 // element Llama-3.2-3B weight set against 256 threads: OAS quantize with
 // 128 4-6 % faster (64: up to 3 % slower, 512: 3 % slower), dequantize with
 // 64 2.4 % faster and fake-quant with 64 faster in every mode (OCP 1.6-1.8 %,
-// OAS 4 %, OAS_BITS 1.7 %, OAS_NF 5 %; 128 and 512 slower or equal), while
-// quantize OCP, OAS_BITS and OAS_NF keep 256 (64 and 128: 2-5 % slower). A
+// OAS 4 %, OAS_BITS 1.7 %, OAS_NF 5 %; 128 and 512 slower or equal), OAS_NF
+// quantize with 128 threads and two items 3.6-5 % faster than 256 and four,
+// while quantize OCP and OAS_BITS keep 256 with one item (64 and 128: 2-5 %
+// slower; two or four items per thread 6-13 % slower). A
 // plain copy of the same buffer ran 3.4 % faster with 64 than with 256.
 constexpr int threads_of(bool bf16, int mode, int kind, bool large = false) {
   if (!bf16 || !large) return kThreads;
   if (kind == kKindFakequant || kind == kKindDequantize) return 64;
-  if (kind == kKindQuantize && mode == MX_SCALE_OAS) return 128;
+  if (kind == kKindQuantize && (mode == MX_SCALE_OAS || mode == MX_SCALE_OAS_NF)) return 128;
   return kThreads;
 }
 

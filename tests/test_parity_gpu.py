@@ -325,6 +325,30 @@ def test_bf16_8192x4096_student_t_fakequant_full():
         assert_same_bits(c, wc, f"student-t codes {mode}")
 
 
+def test_large_tensor_tiling_every_mode():
+    """One bf16 tensor just at the multi-GB tiling (2^24 * 12 items = 2.0e8
+    elements: one item per thread for quantize OCP / OAS_BITS and
+    fake-quant, two for OAS / OAS_NF quantize and dequantize, 64- or 128-
+    thread workgroups where chosen): every mode's codes, scales and
+    fake-quant output, and the dequantized tensor, whole against the oracle."""
+    x = workloads.bf16_laplace_sparse_outliers(8, shape=(49152, 4096))
+    assert x.numel() // 8 == 3 << 23
+    xh = host_view(x)
+    xd = x.cuda()
+    for mode in MODES:
+        say(f"large tiling {mode} {tuple(x.shape)}")
+        c, s = mx.quantize(xd, mode)
+        wc, ws = oracle.quantize(xh, mode, threads=THREADS)
+        assert_same_bits(s, ws, f"large scales {mode}")
+        assert_same_bits(c, wc, f"large codes {mode}")
+        if mode == "ocp":
+            assert_same_bits(mx.dequantize(c, s, torch.bfloat16),
+                             oracle.dequantize(wc, ws, "bf16", threads=THREADS), "large dequant")
+        del c, s
+        assert_same_bits(mx.fakequant(xd, mode), oracle.fakequant(xh, mode, threads=THREADS),
+                         f"large fakequant {mode}")
+
+
 @pytest.mark.parametrize("rows", [16384, 16385])
 def test_oas_nf_layout_threshold(rows):
     # bf16 OAS_NF quantize changes lane layout above 2^23 items (2^26
