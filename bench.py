@@ -1210,7 +1210,7 @@ PROFILE_HOW = ("Each rocprofv3 command runs on its own, from a scratch working d
 
 
 def _kernel_short(name: str) -> str:
-    """'void mxk::k_quantize<true, 0, 1>(void const*, ...)' -> 'k_quantize<true, 0, 1>'."""
+    """'void mxk::k_quantize<true, 0, 1, 256>(void const*, ...)' -> 'k_quantize<true, 0, 1, 256>'."""
     m = re.search(r"\b(k_\w+(?:<[^()]*>)?)\(", name)
     return m.group(1) if m else name.split("(")[0]
 
