@@ -73,4 +73,8 @@ struct MxiTensor {
 };
 hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, int fakequant,
                             hipStream_t st);
+// Launch plan of a multi-tensor call (host only; see mx_kernels.hip). C
+// linkage, so the host tests can check it without a GPU.
+extern "C" int mxi_multi_plan(const int64_t *nitems, int count, int64_t tile, int max_per_launch, int *order,
+                   int *first, int64_t *gx);
 #endif

@@ -1924,38 +1924,62 @@ hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_sc
   return hipGetLastError();
 }
 
+// Launch plan of a multi-tensor call (host only): the non-empty tensors,
+// largest first (stable), in launches of at most max_per_launch tensors whose
+// tile counts are at least 7/8 of the launch's first one, so at most 1/8 of
+// a launch's workgroups are idle. order[] receives the tensor indices in
+// launch order, first[l] the position in order[] where launch l starts
+// (first[L] = the number of non-empty tensors), gx[l] the tiles of launch
+// l's first tensor (its grid's x size); each array holds count + 1 entries.
+// Returns the number of launches L, or -1 if a tensor has more tiles than
+// one grid dimension takes (nothing is then launched).
+int mxi_multi_plan(const int64_t *nitems, int count, int64_t tile, int max_per_launch, int *order,
+                   int *first, int64_t *gx) {
+  int m = 0;
+  for (int i = 0; i < count; i++)
+    if (nitems[i] > 0) order[m++] = i;
+  std::stable_sort(order, order + m, [&](int p, int q) { return nitems[p] > nitems[q]; });
+  int launches = 0, i = 0;
+  while (i < m) {
+    const int64_t g = (nitems[order[i]] + tile - 1) / tile;
+    if (g > kGridLimit) return -1;
+    first[launches] = i;
+    gx[launches++] = g;
+    int n = 0;
+    for (; i < m && n < max_per_launch; i++, n++)
+      if (8 * ((nitems[order[i]] + tile - 1) / tile) < 7 * g) break;
+  }
+  first[launches] = m;
+  return launches;
+}
+
 hipError_t mxi_launch_multi(const MxiTensor *t, int count, int bf16, int mode, int fakequant,
                             hipStream_t st) {
   const int kind = fakequant ? kKindFakequant : kKindQuantize;
   // the large-tensor tiling when the call as a whole streams that much
   int64_t total = 0;
-  std::vector<int> order;
-  order.reserve(count);
+  std::vector<int64_t> items(count);
   for (int i = 0; i < count; i++) {
-    if (t[i].nitems <= 0) continue;
-    total += t[i].nitems;
-    order.push_back(i);
+    items[i] = t[i].nitems;
+    total += t[i].nitems > 0 ? t[i].nitems : 0;
   }
   const bool large = bf16 && total >= kLargeItems;
   const int nt = large ? threads_of(true, mode, kind, true) : threads_of(bf16, mode, kind);
   const int64_t tile = (int64_t)nt * (large ? unroll_of(true, mode, kind, true)
                                             : unroll_of(bf16, mode, kind));
-  // largest first; each launch takes up to MX_MULTI_MAX tensors of at least
-  // 7/8 of its first one's tiles, so at most 1/8 of its workgroups are idle
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int p, int q) { return t[p].nitems > t[q].nitems; });
-  size_t i = 0;
-  while (i < order.size()) {
-    const int64_t gx = (t[order[i]].nitems + tile - 1) / tile;
-    if (gx > kGridLimit) return hipErrorInvalidValue;
+  std::vector<int> order(count + 1), first(count + 1);
+  std::vector<int64_t> gx(count + 1);
+  const int launches = mxi_multi_plan(items.data(), count, tile, MX_MULTI_MAX, order.data(),
+                                      first.data(), gx.data());
+  if (launches < 0) return hipErrorInvalidValue;
+  for (int l = 0; l < launches; l++) {
     MultiArgs a;
-    int n = 0;
-    for (; i < order.size() && n < MX_MULTI_MAX; i++, n++) {
-      const MxiTensor &q = t[order[i]];
-      if (8 * ((q.nitems + tile - 1) / tile) < 7 * gx) break;
-      a.d[n] = {q.x, q.out, q.scales, q.nitems};
+    const int n = first[l + 1] - first[l];
+    for (int j = 0; j < n; j++) {
+      const MxiTensor &q = t[order[first[l] + j]];
+      a.d[j] = {q.x, q.out, q.scales, q.nitems};
     }
-    const dim3 g((unsigned)gx, (unsigned)n), b((unsigned)nt);
+    const dim3 g((unsigned)gx[l], (unsigned)n), b((unsigned)nt);
     if (bf16) {
       if (large) {
         if (fakequant) { MX_DISPATCH_MULTI(true, true, true, mode, g, b, st, a) }

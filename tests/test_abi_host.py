@@ -293,3 +293,61 @@ def test_multi_helpers_refuse_bad_lists(lib):
     with pytest.raises(ValueError):
         mx.fakequant_multi([], mode="nope")
     assert mx.quantize_multi([]) == [] and mx.fakequant_multi([]) == []
+
+
+def _plan(lib, nitems, tile, per_launch=60):
+    f = lib.mxi_multi_plan
+    f.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                  ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                  ctypes.POINTER(ctypes.c_int64)]
+    f.restype = ctypes.c_int
+    n = len(nitems)
+    items = (ctypes.c_int64 * max(1, n))(*nitems)
+    order, first = (ctypes.c_int * (n + 1))(), (ctypes.c_int * (n + 1))()
+    gx = (ctypes.c_int64 * (n + 1))()
+    launches = f(items, n, tile, per_launch, order, first, gx)
+    if launches < 0:
+        return None
+    return ([list(order[first[l]:first[l + 1]]) for l in range(launches)],
+            [gx[l] for l in range(launches)])
+
+
+def _check_plan(nitems, tile, per_launch, plan):
+    launches, gxs = plan
+    tiles = [-(-v // tile) for v in nitems]
+    seen = [i for group in launches for i in group]
+    # every non-empty tensor exactly once, empty ones never
+    assert sorted(seen) == [i for i, v in enumerate(nitems) if v > 0]
+    # largest first overall, ties in the caller's order (a stable sort)
+    assert seen == sorted(seen, key=lambda i: (-nitems[i], i))
+    for group, gx in zip(launches, gxs):
+        assert 1 <= len(group) <= per_launch
+        assert gx == tiles[group[0]]  # the grid covers the launch's largest tensor
+        # at most 1/8 of the launch's workgroups idle
+        assert all(8 * tiles[i] >= 7 * gx for i in group)
+    # a launch ends only at the cap or where the next tensor is too small for it
+    for group, gx, nxt in zip(launches, gxs, launches[1:]):
+        assert len(group) == per_launch or 8 * tiles[nxt[0]] < 7 * gx
+
+
+def test_multi_launch_plan(lib):
+    """The host plan of mx_quantize_multi / mx_fakequant_multi: launches of
+    similar-sized tensors (2-D grids, no per-workgroup lookup), on random
+    lists with empty, equal and widely different sizes, past 60 tensors."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    llama = [o * i // 8 for _ in range(28) for o, i in
+             ((3072, 3072), (1024, 3072), (1024, 3072), (3072, 3072), (8192, 3072), (8192, 3072),
+              (3072, 8192))]
+    plan = _plan(lib, llama, 256)
+    _check_plan(llama, 256, 60, plan)
+    assert [len(g) for g in plan[0]] == [60, 24, 56, 56]  # 84 large, 56 q/o, 56 k/v
+    cases = [[], [0, 0], [4], [5] * 130, list(rng.integers(0, 10 ** 6, 200)),
+             list(rng.choice([0, 12, 13, 14, 15, 16, 4096, 4095, 3585, 3584], 150)),
+             list(rng.integers(0, 3, 70))]
+    for nitems in cases:
+        for tile, per in ((256, 60), (512, 60), (1024, 7), (128, 1)):
+            plan = _plan(lib, [int(v) for v in nitems], tile, per)
+            _check_plan([int(v) for v in nitems], tile, per, plan)
+    # a tensor with more tiles than one grid dimension takes: refused whole
+    assert _plan(lib, [2 ** 31 * 256 + 256, 10], 256) is None
