@@ -1056,13 +1056,25 @@ def suite(args, dev):
     def multi(_):
         ok(mx.mx_quantize_multi(descs, len(mats), mx.MX_BF16, mx.MX_SCALE_OCP, sh))
 
+    # QAT's weight pass: every weight fake-quantized, into its own output
+    ya, yb = torch.empty_like(a), torch.empty_like(b)
+    fdescs = (mx.MxTensor * len(mats))()
+    for i, (t, c, s_, r0, rows, k) in enumerate(mats):
+        y = ya if t is a else yb
+        fdescs[i] = mx.MxTensor(t[r0].data_ptr(), y[r0].data_ptr(), None, None, rows, k)
+
+    def multi_fq(_):
+        ok(mx.mx_fakequant_multi(fdescs, len(mats), mx.MX_BF16, mx.MX_SCALE_OCP, sh))
+
     report(WL, "quantize_ocp (196 per-matrix launches)", bytes_q,
            _launch_stats(per_matrix, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     report(WL, "quantize_ocp (196 matrices, one multi-tensor call)", bytes_q,
            _launch_stats(multi, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     report(WL, "quantize_ocp (2 launches grouped by K)", bytes_q,
            _launch_stats(grouped, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
-    del a, b, ca, sa, cb, sb, mats
+    report(WL, "fakequant_ocp (196 matrices, one multi-tensor call)", 4.0 * n,
+           _launch_stats(multi_fq, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    del a, b, ca, sa, cb, sb, mats, ya, yb
     torch.cuda.empty_cache()
     # the same 196 matrices end to end in one buffer: one launch (the step's form)
     arena, _ = workloads.llama32_3b_arena(dev)
@@ -1426,10 +1438,14 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
         else:
             key = (f"unattributed (grid {grid})", k, None)
         groups.setdefault(key, []).append(dur)
-    # the OCP quantize launches of the multi-tensor call (bf16, not fake-quant)
-    multi_key = next((key for key in groups
-                      if key[0] == "MULTI" and key[1].startswith("k_multi<true, 0, false")), None)
-    multi = groups.pop(multi_key) if multi_key else None
+    # the OCP quantize and fake-quant launches of the multi-tensor calls (bf16)
+    multis = []
+    for fq, bpe, what in ((False, 2.53125, "one `mx_quantize_multi` call"),
+                          (True, 4.0, "one `mx_fakequant_multi` call")):
+        key = next((key for key in groups if key[0] == "MULTI" and
+                    key[1].startswith(f"k_multi<true, 0, {'true' if fq else 'false'}")), None)
+        if key:
+            multis.append((key[1], groups.pop(key), bpe, what))
     out = ["# Kernel trace: the other workloads (`bench.py --suite`)\n", PROFILE_HOW + "\n",
            "```\n" + PROFILE_CMDS["suite"] + "\n```\n", code,
            "Durations are the GPU's own per-dispatch times from the trace (under the profiler the "
@@ -1449,11 +1465,11 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
         out.append(f"| {wl} | `{k}` | {len(v)} | {avg:.2f} | {min(v):.2f} | {max(v):.2f} | "
                    f"{int(b) if b else '-'} | {f'{b / avg / 1e3:.0f}' if b else '-'} | "
                    f"{f'{b / avg / 1e3 / HBM_PEAK_GBS * 100:.1f}' if b else '-'} |")
-    if multi:
+    for kname, multi, bpe, what in multis:
         per_pass = sum(multi) / passes
-        b = (l3072 + l8192) * 2.53125
-        out.append(f"| Llama-3.2-3B, the 196 weights as separate tensors: one `mx_quantize_multi` "
-                   f"call per pass ({len(multi) // passes} launches) | `{multi_key[1]}` | "
+        b = (l3072 + l8192) * bpe
+        out.append(f"| Llama-3.2-3B, the 196 weights as separate tensors: {what} "
+                   f"per pass ({len(multi) // passes} launches) | `{kname}` | "
                    f"{len(multi)} | {per_pass:.2f} per pass | {min(multi):.2f} | {max(multi):.2f} "
                    f"| {int(b)} | {b / per_pass / 1e3:.0f} | "
                    f"{b / per_pass / 1e3 / HBM_PEAK_GBS * 100:.1f} |")
