@@ -112,8 +112,9 @@ KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0, U>", "quantize_oas": "k_quanti
 # kernels with items-per-thread as their last template argument (or, for
 # NT_KERNELS, U then the threads per workgroup NT), and one tile (NT threads
 # x U items x 8 elements; NT = 256 where not given) per workgroup at these sizes
-U_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize", "k_block_mse", "k_quantize_pair")
-NT_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize")
+NT_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize", "k_quantize8", "k_dequantize8",
+              "k_fakequant8")
+U_KERNELS = NT_KERNELS + ("k_block_mse", "k_quantize_pair")
 ITEM_ELEMS = {"k_quantize_pair": 16}  # elements per item where not 8 (two lanes per block)
 FUSED_ITEMS = 2  # items per thread of k_quantize_fused
 PROFILE_STEM = {"step": "mx_llama32_3b_linears",
@@ -221,8 +222,8 @@ BESIDE_KERNELS = {
     "fakequant_oas_nf": ["k_fakequant<true, 3, U>"],
     "quantize_oas_bits": ["k_quantize<true, 2, U>"],
     "quantize_oas_nf": [("k_quantize_pair<3, U>", "k_quantize<true, 3, U>")],
-    "quantize_mxfp8": ["k_quantize8<true>"], "dequantize_mxfp8_bf16": ["k_dequantize8<true>"],
-    "fakequant_mxfp8": ["k_fakequant8<true>"],
+    "quantize_mxfp8": ["k_quantize8<true, U>"], "dequantize_mxfp8_bf16": ["k_dequantize8<true, U>"],
+    "fakequant_mxfp8": ["k_fakequant8<true, U>"],
     "quantize_nvfp4": ["k_absmax_partials<true>", "k_quantize_nv<true, false>"],
     "dequantize_nvfp4_bf16": ["k_dequantize_nv<true>"],
     "fakequant_nvfp4": ["k_absmax_partials<true>", "k_quantize_nv<true, true>"],
@@ -1110,6 +1111,34 @@ def suite(args, dev):
 
     report(WM, "quantize_ocp (w13 + w2)", (2 + 0.5 + 1 / 32) * n,
            _launch_stats(qm, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    # the same experts in MXFP8 (E4M3, the online path of the vLLM page):
+    # quantize, dequantize -> bf16, fake-quant
+    c8 = [torch.empty(w.numel(), dtype=torch.uint8, device=dev) for w in (w13, w2)]
+
+    def q8(_):
+        for (w, rows, k), c, s_ in zip(shapes, c8, ss):
+            ok(mx.mx_quantize_mxfp8(w.data_ptr(), mx.MX_BF16, rows, k, c.data_ptr(),
+                                    s_.data_ptr(), sh))
+
+    def dq8(_):
+        for (w, rows, k), c, s_, y in zip(shapes, c8, ss, ys):
+            ok(mx.mx_dequantize_mxfp8(c.data_ptr(), s_.data_ptr(), rows, k, mx.MX_BF16,
+                                      y.data_ptr(), sh))
+
+    def fq8(_):
+        for (w, rows, k), y in zip(shapes, ys):
+            ok(mx.mx_fakequant_mxfp8(w.data_ptr(), mx.MX_BF16, rows, k, y.data_ptr(), sh))
+
+    report(WM, "quantize_mxfp8 (w13 + w2)", (2 + 1 + 1 / 32) * n,
+           _launch_stats(q8, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    report(WM, "dequantize_mxfp8_bf16 (w13 + w2)", (1 + 1 / 32 + 2) * n,
+           _launch_stats(dq8, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    report(WM, "fakequant_mxfp8 (w13 + w2)", 4.0 * n,
+           _launch_stats(fq8, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    del c8
+    # MXFP4 dequantize of the codes quantized above (its launches end the
+    # timed part of the suite's profile)
+    qm(0)
     report(WM, "dequantize_bf16 (w13 + w2)", (0.5 + 1 / 32 + 2) * n,
            _launch_stats(dqm, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     del w13, w2, cs, ss, ys
@@ -1154,9 +1183,9 @@ KERNEL_BYTES_PER_ELEM = {
     "k_fakequant<true, 1, U>": EXTRA_BYTES_PER_ELEM["fakequant_oas"],
     "k_fakequant<true, 3, U>": EXTRA_BYTES_PER_ELEM["fakequant_oas_nf"],
     "k_block_mse<true, true, U>": BYTES_PER_ELEM["block_mse"],
-    "k_quantize8<true>": EXTRA_BYTES_PER_ELEM["quantize_mxfp8"],
-    "k_dequantize8<true>": EXTRA_BYTES_PER_ELEM["dequantize_mxfp8_bf16"],
-    "k_fakequant8<true>": EXTRA_BYTES_PER_ELEM["fakequant_mxfp8"],
+    "k_quantize8<true, U>": EXTRA_BYTES_PER_ELEM["quantize_mxfp8"],
+    "k_dequantize8<true, U>": EXTRA_BYTES_PER_ELEM["dequantize_mxfp8_bf16"],
+    "k_fakequant8<true, U>": EXTRA_BYTES_PER_ELEM["fakequant_mxfp8"],
     "k_absmax_partials<true>": 2.0,
     "k_quantize_nv<true, false>": EXTRA_BYTES_PER_ELEM["quantize_nvfp4"] - 2.0,
     "k_quantize_nv<true, true>": EXTRA_BYTES_PER_ELEM["fakequant_nvfp4"] - 2.0,
@@ -1400,6 +1429,10 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
             return n * (4.65625 if f32 else 2.65625)
         if kernel.startswith("k_quantize_fused<"):
             return n * (8.65625 if f32 else 4.65625)
+        if kernel.startswith(("k_quantize8<", "k_dequantize8<")):
+            return n * (5.03125 if f32 else 3.03125)
+        if kernel.startswith("k_fakequant8<"):
+            return n * (8.0 if f32 else 4.0)
         return None
 
     # the timed part ends with the MoE dequantize launches; the QSNR pass

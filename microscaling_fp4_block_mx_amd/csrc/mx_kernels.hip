@@ -1131,15 +1131,14 @@ __device__ __forceinline__ void decode8_item(u32x2 c, uint32_t s, uint32_t (&y)[
 template <bool BF16>
 constexpr int kU8 = BF16 ? 2 : kU<false>;
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_quantize8(const void *__restrict__ x,
-                                                        u32x2 *__restrict__ codes,
-                                                        uint8_t *__restrict__ scales,
-                                                        int64_t nitems) {
-  Item<BF16> xv[kU8<BF16>];
-  u32x2 cw[kU8<BF16>];
-  uint32_t sv[kU8<BF16>];
-  tile_loop<kU8<BF16>>(
+template <bool BF16, int U, int NT>
+__global__ __launch_bounds__(NT) void k_quantize8(const void *__restrict__ x,
+                                                  u32x2 *__restrict__ codes,
+                                                  uint8_t *__restrict__ scales, int64_t nitems) {
+  Item<BF16> xv[U];
+  u32x2 cw[U];
+  uint32_t sv[U];
+  tile_loop<U, false, NT>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) { sv[u] = quantize8_item<BF16>(xv[u], cw[u]); },
       [&](int u, int64_t it) {
@@ -1148,14 +1147,14 @@ __global__ __launch_bounds__(kThreads) void k_quantize8(const void *__restrict__
       });
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_dequantize8(const u32x2 *__restrict__ codes,
-                                                          const uint8_t *__restrict__ scales,
-                                                          void *__restrict__ y, int64_t nitems) {
-  u32x2 cw[kU<BF16>];
-  uint32_t sb[kU<BF16>];
-  uint32_t out[kU<BF16>][BF16 ? 4 : 8];
-  tile_loop<kU<BF16>>(
+template <bool BF16, int U, int NT>
+__global__ __launch_bounds__(NT) void k_dequantize8(const u32x2 *__restrict__ codes,
+                                                    const uint8_t *__restrict__ scales,
+                                                    void *__restrict__ y, int64_t nitems) {
+  u32x2 cw[U];
+  uint32_t sb[U];
+  uint32_t out[U][BF16 ? 4 : 8];
+  tile_loop<U, false, NT>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
@@ -1165,12 +1164,11 @@ __global__ __launch_bounds__(kThreads) void k_dequantize8(const u32x2 *__restric
       [&](int u, int64_t it) { store_item<BF16>(y, it, out[u]); });
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_fakequant8(const void *x, void *y, int64_t nitems) {
-  constexpr int U = unroll_of(BF16, 0, kKindFakequant);  // as MXFP4 fake-quant (3 % faster)
+template <bool BF16, int U, int NT>
+__global__ __launch_bounds__(NT) void k_fakequant8(const void *x, void *y, int64_t nitems) {
   Item<BF16> xv[U];
   uint32_t out[U][BF16 ? 4 : 8];
-  tile_loop<U>(
+  tile_loop<U, false, NT>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) {
         u32x2 c;
@@ -1813,35 +1811,75 @@ hipError_t mxi_scratch_address(int dev, double **out) {
   return hipSuccess;
 }
 
+// Tiling of the MXFP8 kernels: the grid-capped small-tensor tiling (fake-quant
+// as MXFP4 fake-quant, 3 % faster) below kLargeItems items, and on multi-GB
+// bf16 tensors one tile per workgroup, no cap, 64-thread workgroups: on the
+// 1.6e9-element MoE w13 experts quantize and fake-quant with one item per
+// thread ran 12.6 % faster than the small-tensor tiling, dequantize with two
+// 7.4 % faster (the XCD map of MXFP4 dequantize made it 3 % slower here; one
+// item, or 256 threads, 2-6 % slower).
+struct Tiling8 {
+  int u, nt;
+  int64_t cap;
+};
+constexpr Tiling8 tiling8(bool bf16, int kind, bool large) {
+  if (bf16 && large) {
+    if (kind == kKindQuantize) return {1, 64, kGridLimit};
+    if (kind == kKindDequantize) return {2, 64, kGridLimit};
+    return {1, 64, kGridLimit};
+  }
+  if (kind == kKindQuantize) return {bf16 ? kU8<true> : kU8<false>, kThreads, MX_GRID_CAP};
+  if (kind == kKindDequantize) return {bf16 ? kU<true> : kU<false>, kThreads, MX_GRID_CAP};
+  return {unroll_of(bf16, 0, kKindFakequant), kThreads, MX_GRID_CAP};
+}
+
+template <bool BF16, bool LARGE>
+static void launch_quantize8_t(const void *x, int64_t nitems, u32x2 *c, uint8_t *scales,
+                               hipStream_t st) {
+  constexpr Tiling8 t = tiling8(BF16, kKindQuantize, LARGE);
+  hipLaunchKernelGGL((k_quantize8<BF16, t.u, t.nt>), dim3(grid_for(nitems, t.cap, t.u, t.nt)),
+                     dim3(t.nt), 0, st, x, c, scales, nitems);
+}
+
 hipError_t mxi_launch_quantize8(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                 uint8_t *scales, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU8<true> : kU8<false>)), b(kThreads);
   u32x2 *c = reinterpret_cast<u32x2 *>(codes);
-  if (bf16)
-    hipLaunchKernelGGL((k_quantize8<true>), g, b, 0, st, x, c, scales, nitems);
-  else
-    hipLaunchKernelGGL((k_quantize8<false>), g, b, 0, st, x, c, scales, nitems);
+  if (bf16 && nitems >= kLargeItems) launch_quantize8_t<true, true>(x, nitems, c, scales, st);
+  else if (bf16) launch_quantize8_t<true, false>(x, nitems, c, scales, st);
+  else launch_quantize8_t<false, false>(x, nitems, c, scales, st);
   return hipGetLastError();
+}
+
+template <bool BF16, bool LARGE>
+static void launch_dequantize8_t(const u32x2 *c, const uint8_t *scales, int64_t nitems, void *y,
+                                 hipStream_t st) {
+  constexpr Tiling8 t = tiling8(BF16, kKindDequantize, LARGE);
+  hipLaunchKernelGGL((k_dequantize8<BF16, t.u, t.nt>),
+                     dim3(grid_for(nitems, t.cap, t.u, t.nt)), dim3(t.nt), 0, st, c, scales, y,
+                     nitems);
 }
 
 hipError_t mxi_launch_dequantize8(const uint8_t *codes, const uint8_t *scales, int bf16,
                                   int64_t nitems, void *y, hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   const u32x2 *c = reinterpret_cast<const u32x2 *>(codes);
-  if (bf16)
-    hipLaunchKernelGGL((k_dequantize8<true>), g, b, 0, st, c, scales, y, nitems);
-  else
-    hipLaunchKernelGGL((k_dequantize8<false>), g, b, 0, st, c, scales, y, nitems);
+  if (bf16 && nitems >= kLargeItems) launch_dequantize8_t<true, true>(c, scales, nitems, y, st);
+  else if (bf16) launch_dequantize8_t<true, false>(c, scales, nitems, y, st);
+  else launch_dequantize8_t<false, false>(c, scales, nitems, y, st);
   return hipGetLastError();
+}
+
+template <bool BF16, bool LARGE>
+static void launch_fakequant8_t(const void *x, int64_t nitems, void *y, hipStream_t st) {
+  constexpr Tiling8 t = tiling8(BF16, kKindFakequant, LARGE);
+  hipLaunchKernelGGL((k_fakequant8<BF16, t.u, t.nt>), dim3(grid_for(nitems, t.cap, t.u, t.nt)),
+                     dim3(t.nt), 0, st, x, y, nitems);
 }
 
 hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *y,
                                  hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, unroll_of(bf16, 0, kKindFakequant))), b(kThreads);
-  if (bf16)
-    hipLaunchKernelGGL((k_fakequant8<true>), g, b, 0, st, x, y, nitems);
-  else
-    hipLaunchKernelGGL((k_fakequant8<false>), g, b, 0, st, x, y, nitems);
+  if (bf16 && nitems >= kLargeItems) launch_fakequant8_t<true, true>(x, nitems, y, st);
+  else if (bf16) launch_fakequant8_t<true, false>(x, nitems, y, st);
+  else launch_fakequant8_t<false, false>(x, nitems, y, st);
   return hipGetLastError();
 }
 

@@ -81,7 +81,8 @@ def test_kernel_names_and_families():
     assert bench.threads_per_group("k_fakequant<true, 0, 1, 64>") == 64
     assert bench.threads_per_group("k_block_mse<true, true, 2>") == 256
     assert bench.items_per_thread("k_quantize_fused<true, 0, true>") == bench.FUSED_ITEMS
-    assert bench.items_per_thread("k_quantize8<true>") is None
+    assert bench.items_per_thread("k_quantize8<true, 2, 256>") == 2
+    assert bench.items_per_thread("k_quantize_nv<true, false>") is None
     # the two-lanes-per-block kernel: 16 elements per item
     assert bench.kernel_family("k_quantize_pair<3, 1>") == "k_quantize_pair<3, U>"
     assert bench.tile_elems("k_quantize_pair<3, 1>", 8192) == 8192 * 4096
@@ -116,7 +117,7 @@ def test_beside_phase_attributes_by_grid():
     assert elems("k_quantize<true, 3, 4, 256>", 4096) == 8192 * 4096
     assert elems("k_fakequant<true, 0, 2, 256>", 8192) == 8192 * 4096
     assert elems("k_quantize_fused<true, 0, true>", 8192) == 8192 * 4096
-    assert elems("k_quantize8<true>", 4096) == 8192 * 4096
+    assert elems("k_quantize8<true, 2, 256>", 8192) == 8192 * 4096
 
 
 def test_kernel_hash_ignores_comments_only(tmp_path, monkeypatch):

@@ -330,7 +330,8 @@ def test_large_tensor_tiling_every_mode():
     elements: one item per thread for quantize OCP / OAS_BITS and
     fake-quant, two for OAS / OAS_NF quantize and dequantize, 64- or 128-
     thread workgroups where chosen): every mode's codes, scales and
-    fake-quant output, and the dequantized tensor, whole against the oracle."""
+    fake-quant output, and the dequantized tensor, whole against the oracle;
+    likewise MXFP8 quantize, dequantize and fake-quant."""
     x = workloads.bf16_laplace_sparse_outliers(8, shape=(49152, 4096))
     assert x.numel() // 8 == 3 << 23
     xh = host_view(x)
@@ -347,6 +348,17 @@ def test_large_tensor_tiling_every_mode():
         del c, s
         assert_same_bits(mx.fakequant(xd, mode), oracle.fakequant(xh, mode, threads=THREADS),
                          f"large fakequant {mode}")
+    # MXFP8 at its multi-GB tiling (one or two items per 64-thread workgroup)
+    say("large tiling mxfp8")
+    c, s = mx.quantize_mxfp8(xd)
+    wc, ws = oracle.quantize_mxfp8(xh, threads=THREADS)
+    assert_same_bits(s, ws, "large mxfp8 scales")
+    assert_same_bits(c, wc, "large mxfp8 codes")
+    assert_same_bits(mx.dequantize_mxfp8(c, s, torch.bfloat16),
+                     oracle.dequantize_mxfp8(wc, ws, "bf16", threads=THREADS), "large mxfp8 dequant")
+    del c, s
+    assert_same_bits(mx.fakequant_mxfp8(xd), oracle.fakequant_mxfp8(xh, threads=THREADS),
+                     "large mxfp8 fakequant")
 
 
 @pytest.mark.parametrize("rows", [16384, 16385])
