@@ -113,7 +113,7 @@ KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0, U>", "quantize_oas": "k_quanti
 # NT_KERNELS, U then the threads per workgroup NT), and one tile (NT threads
 # x U items x 8 elements; NT = 256 where not given) per workgroup at these sizes
 NT_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize", "k_quantize8", "k_dequantize8",
-              "k_fakequant8")
+              "k_fakequant8", "k_quantize_mbs", "k_dequantize_mbs")
 U_KERNELS = NT_KERNELS + ("k_block_mse", "k_quantize_pair")
 ITEM_ELEMS = {"k_quantize_pair": 16}  # elements per item where not 8 (two lanes per block)
 FUSED_ITEMS = 2  # items per thread of k_quantize_fused
@@ -227,8 +227,9 @@ BESIDE_KERNELS = {
     "quantize_nvfp4": ["k_absmax_partials<true>", "k_quantize_nv<true, false>"],
     "dequantize_nvfp4_bf16": ["k_dequantize_nv<true>"],
     "fakequant_nvfp4": ["k_absmax_partials<true>", "k_quantize_nv<true, true>"],
-    "quantize_mbs": ["k_quantize_mbs<true, false>"], "dequantize_mbs_bf16": ["k_dequantize_mbs<true>"],
-    "fakequant_mbs": ["k_quantize_mbs<true, true>"],
+    "quantize_mbs": ["k_quantize_mbs<true, false, U>"],
+    "dequantize_mbs_bf16": ["k_dequantize_mbs<true, U>"],
+    "fakequant_mbs": ["k_quantize_mbs<true, true, U>"],
     "quantize_fused": ["k_quantize_fused<true, 0, true>"],
     "reference_copy": ["k_ceiling_copy"],
     "quantize_ocp": ["k_quantize<true, 0, U>"], "quantize_oas": ["k_quantize<true, 1, U>"],
@@ -1136,6 +1137,31 @@ def suite(args, dev):
     report(WM, "fakequant_mxfp8 (w13 + w2)", 4.0 * n,
            _launch_stats(fq8, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     del c8
+    # and in MBS-Static (16-element sub-blocks, 8-bit macro mantissas per 128)
+    smb = [torch.empty(w.numel() // 16, dtype=torch.uint8, device=dev) for w in (w13, w2)]
+    mmb = [torch.empty(w.numel() // 128, dtype=torch.uint8, device=dev) for w in (w13, w2)]
+
+    def qmb(_):
+        for (w, rows, k), c, s_, m_ in zip(shapes, cs, smb, mmb):
+            ok(mx.mx_quantize_mbs(w.data_ptr(), mx.MX_BF16, rows, k, c.data_ptr(), s_.data_ptr(),
+                                  m_.data_ptr(), sh))
+
+    def dqmb(_):
+        for (w, rows, k), c, s_, m_, y in zip(shapes, cs, smb, mmb, ys):
+            ok(mx.mx_dequantize_mbs(c.data_ptr(), s_.data_ptr(), m_.data_ptr(), rows, k,
+                                    mx.MX_BF16, y.data_ptr(), sh))
+
+    def fqmb(_):
+        for (w, rows, k), y in zip(shapes, ys):
+            ok(mx.mx_fakequant_mbs(w.data_ptr(), mx.MX_BF16, rows, k, y.data_ptr(), sh))
+
+    report(WM, "quantize_mbs (w13 + w2)", (2 + 0.5 + 1 / 16 + 1 / 128) * n,
+           _launch_stats(qmb, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    report(WM, "dequantize_mbs_bf16 (w13 + w2)", (0.5 + 1 / 16 + 1 / 128 + 2) * n,
+           _launch_stats(dqmb, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    report(WM, "fakequant_mbs (w13 + w2)", 4.0 * n,
+           _launch_stats(fqmb, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    del smb, mmb
     # MXFP4 dequantize of the codes quantized above (its launches end the
     # timed part of the suite's profile)
     qm(0)
@@ -1190,9 +1216,9 @@ KERNEL_BYTES_PER_ELEM = {
     "k_quantize_nv<true, false>": EXTRA_BYTES_PER_ELEM["quantize_nvfp4"] - 2.0,
     "k_quantize_nv<true, true>": EXTRA_BYTES_PER_ELEM["fakequant_nvfp4"] - 2.0,
     "k_dequantize_nv<true>": EXTRA_BYTES_PER_ELEM["dequantize_nvfp4_bf16"],
-    "k_quantize_mbs<true, false>": EXTRA_BYTES_PER_ELEM["quantize_mbs"],
-    "k_quantize_mbs<true, true>": EXTRA_BYTES_PER_ELEM["fakequant_mbs"],
-    "k_dequantize_mbs<true>": EXTRA_BYTES_PER_ELEM["dequantize_mbs_bf16"],
+    "k_quantize_mbs<true, false, U>": EXTRA_BYTES_PER_ELEM["quantize_mbs"],
+    "k_quantize_mbs<true, true, U>": EXTRA_BYTES_PER_ELEM["fakequant_mbs"],
+    "k_dequantize_mbs<true, U>": EXTRA_BYTES_PER_ELEM["dequantize_mbs_bf16"],
     "k_quantize_fused<true, 0, true>": EXTRA_BYTES_PER_ELEM["quantize_fused"],
     "k_ceiling_quantize_shape": CEILING_BYTES_PER_ELEM["quantize_shape"],
     "k_ceiling_dequantize_shape": CEILING_BYTES_PER_ELEM["dequantize_shape"],
@@ -1431,8 +1457,10 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
             return n * (8.65625 if f32 else 4.65625)
         if kernel.startswith(("k_quantize8<", "k_dequantize8<")):
             return n * (5.03125 if f32 else 3.03125)
-        if kernel.startswith("k_fakequant8<"):
+        if kernel.startswith("k_fakequant8<") or kernel.startswith("k_quantize_mbs<true, true"):
             return n * (8.0 if f32 else 4.0)
+        if kernel.startswith(("k_quantize_mbs<", "k_dequantize_mbs<")):
+            return n * ((2.0 if f32 else 0.0) + 2 + 0.5 + 1 / 16 + 1 / 128)
         return None
 
     # the timed part ends with the MoE dequantize launches; the QSNR pass

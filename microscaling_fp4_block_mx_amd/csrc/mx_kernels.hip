@@ -1415,7 +1415,7 @@ __device__ __forceinline__ void mbs_decode_item(uint32_t c, uint32_t s, uint32_t
 // scheduler can overlap their long dependency chains; the rare cases (a
 // subnormal quotient, a NaN/Inf sub-block) are patched afterwards under a
 // branch that a wave without them skips.
-template <bool BF16, int U, bool FQ>
+template <bool BF16, int U, bool FQ, int NT>
 __device__ __forceinline__ void mbs_tile(const Item<BF16> (&xv)[U], const float *inv_tab,
                                          uint32_t *__restrict__ codes,
                                          uint8_t *__restrict__ sub_scales,
@@ -1475,7 +1475,7 @@ __device__ __forceinline__ void mbs_tile(const Item<BF16> (&xv)[U], const float 
 #pragma unroll
   for (int u = 0; u < U; u++) {
     if (__builtin_expect(s[u] == 255u, 0)) c[u] = sign_codes<BF16>(xv[u]);
-    const int64_t it = base + u * kThreads;
+    const int64_t it = base + u * NT;
     if (full || it < nitems) {  // whole rows of 16 lanes drop out together
       if constexpr (FQ) {
         uint32_t out[BF16 ? 4 : 8];
@@ -1492,51 +1492,47 @@ __device__ __forceinline__ void mbs_tile(const Item<BF16> (&xv)[U], const float 
 
 // FQ: fake-quant (y = dequantize(quantize(x)) in x's dtype; y may be x)
 // instead of writing codes and bytes.
-template <bool BF16, bool FQ>
-__global__ __launch_bounds__(kThreads) void k_quantize_mbs(const void *x,
-                                                           uint32_t *__restrict__ codes,
-                                                           uint8_t *__restrict__ sub_scales,
-                                                           uint8_t *__restrict__ macro_mant,
-                                                           void *y, int64_t nitems) {
+template <bool BF16, bool FQ, int U, int NT>
+__global__ __launch_bounds__(NT) void k_quantize_mbs(const void *x, uint32_t *__restrict__ codes,
+                                                     uint8_t *__restrict__ sub_scales,
+                                                     uint8_t *__restrict__ macro_mant, void *y,
+                                                     int64_t nitems) {
   // fl32(1 / f) for every macro mantissa m (f = 1 + m/256): IEEE division,
   // once per workgroup, so the per-item cost is one LDS read
-  static_assert(kThreads == 256, "one table entry per thread");
+  static_assert(256 % NT == 0, "whole table entries per thread");
   __shared__ float inv_tab[256];
-  inv_tab[threadIdx.x] = 1.0f / (1.0f + (float)threadIdx.x * (1.0f / 256.0f));
+  for (int e = threadIdx.x; e < 256; e += NT) inv_tab[e] = 1.0f / (1.0f + (float)e * (1.0f / 256.0f));
   __syncthreads();
-  constexpr int U = kU<BF16>;
-  const int64_t tile = (int64_t)kThreads * U;
+  const int64_t tile = (int64_t)NT * U;
   const int64_t nfull = nitems / tile;
   Item<BF16> xv[U];
   int64_t t = blockIdx.x;
   for (; t < nfull; t += gridDim.x) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < U; u++) load_item<BF16>(x, base + u * kThreads, xv[u]);
+    for (int u = 0; u < U; u++) load_item<BF16>(x, base + u * NT, xv[u]);
     __builtin_amdgcn_sched_barrier(0);
-    mbs_tile<BF16, U, FQ>(xv, inv_tab, codes, sub_scales, macro_mant, y, base, nitems, true);
+    mbs_tile<BF16, U, FQ, NT>(xv, inv_tab, codes, sub_scales, macro_mant, y, base, nitems, true);
   }
   if (t == nfull && nfull * tile < nitems) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      if (base + u * kThreads < nitems) load_item<BF16>(x, base + u * kThreads, xv[u]);
+      if (base + u * NT < nitems) load_item<BF16>(x, base + u * NT, xv[u]);
       else xv[u] = Item<BF16>{};  // zeros: finite, so lanes past the end stay quiet
     }
-    mbs_tile<BF16, U, FQ>(xv, inv_tab, codes, sub_scales, macro_mant, y, base, nitems, false);
+    mbs_tile<BF16, U, FQ, NT>(xv, inv_tab, codes, sub_scales, macro_mant, y, base, nitems, false);
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_dequantize_mbs(const uint32_t *__restrict__ codes,
-                                                             const uint8_t *__restrict__ sub_scales,
-                                                             const uint8_t *__restrict__ macro_mant,
-                                                             void *__restrict__ y, int64_t nitems) {
-  // items per thread as MXFP4 dequantize (two for bf16: 2.5 % faster here)
-  constexpr int U = unroll_of(BF16, 0, kKindDequantize);
+template <bool BF16, int U, int NT>
+__global__ __launch_bounds__(NT) void k_dequantize_mbs(const uint32_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ sub_scales,
+                                                       const uint8_t *__restrict__ macro_mant,
+                                                       void *__restrict__ y, int64_t nitems) {
   uint32_t cw[U], sb[U], mb[U];
   uint32_t out[U][BF16 ? 4 : 8];
-  tile_loop<U>(
+  tile_loop<U, false, NT>(
       nitems,
       [&](int u, int64_t it) {
         cw[u] = ld<false>(codes + it);
@@ -1925,40 +1921,75 @@ hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_s
   return hipGetLastError();
 }
 
+// Tiling of the MBS-Static kernels, as for MXFP8: grid-capped below
+// kLargeItems items (quantize four items per thread, dequantize two as MXFP4
+// dequantize: 2.5 % faster), and on multi-GB bf16 tensors one tile per
+// workgroup with no cap: quantize and fake-quant one item per 256-thread
+// workgroup (on the 1.6e9-element MoE w13 experts 3 % and 10 % faster than
+// the small-tensor tiling; 64 threads 7-17 % slower, 128 x 2 within 1 %),
+// dequantize two items per 64 threads (3 % faster; 128 threads equal).
+struct TilingMbs {
+  int u, nt;
+  int64_t cap;
+};
+constexpr TilingMbs tiling_mbs(bool bf16, int kind, bool large) {
+  if (bf16 && large) {
+    if (kind == kKindDequantize) return {2, 64, kGridLimit};
+    return {1, 256, kGridLimit};
+  }
+  if (kind == kKindDequantize) return {unroll_of(bf16, 0, kKindDequantize), kThreads, MX_GRID_CAP};
+  return {bf16 ? kU<true> : kU<false>, kThreads, MX_GRID_CAP};
+}
+
+template <bool BF16, bool FQ, bool LARGE>
+static void launch_quantize_mbs_t(const void *x, int64_t nitems, uint32_t *c, uint8_t *sub_scales,
+                                  uint8_t *macro_mant, void *y, hipStream_t st) {
+  constexpr TilingMbs t = tiling_mbs(BF16, kKindQuantize, LARGE);
+  hipLaunchKernelGGL((k_quantize_mbs<BF16, FQ, t.u, t.nt>),
+                     dim3(grid_for(nitems, t.cap, t.u, t.nt)), dim3(t.nt), 0, st, x, c,
+                     sub_scales, macro_mant, y, nitems);
+}
+
 hipError_t mxi_launch_quantize_mbs(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                    uint8_t *sub_scales, uint8_t *macro_mant, void *y,
                                    hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, bf16 ? kU<true> : kU<false>)), b(kThreads);
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
+  const bool large = bf16 && nitems >= kLargeItems;
   if (bf16) {
-    if (y)
-      hipLaunchKernelGGL((k_quantize_mbs<true, true>), g, b, 0, st, x, c, sub_scales, macro_mant,
-                         y, nitems);
-    else
-      hipLaunchKernelGGL((k_quantize_mbs<true, false>), g, b, 0, st, x, c, sub_scales,
-                         macro_mant, y, nitems);
+    if (large) {
+      if (y) launch_quantize_mbs_t<true, true, true>(x, nitems, c, sub_scales, macro_mant, y, st);
+      else launch_quantize_mbs_t<true, false, true>(x, nitems, c, sub_scales, macro_mant, y, st);
+    } else {
+      if (y) launch_quantize_mbs_t<true, true, false>(x, nitems, c, sub_scales, macro_mant, y, st);
+      else launch_quantize_mbs_t<true, false, false>(x, nitems, c, sub_scales, macro_mant, y, st);
+    }
   } else {
-    if (y)
-      hipLaunchKernelGGL((k_quantize_mbs<false, true>), g, b, 0, st, x, c, sub_scales,
-                         macro_mant, y, nitems);
-    else
-      hipLaunchKernelGGL((k_quantize_mbs<false, false>), g, b, 0, st, x, c, sub_scales,
-                         macro_mant, y, nitems);
+    if (y) launch_quantize_mbs_t<false, true, false>(x, nitems, c, sub_scales, macro_mant, y, st);
+    else launch_quantize_mbs_t<false, false, false>(x, nitems, c, sub_scales, macro_mant, y, st);
   }
   return hipGetLastError();
+}
+
+template <bool BF16, bool LARGE>
+static void launch_dequantize_mbs_t(const uint32_t *c, const uint8_t *sub_scales,
+                                    const uint8_t *macro_mant, int64_t nitems, void *y,
+                                    hipStream_t st) {
+  constexpr TilingMbs t = tiling_mbs(BF16, kKindDequantize, LARGE);
+  hipLaunchKernelGGL((k_dequantize_mbs<BF16, t.u, t.nt>),
+                     dim3(grid_for(nitems, t.cap, t.u, t.nt)), dim3(t.nt), 0, st, c, sub_scales,
+                     macro_mant, y, nitems);
 }
 
 hipError_t mxi_launch_dequantize_mbs(const uint8_t *codes, const uint8_t *sub_scales,
                                      const uint8_t *macro_mant, int bf16, int64_t nitems, void *y,
                                      hipStream_t st) {
-  const dim3 g(grid_for(nitems, MX_GRID_CAP, unroll_of(bf16, 0, kKindDequantize))),
-      b(kThreads);
   const uint32_t *c = reinterpret_cast<const uint32_t *>(codes);
-  if (bf16)
-    hipLaunchKernelGGL((k_dequantize_mbs<true>), g, b, 0, st, c, sub_scales, macro_mant, y, nitems);
+  if (bf16 && nitems >= kLargeItems)
+    launch_dequantize_mbs_t<true, true>(c, sub_scales, macro_mant, nitems, y, st);
+  else if (bf16)
+    launch_dequantize_mbs_t<true, false>(c, sub_scales, macro_mant, nitems, y, st);
   else
-    hipLaunchKernelGGL((k_dequantize_mbs<false>), g, b, 0, st, c, sub_scales, macro_mant, y,
-                       nitems);
+    launch_dequantize_mbs_t<false, false>(c, sub_scales, macro_mant, nitems, y, st);
   return hipGetLastError();
 }
 

@@ -331,7 +331,7 @@ def test_large_tensor_tiling_every_mode():
     fake-quant, two for OAS / OAS_NF quantize and dequantize, 64- or 128-
     thread workgroups where chosen): every mode's codes, scales and
     fake-quant output, and the dequantized tensor, whole against the oracle;
-    likewise MXFP8 quantize, dequantize and fake-quant."""
+    likewise MXFP8 and MBS-Static quantize, dequantize and fake-quant."""
     x = workloads.bf16_laplace_sparse_outliers(8, shape=(49152, 4096))
     assert x.numel() // 8 == 3 << 23
     xh = host_view(x)
@@ -359,6 +359,18 @@ def test_large_tensor_tiling_every_mode():
     del c, s
     assert_same_bits(mx.fakequant_mxfp8(xd), oracle.fakequant_mxfp8(xh, threads=THREADS),
                      "large mxfp8 fakequant")
+    # and MBS-Static (one item per 256 threads; dequantize two per 64)
+    say("large tiling mbs-static")
+    c, s, m = mx.quantize_mbs(xd)
+    wc, ws, wm = oracle.quantize_mbs(xh)
+    assert_same_bits(m, wm, "large mbs macro bytes")
+    assert_same_bits(s, ws, "large mbs sub-scales")
+    assert_same_bits(c, wc, "large mbs codes")
+    assert_same_bits(mx.dequantize_mbs(c, s, m, torch.bfloat16),
+                     oracle.dequantize_mbs(wc, ws, wm, "bf16"), "large mbs dequant")
+    del c, s, m
+    assert_same_bits(mx.fakequant_mbs(xd), oracle.dequantize_mbs(wc, ws, wm, "bf16"),
+                     "large mbs fakequant")
 
 
 @pytest.mark.parametrize("rows", [16384, 16385])
