@@ -144,7 +144,10 @@ __device__ __forceinline__ double row_sum_f64(double p) {
 // per-instruction footprint is strided (32-byte lane pitch): fp32 loads,
 // and the small code/scale accesses, stay on the default cache policy,
 // which measured faster for them; fp32 stores are regrouped through LDS into
-// contiguous non-temporal stores (store_item).
+// contiguous non-temporal stores (store_item). The per-block errors (one
+// 4-byte store per quad) are stored non-temporally too: on the 2.8e9-
+// element weight set block MSE with its tensor sums took 1197 us against
+// 1226-1240 us on the default policy.
 template <bool NT, typename T>
 __device__ __forceinline__ T ld(const T *p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -890,7 +893,7 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(const void *__restrict__
       },
       [&](int u, int64_t) { bm[u] = mse_item<BF16, SUMS>(xv[u], cw[u], sb[u], mine, mine_sq); },
       [&](int u, int64_t it) {
-        if (block_mse && (threadIdx.x & 3) == 0) st<false>(block_mse + (it >> 2), bm[u]);
+        if (block_mse && (threadIdx.x & 3) == 0) st<true>(block_mse + (it >> 2), bm[u]);
       });
   if constexpr (SUMS) write_partials(mine, mine_sq, partial);
 }
@@ -928,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_fused(const void *__restr
         st<false>(codes + it, cw[u]);
         if ((threadIdx.x & 3) == 0) st<false>(scales + (it >> 2), (uint8_t)sv[u]);
         if (y) store_item<BF16>(y, it, out[u]);
-        if (block_mse && (threadIdx.x & 3) == 0) st<false>(block_mse + (it >> 2), bm[u]);
+        if (block_mse && (threadIdx.x & 3) == 0) st<true>(block_mse + (it >> 2), bm[u]);
       });
   if constexpr (SUMS) write_partials(mine, mine_sq, partial);
 }
