@@ -598,6 +598,58 @@ __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
   tile_loop<U>(nitems, load, use, [](int, int64_t) {});
 }
 
+// The same walk with a per-workgroup prologue (tables, reductions, a
+// barrier) that runs once the workgroup's first tile's loads are issued, so
+// that its latency overlaps theirs instead of delaying them; every thread
+// runs it. Later tiles load at the top of their iteration as in tile_loop.
+template <int U, typename Prologue, typename Load, typename Compute, typename Store>
+__device__ __forceinline__ void tile_loop_pro(int64_t nitems, Prologue prologue, Load load,
+                                              Compute compute, Store store) {
+  const int64_t tile = (int64_t)kThreads * U;
+  const int64_t nfull = nitems / tile;
+  const bool partial = nfull * tile < nitems;
+  const int64_t first = blockIdx.x;
+  int64_t t = first;
+  if (t < nfull) {
+    const int64_t base = t * tile + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; u++) load(u, base + u * kThreads);
+  } else if (t == nfull && partial) {
+    const int64_t base = t * tile + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (base + u * kThreads < nitems) load(u, base + u * kThreads);
+  }
+  prologue();
+  for (; t < nfull; t += gridDim.x) {
+    const int64_t base = t * tile + threadIdx.x;
+    if (t != first) {
+#pragma unroll
+      for (int u = 0; u < U; u++) load(u, base + u * kThreads);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
+#pragma unroll
+    for (int u = 0; u < U; u++) compute(u, base + u * kThreads);
+    __builtin_amdgcn_sched_barrier(0);  // every item's arithmetic ahead of the stores
+#pragma unroll
+    for (int u = 0; u < U; u++) store(u, base + u * kThreads);
+  }
+  if (t == nfull && partial) {
+    const int64_t base = t * tile + threadIdx.x;
+    if (t != first) {
+#pragma unroll
+      for (int u = 0; u < U; u++)
+        if (base + u * kThreads < nitems) load(u, base + u * kThreads);
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++)  // whole lane pairs and quads drop out together
+      if (base + u * kThreads < nitems) compute(u, base + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (base + u * kThreads < nitems) store(u, base + u * kThreads);
+  }
+}
+
 // Items per thread per tile for the streaming kernels: kUnroll bf16 items,
 // a quarter as many fp32 items (an fp32 item is two 16-byte accesses). One
 // fp32 item per thread doubles the workgroups in flight, which measured
@@ -1276,35 +1328,40 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *x,
   // every workgroup reduces the first pass's maxima (max is order-free and
   // idempotent, so clamped duplicate loads are harmless; all loads are issued
   // before the first use), and fills a table of fl32(1 / v) for the E4M3
-  // values v (code 0 -> 0; code 0x7F is NaN and never looked up)
+  // values v (code 0 -> 0; code 0x7F is NaN and never looked up), once its
+  // first tile's loads are in flight
   __shared__ uint32_t wave_max[kThreads / 64];
   __shared__ float rcp_e4m3[128];
   const float one = 1.0f;  // scale operand of the converts: 2^0
-  uint32_t pv[kNvPer];
-#pragma unroll
-  for (int j = 0; j < kNvPer; j++) pv[j] = partial[min((int)threadIdx.x + j * kThreads, npartial - 1)];
-  if (threadIdx.x < 128) {
-    const float v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(threadIdx.x, one, false)[0];
-    rcp_e4m3[threadIdx.x] = threadIdx.x == 0 ? 0.0f : 1.0f / v;
-  }
-  uint32_t a = 0;
-#pragma unroll
-  for (int j = 0; j < kNvPer; j++) a = max(a, pv[j]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off, 64));
-  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = a;
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; w++) a = max(a, wave_max[w]);
-  const int t = nv_tensor_exp(a);
-  if (!FQ && blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = (uint8_t)(t + 127);
-  const float S = __uint_as_float((uint32_t)(t + 127) << 23);
-  const float inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t
-
+  float S = 0.0f, inv_s = 0.0f;
   Item<BF16> xv[kUnroll];
   uint32_t cw[kUnroll], sv[kUnroll], out[kUnroll][FQ ? (BF16 ? 4 : 8) : 1];
-  tile_loop<kUnroll>(
-      nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
+  tile_loop_pro<kUnroll>(
+      nitems,
+      [&]() {
+        uint32_t pv[kNvPer];
+#pragma unroll
+        for (int j = 0; j < kNvPer; j++)
+          pv[j] = partial[min((int)threadIdx.x + j * kThreads, npartial - 1)];
+        if (threadIdx.x < 128) {
+          const float v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(threadIdx.x, one, false)[0];
+          rcp_e4m3[threadIdx.x] = threadIdx.x == 0 ? 0.0f : 1.0f / v;
+        }
+        uint32_t a = 0;
+#pragma unroll
+        for (int j = 0; j < kNvPer; j++) a = max(a, pv[j]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off, 64));
+        if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = a;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; w++) a = max(a, wave_max[w]);
+        const int t = nv_tensor_exp(a);
+        if (!FQ && blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = (uint8_t)(t + 127);
+        S = __uint_as_float((uint32_t)(t + 127) << 23);
+        inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t
+      },
+      [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) {
         const uint32_t ab = dpp_x1_max(item_amax_bits<BF16>(xv[u]));  // NaN/Inf sort above
         uint32_t c;
@@ -1509,31 +1566,44 @@ __global__ __launch_bounds__(NT) void k_quantize_mbs(const void *x, uint32_t *__
                                                      uint8_t *__restrict__ sub_scales,
                                                      uint8_t *__restrict__ macro_mant, void *y,
                                                      int64_t nitems) {
-  // fl32(1 / f) for every macro mantissa m (f = 1 + m/256): IEEE division,
-  // once per workgroup, so the per-item cost is one LDS read
   static_assert(256 % NT == 0, "whole table entries per thread");
   __shared__ float inv_tab[256];
-  for (int e = threadIdx.x; e < 256; e += NT) inv_tab[e] = 1.0f / (1.0f + (float)e * (1.0f / 256.0f));
-  __syncthreads();
   const int64_t tile = (int64_t)NT * U;
   const int64_t nfull = nitems / tile;
   Item<BF16> xv[U];
-  int64_t t = blockIdx.x;
-  for (; t < nfull; t += gridDim.x) {
+  const auto load_tile = [&](int64_t t) {
     const int64_t base = t * tile + threadIdx.x;
+    if (t < nfull) {
 #pragma unroll
-    for (int u = 0; u < U; u++) load_item<BF16>(x, base + u * NT, xv[u]);
+      for (int u = 0; u < U; u++) load_item<BF16>(x, base + u * NT, xv[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        if (base + u * NT < nitems) load_item<BF16>(x, base + u * NT, xv[u]);
+        else xv[u] = Item<BF16>{};  // zeros: finite, so lanes past the end stay quiet
+      }
+    }
+  };
+  // The first tile's loads go out before the table is built, so they are in
+  // flight while it is (with one tile per workgroup on multi-GB tensors the
+  // table would otherwise delay every load).
+  int64_t t = blockIdx.x;
+  const bool has_tile = t < nfull || (t == nfull && nfull * tile < nitems);
+  if (has_tile) load_tile(t);
+  // fl32(1 / f) for every macro mantissa m (f = 1 + m/256): IEEE division,
+  // once per workgroup, so the per-item cost is one LDS read
+  for (int e = threadIdx.x; e < 256; e += NT) inv_tab[e] = 1.0f / (1.0f + (float)e * (1.0f / 256.0f));
+  __syncthreads();
+  for (; t < nfull; t += gridDim.x) {
+    if (t != (int64_t)blockIdx.x) load_tile(t);
     __builtin_amdgcn_sched_barrier(0);
-    mbs_tile<BF16, U, FQ, NT>(xv, inv_tab, codes, sub_scales, macro_mant, y, base, nitems, true);
+    mbs_tile<BF16, U, FQ, NT>(xv, inv_tab, codes, sub_scales, macro_mant, y, t * tile + threadIdx.x,
+                              nitems, true);
   }
   if (t == nfull && nfull * tile < nitems) {
-    const int64_t base = t * tile + threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      if (base + u * NT < nitems) load_item<BF16>(x, base + u * NT, xv[u]);
-      else xv[u] = Item<BF16>{};  // zeros: finite, so lanes past the end stay quiet
-    }
-    mbs_tile<BF16, U, FQ, NT>(xv, inv_tab, codes, sub_scales, macro_mant, y, base, nitems, false);
+    if (t != (int64_t)blockIdx.x) load_tile(t);
+    mbs_tile<BF16, U, FQ, NT>(xv, inv_tab, codes, sub_scales, macro_mant, y, t * tile + threadIdx.x,
+                              nitems, false);
   }
 }
 
