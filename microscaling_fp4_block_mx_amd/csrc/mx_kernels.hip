@@ -143,11 +143,12 @@ __device__ __forceinline__ double row_sum_f64(double p) {
 // at the end of the kernel). fp32 items take two 16-byte accesses whose
 // per-instruction footprint is strided (32-byte lane pitch): fp32 loads,
 // and the small code/scale accesses, stay on the default cache policy,
-// which measured faster for them; fp32 stores are regrouped through LDS into
-// contiguous non-temporal stores (store_item). The per-block errors (one
-// 4-byte store per quad) are stored non-temporally too: on the 2.8e9-
-// element weight set block MSE with its tensor sums took 1197 us against
-// 1226-1240 us on the default policy.
+// which measured faster for them (the code-word stores of the narrow
+// multi-GB quantize tilings excepted: see nt_codes); fp32 stores are
+// regrouped through LDS into contiguous non-temporal stores (store_item).
+// The per-block errors (one 4-byte store per quad) are stored
+// non-temporally too: on the 2.8e9-element weight set block MSE with its
+// tensor sums took 1197 us against 1226-1240 us on the default policy.
 template <bool NT, typename T>
 __device__ __forceinline__ T ld(const T *p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -719,7 +720,9 @@ constexpr int threads_of(bool bf16, int mode, int kind, bool large = false) {
 // default elsewhere. On the 2.8e9-element weight set OAS quantize took 1087
 // against 1122 us with the hint (OAS_NF unchanged), and MXFP8 quantize of the
 // MoE w13 experts 733 against 765 us; OCP quantize (256 x 1) was 2 % slower
-// with it and MBS-Static quantize unchanged, so they keep the default.
+// with it and MBS-Static quantize unchanged, so they keep the default, as do
+// the small-tensor tilings (on bf16 8192x4096 and 16384x8192 the hint made
+// OCP and OAS_BITS quantize 5-7 % and MXFP8 quantize 1-3 % slower).
 constexpr bool nt_codes(int nt) { return nt < kThreads; }
 
 template <bool BF16, int MODE, int U, int NT>
