@@ -157,7 +157,7 @@ def _u_nt(k: str):
 
 
 def kernel_family(k: str) -> str:
-    """k_quantize<true, 0, 1, 256> -> k_quantize<true, 0, U>,
+    """k_quantize<true, 0, 2, 128> -> k_quantize<true, 0, U>,
     k_block_mse<true, true, 2> -> k_block_mse<true, true, U>; other names
     as they are."""
     p = _u_nt(k)
@@ -1277,7 +1277,7 @@ PROFILE_HOW = ("Each rocprofv3 command runs on its own, from a scratch working d
 
 
 def _kernel_short(name: str) -> str:
-    """'void mxk::k_quantize<true, 0, 1, 256>(void const*, ...)' -> 'k_quantize<true, 0, 1, 256>'."""
+    """'void mxk::k_quantize<true, 0, 2, 128>(void const*, ...)' -> 'k_quantize<true, 0, 2, 128>'."""
     m = re.search(r"\b(k_\w+(?:<[^()]*>)?)\(", name)
     return m.group(1) if m else name.split("(")[0]
 

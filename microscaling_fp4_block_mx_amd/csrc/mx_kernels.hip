@@ -673,12 +673,11 @@ constexpr int kU = BF16 ? kUnroll : (kUnroll >= 4 ? kUnroll / 4 : 1);
 // stream; one fp32 fake-quant item was 5 % slower on fp32 1024x4096). Beyond
 // it (multi-GB weight sets streamed once from HBM) fewer items per thread keep
 // the memory that the resident workgroups touch at one time compact: on the
-// 2.8e9-element Llama-3.2-3B weight set, quantize OCP with one item per thread
-// was 3.5 % faster than four, overflow-aware quantize with two 3.6 % faster,
-// fake-quant with one 5 % faster than two, dequantize keeps two; OAS_NF
-// quantize takes two with 128-thread workgroups (see threads_of: 3.6-5 %
-// faster than four items with 256). The multi-tensor launch picks by the items of the whole
-// call.
+// 2.8e9-element Llama-3.2-3B weight set fake-quant with one item per thread
+// was 5 % faster than two and dequantize keeps two; quantize takes two items
+// per 128-thread workgroup in every mode, with non-temporal code stores (see
+// threads_of and nt_codes). The multi-tensor launch picks by the items of
+// the whole call.
 #ifndef MX_LARGE_ITEMS
 #define MX_LARGE_ITEMS (int64_t(3) << 23)
 #endif
@@ -687,8 +686,7 @@ enum { kKindQuantize = 0, kKindFakequant = 1, kKindDequantize = 2 };
 constexpr int unroll_of(bool bf16, int mode, int kind, bool large = false) {
   if (bf16 && large) {
     if (kind == kKindFakequant) return 1;
-    if (kind == kKindDequantize) return 2;
-    return mode == MX_SCALE_OAS_NF || mode == MX_SCALE_OAS ? 2 : 1;
+    return 2;  // quantize (every mode) and dequantize
   }
   if (kind == kKindFakequant) return 2;
   if (!bf16) return kU<false>;
@@ -703,25 +701,32 @@ constexpr int unroll_of(bool bf16, int mode, int kind, bool large = false) {
 // 128 4-6 % faster (64: up to 3 % slower, 512: 3 % slower), dequantize with
 // 64 2.4 % faster and fake-quant with 64 faster in every mode (OCP 1.6-1.8 %,
 // OAS 4 %, OAS_BITS 1.7 %, OAS_NF 5 %; 128 and 512 slower or equal), OAS_NF
-// quantize with 128 threads and two items 3.6-5 % faster than 256 and four,
-// while quantize OCP and OAS_BITS keep 256 with one item (64 and 128: 2-5 %
-// slower; two or four items per thread 6-13 % slower). A
-// plain copy of the same buffer ran 3.4 % faster with 64 than with 256.
+// quantize with 128 threads and two items 3.6-5 % faster than 256 and four.
+// With default-policy code stores quantize OCP and OAS_BITS were fastest at
+// 256 threads with one item (64 and 128: 2-5 % slower; two or four items per
+// thread 6-13 % slower); with the non-temporal code stores of the narrow
+// tilings (nt_codes) 128 x 2 beats that too: OCP 1091 against 1130 us and
+// OAS_BITS 1088 against 1122 us on the weight set, and the multi-tensor call
+// over its 196 matrices 1110 against 1196 us (OCP) and 1107 against 1208 us
+// (OAS_BITS); 128 x 1 was 5-6 % slower. A plain copy of the same buffer ran
+// 3.4 % faster with 64 than with 256.
 constexpr int threads_of(bool bf16, int mode, int kind, bool large = false) {
+  (void)mode;
   if (!bf16 || !large) return kThreads;
   if (kind == kKindFakequant || kind == kKindDequantize) return 64;
-  if (kind == kKindQuantize && (mode == MX_SCALE_OAS || mode == MX_SCALE_OAS_NF)) return 128;
-  return kThreads;
+  return 128;  // quantize, every mode
 }
 
-// Cache policy of the code-word stores of a single-tensor quantize launch:
-// non-temporal for the narrow multi-GB tilings (fewer than kThreads threads
-// per workgroup: the overflow-aware modes' 128 x 2 and MXFP8's 64 x 1),
-// default elsewhere. On the 2.8e9-element weight set OAS quantize took 1087
-// against 1122 us with the hint (OAS_NF unchanged), and MXFP8 quantize of the
-// MoE w13 experts 733 against 765 us; OCP quantize (256 x 1) was 2 % slower
-// with it and MBS-Static quantize unchanged, so they keep the default, as do
-// the small-tensor tilings (on bf16 8192x4096 and 16384x8192 the hint made
+// Cache policy of the code-word stores of a quantize launch: non-temporal
+// for the narrow multi-GB tilings (fewer than kThreads threads per
+// workgroup: MXFP4 quantize's 128 x 2 in every mode, single-tensor and
+// multi-tensor, and MXFP8's 64 x 1), default elsewhere. On the 2.8e9-element
+// weight set OAS quantize took 1087 against 1122 us with the hint (OAS_NF
+// unchanged), the multi-tensor OAS call 1086 against 1227 us, and MXFP8
+// quantize of the MoE w13 experts 733 against 765 us; OCP quantize at 256 x 1
+// was 2 % slower with it (at 128 x 2 it is faster than 256 x 1 without it:
+// see threads_of) and MBS-Static quantize unchanged, so MBS keeps the
+// default, as do the small-tensor tilings (on bf16 8192x4096 and 16384x8192 the hint made
 // OCP and OAS_BITS quantize 5-7 % and MXFP8 quantize 1-3 % slower). The
 // two-lanes-per-block OAS_NF kernel (k_quantize_pair, 8-byte code stores)
 // takes the hint: on bf16 8192x4096 activations its median launch went from
@@ -849,7 +854,7 @@ __global__ __launch_bounds__(NT) void k_multi(const MultiArgs a) {
         if constexpr (FQ) {
           store_item<BF16>(d.out, it, out[u]);
         } else {
-          st<false>(static_cast<uint32_t *>(d.out) + it, cw[u]);
+          st<nt_codes(NT)>(static_cast<uint32_t *>(d.out) + it, cw[u]);
           if ((threadIdx.x & 3) == 0) st<false>(d.scales + (it >> 2), (uint8_t)sv[u]);
         }
       });
