@@ -1562,7 +1562,7 @@ __device__ __forceinline__ void mbs_tile(const Item<BF16> (&xv)[U], const float 
         mbs_decode_item<BF16>(c[u], s[u], m[u], out);
         store_item<BF16>(y, it, out);
       } else {
-        st<false>(codes + it, c[u]);
+        st<true>(codes + it, c[u]);  // non-temporal: see tiling_mbs
         if ((threadIdx.x & 1) == 0) st<false>(sub_scales + (it >> 1), (uint8_t)s[u]);
         if ((threadIdx.x & 15) == 0) st<false>(macro_mant + (it >> 4), (uint8_t)m[u]);
       }
@@ -2017,10 +2017,15 @@ hipError_t mxi_launch_dequantize_nv(const uint8_t *codes, const uint8_t *block_s
 // Tiling of the MBS-Static kernels, as for MXFP8: grid-capped below
 // kLargeItems items (quantize four items per thread, dequantize two as MXFP4
 // dequantize: 2.5 % faster), and on multi-GB bf16 tensors one tile per
-// workgroup with no cap: quantize and fake-quant one item per 256-thread
-// workgroup (on the 1.6e9-element MoE w13 experts 3 % and 10 % faster than
-// the small-tensor tiling; 64 threads 7-17 % slower, 128 x 2 within 1 %),
-// dequantize two items per 64 threads (3 % faster; 128 threads equal).
+// workgroup with no cap: quantize two items per 128-thread workgroup and
+// fake-quant one per 256 threads (on the 1.6e9-element MoE w13 experts
+// fake-quant 10 % faster than the small-tensor tiling; 64 x 1, 128 x 1 and
+// 128 x 2 equal or up to 4 % slower), dequantize two items per 64 threads
+// (3 % faster; 128 threads equal). Quantize stores its code words
+// non-temporally at every size: on the MoE w13 experts 128 x 2 with the hint
+// took 626 against 711 us for 256 x 1 without it (128 x 1: 734 us, 64 x 2:
+// 686 us), on bf16 16384x8192 activations the hint alone 4 % less, on
+// 8192x4096 the same.
 struct TilingMbs {
   int u, nt;
   int64_t cap;
@@ -2028,7 +2033,8 @@ struct TilingMbs {
 constexpr TilingMbs tiling_mbs(bool bf16, int kind, bool large) {
   if (bf16 && large) {
     if (kind == kKindDequantize) return {2, 64, kGridLimit};
-    return {1, 256, kGridLimit};
+    if (kind == kKindQuantize) return {2, 128, kGridLimit};
+    return {1, 256, kGridLimit};  // fake-quant
   }
   if (kind == kKindDequantize) return {unroll_of(bf16, 0, kKindDequantize), kThreads, MX_GRID_CAP};
   return {bf16 ? kU<true> : kU<false>, kThreads, MX_GRID_CAP};
@@ -2037,7 +2043,7 @@ constexpr TilingMbs tiling_mbs(bool bf16, int kind, bool large) {
 template <bool BF16, bool FQ, bool LARGE>
 static void launch_quantize_mbs_t(const void *x, int64_t nitems, uint32_t *c, uint8_t *sub_scales,
                                   uint8_t *macro_mant, void *y, hipStream_t st) {
-  constexpr TilingMbs t = tiling_mbs(BF16, kKindQuantize, LARGE);
+  constexpr TilingMbs t = tiling_mbs(BF16, FQ ? kKindFakequant : kKindQuantize, LARGE);
   hipLaunchKernelGGL((k_quantize_mbs<BF16, FQ, t.u, t.nt>),
                      dim3(grid_for(nitems, t.cap, t.u, t.nt)), dim3(t.nt), 0, st, x, c,
                      sub_scales, macro_mant, y, nitems);
