@@ -557,8 +557,10 @@ __device__ __forceinline__ uint32_t quantize_pair(const PairItem &x, u32x2 &code
 // XCD walks one contiguous eighth of the tensor (a bijection on the tiles,
 // so the results do not change). On the 2.8e9-element weight set this made
 // dequantize 2.5-3.3 % faster (also on the MoE experts), left fake-quant
-// unchanged and made quantize 8 % and block MSE 4 % slower; runs of four
-// tiles per XCD were slower for all of them.
+// unchanged and made block MSE 4 % slower; quantize went 8 % slower at one
+// item per 256 threads, and at two per 128 (with non-temporal code stores)
+// 1.8 % faster in OCP and OAS_BITS, 1.2 % slower in OAS; runs of four tiles
+// per XCD were slower for all of them.
 template <int U, bool XCD_CHUNKS = false, int NT = kThreads, typename Load, typename Compute,
           typename Store>
 __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Compute compute,
@@ -739,7 +741,12 @@ __global__ __launch_bounds__(NT) void k_quantize(const void *__restrict__ x,
                                                  uint8_t *__restrict__ scales, int64_t nitems) {
   Item<BF16> xv[U];
   uint32_t cw[U], sv[U];
-  tile_loop<U, false, NT>(
+  // per-XCD eighths for OCP and OAS_BITS on the multi-GB tiling: on the
+  // 2.8e9-element weight set 1076 against 1096 us (OCP) and 1074 against
+  // 1094 us (OAS_BITS); OAS was 1.2 % slower with the map, so the
+  // error-driven modes keep launch order
+  constexpr bool kXcd = NT == 128 && (MODE == MX_SCALE_OCP || MODE == MX_SCALE_OAS_BITS);
+  tile_loop<U, kXcd, NT>(
       nitems, [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) { sv[u] = quantize_item<BF16, MODE>(xv[u], cw[u]); },
       [&](int u, int64_t it) {
