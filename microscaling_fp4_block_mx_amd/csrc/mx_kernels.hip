@@ -728,8 +728,10 @@ constexpr int threads_of(bool bf16, int mode, int kind, bool large = false) {
 // quantize of the MoE w13 experts 733 against 765 us; OCP quantize at 256 x 1
 // was 2 % slower with it (at 128 x 2 it is faster than 256 x 1 without it:
 // see threads_of) and MBS-Static quantize unchanged, so MBS keeps the
-// default, as do the small-tensor tilings (on bf16 8192x4096 and 16384x8192 the hint made
-// OCP and OAS_BITS quantize 5-7 % and MXFP8 quantize 1-3 % slower). The
+// default, as do the small-tensor tilings (on bf16 8192x4096 and 16384x8192
+// the hint made OCP and OAS_BITS quantize 5-7 % and MXFP8 quantize 1-3 %
+// slower, and the multi-GB 128 x 2 tiling with it was 3-4 % slower there
+// than 256 x 4). The
 // two-lanes-per-block OAS_NF kernel (k_quantize_pair, 8-byte code stores)
 // takes the hint: on bf16 8192x4096 activations its median launch went from
 // 17.1-18.4 to 16.3-16.9 us (same p10, a tighter spread).
