@@ -113,7 +113,7 @@ KERNEL_OF = {"quantize_ocp": "k_quantize<true, 0, U>", "quantize_oas": "k_quanti
 # NT_KERNELS, U then the threads per workgroup NT), and one tile (NT threads
 # x U items x 8 elements; NT = 256 where not given) per workgroup at these sizes
 NT_KERNELS = ("k_quantize", "k_fakequant", "k_dequantize", "k_quantize8", "k_dequantize8",
-              "k_fakequant8", "k_quantize_mbs", "k_dequantize_mbs")
+              "k_fakequant8", "k_quantize_mbs", "k_dequantize_mbs", "k_quantize_nv_big")
 U_KERNELS = NT_KERNELS + ("k_block_mse", "k_quantize_pair")
 ITEM_ELEMS = {"k_quantize_pair": 16}  # elements per item where not 8 (two lanes per block)
 FUSED_ITEMS = 2  # items per thread of k_quantize_fused
@@ -1162,6 +1162,28 @@ def suite(args, dev):
     report(WM, "fakequant_mbs (w13 + w2)", 4.0 * n,
            _launch_stats(fqmb, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
     del smb, mmb
+    # and the NVFP4 comparator (16-element blocks, E4M3 block scales, a
+    # per-tensor factor): quantize (x read twice) and fake-quant
+    bnv = [torch.empty(w.numel() // 16, dtype=torch.uint8, device=dev) for w in (w13, w2)]
+    tnv = torch.empty(16, dtype=torch.uint8, device=dev)
+    wsnv = [mx.mx_nvfp4_workspace_size(rows, k) for (_, rows, k) in shapes]
+    wnv = [torch.empty(b_, dtype=torch.uint8, device=dev) for b_ in wsnv]
+
+    def qnv(_):
+        for (w, rows, k), c, b_, ws, wb in zip(shapes, cs, bnv, wnv, wsnv):
+            ok(mx.mx_quantize_nvfp4(w.data_ptr(), mx.MX_BF16, rows, k, c.data_ptr(), b_.data_ptr(),
+                                    tnv.data_ptr(), ws.data_ptr(), wb, sh))
+
+    def fqnv(_):
+        for (w, rows, k), y, ws, wb in zip(shapes, ys, wnv, wsnv):
+            ok(mx.mx_fakequant_nvfp4(w.data_ptr(), mx.MX_BF16, rows, k, y.data_ptr(),
+                                     ws.data_ptr(), wb, sh))
+
+    report(WM, "quantize_nvfp4 (w13 + w2)", (2 + 2 + 0.5 + 1 / 16) * n,
+           _launch_stats(qnv, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    report(WM, "fakequant_nvfp4 (w13 + w2)", 6.0 * n,
+           _launch_stats(fqnv, BIG_TIMED, BIG_WARM, stream), cache="exceeds cache")
+    del bnv, wnv
     # MXFP4 dequantize of the codes quantized above (its launches end the
     # timed part of the suite's profile)
     qm(0)
@@ -1461,6 +1483,12 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
             return n * (8.0 if f32 else 4.0)
         if kernel.startswith(("k_quantize_mbs<", "k_dequantize_mbs<")):
             return n * ((2.0 if f32 else 0.0) + 2 + 0.5 + 1 / 16 + 1 / 128)
+        if kernel.startswith("k_quantize_nv_big<true, true"):  # NVFP4 block pass, fake-quant
+            return n * 4.0
+        if kernel.startswith("k_quantize_nv_big<"):  # NVFP4 block pass, quantize
+            return n * (2 + 0.5 + 1 / 16)
+        if kernel.startswith("k_absmax_partials<"):  # NVFP4 maximum pass: x read once
+            return n * 2.0
         return None
 
     # the timed part ends with the MoE dequantize launches; the QSNR pass
@@ -1471,6 +1499,7 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
                and tile_elems(_kernel_short(r["Kernel_Name"]), grid_of(r)) in (m13, m2))
     groups = collections.OrderedDict()
     seen_c5 = collections.Counter()
+    seen_abs = collections.Counter()
     per_timing = 10 + 2 * 100  # dispatches of one _launch_stats call at the suite's defaults
     for r in rows[:last + 1]:
         k = _kernel_short(r["Kernel_Name"])
@@ -1483,6 +1512,15 @@ def _summarize_suite(path: str, code: str, out_dir: str) -> None:
             key = ("MULTI", k, None)
         elif k == "k_sum_partials":
             key = ("tensor-sum pass of block MSE (all workloads)", k, None)
+        elif k == "k_nv_prepare":
+            key = ("NVFP4 tensor-exponent reduction (MoE experts)", k, None)
+        elif k.startswith("k_absmax_partials<true"):
+            # NVFP4's maximum pass (a 2,048-workgroup grid for every size):
+            # the suite runs it on w13, then w2, in every call
+            which = seen_abs[k] % 2
+            seen_abs[k] += 1
+            nn = (m13, m2)[which]
+            key = (by_elems[nn], k, nn)
         elif k.startswith("k_ceiling"):
             key = ("fp32 normal [1024, 4096]: reference kernels", k, c1)
         elif "<false" in k:

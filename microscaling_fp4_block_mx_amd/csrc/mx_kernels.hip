@@ -605,10 +605,11 @@ __device__ __forceinline__ void tile_loop(int64_t nitems, Load load, Use use) {
 // barrier) that runs once the workgroup's first tile's loads are issued, so
 // that its latency overlaps theirs instead of delaying them; every thread
 // runs it. Later tiles load at the top of their iteration as in tile_loop.
-template <int U, typename Prologue, typename Load, typename Compute, typename Store>
+template <int U, int NT = kThreads, typename Prologue, typename Load, typename Compute,
+          typename Store>
 __device__ __forceinline__ void tile_loop_pro(int64_t nitems, Prologue prologue, Load load,
                                               Compute compute, Store store) {
-  const int64_t tile = (int64_t)kThreads * U;
+  const int64_t tile = (int64_t)NT * U;
   const int64_t nfull = nitems / tile;
   const bool partial = nfull * tile < nitems;
   const int64_t first = blockIdx.x;
@@ -616,40 +617,40 @@ __device__ __forceinline__ void tile_loop_pro(int64_t nitems, Prologue prologue,
   if (t < nfull) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < U; u++) load(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) load(u, base + u * NT);
   } else if (t == nfull && partial) {
     const int64_t base = t * tile + threadIdx.x;
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (base + u * kThreads < nitems) load(u, base + u * kThreads);
+      if (base + u * NT < nitems) load(u, base + u * NT);
   }
   prologue();
   for (; t < nfull; t += gridDim.x) {
     const int64_t base = t * tile + threadIdx.x;
     if (t != first) {
 #pragma unroll
-      for (int u = 0; u < U; u++) load(u, base + u * kThreads);
+      for (int u = 0; u < U; u++) load(u, base + u * NT);
     }
     __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
 #pragma unroll
-    for (int u = 0; u < U; u++) compute(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) compute(u, base + u * NT);
     __builtin_amdgcn_sched_barrier(0);  // every item's arithmetic ahead of the stores
 #pragma unroll
-    for (int u = 0; u < U; u++) store(u, base + u * kThreads);
+    for (int u = 0; u < U; u++) store(u, base + u * NT);
   }
   if (t == nfull && partial) {
     const int64_t base = t * tile + threadIdx.x;
     if (t != first) {
 #pragma unroll
       for (int u = 0; u < U; u++)
-        if (base + u * kThreads < nitems) load(u, base + u * kThreads);
+        if (base + u * NT < nitems) load(u, base + u * NT);
     }
 #pragma unroll
     for (int u = 0; u < U; u++)  // whole lane pairs and quads drop out together
-      if (base + u * kThreads < nitems) compute(u, base + u * kThreads);
+      if (base + u * NT < nitems) compute(u, base + u * NT);
 #pragma unroll
     for (int u = 0; u < U; u++)
-      if (base + u * kThreads < nitems) store(u, base + u * kThreads);
+      if (base + u * NT < nitems) store(u, base + u * NT);
   }
 }
 
@@ -1316,6 +1317,36 @@ __global__ __launch_bounds__(kThreads) void k_absmax_partials(const void *__rest
   }
 }
 
+// Forward declaration (defined below with the tensor factor's rule).
+__device__ __forceinline__ int nv_tensor_exp(uint32_t amax_bits);
+
+// One workgroup: the tensor exponent t from the npartial first-pass maxima,
+// to partial[npartial] for the block pass of a multi-GB tensor (and t + 127
+// to *tensor_scale when it is not null), so that pass's workgroups, one per
+// tile, read one word instead of reducing the maxima each.
+__global__ __launch_bounds__(kThreads) void k_nv_prepare(uint32_t *__restrict__ partial,
+                                                         int npartial,
+                                                         uint8_t *__restrict__ tensor_scale) {
+  __shared__ uint32_t wave_max[kThreads / 64];
+  uint32_t pv[kNvPer];
+#pragma unroll
+  for (int j = 0; j < kNvPer; j++) pv[j] = partial[min((int)threadIdx.x + j * kThreads, npartial - 1)];
+  uint32_t a = 0;
+#pragma unroll
+  for (int j = 0; j < kNvPer; j++) a = max(a, pv[j]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off, 64));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; w++) a = max(a, wave_max[w]);
+    const int t = nv_tensor_exp(a);
+    partial[npartial] = (uint32_t)t;
+    if (tensor_scale) *tensor_scale = (uint8_t)(t + 127);
+  }
+}
+
 // t of S = 2^t from the tensor amax bits: with amax = (1 + f) 2^(e - 127),
 // 2^t * amax <= 1.3125 * 2^11 gives t = 138 - e when 1 + f <= 1.3125
 // (mantissa field <= 0x280000), else 137 - e; capped at 127 (tiny or
@@ -1337,28 +1368,42 @@ __device__ __forceinline__ void nv_decode_item(uint32_t c, uint32_t sbyte, float
 
 // FQ: fake-quant (y = dequantize(quantize(x)) in x's dtype; y may be x)
 // instead of writing codes, block scales and the tensor byte.
-template <bool BF16, bool FQ>
-__global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *x,
-                                                          const uint32_t *__restrict__ partial,
-                                                          int npartial,
-                                                          uint32_t *__restrict__ codes,
-                                                          uint8_t *__restrict__ block_scales,
-                                                          uint8_t *__restrict__ tensor_scale,
-                                                          void *y, int64_t nitems) {
+// The NVFP4 block pass. PRE: the tensor exponent t was reduced once by
+// k_nv_prepare and sits at partial[npartial] (the multi-GB launch: one tile
+// per workgroup, NT threads, U items); otherwise every workgroup reduces the
+// npartial maxima itself.
+template <bool BF16, bool FQ, bool PRE, int U, int NT>
+__device__ __forceinline__ void nv_block_pass(const void *x, const uint32_t *__restrict__ partial,
+                                              int npartial, uint32_t *__restrict__ codes,
+                                              uint8_t *__restrict__ block_scales,
+                                              uint8_t *__restrict__ tensor_scale, void *y,
+                                              int64_t nitems) {
+  static_assert(PRE || NT == kThreads, "the in-kernel reduction assumes kThreads");
+  static_assert(NT >= 128 && NT % 64 == 0, "the table takes 128 threads");
   // every workgroup reduces the first pass's maxima (max is order-free and
   // idempotent, so clamped duplicate loads are harmless; all loads are issued
-  // before the first use), and fills a table of fl32(1 / v) for the E4M3
-  // values v (code 0 -> 0; code 0x7F is NaN and never looked up), once its
-  // first tile's loads are in flight
-  __shared__ uint32_t wave_max[kThreads / 64];
+  // before the first use), or reads their reduction (PRE), and fills a table
+  // of fl32(1 / v) for the E4M3 values v (code 0 -> 0; code 0x7F is NaN and
+  // never looked up), once its first tile's loads are in flight
+  __shared__ uint32_t wave_max[NT / 64];
   __shared__ float rcp_e4m3[128];
   const float one = 1.0f;  // scale operand of the converts: 2^0
   float S = 0.0f, inv_s = 0.0f;
-  Item<BF16> xv[kUnroll];
-  uint32_t cw[kUnroll], sv[kUnroll], out[kUnroll][FQ ? (BF16 ? 4 : 8) : 1];
-  tile_loop_pro<kUnroll>(
+  Item<BF16> xv[U];
+  uint32_t cw[U], sv[U], out[U][FQ ? (BF16 ? 4 : 8) : 1];
+  tile_loop_pro<U, NT>(
       nitems,
       [&]() {
+        if constexpr (PRE) {
+          const int t = (int)partial[npartial];
+          if (threadIdx.x < 128) {
+            const float v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(threadIdx.x, one, false)[0];
+            rcp_e4m3[threadIdx.x] = threadIdx.x == 0 ? 0.0f : 1.0f / v;
+          }
+          __syncthreads();
+          S = __uint_as_float((uint32_t)(t + 127) << 23);
+          inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t
+        } else {
         uint32_t pv[kNvPer];
 #pragma unroll
         for (int j = 0; j < kNvPer; j++)
@@ -1380,6 +1425,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *x,
         if (!FQ && blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = (uint8_t)(t + 127);
         S = __uint_as_float((uint32_t)(t + 127) << 23);
         inv_s = __uint_as_float((uint32_t)(127 - t) << 23);  // 2^-t
+        }
       },
       [&](int u, int64_t it) { load_item<BF16>(x, it, xv[u]); },
       [&](int u, int64_t) {
@@ -1416,10 +1462,38 @@ __global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *x,
         if constexpr (FQ) {
           store_item<BF16>(y, it, out[u]);
         } else {
-          st<false>(codes + it, cw[u]);
+          st<nt_codes(NT)>(codes + it, cw[u]);
           if ((threadIdx.x & 1) == 0) st<false>(block_scales + (it >> 1), (uint8_t)sv[u]);
         }
       });
+}
+
+// The block pass: 2048 workgroups looping over tiles, each reducing the
+// first pass's maxima itself.
+template <bool BF16, bool FQ>
+__global__ __launch_bounds__(kThreads) void k_quantize_nv(const void *x,
+                                                          const uint32_t *__restrict__ partial,
+                                                          int npartial,
+                                                          uint32_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ block_scales,
+                                                          uint8_t *__restrict__ tensor_scale,
+                                                          void *y, int64_t nitems) {
+  nv_block_pass<BF16, FQ, false, kUnroll, kThreads>(x, partial, npartial, codes, block_scales,
+                                                    tensor_scale, y, nitems);
+}
+
+// The block pass on multi-GB tensors: one tile of NT threads x U items per
+// workgroup, the tensor exponent read from partial[npartial] (k_nv_prepare).
+template <bool BF16, bool FQ, int U, int NT>
+__global__ __launch_bounds__(NT) void k_quantize_nv_big(const void *x,
+                                                        const uint32_t *__restrict__ partial,
+                                                        int npartial,
+                                                        uint32_t *__restrict__ codes,
+                                                        uint8_t *__restrict__ block_scales,
+                                                        uint8_t *__restrict__ tensor_scale,
+                                                        void *y, int64_t nitems) {
+  nv_block_pass<BF16, FQ, true, U, NT>(x, partial, npartial, codes, block_scales, tensor_scale,
+                                       y, nitems);
 }
 
 // Decoded values of one item: E2M1 code * s_b * 2^-t, exact in fp32 (at
@@ -1981,7 +2055,29 @@ hipError_t mxi_launch_fakequant8(const void *x, int bf16, int64_t nitems, void *
   return hipGetLastError();
 }
 
-size_t mxi_nvfp4_partials(int64_t nitems) { return grid_for(nitems, MX_NV_GRID_CAP); }
+// Workspace words of an NVFP4 call: one maximum per first-pass workgroup,
+// then the tensor exponent the multi-GB path reduces them to.
+size_t mxi_nvfp4_partials(int64_t nitems) { return grid_for(nitems, MX_NV_GRID_CAP) + 1; }
+
+// The block pass on multi-GB bf16 tensors: k_nv_prepare reduces the maxima
+// once, then one tile per workgroup with no grid cap, quantize two items per
+// 128 threads (with non-temporal code stores, nt_codes) and fake-quant one
+// per 256. On the 1.6e9-element MoE w13 experts both passes took 1081
+// against 1384 us (quantize) and 1436 against 1749 us (fake-quant) for the
+// 2048-workgroup grid that loops over tiles; 1 x 256, 1 x 128 and 4 x 256
+// quantize took 1128-1177 us, 2 x 128, 1 x 128 and 4 x 256 fake-quant
+// 1437-1596 us.
+template <bool FQ>
+static void launch_nv_large(const void *x, uint32_t *partial, unsigned gp, uint32_t *c,
+                            uint8_t *block_scales, uint8_t *tensor_scale, void *y, int64_t nitems,
+                            hipStream_t st) {
+  constexpr int U = FQ ? 1 : 2, NT = FQ ? 256 : 128;
+  hipLaunchKernelGGL(k_nv_prepare, dim3(1), dim3(kThreads), 0, st, partial, (int)gp,
+                     FQ ? nullptr : tensor_scale);
+  hipLaunchKernelGGL((k_quantize_nv_big<true, FQ, U, NT>),
+                     dim3(grid_for(nitems, kGridLimit, U, NT)), dim3(NT), 0, st, x, partial,
+                     (int)gp, c, block_scales, tensor_scale, y, nitems);
+}
 
 hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t nitems, uint8_t *codes,
                                   uint8_t *block_scales, uint8_t *tensor_scale,
@@ -1991,7 +2087,10 @@ hipError_t mxi_launch_quantize_nv(const void *x, int bf16, int64_t nitems, uint8
   uint32_t *c = reinterpret_cast<uint32_t *>(codes);
   if (bf16) {
     hipLaunchKernelGGL((k_absmax_partials<true>), dim3(gp), b, 0, st, x, partial, nitems);
-    if (y)
+    if (nitems >= kLargeItems) {
+      if (y) launch_nv_large<true>(x, partial, gp, c, block_scales, tensor_scale, y, nitems, st);
+      else launch_nv_large<false>(x, partial, gp, c, block_scales, tensor_scale, y, nitems, st);
+    } else if (y)
       hipLaunchKernelGGL((k_quantize_nv<true, true>), g, b, 0, st, x, partial, (int)gp, c,
                          block_scales, tensor_scale, y, nitems);
     else

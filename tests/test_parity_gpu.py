@@ -327,9 +327,8 @@ def test_bf16_8192x4096_student_t_fakequant_full():
 
 def test_large_tensor_tiling_every_mode():
     """One bf16 tensor just at the multi-GB tiling (2^24 * 12 items = 2.0e8
-    elements: one item per thread for quantize OCP / OAS_BITS and
-    fake-quant, two for OAS / OAS_NF quantize and dequantize, 64- or 128-
-    thread workgroups where chosen): every mode's codes, scales and
+    elements: two items per 128 threads for quantize in every mode, one per
+    64 threads for fake-quant, two per 64 for dequantize): every mode's codes, scales and
     fake-quant output, and the dequantized tensor, whole against the oracle;
     likewise MXFP8 and MBS-Static quantize, dequantize and fake-quant."""
     x = workloads.bf16_laplace_sparse_outliers(8, shape=(49152, 4096))
@@ -359,7 +358,8 @@ def test_large_tensor_tiling_every_mode():
     del c, s
     assert_same_bits(mx.fakequant_mxfp8(xd), oracle.fakequant_mxfp8(xh, threads=THREADS),
                      "large mxfp8 fakequant")
-    # and MBS-Static (one item per 256 threads; dequantize two per 64)
+    # and MBS-Static (quantize two items per 128 threads, fake-quant one per
+    # 256; dequantize two per 64)
     say("large tiling mbs-static")
     c, s, m = mx.quantize_mbs(xd)
     wc, ws, wm = oracle.quantize_mbs(xh)

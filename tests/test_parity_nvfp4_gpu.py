@@ -114,3 +114,19 @@ def test_nvfp4_fakequant_in_place():
     got = mx.fakequant_nvfp4(y, out=y)
     assert got.data_ptr() == y.data_ptr()
     assert torch.equal(want.view(torch.int16), got.view(torch.int16))
+
+
+def test_nvfp4_large_tiling():
+    """The multi-GB path (past 2.0e8 elements the tensor exponent is reduced
+    once and the block pass runs one tile per workgroup: quantize two items
+    per 128 threads, fake-quant one per 256), on a bf16 tensor whose last
+    tile is partial in both tilings (49153 x 4112: 514 items per row), whole
+    against the oracle; fake-quant also in place."""
+    x = workloads.bf16_laplace_sparse_outliers(9, shape=(49153, 4112))
+    assert x.numel() // 8 >= 3 << 23 and (x.numel() // 8) % 256 != 0
+    check_nv(x, "large-tiling")
+    xd = x.cuda()
+    want = mx.fakequant_nvfp4(xd)
+    got = mx.fakequant_nvfp4(xd, out=xd)
+    assert got.data_ptr() == xd.data_ptr()
+    assert torch.equal(want.view(torch.int16), got.view(torch.int16)), "large in-place fake-quant"
