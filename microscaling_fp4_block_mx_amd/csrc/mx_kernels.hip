@@ -1989,7 +1989,9 @@ hipError_t mxi_scratch_address(int dev, double **out) {
 // 1.6e9-element MoE w13 experts quantize and fake-quant with one item per
 // thread ran 12.6 % faster than the small-tensor tiling, dequantize with two
 // 7.4 % faster (the XCD map of MXFP4 dequantize made it 3 % slower here; one
-// item, or 256 threads, 2-6 % slower).
+// item, or 256 threads, 2-6 % slower); dequantize later moved to two items
+// per 128 threads (752 against 769 us on the w13 experts; four per 64:
+// 844 us).
 struct Tiling8 {
   int u, nt;
   int64_t cap;
@@ -1997,7 +1999,7 @@ struct Tiling8 {
 constexpr Tiling8 tiling8(bool bf16, int kind, bool large) {
   if (bf16 && large) {
     if (kind == kKindQuantize) return {1, 64, kGridLimit};
-    if (kind == kKindDequantize) return {2, 64, kGridLimit};
+    if (kind == kKindDequantize) return {2, 128, kGridLimit};
     return {1, 64, kGridLimit};
   }
   if (kind == kKindQuantize) return {bf16 ? kU8<true> : kU8<false>, kThreads, MX_GRID_CAP};

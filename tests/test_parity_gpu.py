@@ -347,7 +347,8 @@ def test_large_tensor_tiling_every_mode():
         del c, s
         assert_same_bits(mx.fakequant(xd, mode), oracle.fakequant(xh, mode, threads=THREADS),
                          f"large fakequant {mode}")
-    # MXFP8 at its multi-GB tiling (one or two items per 64-thread workgroup)
+    # MXFP8 at its multi-GB tiling (quantize and fake-quant one item per 64
+    # threads, dequantize two per 128)
     say("large tiling mxfp8")
     c, s = mx.quantize_mxfp8(xd)
     wc, ws = oracle.quantize_mxfp8(xh, threads=THREADS)
