@@ -54,13 +54,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef MX_UNROLL
 #define MX_UNROLL 4
 #endif
-// Most workgroups a launch of the other formats' kernels uses (beyond it,
-// workgroups loop over tiles). Measured
-// on a 2.1e9-element bf16 tensor with four items per thread: 196,608 (768
-// per CU) beat 65,536 by 5 % (quantize) and 3 % (dequantize), while
-// 8,192-32,768 were slower. The MXFP4 single-tensor kernels are not capped
-// (see kGridLimit). Below the cap every workgroup takes one tile: tensors up
-// to ~1.6e9 elements with four items per thread, ~4e8 with one.
+// Most workgroups a launch of the other formats' kernels uses below the
+// multi-GB size (beyond it, workgroups loop over tiles). Measured on a
+// 2.1e9-element bf16 tensor with four items per thread: 196,608 (768 per CU)
+// beat 65,536 by 5 % (quantize) and 3 % (dequantize), while 8,192-32,768
+// were slower. The MXFP4 single-tensor kernels, and the other formats'
+// multi-GB bf16 tilings, are not capped (see kGridLimit). Below the cap
+// every workgroup takes one tile: tensors up to ~1.6e9 elements with four
+// items per thread, ~4e8 with one.
 #ifndef MX_GRID_CAP
 #define MX_GRID_CAP 196608
 #endif
