@@ -235,7 +235,9 @@ mx_status_t mx_fakequant_mxfp8(const void *x, mx_dtype_t dtype, int64_t rows,
  * (E2M1 * s_b) / S exactly, then rounds to bf16 if asked. A block holding
  * NaN/Inf gets block scale 0x7F and sign-only codes and decodes to NaN.
  * Quantize reads x twice (tensor maximum, then the blocks) and needs a
- * workspace of mx_nvfp4_workspace_size(rows, k) bytes (4-byte aligned).
+ * workspace of mx_nvfp4_workspace_size(rows, k) bytes (4-byte aligned): one
+ * 4-byte maximum per first-pass workgroup (at most 2048) and one word for
+ * the tensor exponent, so 8,196 bytes cover every shape.
  * rows == 0 does nothing. Other conventions as above. */
 size_t mx_nvfp4_workspace_size(int64_t rows, int64_t k);
 /* y = mx_dequantize_nvfp4(mx_quantize_nvfp4(x)) in x's dtype, fused (x is

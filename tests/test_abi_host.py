@@ -214,6 +214,10 @@ def test_nvfp4_validation(lib):
     need = mx.mx_nvfp4_workspace_size(8192, 4096)
     assert 4 <= need <= 8192 * 4 and need % 4 == 0
     assert mx.mx_nvfp4_workspace_size(1, 24) == 0
+    # one maximum per first-pass workgroup (1024 items each, at most 2048) and
+    # the tensor-exponent word
+    assert mx.mx_nvfp4_workspace_size(1, 16) == 2 * 4
+    assert mx.mx_nvfp4_workspace_size(49153, 4112) == 2049 * 4
     assert mx.mx_quantize_nvfp4(A, 1, 1, 24, B, C, W, W + 64, 64, None) == mx.MX_ERR_SHAPE
     assert mx.mx_quantize_nvfp4(A, 1, 0, 16, None, None, None, None, 0, None) == mx.MX_OK
     assert mx.mx_quantize_nvfp4(A, 1, 1, 16, B, C, None, W + 64, 64, None) == mx.MX_ERR_NULL
