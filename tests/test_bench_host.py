@@ -179,3 +179,33 @@ def test_every_op_beside_the_step_has_roofline_kernels():
         r = bench.beside_roofline(op, row)
         assert r["bound"] == "hbm" and r["peak"] == bench.HBM_PEAK_GBS and r["frac"] == 0.5
         assert r["traffic"] is None or r["traffic"] > 0
+
+
+def test_suite_attribution_nvfp4_moe(tmp_path):
+    # NVFP4 on the MoE experts: the 2,048-workgroup maximum pass alternates
+    # w13, w2 in every call; the exponent reduction is one workgroup; the
+    # multi-GB block pass (one tile per workgroup) is told apart by elements
+    wg = 256
+    m13, m2 = 128 * 3072 * 4096, 128 * 4096 * 1536
+    disp = []
+    for _ in range(2):  # two calls: w13 then w2 each
+        for n in (m13, m2):
+            disp += [("k_absmax_partials<true>", 2048, wg), ("k_nv_prepare", 1, wg),
+                     ("k_quantize_nv_big<true, false, 2, 128>", n // 8 // 256, 128)]
+    disp += [("k_dequantize<true, 2, 64>", m2 // 8 // 128, 64)]  # ends the timed part
+    rows = [[f"void mxk::{k}(void const*, long)", g * w, w, 10 * i * 1000, (10 * i + 1) * 1000]
+            for i, (k, g, w) in enumerate(disp)]
+    _write(tmp_path / "suite_kernel_trace.csv",
+           ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"],
+           rows)
+    bench._summarize_suite(str(tmp_path / "suite_kernel_trace.csv"), "", str(tmp_path))
+    text = (tmp_path / "mx_workloads_suite_kernel_trace.md").read_text()
+    lines = {ln.split("|")[1].strip() + " " + ln.split("|")[2].strip(): ln
+             for ln in text.splitlines() if ln.startswith("| ") and "`k_" in ln}
+    for wl, n in (("MoE w13 [128x3072, 4096]", m13), ("MoE w2 [128x4096, 1536]", m2)):
+        absmax = lines[f"{wl} `k_absmax_partials<true>`"].split("|")
+        assert absmax[3].strip() == "2" and int(absmax[7]) == 2 * n  # dispatches, x read once
+        block = lines[f"{wl} `k_quantize_nv_big<true, false, 2, 128>`"].split("|")
+        assert block[3].strip() == "2" and int(block[7]) == int(n * (2 + 0.5 + 1 / 16))
+    assert "NVFP4 tensor-exponent reduction (MoE experts) `k_nv_prepare`" in lines
+    assert "unattributed" not in text
